@@ -1,0 +1,239 @@
+#!/usr/bin/env python3
+"""Benchmark: paged decode attention on one MI355X.
+
+Workload (default): GQA decode in bf16, batch 256, 32 query heads over 8 KV
+heads (group 4), head_dim 128, block size 16, context lengths lognormal with
+mean about 200 tokens capped at 4096, blocks handed out from a shuffled free
+list.  One step is one pass of the whole hot path over one batch:
+  pa_copy_blocks (copy-on-write pairs of this step; none in this workload)
+  -> pa_reshape_and_cache (this step's token for every sequence)
+  -> pa_decode (attention through the block tables; split sequences merged by a
+     second, small launch).
+Step inputs (tables, lengths, slots, work items, queries, new keys/values) are
+resident in device memory before timing; the host block-manager append that
+produces them is timed separately (host_append_us).  R pool replicas (>= 1 GiB
+together, four times the 256 MB last-level cache) rotate so that KV reads come
+from HBM.
+
+Prints one JSON line.  `value` is KV-read GB/s over whole steps: algorithmic KV
+bytes (each live token's K and V row of each KV head, read once) per step
+divided by the step time.  `roofline` reports the decode kernel alone, timed
+per launch with HIP events on the stream it runs on.
+"""
+from __future__ import annotations
+
+import os
+
+for _v in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+    os.environ[_v] = "1"   # the CPU baseline is single-threaded by design
+
+import argparse
+import hashlib
+import json
+import math
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+WORKLOADS = {
+    "c3": "GQA decode bf16: batch 256, 32 q heads / 8 KV heads, head_dim 128, block 16, "
+          "lognormal lengths (mean ~200, cap 4096), shuffled blocks",
+    "c2": "MHA decode bf16: batch 64, 32/32 heads, head_dim 128, block 16, lengths U[1,2048]",
+    "c4": "long-context GQA decode bf16: batch 16, 64 q / 8 KV heads, head_dim 128, block 16, "
+          "lengths U[16384,32768]",
+}
+DEFAULT_PARTITION = {"c3": 256, "c2": 512, "c4": 512}
+PMC_FILE = os.path.join(ROOT, "profiles", "decode_c3_pmc.json")
+KERNEL_SRC = os.path.join(ROOT, "paged_kv_cache_115_amd", "csrc", "decode_kernels.hip")
+
+
+def kernel_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(config: str, partition: int):
+    """HBM bytes per decode launch from committed rocprofv3 counter runs, if
+    they were taken on the current kernel source and this configuration."""
+    try:
+        rec = json.load(open(PMC_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_sha") != kernel_hash() or rec.get("config") != config or rec.get("partition") != partition:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(case, k_host, v_host, tables, lens, budget_s: float):
+    """The float64 oracle over the sequences of the same batch, in order and
+    wrapping around, until about `budget_s` seconds of single-core work;
+    reported in the headline unit (KV GB/s) and as sequences per second."""
+    import oracle
+    cfg = case["cfg"]
+    per_token = cfg["num_kv_heads"] * cfg["head_dim"] * 2 * synth.element_bytes(cfg["dtype"])
+    t0 = time.perf_counter()
+    done, tokens = 0, 0
+    while time.perf_counter() - t0 < budget_s:
+        s = done % len(lens)
+        oracle.decode_attention(case["q"], k_host, v_host, tables, lens, case["scale"], seqs=[s])
+        tokens += int(lens[s])
+        done += 1
+    dt = time.perf_counter() - t0
+    return {"value": round(tokens * per_token / dt / 1e9, 6), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"float64 oracle, {done} sequence decodes cycling through the {len(lens)}-sequence batch "
+                      f"({tokens} context tokens, {dt:.1f} s on one host core)",
+            "seconds": round(dt, 3), "seqs_per_s": round(done / dt, 3)}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="c3", choices=sorted(WORKLOADS))
+    ap.add_argument("--partition", type=int, default=None, help="tokens per split-K partition")
+    ap.add_argument("--replicas", type=int, default=None)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode-only", action="store_true", help="time only pa_decode launches (profiling aid)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the path is single-GPU; see the sharding notes in the design document)", file=sys.stderr)
+        return 2
+
+    import torch
+    import paged_kv_cache_115_amd as pk
+
+    torch.cuda.set_device(0)
+    name = args.config
+    partition = DEFAULT_PARTITION[name] if args.partition is None else args.partition
+    case = synth.decode_case(name)
+    cfg = case["cfg"]
+    S, hq, hkv, d, B = len(case["lengths"]), cfg["num_q_heads"], cfg["num_kv_heads"], cfg["head_dim"], cfg["block_size"]
+    lens_np = case["lengths"]
+    nb = case["num_blocks"]
+
+    # Host block manager: prefill L-1 tokens, then this step's append.
+    bm = pk.BlockManager(nb, B, case["free_order"])
+    for s in range(S):
+        bm.append(s, int(lens_np[s]) - 1)
+    seqs = np.arange(S)
+    t0 = time.perf_counter()
+    slots, cows = bm.append_step(seqs)
+    host_append_us = (time.perf_counter() - t0) * 1e6
+    maxb = int(max(-(-int(L) // B) for L in lens_np))
+    tables, lens = bm.export(seqs, maxb)
+    t0 = time.perf_counter()
+    plan = pk.decode_plan(lens, partition)
+    host_plan_us = (time.perf_counter() - t0) * 1e6
+
+    dev = torch.device("cuda", 0)
+    tables_d = torch.from_numpy(tables).to(dev)
+    lens_d = torch.from_numpy(lens).to(dev)
+    items_d = torch.from_numpy(plan.items).to(dev)
+    slots_d = torch.from_numpy(slots).to(dev)
+    cows_d = torch.from_numpy(np.ascontiguousarray(cows, dtype=np.int32)).to(dev)
+    ws_bytes = pk.decode_workspace_bytes(plan.num_partials, hq, d)
+    ws = torch.empty(max(ws_bytes, 256) // 4, dtype=torch.float32, device=dev)
+    q_d = torch.from_numpy(case["q"].view(np.int16)).view(torch.bfloat16).to(dev)
+
+    pool_bytes = 2 * nb * B * hkv * d * 2
+    R = args.replicas or max(2, math.ceil(2**30 / pool_bytes))
+    pools = []
+    for r in range(R):
+        g = torch.Generator(device=dev)
+        g.manual_seed(cfg["seed"] + 1000 * r)
+        kp = torch.randn((nb, B, hkv, d), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        vp = torch.randn((nb, B, hkv, d), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        pools.append(pk.KvPool(kp, vp))
+    g = torch.Generator(device=dev)
+    g.manual_seed(cfg["seed"] + 7)
+    new_k = torch.randn((S, hkv, d), generator=g, device=dev).to(torch.bfloat16)
+    new_v = torch.randn((S, hkv, d), generator=g, device=dev).to(torch.bfloat16)
+    out = torch.empty((S, hq, d), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(r: int, ev=None):
+        pool = pools[r]
+        if not args.decode_only:
+            pk.copy_blocks(pool, cows_d, stream)
+            pk.reshape_and_cache(pool, new_k, new_v, slots_d, stream)
+        if ev is not None:
+            ev[0].record(stream)
+        pk.decode(pool, q_d, tables_d, lens_d, case["scale"], plan, items_d, ws, out, stream)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for k in range(args.warmup):
+        step(k % R)
+    torch.cuda.synchronize()
+
+    # Timed region: K whole steps, bracketed by synchronisation.
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for k in range(args.steps):
+        step(k % R)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = start.elapsed_time(end) / args.steps
+
+    # Same steps again with an event pair around every decode launch.
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for k in range(args.steps):
+        step(k % R, evs[k])
+    torch.cuda.synchronize()
+    dec_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    decode_us = float(dec_ms.mean() * 1e3)
+
+    kv_bytes = int(lens.astype(np.int64).sum()) * hkv * d * 2 * 2
+    value = kv_bytes / (ms_per_step * 1e-3) / 1e9
+    achieved = kv_bytes / (decode_us * 1e-6) / 1e9
+    traffic = measured_traffic(name, partition)
+    result = {
+        "metric": "paged decode attention KV-read GB/s (% of HBM peak) and decode tokens/s, 1 GPU",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{name}: {WORKLOADS[name]}", "num_seqs": S, "num_q_heads": hq,
+                   "num_kv_heads": hkv, "head_dim": d, "block_size": B, "partition_size": partition,
+                   "total_context_tokens": int(lens.sum()), "max_context": int(lens.max()),
+                   "pool_replicas": R, "decode_only": bool(args.decode_only)},
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "decode_tokens_per_s": round(S / (ms_per_step * 1e-3), 1),
+        "kv_bytes_per_step": kv_bytes,
+        "decode_kernel_us": round(decode_us, 3),
+        "decode_kernel_us_p10_p90": [round(float(np.percentile(dec_ms, 10)) * 1e3, 3),
+                                     round(float(np.percentile(dec_ms, 90)) * 1e3, 3)],
+        "host_append_us": round(host_append_us, 2),
+        "host_plan_us": round(host_plan_us, 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": "decode_bf16_kernel<16>", "bytes_per_launch": kv_bytes},
+    }
+    if not args.no_cpu_baseline:
+        k_host = pools[0].k.cpu().view(torch.int16).numpy().view(np.uint16)
+        v_host = pools[0].v.cpu().view(torch.int16).numpy().view(np.uint16)
+        result["cpu_baseline"] = cpu_baseline(case, k_host, v_host, tables, lens, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

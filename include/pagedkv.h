@@ -1,0 +1,268 @@
+/*
+ * pagedkv.h - C ABI of libpagedkv: decode attention over a paged KV cache on
+ * AMD Instinct MI355X (gfx950), plus the host-side block manager that hands
+ * out the cache's blocks.
+ *
+ * The method (PagedAttention's memory layout):
+ *   - the KV cache is one preallocated pool of fixed-size blocks of B token
+ *     slots, keys and values in separate pools of identical shape
+ *     [num_blocks][B][num_kv_heads][head_dim]
+ *     (aicassindra.com "tm_paged_attention_deep", "Anatomy of a KV block";
+ *      llminference.xinbetween.com S06 "PagedAttention", "Implementation");
+ *   - each sequence owns a block table mapping logical block t / B to a
+ *     physical block; token t lives at flat slot table[t / B] * B + t % B
+ *     (synapticradio.com "The KV Cache Is an Allocator Problem", equation in
+ *      "What the trace shows");
+ *   - blocks come from a free list on demand, carry reference counts so that
+ *     sequences can share a prefix, and are copied on the first write into a
+ *     shared block (mercemay.com "Paged KV Cache Allocation and the Block
+ *     Table", "Blocks, tables, and the indirection" and "Sharing blocks
+ *     between sequences");
+ *   - the attention kernel walks the table itself instead of gathering blocks
+ *     into a contiguous copy first (S06 "Why this needed a custom CUDA kernel";
+ *     mercemay.com "What the design costs").
+ *
+ * Conventions for every GPU entry point:
+ *   - all array arguments are DEVICE pointers owned by the caller; the
+ *     library never allocates device memory and never synchronizes;
+ *   - work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
+ *     and calls on one stream run in call order;
+ *   - arguments the host can check (null pointers, sizes, dtypes, alignment)
+ *     are checked before anything is enqueued; on failure nothing is launched
+ *     and a message is left for pa_last_error();
+ *   - contents of device arrays (slot values, table entries, lengths) are
+ *     preconditions, stated per call; the kernels never read outside the
+ *     arrays when the preconditions hold;
+ *   - launch failures return PA_ERR_HIP.
+ * Supported shapes: dtype F32 or BF16; head_dim 64 or 128 for F32, 128 for
+ * BF16; block_size 8, 16 or 32; num_q_heads a multiple of num_kv_heads with
+ * a group of at most 16 query heads per KV head.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_INVALID = -1,     /* bad argument (null, size, alignment, precondition seen on host) */
+  PA_ERR_UNSUPPORTED = -2, /* valid but not implemented (dtype, head_dim, block size, group) */
+  PA_ERR_OOM = -3,         /* block manager: not enough free blocks; state unchanged */
+  PA_ERR_NOT_FOUND = -4,   /* block manager: unknown sequence */
+  PA_ERR_HIP = -5          /* a HIP runtime call failed */
+} pa_status;
+
+typedef enum { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
+
+/* One layer's KV pool.  k and v each hold num_blocks * block_size *
+ * num_kv_heads * head_dim elements of `dtype`, contiguous, in the order
+ * [block][slot][kv_head][dim], 16-byte aligned.  Owned by the caller. */
+typedef struct pa_kv_pool {
+  void* k;
+  void* v;
+  int32_t num_blocks;
+  int32_t block_size;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t dtype; /* pa_dtype */
+} pa_kv_pool;
+
+/* Message describing the last non-OK status returned on this thread. */
+const char* pa_last_error(void);
+
+/* ---------------------------------------------------------------------------
+ * pa_reshape_and_cache - write new tokens' keys and values into their slots.
+ *
+ * The device half of the append step: pool slot slot_mapping[i] receives
+ * key[i] and value[i] (mercemay.com "Blocks, tables, and the indirection",
+ * the append listing's cache write at physical * block_size + slot).
+ *   key, value   : device, [num_tokens][num_kv_heads][head_dim] of pool dtype,
+ *                  contiguous, 16-byte aligned.
+ *   slot_mapping : device int64 [num_tokens]; flat slot = block * B + offset.
+ *                  A negative slot skips that token (padding).
+ * Preconditions: every non-negative slot < num_blocks * block_size; no slot
+ * repeats within one call.  The copy is bit-exact.  num_tokens == 0 is a
+ * no-op.
+ * ------------------------------------------------------------------------- */
+pa_status pa_reshape_and_cache(const pa_kv_pool* pool, const void* key, const void* value,
+                               const int64_t* slot_mapping, int32_t num_tokens, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * pa_copy_blocks - copy-on-write duplication of whole blocks.
+ *
+ * For every pair p: block pairs[2p+1] of both pools becomes a bit-exact copy
+ * of block pairs[2p] (aicassindra.com "Copy-on-write for shared prefixes":
+ * the one block at the point of divergence is copied for the writer).
+ *   pairs : device int32 [num_pairs][2] = (src, dst).
+ * Preconditions: ids in [0, num_blocks); destinations distinct and never a
+ * source in the same call.  num_pairs == 0 is a no-op.
+ * ------------------------------------------------------------------------- */
+pa_status pa_copy_blocks(const pa_kv_pool* pool, const int32_t* pairs, int32_t num_pairs,
+                         void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Decode attention.
+ *
+ * For each sequence s with L = context_lens[s] tokens and each query head h,
+ * with KV head g = h / (num_q_heads / num_kv_heads):
+ *   out[s][h] = sum_t softmax_t(scale * <q[s][h], K_t[g]>) * V_t[g],
+ * where token t's K/V row is read through the block table
+ * (S06 "Implementation", the paged_attention excerpt; aicassindra.com
+ *  "The block table: logical to physical mapping").  L counts the token
+ * written this step; L == 0 yields zeros.
+ *
+ * Work is split into items (sequence, partition of `partition_size` tokens).
+ * A sequence longer than one partition leaves one (max, sum, accumulator)
+ * record per partition and query head in the workspace; a second launch on
+ * the same stream merges them by log-sum-exp in partition order.  The item
+ * list comes from pa_decode_plan on the host (which knows the lengths) and is
+ * uploaded by the caller with the other step inputs.
+ * ------------------------------------------------------------------------- */
+typedef struct pa_work_item {
+  int32_t seq;          /* sequence index */
+  int32_t part;         /* partition index within the sequence; -1 marks a merge item */
+  int32_t num_parts;    /* partitions of this sequence */
+  int32_t partial_base; /* first workspace record of this sequence, -1 if num_parts == 1 */
+} pa_work_item;
+
+/* pa_decode_plan - build the work list on the host.
+ *   context_lens   : HOST int32 [num_seqs], each >= 0.
+ *   partition_size : tokens per partition; a positive multiple of 16 and of
+ *                    the pool's block size, or 0 for one partition per
+ *                    sequence.
+ *   items          : HOST output of capacity `capacity`: first *num_items
+ *                    work items, one per partition (a sequence with L == 0
+ *                    gets one), largest first so that the longest work starts
+ *                    first; then *num_merges merge items, one per split
+ *                    sequence.
+ *   *num_partials  : workspace records needed (sum of num_parts over split
+ *                    sequences).
+ * Returns PA_ERR_INVALID if capacity is too small (the counts are still
+ * written, so the caller can size a second call). */
+pa_status pa_decode_plan(const int32_t* context_lens, int32_t num_seqs, int32_t partition_size,
+                         pa_work_item* items, int32_t capacity, int32_t* num_items,
+                         int32_t* num_merges, int32_t* num_partials);
+
+/* Bytes of device workspace pa_decode needs for `num_partials` records (0 when
+ * nothing is split).  The workspace needs no initialisation; it holds
+ * per-partition records between the two launches of one call, so two calls
+ * that may overlap in time (different streams) must not share one. */
+size_t pa_decode_workspace_bytes(int32_t num_partials, int32_t num_q_heads, int32_t head_dim);
+
+/* pa_decode - paged decode attention for one batch.
+ *   q            : device [num_seqs][num_q_heads][head_dim], pool dtype.
+ *   out          : device [num_seqs][num_q_heads][head_dim], out_dtype
+ *                  (PA_F32, or the pool dtype: rounded to nearest even).
+ *   block_tables : device int32 [num_seqs][max_blocks_per_seq]; entries past
+ *                  ceil(L / B) are never read.
+ *   context_lens : device int32 [num_seqs].
+ *   scale        : multiplies q.k before the softmax (1/sqrt(head_dim) for
+ *                  standard attention; S06 "Implementation").
+ *   items        : device copy of pa_decode_plan's output (num_items work
+ *                  items followed by num_merges merge items) for the same
+ *                  context lengths and partition_size.
+ *   workspace    : device, >= pa_decode_workspace_bytes(num_partials, ...),
+ *                  256-byte aligned; may be NULL when num_partials == 0.
+ * Preconditions: context_lens equal those given to pa_decode_plan; each
+ * L <= max_blocks_per_seq * B; the first ceil(L / B) table entries of each
+ * sequence are in [0, num_blocks).  Results are deterministic: the order of
+ * every floating-point reduction depends only on logical token positions,
+ * never on physical block ids or on scheduling. */
+pa_status pa_decode(const pa_kv_pool* pool, const void* q, void* out, int32_t out_dtype,
+                    const int32_t* block_tables, int32_t max_blocks_per_seq,
+                    const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                    float scale, const pa_work_item* items, int32_t num_items,
+                    int32_t num_merges, int32_t num_partials, int32_t partition_size,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Host block manager (plain C++ on the CPU; not thread-safe: one scheduler
+ * thread owns an instance).  Tracks per-sequence block tables and lengths,
+ * per-block reference counts and one free list
+ * (S06 "The solution", the BlockManager listing; mercemay.com "Sharing
+ *  blocks between sequences").
+ *
+ * Free list: blocks leave in `initial_order` (initial_order[0] first; NULL =
+ * ascending ids, as the S06 simulator's tables show); a retired block goes
+ * back on top and is the next one handed out.
+ * ------------------------------------------------------------------------- */
+typedef struct pa_bm pa_bm;
+
+typedef struct pa_bm_stats {
+  int32_t num_blocks;
+  int32_t free_blocks;
+  int32_t used_blocks;
+  int32_t num_seqs;
+  int64_t logical_tokens; /* sum of sequence lengths (shared tokens count per sharer) */
+  int32_t shared_blocks;  /* blocks named by more than one table */
+  int32_t pad_;
+  int64_t alloc_failures; /* appends refused for lack of blocks */
+  int64_t cow_copies;     /* copy-on-write pairs issued */
+} pa_bm_stats;
+
+/* Returns NULL on bad sizes or if initial_order is not a permutation of
+ * [0, num_blocks) (message in pa_last_error). */
+pa_bm* pa_bm_create(int32_t num_blocks, int32_t block_size, const int32_t* initial_order);
+void pa_bm_destroy(pa_bm* bm);
+
+/* Append n_new tokens to `seq` (created on first use, S06 listing's
+ * setdefault).  A block is taken whenever the length is a multiple of B
+ * before a write (mercemay.com append listing).  If the first write lands in
+ * a partly filled block that another table also names, that block is first
+ * copied to a fresh block: the pair (src, dst) is reported, the table points
+ * at dst and src's count drops by one (copy-on-write).  The caller must run
+ * pa_copy_blocks on reported pairs before writing the new tokens.
+ *   slots_out     : HOST int64 [n_new], flat slot of each new token.
+ *   cow_pairs_out : HOST int32 [2] (at most one pair per call), may be NULL
+ *                   only if the caller knows no copy can occur.
+ *   *n_cow_out    : pairs written (0 or 1).
+ * All or nothing: PA_ERR_OOM leaves every table, count and list unchanged. */
+pa_status pa_bm_append(pa_bm* bm, int64_t seq, int32_t n_new, int64_t* slots_out,
+                       int32_t* cow_pairs_out, int32_t* n_cow_out);
+
+/* One token for each of `num` distinct sequences, in the given order - a
+ * decode step.  slots_out: HOST int64 [num]; cow_pairs_out: HOST int32
+ * [2*num]; *n_cow_out pairs written.  All or nothing across the whole step. */
+pa_status pa_bm_append_step(pa_bm* bm, const int64_t* seqs, int32_t num, int64_t* slots_out,
+                            int32_t* cow_pairs_out, int32_t* n_cow_out);
+
+/* child gets a copy of parent's table and length; each named block's count
+ * rises by one (prefix sharing).  PA_ERR_NOT_FOUND if parent is unknown,
+ * PA_ERR_INVALID if child exists. */
+pa_status pa_bm_fork(pa_bm* bm, int64_t parent, int64_t child);
+
+/* Retire `seq`: every block in its table loses one count; those reaching zero
+ * return to the free list in table order (mercemay.com: the free list never
+ * receives a block another table still names).  Unknown seq: PA_OK, no-op. */
+pa_status pa_bm_free(pa_bm* bm, int64_t seq);
+
+/* Table length ceil(L / B) of `seq` (-1 if unknown); copies min(that, cap)
+ * entries to HOST `out` (may be NULL when cap == 0). */
+int32_t pa_bm_table(const pa_bm* bm, int64_t seq, int32_t* out, int32_t cap);
+
+/* Dense upload arrays for a batch: tables_out HOST int32 [num][max_blocks]
+ * (unused entries 0), lens_out HOST int32 [num].  PA_ERR_NOT_FOUND for an
+ * unknown sequence, PA_ERR_INVALID if a table exceeds max_blocks. */
+pa_status pa_bm_export(const pa_bm* bm, const int64_t* seqs, int32_t num, int32_t max_blocks,
+                       int32_t* tables_out, int32_t* lens_out);
+
+int32_t pa_bm_len(const pa_bm* bm, int64_t seq);         /* -1 if unknown */
+int32_t pa_bm_refcount(const pa_bm* bm, int32_t block);  /* -1 if out of range */
+void pa_bm_get_stats(const pa_bm* bm, pa_bm_stats* out);
+
+/* Verify that each block's count equals the number of tables naming it, that
+ * no named block is on the free list, that no block is lost, and that every
+ * table holds ceil(L / B) entries (S06 "Reference counts must be exact").
+ * PA_OK or PA_ERR_INVALID with the first violation in pa_last_error. */
+pa_status pa_bm_check(const pa_bm* bm);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

@@ -1,0 +1,242 @@
+"""paged_kv_cache_115_amd: paged-KV-cache decode attention for MI355X.
+
+Thin Python binding over libpagedkv.so (C ABI declared in include/pagedkv.h).
+Every computation runs in the library: this module only marshals torch
+tensors (device memory) and numpy arrays (host memory) into pointers and
+sizes.  Importing it loads the library and fails loudly when it has not been
+built (python -m paged_kv_cache_115_amd.build).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+from ._lib import LIB_PATH, PA_BF16, PA_F32, PaError, PaKvPool, PaWorkItem, lib
+
+__all__ = [
+    "LIB_PATH", "PA_F32", "PA_BF16", "PaError", "BlockManager", "KvPool",
+    "reshape_and_cache", "copy_blocks", "decode_plan", "decode_workspace_bytes",
+    "decode", "DecodePlan",
+]
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        msg = lib.pa_last_error().decode(errors="replace")
+        raise PaError(status, f"{what}: {msg}")
+
+
+def _ptr(t) -> ctypes.c_void_p:
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return PA_F32
+    if t.dtype == torch.bfloat16:
+        return PA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+class KvPool:
+    """One layer's K and V pools: caller-owned device tensors [NB, B, Hkv, D]."""
+
+    def __init__(self, k, v):
+        if k.shape != v.shape or k.dtype != v.dtype or k.dim() != 4:
+            raise ValueError("k and v pools must share a 4-D shape and dtype")
+        if not (k.is_cuda and v.is_cuda and k.is_contiguous() and v.is_contiguous()):
+            raise ValueError("pools must be contiguous device tensors")
+        self.k, self.v = k, v
+        nb, b, hkv, d = k.shape
+        self.c = PaKvPool(_ptr(k), _ptr(v), nb, b, hkv, d, _dtype_code(k))
+
+    @property
+    def block_size(self) -> int:
+        return self.c.block_size
+
+
+def _dev(t, name, dtype=None):
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous device tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t
+
+
+def reshape_and_cache(pool: KvPool, key, value, slot_mapping, stream=None) -> None:
+    """pa_reshape_and_cache: write key[i]/value[i] at flat slot slot_mapping[i]."""
+    import torch
+    _dev(key, "key", pool.k.dtype)
+    _dev(value, "value", pool.k.dtype)
+    _dev(slot_mapping, "slot_mapping", torch.int64)
+    n = slot_mapping.numel()
+    if key.shape[0] != n or value.shape[0] != n or tuple(key.shape[1:]) != tuple(pool.k.shape[2:]):
+        raise ValueError("key/value must be [num_tokens, Hkv, D] matching slot_mapping")
+    _check(lib.pa_reshape_and_cache(ctypes.byref(pool.c), _ptr(key), _ptr(value), _ptr(slot_mapping),
+                                    n, _stream(stream)), "pa_reshape_and_cache")
+
+
+def copy_blocks(pool: KvPool, pairs, stream=None) -> None:
+    """pa_copy_blocks: for each (src, dst) row of int32 device `pairs`, dst := src."""
+    import torch
+    _dev(pairs, "pairs", torch.int32)
+    n = pairs.numel() // 2
+    _check(lib.pa_copy_blocks(ctypes.byref(pool.c), _ptr(pairs) if n else None, n, _stream(stream)),
+           "pa_copy_blocks")
+
+
+class DecodePlan:
+    """Host-built work list for one batch (pa_decode_plan): `items` holds
+    num_items work items followed by num_merges merge items."""
+
+    def __init__(self, items: np.ndarray, num_items: int, num_merges: int, num_partials: int,
+                 partition_size: int):
+        self.items = items                  # int32 [num_items + num_merges, 4]
+        self.num_items = num_items
+        self.num_merges = num_merges
+        self.num_partials = num_partials
+        self.partition_size = partition_size
+
+
+def decode_plan(context_lens, partition_size: int) -> DecodePlan:
+    lens = np.ascontiguousarray(context_lens, dtype=np.int32)
+    n_items, n_merge, n_part = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_int32(0)
+    cap = 1
+    for _ in range(2):
+        items = np.zeros((cap, 4), dtype=np.int32)
+        st = lib.pa_decode_plan(lens.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), lens.size, partition_size,
+                                items.ctypes.data_as(ctypes.POINTER(PaWorkItem)), cap, ctypes.byref(n_items),
+                                ctypes.byref(n_merge), ctypes.byref(n_part))
+        need = n_items.value + n_merge.value
+        if st == 0 or need <= cap:
+            break
+        cap = need
+    _check(st, "pa_decode_plan")
+    return DecodePlan(items[:need].copy(), n_items.value, n_merge.value, n_part.value, partition_size)
+
+
+def decode_workspace_bytes(num_partials: int, num_q_heads: int, head_dim: int) -> int:
+    return int(lib.pa_decode_workspace_bytes(num_partials, num_q_heads, head_dim))
+
+
+def decode(pool: KvPool, q, block_tables, context_lens, scale: float, plan: DecodePlan, items, workspace=None,
+           out=None, stream=None):
+    """pa_decode.  `items` is the device int32 copy of plan.items."""
+    import torch
+    _dev(q, "q", pool.k.dtype)
+    _dev(block_tables, "block_tables", torch.int32)
+    _dev(context_lens, "context_lens", torch.int32)
+    _dev(items, "items", torch.int32)
+    if items.shape[0] < plan.num_items + plan.num_merges:
+        raise ValueError("items holds fewer entries than the plan")
+    s, hq, d = q.shape
+    if out is None:
+        out = torch.empty((s, hq, d), dtype=torch.float32, device=q.device)
+    _dev(out, "out")
+    if tuple(out.shape) != (s, hq, d):
+        raise ValueError("out must be [S, Hq, D]")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.pa_decode(ctypes.byref(pool.c), _ptr(q), _ptr(out), _dtype_code(out), _ptr(block_tables),
+                         block_tables.shape[1], _ptr(context_lens), s, hq, ctypes.c_float(scale),
+                         _ptr(items), plan.num_items, plan.num_merges, plan.num_partials, plan.partition_size,
+                         None if workspace is None else _ptr(workspace), ws_bytes, _stream(stream)),
+           "pa_decode")
+    return out
+
+
+class BlockManager:
+    """Host block manager (pa_bm_*): free list, tables, counts, copy-on-write."""
+
+    def __init__(self, num_blocks: int, block_size: int, initial_order=None):
+        order = None
+        if initial_order is not None:
+            order = np.ascontiguousarray(initial_order, dtype=np.int32)
+            if order.size != num_blocks:
+                raise ValueError("initial_order must list every block once")
+        self._order = order
+        ptr = None if order is None else order.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+        self._h = lib.pa_bm_create(num_blocks, block_size, ptr)
+        if not self._h:
+            raise PaError(-1, "pa_bm_create: " + lib.pa_last_error().decode())
+        self.num_blocks = num_blocks
+        self.block_size = block_size
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h:
+            lib.pa_bm_destroy(h)
+            self._h = None
+
+    def append(self, seq: int, n_new: int = 1):
+        """Returns (slots int64[n_new], cow pairs int32[k, 2])."""
+        slots = np.zeros(max(n_new, 1), dtype=np.int64)
+        cow = np.zeros(2, dtype=np.int32)
+        n_cow = ctypes.c_int32(0)
+        _check(lib.pa_bm_append(self._h, seq, n_new, slots.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                cow.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), ctypes.byref(n_cow)),
+               "pa_bm_append")
+        return slots[:n_new], cow[: 2 * n_cow.value].reshape(-1, 2)
+
+    def append_step(self, seqs):
+        seqs = np.ascontiguousarray(seqs, dtype=np.int64)
+        n = seqs.size
+        slots = np.zeros(max(n, 1), dtype=np.int64)
+        cow = np.zeros(max(2 * n, 2), dtype=np.int32)
+        n_cow = ctypes.c_int32(0)
+        _check(lib.pa_bm_append_step(self._h, seqs.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), n,
+                                     slots.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                     cow.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), ctypes.byref(n_cow)),
+               "pa_bm_append_step")
+        return slots[:n], cow[: 2 * n_cow.value].reshape(-1, 2)
+
+    def fork(self, parent: int, child: int) -> None:
+        _check(lib.pa_bm_fork(self._h, parent, child), "pa_bm_fork")
+
+    def free(self, seq: int) -> None:
+        _check(lib.pa_bm_free(self._h, seq), "pa_bm_free")
+
+    def table(self, seq: int) -> np.ndarray:
+        n = lib.pa_bm_table(self._h, seq, None, 0)
+        if n < 0:
+            raise KeyError(seq)
+        out = np.zeros(max(n, 1), dtype=np.int32)
+        lib.pa_bm_table(self._h, seq, out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), n)
+        return out[:n]
+
+    def export(self, seqs, max_blocks: int):
+        """Dense (tables int32[n, max_blocks], lens int32[n]) for upload."""
+        seqs = np.ascontiguousarray(seqs, dtype=np.int64)
+        tables = np.zeros((seqs.size, max(max_blocks, 1)), dtype=np.int32)
+        lens = np.zeros(seqs.size, dtype=np.int32)
+        _check(lib.pa_bm_export(self._h, seqs.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), seqs.size,
+                                max_blocks, tables.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                lens.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))), "pa_bm_export")
+        return tables[:, :max_blocks] if max_blocks else tables[:, :0], lens
+
+    def length(self, seq: int) -> int:
+        n = lib.pa_bm_len(self._h, seq)
+        if n < 0:
+            raise KeyError(seq)
+        return n
+
+    def refcount(self, block: int) -> int:
+        return lib.pa_bm_refcount(self._h, block)
+
+    def stats(self) -> dict:
+        from ._lib import PaBmStats
+        st = PaBmStats()
+        lib.pa_bm_get_stats(self._h, ctypes.byref(st))
+        return {name: getattr(st, name) for name, _ in PaBmStats._fields_ if not name.endswith("_")}
+
+    def check(self) -> None:
+        _check(lib.pa_bm_check(self._h), "pa_bm_check")

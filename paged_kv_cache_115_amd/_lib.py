@@ -1,0 +1,78 @@
+"""ctypes declarations for libpagedkv.so (mirrors include/pagedkv.h)."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedkv.so")
+
+PA_F32 = 0
+PA_BF16 = 1
+
+
+class PaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+class PaKvPool(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("num_blocks", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class PaWorkItem(ctypes.Structure):
+    _fields_ = [("seq", ctypes.c_int32), ("part", ctypes.c_int32), ("num_parts", ctypes.c_int32),
+                ("partial_base", ctypes.c_int32)]
+
+
+class PaBmStats(ctypes.Structure):
+    _fields_ = [("num_blocks", ctypes.c_int32), ("free_blocks", ctypes.c_int32),
+                ("used_blocks", ctypes.c_int32), ("num_seqs", ctypes.c_int32),
+                ("logical_tokens", ctypes.c_int64), ("shared_blocks", ctypes.c_int32),
+                ("pad_", ctypes.c_int32), ("alloc_failures", ctypes.c_int64),
+                ("cow_copies", ctypes.c_int64)]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m paged_kv_cache_115_amd.build` "
+                          "(there is no fallback implementation)")
+    return ctypes.CDLL(LIB_PATH)
+
+
+lib = _load()
+
+_i32, _i64, _vp, _sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
+_p32 = ctypes.POINTER(ctypes.c_int32)
+_p64 = ctypes.POINTER(ctypes.c_int64)
+_pool = ctypes.POINTER(PaKvPool)
+
+# name: (restype, argtypes)
+SIGNATURES = {
+    "pa_last_error": (ctypes.c_char_p, []),
+    "pa_reshape_and_cache": (_i32, [_pool, _vp, _vp, _vp, _i32, _vp]),
+    "pa_copy_blocks": (_i32, [_pool, _vp, _i32, _vp]),
+    "pa_decode_plan": (_i32, [_p32, _i32, _i32, ctypes.POINTER(PaWorkItem), _i32, _p32, _p32, _p32]),
+    "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32]),
+    "pa_decode": (_i32, [_pool, _vp, _vp, _i32, _vp, _i32, _vp, _i32, _i32, ctypes.c_float, _vp, _i32, _i32,
+                         _i32, _i32, _vp, _sz, _vp]),
+    "pa_bm_create": (_vp, [_i32, _i32, _p32]),
+    "pa_bm_destroy": (None, [_vp]),
+    "pa_bm_append": (_i32, [_vp, _i64, _i32, _p64, _p32, _p32]),
+    "pa_bm_append_step": (_i32, [_vp, _p64, _i32, _p64, _p32, _p32]),
+    "pa_bm_fork": (_i32, [_vp, _i64, _i64]),
+    "pa_bm_free": (_i32, [_vp, _i64]),
+    "pa_bm_table": (_i32, [_vp, _i64, _p32, _i32]),
+    "pa_bm_export": (_i32, [_vp, _p64, _i32, _i32, _p32, _p32]),
+    "pa_bm_len": (_i32, [_vp, _i64]),
+    "pa_bm_refcount": (_i32, [_vp, _i32]),
+    "pa_bm_get_stats": (None, [_vp, ctypes.POINTER(PaBmStats)]),
+    "pa_bm_check": (_i32, [_vp]),
+}
+
+for _name, (_res, _args) in SIGNATURES.items():
+    _f = getattr(lib, _name)
+    _f.restype = _res
+    _f.argtypes = _args

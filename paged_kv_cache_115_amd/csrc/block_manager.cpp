@@ -1,0 +1,281 @@
+// Host block manager: free list, per-sequence block tables, reference counts
+// and copy-on-write for shared prefixes.  Plain C++ on the CPU.
+//
+// Behaviour (pages):
+//  - blocks leave one global free list on demand; any free block fits any
+//    request (llminference.xinbetween.com S06 "PagedAttention", "The
+//    solution"); a retired block is reused first;
+//  - a sequence takes a new block whenever its length is a multiple of B
+//    before a write; the slot of position t is table[t/B]*B + t%B
+//    (mercemay.com "Paged KV Cache Allocation and the Block Table", "Blocks,
+//    tables, and the indirection"; synapticradio.com "The KV Cache Is an
+//    Allocator Problem", equation in "What the trace shows");
+//  - counts per block; fork aliases a table; retiring decrements and frees
+//    only blocks reaching zero; the first write into a shared, partly filled
+//    block copies it (mercemay.com "Sharing blocks between sequences";
+//    aicassindra.com "tm_paged_attention_deep", "Copy-on-write for shared
+//    prefixes").
+// Appends are all-or-nothing: a request that does not fit changes nothing.
+#include <algorithm>
+#include <cstring>
+#include <map>
+#include <new>
+#include <unordered_map>
+#include <vector>
+
+#include "internal.h"
+
+using pagedkv::fail;
+
+struct pa_bm {
+  struct Seq {
+    std::vector<int32_t> table;
+    int32_t len = 0;
+  };
+  int32_t num_blocks = 0;
+  int32_t block_size = 0;
+  std::vector<int32_t> free_stack;  // back() is handed out next
+  std::vector<int32_t> refcount;
+  std::map<int64_t, Seq> seqs;      // ordered: deterministic checks and stats
+  int64_t alloc_failures = 0;
+  int64_t cow_copies = 0;
+
+  int32_t pop() {
+    int32_t b = free_stack.back();
+    free_stack.pop_back();
+    refcount[b] = 1;
+    return b;
+  }
+
+  // Free blocks that appending n_new tokens to (len, table) would consume.
+  // `delta` carries count decrements from earlier sequences of the same step
+  // so that a block shared by several writers is copied by all but the last.
+  int64_t needs(const Seq* s, int32_t n_new, std::unordered_map<int32_t, int32_t>& delta) const {
+    const int64_t len = s ? s->len : 0;
+    const int64_t have = s ? (int64_t)s->table.size() : 0;
+    int64_t need = (len + n_new + block_size - 1) / block_size - have;
+    if (n_new > 0 && s && len % block_size != 0) {
+      const int32_t last = s->table.back();
+      auto it = delta.find(last);
+      const int32_t d = it == delta.end() ? 0 : it->second;
+      if (refcount[last] + d > 1) {
+        need += 1;
+        delta[last] = d - 1;
+      }
+    }
+    return need;
+  }
+
+  // Append without a capacity check; writes slots and at most one CoW pair.
+  void append_unchecked(int64_t id, int32_t n_new, int64_t* slots, int32_t* cow, int32_t* n_cow) {
+    Seq& s = seqs[id];
+    const int32_t B = block_size;
+    if (n_new > 0 && s.len % B != 0 && refcount[s.table.back()] > 1) {
+      const int32_t src = s.table.back();
+      const int32_t dst = pop();
+      refcount[src] -= 1;
+      s.table.back() = dst;
+      cow[2 * *n_cow] = src;
+      cow[2 * *n_cow + 1] = dst;
+      *n_cow += 1;
+      cow_copies += 1;
+    }
+    for (int32_t i = 0; i < n_new; ++i) {
+      const int64_t t = (int64_t)s.len + i;
+      if (t % B == 0) s.table.push_back(pop());
+      slots[i] = (int64_t)s.table[t / B] * B + t % B;
+    }
+    s.len += n_new;
+  }
+};
+
+extern "C" pa_bm* pa_bm_create(int32_t num_blocks, int32_t block_size, const int32_t* initial_order) {
+  if (num_blocks <= 0 || block_size <= 0) {
+    fail(PA_ERR_INVALID, "pa_bm_create: num_blocks=%d block_size=%d must be positive", num_blocks,
+         block_size);
+    return nullptr;
+  }
+  pa_bm* bm = new (std::nothrow) pa_bm();
+  if (!bm) {
+    fail(PA_ERR_INVALID, "pa_bm_create: host allocation failed");
+    return nullptr;
+  }
+  bm->num_blocks = num_blocks;
+  bm->block_size = block_size;
+  bm->refcount.assign(num_blocks, 0);
+  bm->free_stack.resize(num_blocks);
+  if (initial_order) {
+    std::vector<char> seen(num_blocks, 0);
+    for (int32_t i = 0; i < num_blocks; ++i) {
+      const int32_t b = initial_order[i];
+      if (b < 0 || b >= num_blocks || seen[b]) {
+        delete bm;
+        fail(PA_ERR_INVALID, "pa_bm_create: initial_order is not a permutation (entry %d = %d)", i, b);
+        return nullptr;
+      }
+      seen[b] = 1;
+      bm->free_stack[num_blocks - 1 - i] = b;
+    }
+  } else {
+    for (int32_t i = 0; i < num_blocks; ++i) bm->free_stack[num_blocks - 1 - i] = i;
+  }
+  return bm;
+}
+
+extern "C" void pa_bm_destroy(pa_bm* bm) { delete bm; }
+
+extern "C" pa_status pa_bm_append(pa_bm* bm, int64_t seq, int32_t n_new, int64_t* slots_out,
+                                  int32_t* cow_pairs_out, int32_t* n_cow_out) {
+  if (!bm || n_new < 0 || (n_new > 0 && !slots_out) || !n_cow_out)
+    return fail(PA_ERR_INVALID, "pa_bm_append: bad arguments");
+  *n_cow_out = 0;
+  auto it = bm->seqs.find(seq);
+  const pa_bm::Seq* s = it == bm->seqs.end() ? nullptr : &it->second;
+  std::unordered_map<int32_t, int32_t> delta;
+  const int64_t need = bm->needs(s, n_new, delta);
+  if (!delta.empty() && !cow_pairs_out)
+    return fail(PA_ERR_INVALID, "pa_bm_append: a copy-on-write pair is due but cow_pairs_out is NULL");
+  if (need > (int64_t)bm->free_stack.size()) {
+    bm->alloc_failures += 1;
+    return fail(PA_ERR_OOM, "pa_bm_append: sequence %lld needs %lld blocks, %zu free", (long long)seq,
+                (long long)need, bm->free_stack.size());
+  }
+  int32_t dummy[2];
+  bm->append_unchecked(seq, n_new, slots_out, cow_pairs_out ? cow_pairs_out : dummy, n_cow_out);
+  return PA_OK;
+}
+
+extern "C" pa_status pa_bm_append_step(pa_bm* bm, const int64_t* seqs, int32_t num, int64_t* slots_out,
+                                       int32_t* cow_pairs_out, int32_t* n_cow_out) {
+  if (!bm || num < 0 || (num > 0 && (!seqs || !slots_out || !cow_pairs_out)) || !n_cow_out)
+    return fail(PA_ERR_INVALID, "pa_bm_append_step: bad arguments");
+  *n_cow_out = 0;
+  std::vector<int64_t> sorted(seqs, seqs + num);
+  std::sort(sorted.begin(), sorted.end());
+  if (std::adjacent_find(sorted.begin(), sorted.end()) != sorted.end())
+    return fail(PA_ERR_INVALID, "pa_bm_append_step: a sequence is listed twice");
+  std::unordered_map<int32_t, int32_t> delta;
+  int64_t need = 0;
+  for (int32_t i = 0; i < num; ++i) {
+    auto it = bm->seqs.find(seqs[i]);
+    need += bm->needs(it == bm->seqs.end() ? nullptr : &it->second, 1, delta);
+  }
+  if (need > (int64_t)bm->free_stack.size()) {
+    bm->alloc_failures += 1;
+    return fail(PA_ERR_OOM, "pa_bm_append_step: step needs %lld blocks, %zu free", (long long)need,
+                bm->free_stack.size());
+  }
+  for (int32_t i = 0; i < num; ++i)
+    bm->append_unchecked(seqs[i], 1, slots_out + i, cow_pairs_out, n_cow_out);
+  return PA_OK;
+}
+
+extern "C" pa_status pa_bm_fork(pa_bm* bm, int64_t parent, int64_t child) {
+  if (!bm) return fail(PA_ERR_INVALID, "pa_bm_fork: null manager");
+  auto p = bm->seqs.find(parent);
+  if (p == bm->seqs.end()) return fail(PA_ERR_NOT_FOUND, "pa_bm_fork: unknown parent %lld", (long long)parent);
+  if (bm->seqs.count(child)) return fail(PA_ERR_INVALID, "pa_bm_fork: child %lld exists", (long long)child);
+  pa_bm::Seq copy = p->second;
+  for (int32_t b : copy.table) bm->refcount[b] += 1;
+  bm->seqs.emplace(child, std::move(copy));
+  return PA_OK;
+}
+
+extern "C" pa_status pa_bm_free(pa_bm* bm, int64_t seq) {
+  if (!bm) return fail(PA_ERR_INVALID, "pa_bm_free: null manager");
+  auto it = bm->seqs.find(seq);
+  if (it == bm->seqs.end()) return PA_OK;
+  for (int32_t b : it->second.table) {
+    if (--bm->refcount[b] == 0) bm->free_stack.push_back(b);
+  }
+  bm->seqs.erase(it);
+  return PA_OK;
+}
+
+extern "C" int32_t pa_bm_table(const pa_bm* bm, int64_t seq, int32_t* out, int32_t cap) {
+  if (!bm) return -1;
+  auto it = bm->seqs.find(seq);
+  if (it == bm->seqs.end()) return -1;
+  const auto& t = it->second.table;
+  const int32_t n = (int32_t)t.size();
+  if (out && cap > 0) std::memcpy(out, t.data(), sizeof(int32_t) * std::min(n, cap));
+  return n;
+}
+
+extern "C" pa_status pa_bm_export(const pa_bm* bm, const int64_t* seqs, int32_t num, int32_t max_blocks,
+                                  int32_t* tables_out, int32_t* lens_out) {
+  if (!bm || num < 0 || max_blocks < 0 || (num > 0 && (!seqs || !tables_out || !lens_out)))
+    return fail(PA_ERR_INVALID, "pa_bm_export: bad arguments");
+  for (int32_t i = 0; i < num; ++i) {
+    auto it = bm->seqs.find(seqs[i]);
+    if (it == bm->seqs.end())
+      return fail(PA_ERR_NOT_FOUND, "pa_bm_export: unknown sequence %lld", (long long)seqs[i]);
+    const auto& t = it->second.table;
+    if ((int64_t)t.size() > max_blocks)
+      return fail(PA_ERR_INVALID, "pa_bm_export: sequence %lld has %zu blocks > max_blocks %d",
+                  (long long)seqs[i], t.size(), max_blocks);
+  }
+  for (int32_t i = 0; i < num; ++i) {
+    const auto& s = bm->seqs.find(seqs[i])->second;
+    int32_t* row = tables_out + (int64_t)i * max_blocks;
+    std::fill(row, row + max_blocks, 0);
+    std::copy(s.table.begin(), s.table.end(), row);
+    lens_out[i] = s.len;
+  }
+  return PA_OK;
+}
+
+extern "C" int32_t pa_bm_len(const pa_bm* bm, int64_t seq) {
+  if (!bm) return -1;
+  auto it = bm->seqs.find(seq);
+  return it == bm->seqs.end() ? -1 : it->second.len;
+}
+
+extern "C" int32_t pa_bm_refcount(const pa_bm* bm, int32_t block) {
+  if (!bm || block < 0 || block >= bm->num_blocks) return -1;
+  return bm->refcount[block];
+}
+
+extern "C" void pa_bm_get_stats(const pa_bm* bm, pa_bm_stats* out) {
+  if (!bm || !out) return;
+  std::memset(out, 0, sizeof(*out));
+  out->num_blocks = bm->num_blocks;
+  out->free_blocks = (int32_t)bm->free_stack.size();
+  out->used_blocks = bm->num_blocks - out->free_blocks;
+  out->num_seqs = (int32_t)bm->seqs.size();
+  for (const auto& kv : bm->seqs) out->logical_tokens += kv.second.len;
+  for (int32_t c : bm->refcount) out->shared_blocks += c > 1;
+  out->alloc_failures = bm->alloc_failures;
+  out->cow_copies = bm->cow_copies;
+}
+
+extern "C" pa_status pa_bm_check(const pa_bm* bm) {
+  if (!bm) return fail(PA_ERR_INVALID, "pa_bm_check: null manager");
+  std::vector<int32_t> named(bm->num_blocks, 0);
+  for (const auto& kv : bm->seqs) {
+    const auto& s = kv.second;
+    const int64_t expect = ((int64_t)s.len + bm->block_size - 1) / bm->block_size;
+    if ((int64_t)s.table.size() != expect)
+      return fail(PA_ERR_INVALID, "pa_bm_check: sequence %lld length %d has %zu blocks, expected %lld",
+                  (long long)kv.first, s.len, s.table.size(), (long long)expect);
+    for (int32_t b : s.table) {
+      if (b < 0 || b >= bm->num_blocks)
+        return fail(PA_ERR_INVALID, "pa_bm_check: sequence %lld names block %d", (long long)kv.first, b);
+      named[b] += 1;
+    }
+  }
+  std::vector<char> is_free(bm->num_blocks, 0);
+  for (int32_t b : bm->free_stack) {
+    if (is_free[b]) return fail(PA_ERR_INVALID, "pa_bm_check: block %d is on the free list twice", b);
+    is_free[b] = 1;
+  }
+  for (int32_t b = 0; b < bm->num_blocks; ++b) {
+    if (named[b] != bm->refcount[b])
+      return fail(PA_ERR_INVALID, "pa_bm_check: block %d count %d but %d tables name it", b,
+                  bm->refcount[b], named[b]);
+    if ((named[b] == 0) != (is_free[b] != 0))
+      return fail(PA_ERR_INVALID, "pa_bm_check: block %d is %s", b,
+                  named[b] ? "named and free" : "neither named nor free (leaked)");
+  }
+  return PA_OK;
+}

@@ -1,0 +1,75 @@
+// Cache-writing kernels: the slot scatter of newly appended tokens and the
+// whole-block copy used for copy-on-write.  Both are pure byte moves in
+// 16-byte vector loads/stores; rows of one token (num_kv_heads * head_dim
+// elements) are contiguous in the pool, so each token is one coalesced run.
+#include <hip/hip_runtime.h>
+
+#include "launch.h"
+
+namespace pagedkv {
+namespace {
+
+constexpr int kThreads = 256;
+
+// Token i's key row and value row go to flat slot slots[i]
+// (mercemay.com "Paged KV Cache Allocation and the Block Table", the cache
+// write of the append listing).  One workgroup per token; threads [0, n)
+// move the key row, [n, 2n) the value row, n = row bytes / 16.
+__global__ __launch_bounds__(kThreads) void reshape_and_cache_kernel(
+    uint4* __restrict__ kpool, uint4* __restrict__ vpool, const uint4* __restrict__ key,
+    const uint4* __restrict__ value, const int64_t* __restrict__ slots, int64_t num_slots,
+    int32_t row_vec) {
+  const int64_t tok = blockIdx.x;
+  const int64_t slot = slots[tok];
+  if (slot < 0 || slot >= num_slots) return;  // padding, or out of the pool
+  for (int32_t c = threadIdx.x; c < 2 * row_vec; c += kThreads) {
+    const bool is_v = c >= row_vec;
+    const int32_t cc = is_v ? c - row_vec : c;
+    const uint4* src = is_v ? value : key;
+    uint4* dst = is_v ? vpool : kpool;
+    dst[slot * row_vec + cc] = src[tok * row_vec + cc];
+  }
+}
+
+// Block pairs[2p+1] of both pools becomes a copy of block pairs[2p]
+// (aicassindra.com "tm_paged_attention_deep", "Copy-on-write for shared
+// prefixes").  grid = (pairs, 2 pools, chunks of 4 KiB).
+__global__ __launch_bounds__(kThreads) void copy_blocks_kernel(
+    uint4* __restrict__ kpool, uint4* __restrict__ vpool, const int32_t* __restrict__ pairs,
+    int32_t num_blocks, int32_t block_vec) {
+  const int32_t src = pairs[2 * blockIdx.x];
+  const int32_t dst = pairs[2 * blockIdx.x + 1];
+  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
+  uint4* pool = blockIdx.y ? vpool : kpool;
+  const int64_t s0 = (int64_t)src * block_vec;
+  const int64_t d0 = (int64_t)dst * block_vec;
+  for (int32_t c = blockIdx.z * kThreads + threadIdx.x; c < block_vec; c += gridDim.z * kThreads)
+    pool[d0 + c] = pool[s0 + c];
+}
+
+int32_t elem_bytes(int32_t dtype) { return dtype == PA_F32 ? 4 : 2; }
+
+}  // namespace
+
+hipError_t launch_reshape_and_cache(const pa_kv_pool& pool, const void* key, const void* value,
+                                    const int64_t* slots, int32_t num_tokens, hipStream_t stream) {
+  const int32_t row_bytes = pool.num_kv_heads * pool.head_dim * elem_bytes(pool.dtype);
+  const int64_t num_slots = (int64_t)pool.num_blocks * pool.block_size;
+  hipLaunchKernelGGL(reshape_and_cache_kernel, dim3(num_tokens), dim3(kThreads), 0, stream,
+                     (uint4*)pool.k, (uint4*)pool.v, (const uint4*)key, (const uint4*)value, slots,
+                     num_slots, row_bytes / 16);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_blocks(const pa_kv_pool& pool, const int32_t* pairs, int32_t num_pairs,
+                              hipStream_t stream) {
+  const int64_t block_bytes =
+      (int64_t)pool.block_size * pool.num_kv_heads * pool.head_dim * elem_bytes(pool.dtype);
+  const int32_t block_vec = (int32_t)(block_bytes / 16);
+  const int32_t chunks = (block_vec + kThreads - 1) / kThreads;
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3(num_pairs, 2, chunks), dim3(kThreads), 0, stream,
+                     (uint4*)pool.k, (uint4*)pool.v, pairs, pool.num_blocks, block_vec);
+  return hipGetLastError();
+}
+
+}  // namespace pagedkv

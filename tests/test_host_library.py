@@ -1,0 +1,216 @@
+"""CPU tests of the product library: it loads, exports every declared symbol,
+its host block manager agrees with the Python model operation by operation,
+and its argument checks reject bad calls before anything reaches a GPU."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import paged_kv_cache_115_amd as pk
+from paged_kv_cache_115_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = set()
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names |= set(re.findall(r"\b(pa_\w+)\s*\(", text))
+    return sorted(names)
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert len(names) >= 18
+    for name in names:
+        assert hasattr(_lib.lib, name), name
+        assert name in _lib.SIGNATURES, f"{name} has no ctypes signature"
+
+
+def test_widget_tables_through_the_library():
+    bm = pk.BlockManager(64, 4)
+    for r, L in enumerate([17, 16, 18, 8, 17, 10]):
+        bm.append(r, L)
+    assert [bm.table(r).tolist() for r in range(6)] == [
+        [0, 1, 2, 3, 4], [5, 6, 7, 8], [9, 10, 11, 12, 13], [14, 15], [16, 17, 18, 19, 20], [21, 22, 23]]
+    bm.check()
+
+
+def _compare(bm: pk.BlockManager, model: oracle.BlockManagerModel, live):
+    for s in live:
+        assert bm.table(s).tolist() == model.table(s)
+        assert bm.length(s) == model.length(s)
+    for b in range(model.num_blocks):
+        assert bm.refcount(b) == model.refcount[b]
+    st, ms = bm.stats(), model.stats()
+    for k in ms:
+        assert st[k] == ms[k], k
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_block_manager_matches_model_on_random_operations(seed):
+    rng = np.random.default_rng(seed)
+    b = int(rng.choice([1, 4, 8, 16, 32]))
+    nb = int(rng.integers(6, 90))
+    order = rng.permutation(nb) if seed % 2 else None
+    bm = pk.BlockManager(nb, b, order)
+    model = oracle.BlockManagerModel(nb, b, order)
+    live, nxt = [], 0
+    for _ in range(250):
+        op = int(rng.integers(0, 5))
+        if op == 0 or not live:
+            args = ("append", nxt, int(rng.integers(0, 3 * b)))
+        elif op == 1:
+            args = ("append", int(rng.choice(live)), int(rng.integers(0, 2 * b)))
+        elif op == 2:
+            args = ("fork", int(rng.choice(live)), nxt)
+        elif op == 3:
+            k = int(rng.integers(1, len(live) + 1))
+            args = ("step", list(rng.choice(live, size=k, replace=False)))
+        else:
+            args = ("free", int(rng.choice(live)))
+        if args[0] == "append":
+            try:
+                ms, mc = model.append(args[1], args[2])
+                m_ok = True
+            except oracle.OutOfBlocks:
+                m_ok = False
+            try:
+                ps, pc = bm.append(args[1], args[2])
+                p_ok = True
+            except pk.PaError as e:
+                assert e.status == -3
+                p_ok = False
+            assert m_ok == p_ok
+            if m_ok:
+                assert ps.tolist() == ms and [tuple(x) for x in pc.tolist()] == mc
+                if args[1] not in live:
+                    live.append(args[1])
+                    nxt += 1
+        elif args[0] == "fork":
+            model.fork(args[1], args[2])
+            bm.fork(args[1], args[2])
+            live.append(args[2])
+            nxt += 1
+        elif args[0] == "step":
+            try:
+                ms, mc = model.append_step(args[1])
+                m_ok = True
+            except oracle.OutOfBlocks:
+                m_ok = False
+            try:
+                ps, pc = bm.append_step(args[1])
+                p_ok = True
+            except pk.PaError:
+                p_ok = False
+            assert m_ok == p_ok
+            if m_ok:
+                assert ps.tolist() == ms and [tuple(x) for x in pc.tolist()] == mc
+        else:
+            model.free_seq(args[1])
+            bm.free(args[1])
+            live.remove(args[1])
+        bm.check()
+        _compare(bm, model, live)
+
+
+def test_block_manager_errors():
+    with pytest.raises(pk.PaError):
+        pk.BlockManager(0, 16)
+    with pytest.raises(pk.PaError):
+        pk.BlockManager(4, 16, [0, 1, 1, 2])
+    bm = pk.BlockManager(4, 4)
+    with pytest.raises(pk.PaError) as e:
+        bm.fork(7, 8)
+    assert e.value.status == -4
+    bm.append(1, 3)
+    with pytest.raises(pk.PaError) as e:
+        bm.fork(1, 1)
+    assert e.value.status == -1
+    with pytest.raises(pk.PaError) as e:
+        bm.append_step([1, 1])
+    assert e.value.status == -1
+    bm.free(99)           # unknown: no-op
+    with pytest.raises(pk.PaError) as e:
+        bm.append(2, 100)
+    assert e.value.status == -3 and bm.stats()["alloc_failures"] == 1
+    with pytest.raises(KeyError):
+        bm.table(5)
+    assert bm.refcount(-1) == -1 and bm.refcount(4) == -1
+    tables, lens = bm.export([1], 4)
+    assert tables.tolist() == [[0, 0, 0, 0]] and lens.tolist() == [3]
+    with pytest.raises(pk.PaError):
+        bm.export([1, 42], 4)
+
+
+def test_decode_plan_layout():
+    plan = pk.decode_plan([0, 5, 600, 1000], 256)
+    assert (plan.num_items, plan.num_merges, plan.num_partials) == (9, 2, 7)
+    items = [tuple(r) for r in plan.items.tolist()]
+    assert items[:6] == [(2, 0, 3, 0), (2, 1, 3, 0), (3, 0, 4, 3), (3, 1, 4, 3), (3, 2, 4, 3), (3, 3, 4, 3)]
+    assert items[6:9] == [(2, 2, 3, 0), (1, 0, 1, -1), (0, 0, 1, -1)]
+    assert items[9:] == [(2, -1, 3, 0), (3, -1, 4, 3)]
+    whole = pk.decode_plan([3, 70000], 0)
+    assert (whole.num_partials, whole.num_merges) == (0, 0)
+    assert [tuple(r) for r in whole.items.tolist()] == [(1, 0, 1, -1), (0, 0, 1, -1)]
+    with pytest.raises(pk.PaError):
+        pk.decode_plan([1, 2], 24)
+    with pytest.raises(pk.PaError):
+        pk.decode_plan([1, -2], 32)
+    assert pk.decode_workspace_bytes(0, 32, 128) == 0
+    assert pk.decode_workspace_bytes(7, 32, 128) >= 7 * 32 * 130 * 4
+
+
+class _Pool(ctypes.Structure):
+    _fields_ = _lib.PaKvPool._fields_
+
+
+def _pool(dtype=1, b=16, d=128, hkv=8, k=0x10000, v=0x20000):
+    return _lib.PaKvPool(k, v, 100, b, hkv, d, dtype)
+
+
+@pytest.mark.parametrize("pool,status", [
+    (_pool(dtype=5), -2), (_pool(b=12), -2), (_pool(d=64), -2), (_pool(dtype=0, d=96), -2),
+    (_pool(k=0), -1), (_pool(k=0x10004), -1)])
+def test_abi_rejects_bad_pools_without_launching(pool, status):
+    dummy = ctypes.c_void_p(0x30000)
+    st = _lib.lib.pa_reshape_and_cache(ctypes.byref(pool), dummy, dummy, dummy, 4, None)
+    assert st == status
+    assert _lib.lib.pa_last_error()
+    st = _lib.lib.pa_copy_blocks(ctypes.byref(pool), dummy, 1, None)
+    assert st == status
+
+
+def test_abi_rejects_bad_decode_arguments_without_launching():
+    pool = _pool()
+    p = ctypes.c_void_p(0x40000)
+    L = _lib.lib
+
+    def call(**kw):
+        args = dict(q=p, out=p, out_dtype=0, tables=p, maxb=4, lens=p, nseq=2, hq=32, scale=0.1, items=p,
+                    nitems=2, nmerge=0, nparts=0, part=256, ws=None, wsb=0)
+        args.update(kw)
+        return L.pa_decode(ctypes.byref(pool), args["q"], args["out"], args["out_dtype"], args["tables"],
+                           args["maxb"], args["lens"], args["nseq"], args["hq"], ctypes.c_float(args["scale"]),
+                           args["items"], args["nitems"], args["nmerge"], args["nparts"], args["part"], args["ws"],
+                           args["wsb"], None)
+    assert call(hq=30) == -1                    # not a multiple of Hkv
+    assert call(hq=8 * 17) == -2                # group of 17 > 16
+    assert call(out_dtype=7) == -2
+    assert call(part=24) == -1                  # not a multiple of 16
+    assert call(q=None) == -1
+    assert call(q=ctypes.c_void_p(0x40008)) == -1   # misaligned
+    assert call(nparts=3) == -1                 # merges and records disagree
+    assert call(nparts=3, nmerge=1) == -1       # workspace missing
+    assert call(nparts=3, nmerge=1, ws=ctypes.c_void_p(0x50000), wsb=16) == -1   # too small
+    assert call(scale=float("inf")) == -1
+    assert call(nitems=0) == 0                  # nothing to do: OK, no launch
+    pool32 = _pool(dtype=0, d=64)
+    assert L.pa_decode(ctypes.byref(pool32), p, p, 1, p, 4, p, 2, 8, ctypes.c_float(1.0), p, 1, 0, 0, 0, None, 0,
+                       None) == -2              # bf16 output from an f32 pool
