@@ -7,18 +7,18 @@ mean about 200 tokens capped at 4096, blocks handed out from a shuffled free
 list.  One step is one pass of the whole hot path over one batch:
   pa_copy_blocks (copy-on-write pairs of this step; none in this workload)
   -> pa_reshape_and_cache (this step's token for every sequence)
-  -> pa_decode (attention through the block tables; split sequences merged by a
-     second, small launch).
-Step inputs (tables, lengths, slots, work items, queries, new keys/values) are
-resident in device memory before timing; the host block-manager append that
-produces them is timed separately (host_append_us).  R pool replicas (>= 1 GiB
-together, four times the 256 MB last-level cache) rotate so that KV reads come
-from HBM.
+  -> pa_decode (attention through the block tables on a persistent grid, then
+     the merge of cut sequences).
+Step inputs (tables, lengths, slots, the decode plan, queries, new keys and
+values) are resident in device memory before timing; the host block-manager
+append and the host plan that produce them are timed separately
+(host_append_us, host_plan_us).  R pool replicas (>= 1 GiB together, four
+times the 256 MB last-level cache) rotate so that KV reads come from HBM.
 
 Prints one JSON line.  `value` is KV-read GB/s over whole steps: algorithmic KV
 bytes (each live token's K and V row of each KV head, read once) per step
-divided by the step time.  `roofline` reports the decode kernel alone, timed
-per launch with HIP events on the stream it runs on.
+divided by the step time.  `roofline` reports the attention kernel alone,
+timed per launch with HIP events on the stream it runs on.
 """
 from __future__ import annotations
 
@@ -49,7 +49,6 @@ WORKLOADS = {
     "c4": "long-context GQA decode bf16: batch 16, 64 q / 8 KV heads, head_dim 128, block 16, "
           "lengths U[16384,32768]",
 }
-DEFAULT_PARTITION = {"c3": 256, "c2": 512, "c4": 512}
 PMC_FILE = os.path.join(ROOT, "profiles", "decode_c3_pmc.json")
 KERNEL_SRC = os.path.join(ROOT, "paged_kv_cache_115_amd", "csrc", "decode_kernels.hip")
 
@@ -58,14 +57,14 @@ def kernel_hash() -> str:
     return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
 
 
-def measured_traffic(config: str, partition: int):
-    """HBM bytes per decode launch from committed rocprofv3 counter runs, if
-    they were taken on the current kernel source and this configuration."""
+def measured_traffic(config: str, schedule: list):
+    """HBM bytes per attention launch from committed rocprofv3 counter runs,
+    if they were taken on the current kernel source and this workload."""
     try:
         rec = json.load(open(PMC_FILE))
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_sha") != kernel_hash() or rec.get("config") != config or rec.get("partition") != partition:
+    if rec.get("kernel_sha") != kernel_hash() or rec.get("config") != config or rec.get("schedule") != schedule:
         return None
     return rec.get("bytes_per_launch")
 
@@ -97,7 +96,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="c3", choices=sorted(WORKLOADS))
-    ap.add_argument("--partition", type=int, default=None, help="tokens per split-K partition")
+    ap.add_argument("--workgroups", type=int, default=None, help="persistent workgroups (default: fill the GPU)")
+    ap.add_argument("--piece", type=int, default=0, help="longest job piece in 16-token tiles (0: auto)")
     ap.add_argument("--replicas", type=int, default=None)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -113,7 +113,6 @@ def main() -> int:
 
     torch.cuda.set_device(0)
     name = args.config
-    partition = DEFAULT_PARTITION[name] if args.partition is None else args.partition
     case = synth.decode_case(name)
     cfg = case["cfg"]
     S, hq, hkv, d, B = len(case["lengths"]), cfg["num_q_heads"], cfg["num_kv_heads"], cfg["head_dim"], cfg["block_size"]
@@ -130,17 +129,18 @@ def main() -> int:
     host_append_us = (time.perf_counter() - t0) * 1e6
     maxb = int(max(-(-int(L) // B) for L in lens_np))
     tables, lens = bm.export(seqs, maxb)
+    workgroups = args.workgroups or pk.default_workgroups()
     t0 = time.perf_counter()
-    plan = pk.decode_plan(lens, partition)
+    plan = pk.decode_plan(lens, hkv, workgroups, args.piece)
     host_plan_us = (time.perf_counter() - t0) * 1e6
 
     dev = torch.device("cuda", 0)
     tables_d = torch.from_numpy(tables).to(dev)
     lens_d = torch.from_numpy(lens).to(dev)
-    items_d = torch.from_numpy(plan.items).to(dev)
+    plan_d = plan.to_device(dev)
     slots_d = torch.from_numpy(slots).to(dev)
     cows_d = torch.from_numpy(np.ascontiguousarray(cows, dtype=np.int32)).to(dev)
-    ws_bytes = pk.decode_workspace_bytes(plan.num_partials, hq, d)
+    ws_bytes = pk.decode_workspace_bytes(plan, hq, d)
     ws = torch.empty(max(ws_bytes, 256) // 4, dtype=torch.float32, device=dev)
     q_d = torch.from_numpy(case["q"].view(np.int16)).view(torch.bfloat16).to(dev)
 
@@ -167,7 +167,7 @@ def main() -> int:
             pk.reshape_and_cache(pool, new_k, new_v, slots_d, stream)
         if ev is not None:
             ev[0].record(stream)
-        pk.decode(pool, q_d, tables_d, lens_d, case["scale"], plan, items_d, ws, out, stream)
+        pk.decode(pool, q_d, tables_d, lens_d, case["scale"], plan, plan_d, ws, out, stream)
         if ev is not None:
             ev[1].record(stream)
 
@@ -185,7 +185,7 @@ def main() -> int:
     torch.cuda.synchronize()
     ms_per_step = start.elapsed_time(end) / args.steps
 
-    # Same steps again with an event pair around every decode launch.
+    # Same steps again with an event pair around every pa_decode call.
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     torch.cuda.synchronize()
     for k in range(args.steps):
@@ -197,7 +197,7 @@ def main() -> int:
     kv_bytes = int(lens.astype(np.int64).sum()) * hkv * d * 2 * 2
     value = kv_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = kv_bytes / (decode_us * 1e-6) / 1e9
-    traffic = measured_traffic(name, partition)
+    schedule = [int(workgroups), int(args.piece)]
     result = {
         "metric": "paged decode attention KV-read GB/s (% of HBM peak) and decode tokens/s, 1 GPU",
         "value": round(value, 2),
@@ -212,20 +212,22 @@ def main() -> int:
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": f"{name}: {WORKLOADS[name]}", "num_seqs": S, "num_q_heads": hq,
-                   "num_kv_heads": hkv, "head_dim": d, "block_size": B, "partition_size": partition,
+                   "num_kv_heads": hkv, "head_dim": d, "block_size": B,
                    "total_context_tokens": int(lens.sum()), "max_context": int(lens.max()),
+                   "workgroups": int(workgroups), "max_piece_tiles": int(args.piece),
+                   "jobs": int(plan.num_jobs), "merges": int(plan.num_merges), "records": int(plan.num_records),
                    "pool_replicas": R, "decode_only": bool(args.decode_only)},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "decode_tokens_per_s": round(S / (ms_per_step * 1e-3), 1),
         "kv_bytes_per_step": kv_bytes,
-        "decode_kernel_us": round(decode_us, 3),
-        "decode_kernel_us_p10_p90": [round(float(np.percentile(dec_ms, 10)) * 1e3, 3),
-                                     round(float(np.percentile(dec_ms, 90)) * 1e3, 3)],
+        "decode_call_us": round(decode_us, 3),
+        "decode_call_us_p10_p90": [round(float(np.percentile(dec_ms, 10)) * 1e3, 3),
+                                   round(float(np.percentile(dec_ms, 90)) * 1e3, 3)],
         "host_append_us": round(host_append_us, 2),
         "host_plan_us": round(host_plan_us, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "decode_bf16_kernel<16>", "bytes_per_launch": kv_bytes},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(name, schedule),
+                     "kernel": "pa_decode (attention + merge launches)", "bytes_per_launch": kv_bytes},
     }
     if not args.no_cpu_baseline:
         k_host = pools[0].k.cpu().view(torch.int16).numpy().view(np.uint16)

@@ -116,43 +116,75 @@ pa_status pa_copy_blocks(const pa_kv_pool* pool, const int32_t* pairs, int32_t n
  *  "The block table: logical to physical mapping").  L counts the token
  * written this step; L == 0 yields zeros.
  *
- * Work is split into items (sequence, partition of `partition_size` tokens).
- * A sequence longer than one partition leaves one (max, sum, accumulator)
- * record per partition and query head in the workspace; a second launch on
- * the same stream merges them by log-sum-exp in partition order.  The item
- * list comes from pa_decode_plan on the host (which knows the lengths) and is
- * uploaded by the caller with the other step inputs.
+ * Scheduling.  A sequence's context is cut into 16-token tiles.  The host
+ * plan (pa_decode_plan, which knows the lengths) cuts each sequence into
+ * pieces of at most `max_piece_tiles` tiles and makes one job per (piece,
+ * block of four KV heads); jobs are packed onto a fixed number of persistent
+ * workgroups, largest first onto the least-loaded workgroup, so that every
+ * workgroup carries about the same number of tiles.  The four waves of a
+ * workgroup take the four KV heads of each job, so the head slices of a slot
+ * row are read together.  A sequence cut into several pieces leaves one
+ * (max, sum, accumulator) record per piece and KV head in the workspace; a
+ * second launch on the same stream merges the records by log-sum-exp in
+ * piece order.  The plan is one byte buffer that the caller copies to the
+ * device with the other step inputs.
  * ------------------------------------------------------------------------- */
-typedef struct pa_work_item {
-  int32_t seq;          /* sequence index */
-  int32_t part;         /* partition index within the sequence; -1 marks a merge item */
-  int32_t num_parts;    /* partitions of this sequence */
-  int32_t partial_base; /* first workspace record of this sequence, -1 if num_parts == 1 */
-} pa_work_item;
+typedef struct pa_decode_job {
+  int32_t seq;         /* sequence index */
+  int32_t tile_begin;  /* first 16-token tile of the piece */
+  int32_t tile_count;  /* tiles in the piece, 1..64 */
+  int32_t head_block;  /* KV heads 4*head_block .. 4*head_block + 3 */
+  int32_t part;        /* piece index within the sequence */
+  int32_t num_parts;   /* pieces of the sequence (1: the job writes the output) */
+  int32_t record_base; /* workspace record of (seq, KV head g, piece p) = record_base + g * num_parts + p */
+  int32_t reserved;
+} pa_decode_job;
 
-/* pa_decode_plan - build the work list on the host.
- *   context_lens   : HOST int32 [num_seqs], each >= 0.
- *   partition_size : tokens per partition; a positive multiple of 16 and of
- *                    the pool's block size, or 0 for one partition per
- *                    sequence.
- *   items          : HOST output of capacity `capacity`: first *num_items
- *                    work items, one per partition (a sequence with L == 0
- *                    gets one), largest first so that the longest work starts
- *                    first; then *num_merges merge items, one per split
- *                    sequence.
- *   *num_partials  : workspace records needed (sum of num_parts over split
- *                    sequences).
- * Returns PA_ERR_INVALID if capacity is too small (the counts are still
- * written, so the caller can size a second call). */
-pa_status pa_decode_plan(const int32_t* context_lens, int32_t num_seqs, int32_t partition_size,
-                         pa_work_item* items, int32_t capacity, int32_t* num_items,
-                         int32_t* num_merges, int32_t* num_partials);
+typedef struct pa_decode_merge {
+  int32_t seq;
+  int32_t kv_head;
+  int32_t num_parts;   /* 0: the sequence is empty and its output is zero */
+  int32_t record_base; /* first record of this (sequence, KV head), pieces consecutive */
+} pa_decode_merge;
 
-/* Bytes of device workspace pa_decode needs for `num_partials` records (0 when
- * nothing is split).  The workspace needs no initialisation; it holds
- * per-partition records between the two launches of one call, so two calls
- * that may overlap in time (different streams) must not share one. */
-size_t pa_decode_workspace_bytes(int32_t num_partials, int32_t num_q_heads, int32_t head_dim);
+typedef struct pa_decode_plan_info {
+  int32_t num_workgroups; /* grid of the attention launch */
+  int32_t num_jobs;
+  int32_t num_merges;     /* grid of the merge launch (0: no merge launch) */
+  int32_t num_records;    /* workspace records, one per (sequence, KV head, piece) of cut sequences */
+  int32_t num_kv_heads;   /* KV heads the plan was made for */
+  int32_t offsets_at;     /* byte offset of int32 job offsets [num_workgroups + 1] */
+  int32_t jobs_at;        /* byte offset of pa_decode_job [num_jobs] */
+  int32_t merges_at;      /* byte offset of pa_decode_merge [num_merges] */
+  int32_t bytes;          /* total plan bytes */
+} pa_decode_plan_info;
+
+/* Persistent workgroups that fit the current device at full occupancy (all
+ * resident at once): compute units times resident decode workgroups per unit.
+ * Returns 0 and sets pa_last_error when no device can be queried. */
+int32_t pa_decode_default_workgroups(void);
+
+/* pa_decode_plan - build the schedule on the host.
+ *   context_lens    : HOST int32 [num_seqs], each >= 0.
+ *   num_kv_heads    : KV heads of the pool.
+ *   num_workgroups  : persistent workgroups (pa_decode_default_workgroups()).
+ *   max_piece_tiles : longest piece in tiles, 1..64; 0 chooses the average
+ *                     tiles per workgroup (clamped to [4, 64]).
+ *   plan            : HOST output buffer of `capacity` bytes (8-byte aligned).
+ *   info            : filled on success, and with info->bytes set when the
+ *                     capacity is too small (PA_ERR_INVALID) so the caller can
+ *                     size a second call.
+ * Deterministic: the same inputs give the same bytes. */
+pa_status pa_decode_plan(const int32_t* context_lens, int32_t num_seqs, int32_t num_kv_heads,
+                         int32_t num_workgroups, int32_t max_piece_tiles, void* plan,
+                         size_t capacity, pa_decode_plan_info* info);
+
+/* Bytes of device workspace pa_decode needs for a plan (0 when no sequence is
+ * cut).  The workspace needs no initialisation; it carries records from the
+ * attention launch to the merge launch of one call, so calls that may overlap
+ * in time (different streams) must not share one. */
+size_t pa_decode_workspace_bytes(const pa_decode_plan_info* info, int32_t num_q_heads,
+                                 int32_t head_dim);
 
 /* pa_decode - paged decode attention for one batch.
  *   q            : device [num_seqs][num_q_heads][head_dim], pool dtype.
@@ -163,21 +195,19 @@ size_t pa_decode_workspace_bytes(int32_t num_partials, int32_t num_q_heads, int3
  *   context_lens : device int32 [num_seqs].
  *   scale        : multiplies q.k before the softmax (1/sqrt(head_dim) for
  *                  standard attention; S06 "Implementation").
- *   items        : device copy of pa_decode_plan's output (num_items work
- *                  items followed by num_merges merge items) for the same
- *                  context lengths and partition_size.
- *   workspace    : device, >= pa_decode_workspace_bytes(num_partials, ...),
- *                  256-byte aligned; may be NULL when num_partials == 0.
+ *   plan, info   : device copy of the bytes pa_decode_plan wrote for the same
+ *                  context lengths and num_kv_heads, and its host-side info.
+ *   workspace    : device, >= pa_decode_workspace_bytes(info, ...), 256-byte
+ *                  aligned; may be NULL when info->num_records == 0.
  * Preconditions: context_lens equal those given to pa_decode_plan; each
  * L <= max_blocks_per_seq * B; the first ceil(L / B) table entries of each
  * sequence are in [0, num_blocks).  Results are deterministic: the order of
- * every floating-point reduction depends only on logical token positions,
- * never on physical block ids or on scheduling. */
+ * every floating-point reduction depends only on logical token positions and
+ * on the plan, never on physical block ids or on timing. */
 pa_status pa_decode(const pa_kv_pool* pool, const void* q, void* out, int32_t out_dtype,
                     const int32_t* block_tables, int32_t max_blocks_per_seq,
                     const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
-                    float scale, const pa_work_item* items, int32_t num_items,
-                    int32_t num_merges, int32_t num_partials, int32_t partition_size,
+                    float scale, const void* plan, const pa_decode_plan_info* info,
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------

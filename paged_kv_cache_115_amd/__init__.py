@@ -13,12 +13,12 @@ import os
 
 import numpy as np
 
-from ._lib import LIB_PATH, PA_BF16, PA_F32, PaError, PaKvPool, PaWorkItem, lib
+from ._lib import LIB_PATH, PA_BF16, PA_F32, PaDecodePlanInfo, PaError, PaKvPool, lib
 
 __all__ = [
     "LIB_PATH", "PA_F32", "PA_BF16", "PaError", "BlockManager", "KvPool",
     "reshape_and_cache", "copy_blocks", "decode_plan", "decode_workspace_bytes",
-    "decode", "DecodePlan",
+    "decode", "DecodePlan", "default_workgroups",
 ]
 
 
@@ -96,49 +96,78 @@ def copy_blocks(pool: KvPool, pairs, stream=None) -> None:
 
 
 class DecodePlan:
-    """Host-built work list for one batch (pa_decode_plan): `items` holds
-    num_items work items followed by num_merges merge items."""
+    """Host-built schedule for one batch (pa_decode_plan).  `blob` is the plan
+    bytes to copy to the device; `info` describes them."""
 
-    def __init__(self, items: np.ndarray, num_items: int, num_merges: int, num_partials: int,
-                 partition_size: int):
-        self.items = items                  # int32 [num_items + num_merges, 4]
-        self.num_items = num_items
-        self.num_merges = num_merges
-        self.num_partials = num_partials
-        self.partition_size = partition_size
+    JOB_FIELDS = ("seq", "tile_begin", "tile_count", "head_block", "part", "num_parts", "record_base", "reserved")
+
+    def __init__(self, blob: np.ndarray, info: PaDecodePlanInfo):
+        self.blob = blob          # uint8 [info.bytes]
+        self.info = info
+
+    def __getattr__(self, name):
+        if name in ("num_workgroups", "num_jobs", "num_merges", "num_records", "num_kv_heads"):
+            return getattr(self.info, name)
+        raise AttributeError(name)
+
+    def job_offsets(self) -> np.ndarray:
+        return self.blob[self.info.offsets_at:self.info.jobs_at].view(np.int32)[: self.info.num_workgroups + 1]
+
+    def jobs(self) -> np.ndarray:
+        """int32 [num_jobs, 8]: seq, tile_begin, tile_count, head_block, part, num_parts, record_base, 0."""
+        return self.blob[self.info.jobs_at:self.info.merges_at].view(np.int32).reshape(-1, 8)
+
+    def merges(self) -> np.ndarray:
+        """int32 [num_merges, 4]: seq, kv_head, num_parts, record_base."""
+        return self.blob[self.info.merges_at:self.info.bytes].view(np.int32).reshape(-1, 4)
+
+    def to_device(self, device="cuda"):
+        import torch
+        return torch.from_numpy(self.blob.copy()).to(device)
 
 
-def decode_plan(context_lens, partition_size: int) -> DecodePlan:
+def default_workgroups() -> int:
+    """Persistent decode workgroups filling the current device."""
+    n = lib.pa_decode_default_workgroups()
+    if n <= 0:
+        raise PaError(-5, "pa_decode_default_workgroups: " + lib.pa_last_error().decode())
+    return n
+
+
+def decode_plan(context_lens, num_kv_heads: int, num_workgroups: int | None = None,
+                max_piece_tiles: int = 0) -> DecodePlan:
+    """pa_decode_plan.  num_workgroups defaults to default_workgroups()."""
     lens = np.ascontiguousarray(context_lens, dtype=np.int32)
-    n_items, n_merge, n_part = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_int32(0)
-    cap = 1
-    for _ in range(2):
-        items = np.zeros((cap, 4), dtype=np.int32)
-        st = lib.pa_decode_plan(lens.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), lens.size, partition_size,
-                                items.ctypes.data_as(ctypes.POINTER(PaWorkItem)), cap, ctypes.byref(n_items),
-                                ctypes.byref(n_merge), ctypes.byref(n_part))
-        need = n_items.value + n_merge.value
-        if st == 0 or need <= cap:
-            break
-        cap = need
-    _check(st, "pa_decode_plan")
-    return DecodePlan(items[:need].copy(), n_items.value, n_merge.value, n_part.value, partition_size)
+    if num_workgroups is None:
+        num_workgroups = default_workgroups()
+    info = PaDecodePlanInfo()
+    p32 = lens.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    st = lib.pa_decode_plan(p32, lens.size, num_kv_heads, num_workgroups, max_piece_tiles, None, 0,
+                            ctypes.byref(info))
+    if st != 0 and info.bytes <= 0:
+        _check(st, "pa_decode_plan")
+    blob = np.zeros(max(info.bytes, 8) + 8, dtype=np.uint8)
+    off = (-blob.ctypes.data) % 8
+    buf = blob[off:off + max(info.bytes, 8)]
+    _check(lib.pa_decode_plan(p32, lens.size, num_kv_heads, num_workgroups, max_piece_tiles,
+                              ctypes.c_void_p(buf.ctypes.data), buf.size, ctypes.byref(info)), "pa_decode_plan")
+    return DecodePlan(buf[: info.bytes].copy(), info)
 
 
-def decode_workspace_bytes(num_partials: int, num_q_heads: int, head_dim: int) -> int:
-    return int(lib.pa_decode_workspace_bytes(num_partials, num_q_heads, head_dim))
+def decode_workspace_bytes(plan: DecodePlan, num_q_heads: int, head_dim: int) -> int:
+    return int(lib.pa_decode_workspace_bytes(ctypes.byref(plan.info), num_q_heads, head_dim))
 
 
-def decode(pool: KvPool, q, block_tables, context_lens, scale: float, plan: DecodePlan, items, workspace=None,
+def decode(pool: KvPool, q, block_tables, context_lens, scale: float, plan: DecodePlan, plan_dev, workspace=None,
            out=None, stream=None):
-    """pa_decode.  `items` is the device int32 copy of plan.items."""
+    """pa_decode.  `plan_dev` is the device copy of plan.blob (uint8 tensor)."""
     import torch
     _dev(q, "q", pool.k.dtype)
     _dev(block_tables, "block_tables", torch.int32)
     _dev(context_lens, "context_lens", torch.int32)
-    _dev(items, "items", torch.int32)
-    if items.shape[0] < plan.num_items + plan.num_merges:
-        raise ValueError("items holds fewer entries than the plan")
+    _dev(plan_dev, "plan_dev", torch.uint8)
+    if plan_dev.numel() < plan.info.bytes:
+        raise ValueError("plan_dev is shorter than the plan")
     s, hq, d = q.shape
     if out is None:
         out = torch.empty((s, hq, d), dtype=torch.float32, device=q.device)
@@ -147,10 +176,9 @@ def decode(pool: KvPool, q, block_tables, context_lens, scale: float, plan: Deco
         raise ValueError("out must be [S, Hq, D]")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.pa_decode(ctypes.byref(pool.c), _ptr(q), _ptr(out), _dtype_code(out), _ptr(block_tables),
-                         block_tables.shape[1], _ptr(context_lens), s, hq, ctypes.c_float(scale),
-                         _ptr(items), plan.num_items, plan.num_merges, plan.num_partials, plan.partition_size,
-                         None if workspace is None else _ptr(workspace), ws_bytes, _stream(stream)),
-           "pa_decode")
+                         block_tables.shape[1], _ptr(context_lens), s, hq, ctypes.c_float(scale), _ptr(plan_dev),
+                         ctypes.byref(plan.info), None if workspace is None else _ptr(workspace), ws_bytes,
+                         _stream(stream)), "pa_decode")
     return out
 
 

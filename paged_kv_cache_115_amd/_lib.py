@@ -22,9 +22,11 @@ class PaKvPool(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32)]
 
 
-class PaWorkItem(ctypes.Structure):
-    _fields_ = [("seq", ctypes.c_int32), ("part", ctypes.c_int32), ("num_parts", ctypes.c_int32),
-                ("partial_base", ctypes.c_int32)]
+class PaDecodePlanInfo(ctypes.Structure):
+    _fields_ = [("num_workgroups", ctypes.c_int32), ("num_jobs", ctypes.c_int32),
+                ("num_merges", ctypes.c_int32), ("num_records", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("offsets_at", ctypes.c_int32),
+                ("jobs_at", ctypes.c_int32), ("merges_at", ctypes.c_int32), ("bytes", ctypes.c_int32)]
 
 
 class PaBmStats(ctypes.Structure):
@@ -37,8 +39,12 @@ class PaBmStats(ctypes.Structure):
 
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m paged_kv_cache_115_amd.build` "
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python paged_kv_cache_115_amd/build.py` "
                           "(there is no fallback implementation)")
+    # PyTorch ships its own HIP runtime.  Load it first so that the library
+    # binds to that same runtime (same SONAME) instead of bringing a second
+    # copy of the runtime into the process.
+    import torch  # noqa: F401
     return ctypes.CDLL(LIB_PATH)
 
 
@@ -54,10 +60,11 @@ SIGNATURES = {
     "pa_last_error": (ctypes.c_char_p, []),
     "pa_reshape_and_cache": (_i32, [_pool, _vp, _vp, _vp, _i32, _vp]),
     "pa_copy_blocks": (_i32, [_pool, _vp, _i32, _vp]),
-    "pa_decode_plan": (_i32, [_p32, _i32, _i32, ctypes.POINTER(PaWorkItem), _i32, _p32, _p32, _p32]),
-    "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32]),
-    "pa_decode": (_i32, [_pool, _vp, _vp, _i32, _vp, _i32, _vp, _i32, _i32, ctypes.c_float, _vp, _i32, _i32,
-                         _i32, _i32, _vp, _sz, _vp]),
+    "pa_decode_default_workgroups": (_i32, []),
+    "pa_decode_plan": (_i32, [_p32, _i32, _i32, _i32, _i32, _vp, _sz, ctypes.POINTER(PaDecodePlanInfo)]),
+    "pa_decode_workspace_bytes": (_sz, [ctypes.POINTER(PaDecodePlanInfo), _i32, _i32]),
+    "pa_decode": (_i32, [_pool, _vp, _vp, _i32, _vp, _i32, _vp, _i32, _i32, ctypes.c_float, _vp,
+                         ctypes.POINTER(PaDecodePlanInfo), _vp, _sz, _vp]),
     "pa_bm_create": (_vp, [_i32, _i32, _p32]),
     "pa_bm_destroy": (None, [_vp]),
     "pa_bm_append": (_i32, [_vp, _i64, _i32, _p64, _p32, _p32]),

@@ -1,6 +1,6 @@
 """Build libpagedkv.so in-tree with hipcc for gfx950.
 
-    python -m paged_kv_cache_115_amd.build        # or __graft_entry__.build()
+    python paged_kv_cache_115_amd/build.py        # or __graft_entry__.build()
 
 Every translation unit is compiled with packed-FP32 instruction selection
 disabled (hipcc host passes warn that they do not know the feature; the

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cstring>
+#include <queue>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -62,16 +64,17 @@ pa_status hip_status(hipError_t e, const char* who) {
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Workspace carve: (max, sum) pairs | unnormalised accumulators.
+// Workspace carve for `heads` (record, query head) pairs: (max, sum) pairs,
+// then unnormalised accumulators.
 struct WorkspaceLayout {
   size_t ml, o, total;
 };
 
-WorkspaceLayout layout(int64_t num_partials, int64_t hq, int64_t d) {
+WorkspaceLayout layout(int64_t heads, int64_t d) {
   WorkspaceLayout w;
   w.ml = 0;
-  w.o = round_up(sizeof(float) * 2 * num_partials * hq, 256);
-  w.total = w.o + round_up(sizeof(float) * num_partials * hq * d, 256);
+  w.o = round_up(sizeof(float) * 2 * heads, 256);
+  w.total = w.o + round_up(sizeof(float) * heads * d, 256);
   return w;
 }
 
@@ -107,74 +110,141 @@ extern "C" pa_status pa_copy_blocks(const pa_kv_pool* pool, const int32_t* pairs
                              "pa_copy_blocks");
 }
 
-extern "C" pa_status pa_decode_plan(const int32_t* context_lens, int32_t num_seqs, int32_t partition_size,
-                                    pa_work_item* items, int32_t capacity, int32_t* num_items,
-                                    int32_t* num_merges, int32_t* num_partials) {
-  if (!num_items || !num_merges || !num_partials || num_seqs < 0 || capacity < 0 ||
-      (num_seqs > 0 && !context_lens))
+extern "C" int32_t pa_decode_default_workgroups(void) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
+    fail(PA_ERR_HIP, "pa_decode_default_workgroups: no device to query");
+    return 0;
+  }
+  if (pagedkv::decode_resident_workgroups_per_cu(&per_cu) != hipSuccess || per_cu <= 0) {
+    fail(PA_ERR_HIP, "pa_decode_default_workgroups: occupancy query failed");
+    return 0;
+  }
+  return cus * per_cu;
+}
+
+extern "C" pa_status pa_decode_plan(const int32_t* context_lens, int32_t num_seqs, int32_t num_kv_heads,
+                                    int32_t num_workgroups, int32_t max_piece_tiles, void* plan,
+                                    size_t capacity, pa_decode_plan_info* info) {
+  if (!info || num_seqs < 0 || num_kv_heads <= 0 || num_workgroups <= 0 || (num_seqs > 0 && !context_lens))
     return fail(PA_ERR_INVALID, "pa_decode_plan: bad arguments");
-  if (partition_size < 0 || (partition_size > 0 && partition_size % 16 != 0))
-    return fail(PA_ERR_INVALID, "pa_decode_plan: partition_size %d must be 0 or a positive multiple of 16",
-                partition_size);
-  struct Entry {
-    pa_work_item it;
-    int32_t tokens;
-  };
-  std::vector<Entry> work;
-  std::vector<pa_work_item> merges;
-  work.reserve(num_seqs);
-  int64_t partials = 0;
+  if (max_piece_tiles < 0 || max_piece_tiles > 64)
+    return fail(PA_ERR_INVALID, "pa_decode_plan: max_piece_tiles %d outside [0, 64]", max_piece_tiles);
+  if (capacity > 0 && (!plan || !pagedkv::aligned(plan, 8)))
+    return fail(PA_ERR_INVALID, "pa_decode_plan: plan buffer NULL or not 8-byte aligned");
+  const int64_t head_blocks = (num_kv_heads + 3) / 4;
+  int64_t total = 0;  // job tiles summed over head blocks
   for (int32_t s = 0; s < num_seqs; ++s) {
-    const int32_t L = context_lens[s];
-    if (L < 0) return fail(PA_ERR_INVALID, "pa_decode_plan: context_lens[%d] = %d < 0", s, L);
-    const int32_t parts = (partition_size > 0 && L > 0) ? (L + partition_size - 1) / partition_size : 1;
-    const int32_t base = parts > 1 ? (int32_t)partials : -1;
-    if (parts > 1) {
-      partials += parts;
-      merges.push_back(pa_work_item{s, -1, parts, base});
+    if (context_lens[s] < 0) return fail(PA_ERR_INVALID, "pa_decode_plan: context_lens[%d] < 0", s);
+    total += ((int64_t)context_lens[s] + 15) / 16 * head_blocks;
+  }
+  int64_t cap = max_piece_tiles;
+  if (cap == 0) cap = std::min<int64_t>(64, std::max<int64_t>(4, (total + num_workgroups - 1) / num_workgroups));
+
+  // Pieces: each sequence's tiles in near-equal runs of at most `cap`.
+  std::vector<pa_decode_job> jobs;
+  std::vector<pa_decode_merge> merges;
+  int64_t records = 0;
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    const int64_t tiles = ((int64_t)context_lens[s] + 15) / 16;
+    if (tiles == 0) {
+      for (int32_t g = 0; g < num_kv_heads; ++g) merges.push_back(pa_decode_merge{s, g, 0, -1});
+      continue;
     }
-    for (int32_t p = 0; p < parts; ++p) {
-      const int32_t tokens = parts > 1 ? std::min(L - p * partition_size, partition_size) : L;
-      work.push_back(Entry{pa_work_item{s, p, parts, base}, tokens});
+    const int64_t parts = (tiles + cap - 1) / cap;
+    const int64_t base = parts > 1 ? records : -1;
+    if (parts > 1) {
+      for (int32_t g = 0; g < num_kv_heads; ++g)
+        merges.push_back(pa_decode_merge{s, g, (int32_t)parts, (int32_t)(records + g * parts)});
+      records += parts * num_kv_heads;
+    }
+    int64_t t0 = 0;
+    for (int64_t p = 0; p < parts; ++p) {
+      const int64_t cnt = tiles / parts + (p < tiles % parts ? 1 : 0);
+      for (int64_t hb = 0; hb < head_blocks; ++hb)
+        jobs.push_back(pa_decode_job{s, (int32_t)t0, (int32_t)cnt, (int32_t)hb, (int32_t)p, (int32_t)parts,
+                                     (int32_t)base, 0});
+      t0 += cnt;
     }
   }
-  const int64_t total = (int64_t)work.size() + (int64_t)merges.size();
-  if (partials > INT32_MAX / 64 || total > INT32_MAX / 64)
+  if (records > INT32_MAX / 1024 || jobs.size() > (size_t)INT32_MAX / 64)
     return fail(PA_ERR_INVALID, "pa_decode_plan: plan too large");
-  // Largest first; ties in (sequence, partition) order so the plan is unique.
-  std::stable_sort(work.begin(), work.end(), [](const Entry& x, const Entry& y) { return x.tokens > y.tokens; });
-  *num_items = (int32_t)work.size();
-  *num_merges = (int32_t)merges.size();
-  *num_partials = (int32_t)partials;
-  if (total > capacity)
-    return fail(PA_ERR_INVALID, "pa_decode_plan: capacity %d < %lld entries", capacity, (long long)total);
-  for (size_t i = 0; i < work.size(); ++i) items[i] = work[i].it;
-  for (size_t i = 0; i < merges.size(); ++i) items[work.size() + i] = merges[i];
+
+  // Longest processing time first: each job, largest first, goes to the
+  // least-loaded workgroup (ties: lowest index).  Jobs keep sequence order
+  // inside a workgroup.
+  const int32_t nwg = (int32_t)std::min<int64_t>(num_workgroups, std::max<size_t>(jobs.size(), 1));
+  std::vector<int32_t> order(jobs.size());
+  for (size_t i = 0; i < order.size(); ++i) order[i] = (int32_t)i;
+  std::stable_sort(order.begin(), order.end(),
+                   [&](int32_t x, int32_t y) { return jobs[x].tile_count > jobs[y].tile_count; });
+  using Load = std::pair<int64_t, int32_t>;
+  std::priority_queue<Load, std::vector<Load>, std::greater<Load>> heap;
+  for (int32_t w = 0; w < nwg; ++w) heap.push(Load{0, w});
+  std::vector<int32_t> owner(jobs.size());
+  for (int32_t j : order) {
+    Load l = heap.top();
+    heap.pop();
+    owner[j] = l.second;
+    l.first += jobs[j].tile_count;
+    heap.push(l);
+  }
+  std::vector<int32_t> offsets(nwg + 1, 0);
+  for (int32_t o : owner) offsets[o + 1] += 1;
+  for (int32_t w = 0; w < nwg; ++w) offsets[w + 1] += offsets[w];
+  std::vector<pa_decode_job> placed(jobs.size());
+  std::vector<int32_t> fill(offsets.begin(), offsets.end() - 1);
+  for (size_t j = 0; j < jobs.size(); ++j) placed[fill[owner[j]]++] = jobs[j];
+
+  pa_decode_plan_info in{};
+  in.num_workgroups = jobs.empty() ? 0 : nwg;
+  in.num_jobs = (int32_t)jobs.size();
+  in.num_merges = (int32_t)merges.size();
+  in.num_records = (int32_t)records;
+  in.num_kv_heads = num_kv_heads;
+  in.offsets_at = 0;
+  in.jobs_at = (int32_t)pagedkv::round_up(sizeof(int32_t) * (nwg + 1), 32);
+  in.merges_at = in.jobs_at + (int32_t)(sizeof(pa_decode_job) * jobs.size());
+  const size_t bytes = (size_t)in.merges_at + sizeof(pa_decode_merge) * merges.size();
+  if (bytes > (size_t)INT32_MAX) return fail(PA_ERR_INVALID, "pa_decode_plan: plan too large");
+  in.bytes = (int32_t)bytes;
+  *info = in;
+  if (bytes > capacity)
+    return fail(PA_ERR_INVALID, "pa_decode_plan: capacity %zu < %zu bytes", capacity, bytes);
+  char* out = static_cast<char*>(plan);
+  std::memset(out, 0, bytes);
+  std::memcpy(out + in.offsets_at, offsets.data(), sizeof(int32_t) * offsets.size());
+  if (!placed.empty()) std::memcpy(out + in.jobs_at, placed.data(), sizeof(pa_decode_job) * placed.size());
+  if (!merges.empty()) std::memcpy(out + in.merges_at, merges.data(), sizeof(pa_decode_merge) * merges.size());
   return PA_OK;
 }
 
-extern "C" size_t pa_decode_workspace_bytes(int32_t num_partials, int32_t num_q_heads, int32_t head_dim) {
-  if (num_partials <= 0 || num_q_heads <= 0 || head_dim <= 0) return 0;
-  return pagedkv::layout(num_partials, num_q_heads, head_dim).total;
+extern "C" size_t pa_decode_workspace_bytes(const pa_decode_plan_info* info, int32_t num_q_heads,
+                                            int32_t head_dim) {
+  if (!info || info->num_records <= 0 || num_q_heads <= 0 || head_dim <= 0 || info->num_kv_heads <= 0) return 0;
+  const int64_t group = num_q_heads / info->num_kv_heads;
+  return pagedkv::layout((int64_t)info->num_records * group, head_dim).total;
 }
 
 extern "C" pa_status pa_decode(const pa_kv_pool* pool, const void* q, void* out, int32_t out_dtype,
                                const int32_t* block_tables, int32_t max_blocks_per_seq,
                                const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
-                               float scale, const pa_work_item* items, int32_t num_items,
-                               int32_t num_merges, int32_t num_partials, int32_t partition_size,
+                               float scale, const void* plan, const pa_decode_plan_info* info,
                                void* workspace, size_t workspace_bytes, void* stream) {
   if (pa_status st = pagedkv::check_pool(pool, "pa_decode")) return st;
-  if (num_seqs < 0 || num_items < 0 || num_merges < 0 || num_partials < 0 || max_blocks_per_seq < 0)
+  if (!info) return fail(PA_ERR_INVALID, "pa_decode: info is NULL");
+  if (num_seqs < 0 || max_blocks_per_seq < 0 || info->num_workgroups < 0 || info->num_jobs < 0 ||
+      info->num_merges < 0 || info->num_records < 0)
     return fail(PA_ERR_INVALID, "pa_decode: negative size");
-  if ((num_merges > 0) != (num_partials > 0))
-    return fail(PA_ERR_INVALID, "pa_decode: num_merges %d and num_partials %d disagree", num_merges, num_partials);
-  if (num_items == 0) return PA_OK;
-  if (num_seqs == 0) return fail(PA_ERR_INVALID, "pa_decode: work items but num_seqs == 0");
-  if (!q || !out || !block_tables || !context_lens || !items)
-    return fail(PA_ERR_INVALID, "pa_decode: NULL q/out/block_tables/context_lens/items");
+  if (info->num_jobs == 0 && info->num_merges == 0) return PA_OK;
+  if (num_seqs == 0) return fail(PA_ERR_INVALID, "pa_decode: a plan with work but num_seqs == 0");
+  if (!q || !out || !block_tables || !context_lens || !plan)
+    return fail(PA_ERR_INVALID, "pa_decode: NULL q/out/block_tables/context_lens/plan");
   if (max_blocks_per_seq == 0) return fail(PA_ERR_INVALID, "pa_decode: max_blocks_per_seq == 0");
   const int32_t hkv = pool->num_kv_heads;
+  if (info->num_kv_heads != hkv)
+    return fail(PA_ERR_INVALID, "pa_decode: plan made for %d KV heads, pool has %d", info->num_kv_heads, hkv);
   if (num_q_heads <= 0 || num_q_heads % hkv != 0)
     return fail(PA_ERR_INVALID, "pa_decode: num_q_heads %d is not a multiple of num_kv_heads %d",
                 num_q_heads, hkv);
@@ -182,17 +252,17 @@ extern "C" pa_status pa_decode(const pa_kv_pool* pool, const void* q, void* out,
   if (group > 16) return fail(PA_ERR_UNSUPPORTED, "pa_decode: %d query heads per KV head (max 16)", group);
   if (out_dtype != PA_F32 && out_dtype != pool->dtype)
     return fail(PA_ERR_UNSUPPORTED, "pa_decode: out_dtype %d must be f32 or the pool dtype", out_dtype);
-  if (partition_size < 0 || (partition_size > 0 && (partition_size % 16 || partition_size % pool->block_size)))
-    return fail(PA_ERR_INVALID, "pa_decode: partition_size %d must be 0 or a multiple of 16 and of B=%d",
-                partition_size, pool->block_size);
-  if (!pagedkv::aligned(q, 16) || !pagedkv::aligned(out, 16) || !pagedkv::aligned(items, 16))
-    return fail(PA_ERR_INVALID, "pa_decode: q/out/items must be 16-byte aligned");
+  if (!pagedkv::aligned(q, 16) || !pagedkv::aligned(out, 16) || !pagedkv::aligned(plan, 32))
+    return fail(PA_ERR_INVALID, "pa_decode: q/out must be 16-byte and plan 32-byte aligned");
   if (!std::isfinite(scale)) return fail(PA_ERR_INVALID, "pa_decode: scale is not finite");
-  if (((int64_t)num_items + num_merges) * hkv > INT32_MAX)
-    return fail(PA_ERR_INVALID, "pa_decode: num_items * num_kv_heads overflows the grid");
-  const auto lay = pagedkv::layout(num_partials, num_q_heads, pool->head_dim);
-  if (num_partials > 0) {
-    if (!workspace) return fail(PA_ERR_INVALID, "pa_decode: workspace is NULL but num_partials > 0");
+  if (info->jobs_at % 32 != 0 || info->merges_at % 16 != 0 || info->offsets_at != 0 ||
+      (int64_t)info->jobs_at < 4 * ((int64_t)info->num_workgroups + 1) ||
+      (int64_t)info->merges_at < (int64_t)info->jobs_at + 32 * (int64_t)info->num_jobs ||
+      (int64_t)info->bytes < (int64_t)info->merges_at + 16 * (int64_t)info->num_merges)
+    return fail(PA_ERR_INVALID, "pa_decode: inconsistent plan info");
+  const auto lay = pagedkv::layout((int64_t)info->num_records * group, pool->head_dim);
+  if (info->num_records > 0) {
+    if (!workspace) return fail(PA_ERR_INVALID, "pa_decode: workspace is NULL but the plan has records");
     if (!pagedkv::aligned(workspace, 256)) return fail(PA_ERR_INVALID, "pa_decode: workspace not 256-byte aligned");
     if (workspace_bytes < lay.total)
       return fail(PA_ERR_INVALID, "pa_decode: workspace %zu bytes < %zu needed", workspace_bytes, lay.total);
@@ -204,10 +274,13 @@ extern "C" pa_status pa_decode(const pa_kv_pool* pool, const void* q, void* out,
   a.out = out;
   a.tables = block_tables;
   a.lens = context_lens;
-  a.items = items;
+  const char* pb = static_cast<const char*>(plan);
+  a.job_offsets = reinterpret_cast<const int32_t*>(pb + info->offsets_at);
+  a.jobs = reinterpret_cast<const pa_decode_job*>(pb + info->jobs_at);
+  a.merges = reinterpret_cast<const pa_decode_merge*>(pb + info->merges_at);
   char* ws = static_cast<char*>(workspace);
-  a.partial_ml = num_partials > 0 ? reinterpret_cast<float*>(ws + lay.ml) : nullptr;
-  a.partial_o = num_partials > 0 ? reinterpret_cast<float*>(ws + lay.o) : nullptr;
+  a.partial_ml = info->num_records > 0 ? reinterpret_cast<float*>(ws + lay.ml) : nullptr;
+  a.partial_o = info->num_records > 0 ? reinterpret_cast<float*>(ws + lay.o) : nullptr;
   a.num_blocks = pool->num_blocks;
   a.block_size = pool->block_size;
   a.num_kv_heads = hkv;
@@ -216,12 +289,13 @@ extern "C" pa_status pa_decode(const pa_kv_pool* pool, const void* q, void* out,
   a.head_dim = pool->head_dim;
   a.max_blocks = max_blocks_per_seq;
   a.num_seqs = num_seqs;
-  a.partition = partition_size;
-  a.num_partials = num_partials;
-  a.num_items = num_items;
+  a.num_workgroups = info->num_workgroups;
+  a.num_jobs = info->num_jobs;
+  a.num_merges = info->num_merges;
+  a.num_records = info->num_records;
   a.out_bf16 = out_dtype == PA_BF16;
   a.scale_log2e = scale * 1.4426950408889634f;
-  const hipError_t e = pool->dtype == PA_BF16 ? pagedkv::launch_decode_bf16(a, num_merges, (hipStream_t)stream)
-                                              : pagedkv::launch_decode_f32(a, num_merges, (hipStream_t)stream);
+  const hipError_t e = pool->dtype == PA_BF16 ? pagedkv::launch_decode_bf16(a, (hipStream_t)stream)
+                                              : pagedkv::launch_decode_f32(a, (hipStream_t)stream);
   return pagedkv::hip_status(e, "pa_decode");
 }

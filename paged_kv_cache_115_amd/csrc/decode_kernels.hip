@@ -8,18 +8,24 @@
 // directly inside the kernel: no gathered copy is materialised (S06 "Why this
 // needed a custom CUDA kernel").
 //
-// Work decomposition.  One workgroup of kNW wavefronts per (work item, KV
-// head); a work item is one partition of one sequence, built on the host by
-// pa_decode_plan, largest first.  A partition's tokens are cut into 16-token
-// tiles handed round-robin to the wavefronts.  Each wavefront keeps an
-// online-softmax state (running max m, running sum l, unnormalised
-// accumulator o) for the G query heads of its KV head; the kNW states are
-// merged in LDS in wavefront order.  A sequence held in one partition writes
-// its output directly; a split sequence writes (m, l, o) of each partition to
-// the workspace and a second, small kernel merges the partitions in partition
+// Schedule.  The grid is a fixed set of persistent workgroups of four
+// wavefronts.  The host plan gives every workgroup a list of jobs (a piece of
+// one sequence's 16-token tiles, for a block of four KV heads) so that all
+// workgroups carry about the same number of tiles; wavefront w of the
+// workgroup handles KV head 4 * head_block + w of every job, so the four
+// head slices of each slot row are read at about the same time.  A
+// wavefront streams through its jobs back to back: the next job's query,
+// table entries and first tile are fetched while the current job finishes,
+// and within a job the next tile's K/V are in flight while the current one is
+// computed.  Each wavefront keeps one online-softmax state (running max m,
+// running sum l, unnormalised accumulator o) for the G query heads of its KV
+// head.  A job that covers a whole sequence writes the output; a piece of a
+// longer sequence writes a (m, l, o) record and merge_partials_kernel, a
+// second launch, combines the records of each (sequence, KV head) in piece
 // order.  Every floating-point reduction order depends only on logical token
-// positions: results are bitwise reproducible and do not depend on physical
-// block ids.  Softmax runs in base 2 on scores pre-multiplied by log2(e).
+// positions and on the plan: results are bitwise reproducible and do not
+// depend on physical block ids.  Softmax runs in base 2 on scores
+// pre-multiplied by log2(e).
 //
 // bf16 path (head_dim 128, G <= 16): both contractions run on MFMA.
 //   S^T[token][head] = K_tile[16 x 128] . Q^T[128 x 16]  with
@@ -36,9 +42,8 @@
 //     16-bit lane-local shuffles (no LDS round trip, no cross-lane transpose).
 //   Probabilities are rounded to bf16 for the PV product and the running sum
 //   adds the same rounded values, so numerator and denominator agree.
-//   Each wavefront holds the block-table entries of its tiles in one vector
-//   register (lane j: its j-th tile) and reads them with readlane; the K/V
-//   loads of the next tile are issued before the current tile is computed.
+//   A job's block-table entries sit in one vector register (lane i: tile i)
+//   and are read with readlane.
 // f32 path (head_dim 64 or 128, any G <= 16): vector ALU; each lane owns
 //   head_dim/64 dims, a query-key dot product is a wavefront butterfly sum.
 #include <hip/hip_runtime.h>
@@ -54,11 +59,11 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kNW = 4;                   // wavefronts per workgroup
-constexpr int kMaxGroup = 16;            // query heads per KV head
-constexpr int kTile = 16;                // tokens per tile (MFMA rows)
-constexpr int kChunk = kTile * kNW * 64; // tokens whose table entries fit one register per wave
-constexpr int kTblChunk = 256;           // f32 path: table entries staged in LDS at a time
+constexpr int kNW = 4;          // wavefronts per workgroup = KV heads per job
+constexpr int kTile = 16;       // tokens per tile (MFMA rows)
+constexpr int kMaxTiles = 64;   // tiles per job: one table entry per lane
+constexpr int kMergeThreads = 256;
+constexpr int kMergeChunk = 512;  // (piece, head) pairs staged in LDS at a time
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -75,439 +80,514 @@ __device__ __forceinline__ uint32_t word(const uint4& v, int i) {
 
 __device__ __forceinline__ int32_t clamp_block(int32_t b, int32_t nb) { return min(max(b, 0), nb - 1); }
 
-// LDS layout shared by the attention kernels (dynamic shared memory, floats):
-//   [0, kTblChunk)                         int32 staged table entries (f32 path)
-//   m[kNW][kMaxGroup], l[kNW][kMaxGroup]   per-wavefront softmax state
-//   o[kNW][G][D + 4]                       per-wavefront accumulators
-struct Smem {
-  int32_t* tbl;
-  float* m;
-  float* l;
-  float* o;
-  int pitch;
-};
-
-__device__ __forceinline__ Smem carve(float* base, int G, int D) {
-  Smem s;
-  s.tbl = reinterpret_cast<int32_t*>(base);
-  s.m = base + kTblChunk;
-  s.l = s.m + kNW * kMaxGroup;
-  s.o = s.l + kNW * kMaxGroup;
-  s.pitch = D + 4;
-  return s;
-}
-
-size_t smem_bytes(int G, int D) {
-  return sizeof(float) * (kTblChunk + 2 * kNW * kMaxGroup + (size_t)kNW * G * (D + 4));
-}
-
-__device__ __forceinline__ void store_out(const DecodeArgs& a, int64_t idx, float v) {
-  if (a.out_bf16)
-    reinterpret_cast<uint16_t*>(a.out)[idx] = (uint16_t)bf16_rne(v);
-  else
-    reinterpret_cast<float*>(a.out)[idx] = v;
-}
-
-// A work item whose indices would reach outside the workspace is dropped
-// (its plan did not come from pa_decode_plan with these sizes).
-__device__ __forceinline__ bool item_ok(const DecodeArgs& a, const pa_work_item& it) {
-  if (it.part < 0 || it.part >= it.num_parts) return false;
-  if (it.num_parts == 1) return true;
-  return it.partial_base >= 0 && (int64_t)it.partial_base + it.num_parts <= a.num_partials;
-}
-
-// Token range [start, end) of a work item, with L clamped to the table.
-struct Range {
-  int32_t s, g, start, end;
-};
-
-template <int B>
-__device__ __forceinline__ Range item_range(const DecodeArgs& a, const pa_work_item& it) {
-  Range r;
-  r.g = (int32_t)(blockIdx.x % (uint32_t)a.num_kv_heads);
-  r.s = min(max(it.seq, 0), a.num_seqs - 1);
-  const int32_t L = min(max(a.lens[r.s], 0), a.max_blocks * B);
-  const int32_t P = a.partition > 0 ? a.partition : L;
-  r.start = min(it.part * P, L);
-  r.end = min(L, r.start + P);
-  return r;
-}
-
-// Merge the wavefront states held in LDS.  One partition: the output.  Split
-// sequence: this partition's record (max, sum, unnormalised o) in the
-// workspace, merged later by merge_partials_kernel.
-template <int D>
-__device__ void finish(const DecodeArgs& a, const pa_work_item& it, int32_t s, int32_t g,
-                       const Smem& sm) {
-  const int G = a.group;
-  const bool split = it.num_parts > 1;
-  const int64_t out_base = ((int64_t)s * a.num_q_heads + (int64_t)g * G) * D;
-  for (int idx = threadIdx.x; idx < G * D; idx += kNW * 64) {
-    const int h = idx / D;
-    const int d = idx - h * D;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kNW; ++w) M = fmaxf(M, sm.m[w * kMaxGroup + h]);
-    float num = 0.f, den = 0.f;
-#pragma unroll
-    for (int w = 0; w < kNW; ++w) {
-      const float f = M == -INFINITY ? 0.f : fast_exp2(sm.m[w * kMaxGroup + h] - M);
-      den += f * sm.l[w * kMaxGroup + h];
-      num += f * sm.o[(w * G + h) * sm.pitch + d];
-    }
-    if (!split) {
-      store_out(a, out_base + idx, den > 0.f ? num / den : 0.f);
-    } else {
-      const int64_t rec = (int64_t)(it.partial_base + it.part) * a.num_q_heads + (int64_t)g * G + h;
-      a.partial_o[rec * D + d] = num;
-      if (d == 0) {
-        a.partial_ml[2 * rec] = M;
-        a.partial_ml[2 * rec + 1] = den;
-      }
-    }
+// Four consecutive output values at element index idx (a multiple of 4).
+__device__ __forceinline__ void store4(const DecodeArgs& a, int64_t idx, float x0, float x1, float x2, float x3) {
+  if (a.out_bf16) {
+    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.out) + idx) =
+        make_uint2(bf16_rne(x0) | (bf16_rne(x1) << 16), bf16_rne(x2) | (bf16_rne(x3) << 16));
+  } else {
+    *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + idx) = make_float4(x0, x1, x2, x3);
   }
+}
+
+__device__ __forceinline__ void store1(const DecodeArgs& a, int64_t idx, float x) {
+  if (a.out_bf16)
+    reinterpret_cast<uint16_t*>(a.out)[idx] = (uint16_t)bf16_rne(x);
+  else
+    reinterpret_cast<float*>(a.out)[idx] = x;
+}
+
+// Job fields as seen by one wavefront (all wave-uniform).
+struct JobView {
+  int32_t seq, g, t0, cnt, L, rec;
+};
+
+// Job j for wavefront w; false if the wavefront has nothing to do in it.
+__device__ __forceinline__ bool view_job(const DecodeArgs& a, int32_t j, int w, int B, JobView& v) {
+  const pa_decode_job jd = a.jobs[j];
+  v.g = jd.head_block * kNW + w;
+  v.cnt = min(jd.tile_count, kMaxTiles);
+  if (v.g < 0 || v.g >= a.num_kv_heads || v.cnt <= 0 || jd.tile_begin < 0) return false;
+  v.seq = min(max(jd.seq, 0), a.num_seqs - 1);
+  v.t0 = jd.tile_begin;
+  v.L = min(max(a.lens[v.seq], 0), a.max_blocks * B);
+  v.rec = -1;
+  if (jd.num_parts > 1) {
+    const int64_t r = (int64_t)jd.record_base + (int64_t)v.g * jd.num_parts + jd.part;
+    v.rec = (jd.record_base >= 0 && jd.part >= 0 && jd.part < jd.num_parts && r < a.num_records) ? (int32_t)r : -2;
+  }
+  return true;
 }
 
 // --------------------------------------------------------------------------
 // bf16, head_dim 128: MFMA for QK^T and PV.
 // --------------------------------------------------------------------------
+// Addressing state of one job for one wavefront: the job fields and the
+// job's block-table entries, one per lane (lane i: tile i).
 template <int B>
-__global__ __launch_bounds__(kNW * 64, 2) void decode_bf16_kernel(DecodeArgs a) {
-  constexpr int D = 128;
-  static_assert(B == 8 || B == 16 || B == 32, "block size");
-  extern __shared__ float smem_raw[];
-  const int G = a.group;
-  const Smem sm = carve(smem_raw, G, D);
-  const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
-  const int li = lane & 15;  // MFMA row / column within a 16-lane group
-  const int lq = lane >> 4;  // which 16-lane group
-  const pa_work_item it = a.items[blockIdx.x / a.num_kv_heads];
-  if (!item_ok(a, it)) return;
-  const Range rg = item_range<B>(a, it);
+struct JobRef {
+  JobView v;
+  int32_t tb0, tb1;
+};
 
-  // Q^T fragments: lane holds Q[head li][32*ks + 8*lq .. +8] for ks = 0..3.
-  bf16x8_t qf[4];
-  {
-    const uint4* qrow = reinterpret_cast<const uint4*>(
-        reinterpret_cast<const uint16_t*>(a.q) +
-        ((int64_t)rg.s * a.num_q_heads + (int64_t)rg.g * G + li) * D);
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const uint4 v = li < G ? qrow[4 * ks + lq] : make_uint4(0, 0, 0, 0);
-      qf[ks] = __builtin_bit_cast(bf16x8_t, v);
-    }
-  }
-
-  float m_run = -INFINITY;
-  float l_run = 0.f;
-  float4_t o[8];
-#pragma unroll
-  for (int c = 0; c < 8; ++c) o[c] = float4_t{0.f, 0.f, 0.f, 0.f};
-
-  // Byte addressing: slot row r of KV head g starts at base + r * row_bytes.
-  const int64_t row_bytes = (int64_t)a.num_kv_heads * D * 2;
-  const char* kbase = reinterpret_cast<const char*>(a.k) + (int64_t)rg.g * D * 2;
-  const char* vbase = reinterpret_cast<const char*>(a.v) + (int64_t)rg.g * D * 2;
-  const int32_t* trow = a.tables + (int64_t)rg.s * a.max_blocks;
+template <int B>
+__device__ __forceinline__ void load_ref(const DecodeArgs& a, int32_t j, int w, int lane, JobRef<B>& J) {
   constexpr int kTilesPerBlock = B >= kTile ? B / kTile : 1;
+  view_job(a, j, w, B, J.v);
+  // Lanes past the job's last tile read an in-row entry that is never used.
+  const int32_t* trow = a.tables + (int64_t)J.v.seq * a.max_blocks;
+  const int32_t t = J.v.t0 + lane;
+  int32_t e0 = B == 8 ? 2 * t : t / kTilesPerBlock;
+  e0 = min(e0, a.max_blocks - 1);
+  J.tb0 = clamp_block(trow[e0], a.num_blocks);
+  J.tb1 = B == 8 ? clamp_block(trow[min(e0 + 1, a.max_blocks - 1)], a.num_blocks) : 0;
+}
 
-  for (int32_t c0 = rg.start; c0 < rg.end; c0 += kChunk) {
-    const int32_t c1 = min(rg.end, c0 + kChunk);
-    const int32_t ntile = (c1 - c0 + kTile - 1) / kTile;
-    const int32_t mine = ntile > w ? (ntile - w + kNW - 1) / kNW : 0;
-    const int32_t blk0 = c0 / B;
-    // Table entries of this wave's tiles: lane j <-> tile w + kNW * j.  Lanes
-    // past the last tile read an in-row entry that is never used.
-    int32_t tb0, tb1 = 0;
-    {
-      const int32_t k = w + kNW * lane;
-      int32_t e0 = B == 8 ? blk0 + 2 * k : blk0 + k / kTilesPerBlock;
-      e0 = min(e0, a.max_blocks - 1);
-      tb0 = clamp_block(trow[e0], a.num_blocks);
-      if (B == 8) tb1 = clamp_block(trow[min(e0 + 1, a.max_blocks - 1)], a.num_blocks);
-    }
-
-    auto load_tile = [&](int i, uint4 (&kf)[4], uint4 (&vf)[4]) {
-      const int32_t k = w + kNW * i;
-      const int32_t p0 = __builtin_amdgcn_readlane(tb0, i);
-      int64_t krow, vrow[4];
-      if (B == 8) {
-        const int32_t p1 = __builtin_amdgcn_readlane(tb1, i);
-        krow = (int64_t)(li < 8 ? p0 : p1) * B + (li & 7);
+// Q^T fragments: lane holds Q[head li][32*ks + 8*lq .. +8] (zero for li >= G).
+__device__ __forceinline__ void load_q(const DecodeArgs& a, const JobView& v, int li, int lq, bf16x8_t (&qf)[4]) {
+  constexpr int D = 128;
+  const int G = a.group;
+  const uint4* qrow = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.q) +
+                                                     ((int64_t)v.seq * a.num_q_heads + (int64_t)v.g * G + li) * D);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) vrow[r] = (int64_t)(lq < 2 ? p0 : p1) * B + ((4 * lq + r) & 7);
-      } else {
-        const int32_t half = (k % kTilesPerBlock) * kTile;
-        krow = (int64_t)p0 * B + half + li;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) vrow[r] = (int64_t)p0 * B + half + 4 * lq + r;
-      }
-      const uint4* kr = reinterpret_cast<const uint4*>(kbase + krow * row_bytes);
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) kf[ks] = kr[4 * ks + lq];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) vf[r] = reinterpret_cast<const uint4*>(vbase + vrow[r] * row_bytes)[li];
-    };
-
-    auto compute_tile = [&](int i, const uint4 (&kf)[4], uint4 (&vf)[4]) {
-      const int32_t t0 = c0 + kTile * (w + kNW * i);
-      const bool tail = t0 + kTile > c1;  // wave-uniform: only the last tile of a chunk
-      if (tail) {
-        // Slots past the end hold arbitrary bits; V must be exactly zero there
-        // because 0 * NaN would poison the PV product.
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (t0 + 4 * lq + r >= c1) vf[r] = make_uint4(0, 0, 0, 0);
-      }
-      float4_t sacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kf[ks]), qf[ks],
-                                                       sacc, 0, 0, 0);
-      float x[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        x[r] = sacc[r] * a.scale_log2e;
-        if (tail && t0 + 4 * lq + r >= c1) x[r] = -INFINITY;
-      }
-      float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = fast_exp2(m_run - m_new);
-      uint32_t pb[4];
-      float psum = 0.f;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        pb[r] = bf16_rne(fast_exp2(x[r] - m_new));
-        psum += __uint_as_float(pb[r] << 16);
-      }
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-      const short4_t pfrag = __builtin_bit_cast(
-          short4_t, make_uint2(pb[0] | (pb[1] << 16), pb[2] | (pb[3] << 16)));
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const int wd = c >> 1;
-        uint32_t lo, hi;
-        if (c & 1) {
-          lo = (word(vf[0], wd) >> 16) | (word(vf[1], wd) & 0xffff0000u);
-          hi = (word(vf[2], wd) >> 16) | (word(vf[3], wd) & 0xffff0000u);
-        } else {
-          lo = (word(vf[0], wd) & 0xffffu) | (word(vf[1], wd) << 16);
-          hi = (word(vf[2], wd) & 0xffffu) | (word(vf[3], wd) << 16);
-        }
-        o[c] *= alpha;
-        o[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-            __builtin_bit_cast(short4_t, make_uint2(lo, hi)), pfrag, o[c], 0, 0, 0);
-      }
-    };
-
-    // Two register sets: the loads of tile i + 1 are in flight while tile i
-    // is computed.
-    uint4 kA[4], vA[4], kB[4], vB[4];
-    if (mine > 0) load_tile(0, kA, vA);
-    for (int i = 0; i < mine; i += 2) {
-      if (i + 1 < mine) load_tile(i + 1, kB, vB);
-      compute_tile(i, kA, vA);
-      if (i + 1 >= mine) break;
-      if (i + 2 < mine) load_tile(i + 2, kA, vA);
-      compute_tile(i + 1, kB, vB);
-    }
+  for (int ks = 0; ks < 4; ++ks) {
+    const uint4 x = li < G ? qrow[4 * ks + lq] : make_uint4(0, 0, 0, 0);
+    qf[ks] = __builtin_bit_cast(bf16x8_t, x);
   }
+}
 
-  // Wavefront state -> LDS.  Lane (li, lq) holds, for head li, the
-  // accumulator rows 4*lq + r of instance c: dims 32*lq + 8*r + c.
-  float lt = l_run + __shfl_xor(l_run, 16);
-  lt = lt + __shfl_xor(lt, 32);
-  if (li < G) {
-    if (lq == 0) {
-      sm.m[w * kMaxGroup + li] = m_run;
-      sm.l[w * kMaxGroup + li] = lt;
+// Buffer resource for `bytes` bytes at `base` (raw buffer, gfx9 dword3).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char* base, int32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, bytes, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 load_b128(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+}
+
+// K and V of tile t (of the job starting at tile t0) for KV head g: lane
+// (li, lq) gets K row li, dims 32*ks + 8*lq .. +8 (ks = 0..3), and V rows
+// 4*lq + r, dims 8*li .. 8*li + 8 (r = 0..3).
+template <int B>
+__device__ __forceinline__ void load_bf16_tile(const DecodeArgs& a, int32_t g, int32_t t0, int32_t tb0, int32_t tb1,
+                                               int32_t t, int li, int lq, uint4 (&kf)[4], uint4 (&vf)[4]) {
+  constexpr int D = 128;
+  constexpr int kTilesPerBlock = B >= kTile ? B / kTile : 1;
+  const uint32_t row_bytes = (uint32_t)a.num_kv_heads * D * 2;
+  const int64_t blk_bytes = (int64_t)row_bytes * B;
+  const char* kb = reinterpret_cast<const char*>(a.k) + (int64_t)g * D * 2;
+  const char* vb = reinterpret_cast<const char*>(a.v) + (int64_t)g * D * 2;
+  const int32_t p0 = __builtin_amdgcn_readlane(tb0, t);
+  if (B == 8) {
+    // Rows 0..7 of the tile live in block p0, rows 8..15 in block p1.
+    const int32_t p1 = __builtin_amdgcn_readlane(tb1, t);
+    const int64_t kblk = (int64_t)(li < 8 ? p0 : p1) * blk_bytes;
+    const int64_t vblk = (int64_t)(lq < 2 ? p0 : p1) * blk_bytes;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      kf[ks] = *reinterpret_cast<const uint4*>(kb + kblk + (li & 7) * row_bytes + 16 * (4 * ks + lq));
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      vf[r] = *reinterpret_cast<const uint4*>(vb + vblk + ((4 * lq + r) & 7) * row_bytes + 16 * li);
+  } else {
+    // One tile = 16 consecutive slot rows of one block: a buffer resource on
+    // the tile (scalar registers) plus lane offsets that never change.
+    const int64_t tile_off = (int64_t)p0 * blk_bytes + (int64_t)((t0 + t) % kTilesPerBlock) * kTile * row_bytes;
+    const int32_t tile_bytes = (int32_t)(kTile * row_bytes);
+    const __amdgpu_buffer_rsrc_t kr = tile_rsrc(kb + tile_off, tile_bytes);
+    const __amdgpu_buffer_rsrc_t vr = tile_rsrc(vb + tile_off, tile_bytes);
+    const uint32_t koff = li * row_bytes + 16 * lq;
+    const uint32_t voff = 4 * lq * row_bytes + 16 * li;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) kf[ks] = load_b128(kr, koff, 64 * ks);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) vf[r] = load_b128(vr, voff, r * row_bytes);
+  }
+}
+
+struct SoftmaxState {
+  float m, l;
+  float4_t o[8];
+  __device__ __forceinline__ void reset() {
+    m = -INFINITY;
+    l = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) o[c] = float4_t{0.f, 0.f, 0.f, 0.f};
+  }
+};
+
+// One 16-token tile (tile t of job v): scores, online-softmax update, PV
+// accumulation.
+__device__ __forceinline__ void compute_bf16_tile(const DecodeArgs& a, const JobView& v, const bf16x8_t (&qf)[4],
+                                                  int32_t t, int lq, const uint4 (&kf)[4], uint4 (&vf)[4],
+                                                  SoftmaxState& st) {
+  const int32_t tok0 = kTile * (v.t0 + t);
+  if (tok0 >= v.L) return;  // beyond the context (only if the plan and lengths disagree)
+  const bool tail = tok0 + kTile > v.L;
+  if (tail) {
+    // Slots past the end hold arbitrary bits; V must be exactly zero there
+    // because 0 * NaN would poison the PV product.
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (tok0 + 4 * lq + r >= v.L) vf[r] = make_uint4(0, 0, 0, 0);
+  }
+  float4_t sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+    sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kf[ks]), qf[ks], sacc, 0, 0, 0);
+  float x[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    x[r] = sacc[r] * a.scale_log2e;
+    if (tail && tok0 + 4 * lq + r >= v.L) x[r] = -INFINITY;
+  }
+  float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float m_new = fmaxf(st.m, mx);
+  const float alpha = fast_exp2(st.m - m_new);
+  uint32_t pb[4];
+  float psum = 0.f;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    pb[r] = bf16_rne(fast_exp2(x[r] - m_new));
+    psum += __uint_as_float(pb[r] << 16);
+  }
+  st.l = st.l * alpha + psum;
+  st.m = m_new;
+  const short4_t pfrag =
+      __builtin_bit_cast(short4_t, make_uint2(pb[0] | (pb[1] << 16), pb[2] | (pb[3] << 16)));
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const int wd = c >> 1;
+    uint32_t lo, hi;
+    if (c & 1) {
+      lo = (word(vf[0], wd) >> 16) | (word(vf[1], wd) & 0xffff0000u);
+      hi = (word(vf[2], wd) >> 16) | (word(vf[3], wd) & 0xffff0000u);
+    } else {
+      lo = (word(vf[0], wd) & 0xffffu) | (word(vf[1], wd) << 16);
+      hi = (word(vf[2], wd) & 0xffffu) | (word(vf[3], wd) << 16);
     }
-    float* orow = sm.o + (w * G + li) * sm.pitch + 32 * lq;
+    st.o[c] *= alpha;
+    st.o[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4_t, make_uint2(lo, hi)), pfrag,
+                                                        st.o[c], 0, 0, 0);
+  }
+}
+
+// End of a job: output (whole sequence) or the piece's record.  Lane (li, lq)
+// holds, for head li, accumulator rows 4*lq + r of instance c: dims
+// 32*lq + 8*r + c.
+__device__ __forceinline__ void finish_bf16_job(const DecodeArgs& a, const JobView& v, int li, int lq,
+                                                const SoftmaxState& st) {
+  constexpr int D = 128;
+  const int G = a.group;
+  float lt = st.l + __shfl_xor(st.l, 16);
+  lt = lt + __shfl_xor(lt, 32);
+  if (li >= G || v.rec == -2) return;
+  if (v.rec < 0) {
+    const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+    const int64_t base = ((int64_t)v.seq * a.num_q_heads + (int64_t)v.g * G + li) * D + 32 * lq;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      *reinterpret_cast<float4*>(orow + 8 * r) = make_float4(o[0][r], o[1][r], o[2][r], o[3][r]);
-      *reinterpret_cast<float4*>(orow + 8 * r + 4) = make_float4(o[4][r], o[5][r], o[6][r], o[7][r]);
+      store4(a, base + 8 * r, st.o[0][r] * inv, st.o[1][r] * inv, st.o[2][r] * inv, st.o[3][r] * inv);
+      store4(a, base + 8 * r + 4, st.o[4][r] * inv, st.o[5][r] * inv, st.o[6][r] * inv, st.o[7][r] * inv);
     }
+  } else {
+    const int64_t rec = (int64_t)v.rec * G + li;
+    float* po = a.partial_o + rec * D + 32 * lq;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      *reinterpret_cast<float4*>(po + 8 * r) = make_float4(st.o[0][r], st.o[1][r], st.o[2][r], st.o[3][r]);
+      *reinterpret_cast<float4*>(po + 8 * r + 4) = make_float4(st.o[4][r], st.o[5][r], st.o[6][r], st.o[7][r]);
+    }
+    if (lq == 0) *reinterpret_cast<float2*>(a.partial_ml + 2 * rec) = make_float2(st.m, lt);
   }
-  __syncthreads();
-  finish<D>(a, it, rg.s, rg.g, sm);
+}
+
+template <int B>
+__global__ __launch_bounds__(kNW * 64, 2) void decode_bf16_kernel(DecodeArgs a) {
+  static_assert(B == 8 || B == 16 || B == 32, "block size");
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: keeps job fields in SGPRs
+  const int li = lane & 15;  // MFMA row / column within a 16-lane group
+  const int lq = lane >> 4;  // which 16-lane group
+  const int32_t jend = min(a.job_offsets[blockIdx.x + 1], a.num_jobs);
+
+  // Next job index >= j in which this wavefront has work.
+  auto next_job = [&](int32_t j) {
+    JobView tmp;
+    while (j < jend && !view_job(a, j, w, B, tmp)) ++j;
+    return j;
+  };
+  const int32_t jc = next_job(max(a.job_offsets[blockIdx.x], 0));
+  if (jc >= jend) return;
+  int32_t jn = next_job(jc + 1);
+  int32_t jn2 = jn < jend ? next_job(jn + 1) : jend;
+
+  // The wavefront's tiles form one stream.  Position x is tile x - x0 of the
+  // current job (x0 = its first position); the positions past it belong to
+  // the next job and the one after.  Three register slots hold positions x,
+  // x + 1 and x + 2: while tile x is computed the loads of the next two are
+  // in flight.  Every load is issued unconditionally (a position past the
+  // end of the stream reloads the current tile), so the waits the compiler
+  // inserts count exactly the loads in flight.
+  JobRef<B> cur, nxt, nx2;
+  load_ref<B>(a, jc, w, lane, cur);
+  load_ref<B>(a, jn < jend ? jn : jc, w, lane, nxt);
+  load_ref<B>(a, jn2 < jend ? jn2 : jc, w, lane, nx2);
+  bool hn = jn < jend, hn2 = jn2 < jend;
+  bf16x8_t qc[4], qn[4];
+  load_q(a, cur.v, li, lq, qc);
+  load_q(a, nxt.v, li, lq, qn);
+  SoftmaxState st;
+  st.reset();
+  int32_t x = 0, x0 = 0;
+  uint4 k0[4], v0[4], k1[4], v1[4], k2[4], v2[4];
+
+  auto issue = [&](int32_t pos, uint4 (&kf)[4], uint4 (&vf)[4]) {
+    const int32_t r = pos - x0;
+    const int32_t rn = r - cur.v.cnt;
+    const int32_t rn2 = rn - nxt.v.cnt;
+    const bool in_c = r < cur.v.cnt;
+    const bool in_n = !in_c && hn && rn < nxt.v.cnt;
+    const bool in_n2 = !in_c && !in_n && hn && hn2 && rn2 < nx2.v.cnt;
+    const int32_t t = in_c ? r : in_n ? rn : in_n2 ? rn2 : cur.v.cnt - 1;
+    const int32_t g = in_n ? nxt.v.g : in_n2 ? nx2.v.g : cur.v.g;
+    const int32_t t0 = in_n ? nxt.v.t0 : in_n2 ? nx2.v.t0 : cur.v.t0;
+    const int32_t tb0 = in_n ? nxt.tb0 : in_n2 ? nx2.tb0 : cur.tb0;
+    const int32_t tb1 = in_n ? nxt.tb1 : in_n2 ? nx2.tb1 : cur.tb1;
+    load_bf16_tile<B>(a, g, t0, tb0, tb1, t, li, lq, kf, vf);
+  };
+  // Compute position x from slot (kf, vf) after issuing position x + 2 into
+  // slot (kp, vp); false when the stream is done.
+  auto step = [&](uint4 (&kf)[4], uint4 (&vf)[4], uint4 (&kp)[4], uint4 (&vp)[4]) {
+    issue(x + 2, kp, vp);
+    compute_bf16_tile(a, cur.v, qc, x - x0, lq, kf, vf, st);
+    ++x;
+    if (x - x0 < cur.v.cnt) return true;
+    finish_bf16_job(a, cur.v, li, lq, st);
+    if (!hn) return false;
+    x0 += cur.v.cnt;
+    cur = nxt;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qc[ks] = qn[ks];
+    nxt = nx2;
+    hn = hn2;
+    jn = jn2;
+    jn2 = hn ? next_job(jn + 1) : jend;
+    hn2 = jn2 < jend;
+    load_ref<B>(a, hn2 ? jn2 : jn, w, lane, nx2);
+    load_q(a, nxt.v, li, lq, qn);
+    st.reset();
+    return true;
+  };
+  issue(0, k0, v0);
+  issue(1, k1, v1);
+  while (true) {
+    if (!step(k0, v0, k2, v2)) break;
+    if (!step(k1, v1, k0, v0)) break;
+    if (!step(k2, v2, k1, v1)) break;
+  }
 }
 
 // --------------------------------------------------------------------------
-// f32: vector ALU.  Lane owns dims lane + 64*j.  Table entries staged in LDS.
+// f32: vector ALU.  Lane owns dims lane + 64*j; one token at a time.
 // --------------------------------------------------------------------------
 template <int B, int D>
-__global__ __launch_bounds__(kNW * 64, 2) void decode_f32_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kNW * 64) void decode_f32_kernel(DecodeArgs a) {
   constexpr int DPL = D / 64;
-  extern __shared__ float smem_raw[];
-  const int G = a.group;
-  const Smem sm = carve(smem_raw, G, D);
+  constexpr int kMaxGroup = 16;
   const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
-  const pa_work_item it = a.items[blockIdx.x / a.num_kv_heads];
-  if (!item_ok(a, it)) return;
-  const Range rg = item_range<B>(a, it);
-
-  float qv[kMaxGroup][DPL];
-  float m_run[kMaxGroup], l_run[kMaxGroup], o[kMaxGroup][DPL];
-  const float* qrow = reinterpret_cast<const float*>(a.q) +
-                      ((int64_t)rg.s * a.num_q_heads + (int64_t)rg.g * G) * D;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: keeps job fields in SGPRs
+  const int G = a.group;
+  const int32_t jend = min(a.job_offsets[blockIdx.x + 1], a.num_jobs);
+  for (int32_t j = max(a.job_offsets[blockIdx.x], 0); j < jend; ++j) {
+    JobView v;
+    if (!view_job(a, j, w, B, v)) continue;
+    float qv[kMaxGroup][DPL], m_run[kMaxGroup], l_run[kMaxGroup], o[kMaxGroup][DPL];
+    const float* qrow = reinterpret_cast<const float*>(a.q) + ((int64_t)v.seq * a.num_q_heads + (int64_t)v.g * G) * D;
 #pragma unroll
-  for (int h = 0; h < kMaxGroup; ++h) {
-    m_run[h] = -INFINITY;
-    l_run[h] = 0.f;
+    for (int h = 0; h < kMaxGroup; ++h) {
+      m_run[h] = -INFINITY;
+      l_run[h] = 0.f;
 #pragma unroll
-    for (int j = 0; j < DPL; ++j) {
-      qv[h][j] = h < G ? qrow[h * D + lane + 64 * j] : 0.f;
-      o[h][j] = 0.f;
+      for (int jj = 0; jj < DPL; ++jj) {
+        qv[h][jj] = h < G ? qrow[h * D + lane + 64 * jj] : 0.f;
+        o[h][jj] = 0.f;
+      }
+    }
+    const int64_t row_stride = (int64_t)a.num_kv_heads * D;
+    const float* kbase = reinterpret_cast<const float*>(a.k) + (int64_t)v.g * D;
+    const float* vbase = reinterpret_cast<const float*>(a.v) + (int64_t)v.g * D;
+    const int32_t* trow = a.tables + (int64_t)v.seq * a.max_blocks;
+    const int32_t t_end = min(kTile * (v.t0 + v.cnt), v.L);
+    for (int32_t t = kTile * v.t0; t < t_end; ++t) {
+      const int32_t p = clamp_block(trow[t / B], a.num_blocks);
+      const int64_t row = ((int64_t)p * B + t % B) * row_stride;
+      float kv[DPL], vv[DPL];
+#pragma unroll
+      for (int jj = 0; jj < DPL; ++jj) {
+        kv[jj] = kbase[row + lane + 64 * jj];
+        vv[jj] = vbase[row + lane + 64 * jj];
+      }
+#pragma unroll
+      for (int h = 0; h < kMaxGroup; ++h) {
+        if (h >= G) break;
+        float dot = 0.f;
+#pragma unroll
+        for (int jj = 0; jj < DPL; ++jj) dot += qv[h][jj] * kv[jj];
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) dot += __shfl_xor(dot, off);
+        const float x = dot * a.scale_log2e;
+        const float m_new = fmaxf(m_run[h], x);
+        const float alpha = fast_exp2(m_run[h] - m_new);
+        const float pr = fast_exp2(x - m_new);
+        l_run[h] = l_run[h] * alpha + pr;
+#pragma unroll
+        for (int jj = 0; jj < DPL; ++jj) o[h][jj] = o[h][jj] * alpha + pr * vv[jj];
+        m_run[h] = m_new;
+      }
+    }
+    if (v.rec == -2) continue;
+#pragma unroll
+    for (int h = 0; h < kMaxGroup; ++h) {
+      if (h >= G) break;
+      if (v.rec < 0) {
+        const float inv = l_run[h] > 0.f ? 1.0f / l_run[h] : 0.f;
+        const int64_t base = ((int64_t)v.seq * a.num_q_heads + (int64_t)v.g * G + h) * D;
+#pragma unroll
+        for (int jj = 0; jj < DPL; ++jj) store1(a, base + lane + 64 * jj, o[h][jj] * inv);
+      } else {
+        const int64_t rec = (int64_t)v.rec * G + h;
+#pragma unroll
+        for (int jj = 0; jj < DPL; ++jj) a.partial_o[rec * D + lane + 64 * jj] = o[h][jj];
+        if (lane == 0) *reinterpret_cast<float2*>(a.partial_ml + 2 * rec) = make_float2(m_run[h], l_run[h]);
+      }
     }
   }
+}
 
-  const int64_t row_stride = (int64_t)a.num_kv_heads * D;
-  const float* kbase = reinterpret_cast<const float*>(a.k) + (int64_t)rg.g * D;
-  const float* vbase = reinterpret_cast<const float*>(a.v) + (int64_t)rg.g * D;
-  const int32_t* trow = a.tables + (int64_t)rg.s * a.max_blocks;
-
-  for (int32_t c0 = rg.start; c0 < rg.end; c0 += kTblChunk * B) {
-    const int32_t c1 = min(rg.end, c0 + kTblChunk * B);
-    const int32_t blk0 = c0 / B;
-    const int32_t nblk = (c1 - c0 + B - 1) / B;
+// --------------------------------------------------------------------------
+// Merge: for every (sequence, KV head) cut into pieces, combine the piece
+// records in piece order,
+//   M = max_p m_p,  out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p,
+// staging (m, l) in LDS a chunk of pieces at a time (the running numerator
+// and denominator are rescaled when a later chunk raises the maximum).
+// An empty sequence (num_parts == 0) gets zeros.
+// --------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kMergeThreads) void merge_partials_kernel(DecodeArgs a) {
+  constexpr int kPer = 16 * D / kMergeThreads;  // output elements per thread at most
+  __shared__ float2 s_ml[kMergeChunk];
+  const pa_decode_merge mg = a.merges[blockIdx.x];
+  if (mg.seq < 0 || mg.seq >= a.num_seqs || mg.kv_head < 0 || mg.kv_head >= a.num_kv_heads) return;
+  const int G = a.group;
+  const int n = G * D;
+  const int64_t out_base = ((int64_t)mg.seq * a.num_q_heads + (int64_t)mg.kv_head * G) * D;
+  if (mg.num_parts <= 0) {
+    for (int e = threadIdx.x; e < n; e += kMergeThreads) store1(a, out_base + e, 0.f);
+    return;
+  }
+  if (mg.record_base < 0 || (int64_t)mg.record_base + mg.num_parts > a.num_records) return;
+  float M[kPer], num[kPer], den[kPer];
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    M[k] = -INFINITY;
+    num[k] = 0.f;
+    den[k] = 0.f;
+  }
+  const int chunk = kMergeChunk / G;
+  for (int p0 = 0; p0 < mg.num_parts; p0 += chunk) {
+    const int pc = min(chunk, mg.num_parts - p0);
     __syncthreads();
-    for (int i = threadIdx.x; i < nblk; i += kNW * 64) sm.tbl[i] = clamp_block(trow[blk0 + i], a.num_blocks);
+    for (int i = threadIdx.x; i < pc * G; i += kMergeThreads) {
+      const int64_t rec = (int64_t)(mg.record_base + p0 + i / G) * G + i % G;
+      s_ml[i] = *reinterpret_cast<const float2*>(a.partial_ml + 2 * rec);
+    }
     __syncthreads();
-    const int32_t ntile = (c1 - c0 + kTile - 1) / kTile;
-    for (int32_t tile = w; tile < ntile; tile += kNW) {
-      const int32_t t0 = c0 + tile * kTile;
-      const int32_t n = min(kTile, c1 - t0);
-      for (int32_t i = 0; i < n; ++i) {
-        const int32_t t = t0 + i;
-        const int32_t p = sm.tbl[t / B - blk0];
-        const int64_t row = ((int64_t)p * B + t % B) * row_stride;
-        float kv[DPL], vv[DPL];
 #pragma unroll
-        for (int j = 0; j < DPL; ++j) {
-          kv[j] = kbase[row + lane + 64 * j];
-          vv[j] = vbase[row + lane + 64 * j];
-        }
-#pragma unroll
-        for (int h = 0; h < kMaxGroup; ++h) {
-          if (h >= G) break;
-          float dot = 0.f;
-#pragma unroll
-          for (int j = 0; j < DPL; ++j) dot += qv[h][j] * kv[j];
-#pragma unroll
-          for (int off = 32; off >= 1; off >>= 1) dot += __shfl_xor(dot, off);
-          const float x = dot * a.scale_log2e;
-          const float m_new = fmaxf(m_run[h], x);
-          const float alpha = fast_exp2(m_run[h] - m_new);
-          const float pr = fast_exp2(x - m_new);
-          l_run[h] = l_run[h] * alpha + pr;
-#pragma unroll
-          for (int j = 0; j < DPL; ++j) o[h][j] = o[h][j] * alpha + pr * vv[j];
-          m_run[h] = m_new;
+    for (int k = 0; k < kPer; ++k) {
+      const int e = threadIdx.x + k * kMergeThreads;
+      if (e >= n) break;
+      const int h = e / D;
+      const int d = e - h * D;
+      float mc = -INFINITY;
+      for (int p = 0; p < pc; ++p) mc = fmaxf(mc, s_ml[p * G + h].x);
+      const float mn = fmaxf(M[k], mc);
+      if (mn != -INFINITY) {
+        const float rescale = M[k] == -INFINITY ? 0.f : fast_exp2(M[k] - mn);
+        num[k] *= rescale;
+        den[k] *= rescale;
+        M[k] = mn;
+#pragma unroll 4
+        for (int p = 0; p < pc; ++p) {
+          const float2 ml = s_ml[p * G + h];
+          const float f = fast_exp2(ml.x - mn);
+          den[k] += f * ml.y;
+          num[k] += f * a.partial_o[((int64_t)(mg.record_base + p0 + p) * G + h) * D + d];
         }
       }
     }
   }
-
 #pragma unroll
-  for (int h = 0; h < kMaxGroup; ++h) {
-    if (h >= G) break;
-    if (lane == 0) {
-      sm.m[w * kMaxGroup + h] = m_run[h];
-      sm.l[w * kMaxGroup + h] = l_run[h];
-    }
-#pragma unroll
-    for (int j = 0; j < DPL; ++j) sm.o[(w * G + h) * sm.pitch + lane + 64 * j] = o[h][j];
-  }
-  __syncthreads();
-  finish<D>(a, it, rg.s, rg.g, sm);
-}
-
-// --------------------------------------------------------------------------
-// Split-K merge: for every split sequence and KV head, combine the partition
-// records in partition order:
-//   M = max_p m_p,  out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p.
-// --------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(256) void merge_partials_kernel(DecodeArgs a) {
-  const pa_work_item it = a.items[a.num_items + blockIdx.x / a.num_kv_heads];
-  const int32_t g = (int32_t)(blockIdx.x % (uint32_t)a.num_kv_heads);
-  if (it.num_parts < 2 || it.partial_base < 0 ||
-      (int64_t)it.partial_base + it.num_parts > a.num_partials || it.seq < 0 || it.seq >= a.num_seqs)
-    return;
-  const int G = a.group;
-  const int64_t out_base = ((int64_t)it.seq * a.num_q_heads + (int64_t)g * G) * D;
-  for (int idx = threadIdx.x; idx < G * D; idx += 256) {
-    const int h = idx / D;
-    const int d = idx - h * D;
-    const int64_t rec0 = (int64_t)it.partial_base * a.num_q_heads + (int64_t)g * G + h;
-    float M = -INFINITY;
-    for (int p = 0; p < it.num_parts; ++p)
-      M = fmaxf(M, a.partial_ml[2 * (rec0 + (int64_t)p * a.num_q_heads)]);
-    float num = 0.f, den = 0.f;
-    for (int p = 0; p < it.num_parts; ++p) {
-      const int64_t rec = rec0 + (int64_t)p * a.num_q_heads;
-      const float f = M == -INFINITY ? 0.f : fast_exp2(a.partial_ml[2 * rec] - M);
-      den += f * a.partial_ml[2 * rec + 1];
-      num += f * a.partial_o[rec * D + d];
-    }
-    store_out(a, out_base + idx, den > 0.f ? num / den : 0.f);
+  for (int k = 0; k < kPer; ++k) {
+    const int e = threadIdx.x + k * kMergeThreads;
+    if (e >= n) break;
+    store1(a, out_base + e, den[k] > 0.f ? num[k] / den[k] : 0.f);
   }
 }
 
-hipError_t launch_merge(const DecodeArgs& a, int32_t num_merges, hipStream_t stream) {
-  if (num_merges == 0) return hipSuccess;
-  const dim3 grid((unsigned)num_merges * (unsigned)a.num_kv_heads);
+hipError_t launch_merge(const DecodeArgs& a, hipStream_t stream) {
+  if (a.num_merges == 0) return hipSuccess;
   if (a.head_dim == 128)
-    hipLaunchKernelGGL(merge_partials_kernel<128>, grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(merge_partials_kernel<128>, dim3(a.num_merges), dim3(kMergeThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL(merge_partials_kernel<64>, grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(merge_partials_kernel<64>, dim3(a.num_merges), dim3(kMergeThreads), 0, stream, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_decode_bf16(const DecodeArgs& a, int32_t num_merges, hipStream_t stream) {
-  if (a.num_items == 0) return hipSuccess;
-  const dim3 grid((unsigned)a.num_items * (unsigned)a.num_kv_heads);
-  const size_t smem = smem_bytes(a.group, 128);
-  switch (a.block_size) {
-    case 8: hipLaunchKernelGGL(decode_bf16_kernel<8>, grid, dim3(kNW * 64), smem, stream, a); break;
-    case 16: hipLaunchKernelGGL(decode_bf16_kernel<16>, grid, dim3(kNW * 64), smem, stream, a); break;
-    case 32: hipLaunchKernelGGL(decode_bf16_kernel<32>, grid, dim3(kNW * 64), smem, stream, a); break;
-    default: return hipErrorInvalidValue;
+hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream) {
+  if (a.num_workgroups > 0 && a.num_jobs > 0) {
+    const dim3 grid((unsigned)a.num_workgroups);
+    switch (a.block_size) {
+      case 8: hipLaunchKernelGGL(decode_bf16_kernel<8>, grid, dim3(kNW * 64), 0, stream, a); break;
+      case 16: hipLaunchKernelGGL(decode_bf16_kernel<16>, grid, dim3(kNW * 64), 0, stream, a); break;
+      case 32: hipLaunchKernelGGL(decode_bf16_kernel<32>, grid, dim3(kNW * 64), 0, stream, a); break;
+      default: return hipErrorInvalidValue;
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  return launch_merge(a, num_merges, stream);
+  return launch_merge(a, stream);
 }
 
-hipError_t launch_decode_f32(const DecodeArgs& a, int32_t num_merges, hipStream_t stream) {
-  if (a.num_items == 0) return hipSuccess;
-  const dim3 grid((unsigned)a.num_items * (unsigned)a.num_kv_heads);
-  const size_t smem = smem_bytes(a.group, a.head_dim);
-  bool launched = false;
-#define PA_F32_CASE(BS, DD)                                                                       \
-  if (!launched && a.block_size == BS && a.head_dim == DD) {                                      \
-    hipLaunchKernelGGL((decode_f32_kernel<BS, DD>), grid, dim3(kNW * 64), smem, stream, a);       \
-    launched = true;                                                                              \
+hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t stream) {
+  if (a.num_workgroups > 0 && a.num_jobs > 0) {
+    const dim3 grid((unsigned)a.num_workgroups);
+    bool launched = false;
+#define PA_F32_CASE(BS, DD)                                                                  \
+  if (!launched && a.block_size == BS && a.head_dim == DD) {                                 \
+    hipLaunchKernelGGL((decode_f32_kernel<BS, DD>), grid, dim3(kNW * 64), 0, stream, a);     \
+    launched = true;                                                                         \
   }
-  PA_F32_CASE(8, 64)
-  PA_F32_CASE(16, 64)
-  PA_F32_CASE(32, 64)
-  PA_F32_CASE(8, 128)
-  PA_F32_CASE(16, 128)
-  PA_F32_CASE(32, 128)
+    PA_F32_CASE(8, 64)
+    PA_F32_CASE(16, 64)
+    PA_F32_CASE(32, 64)
+    PA_F32_CASE(8, 128)
+    PA_F32_CASE(16, 128)
+    PA_F32_CASE(32, 128)
 #undef PA_F32_CASE
-  if (!launched) return hipErrorInvalidValue;
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  return launch_merge(a, num_merges, stream);
+    if (!launched) return hipErrorInvalidValue;
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return launch_merge(a, stream);
+}
+
+hipError_t decode_resident_workgroups_per_cu(int* n) {
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, decode_bf16_kernel<16>, kNW * 64, 0);
 }
 
 }  // namespace pagedkv

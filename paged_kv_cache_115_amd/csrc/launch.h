@@ -1,5 +1,5 @@
 // Kernel launchers of libpagedkv (internal; called by the C-ABI front after
-// argument validation).  All take a hipStream_t passed as void*.
+// argument validation).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -8,7 +8,7 @@
 
 namespace pagedkv {
 
-// Arguments of one decode launch; pointers are device pointers.
+// Arguments of one decode call; pointers are device pointers.
 struct DecodeArgs {
   const void* k;
   const void* v;
@@ -16,28 +16,33 @@ struct DecodeArgs {
   void* out;
   const int32_t* tables;
   const int32_t* lens;
-  const pa_work_item* items;  // [num_items] work items, then the merge items
-  float* partial_ml;      // [num_partials * num_q_heads][2] = (max, sum) in log2 units
-  float* partial_o;       // [num_partials * num_q_heads][head_dim]
+  const int32_t* job_offsets;    // [num_workgroups + 1]
+  const pa_decode_job* jobs;     // [num_jobs]
+  const pa_decode_merge* merges; // [num_merges]
+  float* partial_ml;             // [num_records * group][2] = (max, sum) in log2 units
+  float* partial_o;              // [num_records * group][head_dim], unnormalised
   int32_t num_blocks;
   int32_t block_size;
   int32_t num_kv_heads;
   int32_t num_q_heads;
-  int32_t group;          // num_q_heads / num_kv_heads
+  int32_t group;                 // num_q_heads / num_kv_heads
   int32_t head_dim;
-  int32_t max_blocks;     // block-table row length
+  int32_t max_blocks;            // block-table row length
   int32_t num_seqs;
-  int32_t partition;      // tokens per partition, 0 = whole sequence
-  int32_t num_partials;   // workspace records available
-  int32_t num_items;      // work items (merge items follow them)
-  int32_t out_bf16;       // 1: write bfloat16, 0: float32
-  float scale_log2e;      // scale * log2(e)
+  int32_t num_workgroups;
+  int32_t num_jobs;
+  int32_t num_merges;
+  int32_t num_records;
+  int32_t out_bf16;              // 1: write bfloat16, 0: float32
+  float scale_log2e;             // scale * log2(e)
 };
 
-// Attention launch over a.num_items work items, then (if num_merges > 0) the
-// split-K merge launch, both on `stream`.
-hipError_t launch_decode_bf16(const DecodeArgs& a, int32_t num_merges, hipStream_t stream);
-hipError_t launch_decode_f32(const DecodeArgs& a, int32_t num_merges, hipStream_t stream);
+// Attention launch (persistent grid of a.num_workgroups), then the merge
+// launch when a.num_merges > 0, both on `stream`.
+hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t stream);
+// Resident decode workgroups per compute unit (occupancy of the bf16 kernel).
+hipError_t decode_resident_workgroups_per_cu(int* n);
 
 hipError_t launch_reshape_and_cache(const pa_kv_pool& pool, const void* key, const void* value,
                                     const int64_t* slots, int32_t num_tokens, hipStream_t stream);

@@ -55,25 +55,25 @@ def assert_close(out: np.ndarray, ref: np.ndarray, dt: str, where: str = "") -> 
     return stats
 
 
-def plan_and_workspace(pk, lens: np.ndarray, partition: int, hq: int, d: int):
-    plan = pk.decode_plan(lens, partition)
-    items = torch.from_numpy(plan.items).cuda()
-    nbytes = pk.decode_workspace_bytes(plan.num_partials, hq, d)
+def plan_and_workspace(pk, lens: np.ndarray, hkv: int, hq: int, d: int, num_workgroups=None, max_piece_tiles=0):
+    plan = pk.decode_plan(lens, hkv, num_workgroups, max_piece_tiles)
+    nbytes = pk.decode_workspace_bytes(plan, hq, d)
     # The workspace needs no initialisation: fill it with NaN to prove it.
     ws = torch.full((nbytes // 4,), float("nan"), dtype=torch.float32, device="cuda") if nbytes else None
-    return plan, items, ws
+    return plan, plan.to_device(), ws
 
 
-def gpu_decode(pk, pool, q_dev, tables, lens, scale, partition, out_dtype=torch.float32):
+def gpu_decode(pk, pool, q_dev, tables, lens, scale, schedule=(None, 0), out_dtype=torch.float32):
+    """schedule = (num_workgroups or None for the device default, max_piece_tiles)."""
     hq = q_dev.shape[1]
-    plan, items, ws = plan_and_workspace(pk, lens, partition, hq, pool.k.shape[3])
+    plan, plan_dev, ws = plan_and_workspace(pk, lens, pool.k.shape[2], hq, pool.k.shape[3], *schedule)
     out = torch.full(tuple(q_dev.shape), float("nan"), dtype=out_dtype, device="cuda")
-    pk.decode(pool, q_dev, to_dev(tables), to_dev(lens), scale, plan, items, ws, out=out)
+    pk.decode(pool, q_dev, to_dev(tables), to_dev(lens), scale, plan, plan_dev, ws, out=out)
     return out
 
 
 # ---------------------------------------------------------------- decode step
-def product_decode_step(pk, case: dict, partition: int, out_dtype=torch.float32):
+def product_decode_step(pk, case: dict, schedule=(None, 0), out_dtype=torch.float32):
     """Prefill L-1 tokens, append this step's token, decode.  Returns dict."""
     cfg = case["cfg"]
     b, hkv, d, dt = cfg["block_size"], cfg["num_kv_heads"], cfg["head_dim"], cfg["dtype"]
@@ -110,7 +110,7 @@ def product_decode_step(pk, case: dict, partition: int, out_dtype=torch.float32)
     maxb = max(1, int(max((-(-int(L) // b)) for L in lens)))
     tables, lens_out = bm.export(np.arange(s_count), maxb)
     assert np.array_equal(lens_out, lens)
-    out = gpu_decode(pk, pool, to_dev(case["q"]), tables, lens_out, case["scale"], partition, out_dtype)
+    out = gpu_decode(pk, pool, to_dev(case["q"]), tables, lens_out, case["scale"], schedule, out_dtype)
     torch.cuda.synchronize()
     return dict(out=to_host(out), kpool=to_host(kpool), vpool=to_host(vpool), tables=tables,
                 pre_slots=pre_slots, new_slots=new_slots, pool=pool, q_dev=to_dev(case["q"]), lens=lens_out)
@@ -157,7 +157,7 @@ def _prefix_ops(case: dict):
     return p, n, case["cfg"]["prefix_len"], case["tail_lengths"]
 
 
-def product_prefix(pk, case: dict, partition: int, shared: bool = True, private_order=None):
+def product_prefix(pk, case: dict, schedule=(None, 0), shared: bool = True, private_order=None):
     cfg = case["cfg"]
     b, hkv, d, dt = case["block_size"], cfg["num_kv_heads"], cfg["head_dim"], cfg["dtype"]
     p, n, pre, tails = _prefix_ops(case)
@@ -206,7 +206,7 @@ def product_prefix(pk, case: dict, partition: int, shared: bool = True, private_
     tables, lens_out = bm.export(np.arange(nseq), maxb)
     assert np.array_equal(lens_out, lens)
     stats = bm.stats()
-    out = gpu_decode(pk, pool, to_dev(case["q"]), tables, lens, case["scale"], partition)
+    out = gpu_decode(pk, pool, to_dev(case["q"]), tables, lens, case["scale"], schedule)
     torch.cuda.synchronize()
     return dict(out=to_host(out), tables=tables, cows=np.concatenate(all_cows) if all_cows else None,
                 stats=stats, pool=pool, lens=lens, kpool=kpool, vpool=vpool, bm=bm)

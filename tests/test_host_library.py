@@ -149,22 +149,68 @@ def test_block_manager_errors():
         bm.export([1, 42], 4)
 
 
-def test_decode_plan_layout():
-    plan = pk.decode_plan([0, 5, 600, 1000], 256)
-    assert (plan.num_items, plan.num_merges, plan.num_partials) == (9, 2, 7)
-    items = [tuple(r) for r in plan.items.tolist()]
-    assert items[:6] == [(2, 0, 3, 0), (2, 1, 3, 0), (3, 0, 4, 3), (3, 1, 4, 3), (3, 2, 4, 3), (3, 3, 4, 3)]
-    assert items[6:9] == [(2, 2, 3, 0), (1, 0, 1, -1), (0, 0, 1, -1)]
-    assert items[9:] == [(2, -1, 3, 0), (3, -1, 4, 3)]
-    whole = pk.decode_plan([3, 70000], 0)
-    assert (whole.num_partials, whole.num_merges) == (0, 0)
-    assert [tuple(r) for r in whole.items.tolist()] == [(1, 0, 1, -1), (0, 0, 1, -1)]
+def test_decode_plan_small_example():
+    """Lengths 0, 5, 600, 1000 (0, 1, 38, 63 tiles), 8 KV heads (two head
+    blocks), 6 workgroups: 204 job tiles, pieces of at most 34 tiles."""
+    plan = pk.decode_plan([0, 5, 600, 1000], 8, num_workgroups=6)
+    assert (plan.num_workgroups, plan.num_jobs, plan.num_merges, plan.num_records) == (6, 10, 24, 32)
+    jobs = plan.jobs()
+    assert sorted(map(tuple, jobs[:, :7].tolist())) == sorted([
+        (1, 0, 1, 0, 0, 1, -1), (1, 0, 1, 1, 0, 1, -1),
+        (2, 0, 19, 0, 0, 2, 0), (2, 0, 19, 1, 0, 2, 0), (2, 19, 19, 0, 1, 2, 0), (2, 19, 19, 1, 1, 2, 0),
+        (3, 0, 32, 0, 0, 2, 16), (3, 0, 32, 1, 0, 2, 16), (3, 32, 31, 0, 1, 2, 16), (3, 32, 31, 1, 1, 2, 16)])
+    offs = plan.job_offsets()
+    loads = [int(jobs[offs[w]:offs[w + 1], 2].sum()) for w in range(6)]
+    assert sorted(loads) == [32, 32, 32, 32, 38, 38]
+    merges = [tuple(m) for m in plan.merges().tolist()]
+    assert merges[:8] == [(0, g, 0, -1) for g in range(8)]
+    assert merges[8:16] == [(2, g, 2, 2 * g) for g in range(8)]
+    assert merges[16:] == [(3, g, 2, 16 + 2 * g) for g in range(8)]
+    assert pk.decode_workspace_bytes(plan, 32, 128) >= 32 * 4 * 130 * 4
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_decode_plan_covers_every_tile_once(seed):
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(0, 3000, size=int(rng.integers(1, 60)))
+    hkv = int(rng.choice([1, 3, 4, 8, 13]))
+    nwg = int(rng.integers(1, 900))
+    cap = int(rng.choice([0, 1, 5, 64]))
+    plan = pk.decode_plan(lens, hkv, num_workgroups=nwg, max_piece_tiles=cap)
+    jobs = plan.jobs()
+    hb = -(-hkv // 4)
+    covered = {}
+    for seq, t0, cnt, blk, part, parts, base, _ in jobs.tolist():
+        assert 1 <= cnt <= 64 and (cap == 0 or cnt <= cap)
+        for t in range(t0, t0 + cnt):
+            key = (seq, blk, t)
+            assert key not in covered
+            covered[key] = (part, parts, base)
+    for s, L in enumerate(lens):
+        tiles = -(-int(L) // 16)
+        for blk in range(hb):
+            for t in range(tiles):
+                assert (s, blk, t) in covered
+    assert len(covered) == sum(-(-int(L) // 16) for L in lens) * hb
+    offs = plan.job_offsets()
+    assert offs[0] == 0 and offs[-1] == plan.num_jobs and np.all(np.diff(offs) >= 0)
+    assert plan.num_workgroups <= nwg
+    if plan.num_jobs:
+        loads = [int(jobs[offs[w]:offs[w + 1], 2].sum()) for w in range(plan.num_workgroups)]
+        assert max(loads) <= np.ceil(sum(loads) / plan.num_workgroups) + jobs[:, 2].max()
+
+
+def test_decode_plan_errors():
     with pytest.raises(pk.PaError):
-        pk.decode_plan([1, 2], 24)
+        pk.decode_plan([1, -2], 8, num_workgroups=4)
     with pytest.raises(pk.PaError):
-        pk.decode_plan([1, -2], 32)
-    assert pk.decode_workspace_bytes(0, 32, 128) == 0
-    assert pk.decode_workspace_bytes(7, 32, 128) >= 7 * 32 * 130 * 4
+        pk.decode_plan([1, 2], 8, num_workgroups=4, max_piece_tiles=65)
+    with pytest.raises(pk.PaError):
+        pk.decode_plan([1, 2], 0, num_workgroups=4)
+    with pytest.raises(pk.PaError):
+        pk.decode_plan([1, 2], 8, num_workgroups=0)
+    empty = pk.decode_plan([], 8, num_workgroups=4)
+    assert (empty.num_jobs, empty.num_merges, empty.num_records) == (0, 0, 0)
 
 
 class _Pool(ctypes.Structure):
@@ -191,26 +237,32 @@ def test_abi_rejects_bad_decode_arguments_without_launching():
     pool = _pool()
     p = ctypes.c_void_p(0x40000)
     L = _lib.lib
+    plan = pk.decode_plan([100, 3000], 8, num_workgroups=4)
+    assert plan.num_records > 0
 
-    def call(**kw):
-        args = dict(q=p, out=p, out_dtype=0, tables=p, maxb=4, lens=p, nseq=2, hq=32, scale=0.1, items=p,
-                    nitems=2, nmerge=0, nparts=0, part=256, ws=None, wsb=0)
+    def call(info=None, **kw):
+        args = dict(q=p, out=p, out_dtype=0, tables=p, maxb=400, lens=p, nseq=2, hq=32, scale=0.1, plan=p,
+                    ws=None, wsb=0)
         args.update(kw)
         return L.pa_decode(ctypes.byref(pool), args["q"], args["out"], args["out_dtype"], args["tables"],
                            args["maxb"], args["lens"], args["nseq"], args["hq"], ctypes.c_float(args["scale"]),
-                           args["items"], args["nitems"], args["nmerge"], args["nparts"], args["part"], args["ws"],
-                           args["wsb"], None)
-    assert call(hq=30) == -1                    # not a multiple of Hkv
-    assert call(hq=8 * 17) == -2                # group of 17 > 16
-    assert call(out_dtype=7) == -2
-    assert call(part=24) == -1                  # not a multiple of 16
-    assert call(q=None) == -1
-    assert call(q=ctypes.c_void_p(0x40008)) == -1   # misaligned
-    assert call(nparts=3) == -1                 # merges and records disagree
-    assert call(nparts=3, nmerge=1) == -1       # workspace missing
-    assert call(nparts=3, nmerge=1, ws=ctypes.c_void_p(0x50000), wsb=16) == -1   # too small
-    assert call(scale=float("inf")) == -1
-    assert call(nitems=0) == 0                  # nothing to do: OK, no launch
+                           args["plan"], ctypes.byref(info or plan.info), args["ws"], args["wsb"], None)
+    ws = dict(ws=ctypes.c_void_p(0x50000), wsb=1 << 30)
+    assert call(hq=30, **ws) == -1                  # not a multiple of Hkv
+    assert call(hq=8 * 17, **ws) == -2              # group of 17 > 16
+    assert call(out_dtype=7, **ws) == -2
+    assert call(q=None, **ws) == -1
+    assert call(q=ctypes.c_void_p(0x40008), **ws) == -1   # misaligned
+    assert call() == -1                             # workspace missing
+    assert call(ws=ctypes.c_void_p(0x50000), wsb=16) == -1   # too small
+    assert call(scale=float("inf"), **ws) == -1
+    other = pk.decode_plan([100, 3000], 4, num_workgroups=4)
+    assert call(info=other.info, **ws) == -1        # plan made for another head count
+    bad = _lib.PaDecodePlanInfo.from_buffer_copy(plan.info)
+    bad.jobs_at = 8
+    assert call(info=bad, **ws) == -1               # inconsistent layout
+    empty = pk.decode_plan([], 8, num_workgroups=4)
+    assert call(info=empty.info) == 0               # nothing to do: OK, no launch
     pool32 = _pool(dtype=0, d=64)
-    assert L.pa_decode(ctypes.byref(pool32), p, p, 1, p, 4, p, 2, 8, ctypes.c_float(1.0), p, 1, 0, 0, 0, None, 0,
-                       None) == -2              # bf16 output from an f32 pool
+    assert L.pa_decode(ctypes.byref(pool32), p, p, 1, p, 400, p, 2, 8, ctypes.c_float(1.0), p,
+                       ctypes.byref(plan.info), ws["ws"], ws["wsb"], None) == -2   # bf16 output, f32 pool
