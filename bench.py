@@ -17,8 +17,11 @@ times the 256 MB last-level cache) rotate so that KV reads come from HBM.
 
 Prints one JSON line.  `value` is KV-read GB/s over whole steps: algorithmic KV
 bytes (each live token's K and V row of each KV head, read once) per step
-divided by the step time.  `roofline` reports the attention kernel alone,
-timed per launch with HIP events on the stream it runs on.
+divided by the step time.  `roofline` reports the attention kernel alone: the
+same algorithmic bytes over its average launch time, from HIP events on the
+stream the launches run on around K back-to-back attention launches (a second
+timed region after the steps; pa_decode is issued as its two launches,
+pa_decode_attention and pa_decode_merge_pieces, for this).
 """
 from __future__ import annotations
 
@@ -90,6 +93,29 @@ def cpu_baseline(case, k_host, v_host, tables, lens, budget_s: float):
             "seconds": round(dt, 3), "seqs_per_s": round(done / dt, 3)}
 
 
+def copy_probe(torch, nbytes: int) -> int:
+    """Device-to-device copy of nbytes (read nbytes, write nbytes): the
+    runtime's copy kernel, timed, so that a counter run over this command
+    gives the reading of a transfer of known size."""
+    torch.cuda.set_device(0)
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 10
+    start.record()
+    for _ in range(reps):
+        b.copy_(a)
+    end.record()
+    torch.cuda.synchronize()
+    us = start.elapsed_time(end) / reps * 1e3
+    print(json.dumps({"copy_bytes": a.numel() * 4, "calls": reps + 3, "us": round(us, 2),
+                      "read_plus_write_GBs": round(2 * a.numel() * 4 / us / 1e3, 1)}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -102,6 +128,9 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-only", action="store_true", help="time only pa_decode launches (profiling aid)")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="profiling aid: run a plain device-to-device copy of BYTES (the reference whose "
+                         "counter readings calibrate the traffic figures) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -109,6 +138,8 @@ def main() -> int:
         return 2
 
     import torch
+    if args.copy_probe:
+        return copy_probe(torch, args.copy_probe)
     import paged_kv_cache_115_amd as pk
 
     torch.cuda.set_device(0)
@@ -160,43 +191,47 @@ def main() -> int:
     out = torch.empty((S, hq, d), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
 
-    def step(r: int, ev=None):
+    def step(r: int):
         pool = pools[r]
         if not args.decode_only:
             pk.copy_blocks(pool, cows_d, stream)
             pk.reshape_and_cache(pool, new_k, new_v, slots_d, stream)
-        if ev is not None:
-            ev[0].record(stream)
         pk.decode(pool, q_d, tables_d, lens_d, case["scale"], plan, plan_d, ws, out, stream)
-        if ev is not None:
-            ev[1].record(stream)
+
+    def attention(r: int):
+        pk.decode(pools[r], q_d, tables_d, lens_d, case["scale"], plan, plan_d, ws, out, stream, stage="attention")
+
+    def decode_call(r: int):
+        pk.decode(pools[r], q_d, tables_d, lens_d, case["scale"], plan, plan_d, ws, out, stream)
+
+    def timed(fn, n: int) -> float:
+        """Milliseconds per call of n back-to-back calls, from HIP events
+        recorded on the launch stream, bracketed by synchronisation."""
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for k in range(n):
+            fn(k % R)
+        end.record(stream)
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / n
 
     for k in range(args.warmup):
         step(k % R)
     torch.cuda.synchronize()
 
-    # Timed region: K whole steps, bracketed by synchronisation.
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # The timed region: K whole steps.
+    ms_per_step = timed(step, args.steps)
+    # The dominant kernel alone: K attention launches back to back (same
+    # inputs, rotating pool replicas), then K whole pa_decode calls.
+    attention_us = timed(attention, args.steps) * 1e3
+    decode_us = timed(decode_call, args.steps) * 1e3
+    pk.decode(pools[0], q_d, tables_d, lens_d, case["scale"], plan, plan_d, ws, out, stream)   # leave a complete result
     torch.cuda.synchronize()
-    start.record(stream)
-    for k in range(args.steps):
-        step(k % R)
-    end.record(stream)
-    torch.cuda.synchronize()
-    ms_per_step = start.elapsed_time(end) / args.steps
-
-    # Same steps again with an event pair around every pa_decode call.
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for k in range(args.steps):
-        step(k % R, evs[k])
-    torch.cuda.synchronize()
-    dec_ms = np.array([a.elapsed_time(b) for a, b in evs])
-    decode_us = float(dec_ms.mean() * 1e3)
 
     kv_bytes = int(lens.astype(np.int64).sum()) * hkv * d * 2 * 2
     value = kv_bytes / (ms_per_step * 1e-3) / 1e9
-    achieved = kv_bytes / (decode_us * 1e-6) / 1e9
+    achieved = kv_bytes / (attention_us * 1e-6) / 1e9
     schedule = [int(workgroups), int(args.piece)]
     result = {
         "metric": "paged decode attention KV-read GB/s (% of HBM peak) and decode tokens/s, 1 GPU",
@@ -221,13 +256,13 @@ def main() -> int:
         "decode_tokens_per_s": round(S / (ms_per_step * 1e-3), 1),
         "kv_bytes_per_step": kv_bytes,
         "decode_call_us": round(decode_us, 3),
-        "decode_call_us_p10_p90": [round(float(np.percentile(dec_ms, 10)) * 1e3, 3),
-                                   round(float(np.percentile(dec_ms, 90)) * 1e3, 3)],
+        "attention_launch_us": round(attention_us, 3),
         "host_append_us": round(host_append_us, 2),
         "host_plan_us": round(host_plan_us, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(name, schedule),
-                     "kernel": "pa_decode (attention + merge launches)", "bytes_per_launch": kv_bytes},
+                     "kernel": "decode_bf16_kernel (the attention launch of pa_decode)",
+                     "bytes_per_launch": kv_bytes},
     }
     if not args.no_cpu_baseline:
         k_host = pools[0].k.cpu().view(torch.int16).numpy().view(np.uint16)

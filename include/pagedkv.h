@@ -210,6 +210,25 @@ pa_status pa_decode(const pa_kv_pool* pool, const void* q, void* out, int32_t ou
                     float scale, const void* plan, const pa_decode_plan_info* info,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/* The two launches of pa_decode as separate calls, with the same arguments
+ * and checks: pa_decode_attention writes the output of every sequence that
+ * is not cut and the records of cut ones; pa_decode_merge_pieces then writes the
+ * output of cut and empty sequences.  Issued in that order on one stream
+ * they equal pa_decode; between them the caller may record events (to time
+ * the attention launch alone) or enqueue other work that touches neither the
+ * output nor the workspace.  Either returns PA_OK without launching when its
+ * part of the plan is empty. */
+pa_status pa_decode_attention(const pa_kv_pool* pool, const void* q, void* out, int32_t out_dtype,
+                              const int32_t* block_tables, int32_t max_blocks_per_seq,
+                              const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                              float scale, const void* plan, const pa_decode_plan_info* info,
+                              void* workspace, size_t workspace_bytes, void* stream);
+pa_status pa_decode_merge_pieces(const pa_kv_pool* pool, const void* q, void* out, int32_t out_dtype,
+                                 const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                 const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                                 float scale, const void* plan, const pa_decode_plan_info* info,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---------------------------------------------------------------------------
  * Host block manager (plain C++ on the CPU; not thread-safe: one scheduler
  * thread owns an instance).  Tracks per-sequence block tables and lengths,

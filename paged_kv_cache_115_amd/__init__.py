@@ -126,6 +126,11 @@ class DecodePlan:
         return torch.from_numpy(self.blob.copy()).to(device)
 
 
+# Host buffer the plan is built in (grown on demand); each DecodePlan copies
+# its bytes out.
+_plan_buf = np.zeros(1 << 13, dtype=np.uint64).view(np.uint8)
+
+
 def default_workgroups() -> int:
     """Persistent decode workgroups filling the current device."""
     n = lib.pa_decode_default_workgroups()
@@ -142,15 +147,15 @@ def decode_plan(context_lens, num_kv_heads: int, num_workgroups: int | None = No
         num_workgroups = default_workgroups()
     info = PaDecodePlanInfo()
     p32 = lens.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
-    st = lib.pa_decode_plan(p32, lens.size, num_kv_heads, num_workgroups, max_piece_tiles, None, 0,
-                            ctypes.byref(info))
-    if st != 0 and info.bytes <= 0:
-        _check(st, "pa_decode_plan")
-    blob = np.zeros(max(info.bytes, 8) + 8, dtype=np.uint8)
-    off = (-blob.ctypes.data) % 8
-    buf = blob[off:off + max(info.bytes, 8)]
-    _check(lib.pa_decode_plan(p32, lens.size, num_kv_heads, num_workgroups, max_piece_tiles,
-                              ctypes.c_void_p(buf.ctypes.data), buf.size, ctypes.byref(info)), "pa_decode_plan")
+    global _plan_buf
+    for _ in range(2):
+        buf = _plan_buf
+        st = lib.pa_decode_plan(p32, lens.size, num_kv_heads, num_workgroups, max_piece_tiles,
+                                ctypes.c_void_p(buf.ctypes.data), buf.size, ctypes.byref(info))
+        if st == 0 or info.bytes <= buf.size:
+            break
+        _plan_buf = np.zeros(2 * info.bytes, dtype=np.uint64).view(np.uint8)   # 8-byte aligned
+    _check(st, "pa_decode_plan")
     return DecodePlan(buf[: info.bytes].copy(), info)
 
 
@@ -158,9 +163,14 @@ def decode_workspace_bytes(plan: DecodePlan, num_q_heads: int, head_dim: int) ->
     return int(lib.pa_decode_workspace_bytes(ctypes.byref(plan.info), num_q_heads, head_dim))
 
 
+_DECODE_STAGES = {"all": "pa_decode", "attention": "pa_decode_attention", "merge": "pa_decode_merge_pieces"}
+
+
 def decode(pool: KvPool, q, block_tables, context_lens, scale: float, plan: DecodePlan, plan_dev, workspace=None,
-           out=None, stream=None):
-    """pa_decode.  `plan_dev` is the device copy of plan.blob (uint8 tensor)."""
+           out=None, stream=None, stage: str = "all"):
+    """pa_decode (stage "all"), or one of its two launches: pa_decode_attention
+    ("attention") or pa_decode_merge_pieces ("merge").  `plan_dev` is the device copy
+    of plan.blob (uint8 tensor)."""
     import torch
     _dev(q, "q", pool.k.dtype)
     _dev(block_tables, "block_tables", torch.int32)
@@ -175,10 +185,11 @@ def decode(pool: KvPool, q, block_tables, context_lens, scale: float, plan: Deco
     if tuple(out.shape) != (s, hq, d):
         raise ValueError("out must be [S, Hq, D]")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib.pa_decode(ctypes.byref(pool.c), _ptr(q), _ptr(out), _dtype_code(out), _ptr(block_tables),
+    fn = _DECODE_STAGES[stage]
+    _check(getattr(lib, fn)(ctypes.byref(pool.c), _ptr(q), _ptr(out), _dtype_code(out), _ptr(block_tables),
                          block_tables.shape[1], _ptr(context_lens), s, hq, ctypes.c_float(scale), _ptr(plan_dev),
                          ctypes.byref(plan.info), None if workspace is None else _ptr(workspace), ws_bytes,
-                         _stream(stream)), "pa_decode")
+                         _stream(stream)), fn)
     return out
 
 

@@ -55,6 +55,9 @@ _p32 = ctypes.POINTER(ctypes.c_int32)
 _p64 = ctypes.POINTER(ctypes.c_int64)
 _pool = ctypes.POINTER(PaKvPool)
 
+_DECODE_ARGS = [_pool, _vp, _vp, _i32, _vp, _i32, _vp, _i32, _i32, ctypes.c_float, _vp,
+                ctypes.POINTER(PaDecodePlanInfo), _vp, _sz, _vp]
+
 # name: (restype, argtypes)
 SIGNATURES = {
     "pa_last_error": (ctypes.c_char_p, []),
@@ -63,8 +66,9 @@ SIGNATURES = {
     "pa_decode_default_workgroups": (_i32, []),
     "pa_decode_plan": (_i32, [_p32, _i32, _i32, _i32, _i32, _vp, _sz, ctypes.POINTER(PaDecodePlanInfo)]),
     "pa_decode_workspace_bytes": (_sz, [ctypes.POINTER(PaDecodePlanInfo), _i32, _i32]),
-    "pa_decode": (_i32, [_pool, _vp, _vp, _i32, _vp, _i32, _vp, _i32, _i32, ctypes.c_float, _vp,
-                         ctypes.POINTER(PaDecodePlanInfo), _vp, _sz, _vp]),
+    "pa_decode": (_i32, _DECODE_ARGS),
+    "pa_decode_attention": (_i32, _DECODE_ARGS),
+    "pa_decode_merge_pieces": (_i32, _DECODE_ARGS),
     "pa_bm_create": (_vp, [_i32, _i32, _p32]),
     "pa_bm_destroy": (None, [_vp]),
     "pa_bm_append": (_i32, [_vp, _i64, _i32, _p64, _p32, _p32]),

@@ -6,7 +6,6 @@
 
 #include <algorithm>
 #include <cstring>
-#include <queue>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -32,8 +31,6 @@ pa_status fail(pa_status st, const char* fmt, ...) {
 namespace {
 
 bool aligned(const void* p, size_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
-
-int32_t elem_bytes(int32_t dtype) { return dtype == PA_F32 ? 4 : 2; }
 
 pa_status check_pool(const pa_kv_pool* pool, const char* who) {
   if (!pool) return fail(PA_ERR_INVALID, "%s: pool is NULL", who);
@@ -143,8 +140,19 @@ extern "C" pa_status pa_decode_plan(const int32_t* context_lens, int32_t num_seq
   if (cap == 0) cap = std::min<int64_t>(64, std::max<int64_t>(4, (total + num_workgroups - 1) / num_workgroups));
 
   // Pieces: each sequence's tiles in near-equal runs of at most `cap`.
+  size_t njobs = 0, nmerges = 0;
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    const int64_t tiles = ((int64_t)context_lens[s] + 15) / 16;
+    const int64_t parts = (tiles + cap - 1) / cap;
+    njobs += (size_t)(parts * head_blocks);
+    nmerges += (parts != 1) ? (size_t)num_kv_heads : 0;
+  }
+  if (njobs > (size_t)INT32_MAX / 64 || nmerges > (size_t)INT32_MAX / 64)
+    return fail(PA_ERR_INVALID, "pa_decode_plan: plan too large");
   std::vector<pa_decode_job> jobs;
   std::vector<pa_decode_merge> merges;
+  jobs.reserve(njobs);
+  merges.reserve(nmerges);
   int64_t records = 0;
   for (int32_t s = 0; s < num_seqs; ++s) {
     const int64_t tiles = ((int64_t)context_lens[s] + 15) / 16;
@@ -168,27 +176,51 @@ extern "C" pa_status pa_decode_plan(const int32_t* context_lens, int32_t num_seq
       t0 += cnt;
     }
   }
-  if (records > INT32_MAX / 1024 || jobs.size() > (size_t)INT32_MAX / 64)
-    return fail(PA_ERR_INVALID, "pa_decode_plan: plan too large");
+  if (records > INT32_MAX / 1024) return fail(PA_ERR_INVALID, "pa_decode_plan: plan too large");
 
   // Longest processing time first: each job, largest first, goes to the
-  // least-loaded workgroup (ties: lowest index).  Jobs keep sequence order
-  // inside a workgroup.
+  // least-loaded workgroup.  Jobs keep sequence order inside a workgroup.
   const int32_t nwg = (int32_t)std::min<int64_t>(num_workgroups, std::max<size_t>(jobs.size(), 1));
+  // Jobs by tile count, largest first, ties in generation order (a counting
+  // sort: counts are 1..cap).
   std::vector<int32_t> order(jobs.size());
-  for (size_t i = 0; i < order.size(); ++i) order[i] = (int32_t)i;
-  std::stable_sort(order.begin(), order.end(),
-                   [&](int32_t x, int32_t y) { return jobs[x].tile_count > jobs[y].tile_count; });
-  using Load = std::pair<int64_t, int32_t>;
-  std::priority_queue<Load, std::vector<Load>, std::greater<Load>> heap;
-  for (int32_t w = 0; w < nwg; ++w) heap.push(Load{0, w});
+  int64_t job_tiles = 0;
+  {
+    std::vector<int32_t> start(cap + 2, 0);
+    for (const pa_decode_job& j : jobs) {
+      start[cap - j.tile_count + 1] += 1;
+      job_tiles += j.tile_count;
+    }
+    for (int64_t c = 1; c <= cap + 1; ++c) start[c] += start[c - 1];
+    for (size_t i = 0; i < jobs.size(); ++i) order[start[cap - jobs[i].tile_count]++] = (int32_t)i;
+  }
+  // Least-loaded workgroup by a bucket queue over load values: loads only
+  // grow, so the smallest non-empty bucket is found by a pointer that only
+  // moves forward.  Workgroups of equal load leave in arrival order
+  // (initially by index).  A workgroup is chosen at a load no larger than
+  // job_tiles / nwg, so no load exceeds that plus one job.
   std::vector<int32_t> owner(jobs.size());
-  for (int32_t j : order) {
-    Load l = heap.top();
-    heap.pop();
-    owner[j] = l.second;
-    l.first += jobs[j].tile_count;
-    heap.push(l);
+  {
+    const int64_t max_load = job_tiles / nwg + cap + 1;
+    std::vector<int32_t> head(max_load + 1, -1), tail(max_load + 1, -1), next(nwg, -1);
+    for (int32_t w = 0; w + 1 < nwg; ++w) next[w] = w + 1;
+    head[0] = 0;
+    tail[0] = nwg - 1;
+    int64_t cur = 0;
+    for (int32_t j : order) {
+      while (head[cur] < 0) ++cur;
+      const int32_t w = head[cur];
+      head[cur] = next[w];
+      if (head[cur] < 0) tail[cur] = -1;
+      owner[j] = w;
+      const int64_t nl = cur + jobs[j].tile_count;
+      next[w] = -1;
+      if (tail[nl] < 0)
+        head[nl] = w;
+      else
+        next[tail[nl]] = w;
+      tail[nl] = w;
+    }
   }
   std::vector<int32_t> offsets(nwg + 1, 0);
   for (int32_t o : owner) offsets[o + 1] += 1;
@@ -227,45 +259,52 @@ extern "C" size_t pa_decode_workspace_bytes(const pa_decode_plan_info* info, int
   return pagedkv::layout((int64_t)info->num_records * group, head_dim).total;
 }
 
-extern "C" pa_status pa_decode(const pa_kv_pool* pool, const void* q, void* out, int32_t out_dtype,
-                               const int32_t* block_tables, int32_t max_blocks_per_seq,
-                               const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
-                               float scale, const void* plan, const pa_decode_plan_info* info,
-                               void* workspace, size_t workspace_bytes, void* stream) {
-  if (pa_status st = pagedkv::check_pool(pool, "pa_decode")) return st;
-  if (!info) return fail(PA_ERR_INVALID, "pa_decode: info is NULL");
+namespace {
+
+constexpr int kStageAttention = 1;
+constexpr int kStageMerge = 2;
+
+// Shared front of pa_decode and its two stages: validation, then the
+// launches the stage mask selects.  `who` names the entry point in errors.
+pa_status decode_stages(int stages, const char* who, const pa_kv_pool* pool, const void* q, void* out,
+                        int32_t out_dtype, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                        const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads, float scale,
+                        const void* plan, const pa_decode_plan_info* info, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  if (pa_status st = pagedkv::check_pool(pool, who)) return st;
+  if (!info) return fail(PA_ERR_INVALID, "%s: info is NULL", who);
   if (num_seqs < 0 || max_blocks_per_seq < 0 || info->num_workgroups < 0 || info->num_jobs < 0 ||
       info->num_merges < 0 || info->num_records < 0)
-    return fail(PA_ERR_INVALID, "pa_decode: negative size");
+    return fail(PA_ERR_INVALID, "%s: negative size", who);
   if (info->num_jobs == 0 && info->num_merges == 0) return PA_OK;
-  if (num_seqs == 0) return fail(PA_ERR_INVALID, "pa_decode: a plan with work but num_seqs == 0");
+  if (num_seqs == 0) return fail(PA_ERR_INVALID, "%s: a plan with work but num_seqs == 0", who);
   if (!q || !out || !block_tables || !context_lens || !plan)
-    return fail(PA_ERR_INVALID, "pa_decode: NULL q/out/block_tables/context_lens/plan");
-  if (max_blocks_per_seq == 0) return fail(PA_ERR_INVALID, "pa_decode: max_blocks_per_seq == 0");
+    return fail(PA_ERR_INVALID, "%s: NULL q/out/block_tables/context_lens/plan", who);
+  if (max_blocks_per_seq == 0) return fail(PA_ERR_INVALID, "%s: max_blocks_per_seq == 0", who);
   const int32_t hkv = pool->num_kv_heads;
   if (info->num_kv_heads != hkv)
-    return fail(PA_ERR_INVALID, "pa_decode: plan made for %d KV heads, pool has %d", info->num_kv_heads, hkv);
+    return fail(PA_ERR_INVALID, "%s: plan made for %d KV heads, pool has %d", who, info->num_kv_heads, hkv);
   if (num_q_heads <= 0 || num_q_heads % hkv != 0)
-    return fail(PA_ERR_INVALID, "pa_decode: num_q_heads %d is not a multiple of num_kv_heads %d",
+    return fail(PA_ERR_INVALID, "%s: num_q_heads %d is not a multiple of num_kv_heads %d", who,
                 num_q_heads, hkv);
   const int32_t group = num_q_heads / hkv;
-  if (group > 16) return fail(PA_ERR_UNSUPPORTED, "pa_decode: %d query heads per KV head (max 16)", group);
+  if (group > 16) return fail(PA_ERR_UNSUPPORTED, "%s: %d query heads per KV head (max 16)", who, group);
   if (out_dtype != PA_F32 && out_dtype != pool->dtype)
-    return fail(PA_ERR_UNSUPPORTED, "pa_decode: out_dtype %d must be f32 or the pool dtype", out_dtype);
+    return fail(PA_ERR_UNSUPPORTED, "%s: out_dtype %d must be f32 or the pool dtype", who, out_dtype);
   if (!pagedkv::aligned(q, 16) || !pagedkv::aligned(out, 16) || !pagedkv::aligned(plan, 32))
-    return fail(PA_ERR_INVALID, "pa_decode: q/out must be 16-byte and plan 32-byte aligned");
-  if (!std::isfinite(scale)) return fail(PA_ERR_INVALID, "pa_decode: scale is not finite");
+    return fail(PA_ERR_INVALID, "%s: q/out must be 16-byte and plan 32-byte aligned", who);
+  if (!std::isfinite(scale)) return fail(PA_ERR_INVALID, "%s: scale is not finite", who);
   if (info->jobs_at % 32 != 0 || info->merges_at % 16 != 0 || info->offsets_at != 0 ||
       (int64_t)info->jobs_at < 4 * ((int64_t)info->num_workgroups + 1) ||
       (int64_t)info->merges_at < (int64_t)info->jobs_at + 32 * (int64_t)info->num_jobs ||
       (int64_t)info->bytes < (int64_t)info->merges_at + 16 * (int64_t)info->num_merges)
-    return fail(PA_ERR_INVALID, "pa_decode: inconsistent plan info");
+    return fail(PA_ERR_INVALID, "%s: inconsistent plan info", who);
   const auto lay = pagedkv::layout((int64_t)info->num_records * group, pool->head_dim);
   if (info->num_records > 0) {
-    if (!workspace) return fail(PA_ERR_INVALID, "pa_decode: workspace is NULL but the plan has records");
-    if (!pagedkv::aligned(workspace, 256)) return fail(PA_ERR_INVALID, "pa_decode: workspace not 256-byte aligned");
+    if (!workspace) return fail(PA_ERR_INVALID, "%s: workspace is NULL but the plan has records", who);
+    if (!pagedkv::aligned(workspace, 256)) return fail(PA_ERR_INVALID, "%s: workspace not 256-byte aligned", who);
     if (workspace_bytes < lay.total)
-      return fail(PA_ERR_INVALID, "pa_decode: workspace %zu bytes < %zu needed", workspace_bytes, lay.total);
+      return fail(PA_ERR_INVALID, "%s: workspace %zu bytes < %zu needed", who, workspace_bytes, lay.total);
   }
   pagedkv::DecodeArgs a{};
   a.k = pool->k;
@@ -295,7 +334,33 @@ extern "C" pa_status pa_decode(const pa_kv_pool* pool, const void* q, void* out,
   a.num_records = info->num_records;
   a.out_bf16 = out_dtype == PA_BF16;
   a.scale_log2e = scale * 1.4426950408889634f;
-  const hipError_t e = pool->dtype == PA_BF16 ? pagedkv::launch_decode_bf16(a, (hipStream_t)stream)
-                                              : pagedkv::launch_decode_f32(a, (hipStream_t)stream);
-  return pagedkv::hip_status(e, "pa_decode");
+  a.bf16 = pool->dtype == PA_BF16;
+  if (stages & kStageAttention) {
+    if (pa_status st = pagedkv::hip_status(pagedkv::launch_decode_attention(a, (hipStream_t)stream), who)) return st;
+  }
+  if (stages & kStageMerge) return pagedkv::hip_status(pagedkv::launch_decode_merge(a, (hipStream_t)stream), who);
+  return PA_OK;
+}
+
+}  // namespace
+
+#define PA_DECODE_ARGS                                                                                   \
+  const pa_kv_pool *pool, const void *q, void *out, int32_t out_dtype, const int32_t *block_tables,      \
+      int32_t max_blocks_per_seq, const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,    \
+      float scale, const void *plan, const pa_decode_plan_info *info, void *workspace,                   \
+      size_t workspace_bytes, void *stream
+#define PA_DECODE_PASS                                                                                   \
+  pool, q, out, out_dtype, block_tables, max_blocks_per_seq, context_lens, num_seqs, num_q_heads, scale, \
+      plan, info, workspace, workspace_bytes, stream
+
+extern "C" pa_status pa_decode(PA_DECODE_ARGS) {
+  return decode_stages(kStageAttention | kStageMerge, "pa_decode", PA_DECODE_PASS);
+}
+
+extern "C" pa_status pa_decode_attention(PA_DECODE_ARGS) {
+  return decode_stages(kStageAttention, "pa_decode_attention", PA_DECODE_PASS);
+}
+
+extern "C" pa_status pa_decode_merge_pieces(PA_DECODE_ARGS) {
+  return decode_stages(kStageMerge, "pa_decode_merge_pieces", PA_DECODE_PASS);
 }

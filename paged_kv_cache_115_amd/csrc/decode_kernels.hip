@@ -62,8 +62,7 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 constexpr int kNW = 4;          // wavefronts per workgroup = KV heads per job
 constexpr int kTile = 16;       // tokens per tile (MFMA rows)
 constexpr int kMaxTiles = 64;   // tiles per job: one table entry per lane
-constexpr int kMergeThreads = 256;
-constexpr int kMergeChunk = 512;  // (piece, head) pairs staged in LDS at a time
+constexpr int kMaxMergeThreads = 16 * 128 / 2;  // merge block: G * head_dim / 2 threads
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -470,103 +469,87 @@ __global__ __launch_bounds__(kNW * 64) void decode_f32_kernel(DecodeArgs a) {
 // --------------------------------------------------------------------------
 // Merge: for every (sequence, KV head) cut into pieces, combine the piece
 // records in piece order,
-//   M = max_p m_p,  out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p,
-// staging (m, l) in LDS a chunk of pieces at a time (the running numerator
-// and denominator are rescaled when a later chunk raises the maximum).
-// An empty sequence (num_parts == 0) gets zeros.
+//   M = max_p m_p,  out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p.
+// One workgroup per row with G * D / 2 threads: thread t owns the two
+// adjacent outputs 2t, 2t + 1 (head 2t / D).  Pieces are taken eight at a
+// time, all of their loads issued together, and the running numerator and
+// denominator are rescaled when a later group raises the maximum.  An empty
+// sequence (num_parts == 0) gets zeros.
 // --------------------------------------------------------------------------
+__device__ __forceinline__ void store2(const DecodeArgs& a, int64_t idx, float x0, float x1) {
+  if (a.out_bf16)
+    *reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(a.out) + idx) = bf16_rne(x0) | (bf16_rne(x1) << 16);
+  else
+    *reinterpret_cast<float2*>(reinterpret_cast<float*>(a.out) + idx) = make_float2(x0, x1);
+}
+
 template <int D>
-__global__ __launch_bounds__(kMergeThreads) void merge_partials_kernel(DecodeArgs a) {
-  constexpr int kPer = 16 * D / kMergeThreads;  // output elements per thread at most
-  __shared__ float2 s_ml[kMergeChunk];
+__global__ __launch_bounds__(kMaxMergeThreads) void merge_partials_kernel(DecodeArgs a) {
+  constexpr int kBatch = 8;
   const pa_decode_merge mg = a.merges[blockIdx.x];
   if (mg.seq < 0 || mg.seq >= a.num_seqs || mg.kv_head < 0 || mg.kv_head >= a.num_kv_heads) return;
   const int G = a.group;
-  const int n = G * D;
-  const int64_t out_base = ((int64_t)mg.seq * a.num_q_heads + (int64_t)mg.kv_head * G) * D;
-  if (mg.num_parts <= 0) {
-    for (int e = threadIdx.x; e < n; e += kMergeThreads) store1(a, out_base + e, 0.f);
+  const int e = 2 * (int)threadIdx.x;
+  if (e >= G * D) return;
+  const int h = e / D;
+  const int d = e - h * D;
+  const int64_t out_idx = ((int64_t)mg.seq * a.num_q_heads + (int64_t)mg.kv_head * G) * D + e;
+  const int np = mg.num_parts;
+  if (np <= 0) {
+    store2(a, out_idx, 0.f, 0.f);
     return;
   }
-  if (mg.record_base < 0 || (int64_t)mg.record_base + mg.num_parts > a.num_records) return;
-  float M[kPer], num[kPer], den[kPer];
+  if (mg.record_base < 0 || (int64_t)mg.record_base + np > a.num_records) return;
+  const float2* ml_all = reinterpret_cast<const float2*>(a.partial_ml);
+  float M = -INFINITY, n0 = 0.f, n1 = 0.f, den = 0.f;
+  for (int p0 = 0; p0 < np; p0 += kBatch) {
+    float2 ml[kBatch], ov[kBatch];
 #pragma unroll
-  for (int k = 0; k < kPer; ++k) {
-    M[k] = -INFINITY;
-    num[k] = 0.f;
-    den[k] = 0.f;
-  }
-  const int chunk = kMergeChunk / G;
-  for (int p0 = 0; p0 < mg.num_parts; p0 += chunk) {
-    const int pc = min(chunk, mg.num_parts - p0);
-    __syncthreads();
-    for (int i = threadIdx.x; i < pc * G; i += kMergeThreads) {
-      const int64_t rec = (int64_t)(mg.record_base + p0 + i / G) * G + i % G;
-      s_ml[i] = *reinterpret_cast<const float2*>(a.partial_ml + 2 * rec);
+    for (int i = 0; i < kBatch; ++i) {
+      // Past the last piece, reload the last one (same cache line) so every
+      // load is issued unconditionally; the values are not used.
+      const int64_t rec = (int64_t)(mg.record_base + min(p0 + i, np - 1)) * G + h;
+      ml[i] = ml_all[rec];
+      ov[i] = *reinterpret_cast<const float2*>(a.partial_o + rec * D + d);
     }
-    __syncthreads();
+    float mc = M;
 #pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      const int e = threadIdx.x + k * kMergeThreads;
-      if (e >= n) break;
-      const int h = e / D;
-      const int d = e - h * D;
-      float mc = -INFINITY;
-      for (int p = 0; p < pc; ++p) mc = fmaxf(mc, s_ml[p * G + h].x);
-      const float mn = fmaxf(M[k], mc);
-      if (mn != -INFINITY) {
-        const float rescale = M[k] == -INFINITY ? 0.f : fast_exp2(M[k] - mn);
-        num[k] *= rescale;
-        den[k] *= rescale;
-        M[k] = mn;
-#pragma unroll 4
-        for (int p = 0; p < pc; ++p) {
-          const float2 ml = s_ml[p * G + h];
-          const float f = fast_exp2(ml.x - mn);
-          den[k] += f * ml.y;
-          num[k] += f * a.partial_o[((int64_t)(mg.record_base + p0 + p) * G + h) * D + d];
-        }
+    for (int i = 0; i < kBatch; ++i)
+      if (p0 + i < np) mc = fmaxf(mc, ml[i].x);
+    if (mc == -INFINITY) continue;
+    const float r = fast_exp2(M - mc);  // 0 while M is still -inf
+    n0 *= r;
+    n1 *= r;
+    den *= r;
+    M = mc;
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      if (p0 + i < np) {
+        const float f = fast_exp2(ml[i].x - M);
+        den += f * ml[i].y;
+        n0 += f * ov[i].x;
+        n1 += f * ov[i].y;
       }
     }
   }
-#pragma unroll
-  for (int k = 0; k < kPer; ++k) {
-    const int e = threadIdx.x + k * kMergeThreads;
-    if (e >= n) break;
-    store1(a, out_base + e, den[k] > 0.f ? num[k] / den[k] : 0.f);
-  }
-}
-
-hipError_t launch_merge(const DecodeArgs& a, hipStream_t stream) {
-  if (a.num_merges == 0) return hipSuccess;
-  if (a.head_dim == 128)
-    hipLaunchKernelGGL(merge_partials_kernel<128>, dim3(a.num_merges), dim3(kMergeThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL(merge_partials_kernel<64>, dim3(a.num_merges), dim3(kMergeThreads), 0, stream, a);
-  return hipGetLastError();
+  const float inv = den > 0.f ? 1.0f / den : 0.f;
+  store2(a, out_idx, n0 * inv, n1 * inv);
 }
 
 }  // namespace
 
-hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream) {
-  if (a.num_workgroups > 0 && a.num_jobs > 0) {
-    const dim3 grid((unsigned)a.num_workgroups);
+hipError_t launch_decode_attention(const DecodeArgs& a, hipStream_t stream) {
+  if (a.num_workgroups <= 0 || a.num_jobs <= 0) return hipSuccess;
+  const dim3 grid((unsigned)a.num_workgroups);
+  bool launched = false;
+  if (a.bf16) {
     switch (a.block_size) {
-      case 8: hipLaunchKernelGGL(decode_bf16_kernel<8>, grid, dim3(kNW * 64), 0, stream, a); break;
-      case 16: hipLaunchKernelGGL(decode_bf16_kernel<16>, grid, dim3(kNW * 64), 0, stream, a); break;
-      case 32: hipLaunchKernelGGL(decode_bf16_kernel<32>, grid, dim3(kNW * 64), 0, stream, a); break;
-      default: return hipErrorInvalidValue;
+      case 8: hipLaunchKernelGGL(decode_bf16_kernel<8>, grid, dim3(kNW * 64), 0, stream, a); launched = true; break;
+      case 16: hipLaunchKernelGGL(decode_bf16_kernel<16>, grid, dim3(kNW * 64), 0, stream, a); launched = true; break;
+      case 32: hipLaunchKernelGGL(decode_bf16_kernel<32>, grid, dim3(kNW * 64), 0, stream, a); launched = true; break;
+      default: break;
     }
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  return launch_merge(a, stream);
-}
-
-hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t stream) {
-  if (a.num_workgroups > 0 && a.num_jobs > 0) {
-    const dim3 grid((unsigned)a.num_workgroups);
-    bool launched = false;
+  } else {
 #define PA_F32_CASE(BS, DD)                                                                  \
   if (!launched && a.block_size == BS && a.head_dim == DD) {                                 \
     hipLaunchKernelGGL((decode_f32_kernel<BS, DD>), grid, dim3(kNW * 64), 0, stream, a);     \
@@ -579,11 +562,19 @@ hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t stream) {
     PA_F32_CASE(16, 128)
     PA_F32_CASE(32, 128)
 #undef PA_F32_CASE
-    if (!launched) return hipErrorInvalidValue;
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
   }
-  return launch_merge(a, stream);
+  if (!launched) return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t stream) {
+  if (a.num_merges == 0) return hipSuccess;
+  const dim3 block((unsigned)(a.group * a.head_dim / 2));
+  if (a.head_dim == 128)
+    hipLaunchKernelGGL(merge_partials_kernel<128>, dim3(a.num_merges), block, 0, stream, a);
+  else
+    hipLaunchKernelGGL(merge_partials_kernel<64>, dim3(a.num_merges), block, 0, stream, a);
+  return hipGetLastError();
 }
 
 hipError_t decode_resident_workgroups_per_cu(int* n) {

@@ -33,14 +33,16 @@ struct DecodeArgs {
   int32_t num_jobs;
   int32_t num_merges;
   int32_t num_records;
+  int32_t bf16;                  // pool dtype: 1 bfloat16, 0 float32
   int32_t out_bf16;              // 1: write bfloat16, 0: float32
   float scale_log2e;             // scale * log2(e)
 };
 
-// Attention launch (persistent grid of a.num_workgroups), then the merge
-// launch when a.num_merges > 0, both on `stream`.
-hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
-hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t stream);
+// Attention launch (persistent grid of a.num_workgroups; nothing when the
+// plan has no jobs) on `stream`.
+hipError_t launch_decode_attention(const DecodeArgs& a, hipStream_t stream);
+// Merge launch (one workgroup per merge row; nothing when a.num_merges == 0).
+hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t stream);
 // Resident decode workgroups per compute unit (occupancy of the bf16 kernel).
 hipError_t decode_resident_workgroups_per_cu(int* n);
 

@@ -12,7 +12,8 @@ import torch
 import oracle
 import synth
 
-from flows import (assert_close, bits, gpu_decode, oracle_decode_step, oracle_prefix, product_decode_step,
+from flows import (assert_close, bits, gpu_decode, oracle_decode_step, oracle_prefix, plan_and_workspace,
+                   product_decode_step,
                    product_prefix, to_dev, to_host)
 
 pytestmark = pytest.mark.gpu
@@ -106,6 +107,27 @@ def test_decode_is_deterministic_and_schedule_independent_within_tolerance(pk):
     assert np.array_equal(to_host(again), a["out"])
     b = product_decode_step(pk, case, DEFAULT)
     assert np.abs(a["out"] - b["out"]).max() < 2e-3
+
+
+def test_attention_then_merge_stages_equal_pa_decode(pk):
+    """pa_decode_attention followed by pa_decode_merge_pieces on one stream
+    writes bitwise what pa_decode writes (cut, uncut and empty sequences)."""
+    case = synth.decode_case("c3s")
+    a = product_decode_step(pk, case, SMALL_PIECES)
+    lens = a["lens"].copy()
+    lens[1] = 0          # an empty sequence: only the merge launch writes it
+    plan, plan_dev, ws = plan_and_workspace(pk, lens, a["pool"].k.shape[2], a["q_dev"].shape[1],
+                                            a["pool"].k.shape[3], *SMALL_PIECES)
+    assert plan.num_records > 0 and plan.num_merges > 0
+    args = (a["pool"], a["q_dev"], to_dev(a["tables"]), to_dev(lens), case["scale"], plan, plan_dev, ws)
+    whole = torch.full(tuple(a["q_dev"].shape), float("nan"), device="cuda")
+    pk.decode(*args, out=whole)
+    staged = torch.full(tuple(a["q_dev"].shape), float("nan"), device="cuda")
+    pk.decode(*args, out=staged, stage="attention")
+    pk.decode(*args, out=staged, stage="merge")
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(to_host(whole)), bits(to_host(staged)))
+    assert np.all(to_host(staged)[1] == 0)
 
 
 def test_physical_block_permutation_is_bitwise_invariant(pk):
