@@ -51,6 +51,8 @@ WORKLOADS = {
     "c2": "MHA decode bf16: batch 64, 32/32 heads, head_dim 128, block 16, lengths U[1,2048]",
     "c4": "long-context GQA decode bf16: batch 16, 64 q / 8 KV heads, head_dim 128, block 16, "
           "lengths U[16384,32768]",
+    "c5": "prefix sharing bf16: 32 prompts x 4 samples sharing a 2000-token prefix, private tails U[1,512], "
+          "32 q / 8 KV heads, head_dim 128; the step where the samples diverge",
 }
 PMC_FILE = os.path.join(ROOT, "profiles", "decode_c3_pmc.json")
 KERNEL_SRC = os.path.join(ROOT, "paged_kv_cache_115_amd", "csrc", "decode_kernels.hip")
@@ -72,13 +74,12 @@ def measured_traffic(config: str, schedule: list):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(case, k_host, v_host, tables, lens, budget_s: float):
+def cpu_baseline(case, per_token: int, k_host, v_host, tables, lens, budget_s: float):
     """The float64 oracle over the sequences of the same batch, in order and
     wrapping around, until about `budget_s` seconds of single-core work;
-    reported in the headline unit (KV GB/s) and as sequences per second."""
+    reported in the headline unit (KV GB/s, `per_token` bytes per context
+    token) and as sequences per second."""
     import oracle
-    cfg = case["cfg"]
-    per_token = cfg["num_kv_heads"] * cfg["head_dim"] * 2 * synth.element_bytes(cfg["dtype"])
     t0 = time.perf_counter()
     done, tokens = 0, 0
     while time.perf_counter() - t0 < budget_s:
@@ -91,6 +92,105 @@ def cpu_baseline(case, k_host, v_host, tables, lens, budget_s: float):
             "sample": f"float64 oracle, {done} sequence decodes cycling through the {len(lens)}-sequence batch "
                       f"({tokens} context tokens, {dt:.1f} s on one host core)",
             "seconds": round(dt, 3), "seqs_per_s": round(done / dt, 3)}
+
+
+def decode_workload(pk, name: str) -> dict:
+    """One decode step of a named workload: every sequence holds L - 1
+    tokens; the step appends one token to each (timed host append) and
+    attends over L."""
+    case = synth.decode_case(name)
+    cfg = case["cfg"]
+    lens_np = case["lengths"]
+    S, B = len(lens_np), cfg["block_size"]
+    bm = pk.BlockManager(case["num_blocks"], B, case["free_order"])
+    for s in range(S):
+        bm.append(s, int(lens_np[s]) - 1)
+    seqs = np.arange(S)
+    t0 = time.perf_counter()
+    slots, cows = bm.append_step(seqs)
+    host_append_us = (time.perf_counter() - t0) * 1e6
+    maxb = int(max(-(-int(L) // B) for L in lens_np))
+    tables, lens = bm.export(seqs, maxb)
+    return dict(name=name, desc=WORKLOADS[name], case=case, seed=cfg["seed"], S=S, hq=cfg["num_q_heads"],
+                hkv=cfg["num_kv_heads"], d=cfg["head_dim"], B=B, nb=case["num_blocks"], tables=tables, lens=lens,
+                slots=slots, cows=cows, host_append_us=host_append_us, unique_tokens=int(lens.sum()))
+
+
+def prefix_workload(pk, block_size: int) -> dict:
+    """The step at which shared-prefix samples diverge.  Each prompt's prefix
+    is written once and forked into its samples; every sample then holds its
+    private tail but the last token.  The step: pa_copy_blocks with the
+    copy-on-write pairs of the divergence (the shared partial block, once per
+    sample but the last), pa_reshape_and_cache of every sample's last tail
+    token, pa_decode over prefix + tail."""
+    case = synth.prefix_case("c5", block_size)
+    cfg = case["cfg"]
+    p, n, pre, tails = cfg["num_prompts"], cfg["samples"], cfg["prefix_len"], case["tail_lengths"]
+    B, nseq = block_size, p * n
+    bm = pk.BlockManager(case["num_blocks"], B, case["free_order"])
+    for i in range(p):
+        parent = 1_000_000 + i
+        bm.append(parent, pre)
+        for j in range(n):
+            bm.fork(parent, i * n + j)
+        bm.free(parent)
+    seqs = np.arange(nseq)
+    fork_slots, fork_cows = bm.append_step(seqs)          # first divergent token: copy-on-write
+    for s in range(nseq):
+        if tails[s] > 2:
+            bm.append(s, int(tails[s]) - 2)
+    t0 = time.perf_counter()
+    last = seqs[tails >= 2]
+    slots = np.full(nseq, -1, dtype=np.int64)
+    if last.size:
+        sl, cw = bm.append_step(last)
+        assert len(cw) == 0
+        slots[last] = sl
+    host_append_us = (time.perf_counter() - t0) * 1e6
+    slots[tails == 1] = fork_slots[tails == 1]
+    lens_np = (pre + tails).astype(np.int32)
+    maxb = int(max(-(-int(L) // B) for L in lens_np))
+    tables, lens = bm.export(seqs, maxb)
+    assert np.array_equal(lens, lens_np)
+    # Distinct (block, slot) pairs the step reads: shared prefix slots once.
+    used = {}
+    for s in range(nseq):
+        nblk = -(-int(lens[s]) // B)
+        for j, blk in enumerate(tables[s, :nblk]):
+            fill = B if j < nblk - 1 else int(lens[s]) - j * B
+            used[int(blk)] = max(used.get(int(blk), 0), fill)
+    q = case["q"]
+    return dict(name=f"c5 B={B}", desc=f"{WORKLOADS['c5']}, block {B}", case=dict(q=q, scale=case["scale"]),
+                seed=cfg["seed"] + B, S=nseq, hq=cfg["num_q_heads"], hkv=cfg["num_kv_heads"], d=cfg["head_dim"], B=B,
+                nb=case["num_blocks"], tables=tables, lens=lens, slots=slots,
+                cows=np.asarray(fork_cows, dtype=np.int32).reshape(-1, 2), host_append_us=host_append_us,
+                unique_tokens=int(sum(used.values())))
+
+
+def copy_blocks_probe(torch, pk, B: int, hkv: int, d: int, pairs: int = 4096, reps: int = 20) -> dict:
+    """pa_copy_blocks on `pairs` random disjoint (src, dst) pairs of a pool of
+    2 * pairs blocks, timed back to back; bytes = K and V, read and written."""
+    nb = 2 * pairs
+    dev = torch.device("cuda", 0)
+    kp = torch.zeros((nb, B, hkv, d), dtype=torch.bfloat16, device=dev)
+    vp = torch.zeros_like(kp)
+    pool = pk.KvPool(kp, vp)
+    perm = np.random.default_rng(9).permutation(nb).astype(np.int32)
+    pr = torch.from_numpy(np.stack([perm[:pairs], perm[pairs:]], axis=1).copy()).to(dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        pk.copy_blocks(pool, pr, stream)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(reps):
+        pk.copy_blocks(pool, pr, stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    us = start.elapsed_time(end) / reps * 1e3
+    nbytes = pairs * 2 * B * hkv * d * 2 * 2
+    return {"pairs": pairs, "block_size": B, "us": round(us, 2), "bytes": nbytes,
+            "GBs": round(nbytes / us / 1e3, 1), "pct_hbm_peak": round(100 * nbytes / us / 1e3 / HBM_PEAK_GBS, 2)}
 
 
 def copy_probe(torch, nbytes: int) -> int:
@@ -122,6 +222,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="c3", choices=sorted(WORKLOADS))
+    ap.add_argument("--block-size", type=int, default=16, choices=(8, 16, 32), help="block size of the c5 workload")
     ap.add_argument("--workgroups", type=int, default=None, help="persistent workgroups (default: fill the GPU)")
     ap.add_argument("--piece", type=int, default=0, help="longest job piece in 16-token tiles (0: auto)")
     ap.add_argument("--replicas", type=int, default=None)
@@ -143,23 +244,14 @@ def main() -> int:
     import paged_kv_cache_115_amd as pk
 
     torch.cuda.set_device(0)
-    name = args.config
-    case = synth.decode_case(name)
-    cfg = case["cfg"]
-    S, hq, hkv, d, B = len(case["lengths"]), cfg["num_q_heads"], cfg["num_kv_heads"], cfg["head_dim"], cfg["block_size"]
-    lens_np = case["lengths"]
-    nb = case["num_blocks"]
-
-    # Host block manager: prefill L-1 tokens, then this step's append.
-    bm = pk.BlockManager(nb, B, case["free_order"])
-    for s in range(S):
-        bm.append(s, int(lens_np[s]) - 1)
-    seqs = np.arange(S)
-    t0 = time.perf_counter()
-    slots, cows = bm.append_step(seqs)
-    host_append_us = (time.perf_counter() - t0) * 1e6
-    maxb = int(max(-(-int(L) // B) for L in lens_np))
-    tables, lens = bm.export(seqs, maxb)
+    if args.config == "c5":
+        w = prefix_workload(pk, args.block_size)
+    else:
+        w = decode_workload(pk, args.config)
+    name, case = w["name"], w["case"]
+    S, hq, hkv, d, B, nb = w["S"], w["hq"], w["hkv"], w["d"], w["B"], w["nb"]
+    tables, lens, slots, cows = w["tables"], w["lens"], w["slots"], w["cows"]
+    host_append_us = w["host_append_us"]
     workgroups = args.workgroups or pk.default_workgroups()
     t0 = time.perf_counter()
     plan = pk.decode_plan(lens, hkv, workgroups, args.piece)
@@ -180,12 +272,12 @@ def main() -> int:
     pools = []
     for r in range(R):
         g = torch.Generator(device=dev)
-        g.manual_seed(cfg["seed"] + 1000 * r)
+        g.manual_seed(w["seed"] + 1000 * r)
         kp = torch.randn((nb, B, hkv, d), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
         vp = torch.randn((nb, B, hkv, d), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
         pools.append(pk.KvPool(kp, vp))
     g = torch.Generator(device=dev)
-    g.manual_seed(cfg["seed"] + 7)
+    g.manual_seed(w["seed"] + 7)
     new_k = torch.randn((S, hkv, d), generator=g, device=dev).to(torch.bfloat16)
     new_v = torch.randn((S, hkv, d), generator=g, device=dev).to(torch.bfloat16)
     out = torch.empty((S, hq, d), dtype=torch.float32, device=dev)
@@ -229,7 +321,11 @@ def main() -> int:
     pk.decode(pools[0], q_d, tables_d, lens_d, case["scale"], plan, plan_d, ws, out, stream)   # leave a complete result
     torch.cuda.synchronize()
 
-    kv_bytes = int(lens.astype(np.int64).sum()) * hkv * d * 2 * 2
+    # Algorithmic KV bytes: every distinct (block, slot) the step reads, K and
+    # V of every KV head, once (equal to the logical bytes unless sequences
+    # share blocks).
+    kv_bytes = w["unique_tokens"] * hkv * d * 2 * 2
+    logical_kv_bytes = int(lens.astype(np.int64).sum()) * hkv * d * 2 * 2
     value = kv_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = kv_bytes / (attention_us * 1e-6) / 1e9
     schedule = [int(workgroups), int(args.piece)]
@@ -246,7 +342,7 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{name}: {WORKLOADS[name]}", "num_seqs": S, "num_q_heads": hq,
+        "config": {"workload": f"{name}: {w['desc']}", "num_seqs": S, "num_q_heads": hq,
                    "num_kv_heads": hkv, "head_dim": d, "block_size": B,
                    "total_context_tokens": int(lens.sum()), "max_context": int(lens.max()),
                    "workgroups": int(workgroups), "max_piece_tiles": int(args.piece),
@@ -255,6 +351,9 @@ def main() -> int:
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "decode_tokens_per_s": round(S / (ms_per_step * 1e-3), 1),
         "kv_bytes_per_step": kv_bytes,
+        "logical_kv_bytes_per_step": logical_kv_bytes,
+        "logical_kv_GBs": round(logical_kv_bytes / (ms_per_step * 1e-3) / 1e9, 2),
+        "copy_blocks_per_step": int(len(cows)),
         "decode_call_us": round(decode_us, 3),
         "attention_launch_us": round(attention_us, 3),
         "host_append_us": round(host_append_us, 2),
@@ -264,10 +363,12 @@ def main() -> int:
                      "kernel": "decode_bf16_kernel (the attention launch of pa_decode)",
                      "bytes_per_launch": kv_bytes},
     }
+    if not args.decode_only:
+        result["copy_blocks_probe"] = copy_blocks_probe(torch, pk, B, hkv, d)
     if not args.no_cpu_baseline:
         k_host = pools[0].k.cpu().view(torch.int16).numpy().view(np.uint16)
         v_host = pools[0].v.cpu().view(torch.int16).numpy().view(np.uint16)
-        result["cpu_baseline"] = cpu_baseline(case, k_host, v_host, tables, lens, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(case, hkv * d * 2 * 2, k_host, v_host, tables, lens, args.cpu_seconds)
     print(json.dumps(result), flush=True)
     return 0
 

@@ -24,6 +24,7 @@ cases), then queries.
 from __future__ import annotations
 
 import math
+import os
 
 import numpy as np
 
@@ -78,9 +79,35 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     return ((u + bias) >> np.uint32(16)).astype(np.uint16)
 
 
+_CHUNK = 1 << 22   # elements per independently seeded chunk of a normal draw
+
+
 def _normal(rng: np.random.Generator, shape, dtype: str) -> np.ndarray:
-    x = rng.standard_normal(size=shape, dtype=np.float32)
-    return x if dtype == "f32" else f32_to_bf16_bits(x)
+    """Standard normal float32 values (rounded to bfloat16 for "bf16").
+
+    The case generator draws one 64-bit seed; the array is filled in chunks of
+    _CHUNK elements, chunk i from its own generator spawned as child i of that
+    seed.  Chunks are independent, so they are filled in parallel threads and
+    the result does not depend on the thread count."""
+    n = int(np.prod(shape))
+    seed = int(rng.integers(0, 2**63))
+    nchunks = max(1, -(-n // _CHUNK))
+    children = np.random.SeedSequence(seed).spawn(nchunks)
+    out = np.empty(n, dtype=np.float32 if dtype == "f32" else np.uint16)
+
+    def fill(i: int) -> None:
+        lo, hi = i * _CHUNK, min(n, (i + 1) * _CHUNK)
+        x = np.random.default_rng(children[i]).standard_normal(size=hi - lo, dtype=np.float32)
+        out[lo:hi] = x if dtype == "f32" else f32_to_bf16_bits(x)
+
+    if nchunks == 1:
+        fill(0)
+    else:
+        from concurrent.futures import ThreadPoolExecutor
+        workers = min(nchunks, max(1, min(16, len(os.sched_getaffinity(0)))))
+        with ThreadPoolExecutor(max_workers=workers) as pool:
+            list(pool.map(fill, range(nchunks)))
+    return out.reshape(shape)
 
 
 def element_bytes(dtype: str) -> int:
