@@ -113,7 +113,8 @@ def decode_workload(pk, name: str) -> dict:
     tables, lens = bm.export(seqs, maxb)
     return dict(name=name, desc=WORKLOADS[name], case=case, seed=cfg["seed"], S=S, hq=cfg["num_q_heads"],
                 hkv=cfg["num_kv_heads"], d=cfg["head_dim"], B=B, nb=case["num_blocks"], tables=tables, lens=lens,
-                slots=slots, cows=cows, host_append_us=host_append_us, unique_tokens=int(lens.sum()))
+                slots=slots, cows=cows, host_append_us=host_append_us, unique_tokens=int(lens.sum()),
+                shared_kv=bm.stats()["shared_blocks"] > 0)
 
 
 def prefix_workload(pk, block_size: int) -> dict:
@@ -164,7 +165,7 @@ def prefix_workload(pk, block_size: int) -> dict:
                 seed=cfg["seed"] + B, S=nseq, hq=cfg["num_q_heads"], hkv=cfg["num_kv_heads"], d=cfg["head_dim"], B=B,
                 nb=case["num_blocks"], tables=tables, lens=lens, slots=slots,
                 cows=np.asarray(fork_cows, dtype=np.int32).reshape(-1, 2), host_append_us=host_append_us,
-                unique_tokens=int(sum(used.values())))
+                unique_tokens=int(sum(used.values())), shared_kv=bm.stats()["shared_blocks"] > 0)
 
 
 def copy_blocks_probe(torch, pk, B: int, hkv: int, d: int, pairs: int = 4096, reps: int = 20) -> dict:
@@ -254,7 +255,7 @@ def main() -> int:
     host_append_us = w["host_append_us"]
     workgroups = args.workgroups or pk.default_workgroups()
     t0 = time.perf_counter()
-    plan = pk.decode_plan(lens, hkv, workgroups, args.piece)
+    plan = pk.decode_plan(lens, hkv, workgroups, args.piece, shared_kv=w["shared_kv"])
     host_plan_us = (time.perf_counter() - t0) * 1e6
 
     dev = torch.device("cuda", 0)
@@ -347,7 +348,7 @@ def main() -> int:
                    "total_context_tokens": int(lens.sum()), "max_context": int(lens.max()),
                    "workgroups": int(workgroups), "max_piece_tiles": int(args.piece),
                    "jobs": int(plan.num_jobs), "merges": int(plan.num_merges), "records": int(plan.num_records),
-                   "pool_replicas": R, "decode_only": bool(args.decode_only)},
+                   "pool_replicas": R, "decode_only": bool(args.decode_only), "shared_kv": bool(w["shared_kv"])},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "decode_tokens_per_s": round(S / (ms_per_step * 1e-3), 1),
         "kv_bytes_per_step": kv_bytes,

@@ -157,7 +157,15 @@ typedef struct pa_decode_plan_info {
   int32_t jobs_at;        /* byte offset of pa_decode_job [num_jobs] */
   int32_t merges_at;      /* byte offset of pa_decode_merge [num_merges] */
   int32_t bytes;          /* total plan bytes */
+  int32_t flags;          /* PA_DECODE_* bits; pa_decode_plan sets 0, the caller may set them */
 } pa_decode_plan_info;
+
+/* flags bit: some physical blocks are named by more than one sequence of the
+ * batch (forked, shared prefixes; pa_bm_get_stats().shared_blocks > 0).  K/V
+ * loads then keep blocks in the caches for the other readers.  Without it
+ * every K/V byte is read once and the loads stream past the caches, which is
+ * faster when nothing is shared.  Either setting gives identical results. */
+#define PA_DECODE_SHARED_KV 1
 
 /* Persistent workgroups that fit the current device at full occupancy (all
  * resident at once): compute units times resident decode workgroups per unit.

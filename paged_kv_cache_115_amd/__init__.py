@@ -13,10 +13,10 @@ import os
 
 import numpy as np
 
-from ._lib import LIB_PATH, PA_BF16, PA_F32, PaDecodePlanInfo, PaError, PaKvPool, lib
+from ._lib import LIB_PATH, PA_BF16, PA_DECODE_SHARED_KV, PA_F32, PaDecodePlanInfo, PaError, PaKvPool, lib
 
 __all__ = [
-    "LIB_PATH", "PA_F32", "PA_BF16", "PaError", "BlockManager", "KvPool",
+    "LIB_PATH", "PA_F32", "PA_BF16", "PA_DECODE_SHARED_KV", "PaError", "BlockManager", "KvPool",
     "reshape_and_cache", "copy_blocks", "decode_plan", "decode_workspace_bytes",
     "decode", "DecodePlan", "default_workgroups",
 ]
@@ -140,8 +140,10 @@ def default_workgroups() -> int:
 
 
 def decode_plan(context_lens, num_kv_heads: int, num_workgroups: int | None = None,
-                max_piece_tiles: int = 0) -> DecodePlan:
-    """pa_decode_plan.  num_workgroups defaults to default_workgroups()."""
+                max_piece_tiles: int = 0, shared_kv: bool = False) -> DecodePlan:
+    """pa_decode_plan.  num_workgroups defaults to default_workgroups().
+    shared_kv sets PA_DECODE_SHARED_KV: pass True when sequences of the batch
+    share blocks (forked prefixes), so K/V loads keep them cached."""
     lens = np.ascontiguousarray(context_lens, dtype=np.int32)
     if num_workgroups is None:
         num_workgroups = default_workgroups()
@@ -156,6 +158,7 @@ def decode_plan(context_lens, num_kv_heads: int, num_workgroups: int | None = No
             break
         _plan_buf = np.zeros(2 * info.bytes, dtype=np.uint64).view(np.uint8)   # 8-byte aligned
     _check(st, "pa_decode_plan")
+    info.flags = PA_DECODE_SHARED_KV if shared_kv else 0
     return DecodePlan(buf[: info.bytes].copy(), info)
 
 

@@ -8,6 +8,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedkv.
 
 PA_F32 = 0
 PA_BF16 = 1
+PA_DECODE_SHARED_KV = 1
 
 
 class PaError(RuntimeError):
@@ -26,7 +27,8 @@ class PaDecodePlanInfo(ctypes.Structure):
     _fields_ = [("num_workgroups", ctypes.c_int32), ("num_jobs", ctypes.c_int32),
                 ("num_merges", ctypes.c_int32), ("num_records", ctypes.c_int32),
                 ("num_kv_heads", ctypes.c_int32), ("offsets_at", ctypes.c_int32),
-                ("jobs_at", ctypes.c_int32), ("merges_at", ctypes.c_int32), ("bytes", ctypes.c_int32)]
+                ("jobs_at", ctypes.c_int32), ("merges_at", ctypes.c_int32), ("bytes", ctypes.c_int32),
+                ("flags", ctypes.c_int32)]
 
 
 class PaBmStats(ctypes.Structure):

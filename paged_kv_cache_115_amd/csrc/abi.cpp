@@ -294,6 +294,7 @@ pa_status decode_stages(int stages, const char* who, const pa_kv_pool* pool, con
   if (!pagedkv::aligned(q, 16) || !pagedkv::aligned(out, 16) || !pagedkv::aligned(plan, 32))
     return fail(PA_ERR_INVALID, "%s: q/out must be 16-byte and plan 32-byte aligned", who);
   if (!std::isfinite(scale)) return fail(PA_ERR_INVALID, "%s: scale is not finite", who);
+  if (info->flags & ~PA_DECODE_SHARED_KV) return fail(PA_ERR_INVALID, "%s: unknown plan flags 0x%x", who, info->flags);
   if (info->jobs_at % 32 != 0 || info->merges_at % 16 != 0 || info->offsets_at != 0 ||
       (int64_t)info->jobs_at < 4 * ((int64_t)info->num_workgroups + 1) ||
       (int64_t)info->merges_at < (int64_t)info->jobs_at + 32 * (int64_t)info->num_jobs ||
@@ -335,6 +336,7 @@ pa_status decode_stages(int stages, const char* who, const pa_kv_pool* pool, con
   a.out_bf16 = out_dtype == PA_BF16;
   a.scale_log2e = scale * 1.4426950408889634f;
   a.bf16 = pool->dtype == PA_BF16;
+  a.shared_kv = (info->flags & PA_DECODE_SHARED_KV) != 0;
   if (stages & kStageAttention) {
     if (pa_status st = pagedkv::hip_status(pagedkv::launch_decode_attention(a, (hipStream_t)stream), who)) return st;
   }

@@ -31,9 +31,23 @@ __global__ __launch_bounds__(kThreads) void reshape_and_cache_kernel(
   }
 }
 
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// Streaming 16-byte moves: every byte is read once and written once, so both
+// sides are marked non-temporal.
+__device__ __forceinline__ u32x4_t load_stream(const uint4* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+}
+__device__ __forceinline__ void store_stream(uint4* p, u32x4_t v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(p));
+}
+
+constexpr int kCopyUnroll = 4;  // 16-byte vectors in flight per thread
+
 // Block pairs[2p+1] of both pools becomes a copy of block pairs[2p]
 // (aicassindra.com "tm_paged_attention_deep", "Copy-on-write for shared
-// prefixes").  grid = (pairs, 2 pools, chunks of 4 KiB).
+// prefixes").  grid = (pairs, 2 pools, chunks of kThreads * kCopyUnroll
+// vectors); each thread loads its kCopyUnroll vectors before storing them.
 __global__ __launch_bounds__(kThreads) void copy_blocks_kernel(
     uint4* __restrict__ kpool, uint4* __restrict__ vpool, const int32_t* __restrict__ pairs,
     int32_t num_blocks, int32_t block_vec) {
@@ -41,10 +55,18 @@ __global__ __launch_bounds__(kThreads) void copy_blocks_kernel(
   const int32_t dst = pairs[2 * blockIdx.x + 1];
   if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
   uint4* pool = blockIdx.y ? vpool : kpool;
-  const int64_t s0 = (int64_t)src * block_vec;
-  const int64_t d0 = (int64_t)dst * block_vec;
-  for (int32_t c = blockIdx.z * kThreads + threadIdx.x; c < block_vec; c += gridDim.z * kThreads)
-    pool[d0 + c] = pool[s0 + c];
+  const uint4* s0 = pool + (int64_t)src * block_vec;
+  uint4* d0 = pool + (int64_t)dst * block_vec;
+  constexpr int32_t kChunk = kThreads * kCopyUnroll;
+  for (int32_t c0 = blockIdx.z * kChunk + threadIdx.x; c0 < block_vec; c0 += gridDim.z * kChunk) {
+    u32x4_t v[kCopyUnroll];
+#pragma unroll
+    for (int i = 0; i < kCopyUnroll; ++i)
+      if (c0 + i * kThreads < block_vec) v[i] = load_stream(s0 + c0 + i * kThreads);
+#pragma unroll
+    for (int i = 0; i < kCopyUnroll; ++i)
+      if (c0 + i * kThreads < block_vec) store_stream(d0 + c0 + i * kThreads, v[i]);
+  }
 }
 
 int32_t elem_bytes(int32_t dtype) { return dtype == PA_F32 ? 4 : 2; }
@@ -66,7 +88,7 @@ hipError_t launch_copy_blocks(const pa_kv_pool& pool, const int32_t* pairs, int3
   const int64_t block_bytes =
       (int64_t)pool.block_size * pool.num_kv_heads * pool.head_dim * elem_bytes(pool.dtype);
   const int32_t block_vec = (int32_t)(block_bytes / 16);
-  const int32_t chunks = (block_vec + kThreads - 1) / kThreads;
+  const int32_t chunks = (block_vec + kThreads * kCopyUnroll - 1) / (kThreads * kCopyUnroll);
   hipLaunchKernelGGL(copy_blocks_kernel, dim3(num_pairs, 2, chunks), dim3(kThreads), 0, stream,
                      (uint4*)pool.k, (uint4*)pool.v, pairs, pool.num_blocks, block_vec);
   return hipGetLastError();

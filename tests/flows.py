@@ -55,18 +55,20 @@ def assert_close(out: np.ndarray, ref: np.ndarray, dt: str, where: str = "") -> 
     return stats
 
 
-def plan_and_workspace(pk, lens: np.ndarray, hkv: int, hq: int, d: int, num_workgroups=None, max_piece_tiles=0):
-    plan = pk.decode_plan(lens, hkv, num_workgroups, max_piece_tiles)
+def plan_and_workspace(pk, lens: np.ndarray, hkv: int, hq: int, d: int, num_workgroups=None, max_piece_tiles=0,
+                       shared_kv=False):
+    plan = pk.decode_plan(lens, hkv, num_workgroups, max_piece_tiles, shared_kv=shared_kv)
     nbytes = pk.decode_workspace_bytes(plan, hq, d)
     # The workspace needs no initialisation: fill it with NaN to prove it.
     ws = torch.full((nbytes // 4,), float("nan"), dtype=torch.float32, device="cuda") if nbytes else None
     return plan, plan.to_device(), ws
 
 
-def gpu_decode(pk, pool, q_dev, tables, lens, scale, schedule=(None, 0), out_dtype=torch.float32):
+def gpu_decode(pk, pool, q_dev, tables, lens, scale, schedule=(None, 0), out_dtype=torch.float32, shared_kv=False):
     """schedule = (num_workgroups or None for the device default, max_piece_tiles)."""
     hq = q_dev.shape[1]
-    plan, plan_dev, ws = plan_and_workspace(pk, lens, pool.k.shape[2], hq, pool.k.shape[3], *schedule)
+    plan, plan_dev, ws = plan_and_workspace(pk, lens, pool.k.shape[2], hq, pool.k.shape[3], *schedule,
+                                            shared_kv=shared_kv)
     out = torch.full(tuple(q_dev.shape), float("nan"), dtype=out_dtype, device="cuda")
     pk.decode(pool, q_dev, to_dev(tables), to_dev(lens), scale, plan, plan_dev, ws, out=out)
     return out
@@ -206,7 +208,8 @@ def product_prefix(pk, case: dict, schedule=(None, 0), shared: bool = True, priv
     tables, lens_out = bm.export(np.arange(nseq), maxb)
     assert np.array_equal(lens_out, lens)
     stats = bm.stats()
-    out = gpu_decode(pk, pool, to_dev(case["q"]), tables, lens, case["scale"], schedule)
+    out = gpu_decode(pk, pool, to_dev(case["q"]), tables, lens, case["scale"], schedule,
+                     shared_kv=stats["shared_blocks"] > 0)
     torch.cuda.synchronize()
     return dict(out=to_host(out), tables=tables, cows=np.concatenate(all_cows) if all_cows else None,
                 stats=stats, pool=pool, lens=lens, kpool=kpool, vpool=vpool, bm=bm)

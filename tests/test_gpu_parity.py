@@ -220,6 +220,19 @@ def test_prefix_sharing_matches_oracle_and_private_copies(pk, b):
     assert np.array_equal(bits(got["out"]), bits(private["out"]))
 
 
+@pytest.mark.parametrize("b", [8, 16, 32])
+def test_shared_kv_cache_policy_gives_identical_output(pk, b):
+    """PA_DECODE_SHARED_KV only changes how K/V loads use the caches."""
+    case = synth.prefix_case("c5s", b)
+    got = product_prefix(pk, case, SMALL_PIECES)
+    assert got["stats"]["shared_blocks"] > 0
+    args = (pk, got["pool"], to_dev(case["q"]), got["tables"], got["lens"], case["scale"], SMALL_PIECES)
+    streamed = to_host(gpu_decode(*args, shared_kv=False))
+    cached = to_host(gpu_decode(*args, shared_kv=True))
+    assert np.array_equal(bits(streamed), bits(cached))
+    assert np.array_equal(bits(streamed), bits(got["out"]))
+
+
 def test_use_after_free_poisoning_leaves_sharers_unchanged(pk):
     """Retire one sample, overwrite every block that went back to the free
     list with NaN; the surviving samples' outputs must not change."""

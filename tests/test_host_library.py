@@ -261,6 +261,13 @@ def test_abi_rejects_bad_decode_arguments_without_launching():
     bad = _lib.PaDecodePlanInfo.from_buffer_copy(plan.info)
     bad.jobs_at = 8
     assert call(info=bad, **ws) == -1               # inconsistent layout
+    flagged = _lib.PaDecodePlanInfo.from_buffer_copy(plan.info)
+    flagged.flags = 4
+    assert call(info=flagged, **ws) == -1           # unknown flag bit
+    for stage in (L.pa_decode_attention, L.pa_decode_merge_pieces):   # same checks on both stages
+        assert stage(ctypes.byref(pool), p, p, 0, p, 400, p, 2, 30, ctypes.c_float(0.1), p,
+                     ctypes.byref(plan.info), ws["ws"], ws["wsb"], None) == -1
+        assert b"pa_decode_" in L.pa_last_error()
     empty = pk.decode_plan([], 8, num_workgroups=4)
     assert call(info=empty.info) == 0               # nothing to do: OK, no launch
     pool32 = _pool(dtype=0, d=64)
