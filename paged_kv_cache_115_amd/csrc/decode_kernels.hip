@@ -182,10 +182,18 @@ __device__ __forceinline__ uint4 load_global(const char* p) {
 
 // K and V of tile t (of the job starting at tile t0) for KV head g: lane
 // (li, lq) gets K row li, dims 32*ks + 8*lq .. +8 (ks = 0..3), and V rows
-// 4*lq + r, dims 8*li .. 8*li + 8 (r = 0..3).
+// 4*lq + r, dims 8*li .. 8*li + 8 (r = 0..3).  For B >= 16 only the first
+// `rows` rows are read: the tile's buffer resource covers exactly those rows,
+// and a buffer load past the resource returns zeros without touching memory.
+// `rows` is 0 for the unconditional filler loads past the end of the stream,
+// and below 16 in the last tile of a row, so neither fetches bytes outside
+// the context.  The range check covers the vector offset and the
+// instruction's immediate, not the scalar offset, so every per-row offset is
+// in the vector offset.
 template <int B, bool kStream>
 __device__ __forceinline__ void load_bf16_tile(const DecodeArgs& a, int32_t g, int32_t t0, int32_t tb0, int32_t tb1,
-                                               int32_t t, int li, int lq, uint4 (&kf)[4], uint4 (&vf)[4]) {
+                                               int32_t t, int32_t rows, int li, int lq, uint4 (&kf)[4],
+                                               uint4 (&vf)[4]) {
   constexpr int D = 128;
   constexpr int kTilesPerBlock = B >= kTile ? B / kTile : 1;
   const uint32_t row_bytes = (uint32_t)a.num_kv_heads * D * 2;
@@ -204,17 +212,18 @@ __device__ __forceinline__ void load_bf16_tile(const DecodeArgs& a, int32_t g, i
     for (int r = 0; r < 4; ++r) vf[r] = load_global<kStream>(vb + vblk + ((4 * lq + r) & 7) * row_bytes + 16 * li);
   } else {
     // One tile = 16 consecutive slot rows of one block: a buffer resource on
-    // the tile (scalar registers) plus lane offsets that never change.
+    // the tile's first `rows` rows (scalar registers) plus lane offsets that
+    // never change.
     const int64_t tile_off = (int64_t)p0 * blk_bytes + (int64_t)((t0 + t) % kTilesPerBlock) * kTile * row_bytes;
-    const int32_t tile_bytes = (int32_t)(kTile * row_bytes);
+    const int32_t tile_bytes = min(max(rows, 0), kTile) * (int32_t)row_bytes;
     const __amdgpu_buffer_rsrc_t kr = tile_rsrc(kb + tile_off, tile_bytes);
     const __amdgpu_buffer_rsrc_t vr = tile_rsrc(vb + tile_off, tile_bytes);
     const uint32_t koff = li * row_bytes + 16 * lq;
     const uint32_t voff = 4 * lq * row_bytes + 16 * li;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) kf[ks] = load_b128<kStream>(kr, koff, 64 * ks);
+    for (int ks = 0; ks < 4; ++ks) kf[ks] = load_b128<kStream>(kr, koff + 64 * ks, 0);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) vf[r] = load_b128<kStream>(vr, voff, r * row_bytes);
+    for (int r = 0; r < 4; ++r) vf[r] = load_b128<kStream>(vr, voff + r * row_bytes, 0);
   }
 }
 
@@ -371,7 +380,9 @@ __global__ __launch_bounds__(kNW * 64, kWavesPerSimd) void decode_bf16_kernel(De
     const int32_t t0 = in_n ? nxt.v.t0 : in_n2 ? nx2.v.t0 : cur.v.t0;
     const int32_t tb0 = in_n ? nxt.tb0 : in_n2 ? nx2.tb0 : cur.tb0;
     const int32_t tb1 = in_n ? nxt.tb1 : in_n2 ? nx2.tb1 : cur.tb1;
-    load_bf16_tile<B, kStream>(a, g, t0, tb0, tb1, t, li, lq, ks, vs);
+    const int32_t L = in_n ? nxt.v.L : in_n2 ? nx2.v.L : cur.v.L;
+    const int32_t rows = (in_c || in_n || in_n2) ? L - kTile * (t0 + t) : 0;
+    load_bf16_tile<B, kStream>(a, g, t0, tb0, tb1, t, rows, li, lq, ks, vs);
   };
   // Compute position x from slot (ks, vs) after issuing position x + kDepth
   // into slot (kp, vp); false when the stream is done.
