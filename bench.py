@@ -230,6 +230,7 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-only", action="store_true", help="time only pa_decode launches (profiling aid)")
+    ap.add_argument("--graph", action="store_true", help="replay each step as a captured HIP graph")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="profiling aid: run a plain device-to-device copy of BYTES (the reference whose "
                          "counter readings calibrate the traffic figures) and exit")
@@ -284,12 +285,21 @@ def main() -> int:
     out = torch.empty((S, hq, d), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
 
-    def step(r: int):
+    def step(r: int, st=None):
+        st = st or stream
         pool = pools[r]
         if not args.decode_only:
-            pk.copy_blocks(pool, cows_d, stream)
-            pk.reshape_and_cache(pool, new_k, new_v, slots_d, stream)
-        pk.decode(pool, q_d, tables_d, lens_d, case["scale"], plan, plan_d, ws, out, stream)
+            pk.copy_blocks(pool, cows_d, st)
+            pk.reshape_and_cache(pool, new_k, new_v, slots_d, st)
+        pk.decode(pool, q_d, tables_d, lens_d, case["scale"], plan, plan_d, ws, out, st)
+
+    def step_fused(r: int):
+        # The same step with the append fused into the attention launch:
+        # pa_decode stores every sequence's token L - 1 from new_k/new_v.
+        pool = pools[r]
+        pk.copy_blocks(pool, cows_d, stream)
+        pk.decode(pool, q_d, tables_d, lens_d, case["scale"], plan, plan_d, ws, out, stream,
+                  new_key=new_k, new_value=new_v)
 
     def attention(r: int):
         pk.decode(pools[r], q_d, tables_d, lens_d, case["scale"], plan, plan_d, ws, out, stream, stage="attention")
@@ -314,7 +324,22 @@ def main() -> int:
     torch.cuda.synchronize()
 
     # The timed region: K whole steps.
-    ms_per_step = timed(step, args.steps)
+    ms_per_step_eager = timed(step, args.steps)
+    ms_per_step = ms_per_step_eager
+    if args.graph:
+        # One step per pool replica captured as a HIP graph, replayed in turn.
+        cap = torch.cuda.Stream()
+        graphs = []
+        for r in range(R):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap):
+                step(r, cap)
+            graphs.append(g)
+        for k in range(args.warmup):
+            graphs[k % R].replay()
+        torch.cuda.synchronize()
+        ms_per_step = timed(lambda r: graphs[r].replay(), args.steps)
+    ms_per_step_fused = timed(step_fused, args.steps)
     # The dominant kernel alone: K attention launches back to back (same
     # inputs, rotating pool replicas), then K whole pa_decode calls.
     attention_us = timed(attention, args.steps) * 1e3
@@ -338,6 +363,9 @@ def main() -> int:
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step_eager": round(ms_per_step_eager, 5),
+        "graph": bool(args.graph),
+        "ms_per_step_fused_append": round(ms_per_step_fused, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

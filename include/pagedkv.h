@@ -132,7 +132,7 @@ pa_status pa_copy_blocks(const pa_kv_pool* pool, const int32_t* pairs, int32_t n
 typedef struct pa_decode_job {
   int32_t seq;         /* sequence index */
   int32_t tile_begin;  /* first 16-token tile of the piece */
-  int32_t tile_count;  /* tiles in the piece, 1..64 */
+  int32_t tile_count;  /* tiles in the piece, 1..64; 0 marks an empty slot of the job table */
   int32_t head_block;  /* KV heads 4*head_block .. 4*head_block + 3 */
   int32_t part;        /* piece index within the sequence */
   int32_t num_parts;   /* pieces of the sequence (1: the job writes the output) */
@@ -153,8 +153,10 @@ typedef struct pa_decode_plan_info {
   int32_t num_merges;     /* grid of the merge launch (0: no merge launch) */
   int32_t num_records;    /* workspace records, one per (sequence, KV head, piece) of cut sequences */
   int32_t num_kv_heads;   /* KV heads the plan was made for */
-  int32_t offsets_at;     /* byte offset of int32 job offsets [num_workgroups + 1] */
-  int32_t jobs_at;        /* byte offset of pa_decode_job [num_jobs] */
+  int32_t jobs_per_workgroup; /* rows of the job table */
+  int32_t jobs_at;        /* byte offset (0) of the job table, pa_decode_job [jobs_per_workgroup][num_workgroups]:
+                             slot k of workgroup b at k * num_workgroups + b; a workgroup's jobs fill slots
+                             0, 1, ... in order, the rest are empty (tile_count 0) */
   int32_t merges_at;      /* byte offset of pa_decode_merge [num_merges] */
   int32_t bytes;          /* total plan bytes */
   int32_t flags;          /* PA_DECODE_* bits; pa_decode_plan sets 0, the caller may set them */
@@ -203,6 +205,16 @@ size_t pa_decode_workspace_bytes(const pa_decode_plan_info* info, int32_t num_q_
  *   context_lens : device int32 [num_seqs].
  *   scale        : multiplies q.k before the softmax (1/sqrt(head_dim) for
  *                  standard attention; S06 "Implementation").
+ *   new_key, new_value : device [num_seqs][num_kv_heads][head_dim], pool
+ *                  dtype, 16-byte aligned, or both NULL.  When given, the
+ *                  step's append is fused into the attention launch: for
+ *                  every sequence with L > 0 the token at logical position
+ *                  L - 1 is taken from these arrays and also stored into its
+ *                  slot, table[(L-1)/B] * B + (L-1) % B, which is what
+ *                  pa_reshape_and_cache would have written there with the
+ *                  slots the block manager hands out.  Its block must not be
+ *                  shared (the host's copy-on-write has run; pa_copy_blocks
+ *                  precedes this call on the stream).
  *   plan, info   : device copy of the bytes pa_decode_plan wrote for the same
  *                  context lengths and num_kv_heads, and its host-side info.
  *   workspace    : device, >= pa_decode_workspace_bytes(info, ...), 256-byte
@@ -215,8 +227,9 @@ size_t pa_decode_workspace_bytes(const pa_decode_plan_info* info, int32_t num_q_
 pa_status pa_decode(const pa_kv_pool* pool, const void* q, void* out, int32_t out_dtype,
                     const int32_t* block_tables, int32_t max_blocks_per_seq,
                     const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
-                    float scale, const void* plan, const pa_decode_plan_info* info,
-                    void* workspace, size_t workspace_bytes, void* stream);
+                    float scale, const void* new_key, const void* new_value, const void* plan,
+                    const pa_decode_plan_info* info, void* workspace, size_t workspace_bytes,
+                    void* stream);
 
 /* The two launches of pa_decode as separate calls, with the same arguments
  * and checks: pa_decode_attention writes the output of every sequence that
@@ -229,13 +242,15 @@ pa_status pa_decode(const pa_kv_pool* pool, const void* q, void* out, int32_t ou
 pa_status pa_decode_attention(const pa_kv_pool* pool, const void* q, void* out, int32_t out_dtype,
                               const int32_t* block_tables, int32_t max_blocks_per_seq,
                               const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
-                              float scale, const void* plan, const pa_decode_plan_info* info,
-                              void* workspace, size_t workspace_bytes, void* stream);
+                              float scale, const void* new_key, const void* new_value, const void* plan,
+                              const pa_decode_plan_info* info, void* workspace, size_t workspace_bytes,
+                              void* stream);
 pa_status pa_decode_merge_pieces(const pa_kv_pool* pool, const void* q, void* out, int32_t out_dtype,
                                  const int32_t* block_tables, int32_t max_blocks_per_seq,
                                  const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
-                                 float scale, const void* plan, const pa_decode_plan_info* info,
-                                 void* workspace, size_t workspace_bytes, void* stream);
+                                 float scale, const void* new_key, const void* new_value, const void* plan,
+                                 const pa_decode_plan_info* info, void* workspace, size_t workspace_bytes,
+                                 void* stream);
 
 /* ---------------------------------------------------------------------------
  * Host block manager (plain C++ on the CPU; not thread-safe: one scheduler

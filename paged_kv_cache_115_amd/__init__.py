@@ -106,16 +106,22 @@ class DecodePlan:
         self.info = info
 
     def __getattr__(self, name):
-        if name in ("num_workgroups", "num_jobs", "num_merges", "num_records", "num_kv_heads"):
+        if name in ("num_workgroups", "num_jobs", "num_merges", "num_records", "num_kv_heads", "jobs_per_workgroup"):
             return getattr(self.info, name)
         raise AttributeError(name)
 
-    def job_offsets(self) -> np.ndarray:
-        return self.blob[self.info.offsets_at:self.info.jobs_at].view(np.int32)[: self.info.num_workgroups + 1]
+    def job_table(self) -> np.ndarray:
+        """int32 [jobs_per_workgroup, num_workgroups, 8]: slot k of workgroup b
+        at [k, b]; empty slots have tile_count (field 2) 0."""
+        n = self.info.jobs_per_workgroup * self.info.num_workgroups
+        return self.blob[self.info.jobs_at:self.info.jobs_at + 32 * n].view(np.int32).reshape(
+            self.info.jobs_per_workgroup, self.info.num_workgroups, 8)
 
     def jobs(self) -> np.ndarray:
-        """int32 [num_jobs, 8]: seq, tile_begin, tile_count, head_block, part, num_parts, record_base, 0."""
-        return self.blob[self.info.jobs_at:self.info.merges_at].view(np.int32).reshape(-1, 8)
+        """int32 [num_jobs, 8]: seq, tile_begin, tile_count, head_block, part, num_parts, record_base, 0;
+        workgroup after workgroup, each in its processing order."""
+        t = self.job_table().transpose(1, 0, 2).reshape(-1, 8)
+        return t[t[:, 2] > 0]
 
     def merges(self) -> np.ndarray:
         """int32 [num_merges, 4]: seq, kv_head, num_parts, record_base."""
@@ -170,10 +176,12 @@ _DECODE_STAGES = {"all": "pa_decode", "attention": "pa_decode_attention", "merge
 
 
 def decode(pool: KvPool, q, block_tables, context_lens, scale: float, plan: DecodePlan, plan_dev, workspace=None,
-           out=None, stream=None, stage: str = "all"):
+           out=None, stream=None, stage: str = "all", new_key=None, new_value=None):
     """pa_decode (stage "all"), or one of its two launches: pa_decode_attention
     ("attention") or pa_decode_merge_pieces ("merge").  `plan_dev` is the device copy
-    of plan.blob (uint8 tensor)."""
+    of plan.blob (uint8 tensor).  new_key/new_value ([S, Hkv, D], pool dtype)
+    fuse this step's append: token L - 1 of every sequence is read from them
+    and stored into its slot."""
     import torch
     _dev(q, "q", pool.k.dtype)
     _dev(block_tables, "block_tables", torch.int32)
@@ -188,9 +196,18 @@ def decode(pool: KvPool, q, block_tables, context_lens, scale: float, plan: Deco
     if tuple(out.shape) != (s, hq, d):
         raise ValueError("out must be [S, Hq, D]")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if (new_key is None) != (new_value is None):
+        raise ValueError("new_key and new_value go together")
+    if new_key is not None:
+        for t, n in ((new_key, "new_key"), (new_value, "new_value")):
+            _dev(t, n, pool.k.dtype)
+            if tuple(t.shape) != (s, pool.k.shape[2], d):
+                raise ValueError(f"{n} must be [S, Hkv, D]")
     fn = _DECODE_STAGES[stage]
     _check(getattr(lib, fn)(ctypes.byref(pool.c), _ptr(q), _ptr(out), _dtype_code(out), _ptr(block_tables),
-                         block_tables.shape[1], _ptr(context_lens), s, hq, ctypes.c_float(scale), _ptr(plan_dev),
+                         block_tables.shape[1], _ptr(context_lens), s, hq, ctypes.c_float(scale),
+                         None if new_key is None else _ptr(new_key), None if new_value is None else _ptr(new_value),
+                         _ptr(plan_dev),
                          ctypes.byref(plan.info), None if workspace is None else _ptr(workspace), ws_bytes,
                          _stream(stream)), fn)
     return out

@@ -26,7 +26,7 @@ class PaKvPool(ctypes.Structure):
 class PaDecodePlanInfo(ctypes.Structure):
     _fields_ = [("num_workgroups", ctypes.c_int32), ("num_jobs", ctypes.c_int32),
                 ("num_merges", ctypes.c_int32), ("num_records", ctypes.c_int32),
-                ("num_kv_heads", ctypes.c_int32), ("offsets_at", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("jobs_per_workgroup", ctypes.c_int32),
                 ("jobs_at", ctypes.c_int32), ("merges_at", ctypes.c_int32), ("bytes", ctypes.c_int32),
                 ("flags", ctypes.c_int32)]
 
@@ -57,7 +57,7 @@ _p32 = ctypes.POINTER(ctypes.c_int32)
 _p64 = ctypes.POINTER(ctypes.c_int64)
 _pool = ctypes.POINTER(PaKvPool)
 
-_DECODE_ARGS = [_pool, _vp, _vp, _i32, _vp, _i32, _vp, _i32, _i32, ctypes.c_float, _vp,
+_DECODE_ARGS = [_pool, _vp, _vp, _i32, _vp, _i32, _vp, _i32, _i32, ctypes.c_float, _vp, _vp, _vp,
                 ctypes.POINTER(PaDecodePlanInfo), _vp, _sz, _vp]
 
 # name: (restype, argtypes)

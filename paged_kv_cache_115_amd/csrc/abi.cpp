@@ -222,12 +222,17 @@ extern "C" pa_status pa_decode_plan(const int32_t* context_lens, int32_t num_seq
       tail[nl] = w;
     }
   }
-  std::vector<int32_t> offsets(nwg + 1, 0);
-  for (int32_t o : owner) offsets[o + 1] += 1;
-  for (int32_t w = 0; w < nwg; ++w) offsets[w + 1] += offsets[w];
-  std::vector<pa_decode_job> placed(jobs.size());
-  std::vector<int32_t> fill(offsets.begin(), offsets.end() - 1);
-  for (size_t j = 0; j < jobs.size(); ++j) placed[fill[owner[j]]++] = jobs[j];
+  // Per-workgroup lists, column-major: slot k of workgroup b is entry
+  // k * nwg + b, so a workgroup reads its first job without an index load.
+  // Slots past a workgroup's last job are empty (tile_count 0).
+  std::vector<int32_t> count(nwg, 0);
+  for (int32_t o : owner) count[o] += 1;
+  int64_t per = 0;
+  for (int32_t c : count) per = std::max<int64_t>(per, c);
+  if (per * nwg > (int64_t)INT32_MAX / 64) return fail(PA_ERR_INVALID, "pa_decode_plan: plan too large");
+  std::vector<pa_decode_job> table((size_t)(per * nwg), pa_decode_job{0, 0, 0, 0, 0, 0, -1, 0});
+  std::vector<int32_t> fill(nwg, 0);
+  for (size_t j = 0; j < jobs.size(); ++j) table[(size_t)fill[owner[j]]++ * nwg + owner[j]] = jobs[j];
 
   pa_decode_plan_info in{};
   in.num_workgroups = jobs.empty() ? 0 : nwg;
@@ -235,9 +240,9 @@ extern "C" pa_status pa_decode_plan(const int32_t* context_lens, int32_t num_seq
   in.num_merges = (int32_t)merges.size();
   in.num_records = (int32_t)records;
   in.num_kv_heads = num_kv_heads;
-  in.offsets_at = 0;
-  in.jobs_at = (int32_t)pagedkv::round_up(sizeof(int32_t) * (nwg + 1), 32);
-  in.merges_at = in.jobs_at + (int32_t)(sizeof(pa_decode_job) * jobs.size());
+  in.jobs_per_workgroup = jobs.empty() ? 0 : (int32_t)per;
+  in.jobs_at = 0;
+  in.merges_at = (int32_t)(sizeof(pa_decode_job) * table.size());
   const size_t bytes = (size_t)in.merges_at + sizeof(pa_decode_merge) * merges.size();
   if (bytes > (size_t)INT32_MAX) return fail(PA_ERR_INVALID, "pa_decode_plan: plan too large");
   in.bytes = (int32_t)bytes;
@@ -246,8 +251,7 @@ extern "C" pa_status pa_decode_plan(const int32_t* context_lens, int32_t num_seq
     return fail(PA_ERR_INVALID, "pa_decode_plan: capacity %zu < %zu bytes", capacity, bytes);
   char* out = static_cast<char*>(plan);
   std::memset(out, 0, bytes);
-  std::memcpy(out + in.offsets_at, offsets.data(), sizeof(int32_t) * offsets.size());
-  if (!placed.empty()) std::memcpy(out + in.jobs_at, placed.data(), sizeof(pa_decode_job) * placed.size());
+  if (!jobs.empty()) std::memcpy(out + in.jobs_at, table.data(), sizeof(pa_decode_job) * table.size());
   if (!merges.empty()) std::memcpy(out + in.merges_at, merges.data(), sizeof(pa_decode_merge) * merges.size());
   return PA_OK;
 }
@@ -269,11 +273,12 @@ constexpr int kStageMerge = 2;
 pa_status decode_stages(int stages, const char* who, const pa_kv_pool* pool, const void* q, void* out,
                         int32_t out_dtype, const int32_t* block_tables, int32_t max_blocks_per_seq,
                         const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads, float scale,
-                        const void* plan, const pa_decode_plan_info* info, void* workspace,
-                        size_t workspace_bytes, void* stream) {
+                        const void* new_key, const void* new_value, const void* plan,
+                        const pa_decode_plan_info* info, void* workspace, size_t workspace_bytes, void* stream) {
   if (pa_status st = pagedkv::check_pool(pool, who)) return st;
   if (!info) return fail(PA_ERR_INVALID, "%s: info is NULL", who);
   if (num_seqs < 0 || max_blocks_per_seq < 0 || info->num_workgroups < 0 || info->num_jobs < 0 ||
+      info->jobs_per_workgroup < 0 ||
       info->num_merges < 0 || info->num_records < 0)
     return fail(PA_ERR_INVALID, "%s: negative size", who);
   if (info->num_jobs == 0 && info->num_merges == 0) return PA_OK;
@@ -294,10 +299,15 @@ pa_status decode_stages(int stages, const char* who, const pa_kv_pool* pool, con
   if (!pagedkv::aligned(q, 16) || !pagedkv::aligned(out, 16) || !pagedkv::aligned(plan, 32))
     return fail(PA_ERR_INVALID, "%s: q/out must be 16-byte and plan 32-byte aligned", who);
   if (!std::isfinite(scale)) return fail(PA_ERR_INVALID, "%s: scale is not finite", who);
+  if ((new_key == nullptr) != (new_value == nullptr))
+    return fail(PA_ERR_INVALID, "%s: new_key and new_value must both be given or both be NULL", who);
+  if (new_key && (!pagedkv::aligned(new_key, 16) || !pagedkv::aligned(new_value, 16)))
+    return fail(PA_ERR_INVALID, "%s: new_key/new_value must be 16-byte aligned", who);
   if (info->flags & ~PA_DECODE_SHARED_KV) return fail(PA_ERR_INVALID, "%s: unknown plan flags 0x%x", who, info->flags);
-  if (info->jobs_at % 32 != 0 || info->merges_at % 16 != 0 || info->offsets_at != 0 ||
-      (int64_t)info->jobs_at < 4 * ((int64_t)info->num_workgroups + 1) ||
-      (int64_t)info->merges_at < (int64_t)info->jobs_at + 32 * (int64_t)info->num_jobs ||
+  if (info->jobs_at != 0 || info->merges_at % 16 != 0 ||
+      (info->num_jobs > 0 && (info->num_workgroups == 0 || info->jobs_per_workgroup == 0)) ||
+      (int64_t)info->jobs_per_workgroup * info->num_workgroups < (int64_t)info->num_jobs ||
+      (int64_t)info->merges_at < 32 * (int64_t)info->jobs_per_workgroup * info->num_workgroups ||
       (int64_t)info->bytes < (int64_t)info->merges_at + 16 * (int64_t)info->num_merges)
     return fail(PA_ERR_INVALID, "%s: inconsistent plan info", who);
   const auto lay = pagedkv::layout((int64_t)info->num_records * group, pool->head_dim);
@@ -311,11 +321,12 @@ pa_status decode_stages(int stages, const char* who, const pa_kv_pool* pool, con
   a.k = pool->k;
   a.v = pool->v;
   a.q = q;
+  a.new_k = new_key;
+  a.new_v = new_value;
   a.out = out;
   a.tables = block_tables;
   a.lens = context_lens;
   const char* pb = static_cast<const char*>(plan);
-  a.job_offsets = reinterpret_cast<const int32_t*>(pb + info->offsets_at);
   a.jobs = reinterpret_cast<const pa_decode_job*>(pb + info->jobs_at);
   a.merges = reinterpret_cast<const pa_decode_merge*>(pb + info->merges_at);
   char* ws = static_cast<char*>(workspace);
@@ -330,6 +341,7 @@ pa_status decode_stages(int stages, const char* who, const pa_kv_pool* pool, con
   a.max_blocks = max_blocks_per_seq;
   a.num_seqs = num_seqs;
   a.num_workgroups = info->num_workgroups;
+  a.jobs_per_workgroup = info->jobs_per_workgroup;
   a.num_jobs = info->num_jobs;
   a.num_merges = info->num_merges;
   a.num_records = info->num_records;
@@ -349,11 +361,11 @@ pa_status decode_stages(int stages, const char* who, const pa_kv_pool* pool, con
 #define PA_DECODE_ARGS                                                                                   \
   const pa_kv_pool *pool, const void *q, void *out, int32_t out_dtype, const int32_t *block_tables,      \
       int32_t max_blocks_per_seq, const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,    \
-      float scale, const void *plan, const pa_decode_plan_info *info, void *workspace,                   \
-      size_t workspace_bytes, void *stream
+      float scale, const void *new_key, const void *new_value, const void *plan,                         \
+      const pa_decode_plan_info *info, void *workspace, size_t workspace_bytes, void *stream
 #define PA_DECODE_PASS                                                                                   \
   pool, q, out, out_dtype, block_tables, max_blocks_per_seq, context_lens, num_seqs, num_q_heads, scale, \
-      plan, info, workspace, workspace_bytes, stream
+      new_key, new_value, plan, info, workspace, workspace_bytes, stream
 
 extern "C" pa_status pa_decode(PA_DECODE_ARGS) {
   return decode_stages(kStageAttention | kStageMerge, "pa_decode", PA_DECODE_PASS);

@@ -64,6 +64,7 @@ constexpr int kNW = 4;          // wavefronts per workgroup = KV heads per job
 constexpr int kDepth = 2;       // bf16 kernel: K/V tiles in flight per wavefront
 constexpr int kWavesPerSimd = 2;  // bf16 kernel: occupancy it is compiled for
 constexpr int kTile = 16;       // tokens per tile (MFMA rows)
+constexpr int kHeadDim = 128;   // head_dim of the bf16 path
 constexpr int kMaxTiles = 64;   // tiles per job: one table entry per lane
 constexpr int kMaxMergeThreads = 16 * 128 / 2;  // merge block: G * head_dim / 2 threads
 
@@ -104,21 +105,27 @@ struct JobView {
   int32_t seq, g, t0, cnt, L, rec;
 };
 
-// Job j for wavefront w; false if the wavefront has nothing to do in it.
-__device__ __forceinline__ bool view_job(const DecodeArgs& a, int32_t j, int w, int B, JobView& v) {
-  const pa_decode_job jd = a.jobs[j];
+// What job record jd holds for wavefront w: 1 work, 0 nothing for this
+// wavefront (its KV head is past the last one), -1 an empty slot.
+__device__ __forceinline__ int job_kind(const DecodeArgs& a, const pa_decode_job& jd, int w) {
+  if (jd.tile_count <= 0 || jd.tile_begin < 0) return -1;
+  const int32_t g = jd.head_block * kNW + w;
+  return (g >= 0 && g < a.num_kv_heads) ? 1 : 0;
+}
+
+// The fields of job record jd for wavefront w (job_kind(jd, w) == 1).  The
+// context length is the only dependent load.
+__device__ __forceinline__ void view_job(const DecodeArgs& a, const pa_decode_job& jd, int w, int B, JobView& v) {
   v.g = jd.head_block * kNW + w;
   v.cnt = min(jd.tile_count, kMaxTiles);
-  if (v.g < 0 || v.g >= a.num_kv_heads || v.cnt <= 0 || jd.tile_begin < 0) return false;
   v.seq = min(max(jd.seq, 0), a.num_seqs - 1);
-  v.t0 = jd.tile_begin;
+  v.t0 = max(jd.tile_begin, 0);
   v.L = min(max(a.lens[v.seq], 0), a.max_blocks * B);
   v.rec = -1;
   if (jd.num_parts > 1) {
     const int64_t r = (int64_t)jd.record_base + (int64_t)v.g * jd.num_parts + jd.part;
     v.rec = (jd.record_base >= 0 && jd.part >= 0 && jd.part < jd.num_parts && r < a.num_records) ? (int32_t)r : -2;
   }
-  return true;
 }
 
 // --------------------------------------------------------------------------
@@ -132,15 +139,17 @@ struct JobRef {
   int32_t tb0, tb1;
 };
 
+// The context length, the table entries and (load_q) the query of one job
+// depend only on its record, so they are fetched together.
 template <int B>
-__device__ __forceinline__ void load_ref(const DecodeArgs& a, int32_t j, int w, int lane, JobRef<B>& J) {
+__device__ __forceinline__ void load_ref(const DecodeArgs& a, const pa_decode_job& jd, int w, int lane, JobRef<B>& J) {
   constexpr int kTilesPerBlock = B >= kTile ? B / kTile : 1;
-  view_job(a, j, w, B, J.v);
+  view_job(a, jd, w, B, J.v);
   // Lanes past the job's last tile read an in-row entry that is never used.
   const int32_t* trow = a.tables + (int64_t)J.v.seq * a.max_blocks;
   const int32_t t = J.v.t0 + lane;
   int32_t e0 = B == 8 ? 2 * t : t / kTilesPerBlock;
-  e0 = min(e0, a.max_blocks - 1);
+  e0 = min(max(e0, 0), a.max_blocks - 1);
   J.tb0 = clamp_block(trow[e0], a.num_blocks);
   J.tb1 = B == 8 ? clamp_block(trow[min(e0 + 1, a.max_blocks - 1)], a.num_blocks) : 0;
 }
@@ -190,10 +199,10 @@ __device__ __forceinline__ uint4 load_global(const char* p) {
 // the context.  The range check covers the vector offset and the
 // instruction's immediate, not the scalar offset, so every per-row offset is
 // in the vector offset.
-template <int B, bool kStream>
+template <int B, bool kStream, bool kFused>
 __device__ __forceinline__ void load_bf16_tile(const DecodeArgs& a, int32_t g, int32_t t0, int32_t tb0, int32_t tb1,
-                                               int32_t t, int32_t rows, int li, int lq, uint4 (&kf)[4],
-                                               uint4 (&vf)[4]) {
+                                               int32_t t, int32_t rows, int32_t r_new, const char* nk,
+                                               const char* nv, int li, int lq, uint4 (&kf)[4], uint4 (&vf)[4]) {
   constexpr int D = 128;
   constexpr int kTilesPerBlock = B >= kTile ? B / kTile : 1;
   const uint32_t row_bytes = (uint32_t)a.num_kv_heads * D * 2;
@@ -201,7 +210,23 @@ __device__ __forceinline__ void load_bf16_tile(const DecodeArgs& a, int32_t g, i
   const char* kb = reinterpret_cast<const char*>(a.k) + (int64_t)g * D * 2;
   const char* vb = reinterpret_cast<const char*>(a.v) + (int64_t)g * D * 2;
   const int32_t p0 = __builtin_amdgcn_readlane(tb0, t);
-  if (B == 8) {
+  if (kFused && r_new >= 0) {
+    // The tile holding this step's appended token (row r_new): that row
+    // comes from the new key/value arrays, rows after it (past the context)
+    // read the same row and are masked later, rows before it come from the
+    // pool.  Per-lane addresses, so plain global loads.
+    const int32_t p1 = B == 8 ? __builtin_amdgcn_readlane(tb1, t) : p0;
+    auto row_addr = [&](const char* base, int32_t row) {
+      if (B == 8) return base + (int64_t)(row < 8 ? p0 : p1) * blk_bytes + (row & 7) * row_bytes;
+      return base + (int64_t)p0 * blk_bytes + ((int64_t)((t0 + t) % kTilesPerBlock) * kTile + row) * row_bytes;
+    };
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      kf[ks] = load_global<kStream>(li >= r_new ? nk + 16 * (4 * ks + lq) : row_addr(kb, li) + 16 * (4 * ks + lq));
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      vf[r] = load_global<kStream>(4 * lq + r >= r_new ? nv + 16 * li : row_addr(vb, 4 * lq + r) + 16 * li);
+  } else if (B == 8) {
     // Rows 0..7 of the tile live in block p0, rows 8..15 in block p1.
     const int32_t p1 = __builtin_amdgcn_readlane(tb1, t);
     const int64_t kblk = (int64_t)(li < 8 ? p0 : p1) * blk_bytes;
@@ -214,10 +239,16 @@ __device__ __forceinline__ void load_bf16_tile(const DecodeArgs& a, int32_t g, i
     // One tile = 16 consecutive slot rows of one block: a buffer resource on
     // the tile's first `rows` rows (scalar registers) plus lane offsets that
     // never change.
-    const int64_t tile_off = (int64_t)p0 * blk_bytes + (int64_t)((t0 + t) % kTilesPerBlock) * kTile * row_bytes;
-    const int32_t tile_bytes = min(max(rows, 0), kTile) * (int32_t)row_bytes;
-    const __amdgpu_buffer_rsrc_t kr = tile_rsrc(kb + tile_off, tile_bytes);
-    const __amdgpu_buffer_rsrc_t vr = tile_rsrc(vb + tile_off, tile_bytes);
+    // Every operand is wave-uniform by construction; readfirstlane says so to
+    // the compiler, which otherwise wraps each load in a waterfall loop.
+    const int64_t tile_off = (int64_t)g * D * 2 + (int64_t)p0 * blk_bytes +
+                             (int64_t)((t0 + t) % kTilesPerBlock) * kTile * row_bytes;
+    const uint32_t off_lo = __builtin_amdgcn_readfirstlane((uint32_t)tile_off);
+    const uint32_t off_hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)tile_off >> 32));
+    const int64_t uoff = (int64_t)(((uint64_t)off_hi << 32) | off_lo);
+    const int32_t tile_bytes = __builtin_amdgcn_readfirstlane(min(max(rows, 0), kTile) * (int32_t)row_bytes);
+    const __amdgpu_buffer_rsrc_t kr = tile_rsrc(reinterpret_cast<const char*>(a.k) + uoff, tile_bytes);
+    const __amdgpu_buffer_rsrc_t vr = tile_rsrc(reinterpret_cast<const char*>(a.v) + uoff, tile_bytes);
     const uint32_t koff = li * row_bytes + 16 * lq;
     const uint32_t voff = 4 * lq * row_bytes + 16 * li;
 #pragma unroll
@@ -225,6 +256,43 @@ __device__ __forceinline__ void load_bf16_tile(const DecodeArgs& a, int32_t g, i
 #pragma unroll
     for (int r = 0; r < 4; ++r) vf[r] = load_b128<kStream>(vr, voff + r * row_bytes, 0);
   }
+}
+
+// Fused append: when tile t of job J holds the sequence's token L - 1 (the
+// token appended this step), the registers hold its row from the new
+// key/value arrays (load_bf16_tile); write that row into its pool slot,
+// the slot at logical position L - 1 of the table.  Only the wavefront of
+// the row's last piece meets this tile, so each (sequence, KV head) slice is
+// written once.
+template <int B>
+__device__ __forceinline__ void store_appended_row(const DecodeArgs& a, const JobRef<B>& J, int32_t t, int li,
+                                                   int lq, const uint4 (&kf)[4], const uint4 (&vf)[4]) {
+  constexpr int kTilesPerBlock = B >= kTile ? B / kTile : 1;
+  const int32_t r_new = J.v.L - 1 - kTile * (J.v.t0 + t);
+  if (r_new < 0 || r_new >= kTile) return;
+  const uint32_t row_bytes = (uint32_t)a.num_kv_heads * kHeadDim * 2;
+  const int64_t blk_bytes = (int64_t)row_bytes * B;
+  const int32_t p0 = __builtin_amdgcn_readlane(J.tb0, t);
+  int64_t off;
+  if (B == 8) {
+    const int32_t p1 = __builtin_amdgcn_readlane(J.tb1, t);
+    off = (int64_t)(r_new < 8 ? p0 : p1) * blk_bytes + (r_new & 7) * row_bytes;
+  } else {
+    off = (int64_t)p0 * blk_bytes + ((int64_t)((J.v.t0 + t) % kTilesPerBlock) * kTile + r_new) * row_bytes;
+  }
+  off += (int64_t)J.v.g * kHeadDim * 2;
+  char* kdst = reinterpret_cast<char*>(const_cast<void*>(a.k)) + off;
+  char* vdst = reinterpret_cast<char*>(const_cast<void*>(a.v)) + off;
+  if (li == r_new) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) *reinterpret_cast<uint4*>(kdst + 16 * (4 * ks + lq)) = kf[ks];
+  }
+  // V row r_new sits in register r_new % 4 of the lanes of group r_new / 4
+  // (constant register indices only: a computed one would move the
+  // registers to memory).
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    if (4 * lq + r == r_new) *reinterpret_cast<uint4*>(vdst + 16 * li) = vf[r];
 }
 
 struct SoftmaxState {
@@ -326,25 +394,47 @@ __device__ __forceinline__ void finish_bf16_job(const DecodeArgs& a, const JobVi
   }
 }
 
-template <int B, bool kStream>
+template <int B, bool kStream, bool kFused>
 __global__ __launch_bounds__(kNW * 64, kWavesPerSimd) void decode_bf16_kernel(DecodeArgs a) {
   static_assert(B == 8 || B == 16 || B == 32, "block size");
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: keeps job fields in SGPRs
   const int li = lane & 15;  // MFMA row / column within a 16-lane group
   const int lq = lane >> 4;  // which 16-lane group
-  const int32_t jend = min(a.job_offsets[blockIdx.x + 1], a.num_jobs);
-
-  // Next job index >= j in which this wavefront has work.
-  auto next_job = [&](int32_t j) {
-    JobView tmp;
-    while (j < jend && !view_job(a, j, w, B, tmp)) ++j;
-    return j;
+  // The workgroup's jobs are the slots k = 0, 1, ... of its column of the
+  // job table (entry k * num_workgroups + blockIdx.x); jobs are named by slot.
+  int32_t jend = a.jobs_per_workgroup;
+  if (jend <= 0) return;
+  auto record = [&](int32_t k) { return a.jobs[k * a.num_workgroups + (int32_t)blockIdx.x]; };
+  // Next slot >= k in which this wavefront has work (jend: none; an empty
+  // slot ends the column).
+  auto next_job = [&](int32_t k) {
+    for (; k < jend; ++k) {
+      const int kind = job_kind(a, record(k), w);
+      if (kind > 0) return k;
+      if (kind < 0) return jend;
+    }
+    return jend;
   };
-  const int32_t jc = next_job(max(a.job_offsets[blockIdx.x], 0));
-  if (jc >= jend) return;
-  int32_t jn = next_job(jc + 1);
-  int32_t jn2 = jn < jend ? next_job(jn + 1) : jend;
+  // The first three slots are read together: unless a slot has nothing for
+  // this wavefront (KV-head counts that are not a multiple of four), they
+  // are the first three jobs, and their table entries, lengths and queries
+  // are requested right after.
+  const int k0 = job_kind(a, record(0), w);
+  const int k1 = jend > 1 ? job_kind(a, record(min(1, jend - 1)), w) : -1;
+  const int k2 = jend > 2 ? job_kind(a, record(min(2, jend - 1)), w) : -1;
+  int32_t jc, jn, jn2;
+  const bool fast = k0 > 0 && k1 != 0 && (k1 < 0 || k2 != 0);
+  if (fast) {
+    jc = 0;
+    jn = k1 > 0 ? 1 : jend;
+    jn2 = (k1 > 0 && k2 > 0) ? 2 : jend;
+  } else {
+    jc = next_job(0);
+    if (jc >= jend) return;
+    jn = next_job(jc + 1);
+    jn2 = jn < jend ? next_job(jn + 1) : jend;
+  }
 
   // The wavefront's tiles form one stream.  Position x is tile x - x0 of the
   // current job (x0 = its first position); the positions past it belong to
@@ -355,9 +445,9 @@ __global__ __launch_bounds__(kNW * 64, kWavesPerSimd) void decode_bf16_kernel(De
   // current job's last tile, which the cache still holds), so the waits the
   // compiler inserts count exactly the loads in flight.
   JobRef<B> cur, nxt, nx2;
-  load_ref<B>(a, jc, w, lane, cur);
-  load_ref<B>(a, jn < jend ? jn : jc, w, lane, nxt);
-  load_ref<B>(a, jn2 < jend ? jn2 : jc, w, lane, nx2);
+  load_ref<B>(a, record(jc), w, lane, cur);
+  load_ref<B>(a, record(jn < jend ? jn : jc), w, lane, nxt);
+  load_ref<B>(a, record(jn2 < jend ? jn2 : jc), w, lane, nx2);
   bool hn = jn < jend, hn2 = jn2 < jend;
   bf16x8_t qc[4], qn[4];
   load_q(a, cur.v, li, lq, qc);
@@ -381,18 +471,28 @@ __global__ __launch_bounds__(kNW * 64, kWavesPerSimd) void decode_bf16_kernel(De
     const int32_t tb0 = in_n ? nxt.tb0 : in_n2 ? nx2.tb0 : cur.tb0;
     const int32_t tb1 = in_n ? nxt.tb1 : in_n2 ? nx2.tb1 : cur.tb1;
     const int32_t L = in_n ? nxt.v.L : in_n2 ? nx2.v.L : cur.v.L;
-    const int32_t rows = (in_c || in_n || in_n2) ? L - kTile * (t0 + t) : 0;
-    load_bf16_tile<B, kStream>(a, g, t0, tb0, tb1, t, rows, li, lq, ks, vs);
+    const bool live = in_c || in_n || in_n2;
+    const int32_t rows = live ? L - kTile * (t0 + t) : 0;
+    // Row of this step's appended token in the tile, when the append is fused
+    // into this launch and the tile holds it.
+    const int32_t r_new = (kFused && live && rows >= 1 && rows <= kTile) ? rows - 1 : -1;
+    const int32_t seq = in_n ? nxt.v.seq : in_n2 ? nx2.v.seq : cur.v.seq;
+    const int64_t new_row = ((int64_t)seq * a.num_kv_heads + g) * kHeadDim * 2;
+    const char* nk = reinterpret_cast<const char*>(a.new_k) + new_row;
+    const char* nv = reinterpret_cast<const char*>(a.new_v) + new_row;
+    load_bf16_tile<B, kStream, kFused>(a, g, t0, tb0, tb1, t, rows, r_new, nk, nv, li, lq, ks, vs);
   };
   // Compute position x from slot (ks, vs) after issuing position x + kDepth
   // into slot (kp, vp); false when the stream is done.
   auto step = [&](uint4 (&ks)[4], uint4 (&vs)[4], uint4 (&kp)[4], uint4 (&vp)[4]) {
     issue(x + kDepth, kp, vp);
+    if (kFused) store_appended_row<B>(a, cur, x - x0, li, lq, ks, vs);
     compute_bf16_tile(a, cur.v, qc, x - x0, lq, ks, vs, st);
     ++x;
     if (x - x0 < cur.v.cnt) return true;
     finish_bf16_job(a, cur.v, li, lq, st);
     if (!hn) return false;
+    const int32_t js = jn;  // slot of the job that becomes current (< jend)
     x0 += cur.v.cnt;
     cur = nxt;
 #pragma unroll
@@ -402,7 +502,9 @@ __global__ __launch_bounds__(kNW * 64, kWavesPerSimd) void decode_bf16_kernel(De
     jn = jn2;
     jn2 = hn ? next_job(jn + 1) : jend;
     hn2 = jn2 < jend;
-    load_ref<B>(a, hn2 ? jn2 : jn, w, lane, nx2);
+    // Without a job after next, the third reference is a copy of a known
+    // one (never used): only slots below jend are read.
+    load_ref<B>(a, record(hn2 ? jn2 : hn ? jn : js), w, lane, nx2);
     load_q(a, nxt.v, li, lq, qn);
     st.reset();
     return true;
@@ -429,10 +531,13 @@ __global__ __launch_bounds__(kNW * 64) void decode_f32_kernel(DecodeArgs a) {
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: keeps job fields in SGPRs
   const int G = a.group;
-  const int32_t jend = min(a.job_offsets[blockIdx.x + 1], a.num_jobs);
-  for (int32_t j = max(a.job_offsets[blockIdx.x], 0); j < jend; ++j) {
+  for (int32_t k = 0; k < a.jobs_per_workgroup; ++k) {
+    const pa_decode_job jd = a.jobs[k * a.num_workgroups + (int32_t)blockIdx.x];
+    const int kind = job_kind(a, jd, w);
+    if (kind < 0) break;
+    if (kind == 0) continue;
     JobView v;
-    if (!view_job(a, j, w, B, v)) continue;
+    view_job(a, jd, w, B, v);
     float qv[kMaxGroup][DPL], m_run[kMaxGroup], l_run[kMaxGroup], o[kMaxGroup][DPL];
     const float* qrow = reinterpret_cast<const float*>(a.q) + ((int64_t)v.seq * a.num_q_heads + (int64_t)v.g * G) * D;
 #pragma unroll
@@ -454,10 +559,27 @@ __global__ __launch_bounds__(kNW * 64) void decode_f32_kernel(DecodeArgs a) {
       const int32_t p = clamp_block(trow[t / B], a.num_blocks);
       const int64_t row = ((int64_t)p * B + t % B) * row_stride;
       float kv[DPL], vv[DPL];
+      if (a.new_k != nullptr && t == v.L - 1) {
+        // Fused append: this step's token comes from the new key/value
+        // arrays and is also stored into its pool slot.
+        const int64_t nrow = ((int64_t)v.seq * a.num_kv_heads + v.g) * D;
+        const float* nk = reinterpret_cast<const float*>(a.new_k) + nrow;
+        const float* nv = reinterpret_cast<const float*>(a.new_v) + nrow;
+        float* kdst = reinterpret_cast<float*>(const_cast<void*>(a.k)) + (int64_t)v.g * D + row;
+        float* vdst = reinterpret_cast<float*>(const_cast<void*>(a.v)) + (int64_t)v.g * D + row;
 #pragma unroll
-      for (int jj = 0; jj < DPL; ++jj) {
-        kv[jj] = kbase[row + lane + 64 * jj];
-        vv[jj] = vbase[row + lane + 64 * jj];
+        for (int jj = 0; jj < DPL; ++jj) {
+          kv[jj] = nk[lane + 64 * jj];
+          vv[jj] = nv[lane + 64 * jj];
+          kdst[lane + 64 * jj] = kv[jj];
+          vdst[lane + 64 * jj] = vv[jj];
+        }
+      } else {
+#pragma unroll
+        for (int jj = 0; jj < DPL; ++jj) {
+          kv[jj] = kbase[row + lane + 64 * jj];
+          vv[jj] = vbase[row + lane + 64 * jj];
+        }
       }
 #pragma unroll
       for (int h = 0; h < kMaxGroup; ++h) {
@@ -573,13 +695,19 @@ hipError_t launch_decode_attention(const DecodeArgs& a, hipStream_t stream) {
   const dim3 grid((unsigned)a.num_workgroups);
   bool launched = false;
   if (a.bf16) {
-#define PA_BF16_CASE(BS)                                                                         \
-  case BS:                                                                                       \
-    if (a.shared_kv)                                                                             \
-      hipLaunchKernelGGL((decode_bf16_kernel<BS, false>), grid, dim3(kNW * 64), 0, stream, a);   \
-    else                                                                                         \
-      hipLaunchKernelGGL((decode_bf16_kernel<BS, true>), grid, dim3(kNW * 64), 0, stream, a);    \
-    launched = true;                                                                             \
+#define PA_BF16_LAUNCH(BS, STREAM)                                                                      \
+  if (a.new_k != nullptr)                                                                               \
+    hipLaunchKernelGGL((decode_bf16_kernel<BS, STREAM, true>), grid, dim3(kNW * 64), 0, stream, a);     \
+  else                                                                                                  \
+    hipLaunchKernelGGL((decode_bf16_kernel<BS, STREAM, false>), grid, dim3(kNW * 64), 0, stream, a);
+#define PA_BF16_CASE(BS)                                                                                \
+  case BS:                                                                                              \
+    if (a.shared_kv) {                                                                                  \
+      PA_BF16_LAUNCH(BS, false)                                                                         \
+    } else {                                                                                            \
+      PA_BF16_LAUNCH(BS, true)                                                                          \
+    }                                                                                                   \
+    launched = true;                                                                                    \
     break;
     switch (a.block_size) {
       PA_BF16_CASE(8)
@@ -588,6 +716,7 @@ hipError_t launch_decode_attention(const DecodeArgs& a, hipStream_t stream) {
       default: break;
     }
 #undef PA_BF16_CASE
+#undef PA_BF16_LAUNCH
   } else {
 #define PA_F32_CASE(BS, DD)                                                                  \
   if (!launched && a.block_size == BS && a.head_dim == DD) {                                 \
@@ -617,7 +746,7 @@ hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t stream) {
 }
 
 hipError_t decode_resident_workgroups_per_cu(int* n) {
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, decode_bf16_kernel<16, true>, kNW * 64, 0);
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, decode_bf16_kernel<16, true, false>, kNW * 64, 0);
 }
 
 }  // namespace pagedkv

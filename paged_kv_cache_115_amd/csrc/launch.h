@@ -13,11 +13,12 @@ struct DecodeArgs {
   const void* k;
   const void* v;
   const void* q;
+  const void* new_k;             // [num_seqs][num_kv_heads][head_dim] or null: fused append of token L - 1
+  const void* new_v;
   void* out;
   const int32_t* tables;
   const int32_t* lens;
-  const int32_t* job_offsets;    // [num_workgroups + 1]
-  const pa_decode_job* jobs;     // [num_jobs]
+  const pa_decode_job* jobs;     // [jobs_per_workgroup][num_workgroups], column-major lists
   const pa_decode_merge* merges; // [num_merges]
   float* partial_ml;             // [num_records * group][2] = (max, sum) in log2 units
   float* partial_o;              // [num_records * group][head_dim], unnormalised
@@ -30,6 +31,7 @@ struct DecodeArgs {
   int32_t max_blocks;            // block-table row length
   int32_t num_seqs;
   int32_t num_workgroups;
+  int32_t jobs_per_workgroup;
   int32_t num_jobs;
   int32_t num_merges;
   int32_t num_records;

@@ -64,19 +64,24 @@ def plan_and_workspace(pk, lens: np.ndarray, hkv: int, hq: int, d: int, num_work
     return plan, plan.to_device(), ws
 
 
-def gpu_decode(pk, pool, q_dev, tables, lens, scale, schedule=(None, 0), out_dtype=torch.float32, shared_kv=False):
-    """schedule = (num_workgroups or None for the device default, max_piece_tiles)."""
+def gpu_decode(pk, pool, q_dev, tables, lens, scale, schedule=(None, 0), out_dtype=torch.float32, shared_kv=False,
+               new_key=None, new_value=None):
+    """schedule = (num_workgroups or None for the device default, max_piece_tiles).
+    new_key/new_value: fuse this step's append into the decode call."""
     hq = q_dev.shape[1]
     plan, plan_dev, ws = plan_and_workspace(pk, lens, pool.k.shape[2], hq, pool.k.shape[3], *schedule,
                                             shared_kv=shared_kv)
     out = torch.full(tuple(q_dev.shape), float("nan"), dtype=out_dtype, device="cuda")
-    pk.decode(pool, q_dev, to_dev(tables), to_dev(lens), scale, plan, plan_dev, ws, out=out)
+    pk.decode(pool, q_dev, to_dev(tables), to_dev(lens), scale, plan, plan_dev, ws, out=out,
+              new_key=new_key, new_value=new_value)
     return out
 
 
 # ---------------------------------------------------------------- decode step
-def product_decode_step(pk, case: dict, schedule=(None, 0), out_dtype=torch.float32):
-    """Prefill L-1 tokens, append this step's token, decode.  Returns dict."""
+def product_decode_step(pk, case: dict, schedule=(None, 0), out_dtype=torch.float32, fused: bool = False):
+    """Prefill L-1 tokens, append this step's token, decode.  Returns dict.
+    fused: the appended token is not written by pa_reshape_and_cache but
+    handed to pa_decode (new_key/new_value), which stores it while attending."""
     cfg = case["cfg"]
     b, hkv, d, dt = cfg["block_size"], cfg["num_kv_heads"], cfg["head_dim"], cfg["dtype"]
     nb = case["num_blocks"]
@@ -107,12 +112,14 @@ def product_decode_step(pk, case: dict, schedule=(None, 0), out_dtype=torch.floa
     if pre_rows.size:
         pk.reshape_and_cache(pool, to_dev(case["keys"][pre_rows]), to_dev(case["values"][pre_rows]), to_dev(pre_slot_arr))
     last_rows = np.array([off[s + 1] - 1 if lens[s] > 0 else 0 for s in range(s_count)])
-    pk.reshape_and_cache(pool, to_dev(case["keys"][last_rows]), to_dev(case["values"][last_rows]),
-                         to_dev(np.array(new_slots, dtype=np.int64)))
+    new_k, new_v = to_dev(case["keys"][last_rows]), to_dev(case["values"][last_rows])
+    if not fused:
+        pk.reshape_and_cache(pool, new_k, new_v, to_dev(np.array(new_slots, dtype=np.int64)))
     maxb = max(1, int(max((-(-int(L) // b)) for L in lens)))
     tables, lens_out = bm.export(np.arange(s_count), maxb)
     assert np.array_equal(lens_out, lens)
-    out = gpu_decode(pk, pool, to_dev(case["q"]), tables, lens_out, case["scale"], schedule, out_dtype)
+    out = gpu_decode(pk, pool, to_dev(case["q"]), tables, lens_out, case["scale"], schedule, out_dtype,
+                     new_key=new_k if fused else None, new_value=new_v if fused else None)
     torch.cuda.synchronize()
     return dict(out=to_host(out), kpool=to_host(kpool), vpool=to_host(vpool), tables=tables,
                 pre_slots=pre_slots, new_slots=new_slots, pool=pool, q_dev=to_dev(case["q"]), lens=lens_out)

@@ -100,6 +100,42 @@ def test_decode_step_matches_oracle(pk, name, schedule):
     log(f"  max|err|={stats['max_abs']:.3g} mean|err|={stats['mean_abs']:.3g}")
 
 
+FUSED_CASES = [("c1", DEFAULT), ("c1", TINY_PIECES), ("c2s", SMALL_PIECES), ("c3s", DEFAULT), ("c3s", TINY_PIECES),
+               ("c3s", FEW_WG), ("c4s", SMALL_PIECES)]
+
+
+@pytest.mark.parametrize("name,schedule", FUSED_CASES)
+def test_fused_append_equals_separate_cache_write(pk, name, schedule):
+    """pa_decode with new_key/new_value stores the appended token into its
+    slot while attending: pools byte-identical to the oracle's (untouched
+    slots still NaN), output bitwise equal to pa_reshape_and_cache followed
+    by pa_decode."""
+    log(f"fused append {name} schedule={schedule}")
+    case = synth.decode_case(name)
+    fused = product_decode_step(pk, case, schedule, fused=True)
+    split = product_decode_step(pk, case, schedule)
+    ref = oracle_decode_step(case)
+    assert np.array_equal(bits(fused["kpool"]), bits(ref["kpool"]))
+    assert np.array_equal(bits(fused["vpool"]), bits(ref["vpool"]))
+    assert np.array_equal(bits(fused["out"]), bits(split["out"]))
+    assert_close(fused["out"], ref["out"], case["cfg"]["dtype"], f"fused {name}/{schedule}")
+
+
+@pytest.mark.parametrize("b", [8, 16, 32])
+def test_fused_append_edge_lengths(pk, b):
+    """The appended token at every position of a tile and of a block, in
+    empty, one-token and full-table contexts, for each block size."""
+    lens = [0, 1, 7, 8, 9, 15, 16, 17, 31, 32, 33, 63, 64, 65, 0, 255, 256, 257, 1023, 1024, 1025, 2100]
+    case = _edge_case(lens, b)
+    ref = oracle_decode_step(case)
+    for schedule in (DEFAULT, TINY_PIECES, (5, 64)):
+        log(f"fused edge lengths B={b} schedule={schedule}")
+        got = product_decode_step(pk, case, schedule, fused=True)
+        assert np.array_equal(bits(got["kpool"]), bits(ref["kpool"]))
+        assert np.array_equal(bits(got["vpool"]), bits(ref["vpool"]))
+        assert_close(got["out"], ref["out"], "bf16", f"fused edge/B{b}/{schedule}")
+
+
 def test_decode_is_deterministic_and_schedule_independent_within_tolerance(pk):
     case = synth.decode_case("c3s")
     a = product_decode_step(pk, case, SMALL_PIECES)
@@ -128,6 +164,39 @@ def test_attention_then_merge_stages_equal_pa_decode(pk):
     torch.cuda.synchronize()
     assert np.array_equal(bits(to_host(whole)), bits(to_host(staged)))
     assert np.all(to_host(staged)[1] == 0)
+
+
+def test_captured_graph_replays_match_eager_calls(pk):
+    """A step captured as a HIP graph (the appended tokens' cache write, the
+    attention launch, the merge launch), replayed several times with eager
+    work and synchronisations between replays, writes what eager calls do."""
+    case = synth.decode_case("c3s")
+    a = product_decode_step(pk, case, SMALL_PIECES)
+    off, lens_h = case["offsets"], a["lens"]
+    rows = np.array([off[s + 1] - 1 for s in range(len(lens_h))])
+    new_k, new_v = to_dev(case["keys"][rows]), to_dev(case["values"][rows])
+    slots = to_dev(np.array(a["new_slots"], dtype=np.int64))
+    pool, q = a["pool"], a["q_dev"]
+    plan, plan_dev, ws = plan_and_workspace(pk, lens_h, pool.k.shape[2], q.shape[1], pool.k.shape[3], *SMALL_PIECES)
+    assert plan.num_merges > 0
+    tables, lens = to_dev(a["tables"]), to_dev(lens_h)
+    eager = torch.full(tuple(q.shape), float("nan"), device="cuda")
+    pk.reshape_and_cache(pool, new_k, new_v, slots)
+    pk.decode(pool, q, tables, lens, case["scale"], plan, plan_dev, ws, out=eager)
+    torch.cuda.synchronize()
+    out = torch.full(tuple(q.shape), float("nan"), device="cuda")
+    cap = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=cap):
+        pk.reshape_and_cache(pool, new_k, new_v, slots, cap)
+        pk.decode(pool, q, tables, lens, case["scale"], plan, plan_dev, ws, out=out, stream=cap)
+    for _ in range(4):
+        out.fill_(float("nan"))
+        ws.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(to_host(out)), bits(to_host(eager)))
 
 
 def test_physical_block_permutation_is_bitwise_invariant(pk):

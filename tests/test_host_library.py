@@ -159,8 +159,9 @@ def test_decode_plan_small_example():
         (1, 0, 1, 0, 0, 1, -1), (1, 0, 1, 1, 0, 1, -1),
         (2, 0, 19, 0, 0, 2, 0), (2, 0, 19, 1, 0, 2, 0), (2, 19, 19, 0, 1, 2, 0), (2, 19, 19, 1, 1, 2, 0),
         (3, 0, 32, 0, 0, 2, 16), (3, 0, 32, 1, 0, 2, 16), (3, 32, 31, 0, 1, 2, 16), (3, 32, 31, 1, 1, 2, 16)])
-    offs = plan.job_offsets()
-    loads = [int(jobs[offs[w]:offs[w + 1], 2].sum()) for w in range(6)]
+    tab = plan.job_table()
+    assert tab.shape == (plan.jobs_per_workgroup, 6, 8)
+    loads = [int(tab[:, w, 2].sum()) for w in range(6)]
     assert sorted(loads) == [32, 32, 32, 32, 38, 38]
     merges = [tuple(m) for m in plan.merges().tolist()]
     assert merges[:8] == [(0, g, 0, -1) for g in range(8)]
@@ -192,12 +193,14 @@ def test_decode_plan_covers_every_tile_once(seed):
             for t in range(tiles):
                 assert (s, blk, t) in covered
     assert len(covered) == sum(-(-int(L) // 16) for L in lens) * hb
-    offs = plan.job_offsets()
-    assert offs[0] == 0 and offs[-1] == plan.num_jobs and np.all(np.diff(offs) >= 0)
-    assert plan.num_workgroups <= nwg
+    assert plan.num_workgroups <= nwg and len(jobs) == plan.num_jobs
     if plan.num_jobs:
-        loads = [int(jobs[offs[w]:offs[w + 1], 2].sum()) for w in range(plan.num_workgroups)]
-        assert max(loads) <= np.ceil(sum(loads) / plan.num_workgroups) + jobs[:, 2].max()
+        tab = plan.job_table()
+        filled = tab[:, :, 2] > 0
+        # each workgroup's jobs fill a prefix of its column
+        assert np.all(filled[1:] <= filled[:-1])
+        loads = tab[:, :, 2].sum(axis=0)
+        assert loads.max() <= np.ceil(loads.sum() / plan.num_workgroups) + jobs[:, 2].max()
 
 
 def test_decode_plan_errors():
@@ -242,11 +245,12 @@ def test_abi_rejects_bad_decode_arguments_without_launching():
 
     def call(info=None, **kw):
         args = dict(q=p, out=p, out_dtype=0, tables=p, maxb=400, lens=p, nseq=2, hq=32, scale=0.1, plan=p,
-                    ws=None, wsb=0)
+                    ws=None, wsb=0, nk=None, nv=None)
         args.update(kw)
         return L.pa_decode(ctypes.byref(pool), args["q"], args["out"], args["out_dtype"], args["tables"],
                            args["maxb"], args["lens"], args["nseq"], args["hq"], ctypes.c_float(args["scale"]),
-                           args["plan"], ctypes.byref(info or plan.info), args["ws"], args["wsb"], None)
+                           args["nk"], args["nv"], args["plan"], ctypes.byref(info or plan.info), args["ws"],
+                           args["wsb"], None)
     ws = dict(ws=ctypes.c_void_p(0x50000), wsb=1 << 30)
     assert call(hq=30, **ws) == -1                  # not a multiple of Hkv
     assert call(hq=8 * 17, **ws) == -2              # group of 17 > 16
@@ -256,20 +260,25 @@ def test_abi_rejects_bad_decode_arguments_without_launching():
     assert call() == -1                             # workspace missing
     assert call(ws=ctypes.c_void_p(0x50000), wsb=16) == -1   # too small
     assert call(scale=float("inf"), **ws) == -1
+    assert call(nk=p, **ws) == -1                   # new_key without new_value
+    assert call(nk=ctypes.c_void_p(0x40008), nv=p, **ws) == -1   # misaligned new_key
     other = pk.decode_plan([100, 3000], 4, num_workgroups=4)
     assert call(info=other.info, **ws) == -1        # plan made for another head count
     bad = _lib.PaDecodePlanInfo.from_buffer_copy(plan.info)
     bad.jobs_at = 8
     assert call(info=bad, **ws) == -1               # inconsistent layout
+    bad = _lib.PaDecodePlanInfo.from_buffer_copy(plan.info)
+    bad.merges_at = 0
+    assert call(info=bad, **ws) == -1               # merge list overlaps the job table
     flagged = _lib.PaDecodePlanInfo.from_buffer_copy(plan.info)
     flagged.flags = 4
     assert call(info=flagged, **ws) == -1           # unknown flag bit
     for stage in (L.pa_decode_attention, L.pa_decode_merge_pieces):   # same checks on both stages
-        assert stage(ctypes.byref(pool), p, p, 0, p, 400, p, 2, 30, ctypes.c_float(0.1), p,
+        assert stage(ctypes.byref(pool), p, p, 0, p, 400, p, 2, 30, ctypes.c_float(0.1), None, None, p,
                      ctypes.byref(plan.info), ws["ws"], ws["wsb"], None) == -1
         assert b"pa_decode_" in L.pa_last_error()
     empty = pk.decode_plan([], 8, num_workgroups=4)
     assert call(info=empty.info) == 0               # nothing to do: OK, no launch
     pool32 = _pool(dtype=0, d=64)
-    assert L.pa_decode(ctypes.byref(pool32), p, p, 1, p, 400, p, 2, 8, ctypes.c_float(1.0), p,
+    assert L.pa_decode(ctypes.byref(pool32), p, p, 1, p, 400, p, 2, 8, ctypes.c_float(1.0), None, None, p,
                        ctypes.byref(plan.info), ws["ws"], ws["wsb"], None) == -2   # bf16 output, f32 pool
