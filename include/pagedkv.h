@@ -117,26 +117,26 @@ pa_status pa_copy_blocks(const pa_kv_pool* pool, const int32_t* pairs, int32_t n
  * written this step; L == 0 yields zeros.
  *
  * Scheduling.  A sequence's context is cut into 16-token tiles.  The host
- * plan (pa_decode_plan, which knows the lengths) cuts each sequence into
- * pieces of at most `max_piece_tiles` tiles and makes one job per (piece,
- * block of four KV heads); jobs are packed onto a fixed number of persistent
- * workgroups, largest first onto the least-loaded workgroup, so that every
- * workgroup carries about the same number of tiles.  The four waves of a
- * workgroup take the four KV heads of each job, so the head slices of a slot
- * row are read together.  A sequence cut into several pieces leaves one
- * (max, sum, accumulator) record per piece and KV head in the workspace; a
- * second launch on the same stream merges the records by log-sum-exp in
- * piece order.  The plan is one byte buffer that the caller copies to the
- * device with the other step inputs.
+ * plan (pa_decode_plan, which knows the lengths) lays the tile streams of
+ * every (sequence, block of four KV heads) end to end and cuts them into one
+ * chunk of equal work per persistent workgroup (work = tokens, plus a small
+ * charge per stream), at tile boundaries; the consecutive tiles of one
+ * stream in one chunk form a job (a piece of at most `max_piece_tiles`
+ * tiles).  The four waves of a workgroup take the four KV heads of each job,
+ * so the head slices of a slot row are read together.  A stream cut into
+ * several pieces leaves one (max, sum, accumulator) record per piece and KV
+ * head in the workspace; a second launch on the same stream merges the
+ * records by log-sum-exp in piece order.  The plan is one byte buffer that
+ * the caller copies to the device with the other step inputs.
  * ------------------------------------------------------------------------- */
 typedef struct pa_decode_job {
   int32_t seq;         /* sequence index */
   int32_t tile_begin;  /* first 16-token tile of the piece */
   int32_t tile_count;  /* tiles in the piece, 1..64; 0 marks an empty slot of the job table */
   int32_t head_block;  /* KV heads 4*head_block .. 4*head_block + 3 */
-  int32_t part;        /* piece index within the sequence */
-  int32_t num_parts;   /* pieces of the sequence (1: the job writes the output) */
-  int32_t record_base; /* workspace record of (seq, KV head g, piece p) = record_base + g * num_parts + p */
+  int32_t part;        /* piece index within the (sequence, head block) stream */
+  int32_t num_parts;   /* pieces of the stream (1: the job writes the output) */
+  int32_t record_base; /* workspace record of KV head 4*head_block + w, piece p: record_base + w * num_parts + p */
   int32_t reserved;
 } pa_decode_job;
 
@@ -151,7 +151,7 @@ typedef struct pa_decode_plan_info {
   int32_t num_workgroups; /* grid of the attention launch */
   int32_t num_jobs;
   int32_t num_merges;     /* grid of the merge launch (0: no merge launch) */
-  int32_t num_records;    /* workspace records, one per (sequence, KV head, piece) of cut sequences */
+  int32_t num_records;    /* workspace records, one per (sequence, KV head, piece) of cut streams */
   int32_t num_kv_heads;   /* KV heads the plan was made for */
   int32_t jobs_per_workgroup; /* rows of the job table */
   int32_t jobs_at;        /* byte offset (0) of the job table, pa_decode_job [jobs_per_workgroup][num_workgroups]:
@@ -178,8 +178,7 @@ int32_t pa_decode_default_workgroups(void);
  *   context_lens    : HOST int32 [num_seqs], each >= 0.
  *   num_kv_heads    : KV heads of the pool.
  *   num_workgroups  : persistent workgroups (pa_decode_default_workgroups()).
- *   max_piece_tiles : longest piece in tiles, 1..64; 0 chooses the average
- *                     tiles per workgroup (clamped to [4, 64]).
+ *   max_piece_tiles : longest job in tiles, 1..64; 0 means 64.
  *   plan            : HOST output buffer of `capacity` bytes (8-byte aligned).
  *   info            : filled on success, and with info->bytes set when the
  *                     capacity is too small (PA_ERR_INVALID) so the caller can

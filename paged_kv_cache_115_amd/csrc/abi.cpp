@@ -131,111 +131,118 @@ extern "C" pa_status pa_decode_plan(const int32_t* context_lens, int32_t num_seq
   if (capacity > 0 && (!plan || !pagedkv::aligned(plan, 8)))
     return fail(PA_ERR_INVALID, "pa_decode_plan: plan buffer NULL or not 8-byte aligned");
   const int64_t head_blocks = (num_kv_heads + 3) / 4;
-  int64_t total = 0;  // job tiles summed over head blocks
-  for (int32_t s = 0; s < num_seqs; ++s) {
+  const int64_t cap = max_piece_tiles > 0 ? max_piece_tiles : 64;
+  for (int32_t s = 0; s < num_seqs; ++s)
     if (context_lens[s] < 0) return fail(PA_ERR_INVALID, "pa_decode_plan: context_lens[%d] < 0", s);
-    total += ((int64_t)context_lens[s] + 15) / 16 * head_blocks;
-  }
-  int64_t cap = max_piece_tiles;
-  if (cap == 0) cap = std::min<int64_t>(64, std::max<int64_t>(4, (total + num_workgroups - 1) / num_workgroups));
 
-  // Pieces: each sequence's tiles in near-equal runs of at most `cap`.
-  size_t njobs = 0, nmerges = 0;
-  for (int32_t s = 0; s < num_seqs; ++s) {
-    const int64_t tiles = ((int64_t)context_lens[s] + 15) / 16;
-    const int64_t parts = (tiles + cap - 1) / cap;
-    njobs += (size_t)(parts * head_blocks);
-    nmerges += (parts != 1) ? (size_t)num_kv_heads : 0;
+  // Streams: the tiles of one (sequence, block of four KV heads), in
+  // alternating length order (longest, shortest, second longest, ...) so
+  // that no workgroup collects a run of short sequences.  Empty sequences
+  // have no stream.
+  std::vector<int32_t> by_len;
+  by_len.reserve(num_seqs);
+  for (int32_t s = 0; s < num_seqs; ++s)
+    if (context_lens[s] > 0) by_len.push_back(s);
+  std::stable_sort(by_len.begin(), by_len.end(),
+                   [&](int32_t x, int32_t y) { return context_lens[x] > context_lens[y]; });
+  std::vector<int32_t> seq_order;
+  seq_order.reserve(by_len.size());
+  for (size_t i = 0, j = by_len.size(); i < j;) {
+    seq_order.push_back(by_len[i++]);
+    if (i < j) seq_order.push_back(by_len[--j]);
   }
-  if (njobs > (size_t)INT32_MAX / 64 || nmerges > (size_t)INT32_MAX / 64)
-    return fail(PA_ERR_INVALID, "pa_decode_plan: plan too large");
-  std::vector<pa_decode_job> jobs;
+  // Cost of a tile = the tokens it holds (16, fewer in a sequence's last
+  // tile), plus a fixed charge at the start of every stream for its query
+  // and table fetch and its output.
+  constexpr int64_t kStreamCharge = 4;
+  int64_t total = 0, total_tiles = 0;
+  for (int32_t s : seq_order) {
+    total += (context_lens[s] + kStreamCharge) * head_blocks;
+    total_tiles += ((int64_t)context_lens[s] + 15) / 16 * head_blocks;
+  }
+  if (total_tiles > (int64_t)INT32_MAX / 64) return fail(PA_ERR_INVALID, "pa_decode_plan: plan too large");
+  const int64_t nwg = std::max<int64_t>(1, std::min<int64_t>(num_workgroups, total_tiles));
+
+  // Equal-work chunks: the streams are laid end to end and cut into nwg
+  // consecutive chunks of equal cost at tile boundaries (a tile goes to the
+  // workgroup whose share holds the tile's midpoint), so every workgroup's
+  // cost is within half a tile of total / nwg on either side.  Consecutive
+  // tiles of one stream on one workgroup form a job of at most `cap` tiles.
+  struct Piece {
+    int32_t wg;
+    pa_decode_job job;
+  };
+  std::vector<Piece> pieces;
   std::vector<pa_decode_merge> merges;
-  jobs.reserve(njobs);
-  merges.reserve(nmerges);
-  int64_t records = 0;
-  for (int32_t s = 0; s < num_seqs; ++s) {
-    const int64_t tiles = ((int64_t)context_lens[s] + 15) / 16;
-    if (tiles == 0) {
-      for (int32_t g = 0; g < num_kv_heads; ++g) merges.push_back(pa_decode_merge{s, g, 0, -1});
-      continue;
-    }
-    const int64_t parts = (tiles + cap - 1) / cap;
-    const int64_t base = parts > 1 ? records : -1;
-    if (parts > 1) {
-      for (int32_t g = 0; g < num_kv_heads; ++g)
-        merges.push_back(pa_decode_merge{s, g, (int32_t)parts, (int32_t)(records + g * parts)});
-      records += parts * num_kv_heads;
-    }
-    int64_t t0 = 0;
-    for (int64_t p = 0; p < parts; ++p) {
-      const int64_t cnt = tiles / parts + (p < tiles % parts ? 1 : 0);
-      for (int64_t hb = 0; hb < head_blocks; ++hb)
-        jobs.push_back(pa_decode_job{s, (int32_t)t0, (int32_t)cnt, (int32_t)hb, (int32_t)p, (int32_t)parts,
-                                     (int32_t)base, 0});
-      t0 += cnt;
+  int64_t records = 0, cum = 0;
+  std::vector<int32_t> stream_first;  // index of each stream's first piece
+  for (int32_t s : seq_order) {
+    const int32_t L = context_lens[s];
+    const int32_t tiles = (L + 15) / 16;
+    for (int64_t hb = 0; hb < head_blocks; ++hb) {
+      stream_first.push_back((int32_t)pieces.size());
+      const size_t first = pieces.size();
+      int64_t last_wg = -1;
+      for (int32_t t = 0; t < tiles; ++t) {
+        const int64_t c = std::min(16, L - 16 * t) + (t == 0 ? kStreamCharge : 0);
+        const int64_t wg = std::min<int64_t>(nwg - 1, ((2 * cum + c) * nwg) / (2 * total));
+        cum += c;
+        if (wg != last_wg || pieces.back().job.tile_count >= cap) {
+          pieces.push_back(Piece{(int32_t)wg, pa_decode_job{s, t, 0, (int32_t)hb, 0, 1, -1, 0}});
+          last_wg = wg;
+        }
+        pieces.back().job.tile_count += 1;
+      }
+      const int32_t parts = (int32_t)(pieces.size() - first);
+      if (parts > 1) {
+        const int64_t heads = std::min<int64_t>(4, num_kv_heads - 4 * hb);
+        for (int32_t p = 0; p < parts; ++p) {
+          pieces[first + p].job.part = p;
+          pieces[first + p].job.num_parts = parts;
+          pieces[first + p].job.record_base = (int32_t)records;
+        }
+        records += (int64_t)parts * heads;
+        if (records > INT32_MAX / 1024) return fail(PA_ERR_INVALID, "pa_decode_plan: plan too large");
+      }
     }
   }
-  if (records > INT32_MAX / 1024) return fail(PA_ERR_INVALID, "pa_decode_plan: plan too large");
+  // Merge rows, sequence by sequence: every KV head of an empty sequence
+  // (zeros) and of every cut stream.
+  {
+    std::vector<int32_t> stream_of_seq(num_seqs, -1);
+    for (size_t i = 0; i < seq_order.size(); ++i) stream_of_seq[seq_order[i]] = (int32_t)(i * head_blocks);
+    for (int32_t s = 0; s < num_seqs; ++s) {
+      if (context_lens[s] == 0) {
+        for (int32_t g = 0; g < num_kv_heads; ++g) merges.push_back(pa_decode_merge{s, g, 0, -1});
+        continue;
+      }
+      for (int64_t hb = 0; hb < head_blocks; ++hb) {
+        const pa_decode_job& j = pieces[stream_first[stream_of_seq[s] + hb]].job;
+        if (j.num_parts <= 1) continue;
+        for (int32_t g = 4 * (int32_t)hb; g < std::min<int32_t>(num_kv_heads, 4 * (int32_t)hb + 4); ++g)
+          merges.push_back(pa_decode_merge{s, g, j.num_parts, j.record_base + (g - 4 * (int32_t)hb) * j.num_parts});
+      }
+    }
+  }
+  if (pieces.size() > (size_t)INT32_MAX / 64 || merges.size() > (size_t)INT32_MAX / 64)
+    return fail(PA_ERR_INVALID, "pa_decode_plan: plan too large");
 
-  // Longest processing time first: each job, largest first, goes to the
-  // least-loaded workgroup.  Jobs keep sequence order inside a workgroup.
-  const int32_t nwg = (int32_t)std::min<int64_t>(num_workgroups, std::max<size_t>(jobs.size(), 1));
-  // Jobs by tile count, largest first, ties in generation order (a counting
-  // sort: counts are 1..cap).
-  std::vector<int32_t> order(jobs.size());
-  int64_t job_tiles = 0;
-  {
-    std::vector<int32_t> start(cap + 2, 0);
-    for (const pa_decode_job& j : jobs) {
-      start[cap - j.tile_count + 1] += 1;
-      job_tiles += j.tile_count;
-    }
-    for (int64_t c = 1; c <= cap + 1; ++c) start[c] += start[c - 1];
-    for (size_t i = 0; i < jobs.size(); ++i) order[start[cap - jobs[i].tile_count]++] = (int32_t)i;
-  }
-  // Least-loaded workgroup by a bucket queue over load values: loads only
-  // grow, so the smallest non-empty bucket is found by a pointer that only
-  // moves forward.  Workgroups of equal load leave in arrival order
-  // (initially by index).  A workgroup is chosen at a load no larger than
-  // job_tiles / nwg, so no load exceeds that plus one job.
-  std::vector<int32_t> owner(jobs.size());
-  {
-    const int64_t max_load = job_tiles / nwg + cap + 1;
-    std::vector<int32_t> head(max_load + 1, -1), tail(max_load + 1, -1), next(nwg, -1);
-    for (int32_t w = 0; w + 1 < nwg; ++w) next[w] = w + 1;
-    head[0] = 0;
-    tail[0] = nwg - 1;
-    int64_t cur = 0;
-    for (int32_t j : order) {
-      while (head[cur] < 0) ++cur;
-      const int32_t w = head[cur];
-      head[cur] = next[w];
-      if (head[cur] < 0) tail[cur] = -1;
-      owner[j] = w;
-      const int64_t nl = cur + jobs[j].tile_count;
-      next[w] = -1;
-      if (tail[nl] < 0)
-        head[nl] = w;
-      else
-        next[tail[nl]] = w;
-      tail[nl] = w;
-    }
-  }
   // Per-workgroup lists, column-major: slot k of workgroup b is entry
-  // k * nwg + b, so a workgroup reads its first job without an index load.
-  // Slots past a workgroup's last job are empty (tile_count 0).
+  // k * nwg + b, so a workgroup reads its first jobs without an index load.
+  // Slots past a workgroup's last job are empty (tile_count 0).  A
+  // workgroup's jobs keep stream order.
   std::vector<int32_t> count(nwg, 0);
-  for (int32_t o : owner) count[o] += 1;
+  for (const Piece& pc : pieces) count[pc.wg] += 1;
   int64_t per = 0;
   for (int32_t c : count) per = std::max<int64_t>(per, c);
   if (per * nwg > (int64_t)INT32_MAX / 64) return fail(PA_ERR_INVALID, "pa_decode_plan: plan too large");
   std::vector<pa_decode_job> table((size_t)(per * nwg), pa_decode_job{0, 0, 0, 0, 0, 0, -1, 0});
   std::vector<int32_t> fill(nwg, 0);
-  for (size_t j = 0; j < jobs.size(); ++j) table[(size_t)fill[owner[j]]++ * nwg + owner[j]] = jobs[j];
+  for (const Piece& pc : pieces) table[(size_t)fill[pc.wg]++ * nwg + pc.wg] = pc.job;
+  const std::vector<Piece>& jobs = pieces;
 
   pa_decode_plan_info in{};
-  in.num_workgroups = jobs.empty() ? 0 : nwg;
+  in.num_workgroups = jobs.empty() ? 0 : (int32_t)nwg;
   in.num_jobs = (int32_t)jobs.size();
   in.num_merges = (int32_t)merges.size();
   in.num_records = (int32_t)records;

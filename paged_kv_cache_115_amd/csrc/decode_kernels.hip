@@ -83,6 +83,25 @@ __device__ __forceinline__ uint32_t word(const uint4& v, int i) {
 
 __device__ __forceinline__ int32_t clamp_block(int32_t b, int32_t nb) { return min(max(b, 0), nb - 1); }
 
+// The plan, the context lengths and the merge list are never written while
+// a decode kernel runs.  Reading them through the constant address space lets
+// the compiler use scalar loads, which are tracked apart from the vector
+// memory queue: waiting for a job record then never waits for K/V loads or
+// output stores in flight.
+template <typename T>
+__device__ __forceinline__ const __attribute__((address_space(4))) T* as_const(const T* p) {
+  return (const __attribute__((address_space(4))) T*)(uintptr_t)p;
+}
+
+typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
+
+// Job record i of the plan, by scalar loads.
+__device__ __forceinline__ pa_decode_job load_job(const pa_decode_job* jobs, int64_t i) {
+  const auto* q = as_const(reinterpret_cast<const i32x4_t*>(jobs)) + 2 * i;
+  const i32x4_t x = q[0], y = q[1];
+  return pa_decode_job{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+}
+
 // Four consecutive output values at element index idx (a multiple of 4).
 __device__ __forceinline__ void store4(const DecodeArgs& a, int64_t idx, float x0, float x1, float x2, float x3) {
   if (a.out_bf16) {
@@ -103,29 +122,26 @@ __device__ __forceinline__ void store1(const DecodeArgs& a, int64_t idx, float x
 // Job fields as seen by one wavefront (all wave-uniform).
 struct JobView {
   int32_t seq, g, t0, cnt, L, rec;
+  bool idle;  // the wavefront's KV head is past the last one: read nothing, write nothing
 };
 
-// What job record jd holds for wavefront w: 1 work, 0 nothing for this
-// wavefront (its KV head is past the last one), -1 an empty slot.
-__device__ __forceinline__ int job_kind(const DecodeArgs& a, const pa_decode_job& jd, int w) {
-  if (jd.tile_count <= 0 || jd.tile_begin < 0) return -1;
-  const int32_t g = jd.head_block * kNW + w;
-  return (g >= 0 && g < a.num_kv_heads) ? 1 : 0;
-}
-
-// The fields of job record jd for wavefront w (job_kind(jd, w) == 1).  The
-// context length is the only dependent load.
+// The fields of job record jd for wavefront w.  The context length is the
+// only dependent load.  Any record (an empty slot included) gives in-range
+// addresses; a wavefront whose KV head is past the last one is idle.
 __device__ __forceinline__ void view_job(const DecodeArgs& a, const pa_decode_job& jd, int w, int B, JobView& v) {
-  v.g = jd.head_block * kNW + w;
-  v.cnt = min(jd.tile_count, kMaxTiles);
+  const int32_t g = jd.head_block * kNW + w;
+  v.idle = g < 0 || g >= a.num_kv_heads;
+  v.g = min(max(g, 0), a.num_kv_heads - 1);
+  v.cnt = min(max(jd.tile_count, 0), kMaxTiles);
   v.seq = min(max(jd.seq, 0), a.num_seqs - 1);
   v.t0 = max(jd.tile_begin, 0);
-  v.L = min(max(a.lens[v.seq], 0), a.max_blocks * B);
+  v.L = min(max(as_const(a.lens)[v.seq], 0), a.max_blocks * B);
   v.rec = -1;
   if (jd.num_parts > 1) {
-    const int64_t r = (int64_t)jd.record_base + (int64_t)v.g * jd.num_parts + jd.part;
+    const int64_t r = (int64_t)jd.record_base + (int64_t)w * jd.num_parts + jd.part;
     v.rec = (jd.record_base >= 0 && jd.part >= 0 && jd.part < jd.num_parts && r < a.num_records) ? (int32_t)r : -2;
   }
+  if (v.idle) v.rec = -2;
 }
 
 // --------------------------------------------------------------------------
@@ -150,19 +166,24 @@ __device__ __forceinline__ void load_ref(const DecodeArgs& a, const pa_decode_jo
   const int32_t t = J.v.t0 + lane;
   int32_t e0 = B == 8 ? 2 * t : t / kTilesPerBlock;
   e0 = min(max(e0, 0), a.max_blocks - 1);
-  J.tb0 = clamp_block(trow[e0], a.num_blocks);
-  J.tb1 = B == 8 ? clamp_block(trow[min(e0 + 1, a.max_blocks - 1)], a.num_blocks) : 0;
+  // Raw entries: they are range-checked when used (after readlane), so
+  // nothing waits for this load before the job's first tile is issued.
+  J.tb0 = trow[e0];
+  J.tb1 = B == 8 ? trow[min(e0 + 1, a.max_blocks - 1)] : 0;
 }
 
-// Q^T fragments: lane holds Q[head li][32*ks + 8*lq .. +8] (zero for li >= G).
+// Q^T fragments: lane holds Q[head li][32*ks + 8*lq .. +8].  Columns
+// li >= G repeat head G - 1: every column's softmax and accumulator are
+// independent and only columns below G are written, so the repeats cost
+// nothing and the loaded values are not touched before the job's first tile.
 __device__ __forceinline__ void load_q(const DecodeArgs& a, const JobView& v, int li, int lq, bf16x8_t (&qf)[4]) {
   constexpr int D = 128;
   const int G = a.group;
   const uint4* qrow = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.q) +
-                                                     ((int64_t)v.seq * a.num_q_heads + (int64_t)v.g * G + li) * D);
+                                                     ((int64_t)v.seq * a.num_q_heads + (int64_t)v.g * G + min(li, G - 1)) * D);
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
-    const uint4 x = li < G ? qrow[4 * ks + lq] : make_uint4(0, 0, 0, 0);
+    const uint4 x = qrow[4 * ks + lq];
     qf[ks] = __builtin_bit_cast(bf16x8_t, x);
   }
 }
@@ -209,13 +230,13 @@ __device__ __forceinline__ void load_bf16_tile(const DecodeArgs& a, int32_t g, i
   const int64_t blk_bytes = (int64_t)row_bytes * B;
   const char* kb = reinterpret_cast<const char*>(a.k) + (int64_t)g * D * 2;
   const char* vb = reinterpret_cast<const char*>(a.v) + (int64_t)g * D * 2;
-  const int32_t p0 = __builtin_amdgcn_readlane(tb0, t);
+  const int32_t p0 = clamp_block(__builtin_amdgcn_readlane(tb0, t), a.num_blocks);
   if (kFused && r_new >= 0) {
     // The tile holding this step's appended token (row r_new): that row
     // comes from the new key/value arrays, rows after it (past the context)
     // read the same row and are masked later, rows before it come from the
     // pool.  Per-lane addresses, so plain global loads.
-    const int32_t p1 = B == 8 ? __builtin_amdgcn_readlane(tb1, t) : p0;
+    const int32_t p1 = B == 8 ? clamp_block(__builtin_amdgcn_readlane(tb1, t), a.num_blocks) : p0;
     auto row_addr = [&](const char* base, int32_t row) {
       if (B == 8) return base + (int64_t)(row < 8 ? p0 : p1) * blk_bytes + (row & 7) * row_bytes;
       return base + (int64_t)p0 * blk_bytes + ((int64_t)((t0 + t) % kTilesPerBlock) * kTile + row) * row_bytes;
@@ -228,7 +249,7 @@ __device__ __forceinline__ void load_bf16_tile(const DecodeArgs& a, int32_t g, i
       vf[r] = load_global<kStream>(4 * lq + r >= r_new ? nv + 16 * li : row_addr(vb, 4 * lq + r) + 16 * li);
   } else if (B == 8) {
     // Rows 0..7 of the tile live in block p0, rows 8..15 in block p1.
-    const int32_t p1 = __builtin_amdgcn_readlane(tb1, t);
+    const int32_t p1 = clamp_block(__builtin_amdgcn_readlane(tb1, t), a.num_blocks);
     const int64_t kblk = (int64_t)(li < 8 ? p0 : p1) * blk_bytes;
     const int64_t vblk = (int64_t)(lq < 2 ? p0 : p1) * blk_bytes;
 #pragma unroll
@@ -269,13 +290,13 @@ __device__ __forceinline__ void store_appended_row(const DecodeArgs& a, const Jo
                                                    int lq, const uint4 (&kf)[4], const uint4 (&vf)[4]) {
   constexpr int kTilesPerBlock = B >= kTile ? B / kTile : 1;
   const int32_t r_new = J.v.L - 1 - kTile * (J.v.t0 + t);
-  if (r_new < 0 || r_new >= kTile) return;
+  if (J.v.idle || r_new < 0 || r_new >= kTile) return;
   const uint32_t row_bytes = (uint32_t)a.num_kv_heads * kHeadDim * 2;
   const int64_t blk_bytes = (int64_t)row_bytes * B;
-  const int32_t p0 = __builtin_amdgcn_readlane(J.tb0, t);
+  const int32_t p0 = clamp_block(__builtin_amdgcn_readlane(J.tb0, t), a.num_blocks);
   int64_t off;
   if (B == 8) {
-    const int32_t p1 = __builtin_amdgcn_readlane(J.tb1, t);
+    const int32_t p1 = clamp_block(__builtin_amdgcn_readlane(J.tb1, t), a.num_blocks);
     off = (int64_t)(r_new < 8 ? p0 : p1) * blk_bytes + (r_new & 7) * row_bytes;
   } else {
     off = (int64_t)p0 * blk_bytes + ((int64_t)((J.v.t0 + t) % kTilesPerBlock) * kTile + r_new) * row_bytes;
@@ -364,34 +385,115 @@ __device__ __forceinline__ void compute_bf16_tile(const DecodeArgs& a, const Job
   }
 }
 
-// End of a job: output (whole sequence) or the piece's record.  Lane (li, lq)
-// holds, for head li, accumulator rows 4*lq + r of instance c: dims
-// 32*lq + 8*r + c.
+// Finished jobs are staged in LDS and written to memory after the
+// wavefront's last job (once the staging area is full, later jobs are
+// written directly).  On gfx9 the
+// vector memory counter retires loads and stores in issue order, so a store
+// issued between tile loads makes every later tile wait for the store's
+// acknowledgement; staging keeps the tile stream free of stores.
+//
+// Per wavefront: kStageFloats floats of accumulators (an entry holds, for the
+// G live columns, the 32 values of each lane (li, lq): entry float index
+// ((k * 4 + lq) * G + li) * 4 + c for k = 0..7, c = 0..3, i.e. o[4 * (k & 1) + c][k >> 1]),
+// then (m, l) per (entry, column), then (seq, g, record) per entry.
+constexpr int kStageMax = 7;                      // entries per wavefront
+constexpr int kStageFloats = kStageMax * 4 * 128; // accumulator floats per wavefront (G = 4 fills 7 entries)
+constexpr int kStageWaveFloats = kStageFloats + kStageMax * 16 * 2 + kStageMax * 4;
+
+struct Stage {
+  float* o;      // accumulator entries
+  float* ml;     // [entry][16][2]
+  int32_t* meta; // [entry][4]
+  int n, cap;    // staged entries, capacity for this G
+};
+
+// Write staged entries to out / the workspace records, then empty the stage.
+__device__ __forceinline__ void flush_stage(const DecodeArgs& a, Stage& sg, int li, int lq) {
+  constexpr int D = 128;
+  const int G = a.group;
+  for (int e = 0; e < sg.n; ++e) {
+    const int32_t seq = __builtin_amdgcn_readfirstlane(sg.meta[4 * e + 0]);
+    const int32_t g = __builtin_amdgcn_readfirstlane(sg.meta[4 * e + 1]);
+    const int32_t rec = __builtin_amdgcn_readfirstlane(sg.meta[4 * e + 2]);
+    if (li >= G) continue;
+    const float* eo = sg.o + e * 128 * G;
+    float4 v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = *reinterpret_cast<const float4*>(eo + ((k * 4 + lq) * G + li) * 4);
+    const float m = sg.ml[(e * 16 + li) * 2], lt = sg.ml[(e * 16 + li) * 2 + 1];
+    if (rec < 0) {
+      const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+      const int64_t base = ((int64_t)seq * a.num_q_heads + (int64_t)g * G + li) * D + 32 * lq;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        store4(a, base + 8 * r, v[2 * r].x * inv, v[2 * r].y * inv, v[2 * r].z * inv, v[2 * r].w * inv);
+        store4(a, base + 8 * r + 4, v[2 * r + 1].x * inv, v[2 * r + 1].y * inv, v[2 * r + 1].z * inv,
+               v[2 * r + 1].w * inv);
+      }
+    } else {
+      const int64_t rr = (int64_t)rec * G + li;
+      float* po = a.partial_o + rr * D + 32 * lq;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        *reinterpret_cast<float4*>(po + 8 * r) = v[2 * r];
+        *reinterpret_cast<float4*>(po + 8 * r + 4) = v[2 * r + 1];
+      }
+      if (lq == 0) *reinterpret_cast<float2*>(a.partial_ml + 2 * rr) = make_float2(m, lt);
+    }
+  }
+  sg.n = 0;
+}
+
+// End of a job: stage the output (whole sequence) or the piece's record.
+// Lane (li, lq) holds, for head li, accumulator rows 4*lq + r of instance c:
+// dims 32*lq + 8*r + c.  With the stage full, the job is written directly.
 __device__ __forceinline__ void finish_bf16_job(const DecodeArgs& a, const JobView& v, int li, int lq,
-                                                const SoftmaxState& st) {
+                                                const SoftmaxState& st, Stage& sg) {
   constexpr int D = 128;
   const int G = a.group;
   float lt = st.l + __shfl_xor(st.l, 16);
   lt = lt + __shfl_xor(lt, 32);
-  if (li >= G || v.rec == -2) return;
-  if (v.rec < 0) {
-    const float inv = lt > 0.f ? 1.0f / lt : 0.f;
-    const int64_t base = ((int64_t)v.seq * a.num_q_heads + (int64_t)v.g * G + li) * D + 32 * lq;
+  if (v.rec == -2) return;
+  if (sg.n == sg.cap) {
+    if (li >= G) return;
+    if (v.rec < 0) {
+      const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+      const int64_t base = ((int64_t)v.seq * a.num_q_heads + (int64_t)v.g * G + li) * D + 32 * lq;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      store4(a, base + 8 * r, st.o[0][r] * inv, st.o[1][r] * inv, st.o[2][r] * inv, st.o[3][r] * inv);
-      store4(a, base + 8 * r + 4, st.o[4][r] * inv, st.o[5][r] * inv, st.o[6][r] * inv, st.o[7][r] * inv);
-    }
-  } else {
-    const int64_t rec = (int64_t)v.rec * G + li;
-    float* po = a.partial_o + rec * D + 32 * lq;
+      for (int r = 0; r < 4; ++r) {
+        store4(a, base + 8 * r, st.o[0][r] * inv, st.o[1][r] * inv, st.o[2][r] * inv, st.o[3][r] * inv);
+        store4(a, base + 8 * r + 4, st.o[4][r] * inv, st.o[5][r] * inv, st.o[6][r] * inv, st.o[7][r] * inv);
+      }
+    } else {
+      const int64_t rec = (int64_t)v.rec * G + li;
+      float* po = a.partial_o + rec * D + 32 * lq;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      *reinterpret_cast<float4*>(po + 8 * r) = make_float4(st.o[0][r], st.o[1][r], st.o[2][r], st.o[3][r]);
-      *reinterpret_cast<float4*>(po + 8 * r + 4) = make_float4(st.o[4][r], st.o[5][r], st.o[6][r], st.o[7][r]);
+      for (int r = 0; r < 4; ++r) {
+        *reinterpret_cast<float4*>(po + 8 * r) = make_float4(st.o[0][r], st.o[1][r], st.o[2][r], st.o[3][r]);
+        *reinterpret_cast<float4*>(po + 8 * r + 4) = make_float4(st.o[4][r], st.o[5][r], st.o[6][r], st.o[7][r]);
+      }
+      if (lq == 0) *reinterpret_cast<float2*>(a.partial_ml + 2 * rec) = make_float2(st.m, lt);
     }
-    if (lq == 0) *reinterpret_cast<float2*>(a.partial_ml + 2 * rec) = make_float2(st.m, lt);
+    return;
   }
+  const int e = sg.n;
+  if (li < G) {
+    float* eo = sg.o + e * 128 * G;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      *reinterpret_cast<float4*>(eo + (((2 * r) * 4 + lq) * G + li) * 4) =
+          make_float4(st.o[0][r], st.o[1][r], st.o[2][r], st.o[3][r]);
+      *reinterpret_cast<float4*>(eo + (((2 * r + 1) * 4 + lq) * G + li) * 4) =
+          make_float4(st.o[4][r], st.o[5][r], st.o[6][r], st.o[7][r]);
+    }
+    if (lq == 0) *reinterpret_cast<float2*>(sg.ml + (e * 16 + li) * 2) = make_float2(st.m, lt);
+  }
+  if ((li | lq) == 0) {
+    sg.meta[4 * e + 0] = v.seq;
+    sg.meta[4 * e + 1] = v.g;
+    sg.meta[4 * e + 2] = v.rec;
+  }
+  sg.n = e + 1;
 }
 
 template <int B, bool kStream, bool kFused>
@@ -401,40 +503,31 @@ __global__ __launch_bounds__(kNW * 64, kWavesPerSimd) void decode_bf16_kernel(De
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: keeps job fields in SGPRs
   const int li = lane & 15;  // MFMA row / column within a 16-lane group
   const int lq = lane >> 4;  // which 16-lane group
+  __shared__ float stage_lds[kNW * kStageWaveFloats];
+  Stage sg;
+  sg.o = stage_lds + w * kStageWaveFloats;
+  sg.ml = sg.o + kStageFloats;
+  sg.meta = reinterpret_cast<int32_t*>(sg.ml + kStageMax * 16 * 2);
+  sg.n = 0;
+  sg.cap = min(kStageMax, kStageFloats / (128 * a.group));
   // The workgroup's jobs are the slots k = 0, 1, ... of its column of the
-  // job table (entry k * num_workgroups + blockIdx.x); jobs are named by slot.
-  int32_t jend = a.jobs_per_workgroup;
+  // job table (entry k * num_workgroups + blockIdx.x); an empty slot
+  // (tile_count 0) ends the column.
+  const int32_t jend = a.jobs_per_workgroup;
   if (jend <= 0) return;
-  auto record = [&](int32_t k) { return a.jobs[k * a.num_workgroups + (int32_t)blockIdx.x]; };
-  // Next slot >= k in which this wavefront has work (jend: none; an empty
-  // slot ends the column).
-  auto next_job = [&](int32_t k) {
-    for (; k < jend; ++k) {
-      const int kind = job_kind(a, record(k), w);
-      if (kind > 0) return k;
-      if (kind < 0) return jend;
-    }
-    return jend;
-  };
-  // The first three slots are read together: unless a slot has nothing for
-  // this wavefront (KV-head counts that are not a multiple of four), they
-  // are the first three jobs, and their table entries, lengths and queries
-  // are requested right after.
-  const int k0 = job_kind(a, record(0), w);
-  const int k1 = jend > 1 ? job_kind(a, record(min(1, jend - 1)), w) : -1;
-  const int k2 = jend > 2 ? job_kind(a, record(min(2, jend - 1)), w) : -1;
-  int32_t jc, jn, jn2;
-  const bool fast = k0 > 0 && k1 != 0 && (k1 < 0 || k2 != 0);
-  if (fast) {
-    jc = 0;
-    jn = k1 > 0 ? 1 : jend;
-    jn2 = (k1 > 0 && k2 > 0) ? 2 : jend;
-  } else {
-    jc = next_job(0);
-    if (jc >= jend) return;
-    jn = next_job(jc + 1);
-    jn2 = jn < jend ? next_job(jn + 1) : jend;
-  }
+  auto record = [&](int32_t k) { return load_job(a.jobs, (int64_t)min(k, jend - 1) * a.num_workgroups + blockIdx.x); };
+  // Job lookahead.  cur, nxt and nx2 hold job fields, table entries and
+  // lengths; r3 is the raw record of slot s3, the one after nx2, requested a
+  // whole job before its fields are needed.  No decision waits on a load
+  // issued at the same job boundary: at a boundary the wavefront only
+  // consumes r3 (which has long arrived) and requests the next record.
+  // The first four records are requested together.
+  const pa_decode_job r0 = record(0), r1 = record(1), r2 = record(2);
+  pa_decode_job r3 = record(3);
+  int32_t s3 = 3;
+  if (r0.tile_count <= 0) return;
+  bool hn = jend > 1 && r1.tile_count > 0;
+  bool hn2 = hn && jend > 2 && r2.tile_count > 0;
 
   // The wavefront's tiles form one stream.  Position x is tile x - x0 of the
   // current job (x0 = its first position); the positions past it belong to
@@ -442,13 +535,12 @@ __global__ __launch_bounds__(kNW * 64, kWavesPerSimd) void decode_bf16_kernel(De
   // positions x .. x + kDepth: while tile x is computed the loads of the next
   // kDepth are in flight.  Every load is issued unconditionally (a position
   // past the end of the stream, or past the jobs known so far, reloads the
-  // current job's last tile, which the cache still holds), so the waits the
+  // current job's last tile without fetching anything), so the waits the
   // compiler inserts count exactly the loads in flight.
   JobRef<B> cur, nxt, nx2;
-  load_ref<B>(a, record(jc), w, lane, cur);
-  load_ref<B>(a, record(jn < jend ? jn : jc), w, lane, nxt);
-  load_ref<B>(a, record(jn2 < jend ? jn2 : jc), w, lane, nx2);
-  bool hn = jn < jend, hn2 = jn2 < jend;
+  load_ref<B>(a, r0, w, lane, cur);
+  load_ref<B>(a, r1, w, lane, nxt);
+  load_ref<B>(a, r2, w, lane, nx2);
   bf16x8_t qc[4], qn[4];
   load_q(a, cur.v, li, lq, qc);
   load_q(a, nxt.v, li, lq, qn);
@@ -471,7 +563,8 @@ __global__ __launch_bounds__(kNW * 64, kWavesPerSimd) void decode_bf16_kernel(De
     const int32_t tb0 = in_n ? nxt.tb0 : in_n2 ? nx2.tb0 : cur.tb0;
     const int32_t tb1 = in_n ? nxt.tb1 : in_n2 ? nx2.tb1 : cur.tb1;
     const int32_t L = in_n ? nxt.v.L : in_n2 ? nx2.v.L : cur.v.L;
-    const bool live = in_c || in_n || in_n2;
+    const bool idle = in_n ? nxt.v.idle : in_n2 ? nx2.v.idle : cur.v.idle;
+    const bool live = (in_c || in_n || in_n2) && !idle;
     const int32_t rows = live ? L - kTile * (t0 + t) : 0;
     // Row of this step's appended token in the tile, when the append is fused
     // into this launch and the tile holds it.
@@ -490,21 +583,21 @@ __global__ __launch_bounds__(kNW * 64, kWavesPerSimd) void decode_bf16_kernel(De
     compute_bf16_tile(a, cur.v, qc, x - x0, lq, ks, vs, st);
     ++x;
     if (x - x0 < cur.v.cnt) return true;
-    finish_bf16_job(a, cur.v, li, lq, st);
+    finish_bf16_job(a, cur.v, li, lq, st, sg);
     if (!hn) return false;
-    const int32_t js = jn;  // slot of the job that becomes current (< jend)
     x0 += cur.v.cnt;
     cur = nxt;
 #pragma unroll
     for (int k = 0; k < 4; ++k) qc[k] = qn[k];
     nxt = nx2;
     hn = hn2;
-    jn = jn2;
-    jn2 = hn ? next_job(jn + 1) : jend;
-    hn2 = jn2 < jend;
-    // Without a job after next, the third reference is a copy of a known
-    // one (never used): only slots below jend are read.
-    load_ref<B>(a, record(hn2 ? jn2 : hn ? jn : js), w, lane, nx2);
+    // nx2 becomes the job of record r3 (requested one job ago); then the
+    // record after it is requested.  Past the column (or at an empty slot)
+    // the fields are in-range copies that are never used.
+    hn2 = hn && s3 < jend && r3.tile_count > 0;
+    load_ref<B>(a, r3, w, lane, nx2);
+    ++s3;
+    r3 = record(s3);
     load_q(a, nxt.v, li, lq, qn);
     st.reset();
     return true;
@@ -518,7 +611,8 @@ __global__ __launch_bounds__(kNW * 64, kWavesPerSimd) void decode_bf16_kernel(De
     for (int u = 0; u < kSlots; ++u)
       if (!step(kf[u], vf[u], kf[(u + kDepth) % kSlots], vf[(u + kDepth) % kSlots])) goto done;
   }
-done:;
+done:
+  flush_stage(a, sg, li, lq);
 }
 
 // --------------------------------------------------------------------------
@@ -532,12 +626,11 @@ __global__ __launch_bounds__(kNW * 64) void decode_f32_kernel(DecodeArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: keeps job fields in SGPRs
   const int G = a.group;
   for (int32_t k = 0; k < a.jobs_per_workgroup; ++k) {
-    const pa_decode_job jd = a.jobs[k * a.num_workgroups + (int32_t)blockIdx.x];
-    const int kind = job_kind(a, jd, w);
-    if (kind < 0) break;
-    if (kind == 0) continue;
+    const pa_decode_job jd = load_job(a.jobs, (int64_t)k * a.num_workgroups + blockIdx.x);
+    if (jd.tile_count <= 0) break;
     JobView v;
     view_job(a, jd, w, B, v);
+    if (v.idle) continue;
     float qv[kMaxGroup][DPL], m_run[kMaxGroup], l_run[kMaxGroup], o[kMaxGroup][DPL];
     const float* qrow = reinterpret_cast<const float*>(a.q) + ((int64_t)v.seq * a.num_q_heads + (int64_t)v.g * G) * D;
 #pragma unroll
@@ -638,7 +731,8 @@ __device__ __forceinline__ void store2(const DecodeArgs& a, int64_t idx, float x
 template <int D>
 __global__ __launch_bounds__(kMaxMergeThreads) void merge_partials_kernel(DecodeArgs a) {
   constexpr int kBatch = 8;
-  const pa_decode_merge mg = a.merges[blockIdx.x];
+  const i32x4_t mv = as_const(reinterpret_cast<const i32x4_t*>(a.merges))[blockIdx.x];
+  const pa_decode_merge mg{mv[0], mv[1], mv[2], mv[3]};
   if (mg.seq < 0 || mg.seq >= a.num_seqs || mg.kv_head < 0 || mg.kv_head >= a.num_kv_heads) return;
   const int G = a.group;
   const int e = 2 * (int)threadIdx.x;

@@ -149,25 +149,108 @@ def test_block_manager_errors():
         bm.export([1, 42], 4)
 
 
+def _plan_model(lens, hkv, nwg, cap):
+    """Independent statement of the schedule pa_decode_plan documents:
+    (sequence, head block) tile streams in alternating length order, laid end
+    to end and cut into nwg chunks of equal cost (tokens + 4 per stream) at
+    tile boundaries by the tile midpoint; consecutive tiles of a stream in a
+    chunk form jobs of at most cap tiles.  Returns (jobs per workgroup,
+    merge rows, records)."""
+    lens = [int(x) for x in lens]
+    hb = -(-hkv // 4)
+    cap = cap or 64
+    live = sorted([s for s in range(len(lens)) if lens[s] > 0], key=lambda s: -lens[s])
+    order = []
+    while live:
+        order.append(live.pop(0))
+        if live:
+            order.append(live.pop())
+    total = sum((lens[s] + 4) * hb for s in order)
+    tiles = sum(-(-lens[s] // 16) * hb for s in order)
+    nwg = max(1, min(nwg, tiles))
+    cum, records = 0, 0
+    wg_jobs = [[] for _ in range(nwg)]
+    streams = {}
+    for s in order:
+        for h in range(hb):
+            pcs = []
+            for t in range(-(-lens[s] // 16)):
+                c = min(16, lens[s] - 16 * t) + (4 if t == 0 else 0)
+                w = min(nwg - 1, ((2 * cum + c) * nwg) // (2 * total))
+                cum += c
+                if not pcs or pcs[-1][0] != w or pcs[-1][2] >= cap:
+                    pcs.append([w, t, 0])
+                pcs[-1][2] += 1
+            base = -1
+            if len(pcs) > 1:
+                base = records
+                records += len(pcs) * min(4, hkv - 4 * h)
+            for p, (w, t0, cnt) in enumerate(pcs):
+                wg_jobs[w].append((s, t0, cnt, h, p if len(pcs) > 1 else 0, len(pcs), base))
+            streams[(s, h)] = (len(pcs), base)
+    merges = []
+    for s in range(len(lens)):
+        if lens[s] == 0:
+            merges += [(s, g, 0, -1) for g in range(hkv)]
+            continue
+        for h in range(hb):
+            n, base = streams[(s, h)]
+            if n > 1:
+                merges += [(s, g, n, base + (g - 4 * h) * n) for g in range(4 * h, min(hkv, 4 * h + 4))]
+    return wg_jobs, merges, records
+
+
+def _plan_lists(plan):
+    tab = plan.job_table()
+    return [[tuple(j[:7]) for j in tab[:, b].tolist() if j[2] > 0] for b in range(tab.shape[1])]
+
+
 def test_decode_plan_small_example():
     """Lengths 0, 5, 600, 1000 (0, 1, 38, 63 tiles), 8 KV heads (two head
-    blocks), 6 workgroups: 204 job tiles, pieces of at most 34 tiles."""
+    blocks), 6 workgroups.  Stream order 1000, 5, 600; costs 1004, 9, 604 per
+    head block, 3234 in all, 539 per workgroup."""
     plan = pk.decode_plan([0, 5, 600, 1000], 8, num_workgroups=6)
-    assert (plan.num_workgroups, plan.num_jobs, plan.num_merges, plan.num_records) == (6, 10, 24, 32)
-    jobs = plan.jobs()
-    assert sorted(map(tuple, jobs[:, :7].tolist())) == sorted([
-        (1, 0, 1, 0, 0, 1, -1), (1, 0, 1, 1, 0, 1, -1),
-        (2, 0, 19, 0, 0, 2, 0), (2, 0, 19, 1, 0, 2, 0), (2, 19, 19, 0, 1, 2, 0), (2, 19, 19, 1, 1, 2, 0),
-        (3, 0, 32, 0, 0, 2, 16), (3, 0, 32, 1, 0, 2, 16), (3, 32, 31, 0, 1, 2, 16), (3, 32, 31, 1, 1, 2, 16)])
-    tab = plan.job_table()
-    assert tab.shape == (plan.jobs_per_workgroup, 6, 8)
-    loads = [int(tab[:, w, 2].sum()) for w in range(6)]
-    assert sorted(loads) == [32, 32, 32, 32, 38, 38]
+    lists = _plan_lists(plan)
+    # Worked by hand: a tile of cost c ending at cumulative cost e goes to
+    # workgroup floor((e - c/2) / 539); e.g. the 1000-token stream of head
+    # block 0 has midpoints 10, 28, 44, ... so its tiles 0..32 go to
+    # workgroup 0 (midpoint 524) and 33..62 to workgroup 1.
+    assert lists == [
+        [(3, 0, 33, 0, 0, 2, 0)],
+        [(3, 33, 30, 0, 1, 2, 0), (3, 0, 4, 1, 0, 3, 8)],
+        [(3, 4, 34, 1, 1, 3, 8)],
+        [(3, 38, 25, 1, 2, 3, 8), (1, 0, 1, 0, 0, 1, -1), (1, 0, 1, 1, 0, 1, -1), (2, 0, 8, 0, 0, 2, 20)],
+        [(2, 8, 30, 0, 1, 2, 20), (2, 0, 4, 1, 0, 2, 28)],
+        [(2, 4, 34, 1, 1, 2, 28)]]
+    assert lists == _plan_model([0, 5, 600, 1000], 8, 6, 0)[0]
+    tiles = [sum(j[2] for j in l) for l in lists]
+    assert sum(tiles) == 2 * (63 + 1 + 38)
     merges = [tuple(m) for m in plan.merges().tolist()]
     assert merges[:8] == [(0, g, 0, -1) for g in range(8)]
-    assert merges[8:16] == [(2, g, 2, 2 * g) for g in range(8)]
-    assert merges[16:] == [(3, g, 2, 16 + 2 * g) for g in range(8)]
-    assert pk.decode_workspace_bytes(plan, 32, 128) >= 32 * 4 * 130 * 4
+    assert merges[8:12] == [(2, g, 2, 20 + 2 * g) for g in range(4)]
+    assert merges[12:16] == [(2, g, 2, 28 + 2 * (g - 4)) for g in range(4, 8)]
+    assert merges[16:20] == [(3, g, 2, 2 * g) for g in range(4)]
+    assert merges[20:] == [(3, g, 3, 8 + 3 * (g - 4)) for g in range(4, 8)]
+    assert plan.num_records == 36
+    assert pk.decode_workspace_bytes(plan, 32, 128) >= 36 * 4 * 130 * 4
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_decode_plan_matches_model(seed):
+    rng = np.random.default_rng(100 + seed)
+    lens = rng.integers(0, 3000, size=int(rng.integers(1, 60)))
+    lens[rng.random(len(lens)) < 0.2] = int(rng.integers(0, 40))
+    hkv = int(rng.choice([1, 3, 4, 8, 13]))
+    nwg = int(rng.integers(1, 900))
+    cap = int(rng.choice([0, 1, 5, 64]))
+    plan = pk.decode_plan(lens, hkv, num_workgroups=nwg, max_piece_tiles=cap)
+    wg_jobs, merges, records = _plan_model(lens, hkv, nwg, cap)
+    if plan.num_jobs == 0:
+        assert sum(map(len, wg_jobs)) == 0
+    else:
+        assert _plan_lists(plan) == wg_jobs
+    assert [tuple(m) for m in plan.merges().tolist()] == merges
+    assert plan.num_records == records
 
 
 @pytest.mark.parametrize("seed", range(6))
@@ -199,8 +282,17 @@ def test_decode_plan_covers_every_tile_once(seed):
         filled = tab[:, :, 2] > 0
         # each workgroup's jobs fill a prefix of its column
         assert np.all(filled[1:] <= filled[:-1])
-        loads = tab[:, :, 2].sum(axis=0)
-        assert loads.max() <= np.ceil(loads.sum() / plan.num_workgroups) + jobs[:, 2].max()
+        # cost of a workgroup (tokens + 4 per stream start) within the costs
+        # of half its first and half its last tile (<= 20 each) of the mean
+        cost = np.zeros(plan.num_workgroups)
+        for b in range(plan.num_workgroups):
+            for seq, t0, cnt, *_ in tab[:, b].tolist():
+                if cnt > 0:
+                    cost[b] += sum(min(16, int(lens[seq]) - 16 * t) + (4 if t == 0 else 0) for t in range(t0, t0 + cnt))
+        mean = cost.sum() / plan.num_workgroups
+        assert cost.max() <= mean + 20 + 1e-9
+        if mean >= 40:
+            assert cost.min() >= mean - 20 - 1e-9
 
 
 def test_decode_plan_errors():
