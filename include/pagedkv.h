@@ -137,7 +137,7 @@ typedef struct pa_decode_job {
   int32_t part;        /* piece index within the (sequence, head block) stream */
   int32_t num_parts;   /* pieces of the stream (1: the job writes the output) */
   int32_t record_base; /* workspace record of KV head 4*head_block + w, piece p: record_base + w * num_parts + p */
-  int32_t reserved;
+  int32_t context_len; /* context_lens[seq] as planned: the kernels take the length from here */
 } pa_decode_job;
 
 typedef struct pa_decode_merge {
@@ -160,7 +160,13 @@ typedef struct pa_decode_plan_info {
   int32_t merges_at;      /* byte offset of pa_decode_merge [num_merges] */
   int32_t bytes;          /* total plan bytes */
   int32_t flags;          /* PA_DECODE_* bits; pa_decode_plan sets 0, the caller may set them */
+  int32_t schedule;       /* PA_SCHEDULE_* the plan was built with (informational) */
 } pa_decode_plan_info;
+
+/* Schedules pa_decode_plan builds and chooses between. */
+#define PA_SCHEDULE_AUTO (-1) /* build both, keep the cheaper (pa_decode_plan) */
+#define PA_SCHEDULE_CHUNKS 0  /* equal-work chunks of the concatenated tile streams */
+#define PA_SCHEDULE_LPT 1     /* pieces of at most a workgroup's share, largest first onto the least loaded */
 
 /* flags bit: some physical blocks are named by more than one sequence of the
  * batch (forked, shared prefixes; pa_bm_get_stats().shared_blocks > 0).  K/V
@@ -178,7 +184,8 @@ int32_t pa_decode_default_workgroups(void);
  *   context_lens    : HOST int32 [num_seqs], each >= 0.
  *   num_kv_heads    : KV heads of the pool.
  *   num_workgroups  : persistent workgroups (pa_decode_default_workgroups()).
- *   max_piece_tiles : longest job in tiles, 1..64; 0 means 64.
+ *   max_piece_tiles : longest job in tiles, 1..64; 0: the schedule's default
+ *                     (see pa_decode_plan_schedule).
  *   plan            : HOST output buffer of `capacity` bytes (8-byte aligned).
  *   info            : filled on success, and with info->bytes set when the
  *                     capacity is too small (PA_ERR_INVALID) so the caller can
@@ -187,6 +194,24 @@ int32_t pa_decode_default_workgroups(void);
 pa_status pa_decode_plan(const int32_t* context_lens, int32_t num_seqs, int32_t num_kv_heads,
                          int32_t num_workgroups, int32_t max_piece_tiles, void* plan,
                          size_t capacity, pa_decode_plan_info* info);
+
+/* pa_decode_plan with the schedule named: PA_SCHEDULE_AUTO (what
+ * pa_decode_plan does), PA_SCHEDULE_CHUNKS or PA_SCHEDULE_LPT.
+ *
+ * PA_SCHEDULE_CHUNKS: the (sequence, head block) tile streams, in alternating
+ *   length order (longest, shortest, second longest, ...), are laid end to
+ *   end and cut into one chunk of equal cost per workgroup (cost = tokens, plus
+ *   4 per stream start), at tile boundaries: a tile goes to the workgroup
+ *   whose share holds its midpoint.  A stream's records are per stream.
+ * PA_SCHEDULE_LPT: each sequence is cut into near-equal pieces of at most
+ *   max_piece_tiles tiles (0: the average tiles per workgroup, clamped to
+ *   [4, 64]); one job per (piece, head block); jobs, largest first, go to the
+ *   least-loaded workgroup.  Fewer jobs, coarser balance.
+ * Automatic choice: the schedule whose busiest workgroup costs less, with a
+ * job charged as 56 tokens (calibrated on MI355X), the chunks on a tie. */
+pa_status pa_decode_plan_schedule(const int32_t* context_lens, int32_t num_seqs, int32_t num_kv_heads,
+                                  int32_t num_workgroups, int32_t max_piece_tiles, int32_t schedule, void* plan,
+                                  size_t capacity, pa_decode_plan_info* info);
 
 /* Bytes of device workspace pa_decode needs for a plan (0 when no sequence is
  * cut).  The workspace needs no initialisation; it carries records from the

@@ -106,7 +106,8 @@ class DecodePlan:
         self.info = info
 
     def __getattr__(self, name):
-        if name in ("num_workgroups", "num_jobs", "num_merges", "num_records", "num_kv_heads", "jobs_per_workgroup"):
+        if name in ("num_workgroups", "num_jobs", "num_merges", "num_records", "num_kv_heads", "jobs_per_workgroup",
+                    "schedule"):
             return getattr(self.info, name)
         raise AttributeError(name)
 
@@ -118,7 +119,7 @@ class DecodePlan:
             self.info.jobs_per_workgroup, self.info.num_workgroups, 8)
 
     def jobs(self) -> np.ndarray:
-        """int32 [num_jobs, 8]: seq, tile_begin, tile_count, head_block, part, num_parts, record_base, 0;
+        """int32 [num_jobs, 8]: seq, tile_begin, tile_count, head_block, part, num_parts, record_base, context_len;
         workgroup after workgroup, each in its processing order."""
         t = self.job_table().transpose(1, 0, 2).reshape(-1, 8)
         return t[t[:, 2] > 0]
@@ -145,11 +146,15 @@ def default_workgroups() -> int:
     return n
 
 
+SCHEDULE_AUTO, SCHEDULE_CHUNKS, SCHEDULE_LPT = -1, 0, 1
+
+
 def decode_plan(context_lens, num_kv_heads: int, num_workgroups: int | None = None,
-                max_piece_tiles: int = 0, shared_kv: bool = False) -> DecodePlan:
-    """pa_decode_plan.  num_workgroups defaults to default_workgroups().
-    shared_kv sets PA_DECODE_SHARED_KV: pass True when sequences of the batch
-    share blocks (forked prefixes), so K/V loads keep them cached."""
+                max_piece_tiles: int = 0, shared_kv: bool = False, schedule: int = SCHEDULE_AUTO) -> DecodePlan:
+    """pa_decode_plan_schedule (pa_decode_plan for the automatic choice).
+    num_workgroups defaults to default_workgroups().  shared_kv sets
+    PA_DECODE_SHARED_KV: pass True when sequences of the batch share blocks
+    (forked prefixes), so K/V loads keep them cached."""
     lens = np.ascontiguousarray(context_lens, dtype=np.int32)
     if num_workgroups is None:
         num_workgroups = default_workgroups()
@@ -158,12 +163,12 @@ def decode_plan(context_lens, num_kv_heads: int, num_workgroups: int | None = No
     global _plan_buf
     for _ in range(2):
         buf = _plan_buf
-        st = lib.pa_decode_plan(p32, lens.size, num_kv_heads, num_workgroups, max_piece_tiles,
-                                ctypes.c_void_p(buf.ctypes.data), buf.size, ctypes.byref(info))
+        st = lib.pa_decode_plan_schedule(p32, lens.size, num_kv_heads, num_workgroups, max_piece_tiles, schedule,
+                                         ctypes.c_void_p(buf.ctypes.data), buf.size, ctypes.byref(info))
         if st == 0 or info.bytes <= buf.size:
             break
         _plan_buf = np.zeros(2 * info.bytes, dtype=np.uint64).view(np.uint8)   # 8-byte aligned
-    _check(st, "pa_decode_plan")
+    _check(st, "pa_decode_plan_schedule")
     info.flags = PA_DECODE_SHARED_KV if shared_kv else 0
     return DecodePlan(buf[: info.bytes].copy(), info)
 

@@ -28,7 +28,7 @@ class PaDecodePlanInfo(ctypes.Structure):
                 ("num_merges", ctypes.c_int32), ("num_records", ctypes.c_int32),
                 ("num_kv_heads", ctypes.c_int32), ("jobs_per_workgroup", ctypes.c_int32),
                 ("jobs_at", ctypes.c_int32), ("merges_at", ctypes.c_int32), ("bytes", ctypes.c_int32),
-                ("flags", ctypes.c_int32)]
+                ("flags", ctypes.c_int32), ("schedule", ctypes.c_int32)]
 
 
 class PaBmStats(ctypes.Structure):
@@ -67,6 +67,7 @@ SIGNATURES = {
     "pa_copy_blocks": (_i32, [_pool, _vp, _i32, _vp]),
     "pa_decode_default_workgroups": (_i32, []),
     "pa_decode_plan": (_i32, [_p32, _i32, _i32, _i32, _i32, _vp, _sz, ctypes.POINTER(PaDecodePlanInfo)]),
+    "pa_decode_plan_schedule": (_i32, [_p32, _i32, _i32, _i32, _i32, _i32, _vp, _sz, ctypes.POINTER(PaDecodePlanInfo)]),
     "pa_decode_workspace_bytes": (_sz, [ctypes.POINTER(PaDecodePlanInfo), _i32, _i32]),
     "pa_decode": (_i32, _DECODE_ARGS),
     "pa_decode_attention": (_i32, _DECODE_ARGS),

@@ -121,135 +121,285 @@ extern "C" int32_t pa_decode_default_workgroups(void) {
   return cus * per_cu;
 }
 
-extern "C" pa_status pa_decode_plan(const int32_t* context_lens, int32_t num_seqs, int32_t num_kv_heads,
-                                    int32_t num_workgroups, int32_t max_piece_tiles, void* plan,
-                                    size_t capacity, pa_decode_plan_info* info) {
-  if (!info || num_seqs < 0 || num_kv_heads <= 0 || num_workgroups <= 0 || (num_seqs > 0 && !context_lens))
-    return fail(PA_ERR_INVALID, "pa_decode_plan: bad arguments");
-  if (max_piece_tiles < 0 || max_piece_tiles > 64)
-    return fail(PA_ERR_INVALID, "pa_decode_plan: max_piece_tiles %d outside [0, 64]", max_piece_tiles);
-  if (capacity > 0 && (!plan || !pagedkv::aligned(plan, 8)))
-    return fail(PA_ERR_INVALID, "pa_decode_plan: plan buffer NULL or not 8-byte aligned");
-  const int64_t head_blocks = (num_kv_heads + 3) / 4;
-  const int64_t cap = max_piece_tiles > 0 ? max_piece_tiles : 64;
-  for (int32_t s = 0; s < num_seqs; ++s)
-    if (context_lens[s] < 0) return fail(PA_ERR_INVALID, "pa_decode_plan: context_lens[%d] < 0", s);
+namespace pagedkv {
+namespace {
 
-  // Streams: the tiles of one (sequence, block of four KV heads), in
-  // alternating length order (longest, shortest, second longest, ...) so
-  // that no workgroup collects a run of short sequences.  Empty sequences
-  // have no stream.
+// One candidate schedule: jobs with their workgroup, merge rows, record count.
+struct Piece {
+  int32_t wg;
+  pa_decode_job job;
+};
+struct Schedule {
+  std::vector<Piece> pieces;
+  std::vector<pa_decode_merge> merges;
+  int64_t records = 0;
+  int64_t nwg = 1;
+};
+
+constexpr int64_t kStreamCharge = 4;   // cost units (tokens) charged per stream start by the chunk walk
+// Cost of one job, in tokens, when the two schedules are compared.  A job
+// boundary stalls a wavefront for about one tile, and workgroups holding
+// many jobs finish last; 56 is calibrated on MI355X so that the comparison
+// picks the faster schedule for the batch shapes measured (largest pieces
+// for many short contexts and for lengths near a workgroup's share, chunks
+// for long contexts and shared prefixes).
+constexpr int64_t kJobCharge = 56;
+
+int64_t tile_rows(int32_t L, int64_t t) { return std::min<int64_t>(16, L - 16 * t); }
+
+// Equal-work chunks: the (sequence, head block) tile streams, in alternating
+// length order (longest, shortest, second longest, ...), are laid end to end
+// and cut into nwg consecutive chunks of equal cost (tokens of each tile, plus
+// kStreamCharge at a stream's first tile) at tile boundaries; a tile goes to
+// the workgroup whose share holds the tile's midpoint.  Consecutive tiles of
+// one stream on one workgroup form jobs of at most `cap` tiles.  Records are
+// per stream: KV head 4*hb + w, piece p at record_base + w * parts + p.
+pa_status schedule_chunks(const int32_t* lens, int32_t num_seqs, int32_t num_kv_heads, int64_t nwg_req, int64_t cap,
+                          Schedule& out) {
+  const int64_t head_blocks = (num_kv_heads + 3) / 4;
   std::vector<int32_t> by_len;
   by_len.reserve(num_seqs);
   for (int32_t s = 0; s < num_seqs; ++s)
-    if (context_lens[s] > 0) by_len.push_back(s);
-  std::stable_sort(by_len.begin(), by_len.end(),
-                   [&](int32_t x, int32_t y) { return context_lens[x] > context_lens[y]; });
-  std::vector<int32_t> seq_order;
-  seq_order.reserve(by_len.size());
+    if (lens[s] > 0) by_len.push_back(s);
+  std::stable_sort(by_len.begin(), by_len.end(), [&](int32_t x, int32_t y) { return lens[x] > lens[y]; });
+  std::vector<int32_t> order;
+  order.reserve(by_len.size());
   for (size_t i = 0, j = by_len.size(); i < j;) {
-    seq_order.push_back(by_len[i++]);
-    if (i < j) seq_order.push_back(by_len[--j]);
+    order.push_back(by_len[i++]);
+    if (i < j) order.push_back(by_len[--j]);
   }
-  // Cost of a tile = the tokens it holds (16, fewer in a sequence's last
-  // tile), plus a fixed charge at the start of every stream for its query
-  // and table fetch and its output.
-  constexpr int64_t kStreamCharge = 4;
   int64_t total = 0, total_tiles = 0;
-  for (int32_t s : seq_order) {
-    total += (context_lens[s] + kStreamCharge) * head_blocks;
-    total_tiles += ((int64_t)context_lens[s] + 15) / 16 * head_blocks;
+  for (int32_t s : order) {
+    total += (lens[s] + kStreamCharge) * head_blocks;
+    total_tiles += ((int64_t)lens[s] + 15) / 16 * head_blocks;
   }
-  if (total_tiles > (int64_t)INT32_MAX / 64) return fail(PA_ERR_INVALID, "pa_decode_plan: plan too large");
-  const int64_t nwg = std::max<int64_t>(1, std::min<int64_t>(num_workgroups, total_tiles));
-
-  // Equal-work chunks: the streams are laid end to end and cut into nwg
-  // consecutive chunks of equal cost at tile boundaries (a tile goes to the
-  // workgroup whose share holds the tile's midpoint), so every workgroup's
-  // cost is within half a tile of total / nwg on either side.  Consecutive
-  // tiles of one stream on one workgroup form a job of at most `cap` tiles.
-  struct Piece {
-    int32_t wg;
-    pa_decode_job job;
-  };
-  std::vector<Piece> pieces;
-  std::vector<pa_decode_merge> merges;
-  int64_t records = 0, cum = 0;
-  std::vector<int32_t> stream_first;  // index of each stream's first piece
-  for (int32_t s : seq_order) {
-    const int32_t L = context_lens[s];
-    const int32_t tiles = (L + 15) / 16;
+  const int64_t nwg = std::max<int64_t>(1, std::min<int64_t>(nwg_req, total_tiles));
+  out.nwg = nwg;
+  std::vector<int32_t> first_of_stream(num_seqs, -1);  // piece index of (s, hb = 0); streams of s are consecutive
+  int64_t cum = 0;
+  for (int32_t s : order) {
+    const int32_t L = lens[s];
+    const int64_t tiles = ((int64_t)L + 15) / 16;
     for (int64_t hb = 0; hb < head_blocks; ++hb) {
-      stream_first.push_back((int32_t)pieces.size());
-      const size_t first = pieces.size();
+      const size_t first = out.pieces.size();
+      if (hb == 0) first_of_stream[s] = (int32_t)first;
       int64_t last_wg = -1;
-      for (int32_t t = 0; t < tiles; ++t) {
-        const int64_t c = std::min(16, L - 16 * t) + (t == 0 ? kStreamCharge : 0);
+      for (int64_t t = 0; t < tiles; ++t) {
+        const int64_t c = tile_rows(L, t) + (t == 0 ? kStreamCharge : 0);
         const int64_t wg = std::min<int64_t>(nwg - 1, ((2 * cum + c) * nwg) / (2 * total));
         cum += c;
-        if (wg != last_wg || pieces.back().job.tile_count >= cap) {
-          pieces.push_back(Piece{(int32_t)wg, pa_decode_job{s, t, 0, (int32_t)hb, 0, 1, -1, 0}});
+        if (wg != last_wg || out.pieces.back().job.tile_count >= cap) {
+          out.pieces.push_back(Piece{(int32_t)wg, pa_decode_job{s, (int32_t)t, 0, (int32_t)hb, 0, 1, -1, L}});
           last_wg = wg;
         }
-        pieces.back().job.tile_count += 1;
+        out.pieces.back().job.tile_count += 1;
       }
-      const int32_t parts = (int32_t)(pieces.size() - first);
+      const int32_t parts = (int32_t)(out.pieces.size() - first);
       if (parts > 1) {
         const int64_t heads = std::min<int64_t>(4, num_kv_heads - 4 * hb);
         for (int32_t p = 0; p < parts; ++p) {
-          pieces[first + p].job.part = p;
-          pieces[first + p].job.num_parts = parts;
-          pieces[first + p].job.record_base = (int32_t)records;
+          out.pieces[first + p].job.part = p;
+          out.pieces[first + p].job.num_parts = parts;
+          out.pieces[first + p].job.record_base = (int32_t)out.records;
         }
-        records += (int64_t)parts * heads;
-        if (records > INT32_MAX / 1024) return fail(PA_ERR_INVALID, "pa_decode_plan: plan too large");
+        out.records += (int64_t)parts * heads;
+        if (out.records > INT32_MAX / 1024) return fail(PA_ERR_INVALID, "pa_decode_plan: plan too large");
       }
     }
   }
   // Merge rows, sequence by sequence: every KV head of an empty sequence
   // (zeros) and of every cut stream.
-  {
-    std::vector<int32_t> stream_of_seq(num_seqs, -1);
-    for (size_t i = 0; i < seq_order.size(); ++i) stream_of_seq[seq_order[i]] = (int32_t)(i * head_blocks);
-    for (int32_t s = 0; s < num_seqs; ++s) {
-      if (context_lens[s] == 0) {
-        for (int32_t g = 0; g < num_kv_heads; ++g) merges.push_back(pa_decode_merge{s, g, 0, -1});
-        continue;
-      }
-      for (int64_t hb = 0; hb < head_blocks; ++hb) {
-        const pa_decode_job& j = pieces[stream_first[stream_of_seq[s] + hb]].job;
-        if (j.num_parts <= 1) continue;
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    if (lens[s] == 0) {
+      for (int32_t g = 0; g < num_kv_heads; ++g) out.merges.push_back(pa_decode_merge{s, g, 0, -1});
+      continue;
+    }
+    size_t i = (size_t)first_of_stream[s];
+    for (int64_t hb = 0; hb < head_blocks; ++hb) {
+      const pa_decode_job& j = out.pieces[i].job;
+      if (j.num_parts > 1) {
         for (int32_t g = 4 * (int32_t)hb; g < std::min<int32_t>(num_kv_heads, 4 * (int32_t)hb + 4); ++g)
-          merges.push_back(pa_decode_merge{s, g, j.num_parts, j.record_base + (g - 4 * (int32_t)hb) * j.num_parts});
+          out.merges.push_back(pa_decode_merge{s, g, j.num_parts, j.record_base + (g - 4 * (int32_t)hb) * j.num_parts});
       }
+      i += (size_t)j.num_parts;
     }
   }
-  if (pieces.size() > (size_t)INT32_MAX / 64 || merges.size() > (size_t)INT32_MAX / 64)
+  return PA_OK;
+}
+
+// Largest pieces first: each sequence's tiles are cut into near-equal pieces
+// of at most `cap` tiles (cap = 0: the average tiles per workgroup, clamped to
+// [4, 64]); one job per (piece, head block); jobs, largest first, go to the
+// least-loaded workgroup (by tiles).  Fewer, larger jobs than the chunks when
+// most sequences fit in one workgroup's share.  Records are per sequence: KV
+// head g, piece p at base + g * parts + p.
+pa_status schedule_lpt(const int32_t* lens, int32_t num_seqs, int32_t num_kv_heads, int64_t nwg_req,
+                       int64_t cap_req, Schedule& out) {
+  const int64_t head_blocks = (num_kv_heads + 3) / 4;
+  int64_t total = 0;
+  for (int32_t s = 0; s < num_seqs; ++s) total += ((int64_t)lens[s] + 15) / 16 * head_blocks;
+  const int64_t cap = cap_req > 0 ? cap_req : std::min<int64_t>(64, std::max<int64_t>(4, (total + nwg_req - 1) / nwg_req));
+  std::vector<pa_decode_job> jobs;
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    const int64_t tiles = ((int64_t)lens[s] + 15) / 16;
+    if (tiles == 0) {
+      for (int32_t g = 0; g < num_kv_heads; ++g) out.merges.push_back(pa_decode_merge{s, g, 0, -1});
+      continue;
+    }
+    const int64_t parts = (tiles + cap - 1) / cap;
+    const int64_t base = parts > 1 ? out.records : -1;
+    if (parts > 1) {
+      for (int32_t g = 0; g < num_kv_heads; ++g)
+        out.merges.push_back(pa_decode_merge{s, g, (int32_t)parts, (int32_t)(out.records + g * parts)});
+      out.records += parts * num_kv_heads;
+      if (out.records > INT32_MAX / 1024) return fail(PA_ERR_INVALID, "pa_decode_plan: plan too large");
+    }
+    int64_t t0 = 0;
+    for (int64_t p = 0; p < parts; ++p) {
+      const int64_t cnt = tiles / parts + (p < tiles % parts ? 1 : 0);
+      for (int64_t hb = 0; hb < head_blocks; ++hb)
+        jobs.push_back(pa_decode_job{s, (int32_t)t0, (int32_t)cnt, (int32_t)hb, (int32_t)p, (int32_t)parts,
+                                     (int32_t)(base >= 0 ? base + 4 * hb * parts : -1), lens[s]});
+      t0 += cnt;
+    }
+  }
+  const int64_t nwg = std::max<int64_t>(1, std::min<int64_t>(nwg_req, (int64_t)jobs.size()));
+  out.nwg = nwg;
+  // Jobs by tile count, largest first, ties in generation order (a counting
+  // sort: counts are 1..cap).
+  std::vector<int32_t> order(jobs.size());
+  int64_t job_tiles = 0;
+  {
+    std::vector<int32_t> start(cap + 2, 0);
+    for (const pa_decode_job& j : jobs) {
+      start[cap - j.tile_count + 1] += 1;
+      job_tiles += j.tile_count;
+    }
+    for (int64_t c = 1; c <= cap + 1; ++c) start[c] += start[c - 1];
+    for (size_t i = 0; i < jobs.size(); ++i) order[start[cap - jobs[i].tile_count]++] = (int32_t)i;
+  }
+  // Least-loaded workgroup by a bucket queue over load values: loads only
+  // grow, so the smallest non-empty bucket is found by a pointer that only
+  // moves forward.  Workgroups of equal load leave in arrival order
+  // (initially by index).
+  std::vector<int32_t> owner(jobs.size());
+  {
+    const int64_t max_load = job_tiles / nwg + cap + 1;
+    std::vector<int32_t> head(max_load + 1, -1), tail(max_load + 1, -1), next(nwg, -1);
+    for (int64_t w = 0; w + 1 < nwg; ++w) next[w] = (int32_t)(w + 1);
+    head[0] = 0;
+    tail[0] = (int32_t)(nwg - 1);
+    int64_t cur = 0;
+    for (int32_t j : order) {
+      while (head[cur] < 0) ++cur;
+      const int32_t w = head[cur];
+      head[cur] = next[w];
+      if (head[cur] < 0) tail[cur] = -1;
+      owner[j] = w;
+      const int64_t nl = cur + jobs[j].tile_count;
+      next[w] = -1;
+      if (tail[nl] < 0)
+        head[nl] = w;
+      else
+        next[tail[nl]] = w;
+      tail[nl] = w;
+    }
+  }
+  out.pieces.reserve(jobs.size());
+  for (size_t j = 0; j < jobs.size(); ++j) out.pieces.push_back(Piece{owner[j], jobs[j]});
+  return PA_OK;
+}
+
+// Largest workgroup cost: tokens of its tiles plus kJobCharge per job.
+int64_t schedule_cost(const Schedule& sc, const int32_t* lens) {
+  std::vector<int64_t> cost(sc.nwg, 0);
+  for (const Piece& pc : sc.pieces) {
+    int64_t c = kJobCharge;
+    for (int64_t t = pc.job.tile_begin; t < pc.job.tile_begin + pc.job.tile_count; ++t)
+      c += tile_rows(lens[pc.job.seq], t);
+    cost[pc.wg] += c;
+  }
+  int64_t m = 0;
+  for (int64_t c : cost) m = std::max(m, c);
+  return m;
+}
+
+}  // namespace
+}  // namespace pagedkv
+
+extern "C" pa_status pa_decode_plan(const int32_t* context_lens, int32_t num_seqs, int32_t num_kv_heads,
+                                    int32_t num_workgroups, int32_t max_piece_tiles, void* plan,
+                                    size_t capacity, pa_decode_plan_info* info) {
+  return pa_decode_plan_schedule(context_lens, num_seqs, num_kv_heads, num_workgroups, max_piece_tiles,
+                                 PA_SCHEDULE_AUTO, plan, capacity, info);
+}
+
+extern "C" pa_status pa_decode_plan_schedule(const int32_t* context_lens, int32_t num_seqs, int32_t num_kv_heads,
+                                             int32_t num_workgroups, int32_t max_piece_tiles, int32_t schedule,
+                                             void* plan, size_t capacity, pa_decode_plan_info* info) {
+  using pagedkv::Piece;
+  using pagedkv::Schedule;
+  if (!info || num_seqs < 0 || num_kv_heads <= 0 || num_workgroups <= 0 || (num_seqs > 0 && !context_lens))
+    return fail(PA_ERR_INVALID, "pa_decode_plan: bad arguments");
+  if (max_piece_tiles < 0 || max_piece_tiles > 64)
+    return fail(PA_ERR_INVALID, "pa_decode_plan: max_piece_tiles %d outside [0, 64]", max_piece_tiles);
+  if (schedule != PA_SCHEDULE_AUTO && schedule != PA_SCHEDULE_CHUNKS && schedule != PA_SCHEDULE_LPT)
+    return fail(PA_ERR_INVALID, "pa_decode_plan: unknown schedule %d", schedule);
+  if (capacity > 0 && (!plan || !pagedkv::aligned(plan, 8)))
+    return fail(PA_ERR_INVALID, "pa_decode_plan: plan buffer NULL or not 8-byte aligned");
+  int64_t total_tiles = 0;
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    if (context_lens[s] < 0) return fail(PA_ERR_INVALID, "pa_decode_plan: context_lens[%d] < 0", s);
+    total_tiles += ((int64_t)context_lens[s] + 15) / 16 * ((num_kv_heads + 3) / 4);
+  }
+  if (total_tiles > (int64_t)INT32_MAX / 64) return fail(PA_ERR_INVALID, "pa_decode_plan: plan too large");
+
+  // Automatic choice: both schedules are built and the one whose busiest
+  // workgroup costs less (tokens plus a charge per job) is kept, the chunks
+  // on a tie.
+  Schedule chunks, lpt;
+  if (schedule != PA_SCHEDULE_LPT) {
+    if (pa_status st = pagedkv::schedule_chunks(context_lens, num_seqs, num_kv_heads, num_workgroups,
+                                                max_piece_tiles > 0 ? max_piece_tiles : 64, chunks))
+      return st;
+  }
+  if (schedule != PA_SCHEDULE_CHUNKS) {
+    if (pa_status st = pagedkv::schedule_lpt(context_lens, num_seqs, num_kv_heads, num_workgroups, max_piece_tiles, lpt))
+      return st;
+  }
+  const bool use_lpt = schedule == PA_SCHEDULE_LPT ||
+                       (schedule == PA_SCHEDULE_AUTO && !lpt.pieces.empty() &&
+                        pagedkv::schedule_cost(lpt, context_lens) < pagedkv::schedule_cost(chunks, context_lens));
+  const Schedule& sc = use_lpt ? lpt : chunks;
+  const std::vector<Piece>& jobs = sc.pieces;
+  const std::vector<pa_decode_merge>& merges = sc.merges;
+  const int64_t nwg = sc.nwg;
+  if (jobs.size() > (size_t)INT32_MAX / 64 || merges.size() > (size_t)INT32_MAX / 64)
     return fail(PA_ERR_INVALID, "pa_decode_plan: plan too large");
 
   // Per-workgroup lists, column-major: slot k of workgroup b is entry
   // k * nwg + b, so a workgroup reads its first jobs without an index load.
   // Slots past a workgroup's last job are empty (tile_count 0).  A
-  // workgroup's jobs keep stream order.
+  // workgroup's jobs keep schedule order.
   std::vector<int32_t> count(nwg, 0);
-  for (const Piece& pc : pieces) count[pc.wg] += 1;
+  for (const Piece& pc : jobs) count[pc.wg] += 1;
   int64_t per = 0;
   for (int32_t c : count) per = std::max<int64_t>(per, c);
   if (per * nwg > (int64_t)INT32_MAX / 64) return fail(PA_ERR_INVALID, "pa_decode_plan: plan too large");
   std::vector<pa_decode_job> table((size_t)(per * nwg), pa_decode_job{0, 0, 0, 0, 0, 0, -1, 0});
   std::vector<int32_t> fill(nwg, 0);
-  for (const Piece& pc : pieces) table[(size_t)fill[pc.wg]++ * nwg + pc.wg] = pc.job;
-  const std::vector<Piece>& jobs = pieces;
+  for (const Piece& pc : jobs) table[(size_t)fill[pc.wg]++ * nwg + pc.wg] = pc.job;
 
   pa_decode_plan_info in{};
   in.num_workgroups = jobs.empty() ? 0 : (int32_t)nwg;
   in.num_jobs = (int32_t)jobs.size();
   in.num_merges = (int32_t)merges.size();
-  in.num_records = (int32_t)records;
+  in.num_records = (int32_t)sc.records;
   in.num_kv_heads = num_kv_heads;
   in.jobs_per_workgroup = jobs.empty() ? 0 : (int32_t)per;
   in.jobs_at = 0;
   in.merges_at = (int32_t)(sizeof(pa_decode_job) * table.size());
+  in.schedule = use_lpt ? PA_SCHEDULE_LPT : PA_SCHEDULE_CHUNKS;
   const size_t bytes = (size_t)in.merges_at + sizeof(pa_decode_merge) * merges.size();
   if (bytes > (size_t)INT32_MAX) return fail(PA_ERR_INVALID, "pa_decode_plan: plan too large");
   in.bytes = (int32_t)bytes;

@@ -125,8 +125,8 @@ struct JobView {
   bool idle;  // the wavefront's KV head is past the last one: read nothing, write nothing
 };
 
-// The fields of job record jd for wavefront w.  The context length is the
-// only dependent load.  Any record (an empty slot included) gives in-range
+// The fields of job record jd for wavefront w (the context length comes
+// with the record).  Any record (an empty slot included) gives in-range
 // addresses; a wavefront whose KV head is past the last one is idle.
 __device__ __forceinline__ void view_job(const DecodeArgs& a, const pa_decode_job& jd, int w, int B, JobView& v) {
   const int32_t g = jd.head_block * kNW + w;
@@ -135,7 +135,7 @@ __device__ __forceinline__ void view_job(const DecodeArgs& a, const pa_decode_jo
   v.cnt = min(max(jd.tile_count, 0), kMaxTiles);
   v.seq = min(max(jd.seq, 0), a.num_seqs - 1);
   v.t0 = max(jd.tile_begin, 0);
-  v.L = min(max(as_const(a.lens)[v.seq], 0), a.max_blocks * B);
+  v.L = min(max(jd.context_len, 0), a.max_blocks * B);
   v.rec = -1;
   if (jd.num_parts > 1) {
     const int64_t r = (int64_t)jd.record_base + (int64_t)w * jd.num_parts + jd.part;

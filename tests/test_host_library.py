@@ -200,6 +200,48 @@ def _plan_model(lens, hkv, nwg, cap):
     return wg_jobs, merges, records
 
 
+def _lpt_model(lens, hkv, nwg, cap):
+    """Independent statement of the largest-pieces-first schedule: every
+    sequence cut into near-equal pieces of at most cap tiles (cap 0: the
+    average tiles per workgroup clamped to [4, 64]), one job per (piece, head
+    block); jobs by size, largest first (ties in generation order), each to
+    the least-loaded workgroup (ties: the one that reached that load first,
+    initially by index).  Returns (jobs per workgroup, merge rows, records)."""
+    import heapq
+    lens = [int(x) for x in lens]
+    hb = -(-hkv // 4)
+    total = sum(-(-L // 16) * hb for L in lens)
+    cap = cap or min(64, max(4, -(-total // nwg)))
+    jobs, merges, records = [], [], 0
+    for s, L in enumerate(lens):
+        tiles = -(-L // 16)
+        if tiles == 0:
+            merges += [(s, g, 0, -1) for g in range(hkv)]
+            continue
+        parts = -(-tiles // cap)
+        base = records if parts > 1 else -1
+        if parts > 1:
+            merges += [(s, g, parts, records + g * parts) for g in range(hkv)]
+            records += parts * hkv
+        t0 = 0
+        for p in range(parts):
+            cnt = tiles // parts + (1 if p < tiles % parts else 0)
+            for h in range(hb):
+                jobs.append((s, t0, cnt, h, p if parts > 1 else 0, parts, base + 4 * h * parts if base >= 0 else -1))
+            t0 += cnt
+    nwg = max(1, min(nwg, len(jobs)))
+    order = sorted(range(len(jobs)), key=lambda i: (-jobs[i][2], i))
+    heap = [(0, w, w) for w in range(nwg)]
+    arrival = nwg
+    wg_jobs = [[] for _ in range(nwg)]
+    for i in order:
+        load, _, w = heapq.heappop(heap)
+        wg_jobs[w].append(i)
+        heapq.heappush(heap, (load + jobs[i][2], arrival, w))
+        arrival += 1
+    return [[jobs[i] for i in sorted(l)] for l in wg_jobs], merges, records
+
+
 def _plan_lists(plan):
     tab = plan.job_table()
     return [[tuple(j[:7]) for j in tab[:, b].tolist() if j[2] > 0] for b in range(tab.shape[1])]
@@ -209,7 +251,8 @@ def test_decode_plan_small_example():
     """Lengths 0, 5, 600, 1000 (0, 1, 38, 63 tiles), 8 KV heads (two head
     blocks), 6 workgroups.  Stream order 1000, 5, 600; costs 1004, 9, 604 per
     head block, 3234 in all, 539 per workgroup."""
-    plan = pk.decode_plan([0, 5, 600, 1000], 8, num_workgroups=6)
+    plan = pk.decode_plan([0, 5, 600, 1000], 8, num_workgroups=6, schedule=pk.SCHEDULE_CHUNKS)
+    assert plan.schedule == pk.SCHEDULE_CHUNKS
     lists = _plan_lists(plan)
     # Worked by hand: a tile of cost c ending at cumulative cost e goes to
     # workgroup floor((e - c/2) / 539); e.g. the 1000-token stream of head
@@ -235,6 +278,37 @@ def test_decode_plan_small_example():
     assert pk.decode_workspace_bytes(plan, 32, 128) >= 36 * 4 * 130 * 4
 
 
+def test_decode_plan_small_example_lpt():
+    """The same batch under the largest-pieces-first schedule: 204 job tiles
+    over 6 workgroups, cap 34: 600 tokens (38 tiles) -> pieces 19 + 19,
+    1000 tokens (63 tiles) -> 32 + 31, times two head blocks; the 5-token
+    sequence is one tile per head block."""
+    plan = pk.decode_plan([0, 5, 600, 1000], 8, num_workgroups=6, schedule=pk.SCHEDULE_LPT)
+    assert plan.schedule == pk.SCHEDULE_LPT
+    assert (plan.num_workgroups, plan.num_jobs, plan.num_merges, plan.num_records) == (6, 10, 24, 32)
+    jobs = sorted(map(tuple, plan.jobs()[:, :7].tolist()))
+    assert jobs == sorted([
+        (1, 0, 1, 0, 0, 1, -1), (1, 0, 1, 1, 0, 1, -1),
+        (2, 0, 19, 0, 0, 2, 0), (2, 0, 19, 1, 0, 2, 8), (2, 19, 19, 0, 1, 2, 0), (2, 19, 19, 1, 1, 2, 8),
+        (3, 0, 32, 0, 0, 2, 16), (3, 0, 32, 1, 0, 2, 24), (3, 32, 31, 0, 1, 2, 16), (3, 32, 31, 1, 1, 2, 24)])
+    loads = sorted(int(plan.job_table()[:, w, 2].sum()) for w in range(6))
+    assert loads == [32, 32, 32, 32, 38, 38]
+    merges = [tuple(m) for m in plan.merges().tolist()]
+    assert merges == ([(0, g, 0, -1) for g in range(8)] + [(2, g, 2, 2 * g) for g in range(8)] +
+                      [(3, g, 2, 16 + 2 * g) for g in range(8)])
+    assert lists_equal_model(plan, [0, 5, 600, 1000], 8, 6, 0, _lpt_model)
+    auto = pk.decode_plan([0, 5, 600, 1000], 8, num_workgroups=6)
+    assert auto.schedule in (pk.SCHEDULE_CHUNKS, pk.SCHEDULE_LPT)
+    with pytest.raises(pk.PaError):
+        pk.decode_plan([1], 8, num_workgroups=6, schedule=2)
+
+
+def lists_equal_model(plan, lens, hkv, nwg, cap, model):
+    wg_jobs, merges, records = model(lens, hkv, nwg, cap)
+    return (_plan_lists(plan) == wg_jobs and [tuple(m) for m in plan.merges().tolist()] == merges
+            and plan.num_records == records)
+
+
 @pytest.mark.parametrize("seed", range(12))
 def test_decode_plan_matches_model(seed):
     rng = np.random.default_rng(100 + seed)
@@ -243,8 +317,14 @@ def test_decode_plan_matches_model(seed):
     hkv = int(rng.choice([1, 3, 4, 8, 13]))
     nwg = int(rng.integers(1, 900))
     cap = int(rng.choice([0, 1, 5, 64]))
+    for sched, model in ((pk.SCHEDULE_CHUNKS, _plan_model), (pk.SCHEDULE_LPT, _lpt_model)):
+        p = pk.decode_plan(lens, hkv, num_workgroups=nwg, max_piece_tiles=cap, schedule=sched)
+        assert p.schedule == sched
+        if p.num_jobs:
+            assert lists_equal_model(p, lens, hkv, nwg, cap, model)
     plan = pk.decode_plan(lens, hkv, num_workgroups=nwg, max_piece_tiles=cap)
-    wg_jobs, merges, records = _plan_model(lens, hkv, nwg, cap)
+    model = _plan_model if plan.schedule == 0 else _lpt_model
+    wg_jobs, merges, records = model(lens, hkv, nwg, cap)
     if plan.num_jobs == 0:
         assert sum(map(len, wg_jobs)) == 0
     else:
@@ -290,9 +370,13 @@ def test_decode_plan_covers_every_tile_once(seed):
                 if cnt > 0:
                     cost[b] += sum(min(16, int(lens[seq]) - 16 * t) + (4 if t == 0 else 0) for t in range(t0, t0 + cnt))
         mean = cost.sum() / plan.num_workgroups
-        assert cost.max() <= mean + 20 + 1e-9
-        if mean >= 40:
-            assert cost.min() >= mean - 20 - 1e-9
+        if plan.schedule == 0:
+            assert cost.max() <= mean + 20 + 1e-9
+            if mean >= 40:
+                assert cost.min() >= mean - 20 - 1e-9
+        else:
+            loads = tab[:, :, 2].sum(axis=0)
+            assert loads.max() <= np.ceil(loads.sum() / plan.num_workgroups) + jobs[:, 2].max()
 
 
 def test_decode_plan_errors():
