@@ -161,7 +161,9 @@ def prefix_workload(pk, block_size: int) -> dict:
             fill = B if j < nblk - 1 else int(lens[s]) - j * B
             used[int(blk)] = max(used.get(int(blk), 0), fill)
     q = case["q"]
+    group, prefix_tokens = bm.prefix_groups(seqs)
     return dict(name=f"c5 B={B}", desc=f"{WORKLOADS['c5']}, block {B}", case=dict(q=q, scale=case["scale"]),
+                prefix_group=group, prefix_tokens=prefix_tokens,
                 seed=cfg["seed"] + B, S=nseq, hq=cfg["num_q_heads"], hkv=cfg["num_kv_heads"], d=cfg["head_dim"], B=B,
                 nb=case["num_blocks"], tables=tables, lens=lens, slots=slots,
                 cows=np.asarray(fork_cows, dtype=np.int32).reshape(-1, 2), host_append_us=host_append_us,
@@ -231,6 +233,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-only", action="store_true", help="time only pa_decode launches (profiling aid)")
     ap.add_argument("--graph", action="store_true", help="replay each step as a captured HIP graph")
+    ap.add_argument("--no-cascade", action="store_true",
+                    help="c5: plan every sequence separately instead of reading shared prefixes once per group")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="profiling aid: run a plain device-to-device copy of BYTES (the reference whose "
                          "counter readings calibrate the traffic figures) and exit")
@@ -255,8 +259,12 @@ def main() -> int:
     tables, lens, slots, cows = w["tables"], w["lens"], w["slots"], w["cows"]
     host_append_us = w["host_append_us"]
     workgroups = args.workgroups or pk.default_workgroups()
+    cascade = "prefix_group" in w and not args.no_cascade
     t0 = time.perf_counter()
-    plan = pk.decode_plan(lens, hkv, workgroups, args.piece, shared_kv=w["shared_kv"])
+    if cascade:
+        plan = pk.decode_plan_prefix(lens, hkv, hq, w["prefix_group"], w["prefix_tokens"], workgroups, args.piece)
+    else:
+        plan = pk.decode_plan(lens, hkv, workgroups, args.piece, shared_kv=w["shared_kv"])
     host_plan_us = (time.perf_counter() - t0) * 1e6
 
     dev = torch.device("cuda", 0)
@@ -376,7 +384,9 @@ def main() -> int:
                    "total_context_tokens": int(lens.sum()), "max_context": int(lens.max()),
                    "workgroups": int(workgroups), "max_piece_tiles": int(args.piece),
                    "jobs": int(plan.num_jobs), "merges": int(plan.num_merges), "records": int(plan.num_records),
-                   "pool_replicas": R, "decode_only": bool(args.decode_only), "shared_kv": bool(w["shared_kv"])},
+                   "pool_replicas": R, "decode_only": bool(args.decode_only), "shared_kv": bool(w["shared_kv"]),
+                   "schedule": ["chunks", "largest pieces first"][plan.schedule],
+                   "cascade_prefix_groups": int(plan.num_groups) if cascade else 0},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "decode_tokens_per_s": round(S / (ms_per_step * 1e-3), 1),
         "kv_bytes_per_step": kv_bytes,

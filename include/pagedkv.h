@@ -161,7 +161,29 @@ typedef struct pa_decode_plan_info {
   int32_t bytes;          /* total plan bytes */
   int32_t flags;          /* PA_DECODE_* bits; pa_decode_plan sets 0, the caller may set them */
   int32_t schedule;       /* PA_SCHEDULE_* the plan was built with (informational) */
+  int32_t num_groups;     /* prefix-group descriptors (pa_decode_plan_prefix; 0 otherwise) */
+  int32_t groups_at;      /* byte offset of pa_decode_group [num_groups] */
+  int32_t group_size;     /* largest prefix group planned (members sharing one read of the prefix) */
 } pa_decode_plan_info;
+
+/* A job whose head_block field has this bit reads a prefix shared by the
+ * members of a prefix group once for all of them: seq is the group's first
+ * member (whose table is read), record_base indexes the pa_decode_group,
+ * part is the piece of the shared prefix. */
+#define PA_JOB_SHARED (1 << 16)
+
+/* One prefix group for one head block: up to four sequences whose first
+ * blocks are the same physical blocks.  Member i's record for KV head
+ * 4*head_block + w and piece p is record_base[i] + w * num_parts[i] + p;
+ * the shared prefix pieces are its parts 0, 1, ..., its own tiles follow. */
+typedef struct pa_decode_group {
+  int32_t num_members;
+  int32_t head_block;
+  int32_t seq[4];
+  int32_t record_base[4];
+  int32_t num_parts[4];
+  int32_t reserved[2];
+} pa_decode_group;
 
 /* Schedules pa_decode_plan builds and chooses between. */
 #define PA_SCHEDULE_AUTO (-1) /* build both, keep the cheaper (pa_decode_plan) */
@@ -212,6 +234,35 @@ pa_status pa_decode_plan(const int32_t* context_lens, int32_t num_seqs, int32_t 
 pa_status pa_decode_plan_schedule(const int32_t* context_lens, int32_t num_seqs, int32_t num_kv_heads,
                                   int32_t num_workgroups, int32_t max_piece_tiles, int32_t schedule, void* plan,
                                   size_t capacity, pa_decode_plan_info* info);
+
+/* pa_decode_plan_prefix - chunk schedule with shared prefixes read once.
+ *
+ * Cascade decode for forked sequences (S06 "Copy-on-write, for free": n
+ * samples of one prompt hold the same prefix blocks): the tiles of a prefix
+ * that several sequences of the batch share are read once per head block
+ * and scored against the queries of all members together (up to
+ * min(4, 16 / G) members per group, G = num_q_heads / num_kv_heads, so that
+ * members x G query columns fill one 16-wide MFMA), and every member's own
+ * tiles are scheduled as usual; the merge launch combines the shared and the
+ * own pieces by log-sum-exp.
+ *   prefix_group  : HOST int32 [num_seqs]: sequences with the same value
+ *                   >= 0 share their first prefix_tokens tokens (the same
+ *                   physical blocks); -1: no sharing.  Larger groups are cut
+ *                   into groups of the largest allowed size, in sequence order.
+ *   prefix_tokens : HOST int32 [num_seqs]: tokens shared by the sequence's
+ *                   group.  A group shares the smallest value of its members,
+ *                   rounded down to a multiple of 16 and kept below every
+ *                   member's context length (so the token written this step is
+ *                   never in the shared part).
+ * Other arguments as pa_decode_plan.  Groups of one member, or a shared part
+ * of less than one tile, are planned as unshared sequences.
+ * Precondition (not checked): the members' block tables hold the same block
+ * ids for the shared tokens; the shared blocks are read through the first
+ * member's table. */
+pa_status pa_decode_plan_prefix(const int32_t* context_lens, int32_t num_seqs, int32_t num_kv_heads,
+                                int32_t num_q_heads, int32_t num_workgroups, int32_t max_piece_tiles,
+                                const int32_t* prefix_group, const int32_t* prefix_tokens, void* plan,
+                                size_t capacity, pa_decode_plan_info* info);
 
 /* Bytes of device workspace pa_decode needs for a plan (0 when no sequence is
  * cut).  The workspace needs no initialisation; it carries records from the
@@ -346,6 +397,17 @@ int32_t pa_bm_table(const pa_bm* bm, int64_t seq, int32_t* out, int32_t cap);
  * unknown sequence, PA_ERR_INVALID if a table exceeds max_blocks. */
 pa_status pa_bm_export(const pa_bm* bm, const int64_t* seqs, int32_t num, int32_t max_blocks,
                        int32_t* tables_out, int32_t* lens_out);
+
+/* Prefix groups of a batch, the input of pa_decode_plan_prefix: sequences
+ * whose tables start with the same physical block form a group (group_out =
+ * batch position of its first member; -1 for a sequence alone with its first
+ * block or an empty one); prefix_tokens_out = the group's longest common run
+ * of leading blocks, in tokens, capped by its shortest member's length
+ * (S06 "Copy-on-write, for free": forked samples keep naming the prompt's
+ * blocks).  HOST arrays of num entries.  PA_ERR_NOT_FOUND for an unknown
+ * sequence. */
+pa_status pa_bm_prefix_groups(const pa_bm* bm, const int64_t* seqs, int32_t num, int32_t* group_out,
+                              int32_t* prefix_tokens_out);
 
 int32_t pa_bm_len(const pa_bm* bm, int64_t seq);         /* -1 if unknown */
 int32_t pa_bm_refcount(const pa_bm* bm, int32_t block);  /* -1 if out of range */

@@ -13,10 +13,10 @@ import os
 
 import numpy as np
 
-from ._lib import LIB_PATH, PA_BF16, PA_DECODE_SHARED_KV, PA_F32, PaDecodePlanInfo, PaError, PaKvPool, lib
+from ._lib import LIB_PATH, PA_BF16, PA_DECODE_SHARED_KV, PA_F32, PA_JOB_SHARED, PaDecodePlanInfo, PaError, PaKvPool, lib
 
 __all__ = [
-    "LIB_PATH", "PA_F32", "PA_BF16", "PA_DECODE_SHARED_KV", "PaError", "BlockManager", "KvPool",
+    "LIB_PATH", "PA_F32", "PA_BF16", "PA_DECODE_SHARED_KV", "PA_JOB_SHARED", "PaError", "BlockManager", "KvPool",
     "reshape_and_cache", "copy_blocks", "decode_plan", "decode_workspace_bytes",
     "decode", "DecodePlan", "default_workgroups",
 ]
@@ -107,7 +107,7 @@ class DecodePlan:
 
     def __getattr__(self, name):
         if name in ("num_workgroups", "num_jobs", "num_merges", "num_records", "num_kv_heads", "jobs_per_workgroup",
-                    "schedule"):
+                    "schedule", "num_groups", "group_size"):
             return getattr(self.info, name)
         raise AttributeError(name)
 
@@ -124,9 +124,15 @@ class DecodePlan:
         t = self.job_table().transpose(1, 0, 2).reshape(-1, 8)
         return t[t[:, 2] > 0]
 
+    def groups(self) -> np.ndarray:
+        """int32 [num_groups, 16]: num_members, head_block, seq[4], record_base[4], num_parts[4], 0, 0."""
+        n = self.info.num_groups
+        return self.blob[self.info.groups_at:self.info.groups_at + 64 * n].view(np.int32).reshape(n, 16)
+
     def merges(self) -> np.ndarray:
         """int32 [num_merges, 4]: seq, kv_head, num_parts, record_base."""
-        return self.blob[self.info.merges_at:self.info.bytes].view(np.int32).reshape(-1, 4)
+        n = self.info.num_merges
+        return self.blob[self.info.merges_at:self.info.merges_at + 16 * n].view(np.int32).reshape(n, 4)
 
     def to_device(self, device="cuda"):
         import torch
@@ -170,6 +176,34 @@ def decode_plan(context_lens, num_kv_heads: int, num_workgroups: int | None = No
         _plan_buf = np.zeros(2 * info.bytes, dtype=np.uint64).view(np.uint8)   # 8-byte aligned
     _check(st, "pa_decode_plan_schedule")
     info.flags = PA_DECODE_SHARED_KV if shared_kv else 0
+    return DecodePlan(buf[: info.bytes].copy(), info)
+
+
+def decode_plan_prefix(context_lens, num_kv_heads: int, num_q_heads: int, prefix_group, prefix_tokens,
+                       num_workgroups: int | None = None, max_piece_tiles: int = 0) -> DecodePlan:
+    """pa_decode_plan_prefix: shared prefixes read once per group (cascade
+    decode).  prefix_group/prefix_tokens as from BlockManager.prefix_groups.
+    The plan carries PA_DECODE_SHARED_KV (the batch shares blocks)."""
+    lens = np.ascontiguousarray(context_lens, dtype=np.int32)
+    grp = np.ascontiguousarray(prefix_group, dtype=np.int32)
+    tok = np.ascontiguousarray(prefix_tokens, dtype=np.int32)
+    if grp.shape != lens.shape or tok.shape != lens.shape:
+        raise ValueError("prefix_group and prefix_tokens must have one entry per sequence")
+    if num_workgroups is None:
+        num_workgroups = default_workgroups()
+    info = PaDecodePlanInfo()
+    p32 = lambda a: a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    global _plan_buf
+    for _ in range(2):
+        buf = _plan_buf
+        st = lib.pa_decode_plan_prefix(p32(lens), lens.size, num_kv_heads, num_q_heads, num_workgroups,
+                                       max_piece_tiles, p32(grp), p32(tok), ctypes.c_void_p(buf.ctypes.data),
+                                       buf.size, ctypes.byref(info))
+        if st == 0 or info.bytes <= buf.size:
+            break
+        _plan_buf = np.zeros(2 * info.bytes, dtype=np.uint64).view(np.uint8)   # 8-byte aligned
+    _check(st, "pa_decode_plan_prefix")
+    info.flags = PA_DECODE_SHARED_KV
     return DecodePlan(buf[: info.bytes].copy(), info)
 
 
@@ -276,6 +310,16 @@ class BlockManager:
         out = np.zeros(max(n, 1), dtype=np.int32)
         lib.pa_bm_table(self._h, seq, out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), n)
         return out[:n]
+
+    def prefix_groups(self, seqs):
+        """pa_bm_prefix_groups -> (group int32[n], prefix_tokens int32[n])."""
+        seqs = np.ascontiguousarray(seqs, dtype=np.int64)
+        group = np.zeros(seqs.size, dtype=np.int32)
+        tokens = np.zeros(seqs.size, dtype=np.int32)
+        _check(lib.pa_bm_prefix_groups(self._h, seqs.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), seqs.size,
+                                       group.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                       tokens.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))), "pa_bm_prefix_groups")
+        return group, tokens
 
     def export(self, seqs, max_blocks: int):
         """Dense (tables int32[n, max_blocks], lens int32[n]) for upload."""

@@ -9,6 +9,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedkv.
 PA_F32 = 0
 PA_BF16 = 1
 PA_DECODE_SHARED_KV = 1
+PA_JOB_SHARED = 1 << 16
 
 
 class PaError(RuntimeError):
@@ -28,7 +29,8 @@ class PaDecodePlanInfo(ctypes.Structure):
                 ("num_merges", ctypes.c_int32), ("num_records", ctypes.c_int32),
                 ("num_kv_heads", ctypes.c_int32), ("jobs_per_workgroup", ctypes.c_int32),
                 ("jobs_at", ctypes.c_int32), ("merges_at", ctypes.c_int32), ("bytes", ctypes.c_int32),
-                ("flags", ctypes.c_int32), ("schedule", ctypes.c_int32)]
+                ("flags", ctypes.c_int32), ("schedule", ctypes.c_int32), ("num_groups", ctypes.c_int32),
+                ("groups_at", ctypes.c_int32), ("group_size", ctypes.c_int32)]
 
 
 class PaBmStats(ctypes.Structure):
@@ -68,6 +70,8 @@ SIGNATURES = {
     "pa_decode_default_workgroups": (_i32, []),
     "pa_decode_plan": (_i32, [_p32, _i32, _i32, _i32, _i32, _vp, _sz, ctypes.POINTER(PaDecodePlanInfo)]),
     "pa_decode_plan_schedule": (_i32, [_p32, _i32, _i32, _i32, _i32, _i32, _vp, _sz, ctypes.POINTER(PaDecodePlanInfo)]),
+    "pa_decode_plan_prefix": (_i32, [_p32, _i32, _i32, _i32, _i32, _i32, _p32, _p32, _vp, _sz,
+                                     ctypes.POINTER(PaDecodePlanInfo)]),
     "pa_decode_workspace_bytes": (_sz, [ctypes.POINTER(PaDecodePlanInfo), _i32, _i32]),
     "pa_decode": (_i32, _DECODE_ARGS),
     "pa_decode_attention": (_i32, _DECODE_ARGS),
@@ -80,6 +84,7 @@ SIGNATURES = {
     "pa_bm_free": (_i32, [_vp, _i64]),
     "pa_bm_table": (_i32, [_vp, _i64, _p32, _i32]),
     "pa_bm_export": (_i32, [_vp, _p64, _i32, _i32, _p32, _p32]),
+    "pa_bm_prefix_groups": (_i32, [_vp, _p64, _i32, _p32, _p32]),
     "pa_bm_len": (_i32, [_vp, _i64]),
     "pa_bm_refcount": (_i32, [_vp, _i32]),
     "pa_bm_get_stats": (None, [_vp, ctypes.POINTER(PaBmStats)]),

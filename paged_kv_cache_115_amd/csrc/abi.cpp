@@ -132,8 +132,10 @@ struct Piece {
 struct Schedule {
   std::vector<Piece> pieces;
   std::vector<pa_decode_merge> merges;
+  std::vector<pa_decode_group> groups;
   int64_t records = 0;
   int64_t nwg = 1;
+  int32_t group_size = 0;
 };
 
 constexpr int64_t kStreamCharge = 4;   // cost units (tokens) charged per stream start by the chunk walk
@@ -147,65 +149,105 @@ constexpr int64_t kJobCharge = 56;
 
 int64_t tile_rows(int32_t L, int64_t t) { return std::min<int64_t>(16, L - 16 * t); }
 
-// Equal-work chunks: the (sequence, head block) tile streams, in alternating
-// length order (longest, shortest, second longest, ...), are laid end to end
-// and cut into nwg consecutive chunks of equal cost (tokens of each tile, plus
-// kStreamCharge at a stream's first tile) at tile boundaries; a tile goes to
-// the workgroup whose share holds the tile's midpoint.  Consecutive tiles of
-// one stream on one workgroup form jobs of at most `cap` tiles.  Records are
-// per stream: KV head 4*hb + w, piece p at record_base + w * parts + p.
-pa_status schedule_chunks(const int32_t* lens, int32_t num_seqs, int32_t num_kv_heads, int64_t nwg_req, int64_t cap,
-                          Schedule& out) {
-  const int64_t head_blocks = (num_kv_heads + 3) / 4;
-  std::vector<int32_t> by_len;
-  by_len.reserve(num_seqs);
-  for (int32_t s = 0; s < num_seqs; ++s)
-    if (lens[s] > 0) by_len.push_back(s);
-  std::stable_sort(by_len.begin(), by_len.end(), [&](int32_t x, int32_t y) { return lens[x] > lens[y]; });
-  std::vector<int32_t> order;
-  order.reserve(by_len.size());
-  for (size_t i = 0, j = by_len.size(); i < j;) {
-    order.push_back(by_len[i++]);
-    if (i < j) order.push_back(by_len[--j]);
+// A run of tiles to schedule: tiles [t_begin, t_end) of sequence `seq` for
+// KV heads 4*hb .. 4*hb + 3.  A shared stream reads the prefix blocks of a
+// prefix group once for all its members (`group` names its descriptor).
+// The streams of one item (the head blocks of one sequence's run) are
+// consecutive in the stream list and stay together in the layout.
+struct Stream {
+  int32_t seq, hb, t_begin, t_end, L, group, item;
+};
+
+// Equal-work chunks: the items, in alternating length order (longest,
+// shortest, second longest, ...), their streams in list order, are laid end
+// to end and cut into nwg
+// consecutive chunks of equal cost (tokens of each tile, plus kStreamCharge at
+// a stream's first tile) at tile boundaries; a tile goes to the workgroup whose
+// share holds the tile's midpoint.  Consecutive tiles of one stream on one
+// workgroup form jobs of at most `cap` tiles.  Returns, per stream, its
+// pieces in order (indices into out.pieces) through `first`/`count`, and the
+// order in which the streams were laid out.
+void chunk_streams(std::vector<Stream>& streams, int64_t nwg_req, int64_t cap, Schedule& out,
+                   std::vector<int32_t>& first, std::vector<int32_t>& count, std::vector<int32_t>& order) {
+  // Items: runs of consecutive streams with the same item id.
+  std::vector<int32_t> item_first;
+  for (size_t i = 0; i < streams.size(); ++i)
+    if (i == 0 || streams[i].item != streams[i - 1].item) item_first.push_back((int32_t)i);
+  item_first.push_back((int32_t)streams.size());
+  const size_t items = item_first.size() - 1;
+  auto item_len = [&](size_t it) {  // tokens of the item's first stream
+    const Stream& st = streams[item_first[it]];
+    return std::min(st.L, 16 * st.t_end) - 16 * st.t_begin;
+  };
+  std::vector<int32_t> by_len(items);
+  for (size_t i = 0; i < items; ++i) by_len[i] = (int32_t)i;
+  std::stable_sort(by_len.begin(), by_len.end(), [&](int32_t x, int32_t y) { return item_len(x) > item_len(y); });
+  order.clear();
+  order.reserve(streams.size());
+  auto put = [&](int32_t it) {
+    for (int32_t k = item_first[it]; k < item_first[it + 1]; ++k) order.push_back(k);
+  };
+  for (size_t i = 0, j = items; i < j;) {
+    put(by_len[i++]);
+    if (i < j) put(by_len[--j]);
   }
   int64_t total = 0, total_tiles = 0;
-  for (int32_t s : order) {
-    total += (lens[s] + kStreamCharge) * head_blocks;
-    total_tiles += ((int64_t)lens[s] + 15) / 16 * head_blocks;
+  for (const Stream& st : streams) {
+    for (int64_t t = st.t_begin; t < st.t_end; ++t) total += tile_rows(st.L, t);
+    total += kStreamCharge;
+    total_tiles += st.t_end - st.t_begin;
   }
   const int64_t nwg = std::max<int64_t>(1, std::min<int64_t>(nwg_req, total_tiles));
   out.nwg = nwg;
-  std::vector<int32_t> first_of_stream(num_seqs, -1);  // piece index of (s, hb = 0); streams of s are consecutive
+  first.assign(streams.size(), 0);
+  count.assign(streams.size(), 0);
   int64_t cum = 0;
-  for (int32_t s : order) {
-    const int32_t L = lens[s];
-    const int64_t tiles = ((int64_t)L + 15) / 16;
-    for (int64_t hb = 0; hb < head_blocks; ++hb) {
-      const size_t first = out.pieces.size();
-      if (hb == 0) first_of_stream[s] = (int32_t)first;
-      int64_t last_wg = -1;
-      for (int64_t t = 0; t < tiles; ++t) {
-        const int64_t c = tile_rows(L, t) + (t == 0 ? kStreamCharge : 0);
-        const int64_t wg = std::min<int64_t>(nwg - 1, ((2 * cum + c) * nwg) / (2 * total));
-        cum += c;
-        if (wg != last_wg || out.pieces.back().job.tile_count >= cap) {
-          out.pieces.push_back(Piece{(int32_t)wg, pa_decode_job{s, (int32_t)t, 0, (int32_t)hb, 0, 1, -1, L}});
-          last_wg = wg;
-        }
-        out.pieces.back().job.tile_count += 1;
+  for (int32_t si : order) {
+    const Stream& st = streams[si];
+    first[si] = (int32_t)out.pieces.size();
+    int64_t last_wg = -1;
+    for (int64_t t = st.t_begin; t < st.t_end; ++t) {
+      const int64_t c = tile_rows(st.L, t) + (t == st.t_begin ? kStreamCharge : 0);
+      const int64_t wg = std::min<int64_t>(nwg - 1, ((2 * cum + c) * nwg) / (2 * total));
+      cum += c;
+      if (wg != last_wg || out.pieces.back().job.tile_count >= cap) {
+        out.pieces.push_back(Piece{(int32_t)wg, pa_decode_job{st.seq, (int32_t)t, 0, st.hb, 0, 1, -1, st.L}});
+        last_wg = wg;
       }
-      const int32_t parts = (int32_t)(out.pieces.size() - first);
-      if (parts > 1) {
-        const int64_t heads = std::min<int64_t>(4, num_kv_heads - 4 * hb);
-        for (int32_t p = 0; p < parts; ++p) {
-          out.pieces[first + p].job.part = p;
-          out.pieces[first + p].job.num_parts = parts;
-          out.pieces[first + p].job.record_base = (int32_t)out.records;
-        }
-        out.records += (int64_t)parts * heads;
-        if (out.records > INT32_MAX / 1024) return fail(PA_ERR_INVALID, "pa_decode_plan: plan too large");
-      }
+      out.pieces.back().job.tile_count += 1;
     }
+    count[si] = (int32_t)out.pieces.size() - first[si];
+  }
+}
+
+// Chunk schedule of plain (unshared) streams, one per (sequence, head
+// block).  Records are per stream: KV head 4*hb + w, piece p at
+// record_base + w * parts + p.
+pa_status schedule_chunks(const int32_t* lens, int32_t num_seqs, int32_t num_kv_heads, int64_t nwg_req, int64_t cap,
+                          Schedule& out) {
+  const int32_t head_blocks = (num_kv_heads + 3) / 4;
+  std::vector<Stream> streams;
+  for (int32_t s = 0; s < num_seqs; ++s)
+    if (lens[s] > 0)
+      for (int32_t hb = 0; hb < head_blocks; ++hb)
+        streams.push_back(Stream{s, hb, 0, (lens[s] + 15) / 16, lens[s], -1, s});
+  std::vector<int32_t> first, count, order;
+  chunk_streams(streams, nwg_req, cap, out, first, count, order);
+  std::vector<int32_t> stream_of_seq(num_seqs, -1);
+  for (size_t i = 0; i < streams.size(); ++i)
+    if (streams[i].hb == 0) stream_of_seq[streams[i].seq] = (int32_t)i;
+  for (int32_t i : order) {  // records in layout order
+    const int32_t parts = count[i];
+    if (parts <= 1) continue;
+    const int64_t heads = std::min<int64_t>(4, num_kv_heads - 4 * streams[i].hb);
+    for (int32_t p = 0; p < parts; ++p) {
+      pa_decode_job& j = out.pieces[first[i] + p].job;
+      j.part = p;
+      j.num_parts = parts;
+      j.record_base = (int32_t)out.records;
+    }
+    out.records += (int64_t)parts * heads;
+    if (out.records > INT32_MAX / 1024) return fail(PA_ERR_INVALID, "pa_decode_plan: plan too large");
   }
   // Merge rows, sequence by sequence: every KV head of an empty sequence
   // (zeros) and of every cut stream.
@@ -214,14 +256,128 @@ pa_status schedule_chunks(const int32_t* lens, int32_t num_seqs, int32_t num_kv_
       for (int32_t g = 0; g < num_kv_heads; ++g) out.merges.push_back(pa_decode_merge{s, g, 0, -1});
       continue;
     }
-    size_t i = (size_t)first_of_stream[s];
-    for (int64_t hb = 0; hb < head_blocks; ++hb) {
-      const pa_decode_job& j = out.pieces[i].job;
-      if (j.num_parts > 1) {
-        for (int32_t g = 4 * (int32_t)hb; g < std::min<int32_t>(num_kv_heads, 4 * (int32_t)hb + 4); ++g)
-          out.merges.push_back(pa_decode_merge{s, g, j.num_parts, j.record_base + (g - 4 * (int32_t)hb) * j.num_parts});
+    for (int32_t hb = 0; hb < head_blocks; ++hb) {
+      const int32_t i = stream_of_seq[s] + hb;
+      const pa_decode_job& j = out.pieces[first[i]].job;
+      if (count[i] <= 1) continue;
+      for (int32_t g = 4 * hb; g < std::min<int32_t>(num_kv_heads, 4 * hb + 4); ++g)
+        out.merges.push_back(pa_decode_merge{s, g, j.num_parts, j.record_base + (g - 4 * hb) * j.num_parts});
+    }
+  }
+  return PA_OK;
+}
+
+// Chunk schedule with prefix groups.  A group of n members sharing T tiles
+// gives one item of shared streams (tiles [0, T) of the first member, per
+// head block) and, per member, an item of its own streams (tiles [T, end)).
+// Member records are per (member, head block): the shared pieces first, then
+// its own pieces.  Ungrouped sequences are planned as by schedule_chunks.
+pa_status schedule_prefix(const int32_t* lens, int32_t num_seqs, int32_t num_kv_heads, int32_t group_cap,
+                          const int32_t* prefix_group, const int32_t* prefix_tokens, int64_t nwg_req, int64_t cap,
+                          Schedule& out) {
+  const int32_t head_blocks = (num_kv_heads + 3) / 4;
+  // Groups: members in sequence order, cut into groups of at most group_cap.
+  std::vector<int32_t> by_key;
+  for (int32_t s = 0; s < num_seqs; ++s)
+    if (prefix_group[s] >= 0 && lens[s] > 0) by_key.push_back(s);
+  std::stable_sort(by_key.begin(), by_key.end(), [&](int32_t x, int32_t y) { return prefix_group[x] < prefix_group[y]; });
+  std::vector<std::vector<int32_t>> groups;
+  std::vector<int32_t> shared_tiles;
+  for (size_t i = 0; i < by_key.size();) {
+    size_t j = i;
+    while (j < by_key.size() && prefix_group[by_key[j]] == prefix_group[by_key[i]]) ++j;
+    for (size_t k = i; k < j; k += (size_t)group_cap) {
+      std::vector<int32_t> g(by_key.begin() + k, by_key.begin() + std::min(j, k + (size_t)group_cap));
+      int64_t tok = INT64_MAX;
+      for (int32_t m : g) tok = std::min<int64_t>(tok, std::min<int64_t>(prefix_tokens[m], lens[m] - 1));
+      const int32_t t = tok > 0 ? (int32_t)(tok / 16) : 0;
+      if (g.size() >= 2 && t >= 1) {
+        groups.push_back(g);
+        shared_tiles.push_back(t);
       }
-      i += (size_t)j.num_parts;
+    }
+    i = j;
+  }
+  std::vector<int32_t> group_of(num_seqs, -1);
+  for (size_t gi = 0; gi < groups.size(); ++gi)
+    for (int32_t m : groups[gi]) group_of[m] = (int32_t)gi;
+  // Streams: shared items first in the list, then every sequence's own item.
+  std::vector<Stream> streams;
+  int32_t item = 0;
+  for (size_t gi = 0; gi < groups.size(); ++gi, ++item) {
+    const int32_t lead = groups[gi][0];
+    for (int32_t hb = 0; hb < head_blocks; ++hb)
+      streams.push_back(Stream{lead, hb, 0, shared_tiles[gi], lens[lead], (int32_t)(gi * head_blocks + hb), item});
+  }
+  std::vector<int32_t> own_stream(num_seqs, -1);
+  for (int32_t s = 0; s < num_seqs; ++s, ++item) {
+    if (lens[s] == 0) continue;
+    const int32_t t0 = group_of[s] >= 0 ? shared_tiles[group_of[s]] : 0;
+    own_stream[s] = (int32_t)streams.size();
+    for (int32_t hb = 0; hb < head_blocks; ++hb) streams.push_back(Stream{s, hb, t0, (lens[s] + 15) / 16, lens[s], -1, item});
+  }
+  std::vector<int32_t> first, count, order;
+  chunk_streams(streams, nwg_req, cap, out, first, count, order);
+  // Records, in layout order of the own streams: a grouped member always has
+  // records (its shared pieces and its own); others only when cut.
+  std::vector<int32_t> rb((size_t)num_seqs * head_blocks, -1), parts((size_t)num_seqs * head_blocks, 0);
+  for (int32_t i : order) {
+    const Stream& st = streams[i];
+    if (st.group >= 0) continue;
+    const int32_t s = st.seq, hb = st.hb;
+    const int32_t gi = group_of[s];
+    const int32_t ks = gi >= 0 ? count[gi * head_blocks + hb] : 0;  // shared streams come first in the list
+    const int32_t np = ks + count[i];
+    if (np <= 1) continue;
+    const int64_t heads = std::min<int64_t>(4, num_kv_heads - 4 * hb);
+    rb[(size_t)s * head_blocks + hb] = (int32_t)out.records;
+    parts[(size_t)s * head_blocks + hb] = np;
+    for (int32_t p = 0; p < count[i]; ++p) {
+      pa_decode_job& j = out.pieces[first[i] + p].job;
+      j.part = ks + p;
+      j.num_parts = np;
+      j.record_base = (int32_t)out.records;
+    }
+    out.records += (int64_t)np * heads;
+    if (out.records > INT32_MAX / 1024) return fail(PA_ERR_INVALID, "pa_decode_plan: plan too large");
+  }
+  // Group descriptors (one per group and head block) and shared jobs.
+  for (size_t gi = 0; gi < groups.size(); ++gi) {
+    for (int32_t hb = 0; hb < head_blocks; ++hb) {
+      pa_decode_group d{};
+      d.num_members = (int32_t)groups[gi].size();
+      d.head_block = hb;
+      for (int32_t m = 0; m < 4; ++m) {
+        const int32_t s = groups[gi][std::min<size_t>(m, groups[gi].size() - 1)];
+        d.seq[m] = s;
+        d.record_base[m] = rb[(size_t)s * head_blocks + hb];
+        d.num_parts[m] = parts[(size_t)s * head_blocks + hb];
+      }
+      const int32_t di = (int32_t)out.groups.size();
+      out.groups.push_back(d);
+      const int32_t i = (int32_t)(gi * head_blocks + hb);
+      for (int32_t p = 0; p < count[i]; ++p) {
+        pa_decode_job& j = out.pieces[first[i] + p].job;
+        j.head_block = hb | PA_JOB_SHARED;
+        j.part = p;
+        j.num_parts = d.num_members;
+        j.record_base = di;
+      }
+    }
+    out.group_size = std::max<int32_t>(out.group_size, (int32_t)groups[gi].size());
+  }
+  // Merge rows, sequence by sequence.
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    if (lens[s] == 0) {
+      for (int32_t g = 0; g < num_kv_heads; ++g) out.merges.push_back(pa_decode_merge{s, g, 0, -1});
+      continue;
+    }
+    for (int32_t hb = 0; hb < head_blocks; ++hb) {
+      const int32_t np = parts[(size_t)s * head_blocks + hb];
+      if (np <= 1) continue;
+      const int32_t b = rb[(size_t)s * head_blocks + hb];
+      for (int32_t g = 4 * hb; g < std::min<int32_t>(num_kv_heads, 4 * hb + 4); ++g)
+        out.merges.push_back(pa_decode_merge{s, g, np, b + (g - 4 * hb) * np});
     }
   }
   return PA_OK;
@@ -327,6 +483,93 @@ int64_t schedule_cost(const Schedule& sc, const int32_t* lens) {
 }  // namespace
 }  // namespace pagedkv
 
+namespace pagedkv {
+namespace {
+
+// Serialise a schedule: the column-major job table, the merge rows, the
+// group descriptors.
+pa_status emit_plan(const Schedule& sc, int32_t schedule_id, int32_t num_kv_heads, void* plan, size_t capacity,
+                    pa_decode_plan_info* info) {
+  const std::vector<Piece>& jobs = sc.pieces;
+  const std::vector<pa_decode_merge>& merges = sc.merges;
+  const int64_t nwg = sc.nwg;
+  if (jobs.size() > (size_t)INT32_MAX / 64 || merges.size() > (size_t)INT32_MAX / 64 ||
+      sc.groups.size() > (size_t)INT32_MAX / 64)
+    return fail(PA_ERR_INVALID, "pa_decode_plan: plan too large");
+  // Per-workgroup lists, column-major: slot k of workgroup b is entry
+  // k * nwg + b, so a workgroup reads its first jobs without an index load.
+  // Slots past a workgroup's last job are empty (tile_count 0).  A
+  // workgroup's jobs keep schedule order.
+  std::vector<int32_t> count(nwg, 0);
+  for (const Piece& pc : jobs) count[pc.wg] += 1;
+  int64_t per = 0;
+  for (int32_t c : count) per = std::max<int64_t>(per, c);
+  if (per * nwg > (int64_t)INT32_MAX / 64) return fail(PA_ERR_INVALID, "pa_decode_plan: plan too large");
+  std::vector<pa_decode_job> table((size_t)(per * nwg), pa_decode_job{0, 0, 0, 0, 0, 0, -1, 0});
+  std::vector<int32_t> fill(nwg, 0);
+  for (const Piece& pc : jobs) table[(size_t)fill[pc.wg]++ * nwg + pc.wg] = pc.job;
+
+  pa_decode_plan_info in{};
+  in.num_workgroups = jobs.empty() ? 0 : (int32_t)nwg;
+  in.num_jobs = (int32_t)jobs.size();
+  in.num_merges = (int32_t)merges.size();
+  in.num_records = (int32_t)sc.records;
+  in.num_kv_heads = num_kv_heads;
+  in.jobs_per_workgroup = jobs.empty() ? 0 : (int32_t)per;
+  in.jobs_at = 0;
+  in.merges_at = (int32_t)(sizeof(pa_decode_job) * table.size());
+  in.schedule = schedule_id;
+  in.num_groups = (int32_t)sc.groups.size();
+  in.groups_at = (int32_t)round_up((size_t)in.merges_at + sizeof(pa_decode_merge) * merges.size(), 64);
+  in.group_size = sc.group_size;
+  const size_t bytes = (size_t)in.groups_at + sizeof(pa_decode_group) * sc.groups.size();
+  if (bytes > (size_t)INT32_MAX) return fail(PA_ERR_INVALID, "pa_decode_plan: plan too large");
+  in.bytes = (int32_t)bytes;
+  *info = in;
+  if (bytes > capacity)
+    return fail(PA_ERR_INVALID, "pa_decode_plan: capacity %zu < %zu bytes", capacity, bytes);
+  char* out = static_cast<char*>(plan);
+  std::memset(out, 0, bytes);
+  if (!jobs.empty()) std::memcpy(out + in.jobs_at, table.data(), sizeof(pa_decode_job) * table.size());
+  if (!merges.empty()) std::memcpy(out + in.merges_at, merges.data(), sizeof(pa_decode_merge) * merges.size());
+  if (!sc.groups.empty())
+    std::memcpy(out + in.groups_at, sc.groups.data(), sizeof(pa_decode_group) * sc.groups.size());
+  return PA_OK;
+}
+
+}  // namespace
+}  // namespace pagedkv
+
+extern "C" pa_status pa_decode_plan_prefix(const int32_t* context_lens, int32_t num_seqs, int32_t num_kv_heads,
+                                           int32_t num_q_heads, int32_t num_workgroups, int32_t max_piece_tiles,
+                                           const int32_t* prefix_group, const int32_t* prefix_tokens, void* plan,
+                                           size_t capacity, pa_decode_plan_info* info) {
+  if (!info || num_seqs < 0 || num_kv_heads <= 0 || num_workgroups <= 0 ||
+      (num_seqs > 0 && (!context_lens || !prefix_group || !prefix_tokens)))
+    return fail(PA_ERR_INVALID, "pa_decode_plan_prefix: bad arguments");
+  if (num_q_heads <= 0 || num_q_heads % num_kv_heads != 0)
+    return fail(PA_ERR_INVALID, "pa_decode_plan_prefix: num_q_heads %d not a multiple of num_kv_heads %d",
+                num_q_heads, num_kv_heads);
+  if (max_piece_tiles < 0 || max_piece_tiles > 64)
+    return fail(PA_ERR_INVALID, "pa_decode_plan_prefix: max_piece_tiles %d outside [0, 64]", max_piece_tiles);
+  if (capacity > 0 && (!plan || !pagedkv::aligned(plan, 8)))
+    return fail(PA_ERR_INVALID, "pa_decode_plan_prefix: plan buffer NULL or not 8-byte aligned");
+  int64_t total_tiles = 0;
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    if (context_lens[s] < 0) return fail(PA_ERR_INVALID, "pa_decode_plan_prefix: context_lens[%d] < 0", s);
+    total_tiles += ((int64_t)context_lens[s] + 15) / 16 * ((num_kv_heads + 3) / 4);
+  }
+  if (total_tiles > (int64_t)INT32_MAX / 64) return fail(PA_ERR_INVALID, "pa_decode_plan_prefix: plan too large");
+  const int32_t group = num_q_heads / num_kv_heads;
+  const int32_t group_cap = std::min(4, std::max(1, 16 / group));
+  pagedkv::Schedule sc;
+  if (pa_status st = pagedkv::schedule_prefix(context_lens, num_seqs, num_kv_heads, group_cap, prefix_group,
+                                              prefix_tokens, num_workgroups, max_piece_tiles > 0 ? max_piece_tiles : 64,
+                                              sc))
+    return st;
+  return pagedkv::emit_plan(sc, PA_SCHEDULE_CHUNKS, num_kv_heads, plan, capacity, info);
+}
+
 extern "C" pa_status pa_decode_plan(const int32_t* context_lens, int32_t num_seqs, int32_t num_kv_heads,
                                     int32_t num_workgroups, int32_t max_piece_tiles, void* plan,
                                     size_t capacity, pa_decode_plan_info* info) {
@@ -370,47 +613,8 @@ extern "C" pa_status pa_decode_plan_schedule(const int32_t* context_lens, int32_
   const bool use_lpt = schedule == PA_SCHEDULE_LPT ||
                        (schedule == PA_SCHEDULE_AUTO && !lpt.pieces.empty() &&
                         pagedkv::schedule_cost(lpt, context_lens) < pagedkv::schedule_cost(chunks, context_lens));
-  const Schedule& sc = use_lpt ? lpt : chunks;
-  const std::vector<Piece>& jobs = sc.pieces;
-  const std::vector<pa_decode_merge>& merges = sc.merges;
-  const int64_t nwg = sc.nwg;
-  if (jobs.size() > (size_t)INT32_MAX / 64 || merges.size() > (size_t)INT32_MAX / 64)
-    return fail(PA_ERR_INVALID, "pa_decode_plan: plan too large");
-
-  // Per-workgroup lists, column-major: slot k of workgroup b is entry
-  // k * nwg + b, so a workgroup reads its first jobs without an index load.
-  // Slots past a workgroup's last job are empty (tile_count 0).  A
-  // workgroup's jobs keep schedule order.
-  std::vector<int32_t> count(nwg, 0);
-  for (const Piece& pc : jobs) count[pc.wg] += 1;
-  int64_t per = 0;
-  for (int32_t c : count) per = std::max<int64_t>(per, c);
-  if (per * nwg > (int64_t)INT32_MAX / 64) return fail(PA_ERR_INVALID, "pa_decode_plan: plan too large");
-  std::vector<pa_decode_job> table((size_t)(per * nwg), pa_decode_job{0, 0, 0, 0, 0, 0, -1, 0});
-  std::vector<int32_t> fill(nwg, 0);
-  for (const Piece& pc : jobs) table[(size_t)fill[pc.wg]++ * nwg + pc.wg] = pc.job;
-
-  pa_decode_plan_info in{};
-  in.num_workgroups = jobs.empty() ? 0 : (int32_t)nwg;
-  in.num_jobs = (int32_t)jobs.size();
-  in.num_merges = (int32_t)merges.size();
-  in.num_records = (int32_t)sc.records;
-  in.num_kv_heads = num_kv_heads;
-  in.jobs_per_workgroup = jobs.empty() ? 0 : (int32_t)per;
-  in.jobs_at = 0;
-  in.merges_at = (int32_t)(sizeof(pa_decode_job) * table.size());
-  in.schedule = use_lpt ? PA_SCHEDULE_LPT : PA_SCHEDULE_CHUNKS;
-  const size_t bytes = (size_t)in.merges_at + sizeof(pa_decode_merge) * merges.size();
-  if (bytes > (size_t)INT32_MAX) return fail(PA_ERR_INVALID, "pa_decode_plan: plan too large");
-  in.bytes = (int32_t)bytes;
-  *info = in;
-  if (bytes > capacity)
-    return fail(PA_ERR_INVALID, "pa_decode_plan: capacity %zu < %zu bytes", capacity, bytes);
-  char* out = static_cast<char*>(plan);
-  std::memset(out, 0, bytes);
-  if (!jobs.empty()) std::memcpy(out + in.jobs_at, table.data(), sizeof(pa_decode_job) * table.size());
-  if (!merges.empty()) std::memcpy(out + in.merges_at, merges.data(), sizeof(pa_decode_merge) * merges.size());
-  return PA_OK;
+  return pagedkv::emit_plan(use_lpt ? lpt : chunks, use_lpt ? PA_SCHEDULE_LPT : PA_SCHEDULE_CHUNKS, num_kv_heads,
+                            plan, capacity, info);
 }
 
 extern "C" size_t pa_decode_workspace_bytes(const pa_decode_plan_info* info, int32_t num_q_heads,
@@ -465,8 +669,14 @@ pa_status decode_stages(int stages, const char* who, const pa_kv_pool* pool, con
       (info->num_jobs > 0 && (info->num_workgroups == 0 || info->jobs_per_workgroup == 0)) ||
       (int64_t)info->jobs_per_workgroup * info->num_workgroups < (int64_t)info->num_jobs ||
       (int64_t)info->merges_at < 32 * (int64_t)info->jobs_per_workgroup * info->num_workgroups ||
-      (int64_t)info->bytes < (int64_t)info->merges_at + 16 * (int64_t)info->num_merges)
+      (int64_t)info->bytes < (int64_t)info->merges_at + 16 * (int64_t)info->num_merges ||
+      info->num_groups < 0 ||
+      (info->num_groups > 0 && (info->groups_at % 64 != 0 ||
+                                (int64_t)info->groups_at < (int64_t)info->merges_at + 16 * (int64_t)info->num_merges ||
+                                (int64_t)info->bytes < (int64_t)info->groups_at + 64 * (int64_t)info->num_groups)))
     return fail(PA_ERR_INVALID, "%s: inconsistent plan info", who);
+  if (info->num_groups > 0 && pool->dtype != PA_BF16)
+    return fail(PA_ERR_UNSUPPORTED, "%s: shared-prefix plans need a bf16 pool", who);
   const auto lay = pagedkv::layout((int64_t)info->num_records * group, pool->head_dim);
   if (info->num_records > 0) {
     if (!workspace) return fail(PA_ERR_INVALID, "%s: workspace is NULL but the plan has records", who);
@@ -486,6 +696,8 @@ pa_status decode_stages(int stages, const char* who, const pa_kv_pool* pool, con
   const char* pb = static_cast<const char*>(plan);
   a.jobs = reinterpret_cast<const pa_decode_job*>(pb + info->jobs_at);
   a.merges = reinterpret_cast<const pa_decode_merge*>(pb + info->merges_at);
+  a.groups = info->num_groups > 0 ? reinterpret_cast<const pa_decode_group*>(pb + info->groups_at) : nullptr;
+  a.num_groups = info->num_groups;
   char* ws = static_cast<char*>(workspace);
   a.partial_ml = info->num_records > 0 ? reinterpret_cast<float*>(ws + lay.ml) : nullptr;
   a.partial_o = info->num_records > 0 ? reinterpret_cast<float*>(ws + lay.o) : nullptr;

@@ -225,6 +225,53 @@ extern "C" pa_status pa_bm_export(const pa_bm* bm, const int64_t* seqs, int32_t 
   return PA_OK;
 }
 
+extern "C" pa_status pa_bm_prefix_groups(const pa_bm* bm, const int64_t* seqs, int32_t num, int32_t* group_out,
+                                         int32_t* prefix_tokens_out) {
+  if (!bm || num < 0 || (num > 0 && (!seqs || !group_out || !prefix_tokens_out)))
+    return fail(PA_ERR_INVALID, "pa_bm_prefix_groups: bad arguments");
+  std::vector<const pa_bm::Seq*> batch(num);
+  for (int32_t i = 0; i < num; ++i) {
+    auto it = bm->seqs.find(seqs[i]);
+    if (it == bm->seqs.end())
+      return fail(PA_ERR_NOT_FOUND, "pa_bm_prefix_groups: unknown sequence %lld", (long long)seqs[i]);
+    batch[i] = &it->second;
+  }
+  // Group by first physical block: the batch position of the first sequence
+  // holding that block.
+  std::unordered_map<int32_t, int32_t> first_pos;
+  std::vector<int32_t> members(num, 0);
+  for (int32_t i = 0; i < num; ++i) {
+    group_out[i] = -1;
+    prefix_tokens_out[i] = 0;
+    if (batch[i]->table.empty()) continue;
+    auto ins = first_pos.emplace(batch[i]->table[0], i);
+    group_out[i] = ins.first->second;
+    members[ins.first->second] += 1;
+  }
+  // Shared tokens of a group: its longest common run of leading blocks,
+  // in tokens, capped by the shortest member.
+  std::vector<int64_t> common(num, -1), shortest(num, INT64_MAX);
+  for (int32_t i = 0; i < num; ++i) {
+    const int32_t g = group_out[i];
+    if (g < 0) continue;
+    if (members[g] < 2) {
+      group_out[i] = -1;
+      continue;
+    }
+    const auto& lead = batch[g]->table;
+    const auto& t = batch[i]->table;
+    int64_t c = 0;
+    while (c < (int64_t)t.size() && c < (int64_t)lead.size() && t[c] == lead[c]) ++c;
+    common[g] = common[g] < 0 ? c : std::min(common[g], c);
+    shortest[g] = std::min<int64_t>(shortest[g], batch[i]->len);
+  }
+  for (int32_t i = 0; i < num; ++i) {
+    const int32_t g = group_out[i];
+    if (g >= 0) prefix_tokens_out[i] = (int32_t)std::min<int64_t>(common[g] * bm->block_size, shortest[g]);
+  }
+  return PA_OK;
+}
+
 extern "C" int32_t pa_bm_len(const pa_bm* bm, int64_t seq) {
   if (!bm) return -1;
   auto it = bm->seqs.find(seq);

@@ -122,22 +122,32 @@ __device__ __forceinline__ void store1(const DecodeArgs& a, int64_t idx, float x
 // Job fields as seen by one wavefront (all wave-uniform).
 struct JobView {
   int32_t seq, g, t0, cnt, L, rec;
-  bool idle;  // the wavefront's KV head is past the last one: read nothing, write nothing
+  int32_t w;     // wavefront's KV head within the head block
+  int32_t grp;   // shared job: its group descriptor
+  int32_t part;  // shared job: piece of the shared prefix
+  int32_t ncol;  // query columns computed: G, or members x G for a shared job
+  bool idle;     // the wavefront's KV head is past the last one: read nothing, write nothing
+  bool shared;   // the job reads a prefix shared by the members of a group
 };
 
 // The fields of job record jd for wavefront w (the context length comes
 // with the record).  Any record (an empty slot included) gives in-range
 // addresses; a wavefront whose KV head is past the last one is idle.
 __device__ __forceinline__ void view_job(const DecodeArgs& a, const pa_decode_job& jd, int w, int B, JobView& v) {
-  const int32_t g = jd.head_block * kNW + w;
-  v.idle = g < 0 || g >= a.num_kv_heads;
+  v.shared = (jd.head_block & PA_JOB_SHARED) != 0;
+  const int32_t g = (jd.head_block & 0xffff) * kNW + w;
+  v.w = w;
+  v.idle = g < 0 || g >= a.num_kv_heads || (v.shared && a.num_groups <= 0);
+  v.grp = v.shared ? min(max(jd.record_base, 0), max(a.num_groups - 1, 0)) : 0;
+  v.part = max(jd.part, 0);
+  v.ncol = v.shared ? min(max(jd.num_parts, 1), 4) * a.group : a.group;
   v.g = min(max(g, 0), a.num_kv_heads - 1);
   v.cnt = min(max(jd.tile_count, 0), kMaxTiles);
   v.seq = min(max(jd.seq, 0), a.num_seqs - 1);
   v.t0 = max(jd.tile_begin, 0);
   v.L = min(max(jd.context_len, 0), a.max_blocks * B);
   v.rec = -1;
-  if (jd.num_parts > 1) {
+  if (!v.shared && jd.num_parts > 1) {
     const int64_t r = (int64_t)jd.record_base + (int64_t)w * jd.num_parts + jd.part;
     v.rec = (jd.record_base >= 0 && jd.part >= 0 && jd.part < jd.num_parts && r < a.num_records) ? (int32_t)r : -2;
   }
@@ -172,15 +182,27 @@ __device__ __forceinline__ void load_ref(const DecodeArgs& a, const pa_decode_jo
   J.tb1 = B == 8 ? trow[min(e0 + 1, a.max_blocks - 1)] : 0;
 }
 
-// Q^T fragments: lane holds Q[head li][32*ks + 8*lq .. +8].  Columns
-// li >= G repeat head G - 1: every column's softmax and accumulator are
-// independent and only columns below G are written, so the repeats cost
-// nothing and the loaded values are not touched before the job's first tile.
+// Q^T fragments: lane holds Q[column li][32*ks + 8*lq .. +8].  Column li is
+// query head li of the job's KV head (li < G), or, for a shared job, head
+// li % G of member li / G.  Columns past the last live one repeat it: every
+// column's softmax and accumulator are independent and only live columns
+// are written, so the repeats cost nothing and the loaded values are not
+// touched before the job's first tile.
 __device__ __forceinline__ void load_q(const DecodeArgs& a, const JobView& v, int li, int lq, bf16x8_t (&qf)[4]) {
   constexpr int D = 128;
   const int G = a.group;
+  const int col = min(li, v.ncol - 1);
+  int32_t seq = v.seq;
+  if (v.shared && !v.idle) {
+    const auto* gd = as_const(reinterpret_cast<const i32x4_t*>(a.groups + v.grp));
+    const i32x4_t members = gd[0 + 0];  // num_members, head_block, seq[0], seq[1]
+    const i32x4_t more = gd[1];         // seq[2], seq[3], record_base[0], record_base[1]
+    const int m = col / G;
+    const int32_t s0 = members[2], s1 = members[3], s2 = more[0], s3 = more[1];
+    seq = min(max(m == 0 ? s0 : m == 1 ? s1 : m == 2 ? s2 : s3, 0), a.num_seqs - 1);
+  }
   const uint4* qrow = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.q) +
-                                                     ((int64_t)v.seq * a.num_q_heads + (int64_t)v.g * G + min(li, G - 1)) * D);
+                                                     ((int64_t)seq * a.num_q_heads + (int64_t)v.g * G + col % G) * D);
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     const uint4 x = qrow[4 * ks + lq];
@@ -453,6 +475,27 @@ __device__ __forceinline__ void finish_bf16_job(const DecodeArgs& a, const JobVi
   const int G = a.group;
   float lt = st.l + __shfl_xor(st.l, 16);
   lt = lt + __shfl_xor(lt, 32);
+  if (v.shared) {
+    // Shared prefix piece: column li is head li % G of member li / G; each
+    // member's record for this piece is written directly.
+    if (v.idle || li >= v.ncol) return;
+    const auto* gd = as_const(reinterpret_cast<const i32x4_t*>(a.groups + v.grp));
+    const i32x4_t x1 = gd[1], x2 = gd[2], x3 = gd[3];  // seq[2..3] rb[0..1] | rb[2..3] np[0..1] | np[2..3] -
+    const int m = li / G;
+    const int32_t rb = m == 0 ? x1[2] : m == 1 ? x1[3] : m == 2 ? x2[0] : x2[1];
+    const int32_t np = m == 0 ? x2[2] : m == 1 ? x2[3] : m == 2 ? x3[0] : x3[1];
+    const int64_t rec = (int64_t)rb + (int64_t)v.w * np + v.part;
+    if (rb < 0 || v.part >= np || rec >= a.num_records) return;
+    const int64_t rr = rec * G + li % G;
+    float* po = a.partial_o + rr * D + 32 * lq;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      *reinterpret_cast<float4*>(po + 8 * r) = make_float4(st.o[0][r], st.o[1][r], st.o[2][r], st.o[3][r]);
+      *reinterpret_cast<float4*>(po + 8 * r + 4) = make_float4(st.o[4][r], st.o[5][r], st.o[6][r], st.o[7][r]);
+    }
+    if (lq == 0) *reinterpret_cast<float2*>(a.partial_ml + 2 * rr) = make_float2(st.m, lt);
+    return;
+  }
   if (v.rec == -2) return;
   if (sg.n == sg.cap) {
     if (li >= G) return;

@@ -20,6 +20,7 @@ struct DecodeArgs {
   const int32_t* lens;
   const pa_decode_job* jobs;     // [jobs_per_workgroup][num_workgroups], column-major lists
   const pa_decode_merge* merges; // [num_merges]
+  const pa_decode_group* groups; // [num_groups] prefix-group descriptors
   float* partial_ml;             // [num_records * group][2] = (max, sum) in log2 units
   float* partial_o;              // [num_records * group][head_dim], unnormalised
   int32_t num_blocks;
@@ -35,6 +36,7 @@ struct DecodeArgs {
   int32_t num_jobs;
   int32_t num_merges;
   int32_t num_records;
+  int32_t num_groups;
   int32_t bf16;                  // pool dtype: 1 bfloat16, 0 float32
   int32_t shared_kv;             // 1: sequences share blocks (keep K/V cached), 0: stream K/V
   int32_t out_bf16;              // 1: write bfloat16, 0: float32

@@ -166,7 +166,22 @@ def _prefix_ops(case: dict):
     return p, n, case["cfg"]["prefix_len"], case["tail_lengths"]
 
 
-def product_prefix(pk, case: dict, schedule=(None, 0), shared: bool = True, private_order=None):
+def cascade_decode(pk, pool, q_dev, tables, lens, scale, bm, seqs, schedule=(None, 0), new_key=None, new_value=None):
+    """pa_decode over a plan that reads each shared prefix once per group
+    (pa_bm_prefix_groups -> pa_decode_plan_prefix)."""
+    hq = q_dev.shape[1]
+    group, tokens = bm.prefix_groups(seqs)
+    plan = pk.decode_plan_prefix(lens, pool.k.shape[2], hq, group, tokens, schedule[0], schedule[1])
+    nbytes = pk.decode_workspace_bytes(plan, hq, pool.k.shape[3])
+    ws = torch.full((nbytes // 4,), float("nan"), dtype=torch.float32, device="cuda") if nbytes else None
+    out = torch.full(tuple(q_dev.shape), float("nan"), dtype=torch.float32, device="cuda")
+    pk.decode(pool, q_dev, to_dev(tables), to_dev(lens), scale, plan, plan.to_device(), ws, out=out,
+              new_key=new_key, new_value=new_value)
+    return out, plan
+
+
+def product_prefix(pk, case: dict, schedule=(None, 0), shared: bool = True, private_order=None,
+                   cascade: bool = False):
     cfg = case["cfg"]
     b, hkv, d, dt = case["block_size"], cfg["num_kv_heads"], cfg["head_dim"], cfg["dtype"]
     p, n, pre, tails = _prefix_ops(case)
@@ -215,11 +230,16 @@ def product_prefix(pk, case: dict, schedule=(None, 0), shared: bool = True, priv
     tables, lens_out = bm.export(np.arange(nseq), maxb)
     assert np.array_equal(lens_out, lens)
     stats = bm.stats()
-    out = gpu_decode(pk, pool, to_dev(case["q"]), tables, lens, case["scale"], schedule,
-                     shared_kv=stats["shared_blocks"] > 0)
+    plan = None
+    if cascade:
+        out, plan = cascade_decode(pk, pool, to_dev(case["q"]), tables, lens, case["scale"], bm, np.arange(nseq),
+                                   schedule)
+    else:
+        out = gpu_decode(pk, pool, to_dev(case["q"]), tables, lens, case["scale"], schedule,
+                         shared_kv=stats["shared_blocks"] > 0)
     torch.cuda.synchronize()
     return dict(out=to_host(out), tables=tables, cows=np.concatenate(all_cows) if all_cows else None,
-                stats=stats, pool=pool, lens=lens, kpool=kpool, vpool=vpool, bm=bm)
+                stats=stats, pool=pool, lens=lens, kpool=kpool, vpool=vpool, bm=bm, plan=plan)
 
 
 def oracle_prefix(case: dict, seqs=None):

@@ -12,9 +12,8 @@ import torch
 import oracle
 import synth
 
-from flows import (assert_close, bits, gpu_decode, oracle_decode_step, oracle_prefix, plan_and_workspace,
-                   product_decode_step,
-                   product_prefix, to_dev, to_host)
+from flows import (assert_close, bits, cascade_decode, gpu_decode, oracle_decode_step, oracle_prefix,
+                   plan_and_workspace, product_decode_step, product_prefix, to_dev, to_host)
 
 pytestmark = pytest.mark.gpu
 
@@ -300,6 +299,51 @@ def test_shared_kv_cache_policy_gives_identical_output(pk, b):
     cached = to_host(gpu_decode(*args, shared_kv=True))
     assert np.array_equal(bits(streamed), bits(cached))
     assert np.array_equal(bits(streamed), bits(got["out"]))
+
+
+@pytest.mark.parametrize("b", [8, 16, 32])
+@pytest.mark.parametrize("schedule", [DEFAULT, SMALL_PIECES, TINY_PIECES])
+def test_cascade_decode_matches_oracle(pk, b, schedule):
+    """Shared prefixes read once per group of samples (pa_decode_plan_prefix):
+    same outputs as the oracle within tolerance, and as the per-sequence plan
+    within the accumulation-order difference."""
+    log(f"cascade c5s B={b} schedule={schedule}")
+    case = synth.prefix_case("c5s", b)
+    got = product_prefix(pk, case, schedule, cascade=True)
+    assert got["plan"].num_groups > 0
+    ref = oracle_prefix(case)
+    stats = assert_close(got["out"], ref["out"], "bf16", f"cascade c5s/B{b}/{schedule}")
+    log(f"  max|err|={stats['max_abs']:.3g} mean|err|={stats['mean_abs']:.3g} groups={got['plan'].num_groups}")
+    plain = product_prefix(pk, case, schedule)
+    assert np.abs(got["out"] - plain["out"]).max() < 2e-3
+
+
+def test_cascade_decode_with_fused_append(pk):
+    """The append fused into a shared-prefix decode: the appended tokens sit in
+    each sample's own tiles; pools byte-identical to the separate write."""
+    case = synth.prefix_case("c5s", 16)
+    got = product_prefix(pk, case, SMALL_PIECES)
+    bm, pool, lens = got["bm"], got["pool"], got["lens"]
+    nseq = len(lens)
+    # one more token per sample: block manager slots, then fused vs separate
+    rng = np.random.default_rng(7)
+    hkv, d = case["cfg"]["num_kv_heads"], case["cfg"]["head_dim"]
+    nk = synth.f32_to_bf16_bits(rng.standard_normal((nseq, hkv, d), dtype=np.float32))
+    nv = synth.f32_to_bf16_bits(rng.standard_normal((nseq, hkv, d), dtype=np.float32))
+    slots, cows = bm.append_step(np.arange(nseq))
+    assert len(cows) == 0
+    tables, lens2 = bm.export(np.arange(nseq), int(max(-(-int(L) // 16) for L in lens + 1)))
+    k_sep, v_sep = pool.k.clone(), pool.v.clone()
+    sep = pk.KvPool(k_sep, v_sep)
+    pk.reshape_and_cache(sep, to_dev(nk), to_dev(nv), to_dev(np.asarray(slots, np.int64)))
+    out_sep, _ = cascade_decode(pk, sep, to_dev(case["q"]), tables, lens2, case["scale"], bm, np.arange(nseq),
+                                SMALL_PIECES)
+    out_fused, _ = cascade_decode(pk, pool, to_dev(case["q"]), tables, lens2, case["scale"], bm, np.arange(nseq),
+                                  SMALL_PIECES, new_key=to_dev(nk), new_value=to_dev(nv))
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(to_host(pool.k)), bits(to_host(k_sep)))
+    assert np.array_equal(bits(to_host(pool.v)), bits(to_host(v_sep)))
+    assert np.array_equal(bits(to_host(out_fused)), bits(to_host(out_sep)))
 
 
 def test_use_after_free_poisoning_leaves_sharers_unchanged(pk):

@@ -84,3 +84,12 @@ def test_full_size_prefix_sharing(pk, b):
     assert np.all(np.isfinite(got["out"]))
     stats = assert_close(got["out"][seqs], ref["out"][seqs], "bf16", f"c5 B={b}")
     log(f"  max|err|={stats['max_abs']:.3g} mean|err|={stats['mean_abs']:.3g}")
+    # The same batch with each shared prefix read once per group of samples.
+    from flows import cascade_decode, to_dev
+    out, plan = cascade_decode(pk, got["pool"], to_dev(case["q"]), got["tables"], got["lens"], case["scale"],
+                               got["bm"], np.arange(len(lens)))
+    assert plan.num_groups == case["cfg"]["num_prompts"] * -(-hkv // 4)
+    out = to_host(out)
+    assert np.all(np.isfinite(out))
+    stats = assert_close(out[seqs], ref["out"][seqs], "bf16", f"c5 B={b} cascade")
+    log(f"  cascade max|err|={stats['max_abs']:.3g} mean|err|={stats['mean_abs']:.3g}")

@@ -458,3 +458,128 @@ def test_abi_rejects_bad_decode_arguments_without_launching():
     pool32 = _pool(dtype=0, d=64)
     assert L.pa_decode(ctypes.byref(pool32), p, p, 1, p, 400, p, 2, 8, ctypes.c_float(1.0), None, None, p,
                        ctypes.byref(plan.info), ws["ws"], ws["wsb"], None) == -2   # bf16 output, f32 pool
+
+
+# ------------------------------------------------------------ prefix groups
+def _forked_batch(b, prompts, samples, prefix, tails, order_seed=3):
+    """Block manager holding `prompts` prompts of `prefix` tokens, each forked
+    into `samples` sequences that then append their own tails (the first
+    divergent token copies the shared partial block)."""
+    rng = np.random.default_rng(order_seed)
+    nb = prompts * (prefix // b + 2) + samples * prompts * (max(tails) // b + 3) + 8
+    bm = pk.BlockManager(nb, b, rng.permutation(nb).astype(np.int32))
+    for i in range(prompts):
+        bm.append(1000 + i, prefix)
+        for j in range(samples):
+            bm.fork(1000 + i, i * samples + j)
+        bm.free(1000 + i)
+    seqs = np.arange(prompts * samples)
+    bm.append_step(seqs)
+    for s in seqs:
+        if tails[s] > 1:
+            bm.append(int(s), int(tails[s]) - 1)
+    return bm, seqs
+
+
+@pytest.mark.parametrize("b", [8, 16, 32])
+def test_prefix_groups_of_forked_samples(b):
+    """Samples of one prompt form one group sharing the prompt's full blocks
+    (the partial block is copied at the fork); unrelated sequences are alone."""
+    tails = np.array([5, 1, 30, 2, 7, 3, 9, 1])
+    bm, seqs = _forked_batch(b, 2, 4, 100, tails)
+    bm.append(77, 40)                       # an unrelated sequence
+    batch = np.concatenate([seqs, [77]])
+    group, tokens = bm.prefix_groups(batch)
+    assert group.tolist() == [0, 0, 0, 0, 4, 4, 4, 4, -1]
+    full = (100 // b) * b
+    assert tokens.tolist() == [full] * 8 + [0]
+    # The same from the exported tables: longest common run of leading blocks.
+    tables, lens = bm.export(batch, 64)
+    for g0 in (0, 4):
+        rows = tables[g0:g0 + 4]
+        nb = [min(-(-int(L) // b), 64) for L in lens[g0:g0 + 4]]
+        c = 0
+        while all(c < n for n in nb) and len({int(r[c]) for r in rows}) == 1:
+            c += 1
+        assert c * b == full
+
+
+def _check_prefix_plan(plan, lens, hkv, hq, group, tokens):
+    """Structural invariants of a shared-prefix plan."""
+    G = hq // hkv
+    cap = min(4, max(1, 16 // G))
+    hb_n = -(-hkv // 4)
+    tab = plan.job_table()
+    jobs = [tuple(j) for b in range(tab.shape[1]) for j in tab[:, b].tolist() if j[2] > 0]
+    groups = plan.groups()
+    covered = {}
+    own = {}
+    for seq, t0, cnt, hbf, part, nparts, rb, L in jobs:
+        shared = bool(hbf & pk.PA_JOB_SHARED)
+        hb = hbf & 0xFFFF
+        assert L == lens[seq] and 1 <= cnt <= 64
+        if shared:
+            d = groups[rb]
+            n = int(d[0])
+            assert 2 <= n <= cap and d[1] == hb and d[2] == seq and nparts == n
+            for m in range(n):
+                s = int(d[2 + m])
+                for t in range(t0, t0 + cnt):
+                    assert (s, hb, t) not in covered
+                    covered[(s, hb, t)] = ("shared", part)
+        else:
+            for t in range(t0, t0 + cnt):
+                assert (seq, hb, t) not in covered
+                covered[(seq, hb, t)] = ("own", part)
+            own.setdefault((seq, hb), []).append((part, nparts, rb))
+    for s, L in enumerate(lens):
+        for hb in range(hb_n):
+            for t in range(-(-int(L) // 16)):
+                assert (s, hb, t) in covered
+    # every group's members: shared tiles below T, same T for all, records consistent
+    used = set()
+    for d in groups:
+        n, hb = int(d[0]), int(d[1])
+        for m in range(n):
+            s, rb, np_ = int(d[2 + m]), int(d[6 + m]), int(d[10 + m])
+            parts = sorted(own[(s, hb)])
+            assert all(p[1] == np_ and p[2] == rb for p in parts)
+            shared_parts = {v[1] for k, v in covered.items() if k[0] == s and k[1] == hb and v[0] == "shared"}
+            assert sorted(shared_parts) == list(range(len(shared_parts)))
+            assert [p[0] for p in parts] == list(range(len(shared_parts), np_))
+            for w in range(min(4, hkv - 4 * hb)):
+                for p in range(np_):
+                    r = rb + w * np_ + p
+                    assert r not in used and 0 <= r < plan.num_records
+                    used.add(r)
+    merges = {(int(m[0]), int(m[1])): (int(m[2]), int(m[3])) for m in plan.merges()}
+    for (s, hb), parts in own.items():
+        np_, rb = parts[0][1], parts[0][2]
+        for g in range(4 * hb, min(hkv, 4 * hb + 4)):
+            if np_ > 1:
+                assert merges[(s, g)] == (np_, rb + (g - 4 * hb) * np_)
+            else:
+                assert (s, g) not in merges
+
+
+@pytest.mark.parametrize("b", [8, 16, 32])
+def test_prefix_plan_structure(b):
+    tails = np.array([5, 1, 30, 2, 7, 3, 9, 1, 60, 4])
+    bm, seqs = _forked_batch(b, 2, 5, 300, tails)
+    bm.append(77, 40)
+    batch = np.concatenate([seqs, [77]])
+    tables, lens = bm.export(batch, 64)
+    group, tokens = bm.prefix_groups(batch)
+    for hkv, hq, nwg in [(8, 32, 7), (8, 32, 512), (4, 32, 5), (3, 6, 9)]:
+        plan = pk.decode_plan_prefix(lens, hkv, hq, group, tokens, num_workgroups=nwg)
+        assert plan.num_groups > 0
+        G = hq // hkv
+        assert plan.group_size == min(4, 16 // G, 5)
+        _check_prefix_plan(plan, lens, hkv, hq, group, tokens)
+    # a shared part below one tile, or groups of one, plan no sharing
+    none = pk.decode_plan_prefix(lens, 8, 32, group, np.minimum(tokens, 15), num_workgroups=8)
+    assert none.num_groups == 0
+    alone = pk.decode_plan_prefix(lens, 8, 32, np.arange(len(lens)), tokens, num_workgroups=8)
+    assert alone.num_groups == 0
+    with pytest.raises(pk.PaError):
+        pk.decode_plan_prefix(lens, 8, 30, group, tokens, num_workgroups=8)
