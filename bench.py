@@ -94,14 +94,19 @@ def cpu_baseline(case, per_token: int, k_host, v_host, tables, lens, budget_s: f
             "seconds": round(dt, 3), "seqs_per_s": round(done / dt, 3)}
 
 
-def decode_workload(pk, name: str) -> dict:
+def decode_workload(pk, name: str, block_size: int | None = None) -> dict:
     """One decode step of a named workload: every sequence holds L - 1
     tokens; the step appends one token to each (timed host append) and
-    attends over L."""
+    attends over L.  block_size overrides the workload's block size (same
+    lengths; a pool of the same slack and a seeded shuffled free list)."""
     case = synth.decode_case(name)
     cfg = case["cfg"]
     lens_np = case["lengths"]
     S, B = len(lens_np), cfg["block_size"]
+    if block_size is not None and block_size != B:
+        B = block_size
+        nb = synth.pool_blocks_for(lens_np, B)
+        case = dict(case, num_blocks=nb, free_order=np.random.default_rng(cfg["seed"] + 100 * B).permutation(nb).astype(np.int32))
     bm = pk.BlockManager(case["num_blocks"], B, case["free_order"])
     for s in range(S):
         bm.append(s, int(lens_np[s]) - 1)
@@ -111,7 +116,8 @@ def decode_workload(pk, name: str) -> dict:
     host_append_us = (time.perf_counter() - t0) * 1e6
     maxb = int(max(-(-int(L) // B) for L in lens_np))
     tables, lens = bm.export(seqs, maxb)
-    return dict(name=name, desc=WORKLOADS[name], case=case, seed=cfg["seed"], S=S, hq=cfg["num_q_heads"],
+    desc = WORKLOADS[name] if B == cfg["block_size"] else WORKLOADS[name].replace("block 16", f"block {B}")
+    return dict(name=name, desc=desc, case=case, seed=cfg["seed"], S=S, hq=cfg["num_q_heads"],
                 hkv=cfg["num_kv_heads"], d=cfg["head_dim"], B=B, nb=case["num_blocks"], tables=tables, lens=lens,
                 slots=slots, cows=cows, host_append_us=host_append_us, unique_tokens=int(lens.sum()),
                 shared_kv=bm.stats()["shared_blocks"] > 0)
@@ -225,9 +231,12 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="c3", choices=sorted(WORKLOADS))
-    ap.add_argument("--block-size", type=int, default=16, choices=(8, 16, 32), help="block size of the c5 workload")
+    ap.add_argument("--block-size", type=int, default=None, choices=(8, 16, 32),
+                    help="block size (default: the workload's; c5: 16)")
     ap.add_argument("--workgroups", type=int, default=None, help="persistent workgroups (default: fill the GPU)")
     ap.add_argument("--piece", type=int, default=0, help="longest job piece in 16-token tiles (0: auto)")
+    ap.add_argument("--schedule", default="auto", choices=("auto", "chunks", "lpt"),
+                    help="host schedule (auto: the cheaper of the two by the planner's cost)")
     ap.add_argument("--replicas", type=int, default=None)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -251,9 +260,9 @@ def main() -> int:
 
     torch.cuda.set_device(0)
     if args.config == "c5":
-        w = prefix_workload(pk, args.block_size)
+        w = prefix_workload(pk, args.block_size or 16)
     else:
-        w = decode_workload(pk, args.config)
+        w = decode_workload(pk, args.config, args.block_size)
     name, case = w["name"], w["case"]
     S, hq, hkv, d, B, nb = w["S"], w["hq"], w["hkv"], w["d"], w["B"], w["nb"]
     tables, lens, slots, cows = w["tables"], w["lens"], w["slots"], w["cows"]
@@ -264,7 +273,8 @@ def main() -> int:
     if cascade:
         plan = pk.decode_plan_prefix(lens, hkv, hq, w["prefix_group"], w["prefix_tokens"], workgroups, args.piece)
     else:
-        plan = pk.decode_plan(lens, hkv, workgroups, args.piece, shared_kv=w["shared_kv"])
+        sched = {"auto": pk.SCHEDULE_AUTO, "chunks": pk.SCHEDULE_CHUNKS, "lpt": pk.SCHEDULE_LPT}[args.schedule]
+        plan = pk.decode_plan(lens, hkv, workgroups, args.piece, shared_kv=w["shared_kv"], schedule=sched)
     host_plan_us = (time.perf_counter() - t0) * 1e6
 
     dev = torch.device("cuda", 0)
@@ -393,6 +403,10 @@ def main() -> int:
         "logical_kv_bytes_per_step": logical_kv_bytes,
         "logical_kv_GBs": round(logical_kv_bytes / (ms_per_step * 1e-3) / 1e9, 2),
         "copy_blocks_per_step": int(len(cows)),
+        # block-size trade-off: slots reserved by the tables against live tokens (tail waste)
+        "reserved_slots": int(sum(-(-int(L) // B) * B for L in lens)),
+        "tail_waste_frac": round(1 - int(lens.sum()) / max(1, sum(-(-int(L) // B) * B for L in lens)), 5),
+        "us_per_output_token": round(ms_per_step * 1e3 / S, 5),
         "decode_call_us": round(decode_us, 3),
         "attention_launch_us": round(attention_us, 3),
         "host_append_us": round(host_append_us, 2),
