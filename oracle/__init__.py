@@ -7,8 +7,8 @@ from the product package: the two share no code.
 """
 from .attention import attend, decode_attention, gather_logical, widen
 from .block_manager import BlockManagerModel, OutOfBlocks
-from .cache_ops import copy_blocks, reshape_and_cache, slot_address
+from .cache_ops import copy_blocks, reshape_and_cache, slot_address, swap_blocks
 
 __all__ = ["attend", "decode_attention", "gather_logical", "widen",
            "BlockManagerModel", "OutOfBlocks", "copy_blocks",
-           "reshape_and_cache", "slot_address"]
+           "reshape_and_cache", "slot_address", "swap_blocks"]

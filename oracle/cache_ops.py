@@ -1,4 +1,4 @@
-"""CPU oracle for the two cache-writing operations and slot addressing.
+"""CPU oracle for the cache-writing operations, swapping and slot addressing.
 
 TEST INFRASTRUCTURE.  Only tests/, __graft_entry__.smoke() and the
 cpu_baseline leg of bench.py may import or call anything in oracle/.
@@ -58,3 +58,28 @@ def copy_blocks(k_pool: np.ndarray, v_pool: np.ndarray, pairs: np.ndarray) -> No
     for src, dst in pairs:
         k_pool[dst] = k_pool[src]
         v_pool[dst] = v_pool[src]
+
+
+def swap_blocks(src_k: np.ndarray, src_v: np.ndarray, dst_k: np.ndarray, dst_v: np.ndarray,
+                pairs: np.ndarray) -> None:
+    """Swap copy between a device pool and a host pool: dst[d] = src[s] for
+    every (s, d), keys and values, whole blocks, bytes unchanged.
+
+    The preemption option of copying a sequence's cache out to host memory and
+    back instead of recomputing it (mercemay.com "Paged KV Cache Allocation
+    and the Block Table", "Three ways contiguous reservation loses memory";
+    llminference.xinbetween.com S06, third exercise).  The two pools share the
+    per-block shape [B, Hkv, D]; their block counts may differ.  Modified in
+    place.
+    """
+    if src_k.shape[1:] != dst_k.shape[1:] or src_k.dtype != dst_k.dtype:
+        raise ValueError("pools must share block shape and dtype")
+    pairs = np.asarray(pairs, dtype=np.int64).reshape(-1, 2)
+    if len(set(pairs[:, 1].tolist())) != len(pairs):
+        raise ValueError("destinations must be distinct")
+    if len(pairs) and (pairs[:, 0].min() < 0 or pairs[:, 0].max() >= len(src_k)
+                       or pairs[:, 1].min() < 0 or pairs[:, 1].max() >= len(dst_k)):
+        raise ValueError("block id outside its pool")
+    for s, d in pairs:
+        dst_k[d] = src_k[s]
+        dst_v[d] = src_v[s]
