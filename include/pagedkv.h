@@ -106,6 +106,44 @@ pa_status pa_copy_blocks(const pa_kv_pool* pool, const int32_t* pairs, int32_t n
                          void* stream);
 
 /* ---------------------------------------------------------------------------
+ * pa_swap_blocks - copy whole blocks between the device pool and a pool in
+ * pinned host memory: the swap half of preemption.
+ *
+ * When blocks run out, the scheduler can stop admitting, copy a sequence's
+ * cache out to host memory and back later, or discard and recompute it
+ * (mercemay.com "Paged KV Cache Allocation and the Block Table", "Three ways
+ * contiguous reservation loses memory" and the end of "Blocks, tables, and
+ * the indirection"; llminference.xinbetween.com S06, third exercise).  This
+ * call is the copy; pa_bm_swap_out / pa_bm_swap_in produce its pairs.
+ *   device_pool : the layer's pool, device memory, as for every other call.
+ *   host_pool   : caller-owned pool of the same block_size, num_kv_heads,
+ *                 head_dim and dtype whose k and v are PINNED host memory
+ *                 (hipHostMalloc, or a tensor made with pin_memory=True),
+ *                 host_pool->num_blocks blocks each, 16-byte aligned.
+ *   pairs       : HOST int32 [num_pairs][2] = (src, dst), read during the
+ *                 call only.  PA_SWAP_OUT: src a device block, dst a host
+ *                 block; PA_SWAP_IN: src a host block, dst a device block.
+ *   engine      : PA_SWAP_ENGINE_KERNEL - kernels move the blocks through
+ *                 the host memory's device mapping, up to 240 pairs per
+ *                 launch; PA_SWAP_ENGINE_DMA - one hipMemcpyAsync per pool
+ *                 for every run of pairs that continue each other on both
+ *                 sides (src + 1, dst + 1).
+ * Checked on the host before anything is enqueued (PA_ERR_INVALID): ids
+ * inside their pools, destinations distinct, both host arrays pinned and
+ * device-mapped over their whole extent, both device arrays device memory.
+ * The copy is bit-exact.  It is ordered on `stream` like every other call:
+ * the host pool holds the swapped-out bytes only once the stream has been
+ * synchronized, and host blocks a swap-in reads must not be rewritten by the
+ * host before that.  num_pairs == 0 is a no-op.
+ * ------------------------------------------------------------------------- */
+#define PA_SWAP_OUT 0
+#define PA_SWAP_IN 1
+#define PA_SWAP_ENGINE_KERNEL 0
+#define PA_SWAP_ENGINE_DMA 1
+pa_status pa_swap_blocks(const pa_kv_pool* device_pool, const pa_kv_pool* host_pool, const int32_t* pairs,
+                         int32_t num_pairs, int32_t direction, int32_t engine, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Decode attention.
  *
  * For each sequence s with L = context_lens[s] tokens and each query head h,
@@ -350,6 +388,12 @@ typedef struct pa_bm_stats {
   int32_t pad_;
   int64_t alloc_failures; /* appends refused for lack of blocks */
   int64_t cow_copies;     /* copy-on-write pairs issued */
+  int32_t host_blocks;    /* size of the host swap pool */
+  int32_t free_host_blocks;
+  int32_t swapped_seqs;   /* sequences whose blocks are on the host (counted in num_seqs too) */
+  int32_t pad2_;
+  int64_t swap_out_blocks; /* device -> host pairs issued */
+  int64_t swap_in_blocks;  /* host -> device pairs issued */
 } pa_bm_stats;
 
 /* Returns NULL on bad sizes or if initial_order is not a permutation of
@@ -389,7 +433,8 @@ pa_status pa_bm_fork(pa_bm* bm, int64_t parent, int64_t child);
 pa_status pa_bm_free(pa_bm* bm, int64_t seq);
 
 /* Table length ceil(L / B) of `seq` (-1 if unknown); copies min(that, cap)
- * entries to HOST `out` (may be NULL when cap == 0). */
+ * entries to HOST `out` (may be NULL when cap == 0).  For a swapped sequence
+ * the entries are host-pool blocks. */
 int32_t pa_bm_table(const pa_bm* bm, int64_t seq, int32_t* out, int32_t cap);
 
 /* Dense upload arrays for a batch: tables_out HOST int32 [num][max_blocks]
@@ -409,13 +454,45 @@ pa_status pa_bm_export(const pa_bm* bm, const int64_t* seqs, int32_t num, int32_
 pa_status pa_bm_prefix_groups(const pa_bm* bm, const int64_t* seqs, int32_t num, int32_t* group_out,
                               int32_t* prefix_tokens_out);
 
+/* Swapping (preemption by copying out; mercemay.com "Three ways contiguous
+ * reservation loses memory", S06 third exercise).  The host swap pool is a
+ * second pool of blocks with its own free list and counts, under the device
+ * list's discipline (ascending ids first, last retired reused first).
+ *
+ * pa_bm_set_host_blocks sizes it (0 at creation); PA_ERR_INVALID while any
+ * sequence is swapped out.
+ *
+ * pa_bm_swap_out moves `num` distinct resident sequences to host blocks:
+ * every distinct device block of their tables gets one host block, in batch
+ * and table order, so sequences that shared a block share its host copy;
+ * then each table is retired as pa_bm_free retires it (a block that a
+ * resident sequence still names stays on the device and is copied as well).
+ * pairs_out (HOST int32 [cap_pairs][2]) receives the (device, host) copies
+ * for pa_swap_blocks(PA_SWAP_OUT), which must run before the freed device
+ * blocks are written again; *n_pairs_out the count.  A swapped sequence keeps
+ * its length; pa_bm_table returns its host table; append, fork, export and
+ * prefix grouping refuse it (PA_ERR_INVALID); pa_bm_free releases its host
+ * blocks.  pa_bm_swap_in is the mirror image: (host, device) pairs for
+ * pa_swap_blocks(PA_SWAP_IN), which must run before the sequences are read.
+ * Both are all or nothing: PA_ERR_OOM when the destination pool is short,
+ * PA_ERR_INVALID when cap_pairs is too small or a sequence repeats or is in
+ * the wrong state, PA_ERR_NOT_FOUND for an unknown one. */
+pa_status pa_bm_set_host_blocks(pa_bm* bm, int32_t num_host_blocks);
+pa_status pa_bm_swap_out(pa_bm* bm, const int64_t* seqs, int32_t num, int32_t* pairs_out, int32_t cap_pairs,
+                         int32_t* n_pairs_out);
+pa_status pa_bm_swap_in(pa_bm* bm, const int64_t* seqs, int32_t num, int32_t* pairs_out, int32_t cap_pairs,
+                        int32_t* n_pairs_out);
+int32_t pa_bm_swapped(const pa_bm* bm, int64_t seq);            /* 1 swapped, 0 resident, -1 unknown */
+int32_t pa_bm_host_refcount(const pa_bm* bm, int32_t host_block); /* -1 if out of range */
+
 int32_t pa_bm_len(const pa_bm* bm, int64_t seq);         /* -1 if unknown */
 int32_t pa_bm_refcount(const pa_bm* bm, int32_t block);  /* -1 if out of range */
 void pa_bm_get_stats(const pa_bm* bm, pa_bm_stats* out);
 
 /* Verify that each block's count equals the number of tables naming it, that
  * no named block is on the free list, that no block is lost, and that every
- * table holds ceil(L / B) entries (S06 "Reference counts must be exact").
+ * table holds ceil(L / B) entries (S06 "Reference counts must be exact"); the
+ * same for host blocks and the tables of swapped sequences.
  * PA_OK or PA_ERR_INVALID with the first violation in pa_last_error. */
 pa_status pa_bm_check(const pa_bm* bm);
 

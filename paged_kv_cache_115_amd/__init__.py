@@ -13,12 +13,14 @@ import os
 
 import numpy as np
 
-from ._lib import LIB_PATH, PA_BF16, PA_DECODE_SHARED_KV, PA_F32, PA_JOB_SHARED, PaDecodePlanInfo, PaError, PaKvPool, lib
+from ._lib import (LIB_PATH, PA_BF16, PA_DECODE_SHARED_KV, PA_F32, PA_JOB_SHARED, PA_SWAP_ENGINE_DMA,
+                   PA_SWAP_ENGINE_KERNEL, PA_SWAP_IN, PA_SWAP_OUT, PaDecodePlanInfo, PaError, PaKvPool, lib)
 
 __all__ = [
     "LIB_PATH", "PA_F32", "PA_BF16", "PA_DECODE_SHARED_KV", "PA_JOB_SHARED", "PaError", "BlockManager", "KvPool",
     "reshape_and_cache", "copy_blocks", "decode_plan", "decode_workspace_bytes",
-    "decode", "DecodePlan", "default_workgroups",
+    "decode", "DecodePlan", "default_workgroups", "HostKvPool", "swap_blocks", "PA_SWAP_OUT", "PA_SWAP_IN",
+    "PA_SWAP_ENGINE_KERNEL", "PA_SWAP_ENGINE_DMA",
 ]
 
 
@@ -63,6 +65,34 @@ class KvPool:
     @property
     def block_size(self) -> int:
         return self.c.block_size
+
+
+class HostKvPool:
+    """Swap space for one layer: caller-owned PINNED host tensors [NH, B, Hkv, D]
+    with the device pool's block shape and dtype (torch.empty(..., pin_memory=True))."""
+
+    def __init__(self, k, v):
+        if k.shape != v.shape or k.dtype != v.dtype or k.dim() != 4:
+            raise ValueError("k and v host pools must share a 4-D shape and dtype")
+        if k.is_cuda or v.is_cuda or not (k.is_contiguous() and v.is_contiguous()):
+            raise ValueError("host pools must be contiguous host tensors")
+        if not (k.is_pinned() and v.is_pinned()):
+            raise ValueError("host pools must be pinned (pin_memory=True)")
+        self.k, self.v = k, v
+        nb, b, hkv, d = k.shape
+        self.c = PaKvPool(_ptr(k), _ptr(v), nb, b, hkv, d, _dtype_code(k))
+
+
+def swap_blocks(pool: KvPool, host: HostKvPool, pairs, direction: int, engine: int = PA_SWAP_ENGINE_KERNEL,
+                stream=None) -> None:
+    """pa_swap_blocks: copy blocks between the device pool and the host pool.
+    `pairs` is a host int32 array [n, 2] of (src, dst); PA_SWAP_OUT copies
+    device -> host, PA_SWAP_IN host -> device.  Ordered on `stream`."""
+    pairs = np.ascontiguousarray(pairs, dtype=np.int32).reshape(-1, 2)
+    n = pairs.shape[0]
+    _check(lib.pa_swap_blocks(ctypes.byref(pool.c), ctypes.byref(host.c),
+                              pairs.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)) if n else None, n,
+                              direction, engine, _stream(stream)), "pa_swap_blocks")
 
 
 def _dev(t, name, dtype=None):
@@ -330,6 +360,38 @@ class BlockManager:
                                 max_blocks, tables.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
                                 lens.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))), "pa_bm_export")
         return tables[:, :max_blocks] if max_blocks else tables[:, :0], lens
+
+    def set_host_blocks(self, n: int) -> None:
+        _check(lib.pa_bm_set_host_blocks(self._h, n), "pa_bm_set_host_blocks")
+
+    def _swap(self, fn, seqs, what):
+        seqs = np.ascontiguousarray(seqs, dtype=np.int64)
+        cap = 0
+        for s in seqs.tolist():
+            n = lib.pa_bm_table(self._h, s, None, 0)
+            cap += max(n, 0)
+        pairs = np.zeros((max(cap, 1), 2), dtype=np.int32)
+        n_pairs = ctypes.c_int32(0)
+        _check(fn(self._h, seqs.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), seqs.size,
+                  pairs.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), cap, ctypes.byref(n_pairs)), what)
+        return pairs[:n_pairs.value]
+
+    def swap_out(self, seqs) -> np.ndarray:
+        """pa_bm_swap_out -> int32 [n, 2] (device block, host block) copies."""
+        return self._swap(lib.pa_bm_swap_out, seqs, "pa_bm_swap_out")
+
+    def swap_in(self, seqs) -> np.ndarray:
+        """pa_bm_swap_in -> int32 [n, 2] (host block, device block) copies."""
+        return self._swap(lib.pa_bm_swap_in, seqs, "pa_bm_swap_in")
+
+    def is_swapped(self, seq: int) -> bool:
+        r = lib.pa_bm_swapped(self._h, seq)
+        if r < 0:
+            raise KeyError(seq)
+        return bool(r)
+
+    def host_refcount(self, block: int) -> int:
+        return lib.pa_bm_host_refcount(self._h, block)
 
     def length(self, seq: int) -> int:
         n = lib.pa_bm_len(self._h, seq)

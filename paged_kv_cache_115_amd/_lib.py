@@ -10,6 +10,10 @@ PA_F32 = 0
 PA_BF16 = 1
 PA_DECODE_SHARED_KV = 1
 PA_JOB_SHARED = 1 << 16
+PA_SWAP_OUT = 0
+PA_SWAP_IN = 1
+PA_SWAP_ENGINE_KERNEL = 0
+PA_SWAP_ENGINE_DMA = 1
 
 
 class PaError(RuntimeError):
@@ -38,7 +42,10 @@ class PaBmStats(ctypes.Structure):
                 ("used_blocks", ctypes.c_int32), ("num_seqs", ctypes.c_int32),
                 ("logical_tokens", ctypes.c_int64), ("shared_blocks", ctypes.c_int32),
                 ("pad_", ctypes.c_int32), ("alloc_failures", ctypes.c_int64),
-                ("cow_copies", ctypes.c_int64)]
+                ("cow_copies", ctypes.c_int64), ("host_blocks", ctypes.c_int32),
+                ("free_host_blocks", ctypes.c_int32), ("swapped_seqs", ctypes.c_int32),
+                ("pad2_", ctypes.c_int32), ("swap_out_blocks", ctypes.c_int64),
+                ("swap_in_blocks", ctypes.c_int64)]
 
 
 def _load() -> ctypes.CDLL:
@@ -67,6 +74,7 @@ SIGNATURES = {
     "pa_last_error": (ctypes.c_char_p, []),
     "pa_reshape_and_cache": (_i32, [_pool, _vp, _vp, _vp, _i32, _vp]),
     "pa_copy_blocks": (_i32, [_pool, _vp, _i32, _vp]),
+    "pa_swap_blocks": (_i32, [_pool, _pool, _p32, _i32, _i32, _i32, _vp]),
     "pa_decode_default_workgroups": (_i32, []),
     "pa_decode_plan": (_i32, [_p32, _i32, _i32, _i32, _i32, _vp, _sz, ctypes.POINTER(PaDecodePlanInfo)]),
     "pa_decode_plan_schedule": (_i32, [_p32, _i32, _i32, _i32, _i32, _i32, _vp, _sz, ctypes.POINTER(PaDecodePlanInfo)]),
@@ -85,6 +93,11 @@ SIGNATURES = {
     "pa_bm_table": (_i32, [_vp, _i64, _p32, _i32]),
     "pa_bm_export": (_i32, [_vp, _p64, _i32, _i32, _p32, _p32]),
     "pa_bm_prefix_groups": (_i32, [_vp, _p64, _i32, _p32, _p32]),
+    "pa_bm_set_host_blocks": (_i32, [_vp, _i32]),
+    "pa_bm_swap_out": (_i32, [_vp, _p64, _i32, _p32, _i32, _p32]),
+    "pa_bm_swap_in": (_i32, [_vp, _p64, _i32, _p32, _i32, _p32]),
+    "pa_bm_swapped": (_i32, [_vp, _i64]),
+    "pa_bm_host_refcount": (_i32, [_vp, _i32]),
     "pa_bm_len": (_i32, [_vp, _i64]),
     "pa_bm_refcount": (_i32, [_vp, _i32]),
     "pa_bm_get_stats": (None, [_vp, ctypes.POINTER(PaBmStats)]),

@@ -107,6 +107,127 @@ extern "C" pa_status pa_copy_blocks(const pa_kv_pool* pool, const int32_t* pairs
                              "pa_copy_blocks");
 }
 
+namespace pagedkv {
+namespace {
+
+// The device address of [p, p + bytes) when that whole range is pinned host
+// memory mapped into the device's address space; fails otherwise.  A failed
+// query leaves an error in the runtime's last-error slot: it is cleared here so
+// that the next launch check does not report it.
+pa_status mapped_host_range(void* p, int64_t bytes, void** dev, const char* who, const char* name) {
+  char* last = static_cast<char*>(p) + bytes - 1;
+  hipPointerAttribute_t a0{}, a1{};
+  void* d0 = nullptr;
+  void* d1 = nullptr;
+  const bool ok = hipPointerGetAttributes(&a0, p) == hipSuccess && a0.type == hipMemoryTypeHost &&
+                  hipPointerGetAttributes(&a1, last) == hipSuccess && a1.type == hipMemoryTypeHost &&
+                  hipHostGetDevicePointer(&d0, p, 0) == hipSuccess &&
+                  hipHostGetDevicePointer(&d1, last, 0) == hipSuccess && d0 &&
+                  static_cast<char*>(d1) - static_cast<char*>(d0) == bytes - 1;
+  if (!ok) {
+    (void)hipGetLastError();
+    return fail(PA_ERR_INVALID,
+                "%s: host_pool %s is not pinned, device-mapped host memory over all %lld bytes "
+                "(allocate it with hipHostMalloc or pin_memory=True)",
+                who, name, (long long)bytes);
+  }
+  *dev = d0;
+  return PA_OK;
+}
+
+pa_status device_memory(const void* p, const char* who, const char* name) {
+  hipPointerAttribute_t a{};
+  if (hipPointerGetAttributes(&a, p) != hipSuccess || a.type != hipMemoryTypeDevice) {
+    (void)hipGetLastError();
+    return fail(PA_ERR_INVALID, "%s: device_pool %s is not device memory", who, name);
+  }
+  return PA_OK;
+}
+
+}  // namespace
+}  // namespace pagedkv
+
+extern "C" pa_status pa_swap_blocks(const pa_kv_pool* device_pool, const pa_kv_pool* host_pool,
+                                    const int32_t* pairs, int32_t num_pairs, int32_t direction,
+                                    int32_t engine, void* stream) {
+  using namespace pagedkv;
+  const char* who = "pa_swap_blocks";
+  if (pa_status st = check_pool(device_pool, who)) return st;
+  if (!host_pool || !host_pool->k || !host_pool->v) return fail(PA_ERR_INVALID, "%s: host_pool or its k/v is NULL", who);
+  if (host_pool->num_blocks <= 0 || host_pool->block_size != device_pool->block_size ||
+      host_pool->num_kv_heads != device_pool->num_kv_heads || host_pool->head_dim != device_pool->head_dim ||
+      host_pool->dtype != device_pool->dtype)
+    return fail(PA_ERR_INVALID, "%s: host_pool must have num_blocks > 0 and the device pool's block shape and dtype",
+                who);
+  if (!aligned(host_pool->k, 16) || !aligned(host_pool->v, 16))
+    return fail(PA_ERR_INVALID, "%s: host_pool pointers must be 16-byte aligned", who);
+  if (direction != PA_SWAP_OUT && direction != PA_SWAP_IN)
+    return fail(PA_ERR_INVALID, "%s: direction %d (PA_SWAP_OUT=0, PA_SWAP_IN=1)", who, direction);
+  if (engine != PA_SWAP_ENGINE_KERNEL && engine != PA_SWAP_ENGINE_DMA)
+    return fail(PA_ERR_INVALID, "%s: engine %d (PA_SWAP_ENGINE_KERNEL=0, PA_SWAP_ENGINE_DMA=1)", who, engine);
+  if (num_pairs < 0) return fail(PA_ERR_INVALID, "%s: num_pairs %d < 0", who, num_pairs);
+  if (num_pairs == 0) return PA_OK;
+  if (!pairs) return fail(PA_ERR_INVALID, "%s: pairs is NULL", who);
+
+  const bool out = direction == PA_SWAP_OUT;
+  const int32_t n_src = out ? device_pool->num_blocks : host_pool->num_blocks;
+  const int32_t n_dst = out ? host_pool->num_blocks : device_pool->num_blocks;
+  std::vector<char> seen(n_dst, 0);
+  for (int32_t i = 0; i < num_pairs; ++i) {
+    const int32_t s = pairs[2 * i], d = pairs[2 * i + 1];
+    if (s < 0 || s >= n_src || d < 0 || d >= n_dst)
+      return fail(PA_ERR_INVALID, "%s: pair %d = (%d, %d) outside the pools (%d source, %d destination blocks)", who,
+                  i, s, d, n_src, n_dst);
+    if (seen[d]) return fail(PA_ERR_INVALID, "%s: destination block %d appears twice", who, d);
+    seen[d] = 1;
+  }
+
+  const int64_t block_bytes = pool_block_bytes(*device_pool);
+  const int64_t host_bytes = block_bytes * host_pool->num_blocks;
+  void *hk = nullptr, *hv = nullptr;
+  if (pa_status st = mapped_host_range(host_pool->k, host_bytes, &hk, who, "k")) return st;
+  if (pa_status st = mapped_host_range(host_pool->v, host_bytes, &hv, who, "v")) return st;
+  if (pa_status st = device_memory(device_pool->k, who, "k")) return st;
+  if (pa_status st = device_memory(device_pool->v, who, "v")) return st;
+
+  const hipStream_t hs = (hipStream_t)stream;
+  if (engine == PA_SWAP_ENGINE_KERNEL) {
+    const void* sk = out ? device_pool->k : hk;
+    const void* sv = out ? device_pool->v : hv;
+    void* dk = out ? hk : device_pool->k;
+    void* dv = out ? hv : device_pool->v;
+    SwapBatch batch;
+    for (int32_t i0 = 0; i0 < num_pairs; i0 += kSwapPairsPerLaunch) {
+      const int32_t n = std::min(kSwapPairsPerLaunch, num_pairs - i0);
+      for (int32_t i = 0; i < n; ++i) {
+        batch.src[i] = pairs[2 * (i0 + i)];
+        batch.dst[i] = pairs[2 * (i0 + i) + 1];
+      }
+      if (pa_status st = hip_status(launch_swap_blocks(sk, sv, dk, dv, block_bytes, batch, n, out, hs), who))
+        return st;
+    }
+    return PA_OK;
+  }
+  // DMA engine: one copy per pool for every run of pairs that continue each
+  // other on both sides (src + 1, dst + 1).
+  char* src_k = static_cast<char*>(out ? device_pool->k : host_pool->k);
+  char* src_v = static_cast<char*>(out ? device_pool->v : host_pool->v);
+  char* dst_k = static_cast<char*>(out ? host_pool->k : device_pool->k);
+  char* dst_v = static_cast<char*>(out ? host_pool->v : device_pool->v);
+  const hipMemcpyKind kind = out ? hipMemcpyDeviceToHost : hipMemcpyHostToDevice;
+  for (int32_t i = 0; i < num_pairs;) {
+    int32_t j = i + 1;
+    while (j < num_pairs && pairs[2 * j] == pairs[2 * (j - 1)] + 1 && pairs[2 * j + 1] == pairs[2 * (j - 1) + 1] + 1)
+      ++j;
+    const int64_t so = pairs[2 * i] * block_bytes, dof = pairs[2 * i + 1] * block_bytes;
+    const size_t bytes = (size_t)((j - i) * block_bytes);
+    if (pa_status st = hip_status(hipMemcpyAsync(dst_k + dof, src_k + so, bytes, kind, hs), who)) return st;
+    if (pa_status st = hip_status(hipMemcpyAsync(dst_v + dof, src_v + so, bytes, kind, hs), who)) return st;
+    i = j;
+  }
+  return PA_OK;
+}
+
 extern "C" int32_t pa_decode_default_workgroups(void) {
   int dev = 0, cus = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess ||

@@ -14,8 +14,15 @@
 //    only blocks reaching zero; the first write into a shared, partly filled
 //    block copies it (mercemay.com "Sharing blocks between sequences";
 //    aicassindra.com "tm_paged_attention_deep", "Copy-on-write for shared
-//    prefixes").
-// Appends are all-or-nothing: a request that does not fit changes nothing.
+//    prefixes");
+//  - when blocks run out, a sequence's blocks can be copied to host memory
+//    and back instead of recomputing it (mercemay.com, "Three ways contiguous
+//    reservation loses memory"; S06, third exercise).  Host memory is a
+//    second pool of blocks with its own free list and counts under the same
+//    discipline; the distinct blocks of the listed tables move once each, so
+//    sharing survives the round trip.
+// Appends and swaps are all-or-nothing: a request that does not fit changes
+// nothing.
 #include <algorithm>
 #include <cstring>
 #include <map>
@@ -29,21 +36,41 @@ using pagedkv::fail;
 
 struct pa_bm {
   struct Seq {
-    std::vector<int32_t> table;
+    std::vector<int32_t> table;     // host-pool blocks while swapped
     int32_t len = 0;
+    bool swapped = false;
+  };
+  // One pool of blocks: free list and counts.
+  struct Pool {
+    std::vector<int32_t> free_stack;  // back() is handed out next
+    std::vector<int32_t> refcount;
+    void reset(int32_t n) {
+      refcount.assign(n, 0);
+      free_stack.resize(n);
+      for (int32_t i = 0; i < n; ++i) free_stack[n - 1 - i] = i;
+    }
+    // Drop one count of every block of `table`; blocks reaching zero go back
+    // on the list in table order.
+    void release(const std::vector<int32_t>& table) {
+      for (int32_t b : table)
+        if (--refcount[b] == 0) free_stack.push_back(b);
+    }
   };
   int32_t num_blocks = 0;
   int32_t block_size = 0;
-  std::vector<int32_t> free_stack;  // back() is handed out next
-  std::vector<int32_t> refcount;
+  Pool dev;
+  Pool host;
   std::map<int64_t, Seq> seqs;      // ordered: deterministic checks and stats
   int64_t alloc_failures = 0;
   int64_t cow_copies = 0;
+  int64_t swap_out_blocks = 0;
+  int64_t swap_in_blocks = 0;
+  int32_t num_swapped = 0;
 
   int32_t pop() {
-    int32_t b = free_stack.back();
-    free_stack.pop_back();
-    refcount[b] = 1;
+    int32_t b = dev.free_stack.back();
+    dev.free_stack.pop_back();
+    dev.refcount[b] = 1;
     return b;
   }
 
@@ -58,7 +85,7 @@ struct pa_bm {
       const int32_t last = s->table.back();
       auto it = delta.find(last);
       const int32_t d = it == delta.end() ? 0 : it->second;
-      if (refcount[last] + d > 1) {
+      if (dev.refcount[last] + d > 1) {
         need += 1;
         delta[last] = d - 1;
       }
@@ -70,10 +97,10 @@ struct pa_bm {
   void append_unchecked(int64_t id, int32_t n_new, int64_t* slots, int32_t* cow, int32_t* n_cow) {
     Seq& s = seqs[id];
     const int32_t B = block_size;
-    if (n_new > 0 && s.len % B != 0 && refcount[s.table.back()] > 1) {
+    if (n_new > 0 && s.len % B != 0 && dev.refcount[s.table.back()] > 1) {
       const int32_t src = s.table.back();
       const int32_t dst = pop();
-      refcount[src] -= 1;
+      dev.refcount[src] -= 1;
       s.table.back() = dst;
       cow[2 * *n_cow] = src;
       cow[2 * *n_cow + 1] = dst;
@@ -102,8 +129,8 @@ extern "C" pa_bm* pa_bm_create(int32_t num_blocks, int32_t block_size, const int
   }
   bm->num_blocks = num_blocks;
   bm->block_size = block_size;
-  bm->refcount.assign(num_blocks, 0);
-  bm->free_stack.resize(num_blocks);
+  bm->dev.refcount.assign(num_blocks, 0);
+  bm->dev.free_stack.resize(num_blocks);
   if (initial_order) {
     std::vector<char> seen(num_blocks, 0);
     for (int32_t i = 0; i < num_blocks; ++i) {
@@ -114,10 +141,10 @@ extern "C" pa_bm* pa_bm_create(int32_t num_blocks, int32_t block_size, const int
         return nullptr;
       }
       seen[b] = 1;
-      bm->free_stack[num_blocks - 1 - i] = b;
+      bm->dev.free_stack[num_blocks - 1 - i] = b;
     }
   } else {
-    for (int32_t i = 0; i < num_blocks; ++i) bm->free_stack[num_blocks - 1 - i] = i;
+    for (int32_t i = 0; i < num_blocks; ++i) bm->dev.free_stack[num_blocks - 1 - i] = i;
   }
   return bm;
 }
@@ -131,14 +158,15 @@ extern "C" pa_status pa_bm_append(pa_bm* bm, int64_t seq, int32_t n_new, int64_t
   *n_cow_out = 0;
   auto it = bm->seqs.find(seq);
   const pa_bm::Seq* s = it == bm->seqs.end() ? nullptr : &it->second;
+  if (s && s->swapped) return fail(PA_ERR_INVALID, "pa_bm_append: sequence %lld is swapped out", (long long)seq);
   std::unordered_map<int32_t, int32_t> delta;
   const int64_t need = bm->needs(s, n_new, delta);
   if (!delta.empty() && !cow_pairs_out)
     return fail(PA_ERR_INVALID, "pa_bm_append: a copy-on-write pair is due but cow_pairs_out is NULL");
-  if (need > (int64_t)bm->free_stack.size()) {
+  if (need > (int64_t)bm->dev.free_stack.size()) {
     bm->alloc_failures += 1;
     return fail(PA_ERR_OOM, "pa_bm_append: sequence %lld needs %lld blocks, %zu free", (long long)seq,
-                (long long)need, bm->free_stack.size());
+                (long long)need, bm->dev.free_stack.size());
   }
   int32_t dummy[2];
   bm->append_unchecked(seq, n_new, slots_out, cow_pairs_out ? cow_pairs_out : dummy, n_cow_out);
@@ -158,12 +186,17 @@ extern "C" pa_status pa_bm_append_step(pa_bm* bm, const int64_t* seqs, int32_t n
   int64_t need = 0;
   for (int32_t i = 0; i < num; ++i) {
     auto it = bm->seqs.find(seqs[i]);
+    if (it != bm->seqs.end() && it->second.swapped)
+      return fail(PA_ERR_INVALID, "pa_bm_append_step: sequence %lld is swapped out", (long long)seqs[i]);
+  }
+  for (int32_t i = 0; i < num; ++i) {
+    auto it = bm->seqs.find(seqs[i]);
     need += bm->needs(it == bm->seqs.end() ? nullptr : &it->second, 1, delta);
   }
-  if (need > (int64_t)bm->free_stack.size()) {
+  if (need > (int64_t)bm->dev.free_stack.size()) {
     bm->alloc_failures += 1;
     return fail(PA_ERR_OOM, "pa_bm_append_step: step needs %lld blocks, %zu free", (long long)need,
-                bm->free_stack.size());
+                bm->dev.free_stack.size());
   }
   for (int32_t i = 0; i < num; ++i)
     bm->append_unchecked(seqs[i], 1, slots_out + i, cow_pairs_out, n_cow_out);
@@ -174,9 +207,10 @@ extern "C" pa_status pa_bm_fork(pa_bm* bm, int64_t parent, int64_t child) {
   if (!bm) return fail(PA_ERR_INVALID, "pa_bm_fork: null manager");
   auto p = bm->seqs.find(parent);
   if (p == bm->seqs.end()) return fail(PA_ERR_NOT_FOUND, "pa_bm_fork: unknown parent %lld", (long long)parent);
+  if (p->second.swapped) return fail(PA_ERR_INVALID, "pa_bm_fork: parent %lld is swapped out", (long long)parent);
   if (bm->seqs.count(child)) return fail(PA_ERR_INVALID, "pa_bm_fork: child %lld exists", (long long)child);
   pa_bm::Seq copy = p->second;
-  for (int32_t b : copy.table) bm->refcount[b] += 1;
+  for (int32_t b : copy.table) bm->dev.refcount[b] += 1;
   bm->seqs.emplace(child, std::move(copy));
   return PA_OK;
 }
@@ -185,8 +219,11 @@ extern "C" pa_status pa_bm_free(pa_bm* bm, int64_t seq) {
   if (!bm) return fail(PA_ERR_INVALID, "pa_bm_free: null manager");
   auto it = bm->seqs.find(seq);
   if (it == bm->seqs.end()) return PA_OK;
-  for (int32_t b : it->second.table) {
-    if (--bm->refcount[b] == 0) bm->free_stack.push_back(b);
+  if (it->second.swapped) {
+    bm->host.release(it->second.table);
+    bm->num_swapped -= 1;
+  } else {
+    bm->dev.release(it->second.table);
   }
   bm->seqs.erase(it);
   return PA_OK;
@@ -210,6 +247,8 @@ extern "C" pa_status pa_bm_export(const pa_bm* bm, const int64_t* seqs, int32_t 
     auto it = bm->seqs.find(seqs[i]);
     if (it == bm->seqs.end())
       return fail(PA_ERR_NOT_FOUND, "pa_bm_export: unknown sequence %lld", (long long)seqs[i]);
+    if (it->second.swapped)
+      return fail(PA_ERR_INVALID, "pa_bm_export: sequence %lld is swapped out", (long long)seqs[i]);
     const auto& t = it->second.table;
     if ((int64_t)t.size() > max_blocks)
       return fail(PA_ERR_INVALID, "pa_bm_export: sequence %lld has %zu blocks > max_blocks %d",
@@ -234,6 +273,8 @@ extern "C" pa_status pa_bm_prefix_groups(const pa_bm* bm, const int64_t* seqs, i
     auto it = bm->seqs.find(seqs[i]);
     if (it == bm->seqs.end())
       return fail(PA_ERR_NOT_FOUND, "pa_bm_prefix_groups: unknown sequence %lld", (long long)seqs[i]);
+    if (it->second.swapped)
+      return fail(PA_ERR_INVALID, "pa_bm_prefix_groups: sequence %lld is swapped out", (long long)seqs[i]);
     batch[i] = &it->second;
   }
   // Group by first physical block: the batch position of the first sequence
@@ -280,49 +321,164 @@ extern "C" int32_t pa_bm_len(const pa_bm* bm, int64_t seq) {
 
 extern "C" int32_t pa_bm_refcount(const pa_bm* bm, int32_t block) {
   if (!bm || block < 0 || block >= bm->num_blocks) return -1;
-  return bm->refcount[block];
+  return bm->dev.refcount[block];
 }
 
 extern "C" void pa_bm_get_stats(const pa_bm* bm, pa_bm_stats* out) {
   if (!bm || !out) return;
   std::memset(out, 0, sizeof(*out));
   out->num_blocks = bm->num_blocks;
-  out->free_blocks = (int32_t)bm->free_stack.size();
+  out->free_blocks = (int32_t)bm->dev.free_stack.size();
   out->used_blocks = bm->num_blocks - out->free_blocks;
   out->num_seqs = (int32_t)bm->seqs.size();
   for (const auto& kv : bm->seqs) out->logical_tokens += kv.second.len;
-  for (int32_t c : bm->refcount) out->shared_blocks += c > 1;
+  for (int32_t c : bm->dev.refcount) out->shared_blocks += c > 1;
   out->alloc_failures = bm->alloc_failures;
   out->cow_copies = bm->cow_copies;
+  out->host_blocks = (int32_t)bm->host.refcount.size();
+  out->free_host_blocks = (int32_t)bm->host.free_stack.size();
+  out->swapped_seqs = bm->num_swapped;
+  out->swap_out_blocks = bm->swap_out_blocks;
+  out->swap_in_blocks = bm->swap_in_blocks;
+}
+
+namespace {
+
+// Counts of one pool against the tables of the sequences in `swapped` state.
+pa_status check_pool(const pa_bm* bm, const pa_bm::Pool& pool, bool swapped, const char* what) {
+  const int32_t n = (int32_t)pool.refcount.size();
+  std::vector<int32_t> named(n, 0);
+  for (const auto& kv : bm->seqs) {
+    const auto& s = kv.second;
+    if (s.swapped != swapped) continue;
+    const int64_t expect = ((int64_t)s.len + bm->block_size - 1) / bm->block_size;
+    if ((int64_t)s.table.size() != expect)
+      return fail(PA_ERR_INVALID, "pa_bm_check: sequence %lld length %d has %zu %s blocks, expected %lld",
+                  (long long)kv.first, s.len, s.table.size(), what, (long long)expect);
+    for (int32_t b : s.table) {
+      if (b < 0 || b >= n)
+        return fail(PA_ERR_INVALID, "pa_bm_check: sequence %lld names %s block %d", (long long)kv.first, what, b);
+      named[b] += 1;
+    }
+  }
+  std::vector<char> is_free(n, 0);
+  for (int32_t b : pool.free_stack) {
+    if (b < 0 || b >= n || is_free[b])
+      return fail(PA_ERR_INVALID, "pa_bm_check: %s block %d is on the free list twice or out of range", what, b);
+    is_free[b] = 1;
+  }
+  for (int32_t b = 0; b < n; ++b) {
+    if (named[b] != pool.refcount[b])
+      return fail(PA_ERR_INVALID, "pa_bm_check: %s block %d count %d but %d tables name it", what, b,
+                  pool.refcount[b], named[b]);
+    if ((named[b] == 0) != (is_free[b] != 0))
+      return fail(PA_ERR_INVALID, "pa_bm_check: %s block %d is %s", what, b,
+                  named[b] ? "named and free" : "neither named nor free (leaked)");
+  }
+  return PA_OK;
+}
+
+// Copy the distinct blocks of the listed tables from pool `src` to pool
+// `dst` (one destination block each, in batch and table order), point the
+// tables at the copies and retire the source tables.  The caller has checked
+// states, distinctness and capacity.
+void move_tables(pa_bm* bm, const std::vector<pa_bm::Seq*>& list, pa_bm::Pool& src, pa_bm::Pool& dst,
+                 bool to_host, int32_t* pairs) {
+  std::unordered_map<int32_t, int32_t> mapping;
+  int32_t n = 0;
+  std::vector<std::vector<int32_t>> old(list.size());
+  for (size_t i = 0; i < list.size(); ++i) {
+    pa_bm::Seq* s = list[i];
+    old[i] = s->table;
+    for (int32_t& b : s->table) {
+      auto ins = mapping.emplace(b, -1);
+      if (ins.second) {
+        const int32_t d = dst.free_stack.back();
+        dst.free_stack.pop_back();
+        ins.first->second = d;
+        pairs[2 * n] = b;
+        pairs[2 * n + 1] = d;
+        ++n;
+      }
+      b = ins.first->second;
+      dst.refcount[b] += 1;
+    }
+    s->swapped = to_host;
+  }
+  for (const auto& t : old) src.release(t);
+  bm->num_swapped += to_host ? (int32_t)list.size() : -(int32_t)list.size();
+}
+
+pa_status swap(pa_bm* bm, const int64_t* seqs, int32_t num, int32_t* pairs_out, int32_t cap_pairs,
+               int32_t* n_pairs_out, bool to_host, const char* who) {
+  if (!bm || num < 0 || (num > 0 && !seqs) || !n_pairs_out || cap_pairs < 0 || (cap_pairs > 0 && !pairs_out))
+    return fail(PA_ERR_INVALID, "%s: bad arguments", who);
+  *n_pairs_out = 0;
+  std::vector<int64_t> sorted(seqs, seqs + num);
+  std::sort(sorted.begin(), sorted.end());
+  if (std::adjacent_find(sorted.begin(), sorted.end()) != sorted.end())
+    return fail(PA_ERR_INVALID, "%s: a sequence is listed twice", who);
+  std::vector<pa_bm::Seq*> list(num);
+  std::unordered_map<int32_t, char> distinct;
+  for (int32_t i = 0; i < num; ++i) {
+    auto it = bm->seqs.find(seqs[i]);
+    if (it == bm->seqs.end()) return fail(PA_ERR_NOT_FOUND, "%s: unknown sequence %lld", who, (long long)seqs[i]);
+    if (it->second.swapped == to_host)
+      return fail(PA_ERR_INVALID, "%s: sequence %lld is %s", who, (long long)seqs[i],
+                  to_host ? "already swapped out" : "not swapped out");
+    list[i] = &it->second;
+    for (int32_t b : it->second.table) distinct.emplace(b, 0);
+  }
+  pa_bm::Pool& src = to_host ? bm->dev : bm->host;
+  pa_bm::Pool& dst = to_host ? bm->host : bm->dev;
+  const int64_t need = (int64_t)distinct.size();
+  if (need > (int64_t)dst.free_stack.size())
+    return fail(PA_ERR_OOM, "%s: %lld blocks to copy, %zu free %s blocks", who, (long long)need,
+                dst.free_stack.size(), to_host ? "host" : "device");
+  if (need > cap_pairs)
+    return fail(PA_ERR_INVALID, "%s: %lld pairs due, cap_pairs is %d", who, (long long)need, cap_pairs);
+  move_tables(bm, list, src, dst, to_host, pairs_out);
+  *n_pairs_out = (int32_t)need;
+  (to_host ? bm->swap_out_blocks : bm->swap_in_blocks) += need;
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" pa_status pa_bm_set_host_blocks(pa_bm* bm, int32_t num_host_blocks) {
+  if (!bm || num_host_blocks < 0) return fail(PA_ERR_INVALID, "pa_bm_set_host_blocks: bad arguments");
+  if (bm->num_swapped) return fail(PA_ERR_INVALID, "pa_bm_set_host_blocks: %d sequences are swapped out", bm->num_swapped);
+  bm->host.reset(num_host_blocks);
+  return PA_OK;
+}
+
+extern "C" pa_status pa_bm_swap_out(pa_bm* bm, const int64_t* seqs, int32_t num, int32_t* pairs_out, int32_t cap_pairs,
+                                    int32_t* n_pairs_out) {
+  return swap(bm, seqs, num, pairs_out, cap_pairs, n_pairs_out, true, "pa_bm_swap_out");
+}
+
+extern "C" pa_status pa_bm_swap_in(pa_bm* bm, const int64_t* seqs, int32_t num, int32_t* pairs_out, int32_t cap_pairs,
+                                   int32_t* n_pairs_out) {
+  return swap(bm, seqs, num, pairs_out, cap_pairs, n_pairs_out, false, "pa_bm_swap_in");
+}
+
+extern "C" int32_t pa_bm_swapped(const pa_bm* bm, int64_t seq) {
+  if (!bm) return -1;
+  auto it = bm->seqs.find(seq);
+  return it == bm->seqs.end() ? -1 : (it->second.swapped ? 1 : 0);
+}
+
+extern "C" int32_t pa_bm_host_refcount(const pa_bm* bm, int32_t host_block) {
+  if (!bm || host_block < 0 || host_block >= (int32_t)bm->host.refcount.size()) return -1;
+  return bm->host.refcount[host_block];
 }
 
 extern "C" pa_status pa_bm_check(const pa_bm* bm) {
   if (!bm) return fail(PA_ERR_INVALID, "pa_bm_check: null manager");
-  std::vector<int32_t> named(bm->num_blocks, 0);
-  for (const auto& kv : bm->seqs) {
-    const auto& s = kv.second;
-    const int64_t expect = ((int64_t)s.len + bm->block_size - 1) / bm->block_size;
-    if ((int64_t)s.table.size() != expect)
-      return fail(PA_ERR_INVALID, "pa_bm_check: sequence %lld length %d has %zu blocks, expected %lld",
-                  (long long)kv.first, s.len, s.table.size(), (long long)expect);
-    for (int32_t b : s.table) {
-      if (b < 0 || b >= bm->num_blocks)
-        return fail(PA_ERR_INVALID, "pa_bm_check: sequence %lld names block %d", (long long)kv.first, b);
-      named[b] += 1;
-    }
-  }
-  std::vector<char> is_free(bm->num_blocks, 0);
-  for (int32_t b : bm->free_stack) {
-    if (is_free[b]) return fail(PA_ERR_INVALID, "pa_bm_check: block %d is on the free list twice", b);
-    is_free[b] = 1;
-  }
-  for (int32_t b = 0; b < bm->num_blocks; ++b) {
-    if (named[b] != bm->refcount[b])
-      return fail(PA_ERR_INVALID, "pa_bm_check: block %d count %d but %d tables name it", b,
-                  bm->refcount[b], named[b]);
-    if ((named[b] == 0) != (is_free[b] != 0))
-      return fail(PA_ERR_INVALID, "pa_bm_check: block %d is %s", b,
-                  named[b] ? "named and free" : "neither named nor free (leaked)");
-  }
-  return PA_OK;
+  int32_t swapped = 0;
+  for (const auto& kv : bm->seqs) swapped += kv.second.swapped;
+  if (swapped != bm->num_swapped)
+    return fail(PA_ERR_INVALID, "pa_bm_check: %d swapped sequences, counter says %d", swapped, bm->num_swapped);
+  if (pa_status st = check_pool(bm, bm->dev, false, "device")) return st;
+  return check_pool(bm, bm->host, true, "host");
 }

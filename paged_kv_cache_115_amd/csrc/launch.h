@@ -56,4 +56,21 @@ hipError_t launch_reshape_and_cache(const pa_kv_pool& pool, const void* key, con
 hipError_t launch_copy_blocks(const pa_kv_pool& pool, const int32_t* pairs, int32_t num_pairs,
                               hipStream_t stream);
 
+// Bytes of one block of one pool (B * num_kv_heads * head_dim elements).
+int64_t pool_block_bytes(const pa_kv_pool& pool);
+
+// Pair lists of one swap launch, passed by value in the kernel arguments.
+constexpr int kSwapPairsPerLaunch = 240;
+struct SwapBatch {
+  int32_t src[kSwapPairsPerLaunch];
+  int32_t dst[kSwapPairsPerLaunch];
+};
+
+// One swap launch over batch.src/dst[0, num_pairs): src/dst pointers are
+// device addresses (a host pool's mapped address on its side).  out: the
+// source is the device pool.
+hipError_t launch_swap_blocks(const void* src_k, const void* src_v, void* dst_k, void* dst_v,
+                              int64_t block_bytes, const SwapBatch& batch, int32_t num_pairs, bool out,
+                              hipStream_t stream);
+
 }  // namespace pagedkv

@@ -201,6 +201,48 @@ def prefix_case(name: str, block_size: int, seed: int | None = None) -> dict:
                 scale=default_scale(d), num_blocks=nb)
 
 
+# Preemption: a pool too small for the batch's growth, so that decode steps run
+# the allocator dry and sequences are swapped to host memory and back
+# (mercemay.com "Paged KV Cache Allocation and the Block Table", "Three ways
+# contiguous reservation loses memory"; llminference.xinbetween.com S06, third
+# exercise).  Prompt lengths follow the c3 mix, capped low; one prompt is
+# sampled three times (fork) so that shared blocks are swapped too.
+PREEMPT_CONFIGS: dict[str, dict] = {
+    "p1s": dict(seed=21, num_seqs=8, samples=3, prompt=(20, 200), steps=64, block_size=16,
+                num_q_heads=32, num_kv_heads=8, head_dim=128, dtype="bf16",
+                pool_slack=1.15, host_blocks=96, retire_at=(24, 40), group_out_at=10),
+    "p1f": dict(seed=22, num_seqs=6, samples=2, prompt=(10, 90), steps=48, block_size=8,
+                num_q_heads=8, num_kv_heads=4, head_dim=64, dtype="f32",
+                pool_slack=1.10, host_blocks=80, retire_at=(20, 30), group_out_at=16),
+}
+
+
+def preempt_case(name: str, seed: int | None = None) -> dict:
+    """Inputs of a decode run that outgrows its pool.
+
+    Keys: cfg, prompts[S] (prompt tokens per sequence), free_order[NB],
+    rows_k/rows_v [R, Hkv, D] (token rows in the order they are appended,
+    whichever sequence appends them; R bounds every run), q[S + samples - 1,
+    Hq, D] (one query per sequence that can be alive at the end), scale,
+    num_blocks, host_blocks."""
+    cfg = dict(PREEMPT_CONFIGS[name])
+    rng = np.random.default_rng(cfg["seed"] if seed is None else seed)
+    lo, hi = cfg["prompt"]
+    s, b = cfg["num_seqs"], cfg["block_size"]
+    prompts = rng.integers(lo, hi + 1, size=s).astype(np.int32)
+    nb = int(cfg["pool_slack"] * sum(-(-int(p) // b) for p in prompts)) + 1
+    free_order = rng.permutation(nb).astype(np.int32)
+    hkv, d, dt = cfg["num_kv_heads"], cfg["head_dim"], cfg["dtype"]
+    alive = s + cfg["samples"] - 1
+    rows = int(prompts.sum()) + cfg["steps"] * alive
+    rows_k = _normal(rng, (rows, hkv, d), dt)
+    rows_v = _normal(rng, (rows, hkv, d), dt)
+    q = _normal(rng, (alive, cfg["num_q_heads"], d), dt)
+    return dict(cfg=cfg, name=name, prompts=prompts, free_order=free_order, rows_k=rows_k,
+                rows_v=rows_v, q=q, scale=default_scale(d), num_blocks=nb,
+                host_blocks=cfg["host_blocks"])
+
+
 def byte_pattern(shape, dtype: str, seed: int) -> np.ndarray:
     """Seeded arbitrary bit patterns (any bits, NaNs included) for copy tests."""
     rng = np.random.default_rng(seed)

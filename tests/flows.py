@@ -279,3 +279,209 @@ def oracle_prefix(case: dict, seqs=None):
     out = oracle.decode_attention(case["q"], kpool, vpool, tables, lens, case["scale"], seqs=seqs)
     return dict(out=out, tables=tables, cows=np.array(cows, dtype=np.int32).reshape(-1, 2), stats=bm.stats(),
                 kpool=kpool, vpool=vpool)
+
+
+# ------------------------------------------------------------- preemption
+class _OracleSide:
+    """Python block-manager model, numpy pools and byte copies."""
+
+    def __init__(self, case):
+        cfg = case["cfg"]
+        self.b, dt = cfg["block_size"], cfg["dtype"]
+        shape = (case["num_blocks"], self.b, cfg["num_kv_heads"], cfg["head_dim"])
+        hshape = (case["host_blocks"],) + shape[1:]
+        self.bm = oracle.BlockManagerModel(case["num_blocks"], self.b, case["free_order"])
+        self.bm.set_host_blocks(case["host_blocks"])
+        self.k, self.v = synth.nan_fill(shape, dt), synth.nan_fill(shape, dt)
+        self.hk, self.hv = synth.nan_fill(hshape, dt), synth.nan_fill(hshape, dt)
+
+    def append(self, seqs, n=1):
+        """n tokens for one sequence (n given) or one token for each of seqs."""
+        try:
+            slots, cows = self.bm.append(seqs[0], n) if len(seqs) == 1 and n != 1 else self.bm.append_step(seqs)
+        except oracle.OutOfBlocks:
+            return None
+        if cows:
+            oracle.copy_blocks(self.k, self.v, np.array(cows))
+        return np.array(slots, dtype=np.int64)
+
+    def write(self, slots, rk, rv):
+        oracle.reshape_and_cache(self.k, self.v, rk, rv, slots)
+
+    def swap(self, seqs, out):
+        try:
+            pairs = self.bm.swap_out(seqs) if out else self.bm.swap_in(seqs)
+        except oracle.OutOfBlocks:
+            return None
+        if out:
+            oracle.swap_blocks(self.k, self.v, self.hk, self.hv, np.array(pairs))
+        else:
+            oracle.swap_blocks(self.hk, self.hv, self.k, self.v, np.array(pairs))
+        return [tuple(p) for p in pairs]
+
+    def fork(self, p, c):
+        self.bm.fork(p, c)
+
+    def free(self, s):
+        self.bm.free_seq(s)
+
+    def free_blocks(self):
+        return len(self.bm.free)
+
+    def table_len(self, s):
+        return len(self.bm.table(s))
+
+    def decode(self, seqs, q, scale):
+        maxb = max(1, max(self.table_len(s) for s in seqs))
+        tables = np.zeros((len(seqs), maxb), dtype=np.int32)
+        for i, s in enumerate(seqs):
+            t = self.bm.table(s)
+            tables[i, :len(t)] = t
+        lens = np.array([self.bm.length(s) for s in seqs], dtype=np.int32)
+        self.bm.check()
+        return oracle.decode_attention(q, self.k, self.v, tables, lens, scale), tables
+
+
+class _ProductSide:
+    """The library: C++ block manager, device pools, pinned host pools."""
+
+    def __init__(self, pk, case, engine):
+        cfg = case["cfg"]
+        self.pk, self.engine = pk, engine
+        self.b, dt = cfg["block_size"], cfg["dtype"]
+        shape = (case["num_blocks"], self.b, cfg["num_kv_heads"], cfg["head_dim"])
+        hshape = (case["host_blocks"],) + shape[1:]
+        self.bm = pk.BlockManager(case["num_blocks"], self.b, case["free_order"])
+        self.bm.set_host_blocks(case["host_blocks"])
+        self.kd, self.vd = to_dev(synth.nan_fill(shape, dt)), to_dev(synth.nan_fill(shape, dt))
+        self.pool = pk.KvPool(self.kd, self.vd)
+        self.hk, self.hv = to_pinned(synth.nan_fill(hshape, dt)), to_pinned(synth.nan_fill(hshape, dt))
+        self.host = pk.HostKvPool(self.hk, self.hv)
+
+    def append(self, seqs, n=1):
+        try:
+            slots, cows = self.bm.append(seqs[0], n) if len(seqs) == 1 and n != 1 else self.bm.append_step(seqs)
+        except self.pk.PaError as e:
+            assert e.status == -3, e
+            return None
+        if len(cows):
+            self.pk.copy_blocks(self.pool, to_dev(cows))
+        return slots
+
+    def write(self, slots, rk, rv):
+        self.pk.reshape_and_cache(self.pool, to_dev(rk), to_dev(rv), to_dev(slots))
+
+    def swap(self, seqs, out):
+        try:
+            pairs = self.bm.swap_out(seqs) if out else self.bm.swap_in(seqs)
+        except self.pk.PaError as e:
+            assert e.status == -3, e
+            return None
+        self.pk.swap_blocks(self.pool, self.host, pairs, self.pk.PA_SWAP_OUT if out else self.pk.PA_SWAP_IN,
+                            self.engine)
+        return [tuple(p) for p in pairs.tolist()]
+
+    def fork(self, p, c):
+        self.bm.fork(p, c)
+
+    def free(self, s):
+        self.bm.free(s)
+
+    def free_blocks(self):
+        return self.bm.stats()["free_blocks"]
+
+    def table_len(self, s):
+        return len(self.bm.table(s))
+
+    def decode(self, seqs, q, scale):
+        maxb = max(1, max(self.table_len(s) for s in seqs))
+        tables, lens = self.bm.export(seqs, maxb)
+        self.bm.check()
+        out = gpu_decode(self.pk, self.pool, to_dev(q), tables, lens, scale)
+        torch.cuda.synchronize()
+        return to_host(out), tables
+
+
+def to_pinned(a: np.ndarray) -> torch.Tensor:
+    """Host array -> pinned host tensor; uint16 arrays are bfloat16 bit patterns."""
+    t = torch.from_numpy(a.view(np.int16).copy()).view(torch.bfloat16) if a.dtype == np.uint16 \
+        else torch.from_numpy(np.ascontiguousarray(a).copy())
+    return t.pin_memory()
+
+
+def preempt_run(side, case: dict):
+    """A decode run that outgrows its pool, identical on both sides.
+
+    Policy (a scheduler's choice; the pages leave it open): prompts are
+    prefilled in order, then sequence 0 is forked into its samples, which
+    join the end of the running list; each step first swaps the oldest
+    swapped sequence back in if its table plus one block per running
+    sequence fits in the free list, then appends one token to every running
+    sequence; when that does not fit, the most recently admitted running
+    sequence is swapped out alone and the step is retried.  At step
+    `group_out_at` the two most recently admitted running sequences are
+    swapped out together; at the `retire_at` steps the oldest running
+    sequence retires.  At the end all swapped sequences come back in one call
+    (retiring the oldest runners until they fit) and every running sequence
+    is decoded.  Returns (event log, output, tables,
+    running sequence ids)."""
+    cfg = case["cfg"]
+    s_count, samples = cfg["num_seqs"], cfg["samples"]
+    cursor = 0
+
+    def rows(n):
+        nonlocal cursor
+        r = slice(cursor, cursor + n)
+        cursor += n
+        return case["rows_k"][r], case["rows_v"][r]
+
+    log_ = []
+    running, swapped = [], []
+    for s in range(s_count):
+        n = int(case["prompts"][s])
+        slots = side.append([s], n)
+        assert slots is not None, "prompts are sized to fit the pool"
+        side.write(slots, *rows(n))
+        running.append(s)
+    for j in range(1, samples):
+        side.fork(0, s_count + j - 1)
+        running.append(s_count + j - 1)
+    for step in range(cfg["steps"]):
+        if step == cfg["group_out_at"] and len(running) >= 2:
+            group = running[-2:]
+            pairs = side.swap(group, out=True)
+            assert pairs is not None, "host pool is sized to hold every victim"
+            log_.append((step, "out", tuple(group), pairs))
+            del running[-2:]
+            swapped.extend(group)
+        if swapped and side.free_blocks() >= side.table_len(swapped[0]) + len(running) + 1:
+            pairs = side.swap([swapped[0]], out=False)
+            if pairs is not None:
+                log_.append((step, "in", swapped[0], pairs))
+                running.append(swapped.pop(0))
+        while running:
+            slots = side.append(running)
+            if slots is not None:
+                break
+            victim = running.pop()
+            pairs = side.swap([victim], out=True)
+            assert pairs is not None, "host pool is sized to hold every victim"
+            log_.append((step, "out", victim, pairs))
+            swapped.append(victim)
+        if running:
+            side.write(slots, *rows(len(running)))
+        if step in cfg["retire_at"] and running:
+            log_.append((step, "retire", running[0], []))
+            side.free(running.pop(0))
+    while swapped:
+        pairs = side.swap(swapped, out=False)
+        if pairs is None:
+            log_.append(("end", "retire", running[0], []))
+            side.free(running.pop(0))
+            continue
+        log_.append(("end", "in", tuple(swapped), pairs))
+        running.extend(swapped)
+        swapped = []
+    q = case["q"][np.array(running)]
+    out, tables = side.decode(running, q, case["scale"])
+    return log_, out, tables, running

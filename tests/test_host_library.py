@@ -120,6 +120,135 @@ def test_block_manager_matches_model_on_random_operations(seed):
         _compare(bm, model, live)
 
 
+def _compare_swaps(bm: pk.BlockManager, model: oracle.BlockManagerModel, live):
+    _compare(bm, model, live)
+    for s in live:
+        assert bm.is_swapped(s) == model.is_swapped(s)
+    for b in range(model.num_host_blocks):
+        assert bm.host_refcount(b) == model.host_refcount[b]
+    assert bm.host_refcount(model.num_host_blocks) == -1
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_block_manager_swaps_match_model(seed):
+    """Appends, forks, frees and swaps in both directions, operation by
+    operation: same pairs, tables, counts and failures as the model."""
+    rng = np.random.default_rng(100 + seed)
+    b = int(rng.choice([1, 4, 8, 16]))
+    nb = int(rng.integers(8, 60))
+    nh = int(rng.integers(0, 50))
+    order = rng.permutation(nb) if seed % 2 else None
+    bm = pk.BlockManager(nb, b, order)
+    model = oracle.BlockManagerModel(nb, b, order)
+    bm.set_host_blocks(nh)
+    model.set_host_blocks(nh)
+    live, nxt = [], 0
+    for _ in range(250):
+        resident = [s for s in live if not model.is_swapped(s)]
+        swapped = [s for s in live if model.is_swapped(s)]
+        op = int(rng.integers(0, 6))
+        if op == 0 or not live:
+            n = int(rng.integers(0, 3 * b))
+            m_ok = p_ok = True
+            try:
+                ms, mc = model.append(nxt, n)
+            except oracle.OutOfBlocks:
+                m_ok = False
+            try:
+                ps, pc = bm.append(nxt, n)
+            except pk.PaError:
+                p_ok = False
+            assert m_ok == p_ok
+            if m_ok:
+                assert ps.tolist() == ms and [tuple(x) for x in pc.tolist()] == mc
+                live.append(nxt)
+                nxt += 1
+        elif op == 1 and resident:
+            parent = int(rng.choice(resident))
+            model.fork(parent, nxt)
+            bm.fork(parent, nxt)
+            live.append(nxt)
+            nxt += 1
+        elif op in (2, 3) and (resident if op == 2 else swapped):
+            src = resident if op == 2 else swapped
+            k = int(rng.integers(1, len(src) + 1))
+            pick = [int(x) for x in rng.choice(src, size=k, replace=False)]
+            m_fn, p_fn = (model.swap_out, bm.swap_out) if op == 2 else (model.swap_in, bm.swap_in)
+            try:
+                mp = m_fn(pick)
+                m_ok = True
+            except oracle.OutOfBlocks:
+                m_ok = False
+            try:
+                pp = p_fn(pick)
+                p_ok = True
+            except pk.PaError as e:
+                assert e.status == -3
+                p_ok = False
+            assert m_ok == p_ok
+            if m_ok:
+                assert [tuple(x) for x in pp.tolist()] == mp
+        elif op == 4 and resident:
+            s = int(rng.choice(resident))
+            n = int(rng.integers(0, 2 * b))
+            m_ok = p_ok = True
+            try:
+                model.append(s, n)
+            except oracle.OutOfBlocks:
+                m_ok = False
+            try:
+                bm.append(s, n)
+            except pk.PaError:
+                p_ok = False
+            assert m_ok == p_ok
+        elif op == 5:
+            s = int(rng.choice(live))
+            model.free_seq(s)
+            bm.free(s)
+            live.remove(s)
+        bm.check()
+        model.check()
+        _compare_swaps(bm, model, live)
+
+
+def test_block_manager_swap_errors():
+    bm = pk.BlockManager(8, 4)
+    bm.set_host_blocks(2)
+    bm.append(0, 9)
+    with pytest.raises(pk.PaError) as e:
+        bm.swap_out([0])                  # three blocks, two host blocks
+    assert e.value.status == -3 and not bm.is_swapped(0)
+    bm.set_host_blocks(4)
+    with pytest.raises(pk.PaError) as e:
+        bm.swap_out([0, 0])
+    assert e.value.status == -1
+    with pytest.raises(pk.PaError) as e:
+        bm.swap_out([5])
+    assert e.value.status == -4
+    with pytest.raises(pk.PaError) as e:
+        bm.swap_in([0])                   # resident
+    assert e.value.status == -1
+    assert bm.swap_out([0]).tolist() == [[0, 0], [1, 1], [2, 2]]
+    for call in (lambda: bm.append(0, 1), lambda: bm.append_step([0]), lambda: bm.fork(0, 1),
+                 lambda: bm.export([0], 4), lambda: bm.prefix_groups([0]), lambda: bm.set_host_blocks(8)):
+        with pytest.raises(pk.PaError) as e:
+            call()
+        assert e.value.status == -1
+    assert bm.table(0).tolist() == [0, 1, 2] and bm.length(0) == 9
+    # Too small a pair buffer changes nothing.
+    seqs = np.array([0], dtype=np.int64)
+    pairs = np.zeros((2, 2), dtype=np.int32)
+    n = ctypes.c_int32(0)
+    st = _lib.lib.pa_bm_swap_in(bm._h, seqs.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), 1,
+                                pairs.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), 2, ctypes.byref(n))
+    assert st == -1 and bm.is_swapped(0)
+    bm.free(0)
+    assert bm.stats()["free_host_blocks"] == 4 and bm.stats()["num_seqs"] == 0
+    bm.check()
+    with pytest.raises(KeyError):
+        bm.is_swapped(0)
+
+
 def test_block_manager_errors():
     with pytest.raises(pk.PaError):
         pk.BlockManager(0, 16)
@@ -410,6 +539,33 @@ def test_abi_rejects_bad_pools_without_launching(pool, status):
     assert _lib.lib.pa_last_error()
     st = _lib.lib.pa_copy_blocks(ctypes.byref(pool), dummy, 1, None)
     assert st == status
+
+
+def test_abi_rejects_bad_swap_arguments_without_launching():
+    dev = _pool()
+    L = _lib.lib
+
+    def call(host=None, pairs=((0, 1),), direction=0, engine=0, n=None):
+        arr = np.ascontiguousarray(np.array(pairs, dtype=np.int32).reshape(-1, 2))
+        ptr = arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)) if arr.size else None
+        return L.pa_swap_blocks(ctypes.byref(dev), ctypes.byref(host or _pool(k=0x50000, v=0x60000)), ptr,
+                                arr.shape[0] if n is None else n, direction, engine, None)
+
+    assert call(pairs=(), n=0) == 0                          # no pairs: no-op, no HIP call
+    assert call(host=_pool(b=8, k=0x50000, v=0x60000)) == -1  # block shape differs
+    assert call(host=_pool(dtype=0, k=0x50000, v=0x60000)) == -1
+    assert call(host=_pool(k=0)) == -1
+    assert call(host=_pool(k=0x50004, v=0x60000)) == -1      # alignment
+    assert call(direction=2) == -1
+    assert call(engine=7) == -1
+    assert call(n=-1) == -1
+    assert call(pairs=((100, 0),)) == -1                     # source outside the device pool
+    assert call(pairs=((0, 100),)) == -1                     # destination outside the host pool
+    assert call(pairs=((0, 1), (2, 1))) == -1                # destination repeats
+    assert call(pairs=((0, -1),), direction=1) == -1
+    assert b"destination" in L.pa_last_error()
+    dev_bad = _pool(b=12)
+    assert L.pa_swap_blocks(ctypes.byref(dev_bad), ctypes.byref(_pool()), None, 0, 0, 0, None) == -2
 
 
 def test_abi_rejects_bad_decode_arguments_without_launching():
