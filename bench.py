@@ -225,6 +225,81 @@ def copy_probe(torch, nbytes: int) -> int:
     return 0
 
 
+def swap_sweep(torch, pk, lengths, reps: int = 10) -> int:
+    """Preemption by swapping, one layer of the c3 head layout (8 KV heads,
+    head_dim 128, bf16, block 16): a sequence of L tokens is swapped out to
+    pinned host memory and back in with each engine, through pairs from the
+    block manager.  `shuffled`: device blocks from a shuffled free list (one
+    DMA copy per block and pool); `contiguous`: ascending device blocks (one
+    DMA copy per pool).  Times are HIP events on the stream around `reps`
+    back-to-back calls.  recompute_floor_us prices the other recovery option
+    for the same layer from what the head layout fixes: the Q/K/V/O
+    projections (2 * hidden * (2 * hidden + 2 * kv_width) FLOPs per token)
+    plus causal attention over the prompt, at the dense bf16 MFMA peak, no
+    MLP: any real layer recomputes slower than this."""
+    B, hkv, d, hq = 16, 8, 128, 32
+    hidden, kv_width = hq * d, hkv * d
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream()
+    max_blocks = -(-max(lengths) // B)
+    nb = 2 * max_blocks
+    kp = torch.randn((nb, B, hkv, d), device=dev, dtype=torch.float32).to(torch.bfloat16)
+    vp = torch.randn((nb, B, hkv, d), device=dev, dtype=torch.float32).to(torch.bfloat16)
+    pool = pk.KvPool(kp, vp)
+    hk = torch.empty((max_blocks, B, hkv, d), dtype=torch.bfloat16).pin_memory()
+    hv = torch.empty((max_blocks, B, hkv, d), dtype=torch.bfloat16).pin_memory()
+    host = pk.HostKvPool(hk, hv)
+    engines = {"kernel": pk.PA_SWAP_ENGINE_KERNEL, "dma": pk.PA_SWAP_ENGINE_DMA}
+
+    def timed(pairs, direction, engine):
+        for _ in range(2):
+            pk.swap_blocks(pool, host, pairs, direction, engine, stream)
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        start.record(stream)
+        for _ in range(reps):
+            pk.swap_blocks(pool, host, pairs, direction, engine, stream)
+        end.record(stream)
+        host_us = (time.perf_counter() - t0) * 1e6 / reps
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / reps * 1e3, host_us
+
+    rows = []
+    for L in lengths:
+        blocks = -(-L // B)
+        nbytes = 2 * blocks * B * hkv * d * 2
+        row = {"context_len": L, "blocks": blocks, "bytes": nbytes}
+        for layout, order in (("shuffled", np.random.default_rng(L).permutation(nb)), ("contiguous", None)):
+            bm = pk.BlockManager(nb, B, order)
+            bm.set_host_blocks(max_blocks)
+            bm.append(0, L)
+            out_pairs = bm.swap_out([0])
+            in_pairs = bm.swap_in([0])
+            for ename, eng in engines.items():
+                if layout == "contiguous" and ename == "kernel":
+                    continue
+                us_out, h_out = timed(out_pairs, pk.PA_SWAP_OUT, eng)
+                us_in, h_in = timed(in_pairs, pk.PA_SWAP_IN, eng)
+                key = f"{ename}_{layout}"
+                row[key] = {"out_us": round(us_out, 2), "in_us": round(us_in, 2),
+                            "out_GBs": round(nbytes / us_out / 1e3, 2), "in_GBs": round(nbytes / us_in / 1e3, 2),
+                            "host_call_us": round(max(h_out, h_in), 2)}
+        flops = L * 2 * hidden * (2 * hidden + 2 * kv_width) + 2 * 2 * (L * (L + 1) // 2) * hq * d
+        row["recompute_floor_us"] = round(flops / 2.5e15 * 1e6, 2)
+        best_swap = min(row[k]["out_us"] + row[k]["in_us"] for k in ("kernel_shuffled", "dma_shuffled"))
+        row["swap_round_trip_us"] = round(best_swap, 2)
+        row["swap_us_per_token"] = round(best_swap / L, 4)
+        rows.append(row)
+    big = rows[-1]
+    print(json.dumps({"metric": "swap_round_trip_GBs", "value": round(2 * big["bytes"] / big["swap_round_trip_us"] / 1e3, 2),
+                      "unit": "GB/s", "n_gpus": 1, "dtype": "bf16", "data": "synthetic",
+                      "config": {"workload": "swap one layer (8 KV heads, head_dim 128, block 16) of a sequence "
+                                             "to pinned host memory and back", "reps": reps},
+                      "sweep": rows}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -247,6 +322,9 @@ def main() -> int:
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="profiling aid: run a plain device-to-device copy of BYTES (the reference whose "
                          "counter readings calibrate the traffic figures) and exit")
+    ap.add_argument("--swap-sweep", action="store_true",
+                    help="measure swapping a sequence out to pinned host memory and back at several context "
+                         "lengths (both engines) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -257,6 +335,9 @@ def main() -> int:
     if args.copy_probe:
         return copy_probe(torch, args.copy_probe)
     import paged_kv_cache_115_amd as pk
+    if args.swap_sweep:
+        torch.cuda.set_device(0)
+        return swap_sweep(torch, pk, [256, 1024, 4096, 16384, 32768])
 
     torch.cuda.set_device(0)
     if args.config == "c5":
