@@ -230,9 +230,10 @@ def swap_sweep(torch, pk, lengths, reps: int = 10) -> int:
     head_dim 128, bf16, block 16): a sequence of L tokens is swapped out to
     pinned host memory and back in with each engine, through pairs from the
     block manager.  `shuffled`: device blocks from a shuffled free list (one
-    DMA copy per block and pool); `contiguous`: ascending device blocks (one
-    DMA copy per pool).  Times are HIP events on the stream around `reps`
-    back-to-back calls.  recompute_floor_us prices the other recovery option
+    runtime copy per block and pool); `contiguous`: ascending device blocks
+    (one runtime copy per pool on the way out; swap-in takes the freed blocks
+    back last retired first, so its runs are single blocks again).  Times are
+    HIP events on the stream around `reps` back-to-back calls.  recompute_floor_us prices the other recovery option
     for the same layer from what the head layout fixes: the Q/K/V/O
     projections (2 * hidden * (2 * hidden + 2 * kv_width) FLOPs per token)
     plus causal attention over the prompt, at the dense bf16 MFMA peak, no
@@ -249,7 +250,7 @@ def swap_sweep(torch, pk, lengths, reps: int = 10) -> int:
     hk = torch.empty((max_blocks, B, hkv, d), dtype=torch.bfloat16).pin_memory()
     hv = torch.empty((max_blocks, B, hkv, d), dtype=torch.bfloat16).pin_memory()
     host = pk.HostKvPool(hk, hv)
-    engines = {"kernel": pk.PA_SWAP_ENGINE_KERNEL, "dma": pk.PA_SWAP_ENGINE_DMA}
+    engines = {"kernel": pk.PA_SWAP_ENGINE_KERNEL, "memcpy": pk.PA_SWAP_ENGINE_MEMCPY}
 
     def timed(pairs, direction, engine):
         for _ in range(2):
@@ -287,7 +288,7 @@ def swap_sweep(torch, pk, lengths, reps: int = 10) -> int:
                             "host_call_us": round(max(h_out, h_in), 2)}
         flops = L * 2 * hidden * (2 * hidden + 2 * kv_width) + 2 * 2 * (L * (L + 1) // 2) * hq * d
         row["recompute_floor_us"] = round(flops / 2.5e15 * 1e6, 2)
-        best_swap = min(row[k]["out_us"] + row[k]["in_us"] for k in ("kernel_shuffled", "dma_shuffled"))
+        best_swap = min(row[k]["out_us"] + row[k]["in_us"] for k in ("kernel_shuffled", "memcpy_shuffled"))
         row["swap_round_trip_us"] = round(best_swap, 2)
         row["swap_us_per_token"] = round(best_swap / L, 4)
         rows.append(row)

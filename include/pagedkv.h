@@ -125,9 +125,11 @@ pa_status pa_copy_blocks(const pa_kv_pool* pool, const int32_t* pairs, int32_t n
  *                 block; PA_SWAP_IN: src a host block, dst a device block.
  *   engine      : PA_SWAP_ENGINE_KERNEL - kernels move the blocks through
  *                 the host memory's device mapping, up to 240 pairs per
- *                 launch; PA_SWAP_ENGINE_DMA - one hipMemcpyAsync per pool
- *                 for every run of pairs that continue each other on both
- *                 sides (src + 1, dst + 1).
+ *                 launch (the fast path: PCIe-bound whatever the layout);
+ *                 PA_SWAP_ENGINE_MEMCPY - one hipMemcpyAsync per pool for
+ *                 every run of pairs that continue each other on both sides
+ *                 (src + 1, dst + 1); per-call cost dominates unless the
+ *                 runs are long.
  * Checked on the host before anything is enqueued (PA_ERR_INVALID): ids
  * inside their pools, destinations distinct, both host arrays pinned and
  * device-mapped over their whole extent, both device arrays device memory.
@@ -139,7 +141,7 @@ pa_status pa_copy_blocks(const pa_kv_pool* pool, const int32_t* pairs, int32_t n
 #define PA_SWAP_OUT 0
 #define PA_SWAP_IN 1
 #define PA_SWAP_ENGINE_KERNEL 0
-#define PA_SWAP_ENGINE_DMA 1
+#define PA_SWAP_ENGINE_MEMCPY 1
 pa_status pa_swap_blocks(const pa_kv_pool* device_pool, const pa_kv_pool* host_pool, const int32_t* pairs,
                          int32_t num_pairs, int32_t direction, int32_t engine, void* stream);
 

@@ -13,14 +13,14 @@ import os
 
 import numpy as np
 
-from ._lib import (LIB_PATH, PA_BF16, PA_DECODE_SHARED_KV, PA_F32, PA_JOB_SHARED, PA_SWAP_ENGINE_DMA,
+from ._lib import (LIB_PATH, PA_BF16, PA_DECODE_SHARED_KV, PA_F32, PA_JOB_SHARED, PA_SWAP_ENGINE_MEMCPY,
                    PA_SWAP_ENGINE_KERNEL, PA_SWAP_IN, PA_SWAP_OUT, PaDecodePlanInfo, PaError, PaKvPool, lib)
 
 __all__ = [
     "LIB_PATH", "PA_F32", "PA_BF16", "PA_DECODE_SHARED_KV", "PA_JOB_SHARED", "PaError", "BlockManager", "KvPool",
     "reshape_and_cache", "copy_blocks", "decode_plan", "decode_workspace_bytes",
     "decode", "DecodePlan", "default_workgroups", "HostKvPool", "swap_blocks", "PA_SWAP_OUT", "PA_SWAP_IN",
-    "PA_SWAP_ENGINE_KERNEL", "PA_SWAP_ENGINE_DMA",
+    "PA_SWAP_ENGINE_KERNEL", "PA_SWAP_ENGINE_MEMCPY",
 ]
 
 

@@ -13,7 +13,7 @@ PA_JOB_SHARED = 1 << 16
 PA_SWAP_OUT = 0
 PA_SWAP_IN = 1
 PA_SWAP_ENGINE_KERNEL = 0
-PA_SWAP_ENGINE_DMA = 1
+PA_SWAP_ENGINE_MEMCPY = 1
 
 
 class PaError(RuntimeError):

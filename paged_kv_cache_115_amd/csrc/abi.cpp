@@ -163,8 +163,8 @@ extern "C" pa_status pa_swap_blocks(const pa_kv_pool* device_pool, const pa_kv_p
     return fail(PA_ERR_INVALID, "%s: host_pool pointers must be 16-byte aligned", who);
   if (direction != PA_SWAP_OUT && direction != PA_SWAP_IN)
     return fail(PA_ERR_INVALID, "%s: direction %d (PA_SWAP_OUT=0, PA_SWAP_IN=1)", who, direction);
-  if (engine != PA_SWAP_ENGINE_KERNEL && engine != PA_SWAP_ENGINE_DMA)
-    return fail(PA_ERR_INVALID, "%s: engine %d (PA_SWAP_ENGINE_KERNEL=0, PA_SWAP_ENGINE_DMA=1)", who, engine);
+  if (engine != PA_SWAP_ENGINE_KERNEL && engine != PA_SWAP_ENGINE_MEMCPY)
+    return fail(PA_ERR_INVALID, "%s: engine %d (PA_SWAP_ENGINE_KERNEL=0, PA_SWAP_ENGINE_MEMCPY=1)", who, engine);
   if (num_pairs < 0) return fail(PA_ERR_INVALID, "%s: num_pairs %d < 0", who, num_pairs);
   if (num_pairs == 0) return PA_OK;
   if (!pairs) return fail(PA_ERR_INVALID, "%s: pairs is NULL", who);
@@ -208,7 +208,7 @@ extern "C" pa_status pa_swap_blocks(const pa_kv_pool* device_pool, const pa_kv_p
     }
     return PA_OK;
   }
-  // DMA engine: one copy per pool for every run of pairs that continue each
+  // Runtime copies: one hipMemcpyAsync per pool for every run of pairs that continue each
   // other on both sides (src + 1, dst + 1).
   char* src_k = static_cast<char*>(out ? device_pool->k : host_pool->k);
   char* src_v = static_cast<char*>(out ? device_pool->v : host_pool->v);

@@ -15,7 +15,7 @@ from flows import _OracleSide, _ProductSide, assert_close, bits, preempt_run, to
 
 pytestmark = pytest.mark.gpu
 
-ENGINES = ["kernel", "dma"]
+ENGINES = ["kernel", "memcpy"]
 
 
 @pytest.fixture(scope="module")
@@ -27,12 +27,12 @@ def pk():
 
 
 def _engine(pk, name):
-    return pk.PA_SWAP_ENGINE_KERNEL if name == "kernel" else pk.PA_SWAP_ENGINE_DMA
+    return pk.PA_SWAP_ENGINE_KERNEL if name == "kernel" else pk.PA_SWAP_ENGINE_MEMCPY
 
 
 def _pairs(rng, n, n_src, n_dst, run):
     """n (src, dst) pairs with distinct destinations: a leading run of `run`
-    consecutive ids on both sides (one DMA copy), the rest scattered."""
+    consecutive ids on both sides (one runtime copy per pool), the rest scattered."""
     src = rng.choice(n_src, size=n, replace=True)
     dst = rng.permutation(n_dst)[:n]
     s0, d0 = int(rng.integers(0, n_src - run)), int(rng.integers(0, n_dst - run))
