@@ -56,6 +56,22 @@ Readings where the pages leave a choice open:
     copied as well.  Swapping in is the mirror image.  A swapped sequence
     keeps its length, cannot grow or fork, and free_seq releases its host
     blocks.  Both directions are all or nothing.
+  * prefix caching across requests (the pages: a server hashes block contents
+    so that any two requests with a common prefix share the same physical
+    blocks; llminference.xinbetween.com S06, "What's next"; the same page's
+    "Production notes" on a radix tree of prefixes).  This model keys a cached
+    block by its whole token prefix, the plain definition of "same content":
+    the keys and values of a block depend on every token up to its end.
+    Readings: only full blocks of an admitted prompt are cached and looked up;
+    the lookup walks the prompt's full blocks from the first and stops at the
+    first miss; at least the prompt's last token is always left to compute, so
+    at most (n - 1) // B blocks are reused; a block whose count drops to zero
+    stays cached and becomes evictable; new blocks come from the free list
+    first and only then from the least recently retired evictable block; a
+    retiring table's cached blocks become evictable deepest first (the tail
+    goes before the shared prompt); evicting a block also drops every cached
+    block whose prefix extends it (it can no longer be reached), and those go
+    to the free list in ascending id order.
 """
 from __future__ import annotations
 
@@ -86,6 +102,48 @@ class BlockManagerModel:
         self.host_tables: dict[int, list[int]] = {}
         self.swap_out_blocks = 0
         self.swap_in_blocks = 0
+        self.prefix_cache = False
+        self.index: dict[tuple, int] = {}        # token prefix -> cached block
+        self.block_key: dict[int, tuple] = {}    # cached block -> its token prefix
+        self.evictable: dict[int, int] = {}      # cached block with count 0 -> retire tick
+        self.tick = 0
+        self.prefix_query_tokens = 0
+        self.prefix_hit_tokens = 0
+
+    # -- allocation -------------------------------------------------------
+    def _capacity(self) -> int:
+        return len(self.free) + len(self.evictable)
+
+    def _uncache(self, blk: int) -> None:
+        del self.index[self.block_key.pop(blk)]
+        self.evictable.pop(blk, None)
+
+    def _take(self) -> int:
+        """A block for a new table entry: the free list first, then the least
+        recently retired evictable cached block."""
+        if self.free:
+            blk = self.free.pop()
+        else:
+            blk = min(self.evictable, key=self.evictable.get)
+            key = self.block_key[blk]
+            self._uncache(blk)
+            below = sorted(b for k, b in self.index.items() if len(k) > len(key) and k[:len(key)] == key)
+            for b in below:
+                assert b in self.evictable, "a reachable-only-through-evicted block is in use"
+                self._uncache(b)
+                self.free.append(b)
+        self.refcount[blk] = 1
+        return blk
+
+    def _release_device(self, table) -> None:
+        for blk in table:
+            self.refcount[blk] -= 1
+            if self.refcount[blk] == 0 and blk not in self.block_key:
+                self.free.append(blk)
+        for blk in reversed(table):
+            if self.refcount[blk] == 0 and blk in self.block_key and blk not in self.evictable:
+                self.evictable[blk] = self.tick
+                self.tick += 1
 
     # -- sizing ---------------------------------------------------------
     def _needs(self, seq: int, n_new: int, refcount_delta: dict) -> int:
@@ -109,18 +167,15 @@ class BlockManagerModel:
         cow = []
         if n_new > 0 and length % b != 0 and self.refcount[table[-1]] > 1:
             src = table[-1]
-            dst = self.free.pop()
+            dst = self._take()
             self.refcount[src] -= 1
-            self.refcount[dst] = 1
             table[-1] = dst
             cow.append((src, dst))
             self.cow_copies += 1
         slots = []
         for t in range(length, length + n_new):
             if t % b == 0:
-                blk = self.free.pop()
-                self.refcount[blk] = 1
-                table.append(blk)
+                table.append(self._take())
             slots.append(table[t // b] * b + t % b)
         self.lengths[seq] = length + n_new
         return slots, cow
@@ -134,7 +189,7 @@ class BlockManagerModel:
         if n_new < 0:
             raise ValueError("n_new must be >= 0")
         self._resident(seq)
-        if self._needs(seq, n_new, {}) > len(self.free):
+        if self._needs(seq, n_new, {}) > self._capacity():
             self.alloc_failures += 1
             raise OutOfBlocks(f"sequence {seq}: not enough free blocks")
         return self._append_unchecked(seq, n_new)
@@ -148,7 +203,7 @@ class BlockManagerModel:
             self._resident(s)
         delta: dict = {}
         need = sum(self._needs(s, 1, delta) for s in seqs)
-        if need > len(self.free):
+        if need > self._capacity():
             self.alloc_failures += 1
             raise OutOfBlocks("step does not fit in the free list")
         slots, cows = [], []
@@ -174,7 +229,7 @@ class BlockManagerModel:
         if seq in self.host_tables:
             self._release(self.host_tables.pop(seq), self.host_refcount, self.host_free)
             return
-        self._release(self.tables.pop(seq, []), self.refcount, self.free)
+        self._release_device(self.tables.pop(seq, []))
 
     @staticmethod
     def _release(table, counts, free) -> None:
@@ -195,7 +250,7 @@ class BlockManagerModel:
         self.host_refcount = [0] * n
 
     @staticmethod
-    def _move(seqs, src_tables, dst_tables, src_counts, src_free, dst_counts, dst_free):
+    def _move(seqs, src_tables, dst_tables, release, dst_counts, take):
         """Copy the distinct blocks of the listed tables from one pool to the
         other, then retire the source tables.  Returns the (src, dst) pairs."""
         mapping: dict[int, int] = {}
@@ -204,13 +259,14 @@ class BlockManagerModel:
             new = []
             for blk in src_tables[s]:
                 if blk not in mapping:
-                    mapping[blk] = dst_free.pop()
+                    mapping[blk] = take()
+                    dst_counts[mapping[blk]] = 0
                     pairs.append((blk, mapping[blk]))
                 dst_counts[mapping[blk]] += 1
                 new.append(mapping[blk])
             dst_tables[s] = new
         for s in seqs:
-            BlockManagerModel._release(src_tables.pop(s), src_counts, src_free)
+            release(src_tables.pop(s))
         return pairs
 
     def _distinct(self, seqs, tables) -> list[int]:
@@ -230,8 +286,8 @@ class BlockManagerModel:
         need = len({blk for s in seqs for blk in self.tables[s]})
         if need > len(self.host_free):
             raise OutOfBlocks("not enough free host blocks")
-        pairs = self._move(seqs, self.tables, self.host_tables, self.refcount, self.free,
-                           self.host_refcount, self.host_free)
+        pairs = self._move(seqs, self.tables, self.host_tables, self._release_device,
+                           self.host_refcount, self.host_free.pop)
         self.swap_out_blocks += len(pairs)
         return pairs
 
@@ -241,10 +297,11 @@ class BlockManagerModel:
         read.  All or nothing: OutOfBlocks when device blocks are short."""
         seqs = self._distinct(seqs, self.host_tables)
         need = len({blk for s in seqs for blk in self.host_tables[s]})
-        if need > len(self.free):
+        if need > self._capacity():
             raise OutOfBlocks("not enough free device blocks")
-        pairs = self._move(seqs, self.host_tables, self.tables, self.host_refcount, self.host_free,
-                           self.refcount, self.free)
+        pairs = self._move(seqs, self.host_tables, self.tables,
+                           lambda t: self._release(t, self.host_refcount, self.host_free),
+                           self.refcount, self._take)
         self.swap_in_blocks += len(pairs)
         return pairs
 
@@ -252,6 +309,59 @@ class BlockManagerModel:
         if seq not in self.lengths:
             raise KeyError(seq)
         return seq in self.host_tables
+
+    # -- prefix caching across requests ----------------------------------
+    def enable_prefix_cache(self) -> None:
+        if self.lengths:
+            raise ValueError("enable the prefix cache before any sequence exists")
+        self.prefix_cache = True
+
+    def append_prompt(self, seq: int, tokens):
+        """Admit a new sequence with its prompt token ids.  Leading full
+        blocks whose token prefix is cached are shared instead of allocated;
+        returns (slots, cached_tokens) with slot -1 for every cached token (its
+        keys and values are already in the pool).  The prompt's new full blocks
+        are cached once the call returns; their rows must be written (on the
+        stream that later reads them) before another request can read them.
+        All or nothing."""
+        if not self.prefix_cache:
+            raise ValueError("prefix cache is not enabled")
+        if seq in self.lengths:
+            raise ValueError(f"sequence {seq} exists")
+        tokens = tuple(int(t) for t in tokens)
+        n, b = len(tokens), self.block_size
+        hits = []
+        for j in range((n - 1) // b if n else 0):
+            blk = self.index.get(tokens[:(j + 1) * b])
+            if blk is None:
+                break
+            hits.append(blk)
+        new = -(-n // b) - len(hits)
+        revived = sum(1 for blk in hits if blk in self.evictable)
+        if new > self._capacity() - revived:
+            self.alloc_failures += 1
+            raise OutOfBlocks(f"sequence {seq}: not enough free blocks")
+        self.prefix_query_tokens += n
+        self.prefix_hit_tokens += len(hits) * b
+        for blk in hits:
+            self.evictable.pop(blk, None)
+            self.refcount[blk] += 1
+        table = list(hits)
+        while len(table) < -(-n // b):
+            table.append(self._take())
+        self.tables[seq] = table
+        self.lengths[seq] = n
+        for j in range(len(hits), n // b):
+            key = tokens[:(j + 1) * b]
+            if key not in self.index:
+                self.index[key] = table[j]
+                self.block_key[table[j]] = key
+        cached = len(hits) * b
+        slots = [-1] * cached + [table[t // b] * b + t % b for t in range(cached, n)]
+        return slots, cached
+
+    def is_cached(self, blk: int) -> bool:
+        return blk in self.block_key
 
     # -- queries --------------------------------------------------------
     def table(self, seq: int) -> list[int]:
@@ -264,7 +374,7 @@ class BlockManagerModel:
         return self.lengths[seq]
 
     def stats(self) -> dict:
-        used = self.num_blocks - len(self.free)
+        used = self.num_blocks - len(self.free) - len(self.evictable)
         return dict(num_blocks=self.num_blocks, free_blocks=len(self.free),
                     used_blocks=used, num_seqs=len(self.lengths),
                     logical_tokens=sum(self.lengths.values()),
@@ -272,7 +382,9 @@ class BlockManagerModel:
                     alloc_failures=self.alloc_failures, cow_copies=self.cow_copies,
                     host_blocks=self.num_host_blocks, free_host_blocks=len(self.host_free),
                     swapped_seqs=len(self.host_tables), swap_out_blocks=self.swap_out_blocks,
-                    swap_in_blocks=self.swap_in_blocks)
+                    swap_in_blocks=self.swap_in_blocks, cached_blocks=len(self.index),
+                    evictable_blocks=len(self.evictable), prefix_query_tokens=self.prefix_query_tokens,
+                    prefix_hit_tokens=self.prefix_hit_tokens)
 
     def check(self) -> None:
         """Raise AssertionError unless counts equal table references exactly."""
@@ -289,5 +401,13 @@ class BlockManagerModel:
             assert named == counts, "refcount differs from table references"
             free = set(free_list)
             assert len(free) == len(free_list), "block listed twice as free"
+            parked = set(self.evictable) if counts is self.refcount else set()
+            assert not free & parked, "block both free and evictable"
             for blk in range(n):
-                assert (blk in free) == (named[blk] == 0), f"block {blk} leaked or aliased"
+                assert (blk in free or blk in parked) == (named[blk] == 0), f"block {blk} leaked or aliased"
+        assert len(self.index) == len(self.block_key)
+        for key, blk in self.index.items():
+            assert self.block_key[blk] == key and len(key) % self.block_size == 0 and key
+            assert (self.refcount[blk] == 0) == (blk in self.evictable), f"cached block {blk} count/evictable"
+            if len(key) > self.block_size:
+                assert key[:-self.block_size] in self.index, f"cached block {blk} has no cached parent"

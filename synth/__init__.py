@@ -243,6 +243,64 @@ def preempt_case(name: str, seed: int | None = None) -> dict:
                 host_blocks=cfg["host_blocks"])
 
 
+def _splitmix64(x: int) -> int:
+    x = (x + 0x9E3779B97F4A7C15) & 0xFFFFFFFFFFFFFFFF
+    x = ((x ^ (x >> 30)) * 0xBF58476D1CE4E5B9) & 0xFFFFFFFFFFFFFFFF
+    x = ((x ^ (x >> 27)) * 0x94D049BB133111EB) & 0xFFFFFFFFFFFFFFFF
+    return x ^ (x >> 31)
+
+
+def token_rows(tokens, hkv: int, d: int, dtype: str, salt: int = 0):
+    """Stand-in for a model's keys and values of a token sequence: row t is
+    drawn from a generator seeded by the whole prefix tokens[:t+1] (a rolling
+    64-bit state), so two sequences get bit-identical rows exactly where
+    their prefixes agree.  Returns (keys, values) [n, Hkv, D]."""
+    n = len(tokens)
+    k = np.empty((n, hkv, d), dtype=np.float32 if dtype == "f32" else np.uint16)
+    v = np.empty_like(k)
+    state = _splitmix64(salt)
+    for t, tok in enumerate(tokens):
+        state = _splitmix64(state ^ (int(tok) & 0xFFFFFFFF))
+        x = np.random.default_rng(state).standard_normal(size=(2, hkv, d), dtype=np.float32)
+        if dtype != "f32":
+            x = f32_to_bf16_bits(x)
+        k[t], v[t] = x[0], x[1]
+    return k, v
+
+
+# Prefix caching across requests: requests that open with one of a few
+# system prompts (the pages' example: the same 2,000-token system prompt sent
+# thousands of times an hour; llminference.xinbetween.com S06, "What's next"
+# and "Unshareable duplicates"), each followed by a private user turn.
+PREFIX_CACHE_CONFIGS: dict[str, dict] = {
+    "h1s": dict(seed=31, requests=12, system_prompts=2, system_len=(40, 90), user=(1, 50), vocab=50,
+                block_size=16, num_q_heads=32, num_kv_heads=8, head_dim=128, dtype="bf16"),
+    "h1f": dict(seed=32, requests=10, system_prompts=3, system_len=(8, 40), user=(1, 20), vocab=7,
+                block_size=8, num_q_heads=8, num_kv_heads=4, head_dim=64, dtype="f32"),
+}
+
+
+def prefix_cache_case(name: str, seed: int | None = None) -> dict:
+    """Token-id prompts of a request stream.  Keys: cfg, prompts (list of int32
+    arrays, one per request in arrival order), system (which system prompt each
+    request opens with), q[requests, Hq, D], scale, num_blocks (room for every
+    prompt privately, plus one block per request)."""
+    cfg = dict(PREFIX_CACHE_CONFIGS[name])
+    rng = np.random.default_rng(cfg["seed"] if seed is None else seed)
+    lo, hi = cfg["system_len"]
+    systems = [rng.integers(0, cfg["vocab"], size=int(rng.integers(lo, hi + 1))).astype(np.int32)
+               for _ in range(cfg["system_prompts"])]
+    which = rng.integers(0, cfg["system_prompts"], size=cfg["requests"])
+    ulo, uhi = cfg["user"]
+    prompts = [np.concatenate([systems[w], rng.integers(0, cfg["vocab"], size=int(rng.integers(ulo, uhi + 1)))
+                               .astype(np.int32)]) for w in which]
+    b = cfg["block_size"]
+    nb = sum(-(-len(p) // b) for p in prompts) + cfg["requests"]
+    q = _normal(rng, (cfg["requests"], cfg["num_q_heads"], cfg["head_dim"]), cfg["dtype"])
+    return dict(cfg=cfg, name=name, prompts=prompts, system=which, q=q, scale=default_scale(cfg["head_dim"]),
+                num_blocks=nb)
+
+
 def byte_pattern(shape, dtype: str, seed: int) -> np.ndarray:
     """Seeded arbitrary bit patterns (any bits, NaNs included) for copy tests."""
     rng = np.random.default_rng(seed)
