@@ -396,6 +396,10 @@ typedef struct pa_bm_stats {
   int32_t pad2_;
   int64_t swap_out_blocks; /* device -> host pairs issued */
   int64_t swap_in_blocks;  /* host -> device pairs issued */
+  int32_t cached_blocks;    /* prefix cache: full blocks indexed by content */
+  int32_t evictable_blocks; /* cached blocks no table names (reusable, not in free_blocks) */
+  int64_t prefix_query_tokens; /* prompt tokens looked up */
+  int64_t prefix_hit_tokens;   /* of those, found in the cache */
 } pa_bm_stats;
 
 /* Returns NULL on bad sizes or if initial_order is not a permutation of
@@ -487,6 +491,35 @@ pa_status pa_bm_swap_in(pa_bm* bm, const int64_t* seqs, int32_t num, int32_t* pa
 int32_t pa_bm_swapped(const pa_bm* bm, int64_t seq);            /* 1 swapped, 0 resident, -1 unknown */
 int32_t pa_bm_host_refcount(const pa_bm* bm, int32_t host_block); /* -1 if out of range */
 
+/* Prefix caching across requests (S06 "What's next": block contents are
+ * hashed so that any two requests with a common prefix share the same
+ * physical blocks; the same page's production notes on a radix tree of
+ * prefixes).  Off at creation; pa_bm_enable_prefix_cache turns it on while no
+ * sequence exists (PA_ERR_INVALID otherwise).
+ *
+ * pa_bm_append_prompt admits a NEW sequence with its prompt token ids
+ * (tokens: HOST int32 [n]).  Its leading full blocks are looked up by content
+ * - the block's B token ids after the same cached parent block, found by a
+ * 64-bit hash and then compared exactly, so the match is the whole token
+ * prefix - from the first block to the first miss, reusing at most
+ * (n - 1) / B blocks so that the last token is always computed.  A hit
+ * shares the cached block (count + 1); the rest of the prompt takes new
+ * blocks.  slots_out (HOST int64 [n]) gets -1 for every reused token, whose
+ * keys and values are already in the pool (pa_reshape_and_cache skips
+ * negative slots), and the flat slot otherwise; *n_cached_out = reused
+ * tokens (a multiple of B).  The prompt's new full blocks become cached when
+ * the call returns: write their rows on the stream that later reads them.
+ * Cached blocks whose count drops to zero stay cached ("evictable", counted
+ * apart from free_blocks); every allocation takes the free list first and
+ * then the least recently retired evictable block (a retiring table's blocks
+ * are ranked deepest first), dropping the cache entries below it.  All or
+ * nothing: PA_ERR_OOM changes nothing; PA_ERR_INVALID if the sequence exists
+ * or the cache is off. */
+pa_status pa_bm_enable_prefix_cache(pa_bm* bm);
+pa_status pa_bm_append_prompt(pa_bm* bm, int64_t seq, const int32_t* tokens, int32_t n, int64_t* slots_out,
+                              int32_t* n_cached_out);
+int32_t pa_bm_cached(const pa_bm* bm, int32_t block); /* 1 cached, 0 not, -1 out of range */
+
 int32_t pa_bm_len(const pa_bm* bm, int64_t seq);         /* -1 if unknown */
 int32_t pa_bm_refcount(const pa_bm* bm, int32_t block);  /* -1 if out of range */
 void pa_bm_get_stats(const pa_bm* bm, pa_bm_stats* out);
@@ -494,7 +527,9 @@ void pa_bm_get_stats(const pa_bm* bm, pa_bm_stats* out);
 /* Verify that each block's count equals the number of tables naming it, that
  * no named block is on the free list, that no block is lost, and that every
  * table holds ceil(L / B) entries (S06 "Reference counts must be exact"); the
- * same for host blocks and the tables of swapped sequences.
+ * same for host blocks and the tables of swapped sequences; and the prefix
+ * cache's own consistency (every entry found by its key, parents cached,
+ * evictable exactly when cached with count zero).
  * PA_OK or PA_ERR_INVALID with the first violation in pa_last_error. */
 pa_status pa_bm_check(const pa_bm* bm);
 

@@ -384,6 +384,23 @@ class BlockManager:
         """pa_bm_swap_in -> int32 [n, 2] (host block, device block) copies."""
         return self._swap(lib.pa_bm_swap_in, seqs, "pa_bm_swap_in")
 
+    def enable_prefix_cache(self) -> None:
+        _check(lib.pa_bm_enable_prefix_cache(self._h), "pa_bm_enable_prefix_cache")
+
+    def append_prompt(self, seq: int, tokens):
+        """pa_bm_append_prompt -> (slots int64[n] with -1 for reused tokens, cached token count)."""
+        tokens = np.ascontiguousarray(tokens, dtype=np.int32)
+        n = tokens.size
+        slots = np.zeros(max(n, 1), dtype=np.int64)
+        cached = ctypes.c_int32(0)
+        _check(lib.pa_bm_append_prompt(self._h, seq, tokens.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), n,
+                                       slots.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), ctypes.byref(cached)),
+               "pa_bm_append_prompt")
+        return slots[:n], cached.value
+
+    def is_cached(self, block: int) -> bool:
+        return lib.pa_bm_cached(self._h, block) == 1
+
     def is_swapped(self, seq: int) -> bool:
         r = lib.pa_bm_swapped(self._h, seq)
         if r < 0:

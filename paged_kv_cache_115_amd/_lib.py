@@ -45,7 +45,9 @@ class PaBmStats(ctypes.Structure):
                 ("cow_copies", ctypes.c_int64), ("host_blocks", ctypes.c_int32),
                 ("free_host_blocks", ctypes.c_int32), ("swapped_seqs", ctypes.c_int32),
                 ("pad2_", ctypes.c_int32), ("swap_out_blocks", ctypes.c_int64),
-                ("swap_in_blocks", ctypes.c_int64)]
+                ("swap_in_blocks", ctypes.c_int64), ("cached_blocks", ctypes.c_int32),
+                ("evictable_blocks", ctypes.c_int32), ("prefix_query_tokens", ctypes.c_int64),
+                ("prefix_hit_tokens", ctypes.c_int64)]
 
 
 def _load() -> ctypes.CDLL:
@@ -98,6 +100,9 @@ SIGNATURES = {
     "pa_bm_swap_in": (_i32, [_vp, _p64, _i32, _p32, _i32, _p32]),
     "pa_bm_swapped": (_i32, [_vp, _i64]),
     "pa_bm_host_refcount": (_i32, [_vp, _i32]),
+    "pa_bm_enable_prefix_cache": (_i32, [_vp]),
+    "pa_bm_append_prompt": (_i32, [_vp, _i64, _p32, _i32, _p64, _p32]),
+    "pa_bm_cached": (_i32, [_vp, _i32]),
     "pa_bm_len": (_i32, [_vp, _i64]),
     "pa_bm_refcount": (_i32, [_vp, _i32]),
     "pa_bm_get_stats": (None, [_vp, ctypes.POINTER(PaBmStats)]),

@@ -21,12 +21,24 @@
 //    second pool of blocks with its own free list and counts under the same
 //    discipline; the distinct blocks of the listed tables move once each, so
 //    sharing survives the round trip.
+//  - prefix caching across requests: block contents are hashed so that any
+//    two requests with a common prefix share the same physical blocks
+//    (S06, "What's next"; the same page's production notes on a radix tree
+//    of prefixes).  A cached block is keyed by (parent cached block, its B
+//    token ids), found through a 64-bit hash of that pair and then compared
+//    exactly, so a hash collision is a miss, never a wrong share; by
+//    induction over the parents the key is the block's whole token prefix.
+//    Cached blocks whose count drops to zero stay cached and become
+//    evictable; new blocks come from the free list first, then from the least
+//    recently retired evictable block (a retiring table's blocks are ranked
+//    deepest first), and evicting a block drops every cached block below it.
 // Appends and swaps are all-or-nothing: a request that does not fit changes
 // nothing.
 #include <algorithm>
 #include <cstring>
 #include <map>
 #include <new>
+#include <set>
 #include <unordered_map>
 #include <vector>
 
@@ -67,11 +79,117 @@ struct pa_bm {
   int64_t swap_in_blocks = 0;
   int32_t num_swapped = 0;
 
+  // Prefix cache.
+  struct Cached {
+    int32_t parent = -1;          // cached block holding the previous B tokens; -1 at position 0
+    uint64_t hash = 0;
+    std::vector<int32_t> tokens;  // this block's B token ids
+    std::vector<int32_t> children;
+  };
+  bool prefix_cache = false;
+  std::unordered_map<int32_t, Cached> cached;          // block -> entry
+  std::unordered_multimap<uint64_t, int32_t> index;    // hash -> block
+  std::set<std::pair<int64_t, int32_t>> evictable;     // (retire tick, block), count 0
+  std::vector<int64_t> tick_of;                        // retire tick of an evictable block, else -1
+  int64_t tick = 0;
+  int64_t prefix_query_tokens = 0;
+  int64_t prefix_hit_tokens = 0;
+
+  int64_t capacity() const { return (int64_t)dev.free_stack.size() + (int64_t)evictable.size(); }
+
+  static uint64_t mix(uint64_t x) {  // splitmix64 finalizer
+    x += 0x9e3779b97f4a7c15ull;
+    x = (x ^ (x >> 30)) * 0xbf58476d1ce4e5b9ull;
+    x = (x ^ (x >> 27)) * 0x94d049bb133111ebull;
+    return x ^ (x >> 31);
+  }
+  uint64_t key_hash(int32_t parent, const int32_t* tok) const {
+    uint64_t h = mix((uint64_t)(int64_t)parent);
+    for (int32_t i = 0; i < block_size; ++i) h = mix(h ^ (uint32_t)tok[i]);
+    return h;
+  }
+  // The cached block holding `tok` after `parent`, or -1.
+  int32_t lookup(int32_t parent, const int32_t* tok) const {
+    auto range = index.equal_range(key_hash(parent, tok));
+    for (auto it = range.first; it != range.second; ++it) {
+      const Cached& c = cached.at(it->second);
+      if (c.parent == parent && std::equal(c.tokens.begin(), c.tokens.end(), tok)) return it->second;
+    }
+    return -1;
+  }
+  void insert_cached(int32_t b, int32_t parent, const int32_t* tok) {
+    Cached c;
+    c.parent = parent;
+    c.hash = key_hash(parent, tok);
+    c.tokens.assign(tok, tok + block_size);
+    index.emplace(c.hash, b);
+    if (parent >= 0) cached.at(parent).children.push_back(b);
+    cached.emplace(b, std::move(c));
+  }
+  // Forget block b's cache entry (and its evictable rank).
+  void uncache(int32_t b) {
+    Cached& c = cached.at(b);
+    auto range = index.equal_range(c.hash);
+    for (auto it = range.first; it != range.second; ++it)
+      if (it->second == b) {
+        index.erase(it);
+        break;
+      }
+    if (c.parent >= 0) {
+      auto pit = cached.find(c.parent);
+      if (pit != cached.end()) {
+        auto& ch = pit->second.children;
+        ch.erase(std::find(ch.begin(), ch.end(), b));
+      }
+    }
+    if (tick_of[b] >= 0) {
+      evictable.erase({tick_of[b], b});
+      tick_of[b] = -1;
+    }
+    cached.erase(b);
+  }
+
+  // A block for a new table entry, count 1: the free list first, then the
+  // least recently retired evictable block, whose cached descendants (no
+  // longer reachable) go to the free list in ascending id order.
   int32_t pop() {
-    int32_t b = dev.free_stack.back();
-    dev.free_stack.pop_back();
+    int32_t b;
+    if (!dev.free_stack.empty()) {
+      b = dev.free_stack.back();
+      dev.free_stack.pop_back();
+    } else {
+      b = evictable.begin()->second;
+      std::vector<int32_t> below, todo(cached.at(b).children);
+      while (!todo.empty()) {
+        const int32_t x = todo.back();
+        todo.pop_back();
+        below.push_back(x);
+        for (int32_t y : cached.at(x).children) todo.push_back(y);
+      }
+      std::sort(below.begin(), below.end());
+      for (int32_t x : below) {
+        uncache(x);
+        dev.free_stack.push_back(x);
+      }
+      uncache(b);
+    }
     dev.refcount[b] = 1;
     return b;
+  }
+
+  // Retire a device table: counts drop in table order, uncached blocks at
+  // zero return to the free list in that order; cached blocks at zero become
+  // evictable, ranked deepest first.
+  void release_dev(const std::vector<int32_t>& table) {
+    for (int32_t b : table)
+      if (--dev.refcount[b] == 0 && !cached.count(b)) dev.free_stack.push_back(b);
+    for (auto it = table.rbegin(); it != table.rend(); ++it) {
+      const int32_t b = *it;
+      if (dev.refcount[b] == 0 && cached.count(b) && tick_of[b] < 0) {
+        tick_of[b] = tick++;
+        evictable.emplace(tick_of[b], b);
+      }
+    }
   }
 
   // Free blocks that appending n_new tokens to (len, table) would consume.
@@ -130,6 +248,7 @@ extern "C" pa_bm* pa_bm_create(int32_t num_blocks, int32_t block_size, const int
   bm->num_blocks = num_blocks;
   bm->block_size = block_size;
   bm->dev.refcount.assign(num_blocks, 0);
+  bm->tick_of.assign(num_blocks, -1);
   bm->dev.free_stack.resize(num_blocks);
   if (initial_order) {
     std::vector<char> seen(num_blocks, 0);
@@ -163,10 +282,10 @@ extern "C" pa_status pa_bm_append(pa_bm* bm, int64_t seq, int32_t n_new, int64_t
   const int64_t need = bm->needs(s, n_new, delta);
   if (!delta.empty() && !cow_pairs_out)
     return fail(PA_ERR_INVALID, "pa_bm_append: a copy-on-write pair is due but cow_pairs_out is NULL");
-  if (need > (int64_t)bm->dev.free_stack.size()) {
+  if (need > bm->capacity()) {
     bm->alloc_failures += 1;
-    return fail(PA_ERR_OOM, "pa_bm_append: sequence %lld needs %lld blocks, %zu free", (long long)seq,
-                (long long)need, bm->dev.free_stack.size());
+    return fail(PA_ERR_OOM, "pa_bm_append: sequence %lld needs %lld blocks, %lld free", (long long)seq,
+                (long long)need, (long long)bm->capacity());
   }
   int32_t dummy[2];
   bm->append_unchecked(seq, n_new, slots_out, cow_pairs_out ? cow_pairs_out : dummy, n_cow_out);
@@ -193,10 +312,10 @@ extern "C" pa_status pa_bm_append_step(pa_bm* bm, const int64_t* seqs, int32_t n
     auto it = bm->seqs.find(seqs[i]);
     need += bm->needs(it == bm->seqs.end() ? nullptr : &it->second, 1, delta);
   }
-  if (need > (int64_t)bm->dev.free_stack.size()) {
+  if (need > bm->capacity()) {
     bm->alloc_failures += 1;
-    return fail(PA_ERR_OOM, "pa_bm_append_step: step needs %lld blocks, %zu free", (long long)need,
-                bm->dev.free_stack.size());
+    return fail(PA_ERR_OOM, "pa_bm_append_step: step needs %lld blocks, %lld free", (long long)need,
+                (long long)bm->capacity());
   }
   for (int32_t i = 0; i < num; ++i)
     bm->append_unchecked(seqs[i], 1, slots_out + i, cow_pairs_out, n_cow_out);
@@ -223,7 +342,7 @@ extern "C" pa_status pa_bm_free(pa_bm* bm, int64_t seq) {
     bm->host.release(it->second.table);
     bm->num_swapped -= 1;
   } else {
-    bm->dev.release(it->second.table);
+    bm->release_dev(it->second.table);
   }
   bm->seqs.erase(it);
   return PA_OK;
@@ -329,7 +448,7 @@ extern "C" void pa_bm_get_stats(const pa_bm* bm, pa_bm_stats* out) {
   std::memset(out, 0, sizeof(*out));
   out->num_blocks = bm->num_blocks;
   out->free_blocks = (int32_t)bm->dev.free_stack.size();
-  out->used_blocks = bm->num_blocks - out->free_blocks;
+  out->used_blocks = bm->num_blocks - out->free_blocks - (int32_t)bm->evictable.size();
   out->num_seqs = (int32_t)bm->seqs.size();
   for (const auto& kv : bm->seqs) out->logical_tokens += kv.second.len;
   for (int32_t c : bm->dev.refcount) out->shared_blocks += c > 1;
@@ -340,6 +459,10 @@ extern "C" void pa_bm_get_stats(const pa_bm* bm, pa_bm_stats* out) {
   out->swapped_seqs = bm->num_swapped;
   out->swap_out_blocks = bm->swap_out_blocks;
   out->swap_in_blocks = bm->swap_in_blocks;
+  out->cached_blocks = (int32_t)bm->cached.size();
+  out->evictable_blocks = (int32_t)bm->evictable.size();
+  out->prefix_query_tokens = bm->prefix_query_tokens;
+  out->prefix_hit_tokens = bm->prefix_hit_tokens;
 }
 
 namespace {
@@ -367,6 +490,14 @@ pa_status check_pool(const pa_bm* bm, const pa_bm::Pool& pool, bool swapped, con
       return fail(PA_ERR_INVALID, "pa_bm_check: %s block %d is on the free list twice or out of range", what, b);
     is_free[b] = 1;
   }
+  if (!swapped) {
+    for (const auto& e : bm->evictable) {
+      const int32_t b = e.second;
+      if (b < 0 || b >= n || is_free[b] || bm->tick_of[b] != e.first)
+        return fail(PA_ERR_INVALID, "pa_bm_check: evictable block %d is free, out of range or misranked", b);
+      is_free[b] = 2;
+    }
+  }
   for (int32_t b = 0; b < n; ++b) {
     if (named[b] != pool.refcount[b])
       return fail(PA_ERR_INVALID, "pa_bm_check: %s block %d count %d but %d tables name it", what, b,
@@ -378,12 +509,44 @@ pa_status check_pool(const pa_bm* bm, const pa_bm::Pool& pool, bool swapped, con
   return PA_OK;
 }
 
+// The prefix cache's own invariants: entries and the hash index agree, every
+// entry's parent is cached and lists it as a child, a cached block has count
+// zero exactly when it is evictable, and only cached blocks are evictable.
+pa_status check_cache(const pa_bm* bm) {
+  if (bm->index.size() != bm->cached.size())
+    return fail(PA_ERR_INVALID, "pa_bm_check: %zu index entries for %zu cached blocks", bm->index.size(),
+                bm->cached.size());
+  for (const auto& kv : bm->cached) {
+    const int32_t b = kv.first;
+    const auto& c = kv.second;
+    if ((int32_t)c.tokens.size() != bm->block_size || c.hash != bm->key_hash(c.parent, c.tokens.data()) ||
+        bm->lookup(c.parent, c.tokens.data()) != b)
+      return fail(PA_ERR_INVALID, "pa_bm_check: cached block %d is not found by its own key", b);
+    if (c.parent >= 0) {
+      auto p = bm->cached.find(c.parent);
+      if (p == bm->cached.end() ||
+          std::count(p->second.children.begin(), p->second.children.end(), b) != 1)
+        return fail(PA_ERR_INVALID, "pa_bm_check: cached block %d has no cached parent listing it", b);
+    }
+    for (int32_t ch : c.children)
+      if (!bm->cached.count(ch) || bm->cached.at(ch).parent != b)
+        return fail(PA_ERR_INVALID, "pa_bm_check: cached block %d lists a stale child %d", b, ch);
+    if ((bm->dev.refcount[b] == 0) != (bm->tick_of[b] >= 0))
+      return fail(PA_ERR_INVALID, "pa_bm_check: cached block %d count %d but %sevictable", b, bm->dev.refcount[b],
+                  bm->tick_of[b] >= 0 ? "" : "not ");
+  }
+  for (int32_t b = 0; b < bm->num_blocks; ++b)
+    if (bm->tick_of[b] >= 0 && !bm->cached.count(b))
+      return fail(PA_ERR_INVALID, "pa_bm_check: block %d is evictable but not cached", b);
+  return PA_OK;
+}
+
 // Copy the distinct blocks of the listed tables from pool `src` to pool
 // `dst` (one destination block each, in batch and table order), point the
 // tables at the copies and retire the source tables.  The caller has checked
 // states, distinctness and capacity.
-void move_tables(pa_bm* bm, const std::vector<pa_bm::Seq*>& list, pa_bm::Pool& src, pa_bm::Pool& dst,
-                 bool to_host, int32_t* pairs) {
+void move_tables(pa_bm* bm, const std::vector<pa_bm::Seq*>& list, pa_bm::Pool& dst, bool to_host,
+                 int32_t* pairs) {
   std::unordered_map<int32_t, int32_t> mapping;
   int32_t n = 0;
   std::vector<std::vector<int32_t>> old(list.size());
@@ -393,8 +556,14 @@ void move_tables(pa_bm* bm, const std::vector<pa_bm::Seq*>& list, pa_bm::Pool& s
     for (int32_t& b : s->table) {
       auto ins = mapping.emplace(b, -1);
       if (ins.second) {
-        const int32_t d = dst.free_stack.back();
-        dst.free_stack.pop_back();
+        int32_t d;
+        if (to_host) {
+          d = dst.free_stack.back();
+          dst.free_stack.pop_back();
+        } else {
+          d = bm->pop();
+          dst.refcount[d] = 0;
+        }
         ins.first->second = d;
         pairs[2 * n] = b;
         pairs[2 * n + 1] = d;
@@ -405,7 +574,12 @@ void move_tables(pa_bm* bm, const std::vector<pa_bm::Seq*>& list, pa_bm::Pool& s
     }
     s->swapped = to_host;
   }
-  for (const auto& t : old) src.release(t);
+  for (const auto& t : old) {
+    if (to_host)
+      bm->release_dev(t);
+    else
+      bm->host.release(t);
+  }
   bm->num_swapped += to_host ? (int32_t)list.size() : -(int32_t)list.size();
 }
 
@@ -429,15 +603,15 @@ pa_status swap(pa_bm* bm, const int64_t* seqs, int32_t num, int32_t* pairs_out, 
     list[i] = &it->second;
     for (int32_t b : it->second.table) distinct.emplace(b, 0);
   }
-  pa_bm::Pool& src = to_host ? bm->dev : bm->host;
   pa_bm::Pool& dst = to_host ? bm->host : bm->dev;
   const int64_t need = (int64_t)distinct.size();
-  if (need > (int64_t)dst.free_stack.size())
-    return fail(PA_ERR_OOM, "%s: %lld blocks to copy, %zu free %s blocks", who, (long long)need,
-                dst.free_stack.size(), to_host ? "host" : "device");
+  const int64_t room = to_host ? (int64_t)bm->host.free_stack.size() : bm->capacity();
+  if (need > room)
+    return fail(PA_ERR_OOM, "%s: %lld blocks to copy, %lld free %s blocks", who, (long long)need, (long long)room,
+                to_host ? "host" : "device");
   if (need > cap_pairs)
     return fail(PA_ERR_INVALID, "%s: %lld pairs due, cap_pairs is %d", who, (long long)need, cap_pairs);
-  move_tables(bm, list, src, dst, to_host, pairs_out);
+  move_tables(bm, list, dst, to_host, pairs_out);
   *n_pairs_out = (int32_t)need;
   (to_host ? bm->swap_out_blocks : bm->swap_in_blocks) += need;
   return PA_OK;
@@ -473,6 +647,72 @@ extern "C" int32_t pa_bm_host_refcount(const pa_bm* bm, int32_t host_block) {
   return bm->host.refcount[host_block];
 }
 
+extern "C" pa_status pa_bm_enable_prefix_cache(pa_bm* bm) {
+  if (!bm) return fail(PA_ERR_INVALID, "pa_bm_enable_prefix_cache: null manager");
+  if (!bm->seqs.empty())
+    return fail(PA_ERR_INVALID, "pa_bm_enable_prefix_cache: enable it before any sequence exists");
+  bm->prefix_cache = true;
+  return PA_OK;
+}
+
+extern "C" pa_status pa_bm_append_prompt(pa_bm* bm, int64_t seq, const int32_t* tokens, int32_t n,
+                                         int64_t* slots_out, int32_t* n_cached_out) {
+  if (!bm || n < 0 || (n > 0 && (!tokens || !slots_out)) || !n_cached_out)
+    return fail(PA_ERR_INVALID, "pa_bm_append_prompt: bad arguments");
+  *n_cached_out = 0;
+  if (!bm->prefix_cache) return fail(PA_ERR_INVALID, "pa_bm_append_prompt: the prefix cache is not enabled");
+  if (bm->seqs.count(seq)) return fail(PA_ERR_INVALID, "pa_bm_append_prompt: sequence %lld exists", (long long)seq);
+  const int32_t B = bm->block_size;
+  const int64_t blocks = ((int64_t)n + B - 1) / B;
+  // Leading full blocks already cached, at most (n - 1) / B of them: the
+  // prompt's last token is always computed.
+  std::vector<int32_t> hits;
+  int32_t parent = -1;
+  int64_t revived = 0;
+  for (int64_t j = 0; n > 0 && j < (n - 1) / B; ++j) {
+    const int32_t b = bm->lookup(parent, tokens + j * B);
+    if (b < 0) break;
+    hits.push_back(b);
+    revived += bm->dev.refcount[b] == 0;
+    parent = b;
+  }
+  const int64_t need = blocks - (int64_t)hits.size();
+  if (need > bm->capacity() - revived) {
+    bm->alloc_failures += 1;
+    return fail(PA_ERR_OOM, "pa_bm_append_prompt: sequence %lld needs %lld blocks, %lld free", (long long)seq,
+                (long long)need, (long long)(bm->capacity() - revived));
+  }
+  bm->prefix_query_tokens += n;
+  bm->prefix_hit_tokens += (int64_t)hits.size() * B;
+  for (int32_t b : hits) {
+    if (bm->tick_of[b] >= 0) {
+      bm->evictable.erase({bm->tick_of[b], b});
+      bm->tick_of[b] = -1;
+    }
+    bm->dev.refcount[b] += 1;
+  }
+  pa_bm::Seq s;
+  s.table = hits;
+  s.len = n;
+  while ((int64_t)s.table.size() < blocks) s.table.push_back(bm->pop());
+  // The prompt's new full blocks become cached (unless that content already is).
+  for (int64_t j = (int64_t)hits.size(); j < n / B; ++j) {
+    const int32_t par = j ? s.table[j - 1] : -1;
+    if ((par < 0 || bm->cached.count(par)) && bm->lookup(par, tokens + j * B) < 0)
+      bm->insert_cached(s.table[j], par, tokens + j * B);
+  }
+  const int64_t cached_tokens = (int64_t)hits.size() * B;
+  for (int64_t t = 0; t < n; ++t) slots_out[t] = t < cached_tokens ? -1 : (int64_t)s.table[t / B] * B + t % B;
+  bm->seqs.emplace(seq, std::move(s));
+  *n_cached_out = (int32_t)cached_tokens;
+  return PA_OK;
+}
+
+extern "C" int32_t pa_bm_cached(const pa_bm* bm, int32_t block) {
+  if (!bm || block < 0 || block >= bm->num_blocks) return -1;
+  return bm->cached.count(block) ? 1 : 0;
+}
+
 extern "C" pa_status pa_bm_check(const pa_bm* bm) {
   if (!bm) return fail(PA_ERR_INVALID, "pa_bm_check: null manager");
   int32_t swapped = 0;
@@ -480,5 +720,6 @@ extern "C" pa_status pa_bm_check(const pa_bm* bm) {
   if (swapped != bm->num_swapped)
     return fail(PA_ERR_INVALID, "pa_bm_check: %d swapped sequences, counter says %d", swapped, bm->num_swapped);
   if (pa_status st = check_pool(bm, bm->dev, false, "device")) return st;
-  return check_pool(bm, bm->host, true, "host");
+  if (pa_status st = check_pool(bm, bm->host, true, "host")) return st;
+  return check_cache(bm);
 }

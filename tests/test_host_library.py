@@ -211,6 +211,128 @@ def test_block_manager_swaps_match_model(seed):
         _compare_swaps(bm, model, live)
 
 
+def _compare_cache(bm: pk.BlockManager, model: oracle.BlockManagerModel, live):
+    _compare_swaps(bm, model, live)
+    for b in range(model.num_blocks):
+        assert bm.is_cached(b) == model.is_cached(b), b
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_prefix_cache_matches_model(seed):
+    """Prompts drawn from a small vocabulary after one of a few system
+    prompts (so that blocks repeat), plus appends, forks, swaps and frees:
+    same slots, reuse counts, tables, counts, cache membership and failures
+    as the model, operation by operation."""
+    rng = np.random.default_rng(200 + seed)
+    b = int(rng.choice([1, 2, 4, 8, 16]))
+    nb = int(rng.integers(6, 70))
+    order = rng.permutation(nb) if seed % 2 else None
+    bm = pk.BlockManager(nb, b, order)
+    model = oracle.BlockManagerModel(nb, b, order)
+    bm.enable_prefix_cache()
+    model.enable_prefix_cache()
+    nh = int(rng.integers(0, 40))
+    bm.set_host_blocks(nh)
+    model.set_host_blocks(nh)
+    vocab = int(rng.integers(2, 5))
+    systems = [list(rng.integers(0, vocab, size=int(rng.integers(0, 4 * b + 2)))) for _ in range(3)]
+    live, nxt = [], 0
+    for _ in range(300):
+        resident = [s for s in live if not model.is_swapped(s)]
+        swapped = [s for s in live if model.is_swapped(s)]
+        op = int(rng.integers(0, 8))
+        if op <= 2 or not live:
+            prompt = systems[int(rng.integers(0, 3))] + list(rng.integers(0, vocab, size=int(rng.integers(0, 3 * b))))
+            m_ok = p_ok = True
+            try:
+                ms, mc = model.append_prompt(nxt, prompt)
+            except oracle.OutOfBlocks:
+                m_ok = False
+            try:
+                ps, pc = bm.append_prompt(nxt, prompt)
+            except pk.PaError as e:
+                assert e.status == -3
+                p_ok = False
+            assert m_ok == p_ok
+            if m_ok:
+                assert ps.tolist() == ms and pc == mc
+                live.append(nxt)
+                nxt += 1
+        elif op == 3 and resident:
+            s = int(rng.choice(resident))
+            n = int(rng.integers(0, 2 * b))
+            m_ok = p_ok = True
+            try:
+                ms, mc = model.append(s, n)
+            except oracle.OutOfBlocks:
+                m_ok = False
+            try:
+                ps, pc = bm.append(s, n)
+            except pk.PaError:
+                p_ok = False
+            assert m_ok == p_ok
+            if m_ok:
+                assert ps.tolist() == ms and [tuple(x) for x in pc.tolist()] == mc
+        elif op == 4 and resident:
+            parent = int(rng.choice(resident))
+            model.fork(parent, nxt)
+            bm.fork(parent, nxt)
+            live.append(nxt)
+            nxt += 1
+        elif op == 5 and (resident or swapped):
+            out = bool(resident) and (not swapped or rng.random() < 0.5)
+            pick = [int(rng.choice(resident if out else swapped))]
+            m_fn, p_fn = (model.swap_out, bm.swap_out) if out else (model.swap_in, bm.swap_in)
+            m_ok = p_ok = True
+            try:
+                mp = m_fn(pick)
+            except oracle.OutOfBlocks:
+                m_ok = False
+            try:
+                pp = p_fn(pick)
+            except pk.PaError as e:
+                assert e.status == -3
+                p_ok = False
+            assert m_ok == p_ok
+            if m_ok:
+                assert [tuple(x) for x in pp.tolist()] == mp
+        elif op >= 6 and live:
+            s = int(rng.choice(live))
+            model.free_seq(s)
+            bm.free(s)
+            live.remove(s)
+        bm.check()
+        model.check()
+        _compare_cache(bm, model, live)
+    assert model.stats()["prefix_hit_tokens"] > 0
+
+
+def test_prefix_cache_errors_through_the_library():
+    bm = pk.BlockManager(8, 4)
+    with pytest.raises(pk.PaError) as e:
+        bm.append_prompt(0, [1, 2])               # cache off
+    assert e.value.status == -1
+    bm.append(0, 1)
+    with pytest.raises(pk.PaError) as e:
+        bm.enable_prefix_cache()                  # a sequence exists
+    assert e.value.status == -1
+    bm.free(0)
+    bm.enable_prefix_cache()
+    assert bm.append_prompt(0, [1, 2, 3, 4, 5])[1] == 0
+    with pytest.raises(pk.PaError) as e:
+        bm.append_prompt(0, [1, 2])               # sequence exists
+    assert e.value.status == -1
+    slots, cached = bm.append_prompt(1, [1, 2, 3, 4, 6])
+    assert cached == 4 and slots.tolist()[:4] == [-1] * 4
+    assert bm.append_prompt(2, [])[1] == 0 and bm.length(2) == 0
+    assert bm.is_cached(0) and not bm.is_cached(1) and lib_cached(bm, 8) == -1
+    bm.check()
+
+
+def lib_cached(bm, block):
+    return _lib.lib.pa_bm_cached(bm._h, block)
+
+
 def test_block_manager_swap_errors():
     bm = pk.BlockManager(8, 4)
     bm.set_host_blocks(2)
