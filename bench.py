@@ -53,6 +53,9 @@ WORKLOADS = {
           "lengths U[16384,32768]",
     "c5": "prefix sharing bf16: 32 prompts x 4 samples sharing a 2000-token prefix, private tails U[1,512], "
           "32 q / 8 KV heads, head_dim 128; the step where the samples diverge",
+    "c6": "prefix cache across requests bf16: 256 requests opening with one of 4 shared 2000-token system "
+          "prompts, private user turns U[1,400], 32 q / 8 KV heads, head_dim 128; admitted through the prefix "
+          "cache, decoded with the cascade plan",
 }
 PMC_FILE = os.path.join(ROOT, "profiles", "decode_c3_pmc.json")
 KERNEL_SRC = os.path.join(ROOT, "paged_kv_cache_115_amd", "csrc", "decode_kernels.hip")
@@ -174,6 +177,54 @@ def prefix_workload(pk, block_size: int) -> dict:
                 nb=case["num_blocks"], tables=tables, lens=lens, slots=slots,
                 cows=np.asarray(fork_cows, dtype=np.int32).reshape(-1, 2), host_append_us=host_append_us,
                 unique_tokens=int(sum(used.values())), shared_kv=bm.stats()["shared_blocks"] > 0)
+
+
+def prefix_cache_workload(pk, block_size: int) -> dict:
+    """Requests that share system prompts, admitted through the prefix cache
+    (pa_bm_append_prompt: the second request of a system prompt onwards reuses
+    its blocks), then one decode step: every request appends one token and
+    attends over its prompt + 1.  Shared system-prompt blocks are read once per
+    prefix group of the cascade plan."""
+    case = synth.prefix_cache_case("c6")
+    cfg = case["cfg"]
+    prompts = case["prompts"]
+    B, S = block_size, len(prompts)
+    private_blocks = sum(-(-(len(p) + 1) // B) for p in prompts)
+    nb = private_blocks + S
+    bm = pk.BlockManager(nb, B, np.random.default_rng(cfg["seed"]).permutation(nb).astype(np.int32))
+    bm.enable_prefix_cache()
+    t0 = time.perf_counter()
+    for r, p in enumerate(prompts):
+        bm.append_prompt(r, p)
+    host_prompt_us = (time.perf_counter() - t0) * 1e6 / S
+    st = bm.stats()
+    seqs = np.arange(S)
+    t0 = time.perf_counter()
+    slots, cows = bm.append_step(seqs)
+    host_append_us = (time.perf_counter() - t0) * 1e6
+    lens_np = np.array([len(p) + 1 for p in prompts], dtype=np.int32)
+    maxb = int(max(-(-int(L) // B) for L in lens_np))
+    tables, lens = bm.export(seqs, maxb)
+    assert np.array_equal(lens, lens_np)
+    used = {}
+    for s in range(S):
+        nblk = -(-int(lens[s]) // B)
+        for j, blk in enumerate(tables[s, :nblk]):
+            fill = B if j < nblk - 1 else int(lens[s]) - j * B
+            used[int(blk)] = max(used.get(int(blk), 0), fill)
+    group, prefix_tokens = bm.prefix_groups(seqs)
+    desc = WORKLOADS["c6"] if B == 16 else WORKLOADS["c6"].replace("head_dim 128;", f"head_dim 128, block {B};")
+    return dict(name="c6", desc=desc, case=dict(q=case["q"], scale=case["scale"]), prefix_group=group,
+                prefix_tokens=prefix_tokens, seed=cfg["seed"], S=S, hq=cfg["num_q_heads"], hkv=cfg["num_kv_heads"],
+                d=cfg["head_dim"], B=B, nb=nb, tables=tables, lens=lens, slots=slots,
+                cows=np.asarray(cows, dtype=np.int32).reshape(-1, 2), host_append_us=host_append_us,
+                unique_tokens=int(sum(used.values())), shared_kv=True,
+                prefix_cache={"host_prompt_us_per_request": round(host_prompt_us, 2),
+                              "prompt_tokens": int(st["prefix_query_tokens"]),
+                              "reused_tokens": int(st["prefix_hit_tokens"]),
+                              "prefill_tokens_to_compute": int(st["prefix_query_tokens"] - st["prefix_hit_tokens"]),
+                              "blocks_held": int(st["used_blocks"]), "blocks_held_private": int(private_blocks - S),
+                              "cached_blocks": int(st["cached_blocks"])})
 
 
 def copy_blocks_probe(torch, pk, B: int, hkv: int, d: int, pairs: int = 4096, reps: int = 20) -> dict:
@@ -308,7 +359,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="c3", choices=sorted(WORKLOADS))
     ap.add_argument("--block-size", type=int, default=None, choices=(8, 16, 32),
-                    help="block size (default: the workload's; c5: 16)")
+                    help="block size (default: the workload's; c5, c6: 16)")
     ap.add_argument("--workgroups", type=int, default=None, help="persistent workgroups (default: fill the GPU)")
     ap.add_argument("--piece", type=int, default=0, help="longest job piece in 16-token tiles (0: auto)")
     ap.add_argument("--schedule", default="auto", choices=("auto", "chunks", "lpt"),
@@ -319,7 +370,7 @@ def main() -> int:
     ap.add_argument("--decode-only", action="store_true", help="time only pa_decode launches (profiling aid)")
     ap.add_argument("--graph", action="store_true", help="replay each step as a captured HIP graph")
     ap.add_argument("--no-cascade", action="store_true",
-                    help="c5: plan every sequence separately instead of reading shared prefixes once per group")
+                    help="c5, c6: plan every sequence separately instead of reading shared prefixes once per group")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="profiling aid: run a plain device-to-device copy of BYTES (the reference whose "
                          "counter readings calibrate the traffic figures) and exit")
@@ -343,6 +394,8 @@ def main() -> int:
     torch.cuda.set_device(0)
     if args.config == "c5":
         w = prefix_workload(pk, args.block_size or 16)
+    elif args.config == "c6":
+        w = prefix_cache_workload(pk, args.block_size or 16)
     else:
         w = decode_workload(pk, args.config, args.block_size)
     name, case = w["name"], w["case"]
@@ -498,6 +551,8 @@ def main() -> int:
                      "kernel": "decode_bf16_kernel (the attention launch of pa_decode)",
                      "bytes_per_launch": kv_bytes},
     }
+    if "prefix_cache" in w:
+        result["prefix_cache"] = w["prefix_cache"]
     if not args.decode_only:
         result["copy_blocks_probe"] = copy_blocks_probe(torch, pk, B, hkv, d)
     if not args.no_cpu_baseline:

@@ -250,21 +250,24 @@ def _splitmix64(x: int) -> int:
     return x ^ (x >> 31)
 
 
-def token_rows(tokens, hkv: int, d: int, dtype: str, salt: int = 0):
+def token_rows(tokens, hkv: int, d: int, dtype: str, salt: int = 0, start: int = 0):
     """Stand-in for a model's keys and values of a token sequence: row t is
     drawn from a generator seeded by the whole prefix tokens[:t+1] (a rolling
     64-bit state), so two sequences get bit-identical rows exactly where
-    their prefixes agree.  Returns (keys, values) [n, Hkv, D]."""
+    their prefixes agree.  Returns (keys, values) [n - start, Hkv, D] for
+    positions start .. n - 1."""
     n = len(tokens)
-    k = np.empty((n, hkv, d), dtype=np.float32 if dtype == "f32" else np.uint16)
+    k = np.empty((n - start, hkv, d), dtype=np.float32 if dtype == "f32" else np.uint16)
     v = np.empty_like(k)
     state = _splitmix64(salt)
     for t, tok in enumerate(tokens):
         state = _splitmix64(state ^ (int(tok) & 0xFFFFFFFF))
+        if t < start:
+            continue
         x = np.random.default_rng(state).standard_normal(size=(2, hkv, d), dtype=np.float32)
         if dtype != "f32":
             x = f32_to_bf16_bits(x)
-        k[t], v[t] = x[0], x[1]
+        k[t - start], v[t - start] = x[0], x[1]
     return k, v
 
 
@@ -277,6 +280,10 @@ PREFIX_CACHE_CONFIGS: dict[str, dict] = {
                 block_size=16, num_q_heads=32, num_kv_heads=8, head_dim=128, dtype="bf16"),
     "h1f": dict(seed=32, requests=10, system_prompts=3, system_len=(8, 40), user=(1, 20), vocab=7,
                 block_size=8, num_q_heads=8, num_kv_heads=4, head_dim=64, dtype="f32"),
+    # Full size: 256 requests over four 2,000-token system prompts, user turns
+    # averaging 200 tokens, the c3 head layout.
+    "c6": dict(seed=6, requests=256, system_prompts=4, system_len=(2000, 2000), user=(1, 400), vocab=32000,
+               block_size=16, num_q_heads=32, num_kv_heads=8, head_dim=128, dtype="bf16"),
 }
 
 

@@ -93,3 +93,56 @@ def test_full_size_prefix_sharing(pk, b):
     assert np.all(np.isfinite(out))
     stats = assert_close(out[seqs], ref["out"][seqs], "bf16", f"c5 B={b} cascade")
     log(f"  cascade max|err|={stats['max_abs']:.3g} mean|err|={stats['mean_abs']:.3g}")
+
+
+def test_full_size_prefix_cache_requests(pk):
+    """c6 at full size: 256 requests over four 2,000-token system prompts,
+    admitted through the library's prefix cache and the oracle's model side by
+    side (slots, reuse and tables equal; only non-reused rows written; both
+    pools bit-exact), then decoded with the cascade plan that bench.py times
+    and with per-request plans; sampled requests against the oracle."""
+    import oracle
+    from flows import cascade_decode, gpu_decode, to_dev, to_host
+    case = synth.prefix_cache_case("c6")
+    cfg = case["cfg"]
+    b, hkv, d, dt = cfg["block_size"], cfg["num_kv_heads"], cfg["head_dim"], cfg["dtype"]
+    prompts = case["prompts"]
+    S = len(prompts)
+    nb = sum(-(-(len(p) + 1) // b) for p in prompts)
+    order = np.random.default_rng(cfg["seed"]).permutation(nb).astype(np.int32)
+    log(f"c6 full size: {S} requests, {nb} blocks")
+    om = oracle.BlockManagerModel(nb, b, order)
+    om.enable_prefix_cache()
+    bm = pk.BlockManager(nb, b, order)
+    bm.enable_prefix_cache()
+    ok, ov = synth.nan_fill((nb, b, hkv, d), dt), synth.nan_fill((nb, b, hkv, d), dt)
+    kd, vd = to_dev(ok), to_dev(ov)
+    pool = pk.KvPool(kd, vd)
+    for r, p in enumerate(prompts):
+        ms, mc = om.append_prompt(r, p)
+        ps, pc = bm.append_prompt(r, p)
+        assert pc == mc and ps.tolist() == ms, r
+        rk, rv = synth.token_rows(p, hkv, d, dt, start=mc)
+        oracle.reshape_and_cache(ok, ov, rk, rv, np.array(ms[mc:], dtype=np.int64))
+        pk.reshape_and_cache(pool, to_dev(rk), to_dev(rv), to_dev(ps[mc:]))
+    st = bm.stats()
+    assert st["prefix_hit_tokens"] == om.stats()["prefix_hit_tokens"] > 0
+    bm.check()
+    seqs = np.arange(S)
+    maxb = max(len(bm.table(s)) for s in seqs)
+    tables, lens = bm.export(seqs, maxb)
+    for s in seqs:
+        assert tables[s, :len(om.table(s))].tolist() == om.table(s)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(to_host(kd)), bits(ok)) and np.array_equal(bits(to_host(vd)), bits(ov))
+    sample = sample_seqs(pk, lens, hkv, 6)
+    ref = oracle.decode_attention(case["q"], ok, ov, tables, lens, case["scale"], seqs=sample)
+    out, plan = cascade_decode(pk, pool, to_dev(case["q"]), tables, lens, case["scale"], bm, seqs)
+    assert plan.num_groups > 0
+    out = to_host(out)
+    assert np.all(np.isfinite(out))
+    stats = assert_close(out[sample], ref[sample], dt, "c6 cascade")
+    log(f"  cascade max|err|={stats['max_abs']:.3g} mean|err|={stats['mean_abs']:.3g}")
+    out2 = to_host(gpu_decode(pk, pool, to_dev(case["q"]), tables, lens, case["scale"], shared_kv=True))
+    stats = assert_close(out2[sample], ref[sample], dt, "c6 per-request plans")
+    log(f"  per-request max|err|={stats['max_abs']:.3g} mean|err|={stats['mean_abs']:.3g}")
