@@ -299,10 +299,14 @@ class BlockManager:
         self.num_blocks = num_blocks
         self.block_size = block_size
 
+    # Bound once, so that a manager collected at interpreter shutdown (after
+    # module globals are cleared) can still release its handle.
+    _destroy = staticmethod(lib.pa_bm_destroy)
+
     def __del__(self):
         h = getattr(self, "_h", None)
         if h:
-            lib.pa_bm_destroy(h)
+            self._destroy(h)
             self._h = None
 
     def append(self, seq: int, n_new: int = 1):
