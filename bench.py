@@ -374,6 +374,9 @@ def main() -> int:
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="profiling aid: run a plain device-to-device copy of BYTES (the reference whose "
                          "counter readings calibrate the traffic figures) and exit")
+    ap.add_argument("--no-first-blocks", action="store_true",
+                    help="leave the jobs' first-tile table entries out of the plan (the first tile loads then "
+                         "wait for a table load)")
     ap.add_argument("--swap-sweep", action="store_true",
                     help="measure swapping a sequence out to pinned host memory and back at several context "
                          "lengths (both engines) and exit")
@@ -410,6 +413,8 @@ def main() -> int:
     else:
         sched = {"auto": pk.SCHEDULE_AUTO, "chunks": pk.SCHEDULE_CHUNKS, "lpt": pk.SCHEDULE_LPT}[args.schedule]
         plan = pk.decode_plan(lens, hkv, workgroups, args.piece, shared_kv=w["shared_kv"], schedule=sched)
+    if not args.no_first_blocks:
+        plan.set_first_blocks(tables, B)
     host_plan_us = (time.perf_counter() - t0) * 1e6
 
     dev = torch.device("cuda", 0)
@@ -531,7 +536,8 @@ def main() -> int:
                    "jobs": int(plan.num_jobs), "merges": int(plan.num_merges), "records": int(plan.num_records),
                    "pool_replicas": R, "decode_only": bool(args.decode_only), "shared_kv": bool(w["shared_kv"]),
                    "schedule": ["chunks", "largest pieces first"][plan.schedule],
-                   "cascade_prefix_groups": int(plan.num_groups) if cascade else 0},
+                   "cascade_prefix_groups": int(plan.num_groups) if cascade else 0,
+                   "first_tile_entries": not args.no_first_blocks},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "decode_tokens_per_s": round(S / (ms_per_step * 1e-3), 1),
         "kv_bytes_per_step": kv_bytes,

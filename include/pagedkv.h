@@ -204,6 +204,9 @@ typedef struct pa_decode_plan_info {
   int32_t num_groups;     /* prefix-group descriptors (pa_decode_plan_prefix; 0 otherwise) */
   int32_t groups_at;      /* byte offset of pa_decode_group [num_groups] */
   int32_t group_size;     /* largest prefix group planned (members sharing one read of the prefix) */
+  int32_t first_at;       /* byte offset of int32 [jobs_per_workgroup * num_workgroups][4]: per job slot, the
+                             table entries of the job's first two tiles (pa_decode_plan_first_blocks) */
+  int32_t first_block_size; /* block size those entries were written for (0: not written) */
 } pa_decode_plan_info;
 
 /* A job whose head_block field has this bit reads a prefix shared by the
@@ -236,6 +239,23 @@ typedef struct pa_decode_group {
  * every K/V byte is read once and the loads stream past the caches, which is
  * faster when nothing is shared.  Either setting gives identical results. */
 #define PA_DECODE_SHARED_KV 1
+
+/* flags bit, set by pa_decode_plan_first_blocks: the plan holds the table
+ * entries of every job's first two tiles, so the attention launch issues its
+ * first tile loads from the job records without waiting for a table load.
+ * The entries must be those of the tables passed to pa_decode (bf16 pools;
+ * fp32 ignores them). */
+#define PA_DECODE_FIRST_BLOCKS 2
+
+/* Write the first-tile table entries into a plan from the HOST copy of the
+ * block tables pa_decode will read (tables: int32 [num_seqs][max_blocks], the
+ * same rows), for pools of block_size; sets PA_DECODE_FIRST_BLOCKS and
+ * info->first_block_size.  Serving loops export the tables on the host
+ * anyway (pa_bm_export); the entries are only valid for those tables.
+ * PA_ERR_INVALID for an inconsistent info or a job naming a sequence past
+ * num_seqs. */
+pa_status pa_decode_plan_first_blocks(void* plan, pa_decode_plan_info* info, const int32_t* tables,
+                                      int32_t max_blocks, int32_t num_seqs, int32_t block_size);
 
 /* Persistent workgroups that fit the current device at full occupancy (all
  * resident at once): compute units times resident decode workgroups per unit.

@@ -13,11 +13,11 @@ import os
 
 import numpy as np
 
-from ._lib import (LIB_PATH, PA_BF16, PA_DECODE_SHARED_KV, PA_F32, PA_JOB_SHARED, PA_SWAP_ENGINE_MEMCPY,
+from ._lib import (LIB_PATH, PA_BF16, PA_DECODE_FIRST_BLOCKS, PA_DECODE_SHARED_KV, PA_F32, PA_JOB_SHARED, PA_SWAP_ENGINE_MEMCPY,
                    PA_SWAP_ENGINE_KERNEL, PA_SWAP_IN, PA_SWAP_OUT, PaDecodePlanInfo, PaError, PaKvPool, lib)
 
 __all__ = [
-    "LIB_PATH", "PA_F32", "PA_BF16", "PA_DECODE_SHARED_KV", "PA_JOB_SHARED", "PaError", "BlockManager", "KvPool",
+    "LIB_PATH", "PA_F32", "PA_BF16", "PA_DECODE_SHARED_KV", "PA_DECODE_FIRST_BLOCKS", "PA_JOB_SHARED", "PaError", "BlockManager", "KvPool",
     "reshape_and_cache", "copy_blocks", "decode_plan", "decode_workspace_bytes",
     "decode", "DecodePlan", "default_workgroups", "HostKvPool", "swap_blocks", "PA_SWAP_OUT", "PA_SWAP_IN",
     "PA_SWAP_ENGINE_KERNEL", "PA_SWAP_ENGINE_MEMCPY",
@@ -163,6 +163,25 @@ class DecodePlan:
         """int32 [num_merges, 4]: seq, kv_head, num_parts, record_base."""
         n = self.info.num_merges
         return self.blob[self.info.merges_at:self.info.merges_at + 16 * n].view(np.int32).reshape(n, 4)
+
+    def set_first_blocks(self, tables, block_size: int) -> "DecodePlan":
+        """pa_decode_plan_first_blocks: write each job's first-tile table
+        entries from the host tables (int32 [num_seqs, max_blocks]) that
+        pa_decode will read; returns self."""
+        tables = np.ascontiguousarray(tables, dtype=np.int32)
+        if tables.ndim != 2:
+            raise ValueError("tables must be [num_seqs, max_blocks]")
+        _check(lib.pa_decode_plan_first_blocks(self.blob.ctypes.data_as(ctypes.c_void_p), ctypes.byref(self.info),
+                                               tables.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                               tables.shape[1], tables.shape[0], block_size),
+               "pa_decode_plan_first_blocks")
+        return self
+
+    def first_blocks(self) -> np.ndarray:
+        """int32 [jobs_per_workgroup, num_workgroups, 4]: first-tile table entries."""
+        n = self.info.jobs_per_workgroup * self.info.num_workgroups
+        return self.blob[self.info.first_at:self.info.first_at + 16 * n].view(np.int32).reshape(
+            self.info.jobs_per_workgroup, self.info.num_workgroups, 4)
 
     def to_device(self, device="cuda"):
         import torch

@@ -9,6 +9,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedkv.
 PA_F32 = 0
 PA_BF16 = 1
 PA_DECODE_SHARED_KV = 1
+PA_DECODE_FIRST_BLOCKS = 2
 PA_JOB_SHARED = 1 << 16
 PA_SWAP_OUT = 0
 PA_SWAP_IN = 1
@@ -34,7 +35,8 @@ class PaDecodePlanInfo(ctypes.Structure):
                 ("num_kv_heads", ctypes.c_int32), ("jobs_per_workgroup", ctypes.c_int32),
                 ("jobs_at", ctypes.c_int32), ("merges_at", ctypes.c_int32), ("bytes", ctypes.c_int32),
                 ("flags", ctypes.c_int32), ("schedule", ctypes.c_int32), ("num_groups", ctypes.c_int32),
-                ("groups_at", ctypes.c_int32), ("group_size", ctypes.c_int32)]
+                ("groups_at", ctypes.c_int32), ("group_size", ctypes.c_int32), ("first_at", ctypes.c_int32),
+                ("first_block_size", ctypes.c_int32)]
 
 
 class PaBmStats(ctypes.Structure):
@@ -82,6 +84,7 @@ SIGNATURES = {
     "pa_decode_plan_schedule": (_i32, [_p32, _i32, _i32, _i32, _i32, _i32, _vp, _sz, ctypes.POINTER(PaDecodePlanInfo)]),
     "pa_decode_plan_prefix": (_i32, [_p32, _i32, _i32, _i32, _i32, _i32, _p32, _p32, _vp, _sz,
                                      ctypes.POINTER(PaDecodePlanInfo)]),
+    "pa_decode_plan_first_blocks": (_i32, [_vp, ctypes.POINTER(PaDecodePlanInfo), _p32, _i32, _i32, _i32]),
     "pa_decode_workspace_bytes": (_sz, [ctypes.POINTER(PaDecodePlanInfo), _i32, _i32]),
     "pa_decode": (_i32, _DECODE_ARGS),
     "pa_decode_attention": (_i32, _DECODE_ARGS),

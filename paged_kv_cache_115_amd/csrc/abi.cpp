@@ -6,6 +6,7 @@
 
 #include <algorithm>
 #include <cstring>
+#include <queue>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -506,10 +507,18 @@ pa_status schedule_prefix(const int32_t* lens, int32_t num_seqs, int32_t num_kv_
 
 // Largest pieces first: each sequence's tiles are cut into near-equal pieces
 // of at most `cap` tiles (cap = 0: the average tiles per workgroup, clamped to
-// [4, 64]); one job per (piece, head block); jobs, largest first, go to the
-// least-loaded workgroup (by tiles).  Fewer, larger jobs than the chunks when
-// most sequences fit in one workgroup's share.  Records are per sequence: KV
-// head g, piece p at base + g * parts + p.
+// [4, 64]); one job per (piece, head block).  Fewer, larger jobs than the
+// chunks when most sequences fit in one workgroup's share.  Records are per
+// sequence: KV head g, piece p at base + g * parts + p.
+//
+// Placement balances compute units, not workgroups.  With two resident
+// workgroups per CU (the default grid), the dispatcher places workgroup b and
+// b + nwg/2 on the same CU, and each SIMD of that CU runs one wavefront of
+// each: a CU's time follows the tiles of both.  So, for an even grid, jobs
+// (largest first) go to the least-loaded pair {b, b + nwg/2} (by tiles; ties
+// to the pair that reached that load first, initially by index), and each
+// pair's jobs, in that order, go to the lighter of its two workgroups (ties
+// to b).  An odd grid places jobs on the least-loaded workgroup directly.
 pa_status schedule_lpt(const int32_t* lens, int32_t num_seqs, int32_t num_kv_heads, int64_t nwg_req,
                        int64_t cap_req, Schedule& out) {
   const int64_t head_blocks = (num_kv_heads + 3) / 4;
@@ -545,41 +554,31 @@ pa_status schedule_lpt(const int32_t* lens, int32_t num_seqs, int32_t num_kv_hea
   // Jobs by tile count, largest first, ties in generation order (a counting
   // sort: counts are 1..cap).
   std::vector<int32_t> order(jobs.size());
-  int64_t job_tiles = 0;
   {
     std::vector<int32_t> start(cap + 2, 0);
-    for (const pa_decode_job& j : jobs) {
-      start[cap - j.tile_count + 1] += 1;
-      job_tiles += j.tile_count;
-    }
+    for (const pa_decode_job& j : jobs) start[cap - j.tile_count + 1] += 1;
     for (int64_t c = 1; c <= cap + 1; ++c) start[c] += start[c - 1];
     for (size_t i = 0; i < jobs.size(); ++i) order[start[cap - jobs[i].tile_count]++] = (int32_t)i;
   }
-  // Least-loaded workgroup by a bucket queue over load values: loads only
-  // grow, so the smallest non-empty bucket is found by a pointer that only
-  // moves forward.  Workgroups of equal load leave in arrival order
-  // (initially by index).
   std::vector<int32_t> owner(jobs.size());
   {
-    const int64_t max_load = job_tiles / nwg + cap + 1;
-    std::vector<int32_t> head(max_load + 1, -1), tail(max_load + 1, -1), next(nwg, -1);
-    for (int64_t w = 0; w + 1 < nwg; ++w) next[w] = (int32_t)(w + 1);
-    head[0] = 0;
-    tail[0] = (int32_t)(nwg - 1);
-    int64_t cur = 0;
+    const bool paired = nwg % 2 == 0;
+    const int64_t bins = paired ? nwg / 2 : nwg;
+    // (load, arrival, bin): the least-loaded bin first, then the earliest arrival.
+    typedef std::pair<std::pair<int64_t, int64_t>, int32_t> Entry;
+    std::priority_queue<Entry, std::vector<Entry>, std::greater<Entry>> heap;
+    for (int64_t b = 0; b < bins; ++b) heap.push(Entry({0, b}, (int32_t)b));
+    int64_t arrival = bins;
+    std::vector<int64_t> wg_load(nwg, 0);
     for (int32_t j : order) {
-      while (head[cur] < 0) ++cur;
-      const int32_t w = head[cur];
-      head[cur] = next[w];
-      if (head[cur] < 0) tail[cur] = -1;
+      const Entry e = heap.top();
+      heap.pop();
+      const int32_t b = e.second;
+      int32_t w = b;
+      if (paired && wg_load[b + bins] < wg_load[b]) w = (int32_t)(b + bins);
       owner[j] = w;
-      const int64_t nl = cur + jobs[j].tile_count;
-      next[w] = -1;
-      if (tail[nl] < 0)
-        head[nl] = w;
-      else
-        next[tail[nl]] = w;
-      tail[nl] = w;
+      wg_load[w] += jobs[j].tile_count;
+      heap.push(Entry({e.first.first + jobs[j].tile_count, arrival++}, b));
     }
   }
   out.pieces.reserve(jobs.size());
@@ -643,7 +642,11 @@ pa_status emit_plan(const Schedule& sc, int32_t schedule_id, int32_t num_kv_head
   in.num_groups = (int32_t)sc.groups.size();
   in.groups_at = (int32_t)round_up((size_t)in.merges_at + sizeof(pa_decode_merge) * merges.size(), 64);
   in.group_size = sc.group_size;
-  const size_t bytes = (size_t)in.groups_at + sizeof(pa_decode_group) * sc.groups.size();
+  // First-tile table entries: 4 int32 per job slot, written by
+  // pa_decode_plan_first_blocks when the caller has the tables on the host.
+  in.first_at = (int32_t)round_up((size_t)in.groups_at + sizeof(pa_decode_group) * sc.groups.size(), 64);
+  in.first_block_size = 0;
+  const size_t bytes = (size_t)in.first_at + 16 * table.size();
   if (bytes > (size_t)INT32_MAX) return fail(PA_ERR_INVALID, "pa_decode_plan: plan too large");
   in.bytes = (int32_t)bytes;
   *info = in;
@@ -738,6 +741,43 @@ extern "C" pa_status pa_decode_plan_schedule(const int32_t* context_lens, int32_
                             plan, capacity, info);
 }
 
+extern "C" pa_status pa_decode_plan_first_blocks(void* plan, pa_decode_plan_info* info, const int32_t* tables,
+                                                int32_t max_blocks, int32_t num_seqs, int32_t block_size) {
+  const char* who = "pa_decode_plan_first_blocks";
+  if (!plan || !info) return fail(PA_ERR_INVALID, "%s: plan or info is NULL", who);
+  if (block_size != 8 && block_size != 16 && block_size != 32)
+    return fail(PA_ERR_UNSUPPORTED, "%s: block_size %d (supported: 8, 16, 32)", who, block_size);
+  const int64_t slots = (int64_t)info->jobs_per_workgroup * info->num_workgroups;
+  if (info->jobs_at != 0 || info->first_at % 64 != 0 || slots < 0 ||
+      (int64_t)info->first_at < 32 * slots || (int64_t)info->bytes < (int64_t)info->first_at + 16 * slots)
+    return fail(PA_ERR_INVALID, "%s: inconsistent plan info", who);
+  if (slots > 0 && (!tables || max_blocks <= 0 || num_seqs <= 0))
+    return fail(PA_ERR_INVALID, "%s: tables, max_blocks and num_seqs are needed", who);
+  const pa_decode_job* jobs = reinterpret_cast<const pa_decode_job*>(static_cast<const char*>(plan) + info->jobs_at);
+  int32_t* first = reinterpret_cast<int32_t*>(static_cast<char*>(plan) + info->first_at);
+  const int64_t tiles_per_block = block_size >= 16 ? block_size / 16 : 1;
+  for (int64_t i = 0; i < slots; ++i) {
+    const pa_decode_job& j = jobs[i];
+    int32_t* f = first + 4 * i;
+    f[0] = f[1] = f[2] = f[3] = 0;
+    if (j.tile_count <= 0) continue;
+    if (j.seq < 0 || j.seq >= num_seqs)
+      return fail(PA_ERR_INVALID, "%s: job slot %lld names sequence %d of %d", who, (long long)i, j.seq, num_seqs);
+    const int32_t* row = tables + (int64_t)j.seq * max_blocks;
+    // The entries the kernel's table registers would hold for tiles 0 and 1
+    // of the job (index clamped into the row, as there).
+    for (int64_t k = 0; k < 2; ++k) {
+      const int64_t t = (int64_t)std::max(j.tile_begin, 0) + k;
+      const int64_t e0 = block_size == 8 ? 2 * t : t / tiles_per_block;
+      f[k] = row[std::min<int64_t>(std::max<int64_t>(e0, 0), max_blocks - 1)];
+      f[2 + k] = block_size == 8 ? row[std::min<int64_t>(e0 + 1, max_blocks - 1)] : 0;
+    }
+  }
+  info->first_block_size = block_size;
+  info->flags |= PA_DECODE_FIRST_BLOCKS;
+  return PA_OK;
+}
+
 extern "C" size_t pa_decode_workspace_bytes(const pa_decode_plan_info* info, int32_t num_q_heads,
                                             int32_t head_dim) {
   if (!info || info->num_records <= 0 || num_q_heads <= 0 || head_dim <= 0 || info->num_kv_heads <= 0) return 0;
@@ -785,7 +825,17 @@ pa_status decode_stages(int stages, const char* who, const pa_kv_pool* pool, con
     return fail(PA_ERR_INVALID, "%s: new_key and new_value must both be given or both be NULL", who);
   if (new_key && (!pagedkv::aligned(new_key, 16) || !pagedkv::aligned(new_value, 16)))
     return fail(PA_ERR_INVALID, "%s: new_key/new_value must be 16-byte aligned", who);
-  if (info->flags & ~PA_DECODE_SHARED_KV) return fail(PA_ERR_INVALID, "%s: unknown plan flags 0x%x", who, info->flags);
+  if (info->flags & ~(PA_DECODE_SHARED_KV | PA_DECODE_FIRST_BLOCKS))
+    return fail(PA_ERR_INVALID, "%s: unknown plan flags 0x%x", who, info->flags);
+  const bool first_blocks = (info->flags & PA_DECODE_FIRST_BLOCKS) != 0;
+  if (first_blocks && (info->first_block_size != pool->block_size || info->first_at % 64 != 0 ||
+                       (int64_t)info->first_at < (int64_t)info->groups_at + 64 * (int64_t)info->num_groups ||
+                       (int64_t)info->first_at < (int64_t)info->merges_at + 16 * (int64_t)info->num_merges ||
+                       (int64_t)info->bytes < (int64_t)info->first_at +
+                                                  16 * (int64_t)info->jobs_per_workgroup * info->num_workgroups))
+    return fail(PA_ERR_INVALID,
+                "%s: first-tile entries were written for block size %d (pool: %d) or lie outside the plan", who,
+                info->first_block_size, pool->block_size);
   if (info->jobs_at != 0 || info->merges_at % 16 != 0 ||
       (info->num_jobs > 0 && (info->num_workgroups == 0 || info->jobs_per_workgroup == 0)) ||
       (int64_t)info->jobs_per_workgroup * info->num_workgroups < (int64_t)info->num_jobs ||
@@ -818,6 +868,8 @@ pa_status decode_stages(int stages, const char* who, const pa_kv_pool* pool, con
   a.jobs = reinterpret_cast<const pa_decode_job*>(pb + info->jobs_at);
   a.merges = reinterpret_cast<const pa_decode_merge*>(pb + info->merges_at);
   a.groups = info->num_groups > 0 ? reinterpret_cast<const pa_decode_group*>(pb + info->groups_at) : nullptr;
+  a.first_blocks = first_blocks && pool->dtype == PA_BF16 ? reinterpret_cast<const int32_t*>(pb + info->first_at)
+                                                          : nullptr;
   a.num_groups = info->num_groups;
   char* ws = static_cast<char*>(workspace);
   a.partial_ml = info->num_records > 0 ? reinterpret_cast<float*>(ws + lay.ml) : nullptr;

@@ -232,7 +232,9 @@ __device__ __forceinline__ uint4 load_global(const char* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
 
-// K and V of tile t (of the job starting at tile t0) for KV head g: lane
+// K and V of tile t (of the job starting at tile t0) for KV head g, whose
+// raw table entries are e0 (and e1, the second block of an 8-slot-block
+// tile; range-checked here): lane
 // (li, lq) gets K row li, dims 32*ks + 8*lq .. +8 (ks = 0..3), and V rows
 // 4*lq + r, dims 8*li .. 8*li + 8 (r = 0..3).  For B >= 16 only the first
 // `rows` rows are read: the tile's buffer resource covers exactly those rows,
@@ -243,7 +245,7 @@ __device__ __forceinline__ uint4 load_global(const char* p) {
 // instruction's immediate, not the scalar offset, so every per-row offset is
 // in the vector offset.
 template <int B, bool kStream, bool kFused>
-__device__ __forceinline__ void load_bf16_tile(const DecodeArgs& a, int32_t g, int32_t t0, int32_t tb0, int32_t tb1,
+__device__ __forceinline__ void load_bf16_tile(const DecodeArgs& a, int32_t g, int32_t t0, int32_t e0, int32_t e1,
                                                int32_t t, int32_t rows, int32_t r_new, const char* nk,
                                                const char* nv, int li, int lq, uint4 (&kf)[4], uint4 (&vf)[4]) {
   constexpr int D = 128;
@@ -252,13 +254,13 @@ __device__ __forceinline__ void load_bf16_tile(const DecodeArgs& a, int32_t g, i
   const int64_t blk_bytes = (int64_t)row_bytes * B;
   const char* kb = reinterpret_cast<const char*>(a.k) + (int64_t)g * D * 2;
   const char* vb = reinterpret_cast<const char*>(a.v) + (int64_t)g * D * 2;
-  const int32_t p0 = clamp_block(__builtin_amdgcn_readlane(tb0, t), a.num_blocks);
+  const int32_t p0 = clamp_block(e0, a.num_blocks);
   if (kFused && r_new >= 0) {
     // The tile holding this step's appended token (row r_new): that row
     // comes from the new key/value arrays, rows after it (past the context)
     // read the same row and are masked later, rows before it come from the
     // pool.  Per-lane addresses, so plain global loads.
-    const int32_t p1 = B == 8 ? clamp_block(__builtin_amdgcn_readlane(tb1, t), a.num_blocks) : p0;
+    const int32_t p1 = B == 8 ? clamp_block(e1, a.num_blocks) : p0;
     auto row_addr = [&](const char* base, int32_t row) {
       if (B == 8) return base + (int64_t)(row < 8 ? p0 : p1) * blk_bytes + (row & 7) * row_bytes;
       return base + (int64_t)p0 * blk_bytes + ((int64_t)((t0 + t) % kTilesPerBlock) * kTile + row) * row_bytes;
@@ -271,7 +273,7 @@ __device__ __forceinline__ void load_bf16_tile(const DecodeArgs& a, int32_t g, i
       vf[r] = load_global<kStream>(4 * lq + r >= r_new ? nv + 16 * li : row_addr(vb, 4 * lq + r) + 16 * li);
   } else if (B == 8) {
     // Rows 0..7 of the tile live in block p0, rows 8..15 in block p1.
-    const int32_t p1 = clamp_block(__builtin_amdgcn_readlane(tb1, t), a.num_blocks);
+    const int32_t p1 = clamp_block(e1, a.num_blocks);
     const int64_t kblk = (int64_t)(li < 8 ? p0 : p1) * blk_bytes;
     const int64_t vblk = (int64_t)(lq < 2 ? p0 : p1) * blk_bytes;
 #pragma unroll
@@ -556,6 +558,19 @@ __global__ __launch_bounds__(kNW * 64, kWavesPerSimd) void decode_bf16_kernel(De
   // The workgroup's jobs are the slots k = 0, 1, ... of its column of the
   // job table (entry k * num_workgroups + blockIdx.x); an empty slot
   // (tile_count 0) ends the column.
+  // Start-up is a chain of round trips: kernel arguments, job records (and
+  // first-tile entries), then the first tile loads.  Each link is one batch:
+  // the three 64-byte lines of the arguments are requested together here
+  // (later argument reads hit the scalar cache), and every record the
+  // prologue needs is requested before the first of them is waited for.
+  // Without the pins the compiler requests argument fields and records one
+  // at a time as they are used, each behind a wait for all scalar loads.
+  {
+    const uint64_t line0 = reinterpret_cast<uint64_t>(a.k);
+    const uint64_t line1 = reinterpret_cast<uint64_t>(a.first_blocks);
+    const int32_t line1b = a.num_blocks, line2 = a.num_workgroups;
+    asm volatile("" ::"s"(line0), "s"(line1), "s"(line1b), "s"(line2));
+  }
   const int32_t jend = a.jobs_per_workgroup;
   if (jend <= 0) return;
   auto record = [&](int32_t k) { return load_job(a.jobs, (int64_t)min(k, jend - 1) * a.num_workgroups + blockIdx.x); };
@@ -567,6 +582,17 @@ __global__ __launch_bounds__(kNW * 64, kWavesPerSimd) void decode_bf16_kernel(De
   // The first four records are requested together.
   const pa_decode_job r0 = record(0), r1 = record(1), r2 = record(2);
   pa_decode_job r3 = record(3);
+  // First-tile table entries of the first two jobs (when the plan has them;
+  // otherwise the same slots of the job table are read and unused): the
+  // kDepth = 2 positions issued before the stream starts are tiles 0 and 1
+  // of the first job, or tile 0 of each of the first two.
+  const auto* fb = as_const(reinterpret_cast<const i32x4_t*>(
+      a.first_blocks != nullptr ? a.first_blocks : reinterpret_cast<const int32_t*>(a.jobs)));
+  auto first_ids = [&](int32_t k) { return fb[(int64_t)min(k, jend - 1) * a.num_workgroups + blockIdx.x]; };
+  static_assert(kDepth == 2, "the first-tile entries cover two positions");
+  const i32x4_t f0 = first_ids(0), f1 = first_ids(1);
+  asm volatile("" ::"s"(r0.tile_count), "s"(r1.tile_count), "s"(r2.tile_count), "s"(r3.tile_count), "s"(f0),
+               "s"(f1));
   int32_t s3 = 3;
   if (r0.tile_count <= 0) return;
   bool hn = jend > 1 && r1.tile_count > 0;
@@ -593,7 +619,13 @@ __global__ __launch_bounds__(kNW * 64, kWavesPerSimd) void decode_bf16_kernel(De
   constexpr int kSlots = kDepth + 1;
   uint4 kf[kSlots][4], vf[kSlots][4];
 
-  auto issue = [&](int32_t pos, uint4 (&ks)[4], uint4 (&vs)[4]) {
+  // Issue the loads of stream position pos into (ks, vs).  Table entries come
+  // from the jobs' table registers, or, with `first` (the positions issued
+  // before the stream starts), from the plan's first-tile entries f0, f1 of
+  // cur and nxt: scalar values that arrive with the job records, so the
+  // first tiles do not wait for the table loads.
+  auto issue_at = [&](int32_t pos, uint4 (&ks)[4], uint4 (&vs)[4], bool first, const i32x4_t& f0,
+                      const i32x4_t& f1) {
     const int32_t r = pos - x0;
     const int32_t rn = r - cur.v.cnt;
     const int32_t rn2 = rn - nxt.v.cnt;
@@ -603,8 +635,17 @@ __global__ __launch_bounds__(kNW * 64, kWavesPerSimd) void decode_bf16_kernel(De
     const int32_t t = in_c ? r : in_n ? rn : in_n2 ? rn2 : cur.v.cnt - 1;
     const int32_t g = in_n ? nxt.v.g : in_n2 ? nx2.v.g : cur.v.g;
     const int32_t t0 = in_n ? nxt.v.t0 : in_n2 ? nx2.v.t0 : cur.v.t0;
-    const int32_t tb0 = in_n ? nxt.tb0 : in_n2 ? nx2.tb0 : cur.tb0;
-    const int32_t tb1 = in_n ? nxt.tb1 : in_n2 ? nx2.tb1 : cur.tb1;
+    int32_t e0, e1;
+    if (first) {
+      const i32x4_t f = in_n ? f1 : f0;
+      e0 = t <= 0 ? f[0] : f[1];
+      e1 = t <= 0 ? f[2] : f[3];
+    } else {
+      const int32_t tb0 = in_n ? nxt.tb0 : in_n2 ? nx2.tb0 : cur.tb0;
+      const int32_t tb1 = in_n ? nxt.tb1 : in_n2 ? nx2.tb1 : cur.tb1;
+      e0 = __builtin_amdgcn_readlane(tb0, t);
+      e1 = B == 8 ? __builtin_amdgcn_readlane(tb1, t) : 0;
+    }
     const int32_t L = in_n ? nxt.v.L : in_n2 ? nx2.v.L : cur.v.L;
     const bool idle = in_n ? nxt.v.idle : in_n2 ? nx2.v.idle : cur.v.idle;
     const bool live = (in_c || in_n || in_n2) && !idle;
@@ -616,8 +657,10 @@ __global__ __launch_bounds__(kNW * 64, kWavesPerSimd) void decode_bf16_kernel(De
     const int64_t new_row = ((int64_t)seq * a.num_kv_heads + g) * kHeadDim * 2;
     const char* nk = reinterpret_cast<const char*>(a.new_k) + new_row;
     const char* nv = reinterpret_cast<const char*>(a.new_v) + new_row;
-    load_bf16_tile<B, kStream, kFused>(a, g, t0, tb0, tb1, t, rows, r_new, nk, nv, li, lq, ks, vs);
+    load_bf16_tile<B, kStream, kFused>(a, g, t0, e0, e1, t, rows, r_new, nk, nv, li, lq, ks, vs);
   };
+  const i32x4_t none = {0, 0, 0, 0};
+  auto issue = [&](int32_t pos, uint4 (&ks)[4], uint4 (&vs)[4]) { issue_at(pos, ks, vs, false, none, none); };
   // Compute position x from slot (ks, vs) after issuing position x + kDepth
   // into slot (kp, vp); false when the stream is done.
   auto step = [&](uint4 (&ks)[4], uint4 (&vs)[4], uint4 (&kp)[4], uint4 (&vp)[4]) {
@@ -645,8 +688,13 @@ __global__ __launch_bounds__(kNW * 64, kWavesPerSimd) void decode_bf16_kernel(De
     st.reset();
     return true;
   };
+  if (a.first_blocks != nullptr) {
 #pragma unroll
-  for (int u = 0; u < kDepth; ++u) issue(u, kf[u], vf[u]);
+    for (int u = 0; u < kDepth; ++u) issue_at(u, kf[u], vf[u], true, f0, f1);
+  } else {
+#pragma unroll
+    for (int u = 0; u < kDepth; ++u) issue(u, kf[u], vf[u]);
+  }
   // The slot ring, unrolled so that every slot index is a constant and the
   // slots stay in registers.
   while (true) {

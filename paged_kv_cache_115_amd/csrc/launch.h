@@ -21,6 +21,7 @@ struct DecodeArgs {
   const pa_decode_job* jobs;     // [jobs_per_workgroup][num_workgroups], column-major lists
   const pa_decode_merge* merges; // [num_merges]
   const pa_decode_group* groups; // [num_groups] prefix-group descriptors
+  const int32_t* first_blocks;   // [jobs_per_workgroup][num_workgroups][4] first-tile table entries, or null
   float* partial_ml;             // [num_records * group][2] = (max, sum) in log2 units
   float* partial_o;              // [num_records * group][head_dim], unnormalised
   int32_t num_blocks;

@@ -65,12 +65,16 @@ def plan_and_workspace(pk, lens: np.ndarray, hkv: int, hq: int, d: int, num_work
 
 
 def gpu_decode(pk, pool, q_dev, tables, lens, scale, schedule=(None, 0), out_dtype=torch.float32, shared_kv=False,
-               new_key=None, new_value=None):
+               new_key=None, new_value=None, first_blocks=False):
     """schedule = (num_workgroups or None for the device default, max_piece_tiles).
-    new_key/new_value: fuse this step's append into the decode call."""
+    new_key/new_value: fuse this step's append into the decode call.
+    first_blocks: write the jobs' first-tile table entries into the plan."""
     hq = q_dev.shape[1]
     plan, plan_dev, ws = plan_and_workspace(pk, lens, pool.k.shape[2], hq, pool.k.shape[3], *schedule,
                                             shared_kv=shared_kv)
+    if first_blocks:
+        plan.set_first_blocks(tables, pool.block_size)
+        plan_dev = plan.to_device()
     out = torch.full(tuple(q_dev.shape), float("nan"), dtype=out_dtype, device="cuda")
     pk.decode(pool, q_dev, to_dev(tables), to_dev(lens), scale, plan, plan_dev, ws, out=out,
               new_key=new_key, new_value=new_value)
@@ -78,7 +82,8 @@ def gpu_decode(pk, pool, q_dev, tables, lens, scale, schedule=(None, 0), out_dty
 
 
 # ---------------------------------------------------------------- decode step
-def product_decode_step(pk, case: dict, schedule=(None, 0), out_dtype=torch.float32, fused: bool = False):
+def product_decode_step(pk, case: dict, schedule=(None, 0), out_dtype=torch.float32, fused: bool = False,
+                        first_blocks: bool = False):
     """Prefill L-1 tokens, append this step's token, decode.  Returns dict.
     fused: the appended token is not written by pa_reshape_and_cache but
     handed to pa_decode (new_key/new_value), which stores it while attending."""
@@ -119,7 +124,7 @@ def product_decode_step(pk, case: dict, schedule=(None, 0), out_dtype=torch.floa
     tables, lens_out = bm.export(np.arange(s_count), maxb)
     assert np.array_equal(lens_out, lens)
     out = gpu_decode(pk, pool, to_dev(case["q"]), tables, lens_out, case["scale"], schedule, out_dtype,
-                     new_key=new_k if fused else None, new_value=new_v if fused else None)
+                     new_key=new_k if fused else None, new_value=new_v if fused else None, first_blocks=first_blocks)
     torch.cuda.synchronize()
     return dict(out=to_host(out), kpool=to_host(kpool), vpool=to_host(vpool), tables=tables,
                 pre_slots=pre_slots, new_slots=new_slots, pool=pool, q_dev=to_dev(case["q"]), lens=lens_out)
@@ -166,12 +171,15 @@ def _prefix_ops(case: dict):
     return p, n, case["cfg"]["prefix_len"], case["tail_lengths"]
 
 
-def cascade_decode(pk, pool, q_dev, tables, lens, scale, bm, seqs, schedule=(None, 0), new_key=None, new_value=None):
+def cascade_decode(pk, pool, q_dev, tables, lens, scale, bm, seqs, schedule=(None, 0), new_key=None, new_value=None,
+                   first_blocks=False):
     """pa_decode over a plan that reads each shared prefix once per group
     (pa_bm_prefix_groups -> pa_decode_plan_prefix)."""
     hq = q_dev.shape[1]
     group, tokens = bm.prefix_groups(seqs)
     plan = pk.decode_plan_prefix(lens, pool.k.shape[2], hq, group, tokens, schedule[0], schedule[1])
+    if first_blocks:
+        plan.set_first_blocks(tables, pool.block_size)
     nbytes = pk.decode_workspace_bytes(plan, hq, pool.k.shape[3])
     ws = torch.full((nbytes // 4,), float("nan"), dtype=torch.float32, device="cuda") if nbytes else None
     out = torch.full(tuple(q_dev.shape), float("nan"), dtype=torch.float32, device="cuda")

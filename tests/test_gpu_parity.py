@@ -99,6 +99,40 @@ def test_decode_step_matches_oracle(pk, name, schedule):
     log(f"  max|err|={stats['max_abs']:.3g} mean|err|={stats['mean_abs']:.3g}")
 
 
+FIRST_CASES = [("c1", DEFAULT), ("c2s", DEFAULT), ("c2s", SMALL_PIECES), ("c3s", DEFAULT), ("c3s", TINY_PIECES),
+               ("c3s", FEW_WG), ("c4s", SMALL_PIECES)]
+
+
+@pytest.mark.parametrize("name,schedule", FIRST_CASES)
+def test_first_tile_entries_in_the_plan_change_no_bit(pk, name, schedule):
+    """A plan carrying the jobs' first-tile table entries
+    (pa_decode_plan_first_blocks) gives bitwise the output of the same plan
+    without them, separate and fused append alike."""
+    log(f"first-tile entries {name} schedule={schedule}")
+    case = synth.decode_case(name)
+    got = product_decode_step(pk, case, schedule)
+    args = (pk, got["pool"], got["q_dev"], got["tables"], got["lens"], case["scale"], schedule)
+    base = to_host(gpu_decode(*args))
+    first = to_host(gpu_decode(*args, first_blocks=True))
+    assert np.array_equal(bits(base), bits(got["out"])) and np.array_equal(bits(first), bits(base))
+
+
+@pytest.mark.parametrize("b", [8, 16, 32])
+def test_first_tile_entries_at_edge_lengths_and_fused(pk, b):
+    """Lengths that put the first tiles at block and tile edges (1, B-1, B,
+    B+1, 16, 17, 32), with the append fused into the launch: pools and output
+    equal, bit for bit, with and without the plan's first-tile entries."""
+    log(f"first-tile entries edge lengths B={b}")
+    for fused in (False, True):
+        runs = []
+        for first in (False, True):
+            case = _edge_case([1, b - 1, b, b + 1, 16, 17, 32, 3 * b + 5], b)
+            runs.append(product_decode_step(pk, case, FEW_WG, fused=fused, first_blocks=first))
+        assert np.array_equal(bits(runs[0]["out"]), bits(runs[1]["out"]))
+        assert np.array_equal(bits(runs[0]["kpool"]), bits(runs[1]["kpool"]))
+        assert np.array_equal(bits(runs[0]["vpool"]), bits(runs[1]["vpool"]))
+
+
 FUSED_CASES = [("c1", DEFAULT), ("c1", TINY_PIECES), ("c2s", SMALL_PIECES), ("c3s", DEFAULT), ("c3s", TINY_PIECES),
                ("c3s", FEW_WG), ("c4s", SMALL_PIECES)]
 
@@ -316,6 +350,18 @@ def test_cascade_decode_matches_oracle(pk, b, schedule):
     log(f"  max|err|={stats['max_abs']:.3g} mean|err|={stats['mean_abs']:.3g} groups={got['plan'].num_groups}")
     plain = product_prefix(pk, case, schedule)
     assert np.abs(got["out"] - plain["out"]).max() < 2e-3
+
+
+@pytest.mark.parametrize("b", [8, 16, 32])
+def test_cascade_decode_with_first_tile_entries(pk, b):
+    log(f"cascade c5s B={b} with first-tile entries")
+    case = synth.prefix_case("c5s", b)
+    got = product_prefix(pk, case, SMALL_PIECES, cascade=True)
+    seqs = np.arange(len(got["lens"]))
+    out, plan = cascade_decode(pk, got["pool"], to_dev(case["q"]), got["tables"], got["lens"], case["scale"],
+                               got["bm"], seqs, SMALL_PIECES, first_blocks=True)
+    assert plan.info.flags & pk.PA_DECODE_FIRST_BLOCKS
+    assert np.array_equal(bits(to_host(out)), bits(got["out"]))
 
 
 def test_cascade_decode_with_fused_append(pk):

@@ -456,8 +456,10 @@ def _lpt_model(lens, hkv, nwg, cap):
     sequence cut into near-equal pieces of at most cap tiles (cap 0: the
     average tiles per workgroup clamped to [4, 64]), one job per (piece, head
     block); jobs by size, largest first (ties in generation order), each to
-    the least-loaded workgroup (ties: the one that reached that load first,
-    initially by index).  Returns (jobs per workgroup, merge rows, records)."""
+    the least-loaded pair of workgroups {b, b + nwg/2} for an even grid, or
+    the least-loaded workgroup for an odd one (ties: the one that reached that
+    load first, initially by index), and within a pair to the lighter member
+    (ties: b).  Returns (jobs per workgroup, merge rows, records)."""
     import heapq
     lens = [int(x) for x in lens]
     hb = -(-hkv // 4)
@@ -482,13 +484,19 @@ def _lpt_model(lens, hkv, nwg, cap):
             t0 += cnt
     nwg = max(1, min(nwg, len(jobs)))
     order = sorted(range(len(jobs)), key=lambda i: (-jobs[i][2], i))
-    heap = [(0, w, w) for w in range(nwg)]
-    arrival = nwg
+    # An even grid balances pairs {b, b + nwg/2} (the workgroups that share a
+    # compute unit), then splits each pair's jobs to its lighter member.
+    bins = nwg // 2 if nwg % 2 == 0 else nwg
+    heap = [(0, b, b) for b in range(bins)]
+    arrival = bins
     wg_jobs = [[] for _ in range(nwg)]
+    wg_load = [0] * nwg
     for i in order:
-        load, _, w = heapq.heappop(heap)
+        load, _, b = heapq.heappop(heap)
+        w = b + bins if nwg % 2 == 0 and wg_load[b + bins] < wg_load[b] else b
         wg_jobs[w].append(i)
-        heapq.heappush(heap, (load + jobs[i][2], arrival, w))
+        wg_load[w] += jobs[i][2]
+        heapq.heappush(heap, (load + jobs[i][2], arrival, b))
         arrival += 1
     return [[jobs[i] for i in sorted(l)] for l in wg_jobs], merges, records
 
@@ -544,6 +552,12 @@ def test_decode_plan_small_example_lpt():
         (3, 0, 32, 0, 0, 2, 16), (3, 0, 32, 1, 0, 2, 24), (3, 32, 31, 0, 1, 2, 16), (3, 32, 31, 1, 1, 2, 24)])
     loads = sorted(int(plan.job_table()[:, w, 2].sum()) for w in range(6))
     assert loads == [32, 32, 32, 32, 38, 38]
+    # Placement by compute-unit pairs {0, 3}, {1, 4}, {2, 5}: 32 -> 0, 32 -> 1,
+    # 31 -> 2, 31 -> 5 (pair 2 is least loaded, 5 its lighter member), the four
+    # 19-tile jobs alternate over pairs 0 and 1 (to 3, 4, 3, 4), then the two
+    # 1-tile jobs go to pair 2 (to 2, then 5).
+    per_wg = [int(plan.job_table()[:, w, 2].sum()) for w in range(6)]
+    assert per_wg == [32, 32, 32, 38, 38, 32]
     merges = [tuple(m) for m in plan.merges().tolist()]
     assert merges == ([(0, g, 0, -1) for g in range(8)] + [(2, g, 2, 2 * g) for g in range(8)] +
                       [(3, g, 2, 16 + 2 * g) for g in range(8)])
@@ -690,6 +704,41 @@ def test_abi_rejects_bad_swap_arguments_without_launching():
     assert L.pa_swap_blocks(ctypes.byref(dev_bad), ctypes.byref(_pool()), None, 0, 0, 0, None) == -2
 
 
+@pytest.mark.parametrize("b", [8, 16, 32])
+def test_first_tile_entries_match_the_tables(b):
+    """pa_decode_plan_first_blocks writes, per job slot, the table entries
+    of the job's tiles 0 and 1 (entry 2t and 2t + 1 at B = 8, t at B = 16,
+    t / 2 at B = 32; indices clamped into the row), zeros for empty slots."""
+    rng = np.random.default_rng(70 + b)
+    lens = rng.integers(0, 400, size=37)
+    maxb = int(max(-(-int(L) // b) for L in lens))
+    tables = rng.integers(0, 5000, size=(37, maxb)).astype(np.int32)
+    for sched, cap in ((pk.SCHEDULE_CHUNKS, 3), (pk.SCHEDULE_LPT, 0)):
+        plan = pk.decode_plan(lens, 8, num_workgroups=13, max_piece_tiles=cap, schedule=sched)
+        assert plan.info.flags == 0 and plan.info.first_block_size == 0
+        assert plan.first_blocks().sum() == 0
+        plan.set_first_blocks(tables, b)
+        assert plan.info.flags & pk.PA_DECODE_FIRST_BLOCKS and plan.info.first_block_size == b
+        tab, fb = plan.job_table(), plan.first_blocks()
+        for k in range(tab.shape[0]):
+            for w in range(tab.shape[1]):
+                seq, t0, cnt = tab[k, w, :3]
+                if cnt == 0:
+                    assert fb[k, w].tolist() == [0, 0, 0, 0]
+                    continue
+                want = []
+                for part in (0, 1):
+                    for kk in (0, 1):
+                        t = t0 + kk
+                        e = 2 * t + part if b == 8 else (t // (b // 16) if part == 0 else None)
+                        want.append(0 if e is None else int(tables[seq, min(e, maxb - 1)]))
+                assert fb[k, w].tolist() == want, (k, w)
+    with pytest.raises(pk.PaError):
+        plan.set_first_blocks(tables[:5], b)          # jobs name sequences past the rows given
+    with pytest.raises(pk.PaError):
+        plan.set_first_blocks(tables, 12)
+
+
 def test_abi_rejects_bad_decode_arguments_without_launching():
     pool = _pool()
     p = ctypes.c_void_p(0x40000)
@@ -727,6 +776,11 @@ def test_abi_rejects_bad_decode_arguments_without_launching():
     flagged = _lib.PaDecodePlanInfo.from_buffer_copy(plan.info)
     flagged.flags = 4
     assert call(info=flagged, **ws) == -1           # unknown flag bit
+    first = _lib.PaDecodePlanInfo.from_buffer_copy(plan.info)
+    first.flags = pk.PA_DECODE_FIRST_BLOCKS
+    first.first_block_size = 8
+    assert call(info=first, **ws) == -1             # first-tile entries for another block size
+    assert b"first-tile" in L.pa_last_error()
     for stage in (L.pa_decode_attention, L.pa_decode_merge_pieces):   # same checks on both stages
         assert stage(ctypes.byref(pool), p, p, 0, p, 400, p, 2, 30, ctypes.c_float(0.1), None, None, p,
                      ctypes.byref(plan.info), ws["ws"], ws["wsb"], None) == -1
