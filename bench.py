@@ -352,6 +352,59 @@ def swap_sweep(torch, pk, lengths, reps: int = 10) -> int:
     return 0
 
 
+def length_sweep(torch, pk, lengths=(16, 32, 64, 128, 200, 256, 400, 640), reps: int = 100) -> int:
+    """Attention launch time against KV bytes for batches of 256 sequences of
+    one length each (c3 heads: 32 q / 8 KV, head_dim 128, block 16, shuffled
+    blocks): one job per workgroup and no merge, so time = fixed cost + bytes
+    / streaming rate.  The fit over lengths >= 64 separates the two."""
+    S, hq, hkv, d, B = 256, 32, 8, 128, 16
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream()
+    rows = []
+    for L in lengths:
+        lens = np.full(S, L, np.int32)
+        nblk = -(-lens // B)
+        nb = int(nblk.sum()) + S
+        perm = np.random.default_rng(L).permutation(nb).astype(np.int32)
+        maxb = int(nblk.max())
+        tables = np.zeros((S, maxb), np.int32)
+        off = 0
+        for s in range(S):
+            tables[s, :nblk[s]] = perm[off:off + nblk[s]]
+            off += nblk[s]
+        R = max(2, -(-2**30 // (2 * nb * B * hkv * d * 2)))
+        pools = [pk.KvPool(torch.randn((nb, B, hkv, d), device=dev).to(torch.bfloat16),
+                           torch.randn((nb, B, hkv, d), device=dev).to(torch.bfloat16)) for _ in range(R)]
+        plan = pk.decode_plan(lens, hkv).set_first_blocks(tables, B)
+        plan_d = plan.to_device(dev)
+        ws = torch.empty(max(pk.decode_workspace_bytes(plan, hq, d), 256) // 4, device=dev)
+        q = torch.randn((S, hq, d), device=dev).to(torch.bfloat16)
+        out = torch.empty((S, hq, d), device=dev)
+        td, ld = torch.from_numpy(tables).to(dev), torch.from_numpy(lens).to(dev)
+        for i in range(10):
+            pk.decode(pools[i % R], q, td, ld, 0.088, plan, plan_d, ws, out, stream, stage="attention")
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(reps):
+            pk.decode(pools[i % R], q, td, ld, 0.088, plan, plan_d, ws, out, stream, stage="attention")
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / reps * 1e3
+        nbytes = int(lens.sum()) * hkv * d * 2 * 2
+        rows.append({"context_len": L, "us": round(us, 2), "bytes": nbytes, "GBs": round(nbytes / us / 1e3, 1),
+                     "frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)})
+        del pools
+    x = np.array([r["bytes"] for r in rows if r["context_len"] >= 64], float)
+    y = np.array([r["us"] for r in rows if r["context_len"] >= 64], float)
+    slope, fixed = np.polyfit(x, y, 1)
+    print(json.dumps({"metric": "attention launch time against KV bytes", "fixed_us": round(float(fixed), 2),
+                      "streaming_GBs": round(float(1e3 / (slope * 1e9) * 1e3), 1),
+                      "config": {"workload": "256 sequences of one length, 32 q / 8 KV heads, head_dim 128, "
+                                             "block 16, bf16", "reps": reps}, "sweep": rows}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -377,6 +430,9 @@ def main() -> int:
     ap.add_argument("--no-first-blocks", action="store_true",
                     help="leave the jobs' first-tile table entries out of the plan (the first tile loads then "
                          "wait for a table load)")
+    ap.add_argument("--length-sweep", action="store_true",
+                    help="time the attention launch for uniform batches of 16..640 tokens and fit fixed cost "
+                         "and streaming rate, then exit")
     ap.add_argument("--swap-sweep", action="store_true",
                     help="measure swapping a sequence out to pinned host memory and back at several context "
                          "lengths (both engines) and exit")
@@ -393,6 +449,9 @@ def main() -> int:
     if args.swap_sweep:
         torch.cuda.set_device(0)
         return swap_sweep(torch, pk, [256, 1024, 4096, 16384, 32768])
+    if args.length_sweep:
+        torch.cuda.set_device(0)
+        return length_sweep(torch, pk)
 
     torch.cuda.set_device(0)
     if args.config == "c5":
