@@ -156,18 +156,20 @@ pa_status pa_swap_blocks(const pa_kv_pool* device_pool, const pa_kv_pool* host_p
  *  "The block table: logical to physical mapping").  L counts the token
  * written this step; L == 0 yields zeros.
  *
- * Scheduling.  A sequence's context is cut into 16-token tiles.  The host
- * plan (pa_decode_plan, which knows the lengths) lays the tile streams of
- * every (sequence, block of four KV heads) end to end and cuts them into one
- * chunk of equal work per persistent workgroup (work = tokens, plus a small
- * charge per stream), at tile boundaries; the consecutive tiles of one
- * stream in one chunk form a job (a piece of at most `max_piece_tiles`
- * tiles).  The four waves of a workgroup take the four KV heads of each job,
- * so the head slices of a slot row are read together.  A stream cut into
- * several pieces leaves one (max, sum, accumulator) record per piece and KV
- * head in the workspace; a second launch on the same stream merges the
- * records by log-sum-exp in piece order.  The plan is one byte buffer that
- * the caller copies to the device with the other step inputs.
+ * Scheduling.  A sequence's context is cut into 16-token tiles; a job is a
+ * piece of consecutive tiles of one (sequence, block of four KV heads)
+ * stream, and each persistent workgroup runs a list of jobs.  The host plan
+ * (pa_decode_plan, which knows the lengths) builds two schedules and keeps
+ * the one whose busiest workgroup costs less: equal-work chunks of the
+ * streams laid end to end, cut at tile boundaries (PA_SCHEDULE_CHUNKS), or
+ * pieces of at most a workgroup's share placed largest first on the least
+ * loaded compute unit, i.e. pair of workgroups {b, b + nwg/2}
+ * (PA_SCHEDULE_LPT).  The four waves of a workgroup take the four KV heads
+ * of each job, so the head slices of a slot row are read together.  A stream
+ * cut into several pieces leaves one (max, sum, accumulator) record per
+ * piece and KV head in the workspace; a second launch on the same stream
+ * merges the records by log-sum-exp in piece order.  The plan is one byte
+ * buffer that the caller copies to the device with the other step inputs.
  * ------------------------------------------------------------------------- */
 typedef struct pa_decode_job {
   int32_t seq;         /* sequence index */
