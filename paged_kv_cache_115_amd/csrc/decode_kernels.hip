@@ -439,7 +439,7 @@ __device__ __forceinline__ void flush_stage(const DecodeArgs& a, Stage& sg, int 
     const int32_t seq = __builtin_amdgcn_readfirstlane(sg.meta[4 * e + 0]);
     const int32_t g = __builtin_amdgcn_readfirstlane(sg.meta[4 * e + 1]);
     const int32_t rec = __builtin_amdgcn_readfirstlane(sg.meta[4 * e + 2]);
-    if (li >= G) continue;
+    if (li >= G || rec < -1) continue;  // -2: a shared job's member without a valid record
     const float* eo = sg.o + e * 128 * G;
     float4 v[8];
 #pragma unroll
@@ -478,16 +478,41 @@ __device__ __forceinline__ void finish_bf16_job(const DecodeArgs& a, const JobVi
   float lt = st.l + __shfl_xor(st.l, 16);
   lt = lt + __shfl_xor(lt, 32);
   if (v.shared) {
-    // Shared prefix piece: column li is head li % G of member li / G; each
-    // member's record for this piece is written directly.
-    if (v.idle || li >= v.ncol) return;
+    // Shared prefix piece: column li is head li % G of member li / G.  Each
+    // member's record for this piece is staged as an entry of its own (the
+    // member's G columns as the first G of the entry), or, with the stage
+    // full, written directly.
+    if (v.idle) return;
     const auto* gd = as_const(reinterpret_cast<const i32x4_t*>(a.groups + v.grp));
     const i32x4_t x1 = gd[1], x2 = gd[2], x3 = gd[3];  // seq[2..3] rb[0..1] | rb[2..3] np[0..1] | np[2..3] -
-    const int m = li / G;
+    const int members = v.ncol / G;
+    const int m = min(li / G, members - 1);
     const int32_t rb = m == 0 ? x1[2] : m == 1 ? x1[3] : m == 2 ? x2[0] : x2[1];
     const int32_t np = m == 0 ? x2[2] : m == 1 ? x2[3] : m == 2 ? x3[0] : x3[1];
     const int64_t rec = (int64_t)rb + (int64_t)v.w * np + v.part;
-    if (rb < 0 || v.part >= np || rec >= a.num_records) return;
+    const bool valid = rb >= 0 && v.part < np && rec < a.num_records;
+    if (sg.n + members <= sg.cap) {
+      const int e = sg.n + m, lg = li % G;
+      if (li < v.ncol) {
+        float* eo = sg.o + e * 128 * G;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          *reinterpret_cast<float4*>(eo + (((2 * r) * 4 + lq) * G + lg) * 4) =
+              make_float4(st.o[0][r], st.o[1][r], st.o[2][r], st.o[3][r]);
+          *reinterpret_cast<float4*>(eo + (((2 * r + 1) * 4 + lq) * G + lg) * 4) =
+              make_float4(st.o[4][r], st.o[5][r], st.o[6][r], st.o[7][r]);
+        }
+        if (lq == 0) *reinterpret_cast<float2*>(sg.ml + (e * 16 + lg) * 2) = make_float2(st.m, lt);
+        if (lg == 0 && lq == 0) {
+          sg.meta[4 * e + 0] = 0;
+          sg.meta[4 * e + 1] = v.g;
+          sg.meta[4 * e + 2] = valid ? (int32_t)rec : -2;
+        }
+      }
+      sg.n += members;
+      return;
+    }
+    if (li >= v.ncol || !valid) return;
     const int64_t rr = rec * G + li % G;
     float* po = a.partial_o + rr * D + 32 * lq;
 #pragma unroll
@@ -683,8 +708,11 @@ __global__ __launch_bounds__(kNW * 64, kWavesPerSimd) void decode_bf16_kernel(De
     hn2 = hn && s3 < jend && r3.tile_count > 0;
     load_ref<B>(a, r3, w, lane, nx2);
     ++s3;
-    r3 = record(s3);
+    // The query of the next job first: a shared job reads its group
+    // descriptor with a scalar load, and the wait for it would otherwise also
+    // wait for the record requested below.
     load_q(a, nxt.v, li, lq, qn);
+    r3 = record(s3);
     st.reset();
     return true;
   };
