@@ -596,7 +596,8 @@ def main() -> int:
                    "pool_replicas": R, "decode_only": bool(args.decode_only), "shared_kv": bool(w["shared_kv"]),
                    "schedule": ["chunks", "largest pieces first"][plan.schedule],
                    "cascade_prefix_groups": int(plan.num_groups) if cascade else 0,
-                   "first_tile_entries": not args.no_first_blocks},
+                   "first_tile_entries": not args.no_first_blocks,
+                   "kv_loads": "cached" if plan.info.flags & pk.PA_DECODE_SHARED_KV else "streamed"},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "decode_tokens_per_s": round(S / (ms_per_step * 1e-3), 1),
         "kv_bytes_per_step": kv_bytes,

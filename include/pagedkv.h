@@ -317,7 +317,11 @@ pa_status pa_decode_plan_schedule(const int32_t* context_lens, int32_t num_seqs,
  *                   member's context length (so the token written this step is
  *                   never in the shared part).
  * Other arguments as pa_decode_plan.  Groups of one member, or a shared part
- * of less than one tile, are planned as unshared sequences.
+ * of less than one tile, are planned as unshared sequences.  The plan sets
+ * PA_DECODE_SHARED_KV in info->flags only when some shared block is still
+ * read by more than one job (a group larger than the largest allowed size,
+ * or one without a whole shared tile); otherwise every block is read once
+ * and the loads stream past the caches.
  * Precondition (not checked): the members' block tables hold the same block
  * ids for the shared tokens; the shared blocks are read through the first
  * member's table. */

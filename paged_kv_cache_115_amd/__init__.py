@@ -232,7 +232,8 @@ def decode_plan_prefix(context_lens, num_kv_heads: int, num_q_heads: int, prefix
                        num_workgroups: int | None = None, max_piece_tiles: int = 0) -> DecodePlan:
     """pa_decode_plan_prefix: shared prefixes read once per group (cascade
     decode).  prefix_group/prefix_tokens as from BlockManager.prefix_groups.
-    The plan carries PA_DECODE_SHARED_KV (the batch shares blocks)."""
+    The plan carries PA_DECODE_SHARED_KV only when some shared block is still
+    read by more than one job (see pa_decode_plan_prefix)."""
     lens = np.ascontiguousarray(context_lens, dtype=np.int32)
     grp = np.ascontiguousarray(prefix_group, dtype=np.int32)
     tok = np.ascontiguousarray(prefix_tokens, dtype=np.int32)
@@ -252,7 +253,6 @@ def decode_plan_prefix(context_lens, num_kv_heads: int, num_q_heads: int, prefix
             break
         _plan_buf = np.zeros(2 * info.bytes, dtype=np.uint64).view(np.uint8)   # 8-byte aligned
     _check(st, "pa_decode_plan_prefix")
-    info.flags = PA_DECODE_SHARED_KV
     return DecodePlan(buf[: info.bytes].copy(), info)
 
 

@@ -258,6 +258,7 @@ struct Schedule {
   int64_t records = 0;
   int64_t nwg = 1;
   int32_t group_size = 0;
+  bool reread = false;  // some block is read by more than one job (prefix plans)
 };
 
 constexpr int64_t kStreamCharge = 4;   // cost units (tokens) charged per stream start by the chunk walk
@@ -408,6 +409,10 @@ pa_status schedule_prefix(const int32_t* lens, int32_t num_seqs, int32_t num_kv_
   for (size_t i = 0; i < by_key.size();) {
     size_t j = i;
     while (j < by_key.size() && prefix_group[by_key[j]] == prefix_group[by_key[i]]) ++j;
+    // A key group that does not become exactly one planned group (more
+    // members than fit, or no whole shared tile) has its prefix blocks read
+    // by several jobs.
+    if (j - i >= 2 && j - i > (size_t)group_cap) out.reread = true;
     for (size_t k = i; k < j; k += (size_t)group_cap) {
       std::vector<int32_t> g(by_key.begin() + k, by_key.begin() + std::min(j, k + (size_t)group_cap));
       int64_t tok = INT64_MAX;
@@ -416,6 +421,8 @@ pa_status schedule_prefix(const int32_t* lens, int32_t num_seqs, int32_t num_kv_
       if (g.size() >= 2 && t >= 1) {
         groups.push_back(g);
         shared_tiles.push_back(t);
+      } else if (j - i >= 2) {
+        out.reread = true;
       }
     }
     i = j;
@@ -691,7 +698,12 @@ extern "C" pa_status pa_decode_plan_prefix(const int32_t* context_lens, int32_t 
                                               prefix_tokens, num_workgroups, max_piece_tiles > 0 ? max_piece_tiles : 64,
                                               sc))
     return st;
-  return pagedkv::emit_plan(sc, PA_SCHEDULE_CHUNKS, num_kv_heads, plan, capacity, info);
+  const pa_status st = pagedkv::emit_plan(sc, PA_SCHEDULE_CHUNKS, num_kv_heads, plan, capacity, info);
+  // Loads keep blocks in the caches only when some block is read by more
+  // than one job; with every shared prefix read once by its group they
+  // stream past the caches like unshared blocks.
+  if (st == PA_OK) info->flags = sc.reread ? PA_DECODE_SHARED_KV : 0;
+  return st;
 }
 
 extern "C" pa_status pa_decode_plan(const int32_t* context_lens, int32_t num_seqs, int32_t num_kv_heads,

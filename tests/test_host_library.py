@@ -836,6 +836,22 @@ def test_prefix_groups_of_forked_samples(b):
         assert c * b == full
 
 
+def test_prefix_plan_cache_policy():
+    """Loads keep blocks in the caches only if a shared block is read by more
+    than one job: a key group of more members than fit one group (G = 4: four
+    members), or a group without a whole shared tile."""
+    plan = pk.decode_plan_prefix([300] * 4, 8, 32, [0] * 4, [200] * 4, num_workgroups=8)
+    assert plan.num_groups > 0 and plan.info.flags == 0            # one group of four: each block read once
+    plan = pk.decode_plan_prefix([300] * 6, 8, 32, [0] * 6, [200] * 6, num_workgroups=8)
+    assert plan.info.flags == pk.PA_DECODE_SHARED_KV              # six members: two groups read the prefix
+    plan = pk.decode_plan_prefix([300] * 2, 8, 32, [0] * 2, [10] * 2, num_workgroups=8)
+    assert plan.num_groups == 0 and plan.info.flags == pk.PA_DECODE_SHARED_KV   # under one tile: both read it
+    plan = pk.decode_plan_prefix([300, 200], 8, 32, [-1, -1], [0, 0], num_workgroups=8)
+    assert plan.info.flags == 0
+    plan = pk.decode_plan_prefix([300] * 8, 8, 64, [0] * 4 + [4] * 4, [200] * 8, num_workgroups=8)
+    assert plan.info.flags == pk.PA_DECODE_SHARED_KV              # G = 8: two members per group
+
+
 def _check_prefix_plan(plan, lens, hkv, hq, group, tokens):
     """Structural invariants of a shared-prefix plan."""
     G = hq // hkv
