@@ -348,14 +348,14 @@ size_t pa_decode_workspace_bytes(const pa_decode_plan_info* info, int32_t num_q_
  *                  standard attention; S06 "Implementation").
  *   new_key, new_value : device [num_seqs][num_kv_heads][head_dim], pool
  *                  dtype, 16-byte aligned, or both NULL.  When given, the
- *                  step's append is fused into the attention launch: for
- *                  every sequence with L > 0 the token at logical position
- *                  L - 1 is taken from these arrays and also stored into its
- *                  slot, table[(L-1)/B] * B + (L-1) % B, which is what
- *                  pa_reshape_and_cache would have written there with the
- *                  slots the block manager hands out.  Its block must not be
- *                  shared (the host's copy-on-write has run; pa_copy_blocks
- *                  precedes this call on the stream).
+ *                  step's append is fused into the call: for every sequence
+ *                  with L > 0 the attention launch takes the token at
+ *                  logical position L - 1 from these arrays, and the merge
+ *                  launch stores it into its slot, table[(L-1)/B] * B +
+ *                  (L-1) % B, which is what pa_reshape_and_cache would have
+ *                  written there with the slots the block manager hands out.
+ *                  Its block must not be shared (the host's copy-on-write has
+ *                  run; pa_copy_blocks precedes this call on the stream).
  *   plan, info   : device copy of the bytes pa_decode_plan wrote for the same
  *                  context lengths and num_kv_heads, and its host-side info.
  *   workspace    : device, >= pa_decode_workspace_bytes(info, ...), 256-byte
@@ -375,11 +375,12 @@ pa_status pa_decode(const pa_kv_pool* pool, const void* q, void* out, int32_t ou
 /* The two launches of pa_decode as separate calls, with the same arguments
  * and checks: pa_decode_attention writes the output of every sequence that
  * is not cut and the records of cut ones; pa_decode_merge_pieces then writes the
- * output of cut and empty sequences.  Issued in that order on one stream
+ * output of cut and empty sequences and, with new_key/new_value, the appended
+ * rows into the pool.  Issued in that order on one stream
  * they equal pa_decode; between them the caller may record events (to time
  * the attention launch alone) or enqueue other work that touches neither the
- * output nor the workspace.  Either returns PA_OK without launching when its
- * part of the plan is empty. */
+ * output, the workspace nor the appended rows' slots.  Either returns PA_OK
+ * without launching when it has nothing to do. */
 pa_status pa_decode_attention(const pa_kv_pool* pool, const void* q, void* out, int32_t out_dtype,
                               const int32_t* block_tables, int32_t max_blocks_per_seq,
                               const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,

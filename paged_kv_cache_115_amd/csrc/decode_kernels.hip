@@ -303,43 +303,6 @@ __device__ __forceinline__ void load_bf16_tile(const DecodeArgs& a, int32_t g, i
   }
 }
 
-// Fused append: when tile t of job J holds the sequence's token L - 1 (the
-// token appended this step), the registers hold its row from the new
-// key/value arrays (load_bf16_tile); write that row into its pool slot,
-// the slot at logical position L - 1 of the table.  Only the wavefront of
-// the row's last piece meets this tile, so each (sequence, KV head) slice is
-// written once.
-template <int B>
-__device__ __forceinline__ void store_appended_row(const DecodeArgs& a, const JobRef<B>& J, int32_t t, int li,
-                                                   int lq, const uint4 (&kf)[4], const uint4 (&vf)[4]) {
-  constexpr int kTilesPerBlock = B >= kTile ? B / kTile : 1;
-  const int32_t r_new = J.v.L - 1 - kTile * (J.v.t0 + t);
-  if (J.v.idle || r_new < 0 || r_new >= kTile) return;
-  const uint32_t row_bytes = (uint32_t)a.num_kv_heads * kHeadDim * 2;
-  const int64_t blk_bytes = (int64_t)row_bytes * B;
-  const int32_t p0 = clamp_block(__builtin_amdgcn_readlane(J.tb0, t), a.num_blocks);
-  int64_t off;
-  if (B == 8) {
-    const int32_t p1 = clamp_block(__builtin_amdgcn_readlane(J.tb1, t), a.num_blocks);
-    off = (int64_t)(r_new < 8 ? p0 : p1) * blk_bytes + (r_new & 7) * row_bytes;
-  } else {
-    off = (int64_t)p0 * blk_bytes + ((int64_t)((J.v.t0 + t) % kTilesPerBlock) * kTile + r_new) * row_bytes;
-  }
-  off += (int64_t)J.v.g * kHeadDim * 2;
-  char* kdst = reinterpret_cast<char*>(const_cast<void*>(a.k)) + off;
-  char* vdst = reinterpret_cast<char*>(const_cast<void*>(a.v)) + off;
-  if (li == r_new) {
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) *reinterpret_cast<uint4*>(kdst + 16 * (4 * ks + lq)) = kf[ks];
-  }
-  // V row r_new sits in register r_new % 4 of the lanes of group r_new / 4
-  // (constant register indices only: a computed one would move the
-  // registers to memory).
-#pragma unroll
-  for (int r = 0; r < 4; ++r)
-    if (4 * lq + r == r_new) *reinterpret_cast<uint4*>(vdst + 16 * li) = vf[r];
-}
-
 struct SoftmaxState {
   float m, l;
   float4_t o[8];
@@ -690,7 +653,6 @@ __global__ __launch_bounds__(kNW * 64, kWavesPerSimd) void decode_bf16_kernel(De
   // into slot (kp, vp); false when the stream is done.
   auto step = [&](uint4 (&ks)[4], uint4 (&vs)[4], uint4 (&kp)[4], uint4 (&vp)[4]) {
     issue(x + kDepth, kp, vp);
-    if (kFused) store_appended_row<B>(a, cur, x - x0, li, lq, ks, vs);
     compute_bf16_tile(a, cur.v, qc, x - x0, lq, ks, vs, st);
     ++x;
     if (x - x0 < cur.v.cnt) return true;
@@ -773,18 +735,14 @@ __global__ __launch_bounds__(kNW * 64) void decode_f32_kernel(DecodeArgs a) {
       float kv[DPL], vv[DPL];
       if (a.new_k != nullptr && t == v.L - 1) {
         // Fused append: this step's token comes from the new key/value
-        // arrays and is also stored into its pool slot.
+        // arrays (the merge launch stores it into its pool slot).
         const int64_t nrow = ((int64_t)v.seq * a.num_kv_heads + v.g) * D;
         const float* nk = reinterpret_cast<const float*>(a.new_k) + nrow;
         const float* nv = reinterpret_cast<const float*>(a.new_v) + nrow;
-        float* kdst = reinterpret_cast<float*>(const_cast<void*>(a.k)) + (int64_t)v.g * D + row;
-        float* vdst = reinterpret_cast<float*>(const_cast<void*>(a.v)) + (int64_t)v.g * D + row;
 #pragma unroll
         for (int jj = 0; jj < DPL; ++jj) {
           kv[jj] = nk[lane + 64 * jj];
           vv[jj] = nv[lane + 64 * jj];
-          kdst[lane + 64 * jj] = kv[jj];
-          vdst[lane + 64 * jj] = vv[jj];
         }
       } else {
 #pragma unroll
@@ -847,9 +805,38 @@ __device__ __forceinline__ void store2(const DecodeArgs& a, int64_t idx, float x
     *reinterpret_cast<float2*>(reinterpret_cast<float*>(a.out) + idx) = make_float2(x0, x1);
 }
 
+// The appended rows of a launch with a fused append: the attention launch
+// took token L - 1 of every sequence from new_key/new_value; workgroup
+// num_merges + s of the merge launch writes sequence s's row (all KV heads,
+// K and V) into the slot of position L - 1 of its table.  After the
+// attention launch, so no tile load of the same step can see the store.
+__device__ __forceinline__ void append_rows(const DecodeArgs& a, int32_t s) {
+  if (s >= a.num_seqs) return;
+  const int32_t L = a.lens[s];
+  if (L <= 0 || L > a.max_blocks * a.block_size) return;
+  const int32_t t = L - 1;
+  const int32_t p = clamp_block(a.tables[(int64_t)s * a.max_blocks + t / a.block_size], a.num_blocks);
+  const int32_t row_vec = a.num_kv_heads * a.head_dim * (a.bf16 ? 2 : 4) / 16;
+  const int64_t slot = (int64_t)p * a.block_size + t % a.block_size;
+  const uint4* nk = reinterpret_cast<const uint4*>(a.new_k) + (int64_t)s * row_vec;
+  const uint4* nv = reinterpret_cast<const uint4*>(a.new_v) + (int64_t)s * row_vec;
+  uint4* kd = reinterpret_cast<uint4*>(const_cast<void*>(a.k)) + slot * row_vec;
+  uint4* vd = reinterpret_cast<uint4*>(const_cast<void*>(a.v)) + slot * row_vec;
+  for (int32_t c = threadIdx.x; c < 2 * row_vec; c += blockDim.x) {
+    if (c < row_vec)
+      kd[c] = nk[c];
+    else
+      vd[c - row_vec] = nv[c - row_vec];
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(kMaxMergeThreads) void merge_partials_kernel(DecodeArgs a) {
   constexpr int kBatch = 8;
+  if ((int32_t)blockIdx.x >= a.num_merges) {
+    append_rows(a, (int32_t)blockIdx.x - a.num_merges);
+    return;
+  }
   const i32x4_t mv = as_const(reinterpret_cast<const i32x4_t*>(a.merges))[blockIdx.x];
   const pa_decode_merge mg{mv[0], mv[1], mv[2], mv[3]};
   if (mg.seq < 0 || mg.seq >= a.num_seqs || mg.kv_head < 0 || mg.kv_head >= a.num_kv_heads) return;
@@ -949,12 +936,13 @@ hipError_t launch_decode_attention(const DecodeArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t stream) {
-  if (a.num_merges == 0) return hipSuccess;
+  const int64_t blocks = (int64_t)a.num_merges + (a.new_k != nullptr ? a.num_seqs : 0);
+  if (blocks == 0) return hipSuccess;
   const dim3 block((unsigned)(a.group * a.head_dim / 2));
   if (a.head_dim == 128)
-    hipLaunchKernelGGL(merge_partials_kernel<128>, dim3(a.num_merges), block, 0, stream, a);
+    hipLaunchKernelGGL(merge_partials_kernel<128>, dim3((unsigned)blocks), block, 0, stream, a);
   else
-    hipLaunchKernelGGL(merge_partials_kernel<64>, dim3(a.num_merges), block, 0, stream, a);
+    hipLaunchKernelGGL(merge_partials_kernel<64>, dim3((unsigned)blocks), block, 0, stream, a);
   return hipGetLastError();
 }
 

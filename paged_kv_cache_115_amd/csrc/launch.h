@@ -47,7 +47,9 @@ struct DecodeArgs {
 // Attention launch (persistent grid of a.num_workgroups; nothing when the
 // plan has no jobs) on `stream`.
 hipError_t launch_decode_attention(const DecodeArgs& a, hipStream_t stream);
-// Merge launch (one workgroup per merge row; nothing when a.num_merges == 0).
+// Merge launch: one workgroup per merge row, then, with a fused append
+// (a.new_k set), one per sequence writing its appended row into the pool;
+// nothing when neither is needed.
 hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t stream);
 // Resident decode workgroups per compute unit (occupancy of the bf16 kernel).
 hipError_t decode_resident_workgroups_per_cu(int* n);
