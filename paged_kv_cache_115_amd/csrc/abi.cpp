@@ -6,7 +6,6 @@
 
 #include <algorithm>
 #include <cstring>
-#include <queue>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -271,6 +270,11 @@ constexpr int64_t kStreamCharge = 4;   // cost units (tokens) charged per stream
 constexpr int64_t kJobCharge = 56;
 
 int64_t tile_rows(int32_t L, int64_t t) { return std::min<int64_t>(16, L - 16 * t); }
+// Tokens in tiles [t_begin, t_end) of a context of L tokens (every tile but
+// the context's last is full).
+int64_t rows_between(int32_t L, int64_t t_begin, int64_t t_end) {
+  return std::min<int64_t>(L, 16 * t_end) - 16 * t_begin;
+}
 
 // A run of tiles to schedule: tiles [t_begin, t_end) of sequence `seq` for
 // KV heads 4*hb .. 4*hb + 3.  A shared stream reads the prefix blocks of a
@@ -316,50 +320,80 @@ void chunk_streams(std::vector<Stream>& streams, int64_t nwg_req, int64_t cap, S
   }
   int64_t total = 0, total_tiles = 0;
   for (const Stream& st : streams) {
-    for (int64_t t = st.t_begin; t < st.t_end; ++t) total += tile_rows(st.L, t);
-    total += kStreamCharge;
+    total += rows_between(st.L, st.t_begin, st.t_end) + kStreamCharge;
     total_tiles += st.t_end - st.t_begin;
   }
   const int64_t nwg = std::max<int64_t>(1, std::min<int64_t>(nwg_req, total_tiles));
   out.nwg = nwg;
   first.assign(streams.size(), 0);
   count.assign(streams.size(), 0);
-  int64_t cum = 0;
+  out.pieces.reserve(out.pieces.size() + streams.size() + nwg);
+  // The tile whose midpoint m / 2 (m = 2 * cum + c) lies in share w has
+  // w = floor(m * nwg / (2 * total)).  m grows from tile to tile, so w only
+  // advances: it is tracked against the first m of the next share instead of
+  // dividing per tile.
+  int64_t cum = 0, w = 0;
+  auto share_start = [&](int64_t k) { return (k * 2 * total + nwg - 1) / nwg; };  // least m with w >= k
+  int64_t next = share_start(1);
   for (int32_t si : order) {
     const Stream& st = streams[si];
     first[si] = (int32_t)out.pieces.size();
+    const int64_t full_end = std::min<int64_t>(st.t_end, st.L / 16);  // tiles below this are full
     int64_t last_wg = -1;
-    for (int64_t t = st.t_begin; t < st.t_end; ++t) {
+    for (int64_t t = st.t_begin; t < st.t_end;) {
       const int64_t c = tile_rows(st.L, t) + (t == st.t_begin ? kStreamCharge : 0);
-      const int64_t wg = std::min<int64_t>(nwg - 1, ((2 * cum + c) * nwg) / (2 * total));
-      cum += c;
-      if (wg != last_wg || out.pieces.back().job.tile_count >= cap) {
-        out.pieces.push_back(Piece{(int32_t)wg, pa_decode_job{st.seq, (int32_t)t, 0, st.hb, 0, 1, -1, st.L}});
-        last_wg = wg;
+      const int64_t m = 2 * cum + c;
+      while (w < nwg - 1 && m >= next) next = share_start(++w + 1);
+      if (w != last_wg || out.pieces.back().job.tile_count >= cap) {
+        out.pieces.push_back(Piece{(int32_t)w, pa_decode_job{st.seq, (int32_t)t, 0, st.hb, 0, 1, -1, st.L}});
+        last_wg = w;
       }
-      out.pieces.back().job.tile_count += 1;
+      pa_decode_job& j = out.pieces.back().job;
+      // A full tile past the stream's first, and the full tiles after it whose
+      // midpoints stay in share w (each one's m is 32 above the previous),
+      // join the job together while it has room.
+      int64_t k = 1;
+      if (t != st.t_begin && t < full_end) {
+        k = std::min<int64_t>(full_end - t, cap - j.tile_count);
+        if (w < nwg - 1) k = std::min<int64_t>(k, (next - m + 31) / 32);
+      }
+      j.tile_count += (int32_t)k;
+      cum += c + 16 * (k - 1);
+      t += k;
     }
     count[si] = (int32_t)out.pieces.size() - first[si];
   }
 }
 
 // Chunk schedule of plain (unshared) streams, one per (sequence, head
-// block).  Records are per stream: KV head 4*hb + w, piece p at
-// record_base + w * parts + p.
-pa_status schedule_chunks(const int32_t* lens, int32_t num_seqs, int32_t num_kv_heads, int64_t nwg_req, int64_t cap,
-                          Schedule& out) {
-  const int32_t head_blocks = (num_kv_heads + 3) / 4;
+// block), in two steps: the walk places the pieces (all the cost comparison
+// needs), the finish numbers the records and writes the merge rows.  Records
+// are per stream: KV head 4*hb + w, piece p at record_base + w * parts + p.
+struct ChunkWalk {
   std::vector<Stream> streams;
+  std::vector<int32_t> first, count, order;
+};
+void walk_chunks(const int32_t* lens, int32_t num_seqs, int32_t num_kv_heads, int64_t nwg_req, int64_t cap,
+                 Schedule& out, ChunkWalk& cw) {
+  const int32_t head_blocks = (num_kv_heads + 3) / 4;
+  cw.streams.reserve((size_t)num_seqs * head_blocks);
   for (int32_t s = 0; s < num_seqs; ++s)
     if (lens[s] > 0)
       for (int32_t hb = 0; hb < head_blocks; ++hb)
-        streams.push_back(Stream{s, hb, 0, (lens[s] + 15) / 16, lens[s], -1, s});
-  std::vector<int32_t> first, count, order;
-  chunk_streams(streams, nwg_req, cap, out, first, count, order);
+        cw.streams.push_back(Stream{s, hb, 0, (lens[s] + 15) / 16, lens[s], -1, s});
+  chunk_streams(cw.streams, nwg_req, cap, out, cw.first, cw.count, cw.order);
+}
+pa_status finish_chunks(const int32_t* lens, int32_t num_seqs, int32_t num_kv_heads, const ChunkWalk& cw,
+                        Schedule& out) {
+  const int32_t head_blocks = (num_kv_heads + 3) / 4;
+  const std::vector<Stream>& streams = cw.streams;
+  const std::vector<int32_t>& first = cw.first;
+  const std::vector<int32_t>& count = cw.count;
+  out.merges.reserve((size_t)num_seqs * num_kv_heads);
   std::vector<int32_t> stream_of_seq(num_seqs, -1);
   for (size_t i = 0; i < streams.size(); ++i)
     if (streams[i].hb == 0) stream_of_seq[streams[i].seq] = (int32_t)i;
-  for (int32_t i : order) {  // records in layout order
+  for (int32_t i : cw.order) {  // records in layout order
     const int32_t parts = count[i];
     if (parts <= 1) continue;
     const int64_t heads = std::min<int64_t>(4, num_kv_heads - 4 * streams[i].hb);
@@ -394,7 +428,8 @@ pa_status schedule_chunks(const int32_t* lens, int32_t num_seqs, int32_t num_kv_
 // gives one item of shared streams (tiles [0, T) of the first member, per
 // head block) and, per member, an item of its own streams (tiles [T, end)).
 // Member records are per (member, head block): the shared pieces first, then
-// its own pieces.  Ungrouped sequences are planned as by schedule_chunks.
+// its own pieces.  Ungrouped sequences are planned as by the plain chunk
+// schedule.
 pa_status schedule_prefix(const int32_t* lens, int32_t num_seqs, int32_t num_kv_heads, int32_t group_cap,
                           const int32_t* prefix_group, const int32_t* prefix_tokens, int64_t nwg_req, int64_t cap,
                           Schedule& out) {
@@ -533,6 +568,12 @@ pa_status schedule_lpt(const int32_t* lens, int32_t num_seqs, int32_t num_kv_hea
   for (int32_t s = 0; s < num_seqs; ++s) total += ((int64_t)lens[s] + 15) / 16 * head_blocks;
   const int64_t cap = cap_req > 0 ? cap_req : std::min<int64_t>(64, std::max<int64_t>(4, (total + nwg_req - 1) / nwg_req));
   std::vector<pa_decode_job> jobs;
+  {
+    int64_t n = 0;
+    for (int32_t s = 0; s < num_seqs; ++s) n += (((int64_t)lens[s] + 15) / 16 + cap - 1) / cap;
+    jobs.reserve((size_t)(n * head_blocks));
+    out.merges.reserve((size_t)num_seqs * num_kv_heads);
+  }
   for (int32_t s = 0; s < num_seqs; ++s) {
     const int64_t tiles = ((int64_t)lens[s] + 15) / 16;
     if (tiles == 0) {
@@ -567,41 +608,52 @@ pa_status schedule_lpt(const int32_t* lens, int32_t num_seqs, int32_t num_kv_hea
     for (int64_t c = 1; c <= cap + 1; ++c) start[c] += start[c - 1];
     for (size_t i = 0; i < jobs.size(); ++i) order[start[cap - jobs[i].tile_count]++] = (int32_t)i;
   }
-  std::vector<int32_t> owner(jobs.size());
+  out.pieces.resize(jobs.size());
   {
     const bool paired = nwg % 2 == 0;
     const int64_t bins = paired ? nwg / 2 : nwg;
-    // (load, arrival, bin): the least-loaded bin first, then the earliest arrival.
-    typedef std::pair<std::pair<int64_t, int64_t>, int32_t> Entry;
-    std::priority_queue<Entry, std::vector<Entry>, std::greater<Entry>> heap;
-    for (int64_t b = 0; b < bins; ++b) heap.push(Entry({0, b}, (int32_t)b));
-    int64_t arrival = bins;
+    // Min-heap of bins keyed by (load, arrival): the least-loaded bin first,
+    // then the one that reached its load first.  Keys are distinct, so the
+    // bin picked at each step does not depend on the heap's shape.  Loads
+    // and arrivals stay below 2^31 (tiles and jobs are bounded by the plan
+    // size check), so a key packs into one 64-bit word.
+    struct Entry {
+      uint64_t key;
+      int32_t bin;
+    };
+    std::vector<Entry> heap((size_t)bins);
+    for (int64_t b = 0; b < bins; ++b) heap[b] = Entry{(uint64_t)b, (int32_t)b};  // already a heap
+    uint64_t arrival = (uint64_t)bins;
     std::vector<int64_t> wg_load(nwg, 0);
+    const size_t n = heap.size();
     for (int32_t j : order) {
-      const Entry e = heap.top();
-      heap.pop();
-      const int32_t b = e.second;
+      const int32_t b = heap[0].bin;
       int32_t w = b;
       if (paired && wg_load[b + bins] < wg_load[b]) w = (int32_t)(b + bins);
-      owner[j] = w;
+      out.pieces[j] = Piece{w, jobs[j]};
       wg_load[w] += jobs[j].tile_count;
-      heap.push(Entry({e.first.first + jobs[j].tile_count, arrival++}, b));
+      // The top's load grows: replace it and sift down.
+      const Entry e{(((heap[0].key >> 32) + (uint64_t)jobs[j].tile_count) << 32) | arrival++, b};
+      size_t i = 0;
+      for (;;) {
+        size_t c = 2 * i + 1;
+        if (c >= n) break;
+        if (c + 1 < n && heap[c + 1].key < heap[c].key) ++c;
+        if (heap[c].key >= e.key) break;
+        heap[i] = heap[c];
+        i = c;
+      }
+      heap[i] = e;
     }
   }
-  out.pieces.reserve(jobs.size());
-  for (size_t j = 0; j < jobs.size(); ++j) out.pieces.push_back(Piece{owner[j], jobs[j]});
   return PA_OK;
 }
 
 // Largest workgroup cost: tokens of its tiles plus kJobCharge per job.
 int64_t schedule_cost(const Schedule& sc, const int32_t* lens) {
   std::vector<int64_t> cost(sc.nwg, 0);
-  for (const Piece& pc : sc.pieces) {
-    int64_t c = kJobCharge;
-    for (int64_t t = pc.job.tile_begin; t < pc.job.tile_begin + pc.job.tile_count; ++t)
-      c += tile_rows(lens[pc.job.seq], t);
-    cost[pc.wg] += c;
-  }
+  for (const Piece& pc : sc.pieces)
+    cost[pc.wg] += kJobCharge + rows_between(lens[pc.job.seq], pc.job.tile_begin, pc.job.tile_begin + pc.job.tile_count);
   int64_t m = 0;
   for (int64_t c : cost) m = std::max(m, c);
   return m;
@@ -632,9 +684,7 @@ pa_status emit_plan(const Schedule& sc, int32_t schedule_id, int32_t num_kv_head
   int64_t per = 0;
   for (int32_t c : count) per = std::max<int64_t>(per, c);
   if (per * nwg > (int64_t)INT32_MAX / 64) return fail(PA_ERR_INVALID, "pa_decode_plan: plan too large");
-  std::vector<pa_decode_job> table((size_t)(per * nwg), pa_decode_job{0, 0, 0, 0, 0, 0, -1, 0});
-  std::vector<int32_t> fill(nwg, 0);
-  for (const Piece& pc : jobs) table[(size_t)fill[pc.wg]++ * nwg + pc.wg] = pc.job;
+  const size_t slots = (size_t)(per * nwg);
 
   pa_decode_plan_info in{};
   in.num_workgroups = jobs.empty() ? 0 : (int32_t)nwg;
@@ -644,7 +694,7 @@ pa_status emit_plan(const Schedule& sc, int32_t schedule_id, int32_t num_kv_head
   in.num_kv_heads = num_kv_heads;
   in.jobs_per_workgroup = jobs.empty() ? 0 : (int32_t)per;
   in.jobs_at = 0;
-  in.merges_at = (int32_t)(sizeof(pa_decode_job) * table.size());
+  in.merges_at = (int32_t)(sizeof(pa_decode_job) * slots);
   in.schedule = schedule_id;
   in.num_groups = (int32_t)sc.groups.size();
   in.groups_at = (int32_t)round_up((size_t)in.merges_at + sizeof(pa_decode_merge) * merges.size(), 64);
@@ -653,18 +703,31 @@ pa_status emit_plan(const Schedule& sc, int32_t schedule_id, int32_t num_kv_head
   // pa_decode_plan_first_blocks when the caller has the tables on the host.
   in.first_at = (int32_t)round_up((size_t)in.groups_at + sizeof(pa_decode_group) * sc.groups.size(), 64);
   in.first_block_size = 0;
-  const size_t bytes = (size_t)in.first_at + 16 * table.size();
+  const size_t bytes = (size_t)in.first_at + 16 * slots;
   if (bytes > (size_t)INT32_MAX) return fail(PA_ERR_INVALID, "pa_decode_plan: plan too large");
   in.bytes = (int32_t)bytes;
   *info = in;
   if (bytes > capacity)
     return fail(PA_ERR_INVALID, "pa_decode_plan: capacity %zu < %zu bytes", capacity, bytes);
+  // Every byte up to `bytes` is written once: the job slots (jobs, then
+  // empty slots), the merge rows, the groups, zeros in the alignment gaps
+  // and in the first-tile region.
+  if (bytes == 0) return PA_OK;
   char* out = static_cast<char*>(plan);
-  std::memset(out, 0, bytes);
-  if (!jobs.empty()) std::memcpy(out + in.jobs_at, table.data(), sizeof(pa_decode_job) * table.size());
+  char* table = out + in.jobs_at;
+  std::vector<int32_t> fill(nwg, 0);
+  for (const Piece& pc : jobs)
+    std::memcpy(table + sizeof(pa_decode_job) * ((size_t)fill[pc.wg]++ * nwg + pc.wg), &pc.job, sizeof(pa_decode_job));
+  const pa_decode_job empty{0, 0, 0, 0, 0, 0, -1, 0};
+  for (int64_t b = 0; b < nwg; ++b)
+    for (int64_t k = fill[b]; k < per; ++k)
+      std::memcpy(table + sizeof(pa_decode_job) * (size_t)(k * nwg + b), &empty, sizeof(pa_decode_job));
+  const size_t merges_end = (size_t)in.merges_at + sizeof(pa_decode_merge) * merges.size();
+  const size_t groups_end = (size_t)in.groups_at + sizeof(pa_decode_group) * sc.groups.size();
   if (!merges.empty()) std::memcpy(out + in.merges_at, merges.data(), sizeof(pa_decode_merge) * merges.size());
-  if (!sc.groups.empty())
-    std::memcpy(out + in.groups_at, sc.groups.data(), sizeof(pa_decode_group) * sc.groups.size());
+  std::memset(out + merges_end, 0, (size_t)in.groups_at - merges_end);
+  if (!sc.groups.empty()) std::memcpy(out + in.groups_at, sc.groups.data(), sizeof(pa_decode_group) * sc.groups.size());
+  std::memset(out + groups_end, 0, bytes - groups_end);
   return PA_OK;
 }
 
@@ -737,11 +800,10 @@ extern "C" pa_status pa_decode_plan_schedule(const int32_t* context_lens, int32_
   // workgroup costs less (tokens plus a charge per job) is kept, the chunks
   // on a tie.
   Schedule chunks, lpt;
-  if (schedule != PA_SCHEDULE_LPT) {
-    if (pa_status st = pagedkv::schedule_chunks(context_lens, num_seqs, num_kv_heads, num_workgroups,
-                                                max_piece_tiles > 0 ? max_piece_tiles : 64, chunks))
-      return st;
-  }
+  pagedkv::ChunkWalk walk;
+  if (schedule != PA_SCHEDULE_LPT)
+    pagedkv::walk_chunks(context_lens, num_seqs, num_kv_heads, num_workgroups,
+                         max_piece_tiles > 0 ? max_piece_tiles : 64, chunks, walk);
   if (schedule != PA_SCHEDULE_CHUNKS) {
     if (pa_status st = pagedkv::schedule_lpt(context_lens, num_seqs, num_kv_heads, num_workgroups, max_piece_tiles, lpt))
       return st;
@@ -749,6 +811,9 @@ extern "C" pa_status pa_decode_plan_schedule(const int32_t* context_lens, int32_
   const bool use_lpt = schedule == PA_SCHEDULE_LPT ||
                        (schedule == PA_SCHEDULE_AUTO && !lpt.pieces.empty() &&
                         pagedkv::schedule_cost(lpt, context_lens) < pagedkv::schedule_cost(chunks, context_lens));
+  if (!use_lpt) {
+    if (pa_status st = pagedkv::finish_chunks(context_lens, num_seqs, num_kv_heads, walk, chunks)) return st;
+  }
   return pagedkv::emit_plan(use_lpt ? lpt : chunks, use_lpt ? PA_SCHEDULE_LPT : PA_SCHEDULE_CHUNKS, num_kv_heads,
                             plan, capacity, info);
 }
