@@ -793,8 +793,8 @@ __global__ __launch_bounds__(kNW * 64) void decode_f32_kernel(DecodeArgs a) {
 // records in piece order,
 //   M = max_p m_p,  out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p.
 // One workgroup per row with G * D / 2 threads: thread t owns the two
-// adjacent outputs 2t, 2t + 1 (head 2t / D).  Pieces are taken eight at a
-// time, all of their loads issued together, and the running numerator and
+// adjacent outputs 2t, 2t + 1 (head 2t / D).  Pieces are taken in batches,
+// all loads of a batch issued together, and the running numerator and
 // denominator are rescaled when a later group raises the maximum.  An empty
 // sequence (num_parts == 0) gets zeros.
 // --------------------------------------------------------------------------
@@ -830,28 +830,12 @@ __device__ __forceinline__ void append_rows(const DecodeArgs& a, int32_t s) {
   }
 }
 
-template <int D>
-__global__ __launch_bounds__(kMaxMergeThreads) void merge_partials_kernel(DecodeArgs a) {
-  constexpr int kBatch = 8;
-  if ((int32_t)blockIdx.x >= a.num_merges) {
-    append_rows(a, (int32_t)blockIdx.x - a.num_merges);
-    return;
-  }
-  const i32x4_t mv = as_const(reinterpret_cast<const i32x4_t*>(a.merges))[blockIdx.x];
-  const pa_decode_merge mg{mv[0], mv[1], mv[2], mv[3]};
-  if (mg.seq < 0 || mg.seq >= a.num_seqs || mg.kv_head < 0 || mg.kv_head >= a.num_kv_heads) return;
+// Outputs e, e + 1 of head h (dims d, d + 1) of one cut row: its np records
+// from record_base, kBatch per round trip (one round trip when np <= kBatch).
+// head_dim 64 (fp32 pools).
+template <int D, int kBatch>
+__device__ __forceinline__ float2 merge_pair(const DecodeArgs& a, int32_t record_base, int np, int h, int d) {
   const int G = a.group;
-  const int e = 2 * (int)threadIdx.x;
-  if (e >= G * D) return;
-  const int h = e / D;
-  const int d = e - h * D;
-  const int64_t out_idx = ((int64_t)mg.seq * a.num_q_heads + (int64_t)mg.kv_head * G) * D + e;
-  const int np = mg.num_parts;
-  if (np <= 0) {
-    store2(a, out_idx, 0.f, 0.f);
-    return;
-  }
-  if (mg.record_base < 0 || (int64_t)mg.record_base + np > a.num_records) return;
   const float2* ml_all = reinterpret_cast<const float2*>(a.partial_ml);
   float M = -INFINITY, n0 = 0.f, n1 = 0.f, den = 0.f;
   for (int p0 = 0; p0 < np; p0 += kBatch) {
@@ -860,7 +844,7 @@ __global__ __launch_bounds__(kMaxMergeThreads) void merge_partials_kernel(Decode
     for (int i = 0; i < kBatch; ++i) {
       // Past the last piece, reload the last one (same cache line) so every
       // load is issued unconditionally; the values are not used.
-      const int64_t rec = (int64_t)(mg.record_base + min(p0 + i, np - 1)) * G + h;
+      const int64_t rec = (int64_t)(record_base + min(p0 + i, np - 1)) * G + h;
       ml[i] = ml_all[rec];
       ov[i] = *reinterpret_cast<const float2*>(a.partial_o + rec * D + d);
     }
@@ -885,7 +869,106 @@ __global__ __launch_bounds__(kMaxMergeThreads) void merge_partials_kernel(Decode
     }
   }
   const float inv = den > 0.f ? 1.0f / den : 0.f;
-  store2(a, out_idx, n0 * inv, n1 * inv);
+  return make_float2(n0 * inv, n1 * inv);
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+// The same for head_dim 128, where a wavefront's 64 threads cover one head:
+// lane i holds the (max, sum) of piece p0 + i, so a batch costs every lane one
+// (max, sum) load and kBatch accumulator loads; the batch maximum and the
+// denominator are wavefront reductions and piece i's weight is read from
+// lane i.
+template <int kBatch>
+__device__ __forceinline__ float2 merge_pair_wave(const DecodeArgs& a, int32_t record_base, int np, int h, int d,
+                                                  int lane) {
+  constexpr int D = 128;
+  static_assert(kBatch <= 64, "one piece per lane");
+  const int G = a.group;
+  h = __builtin_amdgcn_readfirstlane(h);
+  const float2* ml_all = reinterpret_cast<const float2*>(a.partial_ml);
+  float M = -INFINITY, n0 = 0.f, n1 = 0.f, den = 0.f;
+  for (int p0 = 0; p0 < np; p0 += kBatch) {
+    const int pl = min(p0 + min(lane, kBatch - 1), np - 1);
+    const float2 ml = ml_all[(int64_t)(record_base + pl) * G + h];
+    float2 ov[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int64_t rec = (int64_t)(record_base + min(p0 + i, np - 1)) * G + h;
+      ov[i] = *reinterpret_cast<const float2*>(a.partial_o + rec * D + d);
+    }
+    const bool live = lane < kBatch && p0 + lane < np;
+    const float mc = fmaxf(M, wave_max(live ? ml.x : -INFINITY));
+    if (mc == -INFINITY) continue;
+    const float r = fast_exp2(M - mc);  // 0 while M is still -inf
+    n0 *= r;
+    n1 *= r;
+    den *= r;
+    M = mc;
+    const float f = live ? fast_exp2(ml.x - M) : 0.f;
+    den += wave_sum(f * ml.y);
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      if (p0 + i < np) {
+        const float fi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), i));
+        n0 += fi * ov[i].x;
+        n1 += fi * ov[i].y;
+      }
+    }
+  }
+  const float inv = den > 0.f ? 1.0f / den : 0.f;
+  return make_float2(n0 * inv, n1 * inv);
+}
+
+// The batch follows the row: 4 pieces for short rows (most of them), 16 or
+// kMaxBatch for longer ones, so that a row of up to kMaxBatch pieces takes one
+// round trip without every thread of a short row issuing kMaxBatch loads.
+template <int D, int kMaxBatch>
+__global__ __launch_bounds__(kMaxMergeThreads) void merge_partials_kernel(DecodeArgs a) {
+  if ((int32_t)blockIdx.x >= a.num_merges) {
+    append_rows(a, (int32_t)blockIdx.x - a.num_merges);
+    return;
+  }
+  const i32x4_t mv = as_const(reinterpret_cast<const i32x4_t*>(a.merges))[blockIdx.x];
+  const pa_decode_merge mg{mv[0], mv[1], mv[2], mv[3]};
+  if (mg.seq < 0 || mg.seq >= a.num_seqs || mg.kv_head < 0 || mg.kv_head >= a.num_kv_heads) return;
+  const int G = a.group;
+  const int e = 2 * (int)threadIdx.x;
+  if (e >= G * D) return;
+  const int h = e / D;
+  const int d = e - h * D;
+  const int64_t out_idx = ((int64_t)mg.seq * a.num_q_heads + (int64_t)mg.kv_head * G) * D + e;
+  const int np = mg.num_parts;
+  if (np <= 0) {
+    store2(a, out_idx, 0.f, 0.f);
+    return;
+  }
+  if (mg.record_base < 0 || (int64_t)mg.record_base + np > a.num_records) return;
+  float2 r;
+  if (D == 128) {
+    const int lane = threadIdx.x & 63;
+    if (np <= 4)
+      r = merge_pair_wave<4>(a, mg.record_base, np, h, d, lane);
+    else if (np <= 16)
+      r = merge_pair_wave<16>(a, mg.record_base, np, h, d, lane);
+    else
+      r = merge_pair_wave<kMaxBatch>(a, mg.record_base, np, h, d, lane);
+  } else {
+    if (np <= 4)
+      r = merge_pair<D, 4>(a, mg.record_base, np, h, d);
+    else
+      r = merge_pair<D, kMaxBatch>(a, mg.record_base, np, h, d);
+  }
+  store2(a, out_idx, r.x, r.y);
 }
 
 }  // namespace
@@ -938,11 +1021,11 @@ hipError_t launch_decode_attention(const DecodeArgs& a, hipStream_t stream) {
 hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t stream) {
   const int64_t blocks = (int64_t)a.num_merges + (a.new_k != nullptr ? a.num_seqs : 0);
   if (blocks == 0) return hipSuccess;
-  const dim3 block((unsigned)(a.group * a.head_dim / 2));
+  const dim3 grid((unsigned)blocks), block((unsigned)(a.group * a.head_dim / 2));
   if (a.head_dim == 128)
-    hipLaunchKernelGGL(merge_partials_kernel<128>, dim3((unsigned)blocks), block, 0, stream, a);
+    hipLaunchKernelGGL((merge_partials_kernel<128, 32>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL(merge_partials_kernel<64>, dim3((unsigned)blocks), block, 0, stream, a);
+    hipLaunchKernelGGL((merge_partials_kernel<64, 8>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
