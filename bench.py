@@ -6,9 +6,12 @@ heads (group 4), head_dim 128, block size 16, context lengths lognormal with
 mean about 200 tokens capped at 4096, blocks handed out from a shuffled free
 list.  One step is one pass of the whole hot path over one batch:
   pa_copy_blocks (copy-on-write pairs of this step; none in this workload)
-  -> pa_reshape_and_cache (this step's token for every sequence)
-  -> pa_decode (attention through the block tables on a persistent grid, then
-     the merge of cut sequences).
+  -> pa_decode with this step's new keys and values: the attention launch
+     (through the block tables, on a persistent grid) takes every sequence's
+     token L - 1 from them, and the merge launch (cut sequences) stores that
+     token into its slot, which is pa_reshape_and_cache's work, fused.
+The same step as three calls (pa_copy_blocks -> pa_reshape_and_cache ->
+pa_decode without new keys/values) is timed too (ms_per_step_eager).
 Step inputs (tables, lengths, slots, the decode plan, queries, new keys and
 values) are resident in device memory before timing; the host block-manager
 append and the host plan that produce them are timed separately
@@ -17,11 +20,13 @@ times the 256 MB last-level cache) rotate so that KV reads come from HBM.
 
 Prints one JSON line.  `value` is KV-read GB/s over whole steps: algorithmic KV
 bytes (each live token's K and V row of each KV head, read once) per step
-divided by the step time.  `roofline` reports the attention kernel alone: the
-same algorithmic bytes over its average launch time, from HIP events on the
-stream the launches run on around K back-to-back attention launches (a second
-timed region after the steps; pa_decode is issued as its two launches,
-pa_decode_attention and pa_decode_merge_pieces, for this).
+divided by the step time.  `roofline` reports the step's attention launch
+alone (append fused): the same algorithmic bytes over its average launch time,
+from HIP events on the stream the launches run on around K back-to-back
+attention launches (a second timed region after the steps; pa_decode is issued
+as its two launches, pa_decode_attention and pa_decode_merge_pieces, for
+this).  The launch without the fused append (as in the three-call step) is
+timed the same way (attention_launch_unfused_us, unfused_frac).
 """
 from __future__ import annotations
 
@@ -519,19 +524,27 @@ def main() -> int:
             pk.reshape_and_cache(pool, new_k, new_v, slots_d, st)
         pk.decode(pool, q_d, tables_d, lens_d, case["scale"], plan, plan_d, ws, out, st)
 
-    def step_fused(r: int):
-        # The same step with the append fused into the attention launch:
-        # pa_decode stores every sequence's token L - 1 from new_k/new_v.
+    def step_fused(r: int, st=None):
+        # The step: the append fused into pa_decode, which stores every
+        # sequence's token L - 1 from new_k/new_v into its slot.
+        st = st or stream
         pool = pools[r]
-        pk.copy_blocks(pool, cows_d, stream)
-        pk.decode(pool, q_d, tables_d, lens_d, case["scale"], plan, plan_d, ws, out, stream,
+        if not args.decode_only:
+            pk.copy_blocks(pool, cows_d, st)
+        pk.decode(pool, q_d, tables_d, lens_d, case["scale"], plan, plan_d, ws, out, st,
                   new_key=new_k, new_value=new_v)
 
     def attention(r: int):
+        # The step's attention launch (append fused).
+        pk.decode(pools[r], q_d, tables_d, lens_d, case["scale"], plan, plan_d, ws, out, stream, stage="attention",
+                  new_key=new_k, new_value=new_v)
+
+    def attention_unfused(r: int):
         pk.decode(pools[r], q_d, tables_d, lens_d, case["scale"], plan, plan_d, ws, out, stream, stage="attention")
 
     def decode_call(r: int):
-        pk.decode(pools[r], q_d, tables_d, lens_d, case["scale"], plan, plan_d, ws, out, stream)
+        pk.decode(pools[r], q_d, tables_d, lens_d, case["scale"], plan, plan_d, ws, out, stream,
+                  new_key=new_k, new_value=new_v)
 
     def timed(fn, n: int) -> float:
         """Milliseconds per call of n back-to-back calls, from HIP events
@@ -546,12 +559,11 @@ def main() -> int:
         return start.elapsed_time(end) / n
 
     for k in range(args.warmup):
-        step(k % R)
+        step_fused(k % R)
     torch.cuda.synchronize()
 
     # The timed region: K whole steps.
-    ms_per_step_eager = timed(step, args.steps)
-    ms_per_step = ms_per_step_eager
+    ms_per_step = timed(step_fused, args.steps)
     if args.graph:
         # One step per pool replica captured as a HIP graph, replayed in turn.
         cap = torch.cuda.Stream()
@@ -559,16 +571,21 @@ def main() -> int:
         for r in range(R):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=cap):
-                step(r, cap)
+                step_fused(r, cap)
             graphs.append(g)
         for k in range(args.warmup):
             graphs[k % R].replay()
         torch.cuda.synchronize()
         ms_per_step = timed(lambda r: graphs[r].replay(), args.steps)
-    ms_per_step_fused = timed(step_fused, args.steps)
+    # The same step as three calls, after its own warm-up.
+    for k in range(args.warmup):
+        step(k % R)
+    ms_per_step_eager = timed(step, args.steps)
     # The dominant kernel alone: K attention launches back to back (same
-    # inputs, rotating pool replicas), then K whole pa_decode calls.
+    # inputs, rotating pool replicas); the same without the fused append; K
+    # whole pa_decode calls.
     attention_us = timed(attention, args.steps) * 1e3
+    attention_unfused_us = timed(attention_unfused, args.steps) * 1e3
     decode_us = timed(decode_call, args.steps) * 1e3
     pk.decode(pools[0], q_d, tables_d, lens_d, case["scale"], plan, plan_d, ws, out, stream)   # leave a complete result
     torch.cuda.synchronize()
@@ -591,7 +608,6 @@ def main() -> int:
         "ms_per_step": round(ms_per_step, 5),
         "ms_per_step_eager": round(ms_per_step_eager, 5),
         "graph": bool(args.graph),
-        "ms_per_step_fused_append": round(ms_per_step_fused, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -619,11 +635,13 @@ def main() -> int:
         "us_per_output_token": round(ms_per_step * 1e3 / S, 5),
         "decode_call_us": round(decode_us, 3),
         "attention_launch_us": round(attention_us, 3),
+        "attention_launch_unfused_us": round(attention_unfused_us, 3),
+        "unfused_frac": round(kv_bytes / (attention_unfused_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
         "host_append_us": round(host_append_us, 2),
         "host_plan_us": round(host_plan_us, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(name, schedule),
-                     "kernel": "decode_bf16_kernel (the attention launch of pa_decode)",
+                     "kernel": "decode_bf16_kernel (the attention launch of pa_decode, append fused)",
                      "bytes_per_launch": kv_bytes},
     }
     if "prefix_cache" in w:

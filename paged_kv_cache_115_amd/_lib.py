@@ -36,7 +36,7 @@ class PaDecodePlanInfo(ctypes.Structure):
                 ("jobs_at", ctypes.c_int32), ("merges_at", ctypes.c_int32), ("bytes", ctypes.c_int32),
                 ("flags", ctypes.c_int32), ("schedule", ctypes.c_int32), ("num_groups", ctypes.c_int32),
                 ("groups_at", ctypes.c_int32), ("group_size", ctypes.c_int32), ("first_at", ctypes.c_int32),
-                ("first_block_size", ctypes.c_int32)]
+                ("first_block_size", ctypes.c_int32), ("num_tiles", ctypes.c_int32)]
 
 
 class PaBmStats(ctypes.Structure):

@@ -703,6 +703,9 @@ pa_status emit_plan(const Schedule& sc, int32_t schedule_id, int32_t num_kv_head
   // pa_decode_plan_first_blocks when the caller has the tables on the host.
   in.first_at = (int32_t)round_up((size_t)in.groups_at + sizeof(pa_decode_group) * sc.groups.size(), 64);
   in.first_block_size = 0;
+  int64_t tiles = 0;
+  for (const Piece& pc : jobs) tiles += pc.job.tile_count;
+  in.num_tiles = (int32_t)tiles;
   const size_t bytes = (size_t)in.first_at + 16 * slots;
   if (bytes > (size_t)INT32_MAX) return fail(PA_ERR_INVALID, "pa_decode_plan: plan too large");
   in.bytes = (int32_t)bytes;
@@ -968,6 +971,15 @@ pa_status decode_stages(int stages, const char* who, const pa_kv_pool* pool, con
   a.scale_log2e = scale * 1.4426950408889634f;
   a.bf16 = pool->dtype == PA_BF16;
   a.shared_kv = (info->flags & PA_DECODE_SHARED_KV) != 0;
+  // With the append fused, the tile holding a sequence's appended token
+  // mixes pool rows and the new row.  Loading it on a path of its own costs a
+  // wait for every load in flight where the paths join, once per job that
+  // ends a sequence; loading every tile through per-lane addresses avoids
+  // that but loses the streaming cache policy of buffer loads on every tile.
+  // The first pays when sequences are short (a job end every few tiles).
+  constexpr int64_t kShortSequenceTiles = 24;
+  const int64_t seq_streams = (int64_t)num_seqs * ((hkv + 3) / 4);
+  a.fused_loads = new_key == nullptr ? 0 : (int64_t)info->num_tiles < kShortSequenceTiles * seq_streams ? 2 : 1;
   if (stages & kStageAttention) {
     if (pa_status st = pagedkv::hip_status(pagedkv::launch_decode_attention(a, (hipStream_t)stream), who)) return st;
   }

@@ -244,7 +244,7 @@ __device__ __forceinline__ uint4 load_global(const char* p) {
 // the context.  The range check covers the vector offset and the
 // instruction's immediate, not the scalar offset, so every per-row offset is
 // in the vector offset.
-template <int B, bool kStream, bool kFused>
+template <int B, bool kStream, int kFused>
 __device__ __forceinline__ void load_bf16_tile(const DecodeArgs& a, int32_t g, int32_t t0, int32_t e0, int32_t e1,
                                                int32_t t, int32_t rows, int32_t r_new, const char* nk,
                                                const char* nv, int li, int lq, uint4 (&kf)[4], uint4 (&vf)[4]) {
@@ -255,22 +255,28 @@ __device__ __forceinline__ void load_bf16_tile(const DecodeArgs& a, int32_t g, i
   const char* kb = reinterpret_cast<const char*>(a.k) + (int64_t)g * D * 2;
   const char* vb = reinterpret_cast<const char*>(a.v) + (int64_t)g * D * 2;
   const int32_t p0 = clamp_block(e0, a.num_blocks);
-  if (kFused && r_new >= 0) {
-    // The tile holding this step's appended token (row r_new): that row
-    // comes from the new key/value arrays, rows after it (past the context)
-    // read the same row and are masked later, rows before it come from the
-    // pool.  Per-lane addresses, so plain global loads.
-    const int32_t p1 = B == 8 ? clamp_block(e1, a.num_blocks) : p0;
-    auto row_addr = [&](const char* base, int32_t row) {
-      if (B == 8) return base + (int64_t)(row < 8 ? p0 : p1) * blk_bytes + (row & 7) * row_bytes;
-      return base + (int64_t)p0 * blk_bytes + ((int64_t)((t0 + t) % kTilesPerBlock) * kTile + row) * row_bytes;
-    };
+  // With the append fused (kFused 1 or 2), row r_new of the tile holding the
+  // appended token and the rows after it (past the context; masked in
+  // compute) come from the new key/value row, the rows before it from the
+  // pool, through per-lane addresses.  kFused 1 loads only that tile so, on a
+  // path of its own; kFused 2 loads every tile so (a filler load, rows 0,
+  // reads the new row, which stays in L2): one load path, and no wait for
+  // the loads in flight where two paths would join, at the price of the
+  // buffer loads' cache policy.
+  const int32_t p1f = B == 8 ? clamp_block(e1, a.num_blocks) : p0;
+  auto row_addr = [&](const char* base, int32_t row) {
+    if (B == 8) return base + (int64_t)(row < 8 ? p0 : p1f) * blk_bytes + (row & 7) * row_bytes;
+    return base + (int64_t)p0 * blk_bytes + ((int64_t)((t0 + t) % kTilesPerBlock) * kTile + row) * row_bytes;
+  };
+  if (kFused == 2 || (kFused == 1 && r_new >= 0)) {
+    const int32_t first_new = r_new >= 0 ? r_new : rows <= 0 ? 0 : kTile;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
-      kf[ks] = load_global<kStream>(li >= r_new ? nk + 16 * (4 * ks + lq) : row_addr(kb, li) + 16 * (4 * ks + lq));
+      kf[ks] = load_global<kStream>(li >= first_new ? nk + 16 * (4 * ks + lq)
+                                                    : row_addr(kb, li) + 16 * (4 * ks + lq));
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      vf[r] = load_global<kStream>(4 * lq + r >= r_new ? nv + 16 * li : row_addr(vb, 4 * lq + r) + 16 * li);
+      vf[r] = load_global<kStream>(4 * lq + r >= first_new ? nv + 16 * li : row_addr(vb, 4 * lq + r) + 16 * li);
   } else if (B == 8) {
     // Rows 0..7 of the tile live in block p0, rows 8..15 in block p1.
     const int32_t p1 = clamp_block(e1, a.num_blocks);
@@ -529,7 +535,7 @@ __device__ __forceinline__ void finish_bf16_job(const DecodeArgs& a, const JobVi
   sg.n = e + 1;
 }
 
-template <int B, bool kStream, bool kFused>
+template <int B, bool kStream, int kFused>
 __global__ __launch_bounds__(kNW * 64, kWavesPerSimd) void decode_bf16_kernel(DecodeArgs a) {
   static_assert(B == 8 || B == 16 || B == 32, "block size");
   const int lane = threadIdx.x & 63;
@@ -640,7 +646,7 @@ __global__ __launch_bounds__(kNW * 64, kWavesPerSimd) void decode_bf16_kernel(De
     const int32_t rows = live ? L - kTile * (t0 + t) : 0;
     // Row of this step's appended token in the tile, when the append is fused
     // into this launch and the tile holds it.
-    const int32_t r_new = (kFused && live && rows >= 1 && rows <= kTile) ? rows - 1 : -1;
+    const int32_t r_new = (kFused != 0 && live && rows >= 1 && rows <= kTile) ? rows - 1 : -1;
     const int32_t seq = in_n ? nxt.v.seq : in_n2 ? nx2.v.seq : cur.v.seq;
     const int64_t new_row = ((int64_t)seq * a.num_kv_heads + g) * kHeadDim * 2;
     const char* nk = reinterpret_cast<const char*>(a.new_k) + new_row;
@@ -979,10 +985,12 @@ hipError_t launch_decode_attention(const DecodeArgs& a, hipStream_t stream) {
   bool launched = false;
   if (a.bf16) {
 #define PA_BF16_LAUNCH(BS, STREAM)                                                                      \
-  if (a.new_k != nullptr)                                                                               \
-    hipLaunchKernelGGL((decode_bf16_kernel<BS, STREAM, true>), grid, dim3(kNW * 64), 0, stream, a);     \
+  if (a.new_k == nullptr)                                                                               \
+    hipLaunchKernelGGL((decode_bf16_kernel<BS, STREAM, 0>), grid, dim3(kNW * 64), 0, stream, a);        \
+  else if (a.fused_loads == 2)                                                                          \
+    hipLaunchKernelGGL((decode_bf16_kernel<BS, STREAM, 2>), grid, dim3(kNW * 64), 0, stream, a);        \
   else                                                                                                  \
-    hipLaunchKernelGGL((decode_bf16_kernel<BS, STREAM, false>), grid, dim3(kNW * 64), 0, stream, a);
+    hipLaunchKernelGGL((decode_bf16_kernel<BS, STREAM, 1>), grid, dim3(kNW * 64), 0, stream, a);
 #define PA_BF16_CASE(BS)                                                                                \
   case BS:                                                                                              \
     if (a.shared_kv) {                                                                                  \
@@ -1030,7 +1038,7 @@ hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t stream) {
 }
 
 hipError_t decode_resident_workgroups_per_cu(int* n) {
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, decode_bf16_kernel<16, true, false>, kNW * 64, 0);
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, decode_bf16_kernel<16, true, 0>, kNW * 64, 0);
 }
 
 }  // namespace pagedkv

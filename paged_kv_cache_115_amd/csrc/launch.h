@@ -41,6 +41,8 @@ struct DecodeArgs {
   int32_t bf16;                  // pool dtype: 1 bfloat16, 0 float32
   int32_t shared_kv;             // 1: sequences share blocks (keep K/V cached), 0: stream K/V
   int32_t out_bf16;              // 1: write bfloat16, 0: float32
+  int32_t fused_loads;           // with new_k: 1 a branch at the appended token's tile, 2 per-lane
+                                 // addresses for every tile (one load path)
   float scale_log2e;             // scale * log2(e)
 };
 

@@ -154,15 +154,21 @@ def test_fused_append_equals_separate_cache_write(pk, name, schedule):
     assert_close(fused["out"], ref["out"], case["cfg"]["dtype"], f"fused {name}/{schedule}")
 
 
+@pytest.mark.parametrize("long_context", [False, True])
 @pytest.mark.parametrize("b", [8, 16, 32])
-def test_fused_append_edge_lengths(pk, b):
+def test_fused_append_edge_lengths(pk, b, long_context):
     """The appended token at every position of a tile and of a block, in
-    empty, one-token and full-table contexts, for each block size."""
+    empty, one-token and full-table contexts, for each block size.  These
+    contexts average 18 tiles, so the library loads every tile through
+    per-lane addresses; one added 12,000-token context lifts the average to
+    about 50, where only the appended token's tile is loaded that way."""
     lens = [0, 1, 7, 8, 9, 15, 16, 17, 31, 32, 33, 63, 64, 65, 0, 255, 256, 257, 1023, 1024, 1025, 2100]
+    if long_context:
+        lens.append(12000)
     case = _edge_case(lens, b)
     ref = oracle_decode_step(case)
     for schedule in (DEFAULT, TINY_PIECES, (5, 64)):
-        log(f"fused edge lengths B={b} schedule={schedule}")
+        log(f"fused edge lengths B={b} long={long_context} schedule={schedule}")
         got = product_decode_step(pk, case, schedule, fused=True)
         assert np.array_equal(bits(got["kpool"]), bits(ref["kpool"]))
         assert np.array_equal(bits(got["vpool"]), bits(ref["vpool"]))
