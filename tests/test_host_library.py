@@ -621,6 +621,7 @@ def test_decode_plan_covers_every_tile_once(seed):
             for t in range(tiles):
                 assert (s, blk, t) in covered
     assert len(covered) == sum(-(-int(L) // 16) for L in lens) * hb
+    assert plan.info.num_tiles == len(covered) == int(jobs[:, 2].sum())
     assert plan.num_workgroups <= nwg and len(jobs) == plan.num_jobs
     if plan.num_jobs:
         tab = plan.job_table()
@@ -884,6 +885,8 @@ def _check_prefix_plan(plan, lens, hkv, hq, group, tokens):
         for hb in range(hb_n):
             for t in range(-(-int(L) // 16)):
                 assert (s, hb, t) in covered
+    # num_tiles counts the tiles read: a shared tile once for its whole group
+    assert plan.info.num_tiles == sum(j[2] for j in jobs)
     # every group's members: shared tiles below T, same T for all, records consistent
     used = set()
     for d in groups:
