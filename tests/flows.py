@@ -56,8 +56,9 @@ def assert_close(out: np.ndarray, ref: np.ndarray, dt: str, where: str = "") -> 
 
 
 def plan_and_workspace(pk, lens: np.ndarray, hkv: int, hq: int, d: int, num_workgroups=None, max_piece_tiles=0,
-                       shared_kv=False):
-    plan = pk.decode_plan(lens, hkv, num_workgroups, max_piece_tiles, shared_kv=shared_kv)
+                       kind=-1, shared_kv=False):
+    """kind: a pk.SCHEDULE_* value (-1, the default: the automatic choice)."""
+    plan = pk.decode_plan(lens, hkv, num_workgroups, max_piece_tiles, shared_kv=shared_kv, schedule=kind)
     nbytes = pk.decode_workspace_bytes(plan, hq, d)
     # The workspace needs no initialisation: fill it with NaN to prove it.
     ws = torch.full((nbytes // 4,), float("nan"), dtype=torch.float32, device="cuda") if nbytes else None
@@ -66,7 +67,7 @@ def plan_and_workspace(pk, lens: np.ndarray, hkv: int, hq: int, d: int, num_work
 
 def gpu_decode(pk, pool, q_dev, tables, lens, scale, schedule=(None, 0), out_dtype=torch.float32, shared_kv=False,
                new_key=None, new_value=None, first_blocks=False):
-    """schedule = (num_workgroups or None for the device default, max_piece_tiles).
+    """schedule = (num_workgroups or None for the device default, max_piece_tiles[, schedule kind]).
     new_key/new_value: fuse this step's append into the decode call.
     first_blocks: write the jobs' first-tile table entries into the plan."""
     hq = q_dev.shape[1]

@@ -270,6 +270,31 @@ def _edge_case(lens, b, hq=32, hkv=8, d=128, seed=31):
                 offsets=np.concatenate([[0], np.cumsum(lens)]), scale=synth.default_scale(d))
 
 
+@pytest.mark.parametrize("dt,d", [("bf16", 128), ("f32", 64)])
+@pytest.mark.parametrize("cap,parts", [(25, 4), (7, 15), (3, 34), (1, 100)])
+def test_merge_of_many_pieces(pk, dt, d, cap, parts):
+    """Rows cut into 4, 15, 34 and 100 pieces: the merge launch takes a row's
+    pieces in batches (4, 16 or 32 at a time for head_dim 128, 4 or 8 for
+    64), so these rows cover one batch of each size and several batches of
+    the largest, against the oracle."""
+    lens = np.array([1600, 1599, 5, 300, 0], dtype=np.int32)
+    case = _edge_case(lens, 16, hq=8, hkv=4, d=d, seed=71)
+    if dt == "f32":
+        rng = np.random.default_rng(72)
+        total = int(lens.sum())
+        case["cfg"]["dtype"] = "f32"
+        case["keys"] = rng.standard_normal((total, 4, d), dtype=np.float32)
+        case["values"] = rng.standard_normal((total, 4, d), dtype=np.float32)
+        case["q"] = rng.standard_normal((len(lens), 8, d), dtype=np.float32)
+    plan = pk.decode_plan(lens, 4, max_piece_tiles=cap, schedule=pk.SCHEDULE_LPT)
+    assert int(plan.merges()[:, 2].max()) == parts
+    log(f"merge of {parts} pieces {dt} D={d}")
+    got = product_decode_step(pk, case, (None, cap, pk.SCHEDULE_LPT))
+    ref = oracle_decode_step(case)
+    assert np.array_equal(got["out"][4], np.zeros_like(got["out"][4]))
+    assert_close(got["out"], ref["out"], dt, f"merge {parts} pieces {dt}")
+
+
 @pytest.mark.parametrize("b", [8, 16, 32])
 def test_edge_lengths(pk, b):
     """Empty contexts, one token, exact block/tile multiples and one past
