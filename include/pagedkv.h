@@ -210,7 +210,8 @@ typedef struct pa_decode_plan_info {
                              table entries of the job's first two tiles (pa_decode_plan_first_blocks) */
   int32_t first_block_size; /* block size those entries were written for (0: not written) */
   int32_t num_tiles;      /* 16-token tiles the jobs read, summed over jobs (with the append fused,
-                             pa_decode picks how tiles are loaded from tiles per sequence) */
+                             pa_decode picks how tiles are loaded from the tiles per sequence and the
+                             query heads per KV head) */
 } pa_decode_plan_info;
 
 /* A job whose head_block field has this bit reads a prefix shared by the

@@ -976,10 +976,16 @@ pa_status decode_stages(int stages, const char* who, const pa_kv_pool* pool, con
   // wait for every load in flight where the paths join, once per job that
   // ends a sequence; loading every tile through per-lane addresses avoids
   // that but loses the streaming cache policy of buffer loads on every tile.
-  // The first pays when sequences are short (a job end every few tiles).
+  // Measured on MI355X: per-lane addresses everywhere are faster where
+  // sequences are short (a job end every few tiles: batch 256, mean 200
+  // tokens) and for one query head per KV head (batch 64 of up to 2048
+  // tokens, 3%); the separate path is faster for long contexts with 4 or 8
+  // query heads per KV head (16 x 16-32k tokens, 3%; 2000-token shared
+  // prefixes, 2%).
   constexpr int64_t kShortSequenceTiles = 24;
   const int64_t seq_streams = (int64_t)num_seqs * ((hkv + 3) / 4);
-  a.fused_loads = new_key == nullptr ? 0 : (int64_t)info->num_tiles < kShortSequenceTiles * seq_streams ? 2 : 1;
+  const bool short_seqs = (int64_t)info->num_tiles < kShortSequenceTiles * seq_streams;
+  a.fused_loads = new_key == nullptr ? 0 : (short_seqs || group < 4) ? 2 : 1;
   if (stages & kStageAttention) {
     if (pa_status st = pagedkv::hip_status(pagedkv::launch_decode_attention(a, (hipStream_t)stream), who)) return st;
   }
