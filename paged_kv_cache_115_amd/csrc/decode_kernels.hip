@@ -29,9 +29,10 @@
 //
 // bf16 path (head_dim 128, G <= 16): both contractions run on MFMA.
 //   S^T[token][head] = K_tile[16 x 128] . Q^T[128 x 16]  with
-//     v_mfma_f32_16x16x32_bf16; K is the A operand, loaded straight from the
-//     pool (lane = token row, 16 bytes = 8 dims); Q^T is the B operand, kept in
-//     registers (query heads beyond G are zero).
+//     v_mfma_f32_16x16x32_bf16; K is the A operand (lane = token row, 16 bytes
+//     = 8 dims).  K is read like V below, in whole 256-byte rows, and put into
+//     that layout through the wavefront's own LDS area; Q^T is the B operand,
+//     kept in registers (query heads beyond G are zero).
 //   O^T[dim][head] += V^T[dims x 16 tokens] . P^T[16 tokens x 16 heads] with
 //     v_mfma_f32_16x16x16_bf16.  The S^T result layout (lane holds tokens
 //     4q..4q+3 of head lane%16) is exactly the B-operand layout P^T needs, so
@@ -40,6 +41,9 @@
 //     8i .. 8i + 7.  Instance c of the PV product maps its row i to dim
 //     8i + c, so its A operand is assembled from the loaded registers by
 //     16-bit lane-local shuffles (no LDS round trip, no cross-lane transpose).
+//   With this step's append fused (new_key/new_value), the tile holding
+//   token L - 1 takes that row from the new arrays; the merge launch stores
+//   it into its slot afterwards.
 //   Probabilities are rounded to bf16 for the PV product and the running sum
 //   adds the same rounded values, so numerator and denominator agree.
 //   A job's block-table entries sit in one vector register (lane i: tile i)
@@ -277,8 +281,8 @@ __device__ __forceinline__ void load_bf16_tile(const DecodeArgs& a, int32_t g, i
   if (kFused == 2 || (kFused == 1 && r_new >= 0)) {
     const int32_t first_new = r_new >= 0 ? r_new : rows <= 0 ? 0 : kTile;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      kf[ks] = load_global<kStream>(4 * lq + ks >= first_new ? nk + 16 * li : row_addr(kb, 4 * lq + ks) + 16 * li);
+    for (int r = 0; r < 4; ++r)
+      kf[r] = load_global<kStream>(4 * lq + r >= first_new ? nk + 16 * li : row_addr(kb, 4 * lq + r) + 16 * li);
 #pragma unroll
     for (int r = 0; r < 4; ++r)
       vf[r] = load_global<kStream>(4 * lq + r >= first_new ? nv + 16 * li : row_addr(vb, 4 * lq + r) + 16 * li);
