@@ -2,7 +2,9 @@
 
 Each workload runs at its full size with the device-default schedule
 (resident workgroups, automatic piece length), through the C++ block manager,
-pa_copy_blocks / pa_reshape_and_cache and pa_decode.  Block tables, slots and
+pa_copy_blocks / pa_reshape_and_cache and pa_decode, and the decode step once
+more as bench.py times it (the append fused into pa_decode, first-tile
+entries in the plan).  Block tables, slots and
 both pools are compared in full: bit-exact.  Attention outputs are compared on
 sampled sequences that the float64 oracle computes one by one: the longest,
 the shortest, the ones the plan cuts into the most pieces, and a seeded random
@@ -62,6 +64,14 @@ def test_full_size_decode_step(pk, name):
     assert np.all(np.isfinite(got["out"]))
     stats = assert_close(got["out"][seqs], ref["out"][seqs], cfg["dtype"], name)
     log(f"  max|err|={stats['max_abs']:.3g} mean|err|={stats['mean_abs']:.3g}")
+    # The step bench.py times: the append fused into pa_decode, with the
+    # plan's first-tile entries.  Pools as the oracle's, output bitwise that
+    # of the three calls.
+    log(f"full-size decode {name}: append fused, first-tile entries")
+    fused = product_decode_step(pk, case, DEFAULT, fused=True, first_blocks=True)
+    assert np.array_equal(bits(fused["kpool"]), bits(ref["kpool"]))
+    assert np.array_equal(bits(fused["vpool"]), bits(ref["vpool"]))
+    assert np.array_equal(bits(fused["out"]), bits(got["out"]))
 
 
 @pytest.mark.timeout(600)
