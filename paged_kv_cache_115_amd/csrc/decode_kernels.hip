@@ -623,10 +623,14 @@ __global__ __launch_bounds__(kNW * 64, kWavesPerSimd) void decode_bf16_kernel(De
   JobRef<B> cur, nxt, nx2;
   load_ref<B>(a, r0, w, lane, cur);
   load_ref<B>(a, r1, w, lane, nxt);
-  load_ref<B>(a, r2, w, lane, nx2);
+  // The third job's table entries and the second job's query are requested
+  // after the first two positions (below): the vector memory counter retires
+  // loads in issue order, so the first tile's wait would otherwise also wait
+  // for them.  The first two positions never reach the third job.
+  view_job(a, r2, w, B, nx2.v);
+  nx2.tb0 = nx2.tb1 = 0;
   bf16x8_t qc[4], qn[4];
   load_q(a, cur.v, li, lq, qc);
-  load_q(a, nxt.v, li, lq, qn);
   SoftmaxState st;
   st.reset();
   int32_t x = 0, x0 = 0;
@@ -711,6 +715,8 @@ __global__ __launch_bounds__(kNW * 64, kWavesPerSimd) void decode_bf16_kernel(De
 #pragma unroll
     for (int u = 0; u < kDepth; ++u) issue(u, kf[u], vf[u]);
   }
+  load_ref<B>(a, r2, w, lane, nx2);
+  load_q(a, nxt.v, li, lq, qn);
   // The slot ring, unrolled so that every slot index is a constant and the
   // slots stay in registers.
   while (true) {
