@@ -622,11 +622,14 @@ __global__ __launch_bounds__(kNW * 64, kWavesPerSimd) void decode_bf16_kernel(De
   // compiler inserts count exactly the loads in flight.
   JobRef<B> cur, nxt, nx2;
   load_ref<B>(a, r0, w, lane, cur);
-  load_ref<B>(a, r1, w, lane, nxt);
-  // The third job's table entries and the second job's query are requested
-  // after the first two positions (below): the vector memory counter retires
-  // loads in issue order, so the first tile's wait would otherwise also wait
-  // for them.  The first two positions never reach the third job.
+  view_job(a, r1, w, B, nxt.v);
+  nxt.tb0 = nxt.tb1 = 0;
+  // The third job's table entries and the second job's query, and with the
+  // plan's first-tile entries the second job's table entries too, are
+  // requested after the first two positions (below): the vector memory
+  // counter retires loads in issue order, so the first tile's wait would
+  // otherwise also wait for them.  The first two positions never reach the
+  // third job, and with first-tile entries they read no table.
   view_job(a, r2, w, B, nx2.v);
   nx2.tb0 = nx2.tb1 = 0;
   bf16x8_t qc[4], qn[4];
@@ -711,7 +714,9 @@ __global__ __launch_bounds__(kNW * 64, kWavesPerSimd) void decode_bf16_kernel(De
   if (a.first_blocks != nullptr) {
 #pragma unroll
     for (int u = 0; u < kDepth; ++u) issue_at(u, kf[u], vf[u], true, f0, f1);
+    load_ref<B>(a, r1, w, lane, nxt);
   } else {
+    load_ref<B>(a, r1, w, lane, nxt);
 #pragma unroll
     for (int u = 0; u < kDepth; ++u) issue(u, kf[u], vf[u]);
   }
