@@ -212,6 +212,10 @@ typedef struct pa_decode_plan_info {
   int32_t num_tiles;      /* 16-token tiles the jobs read, summed over jobs (with the append fused,
                              pa_decode picks how tiles are loaded from the tiles per sequence and the
                              query heads per KV head) */
+  int32_t num_seqs;       /* sequences the plan was made for: pa_decode refuses another num_seqs */
+  int32_t max_context_len; /* longest context planned: pa_decode refuses tables too short for it */
+  int32_t reserved;
+  uint64_t lens_digest;   /* digest of the planned context lengths (pa_decode_plan_check_lens) */
 } pa_decode_plan_info;
 
 /* A job whose head_block field has this bit reads a prefix shared by the
@@ -333,6 +337,12 @@ pa_status pa_decode_plan_prefix(const int32_t* context_lens, int32_t num_seqs, i
                                 const int32_t* prefix_group, const int32_t* prefix_tokens, void* plan,
                                 size_t capacity, pa_decode_plan_info* info);
 
+/* PA_OK when the plan was made for exactly these context lengths (HOST int32
+ * [num_seqs]), PA_ERR_INVALID with the first differing sequence otherwise.
+ * Plans are made per step, and lengths grow by one every step: a plan kept
+ * from an earlier step describes other lengths. */
+pa_status pa_decode_plan_check_lens(const pa_decode_plan_info* info, const int32_t* context_lens, int32_t num_seqs);
+
 /* Bytes of device workspace pa_decode needs for a plan (0 when no sequence is
  * cut).  The workspace needs no initialisation; it carries records from the
  * attention launch to the merge launch of one call, so calls that may overlap
@@ -363,9 +373,15 @@ size_t pa_decode_workspace_bytes(const pa_decode_plan_info* info, int32_t num_q_
  *                  context lengths and num_kv_heads, and its host-side info.
  *   workspace    : device, >= pa_decode_workspace_bytes(info, ...), 256-byte
  *                  aligned; may be NULL when info->num_records == 0.
- * Preconditions: context_lens equal those given to pa_decode_plan; each
- * L <= max_blocks_per_seq * B; the first ceil(L / B) table entries of each
- * sequence are in [0, num_blocks).  Results are deterministic: the order of
+ * Checked on the host: num_seqs equals the plan's num_seqs and
+ * max_blocks_per_seq * B covers the plan's longest context (PA_ERR_INVALID).
+ * Preconditions: context_lens equal those given to pa_decode_plan; the first
+ * ceil(L / B) table entries of each sequence are in [0, num_blocks).  The
+ * lengths are checked on the device as well: every job compares its
+ * sequence's context_lens entry with the length it was planned for, and a
+ * sequence whose entry differs gets NaN in every output element (never
+ * plausible numbers computed over other lengths).  pa_validate_decode checks
+ * every precondition on host copies.  Results are deterministic: the order of
  * every floating-point reduction depends only on logical token positions and
  * on the plan, never on physical block ids or on timing. */
 pa_status pa_decode(const pa_kv_pool* pool, const void* q, void* out, int32_t out_dtype,
@@ -396,6 +412,41 @@ pa_status pa_decode_merge_pieces(const pa_kv_pool* pool, const void* q, void* ou
                                  float scale, const void* new_key, const void* new_value, const void* plan,
                                  const pa_decode_plan_info* info, void* workspace, size_t workspace_bytes,
                                  void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Validation of device-resident preconditions on HOST copies (a debug aid).
+ *
+ * The GPU calls check what the host can see (sizes, pointers, alignment) but
+ * take the contents of device arrays on trust: a table entry past the pool is
+ * clamped into it, and a wrong block or count then shows up as wrong
+ * attention scores rather than a crash (mercemay.com "Sharing blocks between
+ * sequences"; S06 "Reference counts must be exact").  These calls check those
+ * contents on host copies the caller holds anyway (the block manager exports
+ * the tables and lengths it uploads) and return PA_ERR_INVALID with the first
+ * violation in pa_last_error.  They read nothing on the device and cost time
+ * linear in their inputs, so a serving loop runs them only when debugging.
+ * ------------------------------------------------------------------------- */
+
+/* Slots of one pa_reshape_and_cache call (HOST int64 [num_tokens]): every
+ * non-negative slot below num_blocks * block_size, none repeated. */
+pa_status pa_validate_slots(const int64_t* slot_mapping, int32_t num_tokens, int32_t num_blocks,
+                            int32_t block_size);
+
+/* Pairs of one pa_copy_blocks call (HOST int32 [num_pairs][2] = (src, dst)):
+ * ids in [0, num_blocks), destinations distinct and never a source. */
+pa_status pa_validate_copy_pairs(const int32_t* pairs, int32_t num_pairs, int32_t num_blocks);
+
+/* The inputs of one pa_decode call, from HOST copies: tables int32
+ * [num_seqs][max_blocks_per_seq], context_lens int32 [num_seqs], and the
+ * plan's bytes as built on the host (plan, info).  Checks that the plan was
+ * made for these lengths (its digest and every job's recorded length), that
+ * every L fits its table row, that the first ceil(L / B) entries of every row
+ * are in [0, num_blocks), and, with fused_append != 0, that no other sequence
+ * of the batch names the block that receives a sequence's appended token
+ * (the block manager's copy-on-write must have given the writer its own). */
+pa_status pa_validate_decode(const pa_kv_pool* pool, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                             const int32_t* context_lens, int32_t num_seqs, const void* plan,
+                             const pa_decode_plan_info* info, int32_t fused_append);
 
 /* ---------------------------------------------------------------------------
  * Host block manager (plain C++ on the CPU; not thread-safe: one scheduler

@@ -17,11 +17,25 @@ from ._lib import (LIB_PATH, PA_BF16, PA_DECODE_FIRST_BLOCKS, PA_DECODE_SHARED_K
                    PA_SWAP_ENGINE_KERNEL, PA_SWAP_IN, PA_SWAP_OUT, PaDecodePlanInfo, PaError, PaKvPool, lib)
 
 __all__ = [
+    "set_debug", "validate_slots", "validate_copy_pairs", "validate_decode",
     "LIB_PATH", "PA_F32", "PA_BF16", "PA_DECODE_SHARED_KV", "PA_DECODE_FIRST_BLOCKS", "PA_JOB_SHARED", "PaError", "BlockManager", "KvPool",
     "reshape_and_cache", "copy_blocks", "decode_plan", "decode_workspace_bytes",
     "decode", "DecodePlan", "default_workgroups", "HostKvPool", "swap_blocks", "PA_SWAP_OUT", "PA_SWAP_IN",
     "PA_SWAP_ENGINE_KERNEL", "PA_SWAP_ENGINE_MEMCPY",
 ]
+
+
+# Debug mode: before each GPU call, validate the contents of its device
+# inputs on host copies (pa_validate_*): slots, copy pairs, table entries,
+# lengths against the plan.  It copies those inputs to the host and therefore
+# synchronizes; off unless PAGEDKV_DEBUG=1 or set_debug(True).
+_debug = os.environ.get("PAGEDKV_DEBUG", "0") not in ("", "0")
+
+
+def set_debug(on: bool) -> None:
+    """Turn host-side validation of device inputs before every call on or off."""
+    global _debug
+    _debug = bool(on)
 
 
 def _check(status: int, what: str) -> None:
@@ -103,6 +117,38 @@ def _dev(t, name, dtype=None):
     return t
 
 
+def _host_i32(a):
+    return np.ascontiguousarray(a.cpu().numpy() if hasattr(a, "cpu") else a, dtype=np.int32)
+
+
+def validate_slots(pool: KvPool, slot_mapping) -> None:
+    """pa_validate_slots on a host copy of a slot mapping (raises PaError)."""
+    slots = np.ascontiguousarray(slot_mapping.cpu().numpy() if hasattr(slot_mapping, "cpu") else slot_mapping,
+                                 dtype=np.int64)
+    _check(lib.pa_validate_slots(slots.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), slots.size,
+                                 pool.c.num_blocks, pool.c.block_size), "pa_validate_slots")
+
+
+def validate_copy_pairs(pool: KvPool, pairs) -> None:
+    """pa_validate_copy_pairs on a host copy of (src, dst) pairs (raises PaError)."""
+    pr = _host_i32(pairs).reshape(-1)
+    _check(lib.pa_validate_copy_pairs(pr.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), pr.size // 2,
+                                      pool.c.num_blocks), "pa_validate_copy_pairs")
+
+
+def validate_decode(pool: KvPool, block_tables, context_lens, plan: "DecodePlan", fused_append: bool = False) -> None:
+    """pa_validate_decode on host copies of a decode call's tables and lengths
+    and the plan's host bytes (raises PaError)."""
+    tables = _host_i32(block_tables)
+    lens = _host_i32(context_lens).reshape(-1)
+    if tables.ndim != 2 or tables.shape[0] != lens.size:
+        raise ValueError("block_tables must be [num_seqs, max_blocks] with one length per row")
+    _check(lib.pa_validate_decode(ctypes.byref(pool.c), tables.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                  tables.shape[1], lens.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), lens.size,
+                                  ctypes.c_void_p(plan.blob.ctypes.data), ctypes.byref(plan.info),
+                                  int(bool(fused_append))), "pa_validate_decode")
+
+
 def reshape_and_cache(pool: KvPool, key, value, slot_mapping, stream=None) -> None:
     """pa_reshape_and_cache: write key[i]/value[i] at flat slot slot_mapping[i]."""
     import torch
@@ -112,6 +158,8 @@ def reshape_and_cache(pool: KvPool, key, value, slot_mapping, stream=None) -> No
     n = slot_mapping.numel()
     if key.shape[0] != n or value.shape[0] != n or tuple(key.shape[1:]) != tuple(pool.k.shape[2:]):
         raise ValueError("key/value must be [num_tokens, Hkv, D] matching slot_mapping")
+    if _debug:
+        validate_slots(pool, slot_mapping)
     _check(lib.pa_reshape_and_cache(ctypes.byref(pool.c), _ptr(key), _ptr(value), _ptr(slot_mapping),
                                     n, _stream(stream)), "pa_reshape_and_cache")
 
@@ -121,6 +169,8 @@ def copy_blocks(pool: KvPool, pairs, stream=None) -> None:
     import torch
     _dev(pairs, "pairs", torch.int32)
     n = pairs.numel() // 2
+    if _debug:
+        validate_copy_pairs(pool, pairs)
     _check(lib.pa_copy_blocks(ctypes.byref(pool.c), _ptr(pairs) if n else None, n, _stream(stream)),
            "pa_copy_blocks")
 
@@ -182,6 +232,13 @@ class DecodePlan:
         n = self.info.jobs_per_workgroup * self.info.num_workgroups
         return self.blob[self.info.first_at:self.info.first_at + 16 * n].view(np.int32).reshape(
             self.info.jobs_per_workgroup, self.info.num_workgroups, 4)
+
+    def check_lens(self, context_lens) -> None:
+        """pa_decode_plan_check_lens: raise PaError unless the plan was made for
+        exactly these (host) context lengths."""
+        lens = _host_i32(context_lens).reshape(-1)
+        _check(lib.pa_decode_plan_check_lens(ctypes.byref(self.info), lens.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                             lens.size), "pa_decode_plan_check_lens")
 
     def to_device(self, device="cuda"):
         import torch
@@ -271,18 +328,36 @@ def decode(pool: KvPool, q, block_tables, context_lens, scale: float, plan: Deco
     fuse this step's append: token L - 1 of every sequence is read from them
     and stored into its slot."""
     import torch
+    # The C ABI receives no head_dim for q, out or the new rows and no row
+    # counts for the tables and lengths: shapes are checked here against the
+    # pool, before anything else.
+    if q.dim() != 3:
+        raise ValueError("q must be [S, Hq, D]")
+    s, hq, d = q.shape
+    if d != pool.k.shape[3]:
+        raise ValueError(f"q has head_dim {d}, the pool {pool.k.shape[3]}")
+    if block_tables.dim() != 2 or block_tables.shape[0] != s:
+        raise ValueError(f"block_tables must be [S={s}, max_blocks]")
+    if context_lens.numel() != s:
+        raise ValueError(f"context_lens must hold S={s} lengths")
+    if out is not None and tuple(out.shape) != (s, hq, d):
+        raise ValueError("out must be [S, Hq, D]")
+    for t, n in ((new_key, "new_key"), (new_value, "new_value")):
+        if t is not None and tuple(t.shape) != (s, pool.k.shape[2], d):
+            raise ValueError(f"{n} must be [S, Hkv, D]")
     _dev(q, "q", pool.k.dtype)
     _dev(block_tables, "block_tables", torch.int32)
     _dev(context_lens, "context_lens", torch.int32)
     _dev(plan_dev, "plan_dev", torch.uint8)
     if plan_dev.numel() < plan.info.bytes:
         raise ValueError("plan_dev is shorter than the plan")
-    s, hq, d = q.shape
     if out is None:
         out = torch.empty((s, hq, d), dtype=torch.float32, device=q.device)
     _dev(out, "out")
     if tuple(out.shape) != (s, hq, d):
         raise ValueError("out must be [S, Hq, D]")
+    if out.dtype not in (torch.float32, pool.k.dtype):
+        raise TypeError("out must be float32 or the pool dtype")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if (new_key is None) != (new_value is None):
         raise ValueError("new_key and new_value go together")
@@ -291,6 +366,8 @@ def decode(pool: KvPool, q, block_tables, context_lens, scale: float, plan: Deco
             _dev(t, n, pool.k.dtype)
             if tuple(t.shape) != (s, pool.k.shape[2], d):
                 raise ValueError(f"{n} must be [S, Hkv, D]")
+    if _debug:
+        validate_decode(pool, block_tables, context_lens, plan, fused_append=new_key is not None)
     fn = _DECODE_STAGES[stage]
     _check(getattr(lib, fn)(ctypes.byref(pool.c), _ptr(q), _ptr(out), _dtype_code(out), _ptr(block_tables),
                          block_tables.shape[1], _ptr(context_lens), s, hq, ctypes.c_float(scale),

@@ -36,7 +36,9 @@ class PaDecodePlanInfo(ctypes.Structure):
                 ("jobs_at", ctypes.c_int32), ("merges_at", ctypes.c_int32), ("bytes", ctypes.c_int32),
                 ("flags", ctypes.c_int32), ("schedule", ctypes.c_int32), ("num_groups", ctypes.c_int32),
                 ("groups_at", ctypes.c_int32), ("group_size", ctypes.c_int32), ("first_at", ctypes.c_int32),
-                ("first_block_size", ctypes.c_int32), ("num_tiles", ctypes.c_int32)]
+                ("first_block_size", ctypes.c_int32), ("num_tiles", ctypes.c_int32),
+                ("num_seqs", ctypes.c_int32), ("max_context_len", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("lens_digest", ctypes.c_uint64)]
 
 
 class PaBmStats(ctypes.Structure):
@@ -86,6 +88,10 @@ SIGNATURES = {
                                      ctypes.POINTER(PaDecodePlanInfo)]),
     "pa_decode_plan_first_blocks": (_i32, [_vp, ctypes.POINTER(PaDecodePlanInfo), _p32, _i32, _i32, _i32]),
     "pa_decode_workspace_bytes": (_sz, [ctypes.POINTER(PaDecodePlanInfo), _i32, _i32]),
+    "pa_decode_plan_check_lens": (_i32, [ctypes.POINTER(PaDecodePlanInfo), _p32, _i32]),
+    "pa_validate_slots": (_i32, [_p64, _i32, _i32, _i32]),
+    "pa_validate_copy_pairs": (_i32, [_p32, _i32, _i32]),
+    "pa_validate_decode": (_i32, [_pool, _p32, _i32, _p32, _i32, _vp, ctypes.POINTER(PaDecodePlanInfo), _i32]),
     "pa_decode": (_i32, _DECODE_ARGS),
     "pa_decode_attention": (_i32, _DECODE_ARGS),
     "pa_decode_merge_pieces": (_i32, _DECODE_ARGS),

@@ -666,9 +666,10 @@ namespace pagedkv {
 namespace {
 
 // Serialise a schedule: the column-major job table, the merge rows, the
-// group descriptors.
-pa_status emit_plan(const Schedule& sc, int32_t schedule_id, int32_t num_kv_heads, void* plan, size_t capacity,
-                    pa_decode_plan_info* info) {
+// group descriptors.  The info also records what the plan was made for: the
+// batch size, the longest context and a digest of the lengths.
+pa_status emit_plan(const Schedule& sc, int32_t schedule_id, int32_t num_kv_heads, const int32_t* lens,
+                    int32_t num_seqs, void* plan, size_t capacity, pa_decode_plan_info* info) {
   const std::vector<Piece>& jobs = sc.pieces;
   const std::vector<pa_decode_merge>& merges = sc.merges;
   const int64_t nwg = sc.nwg;
@@ -706,6 +707,10 @@ pa_status emit_plan(const Schedule& sc, int32_t schedule_id, int32_t num_kv_head
   int64_t tiles = 0;
   for (const Piece& pc : jobs) tiles += pc.job.tile_count;
   in.num_tiles = (int32_t)tiles;
+  in.num_seqs = num_seqs;
+  in.max_context_len = 0;
+  for (int32_t i = 0; i < num_seqs; ++i) in.max_context_len = std::max(in.max_context_len, lens[i]);
+  in.lens_digest = lens_digest(lens, num_seqs);
   const size_t bytes = (size_t)in.first_at + 16 * slots;
   if (bytes > (size_t)INT32_MAX) return fail(PA_ERR_INVALID, "pa_decode_plan: plan too large");
   in.bytes = (int32_t)bytes;
@@ -764,7 +769,8 @@ extern "C" pa_status pa_decode_plan_prefix(const int32_t* context_lens, int32_t 
                                               prefix_tokens, num_workgroups, max_piece_tiles > 0 ? max_piece_tiles : 64,
                                               sc))
     return st;
-  const pa_status st = pagedkv::emit_plan(sc, PA_SCHEDULE_CHUNKS, num_kv_heads, plan, capacity, info);
+  const pa_status st =
+      pagedkv::emit_plan(sc, PA_SCHEDULE_CHUNKS, num_kv_heads, context_lens, num_seqs, plan, capacity, info);
   // Loads keep blocks in the caches only when some block is read by more
   // than one job; with every shared prefix read once by its group they
   // stream past the caches like unshared blocks.
@@ -818,7 +824,7 @@ extern "C" pa_status pa_decode_plan_schedule(const int32_t* context_lens, int32_
     if (pa_status st = pagedkv::finish_chunks(context_lens, num_seqs, num_kv_heads, walk, chunks)) return st;
   }
   return pagedkv::emit_plan(use_lpt ? lpt : chunks, use_lpt ? PA_SCHEDULE_LPT : PA_SCHEDULE_CHUNKS, num_kv_heads,
-                            plan, capacity, info);
+                            context_lens, num_seqs, plan, capacity, info);
 }
 
 extern "C" pa_status pa_decode_plan_first_blocks(void* plan, pa_decode_plan_info* info, const int32_t* tables,
@@ -858,6 +864,17 @@ extern "C" pa_status pa_decode_plan_first_blocks(void* plan, pa_decode_plan_info
   return PA_OK;
 }
 
+extern "C" pa_status pa_decode_plan_check_lens(const pa_decode_plan_info* info, const int32_t* context_lens,
+                                              int32_t num_seqs) {
+  const char* who = "pa_decode_plan_check_lens";
+  if (!info || num_seqs < 0 || (num_seqs > 0 && !context_lens)) return fail(PA_ERR_INVALID, "%s: bad arguments", who);
+  if (num_seqs != info->num_seqs)
+    return fail(PA_ERR_INVALID, "%s: plan made for %d sequences, %d given", who, info->num_seqs, num_seqs);
+  if (pagedkv::lens_digest(context_lens, num_seqs) != info->lens_digest)
+    return fail(PA_ERR_INVALID, "%s: plan made for other context lengths (a plan from another step?)", who);
+  return PA_OK;
+}
+
 extern "C" size_t pa_decode_workspace_bytes(const pa_decode_plan_info* info, int32_t num_q_heads,
                                             int32_t head_dim) {
   if (!info || info->num_records <= 0 || num_q_heads <= 0 || head_dim <= 0 || info->num_kv_heads <= 0) return 0;
@@ -885,9 +902,14 @@ pa_status decode_stages(int stages, const char* who, const pa_kv_pool* pool, con
     return fail(PA_ERR_INVALID, "%s: negative size", who);
   if (info->num_jobs == 0 && info->num_merges == 0) return PA_OK;
   if (num_seqs == 0) return fail(PA_ERR_INVALID, "%s: a plan with work but num_seqs == 0", who);
+  if (num_seqs != info->num_seqs)
+    return fail(PA_ERR_INVALID, "%s: plan made for %d sequences, num_seqs is %d", who, info->num_seqs, num_seqs);
   if (!q || !out || !block_tables || !context_lens || !plan)
     return fail(PA_ERR_INVALID, "%s: NULL q/out/block_tables/context_lens/plan", who);
   if (max_blocks_per_seq == 0) return fail(PA_ERR_INVALID, "%s: max_blocks_per_seq == 0", who);
+  if ((int64_t)info->max_context_len > (int64_t)max_blocks_per_seq * pool->block_size)
+    return fail(PA_ERR_INVALID, "%s: the plan's longest context (%d tokens) needs more than %d table entries of %d slots",
+                who, info->max_context_len, max_blocks_per_seq, pool->block_size);
   const int32_t hkv = pool->num_kv_heads;
   if (info->num_kv_heads != hkv)
     return fail(PA_ERR_INVALID, "%s: plan made for %d KV heads, pool has %d", who, info->num_kv_heads, hkv);

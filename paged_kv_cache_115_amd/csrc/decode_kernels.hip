@@ -170,6 +170,7 @@ template <int B>
 struct JobRef {
   JobView v;
   int32_t tb0, tb1;
+  int32_t len_dev;  // context_lens[seq] on the device, compared with the planned length at the job's end
 };
 
 // The context length, the table entries and (load_q) the query of one job
@@ -187,7 +188,10 @@ __device__ __forceinline__ void load_ref(const DecodeArgs& a, const pa_decode_jo
   // nothing waits for this load before the job's first tile is issued.
   J.tb0 = trow[e0];
   J.tb1 = B == 8 ? trow[min(e0 + 1, a.max_blocks - 1)] : 0;
+  // A scalar load issued a job ahead and first waited for at the job's end.
+  J.len_dev = as_const(a.lens)[J.v.seq];
 }
+
 
 // Q^T fragments: lane holds Q[column li][32*ks + 8*lq .. +8].  Column li is
 // query head li of the job's KV head (li < G), or, for a shared job, head
@@ -326,6 +330,17 @@ struct SoftmaxState {
     for (int c = 0; c < 8; ++c) o[c] = float4_t{0.f, 0.f, 0.f, 0.f};
   }
 };
+
+// A plan made for other lengths than the device's context_lens (a plan kept
+// from an earlier step, say) must not yield plausible numbers: the job's
+// accumulator and sum become NaN, so every output element of the sequence
+// does (directly, or through the merge of its records).
+__device__ __forceinline__ void poison_if_stale(int32_t len_dev, int32_t len_plan, SoftmaxState& st) {
+  if (len_dev == len_plan) return;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) st.o[c] = float4_t{NAN, NAN, NAN, NAN};
+  st.l = NAN;
+}
 
 // One 16-token tile (tile t of job v): scores, online-softmax update, PV
 // accumulation.
@@ -624,6 +639,7 @@ __global__ __launch_bounds__(kNW * 64, kWavesPerSimd) void decode_bf16_kernel(De
   load_ref<B>(a, r0, w, lane, cur);
   view_job(a, r1, w, B, nxt.v);
   nxt.tb0 = nxt.tb1 = 0;
+  nxt.len_dev = nxt.v.L;
   // The third job's table entries and the second job's query, and with the
   // plan's first-tile entries the second job's table entries too, are
   // requested after the first two positions (below): the vector memory
@@ -632,6 +648,7 @@ __global__ __launch_bounds__(kNW * 64, kWavesPerSimd) void decode_bf16_kernel(De
   // third job, and with first-tile entries they read no table.
   view_job(a, r2, w, B, nx2.v);
   nx2.tb0 = nx2.tb1 = 0;
+  nx2.len_dev = nx2.v.L;
   bf16x8_t qc[4], qn[4];
   load_q(a, cur.v, li, lq, qc);
   SoftmaxState st;
@@ -689,6 +706,7 @@ __global__ __launch_bounds__(kNW * 64, kWavesPerSimd) void decode_bf16_kernel(De
     compute_bf16_tile(a, cur.v, qc, x - x0, li, lq, ks, vs, kt, st);
     ++x;
     if (x - x0 < cur.v.cnt) return true;
+    poison_if_stale(cur.len_dev, cur.v.L, st);
     finish_bf16_job(a, cur.v, li, lq, st, sg);
     if (!hn) return false;
     x0 += cur.v.cnt;
@@ -765,6 +783,7 @@ __global__ __launch_bounds__(kNW * 64) void decode_f32_kernel(DecodeArgs a) {
     const float* kbase = reinterpret_cast<const float*>(a.k) + (int64_t)v.g * D;
     const float* vbase = reinterpret_cast<const float*>(a.v) + (int64_t)v.g * D;
     const int32_t* trow = a.tables + (int64_t)v.seq * a.max_blocks;
+    const int32_t len_dev = a.lens[v.seq];
     const int32_t t_end = min(kTile * (v.t0 + v.cnt), v.L);
     for (int32_t t = kTile * v.t0; t < t_end; ++t) {
       const int32_t p = clamp_block(trow[t / B], a.num_blocks);
@@ -807,6 +826,15 @@ __global__ __launch_bounds__(kNW * 64) void decode_f32_kernel(DecodeArgs a) {
       }
     }
     if (v.rec == -2) continue;
+    if (len_dev != v.L) {
+      // Planned for another length: NaN, never plausible numbers.
+#pragma unroll
+      for (int h = 0; h < kMaxGroup; ++h) {
+        l_run[h] = NAN;
+#pragma unroll
+        for (int jj = 0; jj < DPL; ++jj) o[h][jj] = NAN;
+      }
+    }
 #pragma unroll
     for (int h = 0; h < kMaxGroup; ++h) {
       if (h >= G) break;
@@ -986,7 +1014,9 @@ __global__ __launch_bounds__(kMaxMergeThreads) void merge_partials_kernel(Decode
   const int64_t out_idx = ((int64_t)mg.seq * a.num_q_heads + (int64_t)mg.kv_head * G) * D + e;
   const int np = mg.num_parts;
   if (np <= 0) {
-    store2(a, out_idx, 0.f, 0.f);
+    // Planned as empty: zeros, or NaN when the device length says otherwise.
+    const float z = a.lens[mg.seq] == 0 ? 0.f : NAN;
+    store2(a, out_idx, z, z);
     return;
   }
   if (mg.record_base < 0 || (int64_t)mg.record_base + np > a.num_records) return;

@@ -8,4 +8,18 @@ namespace pagedkv {
 // Record a printf-style message for pa_last_error() and return `st`.
 pa_status fail(pa_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 
+// Digest of a batch's context lengths (a splitmix64 chain over the count and
+// every length), recorded in a decode plan and compared by the checks.
+inline uint64_t lens_digest(const int32_t* lens, int32_t n) {
+  auto mix = [](uint64_t z) {
+    z += 0x9e3779b97f4a7c15ull;
+    z = (z ^ (z >> 30)) * 0xbf58476d1ce4e5b9ull;
+    z = (z ^ (z >> 27)) * 0x94d049bb133111ebull;
+    return z ^ (z >> 31);
+  };
+  uint64_t h = mix((uint64_t)(uint32_t)n);
+  for (int32_t i = 0; i < n; ++i) h = mix(h ^ (uint64_t)(uint32_t)lens[i]);
+  return h;
+}
+
 }  // namespace pagedkv

@@ -443,3 +443,45 @@ def test_use_after_free_poisoning_leaves_sharers_unchanged(pk):
     pool.v[freed] = float("nan")
     out = to_host(gpu_decode(pk, pool, to_dev(case["q"]), got["tables"], got["lens"], case["scale"], SMALL_PIECES))
     assert np.array_equal(bits(out[others]), bits(before[others]))
+
+
+@pytest.mark.parametrize("name", ["c1", "c3s"])
+@pytest.mark.parametrize("schedule", [DEFAULT, TINY_PIECES, FEW_WG])
+def test_plan_for_other_lengths_gives_nan_not_numbers(pk, name, schedule):
+    """A plan built for other context lengths than the device's (every odd
+    sequence one token shorter, as a plan kept from the previous step would
+    be, and one non-empty sequence planned as empty) passes the host checks,
+    which cannot see device lengths.  Every job compares its sequence's
+    device length with the planned one: each output element of a sequence
+    whose lengths differ is NaN, whether the job writes it directly or
+    through merged records, and every other sequence matches the oracle."""
+    log(f"stale plan {name} schedule={schedule}")
+    case = synth.decode_case(name)
+    cfg = case["cfg"]
+    got = product_decode_step(pk, case, schedule)
+    ref = oracle_decode_step(case)
+    lens = got["lens"]
+    stale = lens.copy()
+    stale[1::2] = np.maximum(stale[1::2] - 1, 0)
+    live = np.flatnonzero(lens > 0)
+    stale[live[-1]] = 0
+    differ = stale != lens
+    assert differ.any() and (~differ).any()
+    plan, plan_dev, ws = plan_and_workspace(pk, stale, cfg["num_kv_heads"], cfg["num_q_heads"], cfg["head_dim"],
+                                            *schedule)
+    for fused in (False, True):
+        out = torch.zeros(tuple(got["q_dev"].shape), dtype=torch.float32, device="cuda")
+        nk = nv = None
+        if fused:
+            # The appended rows are already in the pool; storing them again
+            # from the device lengths leaves it unchanged.
+            last = np.array([case["offsets"][s + 1] - 1 if lens[s] > 0 else 0 for s in range(len(lens))])
+            nk, nv = to_dev(case["keys"][last]), to_dev(case["values"][last])
+        pk.decode(got["pool"], got["q_dev"], to_dev(got["tables"]), to_dev(lens), case["scale"], plan, plan_dev, ws,
+                  out=out, new_key=nk, new_value=nv)
+        o = to_host(out)
+        assert np.all(np.isnan(o[differ])), f"fused={fused}: a sequence planned for another length is not all NaN"
+        assert_close(o[~differ], ref["out"][~differ], cfg["dtype"], f"stale plan {name}/{schedule}/fused={fused}")
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(to_host(got["pool"].k)), bits(ref["kpool"]))
+        assert np.array_equal(bits(to_host(got["pool"].v)), bits(ref["vpool"]))
