@@ -413,6 +413,24 @@ pa_status pa_decode_merge_pieces(const pa_kv_pool* pool, const void* q, void* ou
                                  const pa_decode_plan_info* info, void* workspace, size_t workspace_bytes,
                                  void* stream);
 
+/* pa_decode_noalloc - pa_decode for callers that cannot allocate device
+ * memory: code under stream capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments and checks as pa_decode without the
+ * workspace: the records of cut sequences go to a device array inside the
+ * library of PA_NOALLOC_SCRATCH_BYTES (32 MiB), one per device, held from the
+ * device's first call until the process ends.  The call allocates nothing.
+ * A plan whose workspace (pa_decode_workspace_bytes) exceeds the array is
+ * refused with PA_ERR_INVALID before anything touches the device.  The array
+ * needs no initialisation (each call writes every record it reads) and keeps
+ * the last call's contents; all calls on one device share it, so calls that
+ * may overlap in time on one device (different streams) race: order them on
+ * one stream. */
+#define PA_NOALLOC_SCRATCH_BYTES (32u << 20)
+pa_status pa_decode_noalloc(const pa_kv_pool* pool, const void* q, void* out, int32_t out_dtype,
+                            const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                            int32_t num_seqs, int32_t num_q_heads, float scale, const void* new_key,
+                            const void* new_value, const void* plan, const pa_decode_plan_info* info, void* stream);
+
 /* ---------------------------------------------------------------------------
  * Validation of device-resident preconditions on HOST copies (a debug aid).
  *

@@ -20,7 +20,7 @@ __all__ = [
     "set_debug", "validate_slots", "validate_copy_pairs", "validate_decode",
     "LIB_PATH", "PA_F32", "PA_BF16", "PA_DECODE_SHARED_KV", "PA_DECODE_FIRST_BLOCKS", "PA_JOB_SHARED", "PaError", "BlockManager", "KvPool",
     "reshape_and_cache", "copy_blocks", "decode_plan", "decode_workspace_bytes",
-    "decode", "DecodePlan", "default_workgroups", "HostKvPool", "swap_blocks", "PA_SWAP_OUT", "PA_SWAP_IN",
+    "decode", "decode_noalloc", "DecodePlan", "default_workgroups", "HostKvPool", "swap_blocks", "PA_SWAP_OUT", "PA_SWAP_IN",
     "PA_SWAP_ENGINE_KERNEL", "PA_SWAP_ENGINE_MEMCPY",
 ]
 
@@ -320,13 +320,9 @@ def decode_workspace_bytes(plan: DecodePlan, num_q_heads: int, head_dim: int) ->
 _DECODE_STAGES = {"all": "pa_decode", "attention": "pa_decode_attention", "merge": "pa_decode_merge_pieces"}
 
 
-def decode(pool: KvPool, q, block_tables, context_lens, scale: float, plan: DecodePlan, plan_dev, workspace=None,
-           out=None, stream=None, stage: str = "all", new_key=None, new_value=None):
-    """pa_decode (stage "all"), or one of its two launches: pa_decode_attention
-    ("attention") or pa_decode_merge_pieces ("merge").  `plan_dev` is the device copy
-    of plan.blob (uint8 tensor).  new_key/new_value ([S, Hkv, D], pool dtype)
-    fuse this step's append: token L - 1 of every sequence is read from them
-    and stored into its slot."""
+def _decode_checked(pool: KvPool, q, block_tables, context_lens, plan: DecodePlan, plan_dev, out, new_key,
+                    new_value) -> tuple:
+    """Checks shared by the decode entry points; returns (S, Hq, out)."""
     import torch
     # The C ABI receives no head_dim for q, out or the new rows and no row
     # counts for the tables and lengths: shapes are checked here against the
@@ -354,20 +350,27 @@ def decode(pool: KvPool, q, block_tables, context_lens, scale: float, plan: Deco
     if out is None:
         out = torch.empty((s, hq, d), dtype=torch.float32, device=q.device)
     _dev(out, "out")
-    if tuple(out.shape) != (s, hq, d):
-        raise ValueError("out must be [S, Hq, D]")
     if out.dtype not in (torch.float32, pool.k.dtype):
         raise TypeError("out must be float32 or the pool dtype")
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if (new_key is None) != (new_value is None):
         raise ValueError("new_key and new_value go together")
     if new_key is not None:
-        for t, n in ((new_key, "new_key"), (new_value, "new_value")):
-            _dev(t, n, pool.k.dtype)
-            if tuple(t.shape) != (s, pool.k.shape[2], d):
-                raise ValueError(f"{n} must be [S, Hkv, D]")
+        _dev(new_key, "new_key", pool.k.dtype)
+        _dev(new_value, "new_value", pool.k.dtype)
     if _debug:
         validate_decode(pool, block_tables, context_lens, plan, fused_append=new_key is not None)
+    return s, hq, out
+
+
+def decode(pool: KvPool, q, block_tables, context_lens, scale: float, plan: DecodePlan, plan_dev, workspace=None,
+           out=None, stream=None, stage: str = "all", new_key=None, new_value=None):
+    """pa_decode (stage "all"), or one of its two launches: pa_decode_attention
+    ("attention") or pa_decode_merge_pieces ("merge").  `plan_dev` is the device copy
+    of plan.blob (uint8 tensor).  new_key/new_value ([S, Hkv, D], pool dtype)
+    fuse this step's append: token L - 1 of every sequence is read from them
+    and stored into its slot."""
+    s, hq, out = _decode_checked(pool, q, block_tables, context_lens, plan, plan_dev, out, new_key, new_value)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     fn = _DECODE_STAGES[stage]
     _check(getattr(lib, fn)(ctypes.byref(pool.c), _ptr(q), _ptr(out), _dtype_code(out), _ptr(block_tables),
                          block_tables.shape[1], _ptr(context_lens), s, hq, ctypes.c_float(scale),
@@ -375,6 +378,23 @@ def decode(pool: KvPool, q, block_tables, context_lens, scale: float, plan: Deco
                          _ptr(plan_dev),
                          ctypes.byref(plan.info), None if workspace is None else _ptr(workspace), ws_bytes,
                          _stream(stream)), fn)
+    return out
+
+
+def decode_noalloc(pool: KvPool, q, block_tables, context_lens, scale: float, plan: DecodePlan, plan_dev, out,
+                   stream=None, new_key=None, new_value=None):
+    """pa_decode_noalloc: pa_decode with the library's built-in scratch array
+    (PA_NOALLOC_SCRATCH_BYTES per device) as its workspace; allocates
+    nothing, so `out` must be given.  Calls on one device share the array:
+    order them on one stream."""
+    if out is None:
+        raise ValueError("decode_noalloc allocates nothing: pass out")
+    s, hq, out = _decode_checked(pool, q, block_tables, context_lens, plan, plan_dev, out, new_key, new_value)
+    _check(lib.pa_decode_noalloc(ctypes.byref(pool.c), _ptr(q), _ptr(out), _dtype_code(out), _ptr(block_tables),
+                                 block_tables.shape[1], _ptr(context_lens), s, hq, ctypes.c_float(scale),
+                                 None if new_key is None else _ptr(new_key),
+                                 None if new_value is None else _ptr(new_value), _ptr(plan_dev),
+                                 ctypes.byref(plan.info), _stream(stream)), "pa_decode_noalloc")
     return out
 
 

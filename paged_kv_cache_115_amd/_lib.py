@@ -15,6 +15,7 @@ PA_SWAP_OUT = 0
 PA_SWAP_IN = 1
 PA_SWAP_ENGINE_KERNEL = 0
 PA_SWAP_ENGINE_MEMCPY = 1
+PA_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 class PaError(RuntimeError):
@@ -95,6 +96,7 @@ SIGNATURES = {
     "pa_decode": (_i32, _DECODE_ARGS),
     "pa_decode_attention": (_i32, _DECODE_ARGS),
     "pa_decode_merge_pieces": (_i32, _DECODE_ARGS),
+    "pa_decode_noalloc": (_i32, _DECODE_ARGS[:14] + [_vp]),
     "pa_bm_create": (_vp, [_i32, _i32, _p32]),
     "pa_bm_destroy": (None, [_vp]),
     "pa_bm_append": (_i32, [_vp, _i64, _i32, _p64, _p32, _p32]),

@@ -882,13 +882,11 @@ extern "C" size_t pa_decode_workspace_bytes(const pa_decode_plan_info* info, int
   return pagedkv::layout((int64_t)info->num_records * group, head_dim).total;
 }
 
-namespace {
+namespace pagedkv {
 
-constexpr int kStageAttention = 1;
-constexpr int kStageMerge = 2;
-
-// Shared front of pa_decode and its two stages: validation, then the
-// launches the stage mask selects.  `who` names the entry point in errors.
+// Shared front of pa_decode, its two stages and pa_decode_noalloc:
+// validation, then the launches the stage mask selects.  `who` names the
+// entry point in errors.
 pa_status decode_stages(int stages, const char* who, const pa_kv_pool* pool, const void* q, void* out,
                         int32_t out_dtype, const int32_t* block_tables, int32_t max_blocks_per_seq,
                         const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads, float scale,
@@ -1015,7 +1013,11 @@ pa_status decode_stages(int stages, const char* who, const pa_kv_pool* pool, con
   return PA_OK;
 }
 
-}  // namespace
+}  // namespace pagedkv
+
+using pagedkv::decode_stages;
+using pagedkv::kStageAttention;
+using pagedkv::kStageMerge;
 
 #define PA_DECODE_ARGS                                                                                   \
   const pa_kv_pool *pool, const void *q, void *out, int32_t out_dtype, const int32_t *block_tables,      \

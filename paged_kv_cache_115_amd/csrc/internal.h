@@ -22,4 +22,14 @@ inline uint64_t lens_digest(const int32_t* lens, int32_t n) {
   return h;
 }
 
+// The decode front shared by the pa_decode entry points: argument checks,
+// then the launches selected by `stages` (kStageAttention | kStageMerge).
+constexpr int kStageAttention = 1;
+constexpr int kStageMerge = 2;
+pa_status decode_stages(int stages, const char* who, const pa_kv_pool* pool, const void* q, void* out,
+                        int32_t out_dtype, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                        const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads, float scale,
+                        const void* new_key, const void* new_value, const void* plan,
+                        const pa_decode_plan_info* info, void* workspace, size_t workspace_bytes, void* stream);
+
 }  // namespace pagedkv
