@@ -96,10 +96,69 @@ def cpu_baseline(case, per_token: int, k_host, v_host, tables, lens, budget_s: f
         tokens += int(lens[s])
         done += 1
     dt = time.perf_counter() - t0
-    return {"value": round(tokens * per_token / dt / 1e9, 6), "unit": "GB/s", "cores": 1, "kind": "oracle",
+    cores_total = len(os.sched_getaffinity(0))
+    return {"value": round(tokens * per_token / dt / 1e9, 6), "unit": "GB/s", "cores": 1, "cores_total": cores_total,
+            "cpu_model": cpu_model(), "kind": "oracle",
             "sample": f"float64 oracle, {done} sequence decodes cycling through the {len(lens)}-sequence batch "
-                      f"({tokens} context tokens, {dt:.1f} s on one host core)",
+                      f"({tokens} context tokens, {dt:.1f} s on 1 host core of {cores_total})",
             "seconds": round(dt, 3), "seqs_per_s": round(done / dt, 3)}
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def percentiles(xs) -> dict:
+    a = np.asarray(xs, dtype=float)
+    return {"p10": round(float(np.percentile(a, 10)), 3), "p50": round(float(np.percentile(a, 50)), 3),
+            "p90": round(float(np.percentile(a, 90)), 3), "mean": round(float(a.mean()), 3)}
+
+
+def read_probe(torch, pk, nbytes: int, reps: int = 50, workgroups: int = 512) -> dict:
+    """pa_probe_read over nbytes, rotating through a buffer of at least
+    1.25 GiB (five times the 256 MB last-level cache) so that every read comes
+    from HBM; microseconds per launch from HIP events on the stream."""
+    dev = torch.device("cuda", 0)
+    span = max(nbytes, 256 << 20)
+    regions = max(2, -(-(5 << 28) // span))
+    buf = torch.ones(span * regions // 4, dtype=torch.float32, device=dev)
+    sink = torch.zeros(workgroups * 256, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    views = [buf[r * span // 4:(r * span + nbytes) // 4] for r in range(regions)]
+    for i in range(5):
+        pk.probe_read(views[i % regions], workgroups, sink, stream=stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(reps):
+        pk.probe_read(views[i % regions], workgroups, sink, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / reps * 1e3
+    del buf
+    return {"bytes": nbytes, "workgroups": workgroups, "us": round(us, 3), "GBs": round(nbytes / us / 1e3, 1),
+            "frac_of_peak": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)}
+
+
+def read_probe_sweep(torch, pk) -> int:
+    """The probe at 16 MB .. 1 GiB: a least-squares fit of launch time against
+    bytes gives the fixed cost of a launch and the streaming rate."""
+    rows = [read_probe(torch, pk, n) for n in (16 << 20, 64 << 20, 220954624, 512 << 20, 1 << 30)]
+    x = np.array([r["bytes"] for r in rows], float)
+    y = np.array([r["us"] for r in rows], float)
+    slope, fixed = np.polyfit(x, y, 1)
+    print(json.dumps({"metric": "streaming read (pa_probe_read) time against bytes", "fixed_us": round(float(fixed), 2),
+                      "streaming_GBs": round(float(1e3 / (slope * 1e9) * 1e3), 1),
+                      "streaming_frac_of_peak": round(float(1e3 / (slope * 1e9) * 1e3) / HBM_PEAK_GBS, 4),
+                      "config": {"workload": "one contiguous read per launch, 512 workgroups of 256 threads, "
+                                             "16-byte non-temporal loads"}, "sweep": rows}), flush=True)
+    return 0
 
 
 def decode_workload(pk, name: str, block_size: int | None = None) -> dict:
@@ -128,7 +187,7 @@ def decode_workload(pk, name: str, block_size: int | None = None) -> dict:
     return dict(name=name, desc=desc, case=case, seed=cfg["seed"], S=S, hq=cfg["num_q_heads"],
                 hkv=cfg["num_kv_heads"], d=cfg["head_dim"], B=B, nb=case["num_blocks"], tables=tables, lens=lens,
                 slots=slots, cows=cows, host_append_us=host_append_us, unique_tokens=int(lens.sum()),
-                shared_kv=bm.stats()["shared_blocks"] > 0)
+                shared_kv=bm.stats()["shared_blocks"] > 0, bm=bm)
 
 
 def prefix_workload(pk, block_size: int) -> dict:
@@ -181,7 +240,7 @@ def prefix_workload(pk, block_size: int) -> dict:
                 seed=cfg["seed"] + B, S=nseq, hq=cfg["num_q_heads"], hkv=cfg["num_kv_heads"], d=cfg["head_dim"], B=B,
                 nb=case["num_blocks"], tables=tables, lens=lens, slots=slots,
                 cows=np.asarray(fork_cows, dtype=np.int32).reshape(-1, 2), host_append_us=host_append_us,
-                unique_tokens=int(sum(used.values())), shared_kv=bm.stats()["shared_blocks"] > 0)
+                unique_tokens=int(sum(used.values())), shared_kv=bm.stats()["shared_blocks"] > 0, bm=bm)
 
 
 def prefix_cache_workload(pk, block_size: int) -> dict:
@@ -223,7 +282,7 @@ def prefix_cache_workload(pk, block_size: int) -> dict:
                 prefix_tokens=prefix_tokens, seed=cfg["seed"], S=S, hq=cfg["num_q_heads"], hkv=cfg["num_kv_heads"],
                 d=cfg["head_dim"], B=B, nb=nb, tables=tables, lens=lens, slots=slots,
                 cows=np.asarray(cows, dtype=np.int32).reshape(-1, 2), host_append_us=host_append_us,
-                unique_tokens=int(sum(used.values())), shared_kv=True,
+                unique_tokens=int(sum(used.values())), shared_kv=True, bm=bm,
                 prefix_cache={"host_prompt_us_per_request": round(host_prompt_us, 2),
                               "prompt_tokens": int(st["prefix_query_tokens"]),
                               "reused_tokens": int(st["prefix_hit_tokens"]),
@@ -357,6 +416,126 @@ def swap_sweep(torch, pk, lengths, reps: int = 10) -> int:
     return 0
 
 
+def e2e_loop(torch, pk, w, pools, q_d, new_k, new_v, out, steps: int, build_plan, native_step=None) -> dict:
+    """A serving loop over the workload's batch, `steps` decode steps long.
+    Each step the host appends one token to every sequence (block manager),
+    writes table rows and lengths, builds the plan for the new lengths,
+    stages all of it in pinned host memory and uploads it, then launches
+    pa_copy_blocks (when the append made copy-on-write pairs) and the fused
+    pa_decode.  Launches are asynchronous, so the host prepares step n + 1
+    while the GPU runs step n; the wall time per step is the larger of the
+    two.  Lengths grow by one per step, as in serving.
+
+    native_step = (num_workgroups, schedule, first_blocks): the host work is
+    one pa_bm_prepare_decode_step call into a pinned buffer and one upload;
+    otherwise (cascade plans) the separate binding calls, staged and uploaded
+    one array at a time."""
+    bm, S, B, R = w["bm"], w["S"], w["B"], len(pools)
+    seqs = np.arange(S)
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream()
+    maxw = int(w["tables"].shape[1]) + -(-(steps + 1) // B) + 1
+    probe_plan = build_plan(w["lens"], w["tables"])
+    plan_cap = 4 * probe_plan.info.bytes + (1 << 16)
+    ws = torch.empty(max(4 * pk.decode_workspace_bytes(probe_plan, w["hq"], w["d"]), 1 << 20) // 4,
+                     dtype=torch.float32, device=dev)
+    stage_done = [torch.cuda.Event() for _ in range(2)]
+    if native_step is not None:
+        nwg, sched, first = native_step
+        parts = {k: [] for k in ("prepare", "upload", "launch")}
+        cap = 256 * (-(-(16 * S + 4 * S * maxw + 4 * S + plan_cap) // 256) + 8)
+        stage = [torch.empty(cap, dtype=torch.uint8).pin_memory() for _ in range(2)]
+        for st_ in stage:
+            st_.numpy()[:] = 0
+        dev_buf = torch.empty(cap, dtype=torch.uint8, device=dev)
+        views = None
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        for k in range(steps):
+            t0 = time.perf_counter()
+            j = k % 2
+            if k >= 2:
+                stage_done[j].synchronize()       # the upload of step k - 2 has read this buffer
+            lay, plan = bm.prepare_decode_step(seqs, maxw, w["hkv"], stage[j], nwg, sched, first)
+            t1 = time.perf_counter()
+            dev_buf[:lay.bytes].copy_(stage[j][:lay.bytes], non_blocking=True)
+            stage_done[j].record(stream)
+            if views is None:                     # offsets depend only on S and maxw
+                views = (dev_buf[lay.tables_at:lay.tables_at + 4 * S * maxw].view(torch.int32).view(S, maxw),
+                         dev_buf[lay.lens_at:lay.lens_at + 4 * S].view(torch.int32),
+                         dev_buf[lay.plan_at:],
+                         dev_buf[lay.cows_at:lay.cows_at + 8 * S].view(torch.int32).view(S, 2))
+            tables_e, lens_e, plan_e, cows_e = views
+            t2 = time.perf_counter()
+            pool = pools[k % R]
+            if lay.n_cows:
+                pk.copy_blocks(pool, cows_e[:lay.n_cows], stream)
+            pk.decode(pool, q_d, tables_e, lens_e, w["case"]["scale"], plan, plan_e, ws, out, stream,
+                      new_key=new_k, new_value=new_v)
+            t3 = time.perf_counter()
+            for name, a, b in (("prepare", t0, t1), ("upload", t1, t2), ("launch", t2, t3)):
+                parts[name].append((b - a) * 1e6)
+        torch.cuda.synchronize()
+        wall_us = (time.perf_counter() - t_start) * 1e6 / steps
+    else:
+        tables_e = torch.empty((S, maxw), dtype=torch.int32, device=dev)
+        lens_e = torch.empty(S, dtype=torch.int32, device=dev)
+        plan_e = torch.empty(plan_cap, dtype=torch.uint8, device=dev)
+        cows_e = torch.empty((S, 2), dtype=torch.int32, device=dev)
+        stage = [dict(tables=torch.empty((S, maxw), dtype=torch.int32).pin_memory(),
+                      lens=torch.empty(S, dtype=torch.int32).pin_memory(),
+                      plan=torch.empty(plan_cap, dtype=torch.uint8).pin_memory(),
+                      cows=torch.empty((S, 2), dtype=torch.int32).pin_memory()) for _ in range(2)]
+        parts = {k: [] for k in ("append", "export", "plan", "stage_upload", "launch")}
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        for k in range(steps):
+            t0 = time.perf_counter()
+            _, cows = bm.append_step(seqs)
+            t1 = time.perf_counter()
+            tables, lens = bm.export(seqs, maxw)
+            t2 = time.perf_counter()
+            plan = build_plan(lens, tables)
+            t3 = time.perf_counter()
+            j = k % 2
+            if k >= 2:
+                stage_done[j].synchronize()       # the uploads of step k - 2 have read this staging set
+            st = stage[j]
+            st["tables"].numpy()[:] = tables
+            st["lens"].numpy()[:] = lens
+            nb = plan.info.bytes
+            st["plan"].numpy()[:nb] = plan.blob
+            tables_e.copy_(st["tables"], non_blocking=True)
+            lens_e.copy_(st["lens"], non_blocking=True)
+            plan_e[:nb].copy_(st["plan"][:nb], non_blocking=True)
+            n_cow = len(cows)
+            if n_cow:
+                st["cows"].numpy()[:n_cow] = cows
+                cows_e[:n_cow].copy_(st["cows"][:n_cow], non_blocking=True)
+            stage_done[j].record(stream)
+            t4 = time.perf_counter()
+            pool = pools[k % R]
+            if n_cow:
+                pk.copy_blocks(pool, cows_e[:n_cow], stream)
+            pk.decode(pool, q_d, tables_e, lens_e, w["case"]["scale"], plan, plan_e, ws, out, stream,
+                      new_key=new_k, new_value=new_v)
+            t5 = time.perf_counter()
+            for name, a, b in (("append", t0, t1), ("export", t1, t2), ("plan", t2, t3), ("stage_upload", t3, t4),
+                               ("launch", t4, t5)):
+                parts[name].append((b - a) * 1e6)
+        torch.cuda.synchronize()
+        wall_us = (time.perf_counter() - t_start) * 1e6 / steps
+    host = {name: round(float(np.median(v)), 2) for name, v in parts.items()}
+    host_total = round(float(np.median([sum(x) for x in zip(*parts.values())])), 2)
+    return {"steps": steps, "us_per_step": round(wall_us, 2), "decode_tokens_per_s": round(S / (wall_us * 1e-6), 1),
+            "host_path": "pa_bm_prepare_decode_step, one upload" if native_step is not None else
+                         "separate binding calls, one upload per array",
+            "host_us_median": host, "host_total_us_median": host_total,
+            "note": "wall time per step of the whole serving loop (host block manager, plan, uploads and the GPU "
+                    "launches of one attention layer), lengths growing by one per step; a model's other layers "
+                    "reuse the step's plan and tables"}
+
+
 def length_sweep(torch, pk, lengths=(16, 32, 64, 128, 200, 256, 400, 640), reps: int = 100) -> int:
     """Attention launch time against KV bytes for batches of 256 sequences of
     one length each (c3 heads: 32 q / 8 KV, head_dim 128, block 16, shuffled
@@ -438,6 +617,12 @@ def main() -> int:
     ap.add_argument("--length-sweep", action="store_true",
                     help="time the attention launch for uniform batches of 16..640 tokens and fit fixed cost "
                          "and streaming rate, then exit")
+    ap.add_argument("--read-probe", action="store_true",
+                    help="time a plain streaming read (pa_probe_read) at 16 MB .. 1 GiB, fit fixed cost and "
+                         "streaming rate, and exit")
+    ap.add_argument("--e2e-steps", type=int, default=32,
+                    help="steps of the end-to-end serving loop timed last (host append, export, plan and upload "
+                         "of every step overlapped with the GPU step before it); 0 skips it")
     ap.add_argument("--swap-sweep", action="store_true",
                     help="measure swapping a sequence out to pinned host memory and back at several context "
                          "lengths (both engines) and exit")
@@ -457,6 +642,9 @@ def main() -> int:
     if args.length_sweep:
         torch.cuda.set_device(0)
         return length_sweep(torch, pk)
+    if args.read_probe:
+        torch.cuda.set_device(0)
+        return read_probe_sweep(torch, pk)
 
     torch.cuda.set_device(0)
     if args.config == "c5":
@@ -558,6 +746,24 @@ def main() -> int:
         torch.cuda.synchronize()
         return start.elapsed_time(end) / n
 
+    def timed_blocks(fn, blocks: int = 40, per: int = 10) -> dict:
+        """Distribution of per-call times: `blocks` blocks of `per` back-to-back
+        calls, an event between blocks (an event between every two calls would
+        cost more than the spread it measures); microseconds per call of
+        each block, summarised by percentiles."""
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(blocks + 1)]
+        torch.cuda.synchronize()
+        ev[0].record(stream)
+        k = 0
+        for b in range(blocks):
+            for _ in range(per):
+                fn(k % R)
+                k += 1
+            ev[b + 1].record(stream)
+        torch.cuda.synchronize()
+        us = [ev[b].elapsed_time(ev[b + 1]) / per * 1e3 for b in range(blocks)]
+        return dict(percentiles(us), blocks=blocks, calls_per_block=per)
+
     for k in range(args.warmup):
         step_fused(k % R)
     torch.cuda.synchronize()
@@ -587,6 +793,10 @@ def main() -> int:
     attention_us = timed(attention, args.steps) * 1e3
     attention_unfused_us = timed(attention_unfused, args.steps) * 1e3
     decode_us = timed(decode_call, args.steps) * 1e3
+    # Spread of the step and of its attention launch (separate regions, after
+    # the timed ones).
+    step_stats = timed_blocks(step_fused)
+    attention_stats = timed_blocks(attention)
     pk.decode(pools[0], q_d, tables_d, lens_d, case["scale"], plan, plan_d, ws, out, stream)   # leave a complete result
     torch.cuda.synchronize()
 
@@ -633,8 +843,10 @@ def main() -> int:
         "reserved_slots": int(sum(-(-int(L) // B) * B for L in lens)),
         "tail_waste_frac": round(1 - int(lens.sum()) / max(1, sum(-(-int(L) // B) * B for L in lens)), 5),
         "us_per_output_token": round(ms_per_step * 1e3 / S, 5),
+        "step_us_stats": step_stats,
         "decode_call_us": round(decode_us, 3),
         "attention_launch_us": round(attention_us, 3),
+        "attention_launch_us_stats": attention_stats,
         "attention_launch_unfused_us": round(attention_unfused_us, 3),
         "unfused_frac": round(kv_bytes / (attention_unfused_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
         "host_append_us": round(host_append_us, 2),
@@ -646,8 +858,34 @@ def main() -> int:
     }
     if "prefix_cache" in w:
         result["prefix_cache"] = w["prefix_cache"]
+    # The achievable read rate for the same bytes: a plain streaming read of
+    # that many bytes on the same grid size.
+    probe = read_probe(torch, pk, kv_bytes - kv_bytes % 16)
+    result["read_probe"] = dict(probe, attention_vs_probe=round(probe["us"] / attention_us, 4))
     if not args.decode_only:
         result["copy_blocks_probe"] = copy_blocks_probe(torch, pk, B, hkv, d)
+    if args.e2e_steps > 0:
+        # Last: it advances the block manager's sequences.
+        def plan_for(lens_h, tables_h):
+            if cascade:
+                grp, tok = w["bm"].prefix_groups(np.arange(S))
+                p = pk.decode_plan_prefix(lens_h, hkv, hq, grp, tok, workgroups, args.piece)
+            else:
+                sched = {"auto": pk.SCHEDULE_AUTO, "chunks": pk.SCHEDULE_CHUNKS, "lpt": pk.SCHEDULE_LPT}[args.schedule]
+                p = pk.decode_plan(lens_h, hkv, workgroups, args.piece, shared_kv=w["shared_kv"], schedule=sched)
+            if not args.no_first_blocks:
+                p.set_first_blocks(tables_h, B)
+            return p
+        native = None if cascade else (workgroups, plan.schedule if args.schedule == "auto" else
+                                       {"chunks": pk.SCHEDULE_CHUNKS, "lpt": pk.SCHEDULE_LPT}[args.schedule],
+                                       not args.no_first_blocks)
+        e2e = e2e_loop(torch, pk, w, pools, q_d, new_k, new_v, out, args.e2e_steps, plan_for, native)
+        if native is not None:
+            e2e["schedule"] = ["chunks", "largest pieces first"][native[1]] + \
+                " (the automatic choice for the batch at the first step, kept)"
+        result["e2e"] = e2e
+        result["decode_tokens_per_s_gpu_only"] = result["decode_tokens_per_s"]
+        result["decode_tokens_per_s"] = e2e["decode_tokens_per_s"]
     if not args.no_cpu_baseline:
         k_host = pools[0].k.cpu().view(torch.int16).numpy().view(np.uint16)
         v_host = pools[0].v.cpu().view(torch.int16).numpy().view(np.uint16)

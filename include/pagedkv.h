@@ -354,8 +354,9 @@ size_t pa_decode_workspace_bytes(const pa_decode_plan_info* info, int32_t num_q_
  *   q            : device [num_seqs][num_q_heads][head_dim], pool dtype.
  *   out          : device [num_seqs][num_q_heads][head_dim], out_dtype
  *                  (PA_F32, or the pool dtype: rounded to nearest even).
- *   block_tables : device int32 [num_seqs][max_blocks_per_seq]; entries past
- *                  ceil(L / B) are never read.
+ *   block_tables : device int32 [num_seqs][max_blocks_per_seq]; the values
+ *                  of entries past ceil(L / B) are never used (they may be
+ *                  loaded with the row, and need not be valid block ids).
  *   context_lens : device int32 [num_seqs].
  *   scale        : multiplies q.k before the softmax (1/sqrt(head_dim) for
  *                  standard attention; S06 "Implementation").
@@ -430,6 +431,21 @@ pa_status pa_decode_noalloc(const pa_kv_pool* pool, const void* q, void* out, in
                             const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
                             int32_t num_seqs, int32_t num_q_heads, float scale, const void* new_key,
                             const void* new_value, const void* plan, const pa_decode_plan_info* info, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Measurement aid (not on the decode path).
+ *
+ * pa_probe_read - read `bytes` of device memory at `src` once, as a plain
+ * stream: num_workgroups workgroups of 256 threads, each reading one
+ * contiguous share with 16-byte non-temporal loads, the decode tiles' load
+ * width and cache policy.  Its rate is the achievable read bandwidth the
+ * decode launch is compared with, beside the published HBM peak.
+ *   src  : device, 16-byte aligned; bytes a multiple of 16.
+ *   sink : device uint32 [num_workgroups * 256]; written only for a value
+ *          the probe's inputs never produce (it keeps the loads alive).
+ * PA_ERR_INVALID for NULL pointers, misalignment or num_workgroups <= 0.
+ * ------------------------------------------------------------------------- */
+pa_status pa_probe_read(const void* src, size_t bytes, int32_t num_workgroups, void* sink, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Validation of device-resident preconditions on HOST copies (a debug aid).
@@ -620,8 +636,47 @@ pa_status pa_bm_append_prompt(pa_bm* bm, int64_t seq, const int32_t* tokens, int
 int32_t pa_bm_cached(const pa_bm* bm, int32_t block); /* 1 cached, 0 not, -1 out of range */
 
 int32_t pa_bm_len(const pa_bm* bm, int64_t seq);         /* -1 if unknown */
+int32_t pa_bm_block_size(const pa_bm* bm);               /* B of the manager, -1 for NULL */
 int32_t pa_bm_refcount(const pa_bm* bm, int32_t block);  /* -1 if out of range */
 void pa_bm_get_stats(const pa_bm* bm, pa_bm_stats* out);
+
+/* One decode step's host work for a serving loop, in one call and one
+ * buffer.  The block manager appends one token to each of the `num` distinct
+ * sequences (as pa_bm_append_step, all or nothing), and the buffer receives
+ * what the step's GPU calls read, at the offsets the layout reports:
+ *   slots  int64 [num]        the new tokens' slots (pa_reshape_and_cache);
+ *   cows   int32 [n_cows][2]  copy-on-write pairs (pa_copy_blocks, first);
+ *   lens   int32 [num]        context lengths after the append;
+ *   tables int32 [num][max_blocks]: of each row only the first ceil(L / B)
+ *          entries are written (the only ones the kernels read); the rest
+ *          keeps whatever the buffer held;
+ *   plan   the decode plan for those lengths (pa_decode_plan_schedule with
+ *          `schedule`, default piece length), with the jobs' first-tile
+ *          entries when first_blocks != 0; layout->plan is its info.
+ * The caller uploads the first layout->bytes bytes in one copy and passes
+ * device addresses at the same offsets to pa_copy_blocks and pa_decode (with
+ * new_key/new_value the append is fused; see pa_decode).  buffer: HOST,
+ * 256-byte aligned, `capacity` bytes (pinned memory lets the upload run
+ * asynchronously).  The plan is built before the append, so PA_ERR_INVALID
+ * for a buffer too small (layout->bytes then gives the size needed), like
+ * every other refusal, leaves the block manager unchanged. */
+typedef struct pa_decode_step_layout {
+  int32_t bytes;      /* bytes to upload, from offset 0 */
+  int32_t num_seqs;
+  int32_t max_blocks;
+  int32_t n_cows;
+  int32_t slots_at;   /* byte offsets in the buffer */
+  int32_t cows_at;
+  int32_t lens_at;
+  int32_t tables_at;
+  int32_t plan_at;
+  int32_t reserved;
+  pa_decode_plan_info plan;
+} pa_decode_step_layout;
+pa_status pa_bm_prepare_decode_step(pa_bm* bm, const int64_t* seqs, int32_t num, int32_t max_blocks,
+                                    int32_t num_kv_heads, int32_t num_workgroups, int32_t schedule,
+                                    int32_t first_blocks, void* buffer, size_t capacity,
+                                    pa_decode_step_layout* layout);
 
 /* Verify that each block's count equals the number of tables naming it, that
  * no named block is on the free list, that no block is lost, and that every

@@ -398,6 +398,17 @@ def decode_noalloc(pool: KvPool, q, block_tables, context_lens, scale: float, pl
     return out
 
 
+def probe_read(src, num_workgroups: int, sink, nbytes: int | None = None, stream=None) -> None:
+    """pa_probe_read: stream-read nbytes (default: all) of device tensor src
+    once; sink is a device tensor of at least num_workgroups * 256 uint32."""
+    _dev(src, "src")
+    _dev(sink, "sink")
+    n = src.numel() * src.element_size() if nbytes is None else int(nbytes)
+    if n > src.numel() * src.element_size() or sink.numel() * sink.element_size() < 4 * 256 * num_workgroups:
+        raise ValueError("probe_read: nbytes past src or sink too small")
+    _check(lib.pa_probe_read(_ptr(src), n, num_workgroups, _ptr(sink), _stream(stream)), "pa_probe_read")
+
+
 class BlockManager:
     """Host block manager (pa_bm_*): free list, tables, counts, copy-on-write."""
 
@@ -529,6 +540,26 @@ class BlockManager:
 
     def host_refcount(self, block: int) -> int:
         return lib.pa_bm_host_refcount(self._h, block)
+
+    def prepare_decode_step(self, seqs, max_blocks: int, num_kv_heads: int, buffer, num_workgroups: int | None = None,
+                            schedule: int = -1, first_blocks: bool = True):
+        """pa_bm_prepare_decode_step: append one token to each sequence and
+        write slots, copy pairs, lengths, table rows and the plan for the new
+        lengths into `buffer` (a 256-byte aligned host uint8 array or pinned
+        tensor).  Returns (layout, DecodePlan whose blob views the buffer's
+        plan bytes)."""
+        from ._lib import PaDecodeStepLayout
+        seqs = np.ascontiguousarray(seqs, dtype=np.int64)
+        arr = buffer.numpy() if hasattr(buffer, "numpy") else buffer
+        if num_workgroups is None:
+            num_workgroups = default_workgroups()
+        lay = PaDecodeStepLayout()
+        _check(lib.pa_bm_prepare_decode_step(self._h, seqs.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), seqs.size,
+                                             max_blocks, num_kv_heads, num_workgroups, schedule, int(first_blocks),
+                                             ctypes.c_void_p(arr.ctypes.data), arr.nbytes, ctypes.byref(lay)),
+               "pa_bm_prepare_decode_step")
+        plan = DecodePlan(arr[lay.plan_at:lay.plan_at + lay.plan.bytes], PaDecodePlanInfo.from_buffer_copy(lay.plan))
+        return lay, plan
 
     def length(self, seq: int) -> int:
         n = lib.pa_bm_len(self._h, seq)

@@ -5,6 +5,10 @@ import ctypes
 import os
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedkv.so")
+# The sanitizer tests load the host-only sanitized build instead (no kernels:
+# its GPU entry points fail after their host checks); set only by them.
+if os.environ.get("PAGEDKV_HOST_SANITIZED_LIB"):
+    LIB_PATH = os.environ["PAGEDKV_HOST_SANITIZED_LIB"]
 
 PA_F32 = 0
 PA_BF16 = 1
@@ -40,6 +44,13 @@ class PaDecodePlanInfo(ctypes.Structure):
                 ("first_block_size", ctypes.c_int32), ("num_tiles", ctypes.c_int32),
                 ("num_seqs", ctypes.c_int32), ("max_context_len", ctypes.c_int32), ("reserved", ctypes.c_int32),
                 ("lens_digest", ctypes.c_uint64)]
+
+
+class PaDecodeStepLayout(ctypes.Structure):
+    _fields_ = [("bytes", ctypes.c_int32), ("num_seqs", ctypes.c_int32), ("max_blocks", ctypes.c_int32),
+                ("n_cows", ctypes.c_int32), ("slots_at", ctypes.c_int32), ("cows_at", ctypes.c_int32),
+                ("lens_at", ctypes.c_int32), ("tables_at", ctypes.c_int32), ("plan_at", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("plan", PaDecodePlanInfo)]
 
 
 class PaBmStats(ctypes.Structure):
@@ -97,6 +108,7 @@ SIGNATURES = {
     "pa_decode_attention": (_i32, _DECODE_ARGS),
     "pa_decode_merge_pieces": (_i32, _DECODE_ARGS),
     "pa_decode_noalloc": (_i32, _DECODE_ARGS[:14] + [_vp]),
+    "pa_probe_read": (_i32, [_vp, _sz, _i32, _vp, _vp]),
     "pa_bm_create": (_vp, [_i32, _i32, _p32]),
     "pa_bm_destroy": (None, [_vp]),
     "pa_bm_append": (_i32, [_vp, _i64, _i32, _p64, _p32, _p32]),
@@ -115,6 +127,9 @@ SIGNATURES = {
     "pa_bm_append_prompt": (_i32, [_vp, _i64, _p32, _i32, _p64, _p32]),
     "pa_bm_cached": (_i32, [_vp, _i32]),
     "pa_bm_len": (_i32, [_vp, _i64]),
+    "pa_bm_block_size": (_i32, [_vp]),
+    "pa_bm_prepare_decode_step": (_i32, [_vp, _p64, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _sz,
+                                         ctypes.POINTER(PaDecodeStepLayout)]),
     "pa_bm_refcount": (_i32, [_vp, _i32]),
     "pa_bm_get_stats": (None, [_vp, ctypes.POINTER(PaBmStats)]),
     "pa_bm_check": (_i32, [_vp]),

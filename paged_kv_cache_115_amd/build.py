@@ -27,7 +27,8 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", INCLUDE, "-I", CSRC,
 ]
-SOURCES = ["abi.cpp", "block_manager.cpp", "validate.cpp", "cache_kernels.hip", "decode_kernels.hip", "noalloc.hip"]
+SOURCES = ["abi.cpp", "block_manager.cpp", "validate.cpp", "step.cpp", "cache_kernels.hip", "decode_kernels.hip", "noalloc.hip",
+           "probe_kernels.hip"]
 
 
 def _hipcc() -> str:
@@ -69,5 +70,37 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+# Host-only library for the address and undefined-behaviour sanitizers: the
+# host sources (C ABI checks, block manager, planner, validation, step
+# preparation) built with g++ and -fsanitize, the kernel launchers replaced by
+# host_stubs.cpp.  A CPU-only target: it has no kernels, every GPU entry point
+# runs its host checks and then fails.  Used by tests/test_sanitized_host.py.
+HOST_SOURCES = ["abi.cpp", "block_manager.cpp", "validate.cpp", "step.cpp", "host_stubs.cpp"]
+SANITIZED_LIB = os.path.join(BUILD, "sanitize", "libpagedkv_host_sanitized.so")
+SANITIZE_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer"]
+
+
+def build_host_sanitized(verbose: bool = False) -> str:
+    """Compile the host sources with g++ under ASan and UBSan; returns the
+    library path."""
+    gxx = shutil.which("g++")
+    if gxx is None:
+        raise RuntimeError("g++ not found: the sanitized host library cannot be built")
+    os.makedirs(os.path.dirname(SANITIZED_LIB), exist_ok=True)
+    cmd = [gxx, "-O1", "-g", "-std=c++17", "-fPIC", "-shared", *SANITIZE_FLAGS, "-D__HIP_PLATFORM_AMD__",
+           "-I", "/opt/rocm/include", "-I", INCLUDE, "-I", CSRC, *[os.path.join(CSRC, f) for f in HOST_SOURCES],
+           "-L", "/opt/rocm/lib", "-Wl,-rpath,/opt/rocm/lib", "-lamdhip64", "-o", SANITIZED_LIB + ".tmp"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"g++ failed on the sanitized host build:\n{res.stderr}")
+    os.replace(SANITIZED_LIB + ".tmp", SANITIZED_LIB)
+    return SANITIZED_LIB
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--host-sanitized" in sys.argv:
+        print(build_host_sanitized(verbose="-v" in sys.argv))
+    else:
+        print(build(verbose="-v" in sys.argv))

@@ -80,6 +80,24 @@ WorkspaceLayout layout(int64_t heads, int64_t d) {
 
 using pagedkv::fail;
 
+namespace pagedkv {
+
+int64_t pool_block_bytes(const pa_kv_pool& pool) {
+  return (int64_t)pool.block_size * pool.num_kv_heads * pool.head_dim * (pool.dtype == PA_F32 ? 4 : 2);
+}
+
+pa_status noalloc_check(const pa_kv_pool* pool, const pa_decode_plan_info* info, int32_t num_q_heads,
+                        const char* who) {
+  if (!pool || !info) return fail(PA_ERR_INVALID, "%s: pool or info is NULL", who);
+  const size_t need = pa_decode_workspace_bytes(info, num_q_heads, pool->head_dim);
+  if (need > (size_t)PA_NOALLOC_SCRATCH_BYTES)
+    return fail(PA_ERR_INVALID, "%s: the plan needs %zu bytes of workspace, the built-in scratch holds %zu", who,
+                need, (size_t)PA_NOALLOC_SCRATCH_BYTES);
+  return PA_OK;
+}
+
+}  // namespace pagedkv
+
 extern "C" const char* pa_last_error(void) { return pagedkv::g_error; }
 
 extern "C" pa_status pa_reshape_and_cache(const pa_kv_pool* pool, const void* key, const void* value,
@@ -850,13 +868,19 @@ extern "C" pa_status pa_decode_plan_first_blocks(void* plan, pa_decode_plan_info
     if (j.seq < 0 || j.seq >= num_seqs)
       return fail(PA_ERR_INVALID, "%s: job slot %lld names sequence %d of %d", who, (long long)i, j.seq, num_seqs);
     const int32_t* row = tables + (int64_t)j.seq * max_blocks;
-    // The entries the kernel's table registers would hold for tiles 0 and 1
-    // of the job (index clamped into the row, as there).
+    // The entries of tiles 0 and 1 of the job: entry t / (B / 16) of tile t,
+    // entries 2t and 2t + 1 at B = 8.  Only the sequence's first
+    // ceil(L / B) entries are read; a position past them (the second tile of
+    // a one-tile job, the second half of a last tile at B = 8) gets 0, which
+    // the kernel never loads from.
+    const int64_t used = std::min<int64_t>(((int64_t)std::max(j.context_len, 0) + block_size - 1) / block_size,
+                                           max_blocks);
+    auto entry = [&](int64_t e) { return e >= 0 && e < used ? row[e] : 0; };
     for (int64_t k = 0; k < 2; ++k) {
       const int64_t t = (int64_t)std::max(j.tile_begin, 0) + k;
       const int64_t e0 = block_size == 8 ? 2 * t : t / tiles_per_block;
-      f[k] = row[std::min<int64_t>(std::max<int64_t>(e0, 0), max_blocks - 1)];
-      f[2 + k] = block_size == 8 ? row[std::min<int64_t>(e0 + 1, max_blocks - 1)] : 0;
+      f[k] = entry(e0);
+      f[2 + k] = block_size == 8 ? entry(e0 + 1) : 0;
     }
   }
   info->first_block_size = block_size;

@@ -432,6 +432,8 @@ extern "C" pa_status pa_bm_prefix_groups(const pa_bm* bm, const int64_t* seqs, i
   return PA_OK;
 }
 
+extern "C" int32_t pa_bm_block_size(const pa_bm* bm) { return bm ? bm->block_size : -1; }
+
 extern "C" int32_t pa_bm_len(const pa_bm* bm, int64_t seq) {
   if (!bm) return -1;
   auto it = bm->seqs.find(seq);

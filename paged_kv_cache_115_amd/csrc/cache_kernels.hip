@@ -113,10 +113,6 @@ int32_t elem_bytes(int32_t dtype) { return dtype == PA_F32 ? 4 : 2; }
 
 }  // namespace
 
-int64_t pool_block_bytes(const pa_kv_pool& pool) {
-  return (int64_t)pool.block_size * pool.num_kv_heads * pool.head_dim * elem_bytes(pool.dtype);
-}
-
 hipError_t launch_reshape_and_cache(const pa_kv_pool& pool, const void* key, const void* value,
                                     const int64_t* slots, int32_t num_tokens, hipStream_t stream) {
   const int32_t row_bytes = pool.num_kv_heads * pool.head_dim * elem_bytes(pool.dtype);

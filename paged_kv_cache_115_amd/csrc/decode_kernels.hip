@@ -277,7 +277,7 @@ __device__ __forceinline__ void load_bf16_tile(const DecodeArgs& a, int32_t g, i
   // reads the new row, which stays in L2): one load path, and no wait for
   // the loads in flight where two paths would join, at the price of the
   // buffer loads' cache policy.
-  const int32_t p1f = B == 8 ? clamp_block(e1, a.num_blocks) : p0;
+  const int32_t p1f = B == 8 && rows > 8 ? clamp_block(e1, a.num_blocks) : p0;
   auto row_addr = [&](const char* base, int32_t row) {
     if (B == 8) return base + (int64_t)(row < 8 ? p0 : p1f) * blk_bytes + (row & 7) * row_bytes;
     return base + (int64_t)p0 * blk_bytes + ((int64_t)((t0 + t) % kTilesPerBlock) * kTile + row) * row_bytes;
@@ -291,8 +291,11 @@ __device__ __forceinline__ void load_bf16_tile(const DecodeArgs& a, int32_t g, i
     for (int r = 0; r < 4; ++r)
       vf[r] = load_global<kStream>(4 * lq + r >= first_new ? nv + 16 * li : row_addr(vb, 4 * lq + r) + 16 * li);
   } else if (B == 8) {
-    // Rows 0..7 of the tile live in block p0, rows 8..15 in block p1.
-    const int32_t p1 = clamp_block(e1, a.num_blocks);
+    // Rows 0..7 of the tile live in block p0, rows 8..15 in block p1.  A
+    // last tile of at most 8 rows has no second block (its table entry lies
+    // past the context and is not read): those rows reload block p0 and are
+    // masked in compute.
+    const int32_t p1 = rows > 8 ? clamp_block(e1, a.num_blocks) : p0;
     const int64_t vblk = (int64_t)(lq < 2 ? p0 : p1) * blk_bytes;
 #pragma unroll
     for (int r = 0; r < 4; ++r) kf[r] = load_global<kStream>(kb + vblk + ((4 * lq + r) & 7) * row_bytes + 16 * li);

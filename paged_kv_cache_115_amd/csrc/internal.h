@@ -22,6 +22,11 @@ inline uint64_t lens_digest(const int32_t* lens, int32_t n) {
   return h;
 }
 
+// pa_decode_noalloc's host-side check: the plan's workspace fits the
+// built-in scratch array (PA_ERR_INVALID otherwise).
+pa_status noalloc_check(const pa_kv_pool* pool, const pa_decode_plan_info* info, int32_t num_q_heads,
+                        const char* who);
+
 // The decode front shared by the pa_decode entry points: argument checks,
 // then the launches selected by `stages` (kStageAttention | kStageMerge).
 constexpr int kStageAttention = 1;

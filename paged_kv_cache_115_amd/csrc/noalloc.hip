@@ -58,13 +58,9 @@ extern "C" pa_status pa_decode_noalloc(const pa_kv_pool* pool, const void* q, vo
                                        float scale, const void* new_key, const void* new_value, const void* plan,
                                        const pa_decode_plan_info* info, void* stream) {
   const char* who = "pa_decode_noalloc";
-  if (!pool || !info) return pagedkv::fail(PA_ERR_INVALID, "%s: pool or info is NULL", who);
   // The size check needs only the plan's info: a plan too large for the
   // array is refused before the device is touched.
-  const size_t need = pa_decode_workspace_bytes(info, num_q_heads, pool->head_dim);
-  if (need > (size_t)PA_NOALLOC_SCRATCH_BYTES)
-    return pagedkv::fail(PA_ERR_INVALID, "%s: the plan needs %zu bytes of workspace, the built-in scratch holds %zu",
-                         who, need, (size_t)PA_NOALLOC_SCRATCH_BYTES);
+  if (pa_status st = pagedkv::noalloc_check(pool, info, num_q_heads, who)) return st;
   if (info->num_jobs == 0 && info->num_merges == 0) return PA_OK;
   void* ws = nullptr;
   if (pa_status st = pagedkv::scratch_address(&ws, who)) return st;

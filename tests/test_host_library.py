@@ -709,7 +709,8 @@ def test_abi_rejects_bad_swap_arguments_without_launching():
 def test_first_tile_entries_match_the_tables(b):
     """pa_decode_plan_first_blocks writes, per job slot, the table entries
     of the job's tiles 0 and 1 (entry 2t and 2t + 1 at B = 8, t at B = 16,
-    t / 2 at B = 32; indices clamped into the row), zeros for empty slots."""
+    t / 2 at B = 32), 0 for an entry past the sequence's ceil(L / B) (never
+    read), zeros for empty slots."""
     rng = np.random.default_rng(70 + b)
     lens = rng.integers(0, 400, size=37)
     maxb = int(max(-(-int(L) // b) for L in lens))
@@ -732,7 +733,8 @@ def test_first_tile_entries_match_the_tables(b):
                     for kk in (0, 1):
                         t = t0 + kk
                         e = 2 * t + part if b == 8 else (t // (b // 16) if part == 0 else None)
-                        want.append(0 if e is None else int(tables[seq, min(e, maxb - 1)]))
+                        used = -(-int(lens[seq]) // b)
+                        want.append(0 if e is None or e >= used else int(tables[seq, e]))
                 assert fb[k, w].tolist() == want, (k, w)
     with pytest.raises(pk.PaError):
         plan.set_first_blocks(tables[:5], b)          # jobs name sequences past the rows given
