@@ -595,7 +595,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="c3", choices=sorted(WORKLOADS))
-    ap.add_argument("--block-size", type=int, default=None, choices=(8, 16, 32),
+    ap.add_argument("--block-size", type=int, default=None, choices=(1, 2, 4, 8, 16, 32),
                     help="block size (default: the workload's; c5, c6: 16)")
     ap.add_argument("--workgroups", type=int, default=None, help="persistent workgroups (default: fill the GPU)")
     ap.add_argument("--piece", type=int, default=0, help="longest job piece in 16-token tiles (0: auto)")
@@ -661,10 +661,12 @@ def main() -> int:
     cascade = "prefix_group" in w and not args.no_cascade
     def build_plan():
         if cascade:
-            p = pk.decode_plan_prefix(lens, hkv, hq, w["prefix_group"], w["prefix_tokens"], workgroups, args.piece)
+            p = pk.decode_plan_prefix(lens, hkv, hq, w["prefix_group"], w["prefix_tokens"], workgroups, args.piece,
+                                      block_size=B)
         else:
             sched = {"auto": pk.SCHEDULE_AUTO, "chunks": pk.SCHEDULE_CHUNKS, "lpt": pk.SCHEDULE_LPT}[args.schedule]
-            p = pk.decode_plan(lens, hkv, workgroups, args.piece, shared_kv=w["shared_kv"], schedule=sched)
+            p = pk.decode_plan(lens, hkv, workgroups, args.piece, shared_kv=w["shared_kv"], schedule=sched,
+                               block_size=B)
         if not args.no_first_blocks:
             p.set_first_blocks(tables, B)
         return p
@@ -842,6 +844,7 @@ def main() -> int:
         # block-size trade-off: slots reserved by the tables against live tokens (tail waste)
         "reserved_slots": int(sum(-(-int(L) // B) * B for L in lens)),
         "tail_waste_frac": round(1 - int(lens.sum()) / max(1, sum(-(-int(L) // B) * B for L in lens)), 5),
+        "table_entries_per_seq": round(float(np.mean([-(-int(L) // B) for L in lens])), 2),
         "us_per_output_token": round(ms_per_step * 1e3 / S, 5),
         "step_us_stats": step_stats,
         "decode_call_us": round(decode_us, 3),
@@ -869,10 +872,11 @@ def main() -> int:
         def plan_for(lens_h, tables_h):
             if cascade:
                 grp, tok = w["bm"].prefix_groups(np.arange(S))
-                p = pk.decode_plan_prefix(lens_h, hkv, hq, grp, tok, workgroups, args.piece)
+                p = pk.decode_plan_prefix(lens_h, hkv, hq, grp, tok, workgroups, args.piece, block_size=B)
             else:
                 sched = {"auto": pk.SCHEDULE_AUTO, "chunks": pk.SCHEDULE_CHUNKS, "lpt": pk.SCHEDULE_LPT}[args.schedule]
-                p = pk.decode_plan(lens_h, hkv, workgroups, args.piece, shared_kv=w["shared_kv"], schedule=sched)
+                p = pk.decode_plan(lens_h, hkv, workgroups, args.piece, shared_kv=w["shared_kv"], schedule=sched,
+                                   block_size=B)
             if not args.no_first_blocks:
                 p.set_first_blocks(tables_h, B)
             return p

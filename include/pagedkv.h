@@ -35,8 +35,9 @@
  *     arrays when the preconditions hold;
  *   - launch failures return PA_ERR_HIP.
  * Supported shapes: dtype F32 or BF16; head_dim 64 or 128 for F32, 128 for
- * BF16; block_size 8, 16 or 32; num_q_heads a multiple of num_kv_heads with
- * a group of at most 16 query heads per KV head.
+ * BF16; block_size 1, 2, 4, 8, 16 or 32 (below 8, a bf16 plan's jobs cover
+ * at most 8 * B tiles); num_q_heads a multiple of num_kv_heads with a group
+ * of at most 16 query heads per KV head.
  */
 #ifndef PAGEDKV_H
 #define PAGEDKV_H
@@ -216,6 +217,8 @@ typedef struct pa_decode_plan_info {
   int32_t max_context_len; /* longest context planned: pa_decode refuses tables too short for it */
   int32_t reserved;
   uint64_t lens_digest;   /* digest of the planned context lengths (pa_decode_plan_check_lens) */
+  int32_t max_job_tiles;  /* tiles of the longest job (block sizes below 8 allow at most 8 * B) */
+  int32_t reserved2;
 } pa_decode_plan_info;
 
 /* A job whose head_block field has this bit reads a prefix shared by the
@@ -260,7 +263,9 @@ typedef struct pa_decode_group {
  * block tables pa_decode will read (tables: int32 [num_seqs][max_blocks], the
  * same rows), for pools of block_size; sets PA_DECODE_FIRST_BLOCKS and
  * info->first_block_size.  Serving loops export the tables on the host
- * anyway (pa_bm_export); the entries are only valid for those tables.
+ * anyway (pa_bm_export); the entries are only valid for those tables.  Block
+ * sizes below 8 (a tile spans more blocks than a job slot's four entries)
+ * write nothing and leave the flag clear.
  * PA_ERR_INVALID for an inconsistent info or a job naming a sequence past
  * num_seqs. */
 pa_status pa_decode_plan_first_blocks(void* plan, pa_decode_plan_info* info, const int32_t* tables,

@@ -261,12 +261,23 @@ def default_workgroups() -> int:
 SCHEDULE_AUTO, SCHEDULE_CHUNKS, SCHEDULE_LPT = -1, 0, 1
 
 
+def _piece_cap(max_piece_tiles: int, block_size: int | None) -> int:
+    """Longest job in tiles: pools of fewer than 8 slots per block take jobs
+    of at most 8 * B tiles (the bf16 kernel's table window)."""
+    if block_size is not None and block_size < 8:
+        return min(max_piece_tiles, 8 * block_size) if max_piece_tiles > 0 else 8 * block_size
+    return max_piece_tiles
+
+
 def decode_plan(context_lens, num_kv_heads: int, num_workgroups: int | None = None,
-                max_piece_tiles: int = 0, shared_kv: bool = False, schedule: int = SCHEDULE_AUTO) -> DecodePlan:
+                max_piece_tiles: int = 0, shared_kv: bool = False, schedule: int = SCHEDULE_AUTO,
+                block_size: int | None = None) -> DecodePlan:
     """pa_decode_plan_schedule (pa_decode_plan for the automatic choice).
     num_workgroups defaults to default_workgroups().  shared_kv sets
     PA_DECODE_SHARED_KV: pass True when sequences of the batch share blocks
-    (forked prefixes), so K/V loads keep them cached."""
+    (forked prefixes), so K/V loads keep them cached.  block_size: the pool's
+    B; below 8 it caps pieces at 8 * B tiles, as pa_decode requires."""
+    max_piece_tiles = _piece_cap(max_piece_tiles, block_size)
     lens = np.ascontiguousarray(context_lens, dtype=np.int32)
     if num_workgroups is None:
         num_workgroups = default_workgroups()
@@ -286,11 +297,14 @@ def decode_plan(context_lens, num_kv_heads: int, num_workgroups: int | None = No
 
 
 def decode_plan_prefix(context_lens, num_kv_heads: int, num_q_heads: int, prefix_group, prefix_tokens,
-                       num_workgroups: int | None = None, max_piece_tiles: int = 0) -> DecodePlan:
+                       num_workgroups: int | None = None, max_piece_tiles: int = 0,
+                       block_size: int | None = None) -> DecodePlan:
     """pa_decode_plan_prefix: shared prefixes read once per group (cascade
     decode).  prefix_group/prefix_tokens as from BlockManager.prefix_groups.
     The plan carries PA_DECODE_SHARED_KV only when some shared block is still
-    read by more than one job (see pa_decode_plan_prefix)."""
+    read by more than one job (see pa_decode_plan_prefix).  block_size as for
+    decode_plan."""
+    max_piece_tiles = _piece_cap(max_piece_tiles, block_size)
     lens = np.ascontiguousarray(context_lens, dtype=np.int32)
     grp = np.ascontiguousarray(prefix_group, dtype=np.int32)
     tok = np.ascontiguousarray(prefix_tokens, dtype=np.int32)

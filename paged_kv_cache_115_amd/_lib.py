@@ -43,7 +43,7 @@ class PaDecodePlanInfo(ctypes.Structure):
                 ("groups_at", ctypes.c_int32), ("group_size", ctypes.c_int32), ("first_at", ctypes.c_int32),
                 ("first_block_size", ctypes.c_int32), ("num_tiles", ctypes.c_int32),
                 ("num_seqs", ctypes.c_int32), ("max_context_len", ctypes.c_int32), ("reserved", ctypes.c_int32),
-                ("lens_digest", ctypes.c_uint64)]
+                ("lens_digest", ctypes.c_uint64), ("max_job_tiles", ctypes.c_int32), ("reserved2", ctypes.c_int32)]
 
 
 class PaDecodeStepLayout(ctypes.Structure):

@@ -32,6 +32,8 @@ namespace {
 
 bool aligned(const void* p, size_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
 
+bool supported_block_size(int32_t b) { return b == 1 || b == 2 || b == 4 || b == 8 || b == 16 || b == 32; }
+
 pa_status check_pool(const pa_kv_pool* pool, const char* who) {
   if (!pool) return fail(PA_ERR_INVALID, "%s: pool is NULL", who);
   if (!pool->k || !pool->v) return fail(PA_ERR_INVALID, "%s: pool k/v pointer is NULL", who);
@@ -40,8 +42,8 @@ pa_status check_pool(const pa_kv_pool* pool, const char* who) {
   if (pool->num_blocks <= 0 || pool->num_kv_heads <= 0)
     return fail(PA_ERR_INVALID, "%s: num_blocks=%d num_kv_heads=%d must be positive", who,
                 pool->num_blocks, pool->num_kv_heads);
-  if (pool->block_size != 8 && pool->block_size != 16 && pool->block_size != 32)
-    return fail(PA_ERR_UNSUPPORTED, "%s: block_size %d (supported: 8, 16, 32)", who, pool->block_size);
+  if (!supported_block_size(pool->block_size))
+    return fail(PA_ERR_UNSUPPORTED, "%s: block_size %d (supported: 1, 2, 4, 8, 16, 32)", who, pool->block_size);
   const bool d_ok = pool->dtype == PA_F32 ? (pool->head_dim == 64 || pool->head_dim == 128)
                                           : pool->head_dim == 128;
   if (!d_ok)
@@ -723,7 +725,11 @@ pa_status emit_plan(const Schedule& sc, int32_t schedule_id, int32_t num_kv_head
   in.first_at = (int32_t)round_up((size_t)in.groups_at + sizeof(pa_decode_group) * sc.groups.size(), 64);
   in.first_block_size = 0;
   int64_t tiles = 0;
-  for (const Piece& pc : jobs) tiles += pc.job.tile_count;
+  in.max_job_tiles = 0;
+  for (const Piece& pc : jobs) {
+    tiles += pc.job.tile_count;
+    in.max_job_tiles = std::max(in.max_job_tiles, pc.job.tile_count);
+  }
   in.num_tiles = (int32_t)tiles;
   in.num_seqs = num_seqs;
   in.max_context_len = 0;
@@ -849,8 +855,11 @@ extern "C" pa_status pa_decode_plan_first_blocks(void* plan, pa_decode_plan_info
                                                 int32_t max_blocks, int32_t num_seqs, int32_t block_size) {
   const char* who = "pa_decode_plan_first_blocks";
   if (!plan || !info) return fail(PA_ERR_INVALID, "%s: plan or info is NULL", who);
-  if (block_size != 8 && block_size != 16 && block_size != 32)
-    return fail(PA_ERR_UNSUPPORTED, "%s: block_size %d (supported: 8, 16, 32)", who, block_size);
+  if (!pagedkv::supported_block_size(block_size))
+    return fail(PA_ERR_UNSUPPORTED, "%s: block_size %d (supported: 1, 2, 4, 8, 16, 32)", who, block_size);
+  // Below 8 slots a tile spans more blocks than the four entries per job
+  // slot hold: nothing is written and the flag stays clear.
+  if (block_size < 8) return PA_OK;
   const int64_t slots = (int64_t)info->jobs_per_workgroup * info->num_workgroups;
   if (info->jobs_at != 0 || info->first_at % 64 != 0 || slots < 0 ||
       (int64_t)info->first_at < 32 * slots || (int64_t)info->bytes < (int64_t)info->first_at + 16 * slots)
@@ -972,6 +981,13 @@ pa_status decode_stages(int stages, const char* who, const pa_kv_pool* pool, con
     return fail(PA_ERR_INVALID, "%s: inconsistent plan info", who);
   if (info->num_groups > 0 && pool->dtype != PA_BF16)
     return fail(PA_ERR_UNSUPPORTED, "%s: shared-prefix plans need a bf16 pool", who);
+  // Below 8 slots per block the bf16 kernel holds a window of 128 table
+  // entries per job, i.e. 8 * B tiles.
+  if (pool->dtype == PA_BF16 && pool->block_size < 8 && info->max_job_tiles > 8 * pool->block_size)
+    return fail(PA_ERR_INVALID,
+                "%s: at block size %d jobs may cover at most %d tiles (plan with max_piece_tiles <= %d); "
+                "the plan's longest covers %d",
+                who, pool->block_size, 8 * pool->block_size, 8 * pool->block_size, info->max_job_tiles);
   const auto lay = pagedkv::layout((int64_t)info->num_records * group, pool->head_dim);
   if (info->num_records > 0) {
     if (!workspace) return fail(PA_ERR_INVALID, "%s: workspace is NULL but the plan has records", who);
@@ -992,8 +1008,9 @@ pa_status decode_stages(int stages, const char* who, const pa_kv_pool* pool, con
   a.jobs = reinterpret_cast<const pa_decode_job*>(pb + info->jobs_at);
   a.merges = reinterpret_cast<const pa_decode_merge*>(pb + info->merges_at);
   a.groups = info->num_groups > 0 ? reinterpret_cast<const pa_decode_group*>(pb + info->groups_at) : nullptr;
-  a.first_blocks = first_blocks && pool->dtype == PA_BF16 ? reinterpret_cast<const int32_t*>(pb + info->first_at)
-                                                          : nullptr;
+  a.first_blocks = first_blocks && pool->dtype == PA_BF16 && pool->block_size >= 8
+                       ? reinterpret_cast<const int32_t*>(pb + info->first_at)
+                       : nullptr;
   a.num_groups = info->num_groups;
   char* ws = static_cast<char*>(workspace);
   a.partial_ml = info->num_records > 0 ? reinterpret_cast<float*>(ws + lay.ml) : nullptr;
@@ -1029,7 +1046,7 @@ pa_status decode_stages(int stages, const char* who, const pa_kv_pool* pool, con
   constexpr int64_t kShortSequenceTiles = 24;
   const int64_t seq_streams = (int64_t)num_seqs * ((hkv + 3) / 4);
   const bool short_seqs = (int64_t)info->num_tiles < kShortSequenceTiles * seq_streams;
-  a.fused_loads = new_key == nullptr ? 0 : (short_seqs || group < 4) ? 2 : 1;
+  a.fused_loads = new_key == nullptr ? 0 : (short_seqs || group < 4 || pool->block_size < 8) ? 2 : 1;
   if (stages & kStageAttention) {
     if (pa_status st = pagedkv::hip_status(pagedkv::launch_decode_attention(a, (hipStream_t)stream), who)) return st;
   }

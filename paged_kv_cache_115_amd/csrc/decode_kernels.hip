@@ -181,13 +181,24 @@ __device__ __forceinline__ void load_ref(const DecodeArgs& a, const pa_decode_jo
   view_job(a, jd, w, B, J.v);
   // Lanes past the job's last tile read an in-row entry that is never used.
   const int32_t* trow = a.tables + (int64_t)J.v.seq * a.max_blocks;
-  const int32_t t = J.v.t0 + lane;
-  int32_t e0 = B == 8 ? 2 * t : t / kTilesPerBlock;
-  e0 = min(max(e0, 0), a.max_blocks - 1);
-  // Raw entries: they are range-checked when used (after readlane), so
-  // nothing waits for this load before the job's first tile is issued.
-  J.tb0 = trow[e0];
-  J.tb1 = B == 8 ? trow[min(e0 + 1, a.max_blocks - 1)] : 0;
+  if (B < 8) {
+    // Blocks of fewer than 8 slots: a tile spans kTile / B entries.  Lane i
+    // holds entries e + i and e + 64 + i of the job's first entry e, a window
+    // of 128 entries = 8 * B tiles; plans for such pools keep every job
+    // within it (pa_decode checks).  Entries past the context are loaded
+    // with the window but never used.
+    const int32_t e = J.v.t0 * (kTile / B) + lane;
+    J.tb0 = trow[min(max(e, 0), a.max_blocks - 1)];
+    J.tb1 = trow[min(max(e + 64, 0), a.max_blocks - 1)];
+  } else {
+    const int32_t t = J.v.t0 + lane;
+    int32_t e0 = B == 8 ? 2 * t : t / kTilesPerBlock;
+    e0 = min(max(e0, 0), a.max_blocks - 1);
+    // Raw entries: they are range-checked when used (after readlane), so
+    // nothing waits for this load before the job's first tile is issued.
+    J.tb0 = trow[e0];
+    J.tb1 = B == 8 ? trow[min(e0 + 1, a.max_blocks - 1)] : 0;
+  }
   // A scalar load issued a job ahead and first waited for at the job's end.
   J.len_dev = as_const(a.lens)[J.v.seq];
 }
@@ -268,6 +279,34 @@ __device__ __forceinline__ void load_bf16_tile(const DecodeArgs& a, int32_t g, i
   const int64_t blk_bytes = (int64_t)row_bytes * B;
   const char* kb = reinterpret_cast<const char*>(a.k) + (int64_t)g * D * 2;
   const char* vb = reinterpret_cast<const char*>(a.v) + (int64_t)g * D * 2;
+  if (B < 8) {
+    // Blocks of fewer than 8 slots: the tile's rows lie in kTile / B blocks.
+    // e0 / e1 are the job's two window registers (lane i: entries i and
+    // 64 + i of the job); row 4 * lq + r takes its entry from the lane that
+    // holds it (one cross-lane permute per distinct block of the lane's four
+    // rows: 1 at B = 4, 2 at B = 2, 4 at B = 1) and is loaded through a
+    // per-lane address.  Rows past the context, and filler loads, read a
+    // fixed in-bounds row instead (the new row with the append fused, else
+    // the first row of q): they are masked in compute.  With the append
+    // fused, rows at and after the appended one read the new row.
+    constexpr int kE = kTile / B;
+    const int32_t jb = t * kE;  // the tile's first entry within the job's window (wave-uniform, < 128)
+    const int32_t win = jb < 64 ? e0 : e1;
+    const int32_t valid = min(rows, kTile);
+    const int32_t first_new = kFused != 0 ? (r_new >= 0 ? r_new : rows <= 0 ? 0 : kTile) : kTile;
+    const char* fk = kFused != 0 ? nk : reinterpret_cast<const char*>(a.q);
+    const char* fv = kFused != 0 ? nv : reinterpret_cast<const char*>(a.q);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 4 * lq + r;
+      const int32_t p = clamp_block(__shfl(win, (jb + row / B) & 63), a.num_blocks);
+      const int64_t off = (int64_t)p * blk_bytes + (int64_t)(row % B) * row_bytes + 16 * li;
+      const bool pool_row = row < valid && row < first_new;
+      kf[r] = load_global<kStream>(pool_row ? kb + off : fk + 16 * li);
+      vf[r] = load_global<kStream>(pool_row ? vb + off : fv + 16 * li);
+    }
+    return;
+  }
   const int32_t p0 = clamp_block(e0, a.num_blocks);
   // With the append fused (kFused 1 or 2), row r_new of the tile holding the
   // appended token and the rows after it (past the context; masked in
@@ -573,7 +612,7 @@ __device__ __forceinline__ void finish_bf16_job(const DecodeArgs& a, const JobVi
 
 template <int B, bool kStream, int kFused>
 __global__ __launch_bounds__(kNW * 64, kWavesPerSimd) void decode_bf16_kernel(DecodeArgs a) {
-  static_assert(B == 8 || B == 16 || B == 32, "block size");
+  static_assert(B == 1 || B == 2 || B == 4 || B == 8 || B == 16 || B == 32, "block size");
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: keeps job fields in SGPRs
   const int li = lane & 15;  // MFMA row / column within a 16-lane group
@@ -677,7 +716,11 @@ __global__ __launch_bounds__(kNW * 64, kWavesPerSimd) void decode_bf16_kernel(De
     const int32_t g = in_n ? nxt.v.g : in_n2 ? nx2.v.g : cur.v.g;
     const int32_t t0 = in_n ? nxt.v.t0 : in_n2 ? nx2.v.t0 : cur.v.t0;
     int32_t e0, e1;
-    if (first) {
+    if (B < 8) {
+      // The job's whole window registers (per lane); see load_bf16_tile.
+      e0 = in_n ? nxt.tb0 : in_n2 ? nx2.tb0 : cur.tb0;
+      e1 = in_n ? nxt.tb1 : in_n2 ? nx2.tb1 : cur.tb1;
+    } else if (first) {
       const i32x4_t f = in_n ? f1 : f0;
       e0 = t <= 0 ? f[0] : f[1];
       e1 = t <= 0 ? f[2] : f[3];
@@ -732,7 +775,7 @@ __global__ __launch_bounds__(kNW * 64, kWavesPerSimd) void decode_bf16_kernel(De
     st.reset();
     return true;
   };
-  if (a.first_blocks != nullptr) {
+  if (B >= 8 && a.first_blocks != nullptr) {
 #pragma unroll
     for (int u = 0; u < kDepth; ++u) issue_at(u, kf[u], vf[u], true, f0, f1);
     load_ref<B>(a, r1, w, lane, nxt);
@@ -1065,6 +1108,9 @@ hipError_t launch_decode_attention(const DecodeArgs& a, hipStream_t stream) {
     launched = true;                                                                                    \
     break;
     switch (a.block_size) {
+      PA_BF16_CASE(1)
+      PA_BF16_CASE(2)
+      PA_BF16_CASE(4)
       PA_BF16_CASE(8)
       PA_BF16_CASE(16)
       PA_BF16_CASE(32)
@@ -1078,9 +1124,15 @@ hipError_t launch_decode_attention(const DecodeArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((decode_f32_kernel<BS, DD>), grid, dim3(kNW * 64), 0, stream, a);     \
     launched = true;                                                                         \
   }
+    PA_F32_CASE(1, 64)
+    PA_F32_CASE(2, 64)
+    PA_F32_CASE(4, 64)
     PA_F32_CASE(8, 64)
     PA_F32_CASE(16, 64)
     PA_F32_CASE(32, 64)
+    PA_F32_CASE(1, 128)
+    PA_F32_CASE(2, 128)
+    PA_F32_CASE(4, 128)
     PA_F32_CASE(8, 128)
     PA_F32_CASE(16, 128)
     PA_F32_CASE(32, 128)

@@ -59,7 +59,9 @@ extern "C" pa_status pa_bm_prepare_decode_step(pa_bm* bm, const int64_t* seqs, i
       return fail(PA_ERR_INVALID, "%s: sequence %lld grows to %d tokens, past max_blocks %d of %d slots", who,
                   (long long)seqs[i], lens[i], max_blocks, B);
   pa_decode_plan_info info{};
-  const pa_status ps = pa_decode_plan_schedule(lens, num, num_kv_heads, num_workgroups, 0, schedule,
+  // Below 8 slots per block the bf16 kernel's jobs cover at most 8 * B tiles.
+  const int32_t max_piece_tiles = B < 8 ? 8 * B : 0;
+  const pa_status ps = pa_decode_plan_schedule(lens, num, num_kv_heads, num_workgroups, max_piece_tiles, schedule,
                                                buf + lay.plan_at, capacity - (size_t)lay.plan_at, &info);
   if (ps != PA_OK) {
     lay.bytes = lay.plan_at + info.bytes;

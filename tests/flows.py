@@ -56,9 +56,11 @@ def assert_close(out: np.ndarray, ref: np.ndarray, dt: str, where: str = "") -> 
 
 
 def plan_and_workspace(pk, lens: np.ndarray, hkv: int, hq: int, d: int, num_workgroups=None, max_piece_tiles=0,
-                       kind=-1, shared_kv=False):
-    """kind: a pk.SCHEDULE_* value (-1, the default: the automatic choice)."""
-    plan = pk.decode_plan(lens, hkv, num_workgroups, max_piece_tiles, shared_kv=shared_kv, schedule=kind)
+                       kind=-1, shared_kv=False, block_size=None):
+    """kind: a pk.SCHEDULE_* value (-1, the default: the automatic choice).
+    block_size: the pool's B (below 8 it caps the pieces)."""
+    plan = pk.decode_plan(lens, hkv, num_workgroups, max_piece_tiles, shared_kv=shared_kv, schedule=kind,
+                          block_size=block_size)
     nbytes = pk.decode_workspace_bytes(plan, hq, d)
     # The workspace needs no initialisation: fill it with NaN to prove it.
     ws = torch.full((nbytes // 4,), float("nan"), dtype=torch.float32, device="cuda") if nbytes else None
@@ -72,7 +74,7 @@ def gpu_decode(pk, pool, q_dev, tables, lens, scale, schedule=(None, 0), out_dty
     first_blocks: write the jobs' first-tile table entries into the plan."""
     hq = q_dev.shape[1]
     plan, plan_dev, ws = plan_and_workspace(pk, lens, pool.k.shape[2], hq, pool.k.shape[3], *schedule,
-                                            shared_kv=shared_kv)
+                                            shared_kv=shared_kv, block_size=pool.block_size)
     if first_blocks:
         plan.set_first_blocks(tables, pool.block_size)
         plan_dev = plan.to_device()
@@ -178,7 +180,8 @@ def cascade_decode(pk, pool, q_dev, tables, lens, scale, bm, seqs, schedule=(Non
     (pa_bm_prefix_groups -> pa_decode_plan_prefix)."""
     hq = q_dev.shape[1]
     group, tokens = bm.prefix_groups(seqs)
-    plan = pk.decode_plan_prefix(lens, pool.k.shape[2], hq, group, tokens, schedule[0], schedule[1])
+    plan = pk.decode_plan_prefix(lens, pool.k.shape[2], hq, group, tokens, schedule[0], schedule[1],
+                                 block_size=pool.block_size)
     if first_blocks:
         plan.set_first_blocks(tables, pool.block_size)
     nbytes = pk.decode_workspace_bytes(plan, hq, pool.k.shape[3])

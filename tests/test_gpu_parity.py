@@ -37,11 +37,12 @@ def log(msg):
 
 # ------------------------------------------------------------ cache kernels
 @pytest.mark.parametrize("dt,b,hkv,d", [("f32", 16, 4, 64), ("bf16", 16, 8, 128), ("bf16", 8, 8, 128),
-                                        ("bf16", 32, 2, 128), ("f32", 32, 3, 128)])
+                                        ("bf16", 32, 2, 128), ("f32", 32, 3, 128), ("bf16", 1, 8, 128),
+                                        ("bf16", 4, 8, 128), ("f32", 2, 4, 64)])
 def test_reshape_and_cache_bit_exact(pk, dt, b, hkv, d):
     log(f"reshape_and_cache dt={dt} B={b} Hkv={hkv} D={d}")
     rng = np.random.default_rng(21)
-    nb = 61
+    nb = max(61, 2 * 400 // b)
     shape = (nb, b, hkv, d)
     kp = synth.byte_pattern(shape, dt, 1)
     vp = synth.byte_pattern(shape, dt, 2)
@@ -58,7 +59,8 @@ def test_reshape_and_cache_bit_exact(pk, dt, b, hkv, d):
     assert np.array_equal(bits(to_host(vd)), bits(vp))
 
 
-@pytest.mark.parametrize("dt,b,hkv,d", [("bf16", 16, 8, 128), ("bf16", 32, 8, 128), ("f32", 8, 4, 64)])
+@pytest.mark.parametrize("dt,b,hkv,d", [("bf16", 16, 8, 128), ("bf16", 32, 8, 128), ("f32", 8, 4, 64),
+                                        ("bf16", 2, 8, 128), ("f32", 1, 4, 64)])
 def test_copy_blocks_bit_exact(pk, dt, b, hkv, d):
     log(f"copy_blocks dt={dt} B={b}")
     rng = np.random.default_rng(22)
@@ -155,7 +157,7 @@ def test_fused_append_equals_separate_cache_write(pk, name, schedule):
 
 
 @pytest.mark.parametrize("long_context", [False, True])
-@pytest.mark.parametrize("b", [8, 16, 32])
+@pytest.mark.parametrize("b", [1, 2, 4, 8, 16, 32])
 def test_fused_append_edge_lengths(pk, b, long_context):
     """The appended token at every position of a tile and of a block, in
     empty, one-token and full-table contexts, for each block size.  These
@@ -295,10 +297,11 @@ def test_merge_of_many_pieces(pk, dt, d, cap, parts):
     assert_close(got["out"], ref["out"], dt, f"merge {parts} pieces {dt}")
 
 
-@pytest.mark.parametrize("b", [8, 16, 32])
+@pytest.mark.parametrize("b", [1, 2, 4, 8, 16, 32])
 def test_edge_lengths(pk, b):
     """Empty contexts, one token, exact block/tile multiples and one past
-    them, pieces of 64 tiles, and a context filling its table exactly."""
+    them, pieces of 64 tiles (8 * B below B = 8), and a context filling its
+    table exactly."""
     lens = [0, 1, 7, 8, 9, 15, 16, 17, 31, 32, 33, 63, 64, 65, 0, 255, 256, 257, 1023, 1024, 1025, 2100]
     case = _edge_case(lens, b)
     ref = oracle_decode_step(case)
@@ -334,7 +337,7 @@ def test_single_token_context_returns_value_exactly(pk):
 
 
 # ------------------------------------------------------- prefix sharing, CoW
-@pytest.mark.parametrize("b", [8, 16, 32])
+@pytest.mark.parametrize("b", [1, 4, 8, 16, 32])
 def test_prefix_sharing_matches_oracle_and_private_copies(pk, b):
     log(f"prefix sharing c5s B={b}")
     case = synth.prefix_case("c5s", b)
@@ -366,7 +369,7 @@ def test_shared_kv_cache_policy_gives_identical_output(pk, b):
     assert np.array_equal(bits(streamed), bits(got["out"]))
 
 
-@pytest.mark.parametrize("b", [8, 16, 32])
+@pytest.mark.parametrize("b", [2, 4, 8, 16, 32])
 @pytest.mark.parametrize("schedule", [DEFAULT, SMALL_PIECES, TINY_PIECES])
 def test_cascade_decode_matches_oracle(pk, b, schedule):
     """Shared prefixes read once per group of samples (pa_decode_plan_prefix):
@@ -485,3 +488,53 @@ def test_plan_for_other_lengths_gives_nan_not_numbers(pk, name, schedule):
         torch.cuda.synchronize()
         assert np.array_equal(bits(to_host(got["pool"].k)), bits(ref["kpool"]))
         assert np.array_equal(bits(to_host(got["pool"].v)), bits(ref["vpool"]))
+
+
+def _at_block_size(case: dict, b: int) -> dict:
+    """The same lengths and K/V with pools of block size b (a seeded pool of
+    the same slack and a shuffled free list)."""
+    out = dict(case)
+    out["cfg"] = dict(case["cfg"], block_size=b)
+    nb = synth.pool_blocks_for(case["lengths"], b)
+    out["num_blocks"] = nb
+    out["free_order"] = np.random.default_rng(500 + b).permutation(nb).astype(np.int32)
+    return out
+
+
+@pytest.mark.parametrize("b", [1, 2, 4])
+@pytest.mark.parametrize("schedule", [DEFAULT, FEW_WG, SMALL_PIECES])
+def test_small_block_sizes_match_oracle(pk, b, schedule):
+    """Blocks of 1, 2 and 4 slots (a 16-token tile spans 16, 8 or 4 blocks;
+    the pages' block-size sweep starts at 1): the batch-256-shaped GQA case
+    (c3s, 24 sequences) through the block manager, the cache kernels and the
+    decode launch, separate and fused append; tables, slots and pools
+    bit-exact, outputs within tolerance of the oracle; fp32 too (c1)."""
+    for name in ("c3s", "c1"):
+        log(f"block size {b} {name} schedule={schedule}")
+        case = _at_block_size(synth.decode_case(name), b)
+        ref = oracle_decode_step(case)
+        for fused in (False, True):
+            got = product_decode_step(pk, case, schedule, fused=fused)
+            assert np.array_equal(got["tables"], ref["tables"])
+            assert got["new_slots"] == ref["new_slots"]
+            assert np.array_equal(bits(got["kpool"]), bits(ref["kpool"]))
+            assert np.array_equal(bits(got["vpool"]), bits(ref["vpool"]))
+            stats = assert_close(got["out"], ref["out"], case["cfg"]["dtype"], f"B={b} {name} {schedule} fused={fused}")
+            log(f"  fused={fused} max|err|={stats['max_abs']:.3g} mean|err|={stats['mean_abs']:.3g}")
+
+
+@pytest.mark.parametrize("b", [1, 2, 4])
+def test_small_block_sizes_refuse_jobs_past_the_table_window(pk, b):
+    """Below 8 slots per block a job may cover at most 8 * B tiles; a plan
+    with longer jobs is refused before any launch."""
+    case = _at_block_size(synth.decode_case("c3s"), b)
+    got = product_decode_step(pk, case, DEFAULT)
+    cfg = case["cfg"]
+    plan = pk.decode_plan(got["lens"], cfg["num_kv_heads"], num_workgroups=4, max_piece_tiles=64,
+                          schedule=pk.SCHEDULE_LPT)
+    assert plan.info.max_job_tiles > 8 * b
+    nbytes = max(pk.decode_workspace_bytes(plan, cfg["num_q_heads"], cfg["head_dim"]), 256)
+    ws = torch.empty(nbytes // 4, device="cuda")
+    with pytest.raises(pk.PaError, match="at most"):
+        pk.decode(got["pool"], got["q_dev"], to_dev(got["tables"]), to_dev(got["lens"]), case["scale"], plan,
+                  plan.to_device(), ws)
