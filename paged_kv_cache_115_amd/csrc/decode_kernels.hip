@@ -77,6 +77,10 @@ typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// 1 / sum for a softmax denominator: 0 for an empty context (sum 0), NaN
+// for a poisoned one (NaN sum), 1 / sum otherwise.
+__device__ __forceinline__ float recip_sum(float l) { return l > 0.f ? 1.0f / l : l == 0.f ? 0.f : l; }
+
 __device__ __forceinline__ uint32_t bf16_rne(float x) {
   uint32_t u = __float_as_uint(x);
   if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
@@ -170,7 +174,6 @@ template <int B>
 struct JobRef {
   JobView v;
   int32_t tb0, tb1;
-  int32_t len_dev;  // context_lens[seq] on the device, compared with the planned length at the job's end
 };
 
 // The context length, the table entries and (load_q) the query of one job
@@ -199,8 +202,6 @@ __device__ __forceinline__ void load_ref(const DecodeArgs& a, const pa_decode_jo
     J.tb0 = trow[e0];
     J.tb1 = B == 8 ? trow[min(e0 + 1, a.max_blocks - 1)] : 0;
   }
-  // A scalar load issued a job ahead and first waited for at the job's end.
-  J.len_dev = as_const(a.lens)[J.v.seq];
 }
 
 
@@ -374,14 +375,16 @@ struct SoftmaxState {
 };
 
 // A plan made for other lengths than the device's context_lens (a plan kept
-// from an earlier step, say) must not yield plausible numbers: the job's
-// accumulator and sum become NaN, so every output element of the sequence
-// does (directly, or through the merge of its records).
-__device__ __forceinline__ void poison_if_stale(int32_t len_dev, int32_t len_plan, SoftmaxState& st) {
-  if (len_dev == len_plan) return;
-#pragma unroll
-  for (int c = 0; c < 8; ++c) st.o[c] = float4_t{NAN, NAN, NAN, NAN};
-  st.l = NAN;
+// from an earlier step, say) must not yield plausible numbers.  When a
+// finished job is written (from the stage after the wavefront's last job, or
+// directly), its planned length is compared with the sequence's device
+// length; on a mismatch the job's softmax sum is written as NaN, and every
+// normalisation (recip_sum) passes NaN on, so every output element of the
+// sequence is NaN, whether written directly or through the merge of its
+// records.  The comparison sits outside the tile loop's hot path: code in
+// the loop costs registers there.
+__device__ __forceinline__ float sum_or_nan(const DecodeArgs& a, int32_t seq, int32_t len_plan, float l) {
+  return as_const(a.lens)[seq] == len_plan ? l : NAN;
 }
 
 // One 16-token tile (tile t of job v): scores, online-softmax update, PV
@@ -483,14 +486,16 @@ __device__ __forceinline__ void flush_stage(const DecodeArgs& a, Stage& sg, int 
     const int32_t seq = __builtin_amdgcn_readfirstlane(sg.meta[4 * e + 0]);
     const int32_t g = __builtin_amdgcn_readfirstlane(sg.meta[4 * e + 1]);
     const int32_t rec = __builtin_amdgcn_readfirstlane(sg.meta[4 * e + 2]);
+    const int32_t len_plan = __builtin_amdgcn_readfirstlane(sg.meta[4 * e + 3]);
     if (li >= G || rec < -1) continue;  // -2: a shared job's member without a valid record
     const float* eo = sg.o + e * 128 * G;
     float4 v[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) v[k] = *reinterpret_cast<const float4*>(eo + ((k * 4 + lq) * G + li) * 4);
-    const float m = sg.ml[(e * 16 + li) * 2], lt = sg.ml[(e * 16 + li) * 2 + 1];
+    const float m = sg.ml[(e * 16 + li) * 2];
+    const float lt = sum_or_nan(a, seq, len_plan, sg.ml[(e * 16 + li) * 2 + 1]);
     if (rec < 0) {
-      const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+      const float inv = recip_sum(lt);
       const int64_t base = ((int64_t)seq * a.num_q_heads + (int64_t)g * G + li) * D + 32 * lq;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -548,15 +553,17 @@ __device__ __forceinline__ void finish_bf16_job(const DecodeArgs& a, const JobVi
         }
         if (lq == 0) *reinterpret_cast<float2*>(sg.ml + (e * 16 + lg) * 2) = make_float2(st.m, lt);
         if (lg == 0 && lq == 0) {
-          sg.meta[4 * e + 0] = 0;
+          sg.meta[4 * e + 0] = v.seq;
           sg.meta[4 * e + 1] = v.g;
           sg.meta[4 * e + 2] = valid ? (int32_t)rec : -2;
+          sg.meta[4 * e + 3] = v.L;
         }
       }
       sg.n += members;
       return;
     }
     if (li >= v.ncol || !valid) return;
+    lt = sum_or_nan(a, v.seq, v.L, lt);
     const int64_t rr = rec * G + li % G;
     float* po = a.partial_o + rr * D + 32 * lq;
 #pragma unroll
@@ -570,8 +577,9 @@ __device__ __forceinline__ void finish_bf16_job(const DecodeArgs& a, const JobVi
   if (v.rec == -2) return;
   if (sg.n == sg.cap) {
     if (li >= G) return;
+    lt = sum_or_nan(a, v.seq, v.L, lt);
     if (v.rec < 0) {
-      const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+      const float inv = recip_sum(lt);
       const int64_t base = ((int64_t)v.seq * a.num_q_heads + (int64_t)v.g * G + li) * D + 32 * lq;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -606,6 +614,7 @@ __device__ __forceinline__ void finish_bf16_job(const DecodeArgs& a, const JobVi
     sg.meta[4 * e + 0] = v.seq;
     sg.meta[4 * e + 1] = v.g;
     sg.meta[4 * e + 2] = v.rec;
+    sg.meta[4 * e + 3] = v.L;
   }
   sg.n = e + 1;
 }
@@ -631,16 +640,17 @@ __global__ __launch_bounds__(kNW * 64, kWavesPerSimd) void decode_bf16_kernel(De
   // (tile_count 0) ends the column.
   // Start-up is a chain of round trips: kernel arguments, job records (and
   // first-tile entries), then the first tile loads.  Each link is one batch:
-  // the three 64-byte lines of the arguments are requested together here
-  // (later argument reads hit the scalar cache), and every record the
-  // prologue needs is requested before the first of them is waited for.
+  // the argument lines holding what the start-up needs (the job table and
+  // its shape, the first-tile entries, tables, lengths, q and the pools; see
+  // DecodeArgs) are requested together here, and every record the prologue
+  // needs is requested before the first of them is waited for.
   // Without the pins the compiler requests argument fields and records one
   // at a time as they are used, each behind a wait for all scalar loads.
   {
-    const uint64_t line0 = reinterpret_cast<uint64_t>(a.k);
-    const uint64_t line1 = reinterpret_cast<uint64_t>(a.first_blocks);
-    const int32_t line1b = a.num_blocks, line2 = a.num_workgroups;
-    asm volatile("" ::"s"(line0), "s"(line1), "s"(line1b), "s"(line2));
+    const uint64_t line0 = reinterpret_cast<uint64_t>(a.jobs);
+    const uint64_t line0b = reinterpret_cast<uint64_t>(a.k);
+    const int32_t line1 = a.num_workgroups, line1b = a.jobs_per_workgroup;
+    asm volatile("" ::"s"(line0), "s"(line0b), "s"(line1), "s"(line1b));
   }
   const int32_t jend = a.jobs_per_workgroup;
   if (jend <= 0) return;
@@ -681,7 +691,6 @@ __global__ __launch_bounds__(kNW * 64, kWavesPerSimd) void decode_bf16_kernel(De
   load_ref<B>(a, r0, w, lane, cur);
   view_job(a, r1, w, B, nxt.v);
   nxt.tb0 = nxt.tb1 = 0;
-  nxt.len_dev = nxt.v.L;
   // The third job's table entries and the second job's query, and with the
   // plan's first-tile entries the second job's table entries too, are
   // requested after the first two positions (below): the vector memory
@@ -690,7 +699,6 @@ __global__ __launch_bounds__(kNW * 64, kWavesPerSimd) void decode_bf16_kernel(De
   // third job, and with first-tile entries they read no table.
   view_job(a, r2, w, B, nx2.v);
   nx2.tb0 = nx2.tb1 = 0;
-  nx2.len_dev = nx2.v.L;
   bf16x8_t qc[4], qn[4];
   load_q(a, cur.v, li, lq, qc);
   SoftmaxState st;
@@ -752,7 +760,6 @@ __global__ __launch_bounds__(kNW * 64, kWavesPerSimd) void decode_bf16_kernel(De
     compute_bf16_tile(a, cur.v, qc, x - x0, li, lq, ks, vs, kt, st);
     ++x;
     if (x - x0 < cur.v.cnt) return true;
-    poison_if_stale(cur.len_dev, cur.v.L, st);
     finish_bf16_job(a, cur.v, li, lq, st, sg);
     if (!hn) return false;
     x0 += cur.v.cnt;
@@ -875,17 +882,13 @@ __global__ __launch_bounds__(kNW * 64) void decode_f32_kernel(DecodeArgs a) {
     if (len_dev != v.L) {
       // Planned for another length: NaN, never plausible numbers.
 #pragma unroll
-      for (int h = 0; h < kMaxGroup; ++h) {
-        l_run[h] = NAN;
-#pragma unroll
-        for (int jj = 0; jj < DPL; ++jj) o[h][jj] = NAN;
-      }
+      for (int h = 0; h < kMaxGroup; ++h) l_run[h] = NAN;
     }
 #pragma unroll
     for (int h = 0; h < kMaxGroup; ++h) {
       if (h >= G) break;
       if (v.rec < 0) {
-        const float inv = l_run[h] > 0.f ? 1.0f / l_run[h] : 0.f;
+        const float inv = recip_sum(l_run[h]);
         const int64_t base = ((int64_t)v.seq * a.num_q_heads + (int64_t)v.g * G + h) * D;
 #pragma unroll
         for (int jj = 0; jj < DPL; ++jj) store1(a, base + lane + 64 * jj, o[h][jj] * inv);
@@ -979,7 +982,7 @@ __device__ __forceinline__ float2 merge_pair(const DecodeArgs& a, int32_t record
       }
     }
   }
-  const float inv = den > 0.f ? 1.0f / den : 0.f;
+  const float inv = recip_sum(den);
   return make_float2(n0 * inv, n1 * inv);
 }
 
@@ -1036,7 +1039,7 @@ __device__ __forceinline__ float2 merge_pair_wave(const DecodeArgs& a, int32_t r
       }
     }
   }
-  const float inv = den > 0.f ? 1.0f / den : 0.f;
+  const float inv = recip_sum(den);
   return make_float2(n0 * inv, n1 * inv);
 }
 

@@ -8,32 +8,35 @@
 
 namespace pagedkv {
 
-// Arguments of one decode call; pointers are device pointers.
+// Arguments of one decode call; pointers are device pointers.  The fields
+// the attention launch's start-up needs (job table, first-tile entries,
+// tables, lengths, q, the pools, the job-table shape) come first, so that
+// they arrive in the first batch of argument loads.
 struct DecodeArgs {
-  const void* k;
-  const void* v;
-  const void* q;
-  const void* new_k;             // [num_seqs][num_kv_heads][head_dim] or null: fused append of token L - 1
-  const void* new_v;
-  void* out;
+  const pa_decode_job* jobs;     // [jobs_per_workgroup][num_workgroups], column-major lists
+  const int32_t* first_blocks;   // [jobs_per_workgroup][num_workgroups][4] first-tile table entries, or null
   const int32_t* tables;
   const int32_t* lens;
-  const pa_decode_job* jobs;     // [jobs_per_workgroup][num_workgroups], column-major lists
-  const pa_decode_merge* merges; // [num_merges]
-  const pa_decode_group* groups; // [num_groups] prefix-group descriptors
-  const int32_t* first_blocks;   // [jobs_per_workgroup][num_workgroups][4] first-tile table entries, or null
-  float* partial_ml;             // [num_records * group][2] = (max, sum) in log2 units
-  float* partial_o;              // [num_records * group][head_dim], unnormalised
-  int32_t num_blocks;
-  int32_t block_size;
-  int32_t num_kv_heads;
-  int32_t num_q_heads;
-  int32_t group;                 // num_q_heads / num_kv_heads
-  int32_t head_dim;
-  int32_t max_blocks;            // block-table row length
-  int32_t num_seqs;
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* new_k;             // [num_seqs][num_kv_heads][head_dim] or null: fused append of token L - 1
   int32_t num_workgroups;
   int32_t jobs_per_workgroup;
+  int32_t num_blocks;
+  int32_t max_blocks;            // block-table row length
+  int32_t num_kv_heads;
+  int32_t num_seqs;
+  int32_t group;                 // num_q_heads / num_kv_heads
+  int32_t num_q_heads;
+  const void* new_v;
+  void* out;
+  const pa_decode_merge* merges; // [num_merges]
+  const pa_decode_group* groups; // [num_groups] prefix-group descriptors
+  float* partial_ml;             // [num_records * group][2] = (max, sum) in log2 units
+  float* partial_o;              // [num_records * group][head_dim], unnormalised
+  int32_t block_size;
+  int32_t head_dim;
   int32_t num_jobs;
   int32_t num_merges;
   int32_t num_records;
