@@ -266,9 +266,11 @@ namespace pagedkv {
 namespace {
 
 // One candidate schedule: jobs with their workgroup, merge rows, record count.
+// A workgroup runs its jobs by rank, then in schedule order.
 struct Piece {
   int32_t wg;
   pa_decode_job job;
+  int32_t rank = 1;
 };
 struct Schedule {
   std::vector<Piece> pieces;
@@ -278,6 +280,7 @@ struct Schedule {
   int64_t nwg = 1;
   int32_t group_size = 0;
   bool reread = false;  // some block is read by more than one job (prefix plans)
+  bool ranked = false;  // some piece has a rank other than 1
 };
 
 constexpr int64_t kStreamCharge = 4;   // cost units (tokens) charged per stream start by the chunk walk
@@ -313,9 +316,13 @@ struct Stream {
 // share holds the tile's midpoint.  Consecutive tiles of one stream on one
 // workgroup form jobs of at most `cap` tiles.  Returns, per stream, its
 // pieces in order (indices into out.pieces) through `first`/`count`, and the
-// order in which the streams were laid out.
+// order in which the streams were laid out.  With `base` (cost already placed
+// on each of the nwg_req workgroups), the shares are not equal but fill every
+// workgroup up to one common level: workgroup b's share is max(0, level -
+// base[b]), with the level at which the shares add up to the streams' cost.
 void chunk_streams(std::vector<Stream>& streams, int64_t nwg_req, int64_t cap, Schedule& out,
-                   std::vector<int32_t>& first, std::vector<int32_t>& count, std::vector<int32_t>& order) {
+                   std::vector<int32_t>& first, std::vector<int32_t>& count, std::vector<int32_t>& order,
+                   const std::vector<int64_t>* base = nullptr) {
   // Items: runs of consecutive streams with the same item id.
   std::vector<int32_t> item_first;
   for (size_t i = 0; i < streams.size(); ++i)
@@ -343,17 +350,42 @@ void chunk_streams(std::vector<Stream>& streams, int64_t nwg_req, int64_t cap, S
     total += rows_between(st.L, st.t_begin, st.t_end) + kStreamCharge;
     total_tiles += st.t_end - st.t_begin;
   }
-  const int64_t nwg = std::max<int64_t>(1, std::min<int64_t>(nwg_req, total_tiles));
+  const int64_t nwg = base ? nwg_req : std::max<int64_t>(1, std::min<int64_t>(nwg_req, total_tiles));
   out.nwg = nwg;
   first.assign(streams.size(), 0);
   count.assign(streams.size(), 0);
   out.pieces.reserve(out.pieces.size() + streams.size() + nwg);
+  // Share boundaries with base loads: starts[k] = 2 * (shares of workgroups
+  // below k), from the water level over the sorted loads.
+  std::vector<int64_t> starts;
+  if (base) {
+    std::vector<int64_t> sorted(base->begin(), base->end());
+    std::sort(sorted.begin(), sorted.end());
+    double below = 0, level = (double)sorted[0] + (double)total;
+    for (int64_t k = 0; k < nwg; ++k) {  // the level with the k + 1 lightest workgroups under it
+      below += (double)sorted[k];
+      const double l = ((double)total + below) / (double)(k + 1);
+      if (k + 1 == nwg || l <= (double)sorted[k + 1]) {
+        level = l;
+        break;
+      }
+    }
+    starts.assign(nwg + 1, 0);
+    double acc = 0;
+    for (int64_t b = 0; b < nwg; ++b) {
+      starts[b] = (int64_t)std::ceil(2 * acc);
+      acc += std::max(0.0, level - (double)(*base)[b]);
+    }
+    starts[nwg] = INT64_MAX;
+  }
   // The tile whose midpoint m / 2 (m = 2 * cum + c) lies in share w has
   // w = floor(m * nwg / (2 * total)).  m grows from tile to tile, so w only
   // advances: it is tracked against the first m of the next share instead of
   // dividing per tile.
   int64_t cum = 0, w = 0;
-  auto share_start = [&](int64_t k) { return (k * 2 * total + nwg - 1) / nwg; };  // least m with w >= k
+  auto share_start = [&](int64_t k) {  // least m with w >= k
+    return base ? starts[k] : (k * 2 * total + nwg - 1) / nwg;
+  };
   int64_t next = share_start(1);
   for (int32_t si : order) {
     const Stream& st = streams[si];
@@ -444,6 +476,103 @@ pa_status finish_chunks(const int32_t* lens, int32_t num_seqs, int32_t num_kv_he
   return PA_OK;
 }
 
+// Compute dies of the device: the dispatcher hands workgroup b to die
+// b mod kDies, and the dies do not share their L2 caches (MI355X: 8 XCDs of
+// 32 compute units, 4 MB of L2 each).
+constexpr int64_t kDies = 8;
+// Cost, in tokens, of a 16-token tile of a prefix that several planned
+// groups share and that is placed as below: after the first reader on a die
+// the tile comes from that die's L2, not from HBM (measured on MI355X: about
+// 1.0 us per tile and wavefront against 1.3 us for a tile from HBM; 12
+// balanced the c6-shaped batch best among 4, 8, 12 and 16).
+constexpr int64_t kWideTileCost = 12;
+
+// Placement of the shared streams of wide prefixes (a key group cut into
+// several planned groups, each reading the same prefix blocks) so that the
+// reads of one prefix meet in one die's L2.  The streams, ordered by (key
+// group, head block), are dealt to the dies at stream granularity in equal
+// shares of tiles.  On a die holding m streams and n workgroups, m <= n,
+// every stream is cut into the same R = floor(n / m) tile ranges (fewer if
+// ranges would be shorter than 8 tiles on average), and the
+// pieces, laid out set by set and range by range (range 0 of every stream
+// of the set, then range 1, ...), go one per workgroup: the workgroups that
+// read range r of one prefix hold it at the same time, all on one die.  (A
+// die with more streams than workgroups cuts them, laid end to end, into
+// equal consecutive chunks.)  The first half of a die's workgroups run their
+// shared piece before their other jobs, the second half after them:
+// workgroups b and b + nwg/2 share a compute unit, which then streams from
+// HBM with one while it reads from L2 with the other.  Adds each workgroup's
+// cost to `base`.
+void place_wide(const std::vector<Stream>& streams, const std::vector<int32_t>& wide,
+                const std::vector<int32_t>& set_of, int64_t nwg, int64_t cap, Schedule& out,
+                std::vector<int32_t>& first, std::vector<int32_t>& count, std::vector<int64_t>& base) {
+  const int64_t per_die = nwg / kDies;
+  int64_t total = 0;
+  for (int32_t i : wide) total += streams[i].t_end - streams[i].t_begin;
+  const int64_t unit = kWideTileCost;
+  std::vector<std::vector<Piece>> own(streams.size());
+  // Tiles [t0, t1) of a stream on slot c (of n) of a die.
+  auto put = [&](int64_t die, int32_t si, int32_t t0, int32_t t1, int64_t c, int64_t n) {
+    const Stream& st = streams[si];
+    const int32_t wg = (int32_t)(die + kDies * (c * per_die / n));
+    const int32_t rank = 2 * c >= n ? 2 : 0;
+    std::vector<Piece>& v = own[si];
+    for (int32_t t = t0; t < t1;) {
+      if (v.empty() || v.back().wg != wg || v.back().job.tile_begin + v.back().job.tile_count != t ||
+          v.back().job.tile_count >= cap)
+        v.push_back(Piece{wg, pa_decode_job{st.seq, t, 0, st.hb, 0, 1, -1, st.L}, rank});
+      const int32_t k = std::min<int32_t>(t1 - t, (int32_t)cap - v.back().job.tile_count);
+      v.back().job.tile_count += k;
+      base[wg] += unit * k;
+      t += k;
+    }
+  };
+  int64_t cum = 0;
+  size_t k = 0;
+  for (int64_t die = 0; die < kDies && k < wide.size(); ++die) {
+    // This die's streams: those whose midpoint falls in its share.
+    std::vector<int32_t> mine;
+    int64_t tiles = 0;
+    for (; k < wide.size(); ++k) {
+      const int64_t t = streams[wide[k]].t_end - streams[wide[k]].t_begin;
+      if (die < kDies - 1 && (2 * cum + t) * kDies >= 2 * total * (die + 1)) break;
+      mine.push_back(wide[k]);
+      tiles += t;
+      cum += t;
+    }
+    const int64_t m = (int64_t)mine.size();
+    if (m == 0) continue;
+    if (m <= per_die) {
+      // Ranges of at least 8 tiles (each piece is a job and a record per member).
+      const int64_t R = std::max<int64_t>(1, std::min<int64_t>(per_die / m, tiles / m / 8)), n = m * R;
+      int64_t c = 0;
+      for (int64_t a = 0; a < m;) {
+        int64_t e = a;
+        while (e < m && set_of[mine[e]] == set_of[mine[a]]) ++e;
+        for (int64_t r = 0; r < R; ++r)
+          for (int64_t j = a; j < e; ++j, ++c) {
+            const Stream& st = streams[mine[j]];
+            const int64_t T = st.t_end - st.t_begin;
+            put(die, mine[j], st.t_begin + (int32_t)(T * r / R), st.t_begin + (int32_t)(T * (r + 1) / R), c, n);
+          }
+        a = e;
+      }
+    } else {
+      // Tile u of the streams laid end to end goes to chunk floor((2u + 1) n / (2 tiles)).
+      int64_t u = 0;
+      for (int32_t si : mine)
+        for (int32_t t = streams[si].t_begin; t < streams[si].t_end; ++t, ++u)
+          put(die, si, t, t + 1, (2 * u + 1) * per_die / (2 * tiles), per_die);
+    }
+  }
+  for (int32_t i : wide) {
+    first[i] = (int32_t)out.pieces.size();
+    count[i] = (int32_t)own[i].size();
+    out.pieces.insert(out.pieces.end(), own[i].begin(), own[i].end());
+  }
+  out.ranked = true;
+}
+
 // Chunk schedule with prefix groups.  A group of n members sharing T tiles
 // gives one item of shared streams (tiles [0, T) of the first member, per
 // head block) and, per member, an item of its own streams (tiles [T, end)).
@@ -501,7 +630,45 @@ pa_status schedule_prefix(const int32_t* lens, int32_t num_seqs, int32_t num_kv_
     for (int32_t hb = 0; hb < head_blocks; ++hb) streams.push_back(Stream{s, hb, t0, (lens[s] + 15) / 16, lens[s], -1, item});
   }
   std::vector<int32_t> first, count, order;
-  chunk_streams(streams, nwg_req, cap, out, first, count, order);
+  // Shared streams of wide prefixes (several planned groups of one key group)
+  // get a placement of their own when the grid covers every die evenly.
+  std::vector<int32_t> wide, rest, set_of(streams.size(), -1);
+  if (nwg_req % kDies == 0 && nwg_req >= 8 * kDies) {
+    // Groups of one key group are consecutive; a set is one (key group, head
+    // block) of a key group planned as several groups.
+    int32_t run = -1;
+    for (size_t gi = 0; gi < groups.size(); ++gi) {
+      const int32_t key = prefix_group[groups[gi][0]];
+      if (gi == 0 || prefix_group[groups[gi - 1][0]] != key) ++run;
+      const bool w = (gi > 0 && prefix_group[groups[gi - 1][0]] == key) ||
+                     (gi + 1 < groups.size() && prefix_group[groups[gi + 1][0]] == key);
+      if (!w) continue;
+      for (int32_t hb = 0; hb < head_blocks; ++hb) set_of[gi * head_blocks + hb] = run * head_blocks + hb;
+    }
+    // By set, then group.
+    std::vector<int32_t> ws;
+    for (size_t i = 0; i < streams.size(); ++i) (set_of[i] >= 0 ? ws : rest).push_back((int32_t)i);
+    std::stable_sort(ws.begin(), ws.end(), [&](int32_t x, int32_t y) { return set_of[x] < set_of[y]; });
+    wide = ws;
+  }
+  if (wide.empty()) {
+    chunk_streams(streams, nwg_req, cap, out, first, count, order);
+  } else {
+    first.assign(streams.size(), 0);
+    count.assign(streams.size(), 0);
+    std::vector<int64_t> base(nwg_req, 0);
+    place_wide(streams, wide, set_of, nwg_req, cap, out, first, count, base);
+    std::vector<Stream> rs;
+    rs.reserve(rest.size());
+    for (int32_t i : rest) rs.push_back(streams[i]);
+    std::vector<int32_t> rf, rc, ro;
+    chunk_streams(rs, nwg_req, cap, out, rf, rc, ro, &base);
+    for (size_t k = 0; k < rest.size(); ++k) {
+      first[rest[k]] = rf[k];
+      count[rest[k]] = rc[k];
+    }
+    for (int32_t k : ro) order.push_back(rest[k]);
+  }
   // Records, in layout order of the own streams: a grouped member always has
   // records (its shared pieces and its own); others only when cut.
   std::vector<int32_t> rb((size_t)num_seqs * head_blocks, -1), parts((size_t)num_seqs * head_blocks, 0);
@@ -748,8 +915,17 @@ pa_status emit_plan(const Schedule& sc, int32_t schedule_id, int32_t num_kv_head
   char* out = static_cast<char*>(plan);
   char* table = out + in.jobs_at;
   std::vector<int32_t> fill(nwg, 0);
-  for (const Piece& pc : jobs)
+  auto put = [&](const Piece& pc) {
     std::memcpy(table + sizeof(pa_decode_job) * ((size_t)fill[pc.wg]++ * nwg + pc.wg), &pc.job, sizeof(pa_decode_job));
+  };
+  if (sc.ranked) {
+    std::vector<int32_t> by_rank(jobs.size());
+    for (size_t i = 0; i < jobs.size(); ++i) by_rank[i] = (int32_t)i;
+    std::stable_sort(by_rank.begin(), by_rank.end(), [&](int32_t x, int32_t y) { return jobs[x].rank < jobs[y].rank; });
+    for (int32_t i : by_rank) put(jobs[i]);
+  } else {
+    for (const Piece& pc : jobs) put(pc);
+  }
   const pa_decode_job empty{0, 0, 0, 0, 0, 0, -1, 0};
   for (int64_t b = 0; b < nwg; ++b)
     for (int64_t k = fill[b]; k < per; ++k)

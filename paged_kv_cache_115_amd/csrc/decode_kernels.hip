@@ -63,6 +63,8 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kNW = 4;          // wavefronts per workgroup = KV heads per job
 constexpr int kDepth = 2;       // bf16 kernel: K/V tiles in flight per wavefront
@@ -86,6 +88,29 @@ __device__ __forceinline__ uint32_t bf16_rne(float x) {
   if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
   u += 0x7fffu + ((u >> 16) & 1u);
   return u >> 16;
+}
+
+// Two floats as packed bfloat16, rounded to nearest even by the hardware
+// conversion (v_cvt_pk_bf16_f32); lo in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(float2_t{lo, hi}, bf16x2_t));
+}
+
+// Max / sum over lanes i, i ^ 16, i ^ 32, i ^ 48 (one column of a 16x16
+// MFMA result: rows 4*lq + r live in lanes li + 16*lq).  Each gfx950 lane
+// swap (lanes i and i ^ 32, then i and i ^ 16) hands every lane its own value
+// and its partner's, without the LDS round trip of a bpermute.
+__device__ __forceinline__ float col_max(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float col_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 __device__ __forceinline__ uint32_t word(const uint4& v, int i) {
@@ -423,34 +448,34 @@ __device__ __forceinline__ void compute_bf16_tile(const DecodeArgs& a, const Job
     x[r] = sacc[r] * a.scale_log2e;
     if (tail && tok0 + 4 * lq + r >= v.L) x[r] = -INFINITY;
   }
-  float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-  mx = fmaxf(mx, __shfl_xor(mx, 16));
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
-  const float m_new = fmaxf(st.m, mx);
-  const float alpha = fast_exp2(st.m - m_new);
-  uint32_t pb[4];
-  float psum = 0.f;
+  const float mx = col_max(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+  // The accumulators and the sum are rescaled only when some column's max
+  // grows (a wave-uniform branch): past the first tiles of a long context the
+  // max rarely moves.  The first tile of a job always rescales (from a max of
+  // -inf, by 0).
+  if (__builtin_amdgcn_ballot_w64(mx > st.m) != 0) {
+    const float m_new = fmaxf(st.m, mx);
+    const float alpha = fast_exp2(st.m - m_new);
+    st.l *= alpha;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    pb[r] = bf16_rne(fast_exp2(x[r] - m_new));
-    psum += __uint_as_float(pb[r] << 16);
+    for (int c = 0; c < 8; ++c) st.o[c] *= alpha;
+    st.m = m_new;
   }
-  st.l = st.l * alpha + psum;
-  st.m = m_new;
-  const short4_t pfrag =
-      __builtin_bit_cast(short4_t, make_uint2(pb[0] | (pb[1] << 16), pb[2] | (pb[3] << 16)));
+  const uint32_t p01 = pack_bf16x2(fast_exp2(x[0] - st.m), fast_exp2(x[1] - st.m));
+  const uint32_t p23 = pack_bf16x2(fast_exp2(x[2] - st.m), fast_exp2(x[3] - st.m));
+  // The sum takes the rounded probabilities, the ones the PV product uses.
+  st.l += ((__uint_as_float(p01 << 16) + __uint_as_float(p01 & 0xffff0000u)) + __uint_as_float(p23 << 16)) +
+          __uint_as_float(p23 & 0xffff0000u);
+  const short4_t pfrag = __builtin_bit_cast(short4_t, make_uint2(p01, p23));
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
+    // Lane (li, lq) holds dims 8*li .. 8*li + 8 of rows 4*lq + r in vf[r];
+    // instance c takes dim 8*li + c of the four rows: 16-bit halves of word
+    // c / 2, gathered by byte permutes.
     const int wd = c >> 1;
-    uint32_t lo, hi;
-    if (c & 1) {
-      lo = (word(vf[0], wd) >> 16) | (word(vf[1], wd) & 0xffff0000u);
-      hi = (word(vf[2], wd) >> 16) | (word(vf[3], wd) & 0xffff0000u);
-    } else {
-      lo = (word(vf[0], wd) & 0xffffu) | (word(vf[1], wd) << 16);
-      hi = (word(vf[2], wd) & 0xffffu) | (word(vf[3], wd) << 16);
-    }
-    st.o[c] *= alpha;
+    const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+    const uint32_t lo = __builtin_amdgcn_perm(word(vf[1], wd), word(vf[0], wd), sel);
+    const uint32_t hi = __builtin_amdgcn_perm(word(vf[3], wd), word(vf[2], wd), sel);
     st.o[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4_t, make_uint2(lo, hi)), pfrag,
                                                         st.o[c], 0, 0, 0);
   }
@@ -524,8 +549,7 @@ __device__ __forceinline__ void finish_bf16_job(const DecodeArgs& a, const JobVi
                                                 const SoftmaxState& st, Stage& sg) {
   constexpr int D = 128;
   const int G = a.group;
-  float lt = st.l + __shfl_xor(st.l, 16);
-  lt = lt + __shfl_xor(lt, 32);
+  float lt = col_sum(st.l);
   if (v.shared) {
     // Shared prefix piece: column li is head li % G of member li / G.  Each
     // member's record for this piece is staged as an entry of its own (the

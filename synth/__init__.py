@@ -67,6 +67,11 @@ PREFIX_CONFIGS: dict[str, dict] = {
     "c5s": dict(seed=15, num_prompts=3, samples=4, prefix_len=100, tail=(1, 40),
                 num_q_heads=32, num_kv_heads=8, head_dim=128, dtype="bf16",
                 block_sizes=(8, 16, 32)),
+    # More samples per prompt than one group of a shared read holds (c6's
+    # shape at oracle size: each prompt's prefix is shared by several groups).
+    "c5w": dict(seed=35, num_prompts=3, samples=14, prefix_len=300, tail=(1, 40),
+                num_q_heads=32, num_kv_heads=8, head_dim=128, dtype="bf16",
+                block_sizes=(8, 16, 32)),
 }
 
 BF16_NAN = np.uint16(0x7FC0)

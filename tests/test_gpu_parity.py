@@ -387,6 +387,26 @@ def test_cascade_decode_matches_oracle(pk, b, schedule):
 
 
 @pytest.mark.parametrize("b", [8, 16, 32])
+@pytest.mark.parametrize("schedule", [(512, 0), (64, 0), (72, 0), (64, 3), (7, 3)])
+def test_wide_prefix_cascade_matches_oracle(pk, b, schedule):
+    """Prompts sampled 14 times: each prefix is shared by four groups (three of
+    four samples and one of two), which the plan places on one die of the grid
+    when the grid is a multiple of 8 of at least 64 workgroups (512, 64, 72),
+    and by the chunk schedule otherwise (7).  Same outputs as the oracle
+    within tolerance and as the per-sequence plan within the
+    accumulation-order difference."""
+    log(f"cascade c5w B={b} schedule={schedule}")
+    case = synth.prefix_case("c5w", b)
+    got = product_prefix(pk, case, schedule, cascade=True)
+    assert got["plan"].num_groups > 0 and got["plan"].info.flags == pk.PA_DECODE_SHARED_KV
+    ref = oracle_prefix(case)
+    stats = assert_close(got["out"], ref["out"], "bf16", f"cascade c5w/B{b}/{schedule}")
+    log(f"  max|err|={stats['max_abs']:.3g} mean|err|={stats['mean_abs']:.3g} groups={got['plan'].num_groups}")
+    plain = product_prefix(pk, case, schedule)
+    assert np.abs(got["out"] - plain["out"]).max() < 2e-3
+
+
+@pytest.mark.parametrize("b", [8, 16, 32])
 def test_cascade_decode_with_first_tile_entries(pk, b):
     log(f"cascade c5s B={b} with first-tile entries")
     case = synth.prefix_case("c5s", b)

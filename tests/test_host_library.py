@@ -936,3 +936,79 @@ def test_prefix_plan_structure(b):
     assert alone.num_groups == 0
     with pytest.raises(pk.PaError):
         pk.decode_plan_prefix(lens, 8, 30, group, tokens, num_workgroups=8)
+
+
+def _wide_batch(b=16, prompts=3, samples=20, prefix=1000, seed=5):
+    rng = np.random.default_rng(seed)
+    tails = rng.integers(1, 200, prompts * samples)
+    bm, seqs = _forked_batch(b, prompts, samples, prefix, tails)
+    tables, lens = bm.export(seqs, 128)
+    group, tokens = bm.prefix_groups(seqs)
+    return lens, group, tokens
+
+
+@pytest.mark.parametrize("nwg", [512, 64, 72, 7])
+def test_wide_prefix_plan_invariants(nwg):
+    """Key groups of more members than one group holds (G = 4: 20 samples of
+    a prompt make 5 groups of 4) keep every plan invariant, whatever the grid
+    (die-aware placement on grids that are multiples of 8 and at least 64,
+    the chunk schedule otherwise)."""
+    lens, group, tokens = _wide_batch()
+    for hkv, hq in [(8, 32), (4, 16), (8, 64), (3, 6)]:
+        plan = pk.decode_plan_prefix(lens, hkv, hq, group, tokens, num_workgroups=nwg)
+        assert plan.num_groups > 0 and plan.info.flags == pk.PA_DECODE_SHARED_KV
+        _check_prefix_plan(plan, lens, hkv, hq, group, tokens)
+
+
+def _placement(plan):
+    """Per workgroup: its jobs in slot order as (shared, group descriptor, head
+    block, tile_begin, tile_count, seq)."""
+    tab = plan.job_table()
+    out = []
+    for b in range(tab.shape[1]):
+        out.append([(bool(j[3] & pk.PA_JOB_SHARED), int(j[6]), int(j[3] & 0xFFFF), int(j[1]), int(j[2]), int(j[0]))
+                    for j in tab[:, b].tolist() if j[2] > 0])
+    return out
+
+
+@pytest.mark.parametrize("nwg", [512, 64])
+def test_wide_prefix_placement_meets_on_one_die(nwg):
+    """The shared streams of one wide prefix (several groups of one key group,
+    per head block) run on one die (workgroup b on die b mod 8), cut into the
+    same tile ranges, one piece per workgroup; the first half of a die's
+    workgroups run it before their other jobs, the second half after them;
+    and the chunk walk tops every workgroup up to about the same cost."""
+    lens, group, tokens = _wide_batch()
+    hkv, hq = 8, 32
+    plan = pk.decode_plan_prefix(lens, hkv, hq, group, tokens, num_workgroups=nwg)
+    groups = plan.groups()
+    place = _placement(plan)
+    per_die = nwg // 8
+    key_of = lambda d: int(group[int(groups[d][2])])
+    sets = {}
+    for b, jobs in enumerate(place):
+        sh = [j for j in jobs if j[0]]
+        for k, j in enumerate(jobs):
+            if j[0]:
+                sets.setdefault((key_of(j[1]), j[2]), []).append((b % 8, b, j[1], j[3], j[4]))
+        if sh:
+            # one shared piece per workgroup here; first half: first, second half: last
+            assert len(sh) == 1
+            i = b // 8
+            pos = jobs.index(sh[0])
+            assert pos == 0 if 2 * i < per_die else pos == len(jobs) - 1
+    for (key, hb), pieces in sets.items():
+        dies = {p[0] for p in pieces}
+        assert len(dies) <= 2
+        # the pieces of one die and set share their tile ranges
+        for die in dies:
+            ranges = {}
+            for _, b, d, t0, cnt in pieces:
+                if b % 8 == die:
+                    ranges.setdefault(d, []).append((t0, cnt))
+            shapes = {tuple(sorted(v)) for v in ranges.values()}
+            assert len(shapes) == 1, shapes
+    # cost balance: shared tile = 12, own token = 1 (+ the walk's stream charge)
+    cost = np.array([sum(12 * j[4] if j[0] else min(int(lens[j[5]]), 16 * (j[3] + j[4])) - 16 * j[3]
+                         for j in jobs) for jobs in place])
+    assert cost.max() <= cost.mean() * 1.15 + 64, (cost.max(), cost.mean())
