@@ -593,7 +593,8 @@ def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=200,
+                    help="untimed steps first: an idle GPU runs its first milliseconds of work slower")
     ap.add_argument("--config", default="c3", choices=sorted(WORKLOADS))
     ap.add_argument("--block-size", type=int, default=None, choices=(1, 2, 4, 8, 16, 32),
                     help="block size (default: the workload's; c5, c6: 16)")
