@@ -416,7 +416,8 @@ def swap_sweep(torch, pk, lengths, reps: int = 10) -> int:
     return 0
 
 
-def e2e_loop(torch, pk, w, pools, q_d, new_k, new_v, out, steps: int, build_plan, native_step=None) -> dict:
+def e2e_loop(torch, pk, w, pools, q_d, new_k, new_v, out, steps: int, build_plan, native_step=None,
+             plan_reuse: int = 0) -> dict:
     """A serving loop over the workload's batch, `steps` decode steps long.
     Each step the host appends one token to every sequence (block manager),
     writes table rows and lengths, builds the plan for the new lengths,
@@ -429,7 +430,8 @@ def e2e_loop(torch, pk, w, pools, q_d, new_k, new_v, out, steps: int, build_plan
     native_step = (num_workgroups, schedule, first_blocks): the host work is
     one pa_bm_prepare_decode_step call into a pinned buffer and one upload;
     otherwise (cascade plans) the separate binding calls, staged and uploaded
-    one array at a time."""
+    one array at a time.  plan_reuse: the block manager advances its last
+    plan (pa_bm_set_plan_reuse) for up to that many steps between builds."""
     bm, S, B, R = w["bm"], w["S"], w["B"], len(pools)
     seqs = np.arange(S)
     dev = torch.device("cuda", 0)
@@ -442,11 +444,15 @@ def e2e_loop(torch, pk, w, pools, q_d, new_k, new_v, out, steps: int, build_plan
     stage_done = [torch.cuda.Event() for _ in range(2)]
     if native_step is not None:
         nwg, sched, first = native_step
-        parts = {k: [] for k in ("prepare", "upload", "launch")}
+        bm.set_plan_reuse(plan_reuse)
+        parts = {k: [] for k in ("wait", "prepare", "upload", "launch")}
         cap = 256 * (-(-(16 * S + 4 * S * maxw + 4 * S + plan_cap) // 256) + 8)
         stage = [torch.empty(cap, dtype=torch.uint8).pin_memory() for _ in range(2)]
         for st_ in stage:
             st_.numpy()[:] = 0
+        # One device buffer, uploaded on the launch stream: an upload on a
+        # copy stream of its own with event waits both ways measured slower
+        # (190 against 82 us per step at C3).
         dev_buf = torch.empty(cap, dtype=torch.uint8, device=dev)
         views = None
         torch.cuda.synchronize()
@@ -456,6 +462,7 @@ def e2e_loop(torch, pk, w, pools, q_d, new_k, new_v, out, steps: int, build_plan
             j = k % 2
             if k >= 2:
                 stage_done[j].synchronize()       # the upload of step k - 2 has read this buffer
+            tw = time.perf_counter()
             lay, plan = bm.prepare_decode_step(seqs, maxw, w["hkv"], stage[j], nwg, sched, first)
             t1 = time.perf_counter()
             dev_buf[:lay.bytes].copy_(stage[j][:lay.bytes], non_blocking=True)
@@ -473,7 +480,7 @@ def e2e_loop(torch, pk, w, pools, q_d, new_k, new_v, out, steps: int, build_plan
             pk.decode(pool, q_d, tables_e, lens_e, w["case"]["scale"], plan, plan_e, ws, out, stream,
                       new_key=new_k, new_value=new_v)
             t3 = time.perf_counter()
-            for name, a, b in (("prepare", t0, t1), ("upload", t1, t2), ("launch", t2, t3)):
+            for name, a, b in (("wait", t0, tw), ("prepare", tw, t1), ("upload", t1, t2), ("launch", t2, t3)):
                 parts[name].append((b - a) * 1e6)
         torch.cuda.synchronize()
         wall_us = (time.perf_counter() - t_start) * 1e6 / steps
@@ -528,7 +535,9 @@ def e2e_loop(torch, pk, w, pools, q_d, new_k, new_v, out, steps: int, build_plan
     host = {name: round(float(np.median(v)), 2) for name, v in parts.items()}
     host_total = round(float(np.median([sum(x) for x in zip(*parts.values())])), 2)
     return {"steps": steps, "us_per_step": round(wall_us, 2), "decode_tokens_per_s": round(S / (wall_us * 1e-6), 1),
-            "host_path": "pa_bm_prepare_decode_step, one upload" if native_step is not None else
+            "host_path": (f"pa_bm_prepare_decode_step, one upload; the plan built every {plan_reuse + 1} steps and "
+                          "advanced (pa_decode_plan_advance) in between" if plan_reuse else
+                          "pa_bm_prepare_decode_step, one upload") if native_step is not None else
                          "separate binding calls, one upload per array",
             "host_us_median": host, "host_total_us_median": host_total,
             "note": "wall time per step of the whole serving loop (host block manager, plan, uploads and the GPU "
@@ -621,6 +630,8 @@ def main() -> int:
     ap.add_argument("--read-probe", action="store_true",
                     help="time a plain streaming read (pa_probe_read) at 16 MB .. 1 GiB, fit fixed cost and "
                          "streaming rate, and exit")
+    ap.add_argument("--plan-reuse", type=int, default=15,
+                    help="end-to-end loop: steps a plan is advanced (pa_decode_plan_advance) before it is rebuilt")
     ap.add_argument("--e2e-steps", type=int, default=32,
                     help="steps of the end-to-end serving loop timed last (host append, export, plan and upload "
                          "of every step overlapped with the GPU step before it); 0 skips it")
@@ -884,7 +895,8 @@ def main() -> int:
         native = None if cascade else (workgroups, plan.schedule if args.schedule == "auto" else
                                        {"chunks": pk.SCHEDULE_CHUNKS, "lpt": pk.SCHEDULE_LPT}[args.schedule],
                                        not args.no_first_blocks)
-        e2e = e2e_loop(torch, pk, w, pools, q_d, new_k, new_v, out, args.e2e_steps, plan_for, native)
+        e2e = e2e_loop(torch, pk, w, pools, q_d, new_k, new_v, out, args.e2e_steps, plan_for, native,
+                       args.plan_reuse)
         if native is not None:
             e2e["schedule"] = ["chunks", "largest pieces first"][native[1]] + \
                 " (the automatic choice for the batch at the first step, kept)"

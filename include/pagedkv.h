@@ -55,7 +55,8 @@ typedef enum {
   PA_ERR_UNSUPPORTED = -2, /* valid but not implemented (dtype, head_dim, block size, group) */
   PA_ERR_OOM = -3,         /* block manager: not enough free blocks; state unchanged */
   PA_ERR_NOT_FOUND = -4,   /* block manager: unknown sequence */
-  PA_ERR_HIP = -5          /* a HIP runtime call failed */
+  PA_ERR_HIP = -5,         /* a HIP runtime call failed */
+  PA_REPLAN = 1            /* pa_decode_plan_advance: the plan cannot follow the new lengths; build a new one */
 } pa_status;
 
 typedef enum { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
@@ -347,6 +348,29 @@ pa_status pa_decode_plan_prefix(const int32_t* context_lens, int32_t num_seqs, i
  * Plans are made per step, and lengths grow by one every step: a plan kept
  * from an earlier step describes other lengths. */
 pa_status pa_decode_plan_check_lens(const pa_decode_plan_info* info, const int32_t* context_lens, int32_t num_seqs);
+
+/* pa_decode_plan_advance - carry a plan to the next step's lengths.
+ * Between decode steps every sequence grows by one token (S06
+ * "Implementation": the length passed per call; mercemay.com "Blocks,
+ * tables, and the indirection": a new block only every B tokens), so most
+ * sequences keep their tiles and the rest gain one.  This updates, in place,
+ * a plan made by pa_decode_plan / pa_decode_plan_schedule (HOST plan bytes
+ * and info) for context_lens (HOST int32 [num_seqs]):
+ *   - every job record takes its sequence's new length;
+ *   - a sequence whose tile count grew by one extends, in every head block,
+ *     the job holding its last tile (its records and merge rows are kept);
+ *   - the info's tile count, longest job, longest context and length digest
+ *     follow; PA_DECODE_FIRST_BLOCKS is cleared (call
+ *     pa_decode_plan_first_blocks again for the new tables).
+ * The work stays where it was placed, so the balance drifts with the steps:
+ * callers rebuild every few steps.  PA_REPLAN, with the plan unchanged, when
+ * the plan cannot follow: a prefix plan (num_groups > 0), a sequence that
+ * lost tiles, gained more than one, or went from empty to non-empty, or an
+ * extended job longer than max_job_tiles (0: 64; block sizes below 8 need
+ * 8 * B).  PA_ERR_INVALID for another num_seqs, a negative length or an
+ * inconsistent plan.  O(jobs + num_seqs). */
+pa_status pa_decode_plan_advance(void* plan, pa_decode_plan_info* info, const int32_t* context_lens,
+                                 int32_t num_seqs, int32_t max_job_tiles);
 
 /* Bytes of device workspace pa_decode needs for a plan (0 when no sequence is
  * cut).  The workspace needs no initialisation; it carries records from the
@@ -682,6 +706,18 @@ pa_status pa_bm_prepare_decode_step(pa_bm* bm, const int64_t* seqs, int32_t num,
                                     int32_t num_kv_heads, int32_t num_workgroups, int32_t schedule,
                                     int32_t first_blocks, void* buffer, size_t capacity,
                                     pa_decode_step_layout* layout);
+
+/* Plan reuse for pa_bm_prepare_decode_step, for serving loops whose batch
+ * stays the same from step to step: with max_advances > 0 the manager keeps
+ * the plan it built last, and the next calls for the same batch (same
+ * sequences in the same order, heads, grid and schedule) advance it to the
+ * new lengths (pa_decode_plan_advance) instead of building one, at most
+ * max_advances times in a row; then, or when the plan cannot follow, a new
+ * one is built.  A plan covers exactly its lengths either way; an advanced
+ * one keeps the last build's placement, so its balance drifts a tile or so
+ * per 16 steps.  0 (the default) builds every step.  PA_ERR_INVALID for a
+ * negative count. */
+pa_status pa_bm_set_plan_reuse(pa_bm* bm, int32_t max_advances);
 
 /* Verify that each block's count equals the number of tables naming it, that
  * no named block is on the free list, that no block is lost, and that every

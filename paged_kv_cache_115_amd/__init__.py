@@ -240,6 +240,21 @@ class DecodePlan:
         _check(lib.pa_decode_plan_check_lens(ctypes.byref(self.info), lens.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
                                              lens.size), "pa_decode_plan_check_lens")
 
+    def advance(self, context_lens, max_job_tiles: int = 0) -> bool:
+        """pa_decode_plan_advance: carry this plan (in place) to the next
+        step's lengths.  False, with the plan unchanged, when it cannot follow
+        them (build a new plan then); the first-tile entries are dropped."""
+        lens = _host_i32(context_lens).reshape(-1)
+        if not self.blob.flags.writeable:
+            raise ValueError("plan bytes are read-only")
+        st = lib.pa_decode_plan_advance(ctypes.c_void_p(self.blob.ctypes.data), ctypes.byref(self.info),
+                                        lens.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), lens.size,
+                                        int(max_job_tiles))
+        if st == PA_REPLAN:
+            return False
+        _check(st, "pa_decode_plan_advance")
+        return True
+
     def to_device(self, device="cuda"):
         import torch
         return torch.from_numpy(self.blob.copy()).to(device)
@@ -259,6 +274,7 @@ def default_workgroups() -> int:
 
 
 SCHEDULE_AUTO, SCHEDULE_CHUNKS, SCHEDULE_LPT = -1, 0, 1
+PA_REPLAN = 1  # pa_decode_plan_advance: build a new plan
 
 
 def _piece_cap(max_piece_tiles: int, block_size: int | None) -> int:
@@ -574,6 +590,12 @@ class BlockManager:
                "pa_bm_prepare_decode_step")
         plan = DecodePlan(arr[lay.plan_at:lay.plan_at + lay.plan.bytes], PaDecodePlanInfo.from_buffer_copy(lay.plan))
         return lay, plan
+
+    def set_plan_reuse(self, max_advances: int) -> None:
+        """pa_bm_set_plan_reuse: let prepare_decode_step advance its last plan
+        (pa_decode_plan_advance) up to max_advances steps in a row; 0 builds
+        every step."""
+        _check(lib.pa_bm_set_plan_reuse(self._h, int(max_advances)), "pa_bm_set_plan_reuse")
 
     def length(self, seq: int) -> int:
         n = lib.pa_bm_len(self._h, seq)

@@ -1084,6 +1084,63 @@ extern "C" pa_status pa_decode_plan_check_lens(const pa_decode_plan_info* info, 
   return PA_OK;
 }
 
+extern "C" pa_status pa_decode_plan_advance(void* plan, pa_decode_plan_info* info, const int32_t* context_lens,
+                                            int32_t num_seqs, int32_t max_job_tiles) {
+  const char* who = "pa_decode_plan_advance";
+  if (!plan || !info || num_seqs < 0 || (num_seqs > 0 && !context_lens) || max_job_tiles < 0)
+    return fail(PA_ERR_INVALID, "%s: bad arguments", who);
+  if (num_seqs != info->num_seqs)
+    return fail(PA_ERR_INVALID, "%s: the plan is for %d sequences, not %d", who, info->num_seqs, num_seqs);
+  if (info->num_groups != 0) return PA_REPLAN;
+  const int32_t cap = max_job_tiles > 0 ? std::min(max_job_tiles, 64) : 64;
+  const int64_t slots = (int64_t)info->jobs_per_workgroup * info->num_workgroups;
+  if (slots < 0 || info->jobs_at < 0 || (int64_t)info->jobs_at + slots * (int64_t)sizeof(pa_decode_job) > info->bytes)
+    return fail(PA_ERR_INVALID, "%s: inconsistent plan info", who);
+  pa_decode_job* jobs = reinterpret_cast<pa_decode_job*>(static_cast<char*>(plan) + info->jobs_at);
+  // Tiles each sequence's jobs cover now (the end of its last piece).
+  std::vector<int32_t> end(num_seqs, 0);
+  for (int64_t i = 0; i < slots; ++i) {
+    const pa_decode_job& j = jobs[i];
+    if (j.tile_count <= 0) continue;
+    if (j.seq < 0 || j.seq >= num_seqs || j.tile_begin < 0)
+      return fail(PA_ERR_INVALID, "%s: job slot %lld names sequence %d", who, (long long)i, j.seq);
+    end[j.seq] = std::max(end[j.seq], j.tile_begin + j.tile_count);
+  }
+  int32_t max_len = 0;
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    const int32_t L = context_lens[s];
+    if (L < 0) return fail(PA_ERR_INVALID, "%s: context_lens[%d] < 0", who, s);
+    const int32_t tiles = (L + 15) / 16;
+    if (tiles != end[s] && (tiles != end[s] + 1 || end[s] == 0)) return PA_REPLAN;
+    max_len = std::max(max_len, L);
+  }
+  for (int64_t i = 0; i < slots; ++i) {
+    const pa_decode_job& j = jobs[i];
+    if (j.tile_count > 0 && (context_lens[j.seq] + 15) / 16 > end[j.seq] && j.tile_begin + j.tile_count == end[j.seq] &&
+        j.tile_count + 1 > cap)
+      return PA_REPLAN;
+  }
+  // Apply: new lengths, the last pieces of grown sequences one tile longer.
+  int64_t tiles = 0;
+  int32_t longest = 0;
+  for (int64_t i = 0; i < slots; ++i) {
+    pa_decode_job& j = jobs[i];
+    if (j.tile_count <= 0) continue;
+    const int32_t L = context_lens[j.seq];
+    if ((L + 15) / 16 > end[j.seq] && j.tile_begin + j.tile_count == end[j.seq]) j.tile_count += 1;
+    j.context_len = L;
+    tiles += j.tile_count;
+    longest = std::max(longest, j.tile_count);
+  }
+  info->num_tiles = (int32_t)tiles;
+  info->max_job_tiles = longest;
+  info->max_context_len = max_len;
+  info->lens_digest = pagedkv::lens_digest(context_lens, num_seqs);
+  info->flags &= ~PA_DECODE_FIRST_BLOCKS;
+  info->first_block_size = 0;
+  return PA_OK;
+}
+
 extern "C" size_t pa_decode_workspace_bytes(const pa_decode_plan_info* info, int32_t num_q_heads,
                                             int32_t head_dim) {
   if (!info || info->num_records <= 0 || num_q_heads <= 0 || head_dim <= 0 || info->num_kv_heads <= 0) return 0;

@@ -47,11 +47,15 @@
 using pagedkv::fail;
 
 struct pa_bm {
+  pagedkv::StepPlanCache plan_cache;  // pa_bm_prepare_decode_step's plan reuse
   struct Seq {
     std::vector<int32_t> table;     // host-pool blocks while swapped
     int32_t len = 0;
     bool swapped = false;
+    uint64_t stamp = 0;             // batch calls: the call that last listed the sequence
   };
+  uint64_t stamp_now = 0;           // batch calls: stamp of the current call
+  std::vector<Seq*> step_seqs;      // pa_bm_prepare_decode_step: the batch, resolved once
   // One pool of blocks: free list and counts.
   struct Pool {
     std::vector<int32_t> free_stack;  // back() is handed out next
@@ -213,7 +217,9 @@ struct pa_bm {
 
   // Append without a capacity check; writes slots and at most one CoW pair.
   void append_unchecked(int64_t id, int32_t n_new, int64_t* slots, int32_t* cow, int32_t* n_cow) {
-    Seq& s = seqs[id];
+    append_unchecked(seqs[id], n_new, slots, cow, n_cow);
+  }
+  void append_unchecked(Seq& s, int32_t n_new, int64_t* slots, int32_t* cow, int32_t* n_cow) {
     const int32_t B = block_size;
     if (n_new > 0 && s.len % B != 0 && dev.refcount[s.table.back()] > 1) {
       const int32_t src = s.table.back();
@@ -270,6 +276,15 @@ extern "C" pa_bm* pa_bm_create(int32_t num_blocks, int32_t block_size, const int
 
 extern "C" void pa_bm_destroy(pa_bm* bm) { delete bm; }
 
+pagedkv::StepPlanCache& pagedkv::step_plan_cache(pa_bm* bm) { return bm->plan_cache; }
+
+extern "C" pa_status pa_bm_set_plan_reuse(pa_bm* bm, int32_t max_advances) {
+  if (!bm || max_advances < 0) return fail(PA_ERR_INVALID, "pa_bm_set_plan_reuse: bad arguments");
+  bm->plan_cache.max_advances = max_advances;
+  bm->plan_cache.valid = false;
+  return PA_OK;
+}
+
 extern "C" pa_status pa_bm_append(pa_bm* bm, int64_t seq, int32_t n_new, int64_t* slots_out,
                                   int32_t* cow_pairs_out, int32_t* n_cow_out) {
   if (!bm || n_new < 0 || (n_new > 0 && !slots_out) || !n_cow_out)
@@ -292,33 +307,89 @@ extern "C" pa_status pa_bm_append(pa_bm* bm, int64_t seq, int32_t n_new, int64_t
   return PA_OK;
 }
 
+// One token for each of `num` sequences, resolved in `ptr` (null: a new
+// sequence); all or nothing.  Listed sequences are stamped with a fresh stamp
+// to find repeats in one pass (a repeat among new sequences is found by a
+// sort, only when there are new ones).
+static pa_status append_batch(pa_bm* bm, const int64_t* seqs, int32_t num, pa_bm::Seq* const* ptr, int64_t* slots_out,
+                              int32_t* cow_pairs_out, int32_t* n_cow_out, const char* who) {
+  *n_cow_out = 0;
+  const uint64_t stamp = ++bm->stamp_now;
+  int32_t fresh = 0;
+  for (int32_t i = 0; i < num; ++i) {
+    pa_bm::Seq* s = ptr[i];
+    if (!s) {
+      fresh += 1;
+      continue;
+    }
+    if (s->swapped) return fail(PA_ERR_INVALID, "%s: sequence %lld is swapped out", who, (long long)seqs[i]);
+    if (s->stamp == stamp) return fail(PA_ERR_INVALID, "%s: a sequence is listed twice", who);
+    s->stamp = stamp;
+  }
+  if (fresh > 1) {
+    std::vector<int64_t> ids;
+    ids.reserve(fresh);
+    for (int32_t i = 0; i < num; ++i)
+      if (!ptr[i]) ids.push_back(seqs[i]);
+    std::sort(ids.begin(), ids.end());
+    if (std::adjacent_find(ids.begin(), ids.end()) != ids.end())
+      return fail(PA_ERR_INVALID, "%s: a sequence is listed twice", who);
+  }
+  std::unordered_map<int32_t, int32_t> delta;
+  int64_t need = 0;
+  for (int32_t i = 0; i < num; ++i) need += bm->needs(ptr[i], 1, delta);
+  if (need > bm->capacity()) {
+    bm->alloc_failures += 1;
+    return fail(PA_ERR_OOM, "%s: step needs %lld blocks, %lld free", who, (long long)need,
+                (long long)bm->capacity());
+  }
+  for (int32_t i = 0; i < num; ++i) {
+    if (ptr[i])
+      bm->append_unchecked(*ptr[i], 1, slots_out + i, cow_pairs_out, n_cow_out);
+    else
+      bm->append_unchecked(seqs[i], 1, slots_out + i, cow_pairs_out, n_cow_out);
+  }
+  return PA_OK;
+}
+
 extern "C" pa_status pa_bm_append_step(pa_bm* bm, const int64_t* seqs, int32_t num, int64_t* slots_out,
                                        int32_t* cow_pairs_out, int32_t* n_cow_out) {
   if (!bm || num < 0 || (num > 0 && (!seqs || !slots_out || !cow_pairs_out)) || !n_cow_out)
     return fail(PA_ERR_INVALID, "pa_bm_append_step: bad arguments");
-  *n_cow_out = 0;
-  std::vector<int64_t> sorted(seqs, seqs + num);
-  std::sort(sorted.begin(), sorted.end());
-  if (std::adjacent_find(sorted.begin(), sorted.end()) != sorted.end())
-    return fail(PA_ERR_INVALID, "pa_bm_append_step: a sequence is listed twice");
-  std::unordered_map<int32_t, int32_t> delta;
-  int64_t need = 0;
+  std::vector<pa_bm::Seq*> ptr(num);
   for (int32_t i = 0; i < num; ++i) {
     auto it = bm->seqs.find(seqs[i]);
-    if (it != bm->seqs.end() && it->second.swapped)
-      return fail(PA_ERR_INVALID, "pa_bm_append_step: sequence %lld is swapped out", (long long)seqs[i]);
+    ptr[i] = it == bm->seqs.end() ? nullptr : &it->second;
   }
+  return append_batch(bm, seqs, num, ptr.data(), slots_out, cow_pairs_out, n_cow_out, "pa_bm_append_step");
+}
+
+pa_status pagedkv::bm_step_resolve(pa_bm* bm, const int64_t* seqs, int32_t num, int32_t* lens, const char* who) {
+  bm->step_seqs.assign(num, nullptr);
   for (int32_t i = 0; i < num; ++i) {
     auto it = bm->seqs.find(seqs[i]);
-    need += bm->needs(it == bm->seqs.end() ? nullptr : &it->second, 1, delta);
+    if (it == bm->seqs.end()) return fail(PA_ERR_NOT_FOUND, "%s: unknown sequence %lld", who, (long long)seqs[i]);
+    if (it->second.swapped) return fail(PA_ERR_INVALID, "%s: sequence %lld is swapped out", who, (long long)seqs[i]);
+    bm->step_seqs[i] = &it->second;
+    lens[i] = it->second.len;
   }
-  if (need > bm->capacity()) {
-    bm->alloc_failures += 1;
-    return fail(PA_ERR_OOM, "pa_bm_append_step: step needs %lld blocks, %lld free", (long long)need,
-                (long long)bm->capacity());
+  return PA_OK;
+}
+
+pa_status pagedkv::bm_step_append(pa_bm* bm, const int64_t* seqs, int32_t num, int64_t* slots, int32_t* cows,
+                                  int32_t* n_cows, const char* who) {
+  if ((int32_t)bm->step_seqs.size() != num) return fail(PA_ERR_INVALID, "%s: batch not resolved", who);
+  return append_batch(bm, seqs, num, bm->step_seqs.data(), slots, cows, n_cows, who);
+}
+
+pa_status pagedkv::bm_step_tables(pa_bm* bm, int32_t num, int32_t* tables, int32_t max_blocks, const char* who) {
+  if ((int32_t)bm->step_seqs.size() != num) return fail(PA_ERR_INVALID, "%s: batch not resolved", who);
+  for (int32_t i = 0; i < num; ++i) {
+    const std::vector<int32_t>& t = bm->step_seqs[i]->table;
+    if ((int64_t)t.size() > max_blocks)
+      return fail(PA_ERR_INVALID, "%s: a sequence holds %zu blocks, rows hold %d", who, t.size(), max_blocks);
+    if (!t.empty()) std::memcpy(tables + (int64_t)i * max_blocks, t.data(), sizeof(int32_t) * t.size());
   }
-  for (int32_t i = 0; i < num; ++i)
-    bm->append_unchecked(seqs[i], 1, slots_out + i, cow_pairs_out, n_cow_out);
   return PA_OK;
 }
 

@@ -1,9 +1,35 @@
 // Internal helpers shared by the translation units of libpagedkv.
 #pragma once
 
+#include <vector>
+
 #include "pagedkv.h"
 
 namespace pagedkv {
+
+// The plan pa_bm_prepare_decode_step built or advanced last (per block
+// manager), kept so that the next step can advance it instead of building a
+// new one (pa_bm_set_plan_reuse).
+struct StepPlanCache {
+  std::vector<char> plan;        // plan bytes
+  pa_decode_plan_info info{};    // its info (first-tile entries not kept)
+  std::vector<int64_t> seqs;     // the batch it is for, in order
+  int32_t num_kv_heads = 0, num_workgroups = 0, schedule = 0, max_piece = 0;
+  int32_t advances = 0;          // steps advanced since it was built
+  int32_t max_advances = 0;      // 0: build every step
+  bool valid = false;
+};
+StepPlanCache& step_plan_cache(pa_bm* bm);
+
+// pa_bm_prepare_decode_step's view of the block manager, one lookup per
+// sequence: resolve the batch (every sequence known and resident) and read
+// its lengths; then append one token to each (all or nothing, as
+// pa_bm_append_step); then copy the table rows (the first table-size entries
+// of each row of `tables`, int32 [num][max_blocks]).
+pa_status bm_step_resolve(pa_bm* bm, const int64_t* seqs, int32_t num, int32_t* lens, const char* who);
+pa_status bm_step_append(pa_bm* bm, const int64_t* seqs, int32_t num, int64_t* slots, int32_t* cows,
+                         int32_t* n_cows, const char* who);
+pa_status bm_step_tables(pa_bm* bm, int32_t num, int32_t* tables, int32_t max_blocks, const char* who);
 
 // Record a printf-style message for pa_last_error() and return `st`.
 pa_status fail(pa_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));

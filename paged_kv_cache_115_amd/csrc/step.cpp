@@ -48,11 +48,8 @@ extern "C" pa_status pa_bm_prepare_decode_step(pa_bm* bm, const int64_t* seqs, i
   int32_t* lens = reinterpret_cast<int32_t*>(buf + lay.lens_at);
   // Lengths after this step's append; the plan is built for them first, so
   // that a buffer too small for it leaves the block manager unchanged.
-  for (int32_t i = 0; i < num; ++i) {
-    const int32_t L = pa_bm_len(bm, seqs[i]);
-    if (L < 0) return fail(PA_ERR_NOT_FOUND, "%s: unknown sequence %lld", who, (long long)seqs[i]);
-    lens[i] = L + 1;
-  }
+  if (pa_status st = pagedkv::bm_step_resolve(bm, seqs, num, lens, who)) return st;
+  for (int32_t i = 0; i < num; ++i) lens[i] += 1;
   const int32_t B = pa_bm_block_size(bm);
   for (int32_t i = 0; i < num; ++i)
     if ((int64_t)lens[i] > (int64_t)max_blocks * B)
@@ -61,27 +58,58 @@ extern "C" pa_status pa_bm_prepare_decode_step(pa_bm* bm, const int64_t* seqs, i
   pa_decode_plan_info info{};
   // Below 8 slots per block the bf16 kernel's jobs cover at most 8 * B tiles.
   const int32_t max_piece_tiles = B < 8 ? 8 * B : 0;
-  const pa_status ps = pa_decode_plan_schedule(lens, num, num_kv_heads, num_workgroups, max_piece_tiles, schedule,
-                                               buf + lay.plan_at, capacity - (size_t)lay.plan_at, &info);
-  if (ps != PA_OK) {
-    lay.bytes = lay.plan_at + info.bytes;
-    *layout = lay;
-    return ps;  // message left by the planner
+  // With plan reuse (pa_bm_set_plan_reuse), the last step's plan advances to
+  // these lengths when it can; otherwise a new one is built (and kept).
+  pagedkv::StepPlanCache& pc = pagedkv::step_plan_cache(bm);
+  const size_t plan_room = capacity - (size_t)lay.plan_at;
+  bool reused = false;
+  if (pc.max_advances > 0 && pc.valid && pc.advances < pc.max_advances && pc.num_kv_heads == num_kv_heads &&
+      pc.num_workgroups == num_workgroups && pc.schedule == schedule && pc.max_piece == max_piece_tiles &&
+      pc.seqs.size() == (size_t)num && std::equal(pc.seqs.begin(), pc.seqs.end(), seqs)) {
+    const pa_status as = pa_decode_plan_advance(pc.plan.data(), &pc.info, lens, num, max_piece_tiles);
+    if (as == PA_OK && (size_t)pc.info.bytes <= plan_room) {
+      std::memcpy(buf + lay.plan_at, pc.plan.data(), (size_t)pc.info.bytes);
+      info = pc.info;
+      pc.advances += 1;
+      reused = true;
+    } else if (as != PA_OK && as != PA_REPLAN) {
+      pc.valid = false;
+      return as;
+    }
+  }
+  if (!reused) {
+    pc.valid = false;
+    const pa_status ps = pa_decode_plan_schedule(lens, num, num_kv_heads, num_workgroups, max_piece_tiles, schedule,
+                                                 buf + lay.plan_at, plan_room, &info);
+    if (ps != PA_OK) {
+      lay.bytes = lay.plan_at + info.bytes;
+      *layout = lay;
+      return ps;  // message left by the planner
+    }
+    if (pc.max_advances > 0) {
+      pc.plan.assign(buf + lay.plan_at, buf + lay.plan_at + info.bytes);
+      pc.info = info;
+      pc.seqs.assign(seqs, seqs + num);
+      pc.num_kv_heads = num_kv_heads;
+      pc.num_workgroups = num_workgroups;
+      pc.schedule = schedule;
+      pc.max_piece = max_piece_tiles;
+      pc.advances = 0;
+      pc.valid = true;
+    }
   }
   // The append (all or nothing).
   int64_t* slots = reinterpret_cast<int64_t*>(buf + lay.slots_at);
   int32_t* cows = reinterpret_cast<int32_t*>(buf + lay.cows_at);
   int32_t n_cows = 0;
-  if (pa_status st = pa_bm_append_step(bm, seqs, num, slots, cows, &n_cows)) return st;
+  if (pa_status st = pagedkv::bm_step_append(bm, seqs, num, slots, cows, &n_cows, who)) {
+    pc.valid = false;
+    return st;
+  }
   // Table rows: only the first ceil(L / B) entries, the ones the kernels
   // read; the rest of each row keeps whatever the buffer held.
   int32_t* tables = reinterpret_cast<int32_t*>(buf + lay.tables_at);
-  for (int32_t i = 0; i < num; ++i) {
-    const int32_t n = pa_bm_table(bm, seqs[i], tables + (int64_t)i * max_blocks, max_blocks);
-    if (n < 0 || n > max_blocks)
-      return fail(PA_ERR_INVALID, "%s: sequence %lld holds %d blocks, rows hold %d", who, (long long)seqs[i], n,
-                  max_blocks);
-  }
+  if (pa_status st = pagedkv::bm_step_tables(bm, num, tables, max_blocks, who)) return st;
   if (first_blocks && info.num_jobs > 0) {
     if (pa_status st = pa_decode_plan_first_blocks(buf + lay.plan_at, &info, tables, max_blocks, num, B)) return st;
   }

@@ -297,6 +297,37 @@ def test_merge_of_many_pieces(pk, dt, d, cap, parts):
     assert_close(got["out"], ref["out"], dt, f"merge {parts} pieces {dt}")
 
 
+@pytest.mark.parametrize("b", [8, 16])
+@pytest.mark.parametrize("kind", ["lpt", "chunks"])
+def test_advanced_plan_matches_oracle(pk, b, kind):
+    """A plan built once and carried forward by pa_decode_plan_advance over
+    four steps of lengths growing by one (crossing tile and block boundaries
+    on the way) decodes like the oracle at every step."""
+    base = np.array([1, 15, 16, 17, 31, 32, 33, 100, 255, 256, 257, 700, 0, 2, 47], dtype=np.int32)
+    steps = 4
+    full = np.where(base > 0, base + steps, 0).astype(np.int32)
+    case = _edge_case(full, b, seed=91)
+    got = product_decode_step(pk, case)
+    ref = oracle_decode_step(case)
+    assert np.array_equal(got["tables"], ref["tables"])
+    sched = pk.SCHEDULE_LPT if kind == "lpt" else pk.SCHEDULE_CHUNKS
+    plan = pk.decode_plan(base, 8, 16, 3, schedule=sched, block_size=b)
+    hq, d = case["cfg"]["num_q_heads"], case["cfg"]["head_dim"]
+    ws = torch.full((max(pk.decode_workspace_bytes(plan, hq, d), 256) // 4,), float("nan"), device="cuda")
+    for k in range(steps + 1):
+        lens = np.where(base > 0, base + k, 0).astype(np.int32)
+        if k:
+            assert plan.advance(lens)
+        plan.check_lens(lens)
+        log(f"advanced plan {kind} B={b} step {k}: {plan.num_jobs} jobs, {plan.info.num_tiles} tiles")
+        out = torch.full((len(base), hq, d), float("nan"), device="cuda")
+        pk.decode(got["pool"], got["q_dev"], to_dev(got["tables"]), to_dev(lens), case["scale"], plan,
+                  plan.to_device(), ws, out=out)
+        torch.cuda.synchronize()
+        expect = oracle.decode_attention(case["q"], ref["kpool"], ref["vpool"], ref["tables"], lens, case["scale"])
+        assert_close(to_host(out), expect, "bf16", f"advanced plan {kind} B={b} step {k}")
+
+
 @pytest.mark.parametrize("b", [1, 2, 4, 8, 16, 32])
 def test_edge_lengths(pk, b):
     """Empty contexts, one token, exact block/tile multiples and one past
