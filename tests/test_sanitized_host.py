@@ -20,7 +20,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HOST_TESTS = ["tests/test_host_library.py", "tests/test_boundary_checks.py", "tests/test_step_prepare.py",
-              "tests/test_zz_no_alloc.py"]
+              "tests/test_plan_advance.py", "tests/test_zz_no_alloc.py"]
 
 
 def _runtime(name: str):
