@@ -165,8 +165,9 @@ pa_status pa_swap_blocks(const pa_kv_pool* device_pool, const pa_kv_pool* host_p
  * the one whose busiest workgroup costs less: equal-work chunks of the
  * streams laid end to end, cut at tile boundaries (PA_SCHEDULE_CHUNKS), or
  * pieces of at most a workgroup's share placed largest first on the least
- * loaded compute unit, i.e. pair of workgroups {b, b + nwg/2}
- * (PA_SCHEDULE_LPT).  The four waves of a workgroup take the four KV heads
+ * loaded compute unit, i.e. pair of workgroups {b, b + nwg/2}, each
+ * workgroup then running its pieces smallest first (PA_SCHEDULE_LPT).  The
+ * four waves of a workgroup take the four KV heads
  * of each job, so the head slices of a slot row are read together.  A stream
  * cut into several pieces leaves one (max, sum, accumulator) record per
  * piece and KV head in the workspace; a second launch on the same stream
@@ -303,7 +304,8 @@ pa_status pa_decode_plan(const int32_t* context_lens, int32_t num_seqs, int32_t 
  * PA_SCHEDULE_LPT: each sequence is cut into near-equal pieces of at most
  *   max_piece_tiles tiles (0: the average tiles per workgroup, clamped to
  *   [4, 64]); one job per (piece, head block); jobs, largest first, go to the
- *   least-loaded workgroup.  Fewer jobs, coarser balance.
+ *   least-loaded compute unit (pair of workgroups), and each workgroup runs
+ *   its jobs smallest first.  Fewer jobs, coarser balance.
  * Automatic choice: the schedule whose busiest workgroup costs less, with a
  * job charged as 56 tokens (calibrated on MI355X), the chunks on a tie. */
 pa_status pa_decode_plan_schedule(const int32_t* context_lens, int32_t num_seqs, int32_t num_kv_heads,

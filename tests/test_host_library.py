@@ -459,7 +459,8 @@ def _lpt_model(lens, hkv, nwg, cap):
     the least-loaded pair of workgroups {b, b + nwg/2} for an even grid, or
     the least-loaded workgroup for an odd one (ties: the one that reached that
     load first, initially by index), and within a pair to the lighter member
-    (ties: b).  Returns (jobs per workgroup, merge rows, records)."""
+    (ties: b); a workgroup runs its jobs smallest first.  Returns (jobs per
+    workgroup, merge rows, records)."""
     import heapq
     lens = [int(x) for x in lens]
     hb = -(-hkv // 4)
@@ -498,7 +499,8 @@ def _lpt_model(lens, hkv, nwg, cap):
         wg_load[w] += jobs[i][2]
         heapq.heappush(heap, (load + jobs[i][2], arrival, b))
         arrival += 1
-    return [[jobs[i] for i in sorted(l)] for l in wg_jobs], merges, records
+    # Each workgroup runs its jobs smallest first, ties in generation order.
+    return [[jobs[i] for i in sorted(l, key=lambda i: (jobs[i][2], i))] for l in wg_jobs], merges, records
 
 
 def _plan_lists(plan):
