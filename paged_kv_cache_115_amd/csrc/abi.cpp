@@ -1296,7 +1296,32 @@ pa_status decode_stages(int stages, const char* who, const pa_kv_pool* pool, con
   constexpr int64_t kShortSequenceTiles = 24;
   const int64_t seq_streams = (int64_t)num_seqs * ((hkv + 3) / 4);
   const bool short_seqs = (int64_t)info->num_tiles < kShortSequenceTiles * seq_streams;
-  a.fused_loads = new_key == nullptr ? 0 : (short_seqs || group < 4 || pool->block_size < 8) ? 2 : 1;
+  // Mode 4, where per-lane addresses win: when each pool and its new rows
+  // lie within one 4 GiB window, every tile is read by buffer loads at
+  // 32-bit lane offsets in that window (the streaming cache policy kept, and
+  // less lane arithmetic than 64-bit addresses): C3 39.65 against 39.85 us.
+  bool windows = false;
+  if (new_key != nullptr && pool->block_size >= 16) {
+    const uint64_t pool_bytes = (uint64_t)pool->num_blocks * (uint64_t)pagedkv::pool_block_bytes(*pool);
+    const uint64_t new_bytes = (uint64_t)num_seqs * hkv * pool->head_dim * 2;
+    auto window = [&](const void* p, const void* n, const void** base, uint32_t* bytes, uint32_t* off,
+                      uint32_t* noff) {
+      const uint64_t a0 = (uint64_t)(uintptr_t)p, b0 = (uint64_t)(uintptr_t)n;
+      const uint64_t lo = std::min(a0, b0), hi = std::max(a0 + pool_bytes, b0 + new_bytes);
+      if (hi - lo >= 0xffff0000ull) return false;
+      *base = reinterpret_cast<const void*>((uintptr_t)lo);
+      *bytes = (uint32_t)(hi - lo);
+      *off = (uint32_t)(a0 - lo);
+      *noff = (uint32_t)(b0 - lo);
+      return true;
+    };
+    windows = window(pool->k, new_key, &a.k_win, &a.k_win_bytes, &a.k_off, &a.nk_off) &&
+              window(pool->v, new_value, &a.v_win, &a.v_win_bytes, &a.v_off, &a.nv_off);
+  }
+  a.fused_loads = new_key == nullptr                                        ? 0
+                  : !(short_seqs || group < 4 || pool->block_size < 8)      ? 1
+                  : windows                                                 ? 4
+                                                                            : 2;
   if (stages & kStageAttention) {
     if (pa_status st = pagedkv::hip_status(pagedkv::launch_decode_attention(a, (hipStream_t)stream), who)) return st;
   }

@@ -334,20 +334,40 @@ __device__ __forceinline__ void load_bf16_tile(const DecodeArgs& a, int32_t g, i
     return;
   }
   const int32_t p0 = clamp_block(e0, a.num_blocks);
-  // With the append fused (kFused 1 or 2), row r_new of the tile holding the
-  // appended token and the rows after it (past the context; masked in
+  // With the append fused (kFused 1, 2 or 4), row r_new of the tile holding
+  // the appended token and the rows after it (past the context; masked in
   // compute) come from the new key/value row, the rows before it from the
   // pool, through per-lane addresses.  kFused 1 loads only that tile so, on a
   // path of its own; kFused 2 loads every tile so (a filler load, rows 0,
   // reads the new row, which stays in L2): one load path, and no wait for
   // the loads in flight where two paths would join, at the price of the
-  // buffer loads' cache policy.
+  // buffer loads' cache policy.  kFused 4 is kFused 2 with buffer loads: the
+  // host found a 4 GiB window holding both the pool and the new rows, so
+  // every lane's row is a 32-bit offset in one buffer resource per pool.
   const int32_t p1f = B == 8 && rows > 8 ? clamp_block(e1, a.num_blocks) : p0;
   auto row_addr = [&](const char* base, int32_t row) {
     if (B == 8) return base + (int64_t)(row < 8 ? p0 : p1f) * blk_bytes + (row & 7) * row_bytes;
     return base + (int64_t)p0 * blk_bytes + ((int64_t)((t0 + t) % kTilesPerBlock) * kTile + row) * row_bytes;
   };
-  if (kFused == 2 || (kFused == 1 && r_new >= 0)) {
+  if (kFused == 4 && B >= kTile) {
+    // Per-lane offsets into one buffer window per pool, which also holds the
+    // new rows: buffer loads with the streaming cache policy, and 32-bit
+    // lane arithmetic.
+    const int32_t first_new = r_new >= 0 ? r_new : rows <= 0 ? 0 : kTile;
+    const uint32_t tile_rel = (uint32_t)((int64_t)g * D * 2 + (int64_t)p0 * blk_bytes +
+                                         (int64_t)((t0 + t) % kTilesPerBlock) * kTile * row_bytes);
+    const uint32_t new_rel = (uint32_t)(nk - reinterpret_cast<const char*>(a.new_k)) + 16 * li;
+    const uint32_t lane_rel = 4 * lq * row_bytes + 16 * li;
+    const __amdgpu_buffer_rsrc_t kr = tile_rsrc(reinterpret_cast<const char*>(a.k_win), (int32_t)a.k_win_bytes);
+    const __amdgpu_buffer_rsrc_t vr = tile_rsrc(reinterpret_cast<const char*>(a.v_win), (int32_t)a.v_win_bytes);
+    const uint32_t kt_off = a.k_off + tile_rel, vt_off = a.v_off + tile_rel;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      kf[r] = load_b128<kStream>(kr, 4 * lq + r >= first_new ? a.nk_off + new_rel : kt_off + lane_rel + r * row_bytes, 0);
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      vf[r] = load_b128<kStream>(vr, 4 * lq + r >= first_new ? a.nv_off + new_rel : vt_off + lane_rel + r * row_bytes, 0);
+  } else if (kFused == 2 || (kFused == 1 && r_new >= 0)) {
     const int32_t first_new = r_new >= 0 ? r_new : rows <= 0 ? 0 : kTile;
 #pragma unroll
     for (int r = 0; r < 4; ++r)
@@ -646,6 +666,7 @@ __device__ __forceinline__ void finish_bf16_job(const DecodeArgs& a, const JobVi
 template <int B, bool kStream, int kFused>
 __global__ __launch_bounds__(kNW * 64, kWavesPerSimd) void decode_bf16_kernel(DecodeArgs a) {
   static_assert(B == 1 || B == 2 || B == 4 || B == 8 || B == 16 || B == 32, "block size");
+  static_assert(kFused != 4 || B >= 16, "window loads read whole tiles of one block");
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: keeps job fields in SGPRs
   const int li = lane & 15;  // MFMA row / column within a 16-lane group
@@ -1123,6 +1144,8 @@ hipError_t launch_decode_attention(const DecodeArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((decode_bf16_kernel<BS, STREAM, 0>), grid, dim3(kNW * 64), 0, stream, a);        \
   else if (a.fused_loads == 2)                                                                          \
     hipLaunchKernelGGL((decode_bf16_kernel<BS, STREAM, 2>), grid, dim3(kNW * 64), 0, stream, a);        \
+  else if (a.fused_loads == 4 && BS >= 16)                                                              \
+    hipLaunchKernelGGL((decode_bf16_kernel<(BS >= 16 ? BS : 16), STREAM, 4>), grid, dim3(kNW * 64), 0, stream, a); \
   else                                                                                                  \
     hipLaunchKernelGGL((decode_bf16_kernel<BS, STREAM, 1>), grid, dim3(kNW * 64), 0, stream, a);
 #define PA_BF16_CASE(BS)                                                                                \

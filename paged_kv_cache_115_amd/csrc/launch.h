@@ -45,7 +45,13 @@ struct DecodeArgs {
   int32_t shared_kv;             // 1: sequences share blocks (keep K/V cached), 0: stream K/V
   int32_t out_bf16;              // 1: write bfloat16, 0: float32
   int32_t fused_loads;           // with new_k: 1 a branch at the appended token's tile, 2 per-lane
-                                 // addresses for every tile (one load path)
+                                 // addresses for every tile (one load path), 4 per-lane offsets in
+                                 // one buffer window per pool (k_win / v_win) for every tile
+  const void* k_win;             // mode 4: window base below both the K pool and new_k
+  const void* v_win;
+  uint32_t k_win_bytes, v_win_bytes;
+  uint32_t k_off, v_off;         // the pools' offsets in their windows
+  uint32_t nk_off, nv_off;       // new_k's and new_v's offsets in their windows
   float scale_log2e;             // scale * log2(e)
 };
 
