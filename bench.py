@@ -704,17 +704,28 @@ def main() -> int:
 
     pool_bytes = 2 * nb * B * hkv * d * 2
     R = args.replicas or max(2, math.ceil(2**30 / pool_bytes))
+    # All replicas' K pools and the new K rows in one allocation, and the same
+    # for V, so that each pool and the new rows share one 4 GiB window (the
+    # fused append then reads every tile with buffer loads; the mode is
+    # reported in the config).
+    pool_elems, new_elems = nb * B * hkv * d, S * hkv * d
+    k_slab = torch.empty(R * pool_elems + new_elems, dtype=torch.bfloat16, device=dev)
+    v_slab = torch.empty(R * pool_elems + new_elems, dtype=torch.bfloat16, device=dev)
     pools = []
     for r in range(R):
         g = torch.Generator(device=dev)
         g.manual_seed(w["seed"] + 1000 * r)
-        kp = torch.randn((nb, B, hkv, d), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
-        vp = torch.randn((nb, B, hkv, d), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        kp = k_slab[r * pool_elems:(r + 1) * pool_elems].view(nb, B, hkv, d)
+        vp = v_slab[r * pool_elems:(r + 1) * pool_elems].view(nb, B, hkv, d)
+        kp.copy_(torch.randn((nb, B, hkv, d), generator=g, device=dev, dtype=torch.float32))
+        vp.copy_(torch.randn((nb, B, hkv, d), generator=g, device=dev, dtype=torch.float32))
         pools.append(pk.KvPool(kp, vp))
     g = torch.Generator(device=dev)
     g.manual_seed(w["seed"] + 7)
-    new_k = torch.randn((S, hkv, d), generator=g, device=dev).to(torch.bfloat16)
-    new_v = torch.randn((S, hkv, d), generator=g, device=dev).to(torch.bfloat16)
+    new_k = k_slab[R * pool_elems:].view(S, hkv, d)
+    new_v = v_slab[R * pool_elems:].view(S, hkv, d)
+    new_k.copy_(torch.randn((S, hkv, d), generator=g, device=dev))
+    new_v.copy_(torch.randn((S, hkv, d), generator=g, device=dev))
     out = torch.empty((S, hq, d), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
 
@@ -846,7 +857,8 @@ def main() -> int:
                    "schedule": ["chunks", "largest pieces first"][plan.schedule],
                    "cascade_prefix_groups": int(plan.num_groups) if cascade else 0,
                    "first_tile_entries": not args.no_first_blocks,
-                   "kv_loads": "cached" if plan.info.flags & pk.PA_DECODE_SHARED_KV else "streamed"},
+                   "kv_loads": "cached" if plan.info.flags & pk.PA_DECODE_SHARED_KV else "streamed",
+                   "fused_loads": pk.FUSED_LOADS[pk.decode_fused_loads(pools[0], new_k, new_v, plan, hq)]},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "decode_tokens_per_s": round(S / (ms_per_step * 1e-3), 1),
         "kv_bytes_per_step": kv_bytes,

@@ -374,6 +374,19 @@ pa_status pa_decode_plan_check_lens(const pa_decode_plan_info* info, const int32
 pa_status pa_decode_plan_advance(void* plan, pa_decode_plan_info* info, const int32_t* context_lens,
                                  int32_t num_seqs, int32_t max_job_tiles);
 
+/* How pa_decode, with these arguments, loads the tiles of its attention
+ * launch, for diagnostics and benchmark reports: 0 without new rows; with
+ * them (the append fused) 1 = the tile holding a sequence's new token on a
+ * path of its own (long contexts), 2 = every tile through per-lane 64-bit
+ * addresses, 4 = every tile by buffer loads at 32-bit offsets in a 4 GiB
+ * window holding the pool and the new rows (taken over 2 when both pools'
+ * windows fit: place the step's new rows within 4 GiB of the pools for it).
+ * Depends on the plan's tiles per sequence, the query heads per KV head, the
+ * block size and the addresses; reads no memory.  -1 (pa_last_error) for bad
+ * arguments. */
+int32_t pa_decode_fused_loads(const pa_kv_pool* pool, const void* new_key, const void* new_value, int32_t num_seqs,
+                              int32_t num_q_heads, const pa_decode_plan_info* info);
+
 /* Bytes of device workspace pa_decode needs for a plan (0 when no sequence is
  * cut).  The workspace needs no initialisation; it carries records from the
  * attention launch to the merge launch of one call, so calls that may overlap

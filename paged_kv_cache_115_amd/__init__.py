@@ -343,6 +343,21 @@ def decode_plan_prefix(context_lens, num_kv_heads: int, num_q_heads: int, prefix
     return DecodePlan(buf[: info.bytes].copy(), info)
 
 
+FUSED_LOADS = {0: "none (no fused append)", 1: "separate path for the appended token's tile",
+               2: "per-lane addresses for every tile", 4: "buffer loads in a window holding pool and new rows"}
+
+
+def decode_fused_loads(pool: KvPool, new_key, new_value, plan: DecodePlan, num_q_heads: int) -> int:
+    """pa_decode_fused_loads: how pa_decode loads tiles for these arguments
+    (see FUSED_LOADS); new_key/new_value are tensors or None."""
+    nk = ctypes.c_void_p(new_key.data_ptr()) if new_key is not None else None
+    nv = ctypes.c_void_p(new_value.data_ptr()) if new_value is not None else None
+    m = lib.pa_decode_fused_loads(ctypes.byref(pool.c), nk, nv, plan.info.num_seqs, num_q_heads, ctypes.byref(plan.info))
+    if m < 0:
+        _check(-1, "pa_decode_fused_loads")
+    return int(m)
+
+
 def decode_workspace_bytes(plan: DecodePlan, num_q_heads: int, head_dim: int) -> int:
     return int(lib.pa_decode_workspace_bytes(ctypes.byref(plan.info), num_q_heads, head_dim))
 

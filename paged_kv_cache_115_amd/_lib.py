@@ -102,6 +102,7 @@ SIGNATURES = {
     "pa_decode_workspace_bytes": (_sz, [ctypes.POINTER(PaDecodePlanInfo), _i32, _i32]),
     "pa_decode_plan_check_lens": (_i32, [ctypes.POINTER(PaDecodePlanInfo), _p32, _i32]),
     "pa_decode_plan_advance": (_i32, [_vp, ctypes.POINTER(PaDecodePlanInfo), _p32, _i32, _i32]),
+    "pa_decode_fused_loads": (_i32, [ctypes.POINTER(PaKvPool), _vp, _vp, _i32, _i32, ctypes.POINTER(PaDecodePlanInfo)]),
     "pa_bm_set_plan_reuse": (_i32, [_vp, _i32]),
     "pa_validate_slots": (_i32, [_p64, _i32, _i32, _i32]),
     "pa_validate_copy_pairs": (_i32, [_p32, _i32, _i32]),

@@ -1170,6 +1170,52 @@ namespace pagedkv {
 // Shared front of pa_decode, its two stages and pa_decode_noalloc:
 // validation, then the launches the stage mask selects.  `who` names the
 // entry point in errors.
+// How the attention launch loads tiles with the append fused (0 without
+// it); with `a`, also the windows mode 4 reads through.
+//
+// The tile holding a sequence's appended token mixes pool rows and the new
+// row.  Loading it on a path of its own (1) costs a wait for every load in
+// flight where the paths join, once per job that ends a sequence; loading
+// every tile through per-lane addresses (2) avoids that but loses the
+// streaming cache policy of buffer loads on every tile.  Measured on
+// MI355X: per-lane addresses everywhere are faster where sequences are short
+// (a job end every few tiles: batch 256, mean 200 tokens) and for one query
+// head per KV head (batch 64 of up to 2048 tokens, 3%); the separate path
+// is faster for long contexts with 4 or 8 query heads per KV head (16 x
+// 16-32k tokens, 3%; 2000-token shared prefixes, 2%).  Where per-lane
+// addresses win and each pool and its new rows lie within one 4 GiB window
+// (4), every tile is read by buffer loads at 32-bit lane offsets in that
+// window: the streaming cache policy is kept, with less lane arithmetic than
+// 64-bit addresses (C3 39.65 against 39.85 us).
+int32_t fused_mode(const pa_kv_pool* pool, const void* new_key, const void* new_value, int32_t num_seqs,
+                   int32_t group, const pa_decode_plan_info* info, DecodeArgs* a) {
+  if (new_key == nullptr) return 0;
+  constexpr int64_t kShortSequenceTiles = 24;
+  const int32_t hkv = pool->num_kv_heads;
+  const int64_t seq_streams = (int64_t)num_seqs * ((hkv + 3) / 4);
+  const bool short_seqs = (int64_t)info->num_tiles < kShortSequenceTiles * seq_streams;
+  if (!(short_seqs || group < 4 || pool->block_size < 8)) return 1;
+  if (pool->block_size < 16) return 2;
+  const uint64_t pool_bytes = (uint64_t)pool->num_blocks * (uint64_t)pool_block_bytes(*pool);
+  const uint64_t new_bytes = (uint64_t)num_seqs * hkv * pool->head_dim * 2;
+  DecodeArgs scratch{};
+  DecodeArgs& w = a ? *a : scratch;
+  auto window = [&](const void* p, const void* n, const void** base, uint32_t* bytes, uint32_t* off,
+                    uint32_t* noff) {
+    const uint64_t a0 = (uint64_t)(uintptr_t)p, b0 = (uint64_t)(uintptr_t)n;
+    const uint64_t lo = std::min(a0, b0), hi = std::max(a0 + pool_bytes, b0 + new_bytes);
+    if (hi - lo >= 0xffff0000ull) return false;
+    *base = reinterpret_cast<const void*>((uintptr_t)lo);
+    *bytes = (uint32_t)(hi - lo);
+    *off = (uint32_t)(a0 - lo);
+    *noff = (uint32_t)(b0 - lo);
+    return true;
+  };
+  const bool windows = window(pool->k, new_key, &w.k_win, &w.k_win_bytes, &w.k_off, &w.nk_off) &&
+                       window(pool->v, new_value, &w.v_win, &w.v_win_bytes, &w.v_off, &w.nv_off);
+  return windows ? 4 : 2;
+}
+
 pa_status decode_stages(int stages, const char* who, const pa_kv_pool* pool, const void* q, void* out,
                         int32_t out_dtype, const int32_t* block_tables, int32_t max_blocks_per_seq,
                         const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads, float scale,
@@ -1282,46 +1328,7 @@ pa_status decode_stages(int stages, const char* who, const pa_kv_pool* pool, con
   a.scale_log2e = scale * 1.4426950408889634f;
   a.bf16 = pool->dtype == PA_BF16;
   a.shared_kv = (info->flags & PA_DECODE_SHARED_KV) != 0;
-  // With the append fused, the tile holding a sequence's appended token
-  // mixes pool rows and the new row.  Loading it on a path of its own costs a
-  // wait for every load in flight where the paths join, once per job that
-  // ends a sequence; loading every tile through per-lane addresses avoids
-  // that but loses the streaming cache policy of buffer loads on every tile.
-  // Measured on MI355X: per-lane addresses everywhere are faster where
-  // sequences are short (a job end every few tiles: batch 256, mean 200
-  // tokens) and for one query head per KV head (batch 64 of up to 2048
-  // tokens, 3%); the separate path is faster for long contexts with 4 or 8
-  // query heads per KV head (16 x 16-32k tokens, 3%; 2000-token shared
-  // prefixes, 2%).
-  constexpr int64_t kShortSequenceTiles = 24;
-  const int64_t seq_streams = (int64_t)num_seqs * ((hkv + 3) / 4);
-  const bool short_seqs = (int64_t)info->num_tiles < kShortSequenceTiles * seq_streams;
-  // Mode 4, where per-lane addresses win: when each pool and its new rows
-  // lie within one 4 GiB window, every tile is read by buffer loads at
-  // 32-bit lane offsets in that window (the streaming cache policy kept, and
-  // less lane arithmetic than 64-bit addresses): C3 39.65 against 39.85 us.
-  bool windows = false;
-  if (new_key != nullptr && pool->block_size >= 16) {
-    const uint64_t pool_bytes = (uint64_t)pool->num_blocks * (uint64_t)pagedkv::pool_block_bytes(*pool);
-    const uint64_t new_bytes = (uint64_t)num_seqs * hkv * pool->head_dim * 2;
-    auto window = [&](const void* p, const void* n, const void** base, uint32_t* bytes, uint32_t* off,
-                      uint32_t* noff) {
-      const uint64_t a0 = (uint64_t)(uintptr_t)p, b0 = (uint64_t)(uintptr_t)n;
-      const uint64_t lo = std::min(a0, b0), hi = std::max(a0 + pool_bytes, b0 + new_bytes);
-      if (hi - lo >= 0xffff0000ull) return false;
-      *base = reinterpret_cast<const void*>((uintptr_t)lo);
-      *bytes = (uint32_t)(hi - lo);
-      *off = (uint32_t)(a0 - lo);
-      *noff = (uint32_t)(b0 - lo);
-      return true;
-    };
-    windows = window(pool->k, new_key, &a.k_win, &a.k_win_bytes, &a.k_off, &a.nk_off) &&
-              window(pool->v, new_value, &a.v_win, &a.v_win_bytes, &a.v_off, &a.nv_off);
-  }
-  a.fused_loads = new_key == nullptr                                        ? 0
-                  : !(short_seqs || group < 4 || pool->block_size < 8)      ? 1
-                  : windows                                                 ? 4
-                                                                            : 2;
+  a.fused_loads = fused_mode(pool, new_key, new_value, num_seqs, group, info, &a);
   if (stages & kStageAttention) {
     if (pa_status st = pagedkv::hip_status(pagedkv::launch_decode_attention(a, (hipStream_t)stream), who)) return st;
   }
@@ -1343,6 +1350,16 @@ using pagedkv::kStageMerge;
 #define PA_DECODE_PASS                                                                                   \
   pool, q, out, out_dtype, block_tables, max_blocks_per_seq, context_lens, num_seqs, num_q_heads, scale, \
       new_key, new_value, plan, info, workspace, workspace_bytes, stream
+
+extern "C" int32_t pa_decode_fused_loads(const pa_kv_pool* pool, const void* new_key, const void* new_value,
+                                         int32_t num_seqs, int32_t num_q_heads, const pa_decode_plan_info* info) {
+  if (!pool || !info || num_seqs < 0 || pool->num_kv_heads <= 0 || num_q_heads <= 0 ||
+      num_q_heads % pool->num_kv_heads != 0 || (new_key == nullptr) != (new_value == nullptr)) {
+    fail(PA_ERR_INVALID, "pa_decode_fused_loads: bad arguments");
+    return -1;
+  }
+  return pagedkv::fused_mode(pool, new_key, new_value, num_seqs, num_q_heads / pool->num_kv_heads, info, nullptr);
+}
 
 extern "C" pa_status pa_decode(PA_DECODE_ARGS) {
   return decode_stages(kStageAttention | kStageMerge, "pa_decode", PA_DECODE_PASS);

@@ -1,0 +1,59 @@
+"""How pa_decode loads tiles when the step's append is fused (CPU: the
+choice reads only sizes and addresses, so fake device addresses do).
+
+The tile holding a sequence's new token mixes pool rows and the new row
+(mercemay.com "Blocks, tables, and the indirection": the token written this
+step is the one attended last).  pa_decode_fused_loads reports the load path
+pa_decode takes: a path of its own for that tile on long contexts (1),
+per-lane addresses on every tile for short ones (2), or buffer loads in a
+4 GiB window holding a pool and its new rows when both windows fit (4)."""
+import ctypes
+
+import numpy as np
+import pytest
+
+import paged_kv_cache_115_amd as pk
+from paged_kv_cache_115_amd._lib import PaKvPool, lib
+
+GiB = 1 << 30
+
+
+def _mode(pool, nk, nv, plan, hq):
+    return lib.pa_decode_fused_loads(ctypes.byref(pool), ctypes.c_void_p(nk) if nk else None,
+                                     ctypes.c_void_p(nv) if nv else None, plan.info.num_seqs, hq,
+                                     ctypes.byref(plan.info))
+
+
+def _pool(base, nb, b, hkv=8, d=128):
+    per = nb * b * hkv * d * 2
+    return PaKvPool(base, base + per, nb, b, hkv, d, 1), per
+
+
+def test_fused_loads_choice():
+    rng = np.random.default_rng(3)
+    short = np.clip(np.rint(rng.lognormal(np.log(200) - 0.5, 1.0, 256)), 1, 4096).astype(np.int32)
+    long = rng.integers(16384, 32768, 16).astype(np.int32)
+    p_short = pk.decode_plan(short, 8, 512, 0)
+    p_long = pk.decode_plan(long, 8, 512, 0)
+    base = 1 << 44
+    pool, per = _pool(base, 5000, 16)
+    new_bytes = 256 * 8 * 128 * 2
+    near_k, near_v = base + 2 * per + (1 << 20), base + 2 * per + (1 << 20) + new_bytes
+    assert _mode(pool, 0, 0, p_short, 32) == 0
+    assert _mode(pool, near_k, near_v, p_short, 32) == 4
+    # new rows below the pools work as well
+    assert _mode(pool, base - (1 << 24), base - (1 << 24) + new_bytes, p_short, 32) == 4
+    # one pool out of reach: per-lane addresses
+    assert _mode(pool, near_k, base + 8 * GiB, p_short, 32) == 2
+    assert _mode(pool, base + 6 * GiB, base + 6 * GiB + new_bytes, p_short, 32) == 2
+    # long contexts with 4 query heads per KV head: the separate path
+    assert _mode(pool, near_k, near_v, p_long, 32) == 1
+    # one query head per KV head: per-lane loads even for long contexts
+    assert _mode(pool, near_k, near_v, p_long, 8) == 4
+    # 8-slot blocks: the window loads read whole 16-row tiles of one block
+    pool8, per8 = _pool(base, 10000, 8)
+    assert _mode(pool8, base + 2 * per8, base + 2 * per8 + new_bytes, p_short, 32) == 2
+    # bad arguments
+    assert _mode(pool, near_k, 0, p_short, 32) == -1
+    assert _mode(pool, near_k, near_v, p_short, 30) == -1
+
