@@ -352,8 +352,12 @@ __device__ __forceinline__ void load_bf16_tile(const DecodeArgs& a, int32_t g, i
   if (kFused == 4 && B >= kTile) {
     // Per-lane offsets into one buffer window per pool, which also holds the
     // new rows: buffer loads with the streaming cache policy, and 32-bit
-    // lane arithmetic.
-    const int32_t first_new = r_new >= 0 ? r_new : rows <= 0 ? 0 : kTile;
+    // lane arithmetic.  Rows before the appended one (or before `rows`) come
+    // from the pool, the appended row from the new rows, and rows past the
+    // context take an offset past every window: such a load returns zeros
+    // and reads nothing, as in the tile resource of the unfused path.
+    constexpr uint32_t kPastWindow = 0xffff0000u;  // windows are shorter (checked on the host)
+    const int32_t lim = r_new >= 0 ? r_new : min(max(rows, 0), kTile);
     const uint32_t tile_rel = (uint32_t)((int64_t)g * D * 2 + (int64_t)p0 * blk_bytes +
                                          (int64_t)((t0 + t) % kTilesPerBlock) * kTile * row_bytes);
     const uint32_t new_rel = (uint32_t)(nk - reinterpret_cast<const char*>(a.new_k)) + 16 * li;
@@ -362,11 +366,17 @@ __device__ __forceinline__ void load_bf16_tile(const DecodeArgs& a, int32_t g, i
     const __amdgpu_buffer_rsrc_t vr = tile_rsrc(reinterpret_cast<const char*>(a.v_win), (int32_t)a.v_win_bytes);
     const uint32_t kt_off = a.k_off + tile_rel, vt_off = a.v_off + tile_rel;
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      kf[r] = load_b128<kStream>(kr, 4 * lq + r >= first_new ? a.nk_off + new_rel : kt_off + lane_rel + r * row_bytes, 0);
+    for (int r = 0; r < 4; ++r) {
+      const int row = 4 * lq + r;
+      kf[r] = load_b128<kStream>(
+          kr, row < lim ? kt_off + lane_rel + r * row_bytes : row == r_new ? a.nk_off + new_rel : kPastWindow, 0);
+    }
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      vf[r] = load_b128<kStream>(vr, 4 * lq + r >= first_new ? a.nv_off + new_rel : vt_off + lane_rel + r * row_bytes, 0);
+    for (int r = 0; r < 4; ++r) {
+      const int row = 4 * lq + r;
+      vf[r] = load_b128<kStream>(
+          vr, row < lim ? vt_off + lane_rel + r * row_bytes : row == r_new ? a.nv_off + new_rel : kPastWindow, 0);
+    }
   } else if (kFused == 2 || (kFused == 1 && r_new >= 0)) {
     const int32_t first_new = r_new >= 0 ? r_new : rows <= 0 ? 0 : kTile;
 #pragma unroll
