@@ -459,8 +459,9 @@ def _lpt_model(lens, hkv, nwg, cap):
     the least-loaded pair of workgroups {b, b + nwg/2} for an even grid, or
     the least-loaded workgroup for an odd one (ties: the one that reached that
     load first, initially by index), and within a pair to the lighter member
-    (ties: b); a workgroup runs its jobs smallest first.  Returns (jobs per
-    workgroup, merge rows, records)."""
+    (ties: b), after which each pair's jobs are re-split by modelled end time;
+    a workgroup runs its jobs smallest first.  Returns (jobs per workgroup,
+    merge rows, records)."""
     import heapq
     lens = [int(x) for x in lens]
     hb = -(-hkv // 4)
@@ -499,6 +500,31 @@ def _lpt_model(lens, hkv, nwg, cap):
         wg_load[w] += jobs[i][2]
         heapq.heappush(heap, (load + jobs[i][2], arrival, b))
         arrival += 1
+    if nwg % 2 == 0:
+        # Each pair's jobs (up to 8) are then split over its two workgroups to
+        # minimise the modelled end time: b (dispatched first) streams 0.51
+        # tiles/us while both run, b + nwg/2 0.32, either alone 0.75, and each
+        # job costs 0.5 us; every subset for b, in mask order, first minimum.
+        for b in range(bins):
+            pj = sorted(wg_jobs[b] + wg_jobs[b + bins])
+            if not 2 <= len(pj) <= 8:
+                continue
+            best, best_m = float("inf"), 0
+            for m in range(1 << len(pj)):
+                older = float(sum(jobs[i][2] for k, i in enumerate(pj) if m >> k & 1))
+                younger = float(sum(jobs[i][2] for k, i in enumerate(pj) if not m >> k & 1))
+                jo = bin(m).count("1")
+                jy = len(pj) - jo
+                t_o = older / 0.51 + 0.5 * jo
+                t_y = younger / 0.32 + 0.5 * jy
+                if t_o <= t_y:
+                    e = t_o + max(0.0, younger - 0.32 * max(0.0, t_o - 0.5 * jy)) / 0.75
+                else:
+                    e = t_y + max(0.0, older - 0.51 * max(0.0, t_y - 0.5 * jo)) / 0.75
+                if e < best:
+                    best, best_m = e, m
+            wg_jobs[b] = [i for k, i in enumerate(pj) if best_m >> k & 1]
+            wg_jobs[b + bins] = [i for k, i in enumerate(pj) if not best_m >> k & 1]
     # Each workgroup runs its jobs smallest first, ties in generation order.
     return [[jobs[i] for i in sorted(l, key=lambda i: (jobs[i][2], i))] for l in wg_jobs], merges, records
 
@@ -553,13 +579,15 @@ def test_decode_plan_small_example_lpt():
         (2, 0, 19, 0, 0, 2, 0), (2, 0, 19, 1, 0, 2, 8), (2, 19, 19, 0, 1, 2, 0), (2, 19, 19, 1, 1, 2, 8),
         (3, 0, 32, 0, 0, 2, 16), (3, 0, 32, 1, 0, 2, 24), (3, 32, 31, 0, 1, 2, 16), (3, 32, 31, 1, 1, 2, 24)])
     loads = sorted(int(plan.job_table()[:, w, 2].sum()) for w in range(6))
-    assert loads == [32, 32, 32, 32, 38, 38]
-    # Placement by compute-unit pairs {0, 3}, {1, 4}, {2, 5}: 32 -> 0, 32 -> 1,
-    # 31 -> 2, 31 -> 5 (pair 2 is least loaded, 5 its lighter member), the four
-    # 19-tile jobs alternate over pairs 0 and 1 (to 3, 4, 3, 4), then the two
-    # 1-tile jobs go to pair 2 (to 2, then 5).
+    assert loads == [31, 32, 32, 33, 38, 38]
+    # Placement by compute-unit pairs {0, 3}, {1, 4}, {2, 5}: 32 -> pair 0,
+    # 32 -> pair 1, 31 and 31 -> pair 2, the four 19-tile jobs alternate over
+    # pairs 0 and 1, the two 1-tile jobs go to pair 2.  Each pair is then split
+    # by modelled end time, the first-dispatched member taking the larger
+    # share: pairs 0 and 1 give 19 + 19 to b and 32 to b + 3, pair 2 gives
+    # 31 + 1 + 1 to 2 and 31 to 5.
     per_wg = [int(plan.job_table()[:, w, 2].sum()) for w in range(6)]
-    assert per_wg == [32, 32, 32, 38, 38, 32]
+    assert per_wg == [38, 38, 33, 32, 32, 31]
     merges = [tuple(m) for m in plan.merges().tolist()]
     assert merges == ([(0, g, 0, -1) for g in range(8)] + [(2, g, 2, 2 * g) for g in range(8)] +
                       [(3, g, 2, 16 + 2 * g) for g in range(8)])
