@@ -53,6 +53,8 @@ HBM_PEAK_GBS = 8000.0
 WORKLOADS = {
     "c3": "GQA decode bf16: batch 256, 32 q heads / 8 KV heads, head_dim 128, block 16, "
           "lognormal lengths (mean ~200, cap 4096), shuffled blocks",
+    "c3f": "GQA decode fp32: batch 256, 32 q heads / 8 KV heads, head_dim 128, block 16, "
+           "lognormal lengths (mean ~200, cap 4096), shuffled blocks (the c3 batch in fp32)",
     "c2": "MHA decode bf16: batch 64, 32/32 heads, head_dim 128, block 16, lengths U[1,2048]",
     "c4": "long-context GQA decode bf16: batch 16, 64 q / 8 KV heads, head_dim 128, block 16, "
           "lengths U[16384,32768]",
@@ -693,6 +695,8 @@ def main() -> int:
     host_plan_us = float(np.median(plan_times[1:]))
 
     dev = torch.device("cuda", 0)
+    f32 = case.get("cfg", {}).get("dtype") == "f32"
+    kv_dtype, e = (torch.float32, 4) if f32 else (torch.bfloat16, 2)
     tables_d = torch.from_numpy(tables).to(dev)
     lens_d = torch.from_numpy(lens).to(dev)
     plan_d = plan.to_device(dev)
@@ -700,17 +704,17 @@ def main() -> int:
     cows_d = torch.from_numpy(np.ascontiguousarray(cows, dtype=np.int32)).to(dev)
     ws_bytes = pk.decode_workspace_bytes(plan, hq, d)
     ws = torch.empty(max(ws_bytes, 256) // 4, dtype=torch.float32, device=dev)
-    q_d = torch.from_numpy(case["q"].view(np.int16)).view(torch.bfloat16).to(dev)
+    q_d = (torch.from_numpy(case["q"]) if f32 else torch.from_numpy(case["q"].view(np.int16)).view(torch.bfloat16)).to(dev)
 
-    pool_bytes = 2 * nb * B * hkv * d * 2
+    pool_bytes = 2 * nb * B * hkv * d * e
     R = args.replicas or max(2, math.ceil(2**30 / pool_bytes))
     # All replicas' K pools and the new K rows in one allocation, and the same
     # for V, so that each pool and the new rows share one 4 GiB window (the
     # fused append then reads every tile with buffer loads; the mode is
     # reported in the config).
     pool_elems, new_elems = nb * B * hkv * d, S * hkv * d
-    k_slab = torch.empty(R * pool_elems + new_elems, dtype=torch.bfloat16, device=dev)
-    v_slab = torch.empty(R * pool_elems + new_elems, dtype=torch.bfloat16, device=dev)
+    k_slab = torch.empty(R * pool_elems + new_elems, dtype=kv_dtype, device=dev)
+    v_slab = torch.empty(R * pool_elems + new_elems, dtype=kv_dtype, device=dev)
     pools = []
     for r in range(R):
         g = torch.Generator(device=dev)
@@ -828,8 +832,8 @@ def main() -> int:
     # Algorithmic KV bytes: every distinct (block, slot) the step reads, K and
     # V of every KV head, once (equal to the logical bytes unless sequences
     # share blocks).
-    kv_bytes = w["unique_tokens"] * hkv * d * 2 * 2
-    logical_kv_bytes = int(lens.astype(np.int64).sum()) * hkv * d * 2 * 2
+    kv_bytes = w["unique_tokens"] * hkv * d * 2 * e
+    logical_kv_bytes = int(lens.astype(np.int64).sum()) * hkv * d * 2 * e
     value = kv_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = kv_bytes / (attention_us * 1e-6) / 1e9
     schedule = [int(workgroups), int(args.piece)]
@@ -846,7 +850,7 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "f32" if f32 else "bf16",
         "data": "synthetic",
         "config": {"workload": f"{name}: {w['desc']}", "num_seqs": S, "num_q_heads": hq,
                    "num_kv_heads": hkv, "head_dim": d, "block_size": B,
@@ -880,7 +884,8 @@ def main() -> int:
         "host_plan_us": round(host_plan_us, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(name, schedule),
-                     "kernel": "decode_bf16_kernel (the attention launch of pa_decode, append fused)",
+                     "kernel": ("decode_f32_kernel" if f32 else "decode_bf16_kernel") +
+                               " (the attention launch of pa_decode, append fused)",
                      "bytes_per_launch": kv_bytes},
     }
     if "prefix_cache" in w:
@@ -916,9 +921,12 @@ def main() -> int:
         result["decode_tokens_per_s_gpu_only"] = result["decode_tokens_per_s"]
         result["decode_tokens_per_s"] = e2e["decode_tokens_per_s"]
     if not args.no_cpu_baseline:
-        k_host = pools[0].k.cpu().view(torch.int16).numpy().view(np.uint16)
-        v_host = pools[0].v.cpu().view(torch.int16).numpy().view(np.uint16)
-        result["cpu_baseline"] = cpu_baseline(case, hkv * d * 2 * 2, k_host, v_host, tables, lens, args.cpu_seconds)
+        if f32:
+            k_host, v_host = pools[0].k.cpu().numpy(), pools[0].v.cpu().numpy()
+        else:
+            k_host = pools[0].k.cpu().view(torch.int16).numpy().view(np.uint16)
+            v_host = pools[0].v.cpu().view(torch.int16).numpy().view(np.uint16)
+        result["cpu_baseline"] = cpu_baseline(case, hkv * d * 2 * e, k_host, v_host, tables, lens, args.cpu_seconds)
     print(json.dumps(result), flush=True)
     return 0
 

@@ -35,7 +35,7 @@
  *     arrays when the preconditions hold;
  *   - launch failures return PA_ERR_HIP.
  * Supported shapes: dtype F32 or BF16; head_dim 64 or 128 for F32, 128 for
- * BF16; block_size 1, 2, 4, 8, 16 or 32 (below 8, a bf16 plan's jobs cover
+ * BF16; block_size 1, 2, 4, 8, 16 or 32 (below 8, a plan's jobs cover
  * at most 8 * B tiles); num_q_heads a multiple of num_kv_heads with a group
  * of at most 16 query heads per KV head.
  */

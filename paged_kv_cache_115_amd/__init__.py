@@ -279,7 +279,7 @@ PA_REPLAN = 1  # pa_decode_plan_advance: build a new plan
 
 def _piece_cap(max_piece_tiles: int, block_size: int | None) -> int:
     """Longest job in tiles: pools of fewer than 8 slots per block take jobs
-    of at most 8 * B tiles (the bf16 kernel's table window)."""
+    of at most 8 * B tiles (the kernels' table window)."""
     if block_size is not None and block_size < 8:
         return min(max_piece_tiles, 8 * block_size) if max_piece_tiles > 0 else 8 * block_size
     return max_piece_tiles

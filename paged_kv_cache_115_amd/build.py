@@ -27,7 +27,7 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", INCLUDE, "-I", CSRC,
 ]
-SOURCES = ["abi.cpp", "block_manager.cpp", "validate.cpp", "step.cpp", "cache_kernels.hip", "decode_kernels.hip", "noalloc.hip",
+SOURCES = ["abi.cpp", "block_manager.cpp", "validate.cpp", "step.cpp", "cache_kernels.hip", "decode_kernels.hip", "decode_f32_kernels.hip", "noalloc.hip",
            "probe_kernels.hip"]
 
 

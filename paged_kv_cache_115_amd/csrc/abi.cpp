@@ -1335,9 +1335,9 @@ pa_status decode_stages(int stages, const char* who, const pa_kv_pool* pool, con
     return fail(PA_ERR_INVALID, "%s: inconsistent plan info", who);
   if (info->num_groups > 0 && pool->dtype != PA_BF16)
     return fail(PA_ERR_UNSUPPORTED, "%s: shared-prefix plans need a bf16 pool", who);
-  // Below 8 slots per block the bf16 kernel holds a window of 128 table
-  // entries per job, i.e. 8 * B tiles.
-  if (pool->dtype == PA_BF16 && pool->block_size < 8 && info->max_job_tiles > 8 * pool->block_size)
+  // Below 8 slots per block the kernels hold a window of 128 table entries
+  // per job, i.e. 8 * B tiles.
+  if (pool->block_size < 8 && info->max_job_tiles > 8 * pool->block_size)
     return fail(PA_ERR_INVALID,
                 "%s: at block size %d jobs may cover at most %d tiles (plan with max_piece_tiles <= %d); "
                 "the plan's longest covers %d",

@@ -48,147 +48,11 @@
 //   adds the same rounded values, so numerator and denominator agree.
 //   A job's block-table entries sit in one vector register (lane i: tile i)
 //   and are read with readlane.
-// f32 path (head_dim 64 or 128, any G <= 16): vector ALU; each lane owns
-//   head_dim/64 dims, a query-key dot product is a wavefront butterfly sum.
-#include <hip/hip_runtime.h>
-
-#include <math.h>
-
-#include "launch.h"
+// The fp32 path is in decode_f32_kernels.hip.
+#include "decode_common.h"
 
 namespace pagedkv {
 namespace {
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef short short4_t __attribute__((ext_vector_type(4)));
-typedef float float4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float float2_t __attribute__((ext_vector_type(2)));
-
-constexpr int kNW = 4;          // wavefronts per workgroup = KV heads per job
-constexpr int kDepth = 2;       // bf16 kernel: K/V tiles in flight per wavefront
-constexpr int kWavesPerSimd = 2;  // bf16 kernel: occupancy it is compiled for
-constexpr int kTile = 16;       // tokens per tile (MFMA rows)
-constexpr int kHeadDim = 128;   // head_dim of the bf16 path
-constexpr int kMaxTiles = 64;   // tiles per job: one table entry per lane
-constexpr int kMaxMergeThreads = 16 * 128 / 2;  // merge block: G * head_dim / 2 threads
-constexpr int kKtRow = 272;     // bf16 kernel: bytes per K row in the LDS transposition area (256 + 16)
-typedef __attribute__((address_space(3))) char lds_char;
-typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// 1 / sum for a softmax denominator: 0 for an empty context (sum 0), NaN
-// for a poisoned one (NaN sum), 1 / sum otherwise.
-__device__ __forceinline__ float recip_sum(float l) { return l > 0.f ? 1.0f / l : l == 0.f ? 0.f : l; }
-
-__device__ __forceinline__ uint32_t bf16_rne(float x) {
-  uint32_t u = __float_as_uint(x);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
-}
-
-// Two floats as packed bfloat16, rounded to nearest even by the hardware
-// conversion (v_cvt_pk_bf16_f32); lo in the low half.
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(float2_t{lo, hi}, bf16x2_t));
-}
-
-// Max / sum over lanes i, i ^ 16, i ^ 32, i ^ 48 (one column of a 16x16
-// MFMA result: rows 4*lq + r live in lanes li + 16*lq).  Each gfx950 lane
-// swap (lanes i and i ^ 32, then i and i ^ 16) hands every lane its own value
-// and its partner's, without the LDS round trip of a bpermute.
-__device__ __forceinline__ float col_max(float x) {
-  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-__device__ __forceinline__ float col_sum(float x) {
-  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-
-__device__ __forceinline__ uint32_t word(const uint4& v, int i) {
-  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
-}
-
-__device__ __forceinline__ int32_t clamp_block(int32_t b, int32_t nb) { return min(max(b, 0), nb - 1); }
-
-// The plan, the context lengths and the merge list are never written while
-// a decode kernel runs.  Reading them through the constant address space lets
-// the compiler use scalar loads, which are tracked apart from the vector
-// memory queue: waiting for a job record then never waits for K/V loads or
-// output stores in flight.
-template <typename T>
-__device__ __forceinline__ const __attribute__((address_space(4))) T* as_const(const T* p) {
-  return (const __attribute__((address_space(4))) T*)(uintptr_t)p;
-}
-
-typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
-
-// Job record i of the plan, by scalar loads.
-__device__ __forceinline__ pa_decode_job load_job(const pa_decode_job* jobs, int64_t i) {
-  const auto* q = as_const(reinterpret_cast<const i32x4_t*>(jobs)) + 2 * i;
-  const i32x4_t x = q[0], y = q[1];
-  return pa_decode_job{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
-}
-
-// Four consecutive output values at element index idx (a multiple of 4).
-__device__ __forceinline__ void store4(const DecodeArgs& a, int64_t idx, float x0, float x1, float x2, float x3) {
-  if (a.out_bf16) {
-    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.out) + idx) =
-        make_uint2(bf16_rne(x0) | (bf16_rne(x1) << 16), bf16_rne(x2) | (bf16_rne(x3) << 16));
-  } else {
-    *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + idx) = make_float4(x0, x1, x2, x3);
-  }
-}
-
-__device__ __forceinline__ void store1(const DecodeArgs& a, int64_t idx, float x) {
-  if (a.out_bf16)
-    reinterpret_cast<uint16_t*>(a.out)[idx] = (uint16_t)bf16_rne(x);
-  else
-    reinterpret_cast<float*>(a.out)[idx] = x;
-}
-
-// Job fields as seen by one wavefront (all wave-uniform).
-struct JobView {
-  int32_t seq, g, t0, cnt, L, rec;
-  int32_t w;     // wavefront's KV head within the head block
-  int32_t grp;   // shared job: its group descriptor
-  int32_t part;  // shared job: piece of the shared prefix
-  int32_t ncol;  // query columns computed: G, or members x G for a shared job
-  bool idle;     // the wavefront's KV head is past the last one: read nothing, write nothing
-  bool shared;   // the job reads a prefix shared by the members of a group
-};
-
-// The fields of job record jd for wavefront w (the context length comes
-// with the record).  Any record (an empty slot included) gives in-range
-// addresses; a wavefront whose KV head is past the last one is idle.
-__device__ __forceinline__ void view_job(const DecodeArgs& a, const pa_decode_job& jd, int w, int B, JobView& v) {
-  v.shared = (jd.head_block & PA_JOB_SHARED) != 0;
-  const int32_t g = (jd.head_block & 0xffff) * kNW + w;
-  v.w = w;
-  v.idle = g < 0 || g >= a.num_kv_heads || (v.shared && a.num_groups <= 0);
-  v.grp = v.shared ? min(max(jd.record_base, 0), max(a.num_groups - 1, 0)) : 0;
-  v.part = max(jd.part, 0);
-  v.ncol = v.shared ? min(max(jd.num_parts, 1), 4) * a.group : a.group;
-  v.g = min(max(g, 0), a.num_kv_heads - 1);
-  v.cnt = min(max(jd.tile_count, 0), kMaxTiles);
-  v.seq = min(max(jd.seq, 0), a.num_seqs - 1);
-  v.t0 = max(jd.tile_begin, 0);
-  v.L = min(max(jd.context_len, 0), a.max_blocks * B);
-  v.rec = -1;
-  if (!v.shared && jd.num_parts > 1) {
-    const int64_t r = (int64_t)jd.record_base + (int64_t)w * jd.num_parts + jd.part;
-    v.rec = (jd.record_base >= 0 && jd.part >= 0 && jd.part < jd.num_parts && r < a.num_records) ? (int32_t)r : -2;
-  }
-  if (v.idle) v.rec = -2;
-}
 
 // --------------------------------------------------------------------------
 // bf16, head_dim 128: MFMA for QK^T and PV.
@@ -860,104 +724,6 @@ done:
 }
 
 // --------------------------------------------------------------------------
-// f32: vector ALU.  Lane owns dims lane + 64*j; one token at a time.
-// --------------------------------------------------------------------------
-template <int B, int D>
-__global__ __launch_bounds__(kNW * 64) void decode_f32_kernel(DecodeArgs a) {
-  constexpr int DPL = D / 64;
-  constexpr int kMaxGroup = 16;
-  const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: keeps job fields in SGPRs
-  const int G = a.group;
-  for (int32_t k = 0; k < a.jobs_per_workgroup; ++k) {
-    const pa_decode_job jd = load_job(a.jobs, (int64_t)k * a.num_workgroups + blockIdx.x);
-    if (jd.tile_count <= 0) break;
-    JobView v;
-    view_job(a, jd, w, B, v);
-    if (v.idle) continue;
-    float qv[kMaxGroup][DPL], m_run[kMaxGroup], l_run[kMaxGroup], o[kMaxGroup][DPL];
-    const float* qrow = reinterpret_cast<const float*>(a.q) + ((int64_t)v.seq * a.num_q_heads + (int64_t)v.g * G) * D;
-#pragma unroll
-    for (int h = 0; h < kMaxGroup; ++h) {
-      m_run[h] = -INFINITY;
-      l_run[h] = 0.f;
-#pragma unroll
-      for (int jj = 0; jj < DPL; ++jj) {
-        qv[h][jj] = h < G ? qrow[h * D + lane + 64 * jj] : 0.f;
-        o[h][jj] = 0.f;
-      }
-    }
-    const int64_t row_stride = (int64_t)a.num_kv_heads * D;
-    const float* kbase = reinterpret_cast<const float*>(a.k) + (int64_t)v.g * D;
-    const float* vbase = reinterpret_cast<const float*>(a.v) + (int64_t)v.g * D;
-    const int32_t* trow = a.tables + (int64_t)v.seq * a.max_blocks;
-    const int32_t len_dev = a.lens[v.seq];
-    const int32_t t_end = min(kTile * (v.t0 + v.cnt), v.L);
-    for (int32_t t = kTile * v.t0; t < t_end; ++t) {
-      const int32_t p = clamp_block(trow[t / B], a.num_blocks);
-      const int64_t row = ((int64_t)p * B + t % B) * row_stride;
-      float kv[DPL], vv[DPL];
-      if (a.new_k != nullptr && t == v.L - 1) {
-        // Fused append: this step's token comes from the new key/value
-        // arrays (the merge launch stores it into its pool slot).
-        const int64_t nrow = ((int64_t)v.seq * a.num_kv_heads + v.g) * D;
-        const float* nk = reinterpret_cast<const float*>(a.new_k) + nrow;
-        const float* nv = reinterpret_cast<const float*>(a.new_v) + nrow;
-#pragma unroll
-        for (int jj = 0; jj < DPL; ++jj) {
-          kv[jj] = nk[lane + 64 * jj];
-          vv[jj] = nv[lane + 64 * jj];
-        }
-      } else {
-#pragma unroll
-        for (int jj = 0; jj < DPL; ++jj) {
-          kv[jj] = kbase[row + lane + 64 * jj];
-          vv[jj] = vbase[row + lane + 64 * jj];
-        }
-      }
-#pragma unroll
-      for (int h = 0; h < kMaxGroup; ++h) {
-        if (h >= G) break;
-        float dot = 0.f;
-#pragma unroll
-        for (int jj = 0; jj < DPL; ++jj) dot += qv[h][jj] * kv[jj];
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) dot += __shfl_xor(dot, off);
-        const float x = dot * a.scale_log2e;
-        const float m_new = fmaxf(m_run[h], x);
-        const float alpha = fast_exp2(m_run[h] - m_new);
-        const float pr = fast_exp2(x - m_new);
-        l_run[h] = l_run[h] * alpha + pr;
-#pragma unroll
-        for (int jj = 0; jj < DPL; ++jj) o[h][jj] = o[h][jj] * alpha + pr * vv[jj];
-        m_run[h] = m_new;
-      }
-    }
-    if (v.rec == -2) continue;
-    if (len_dev != v.L) {
-      // Planned for another length: NaN, never plausible numbers.
-#pragma unroll
-      for (int h = 0; h < kMaxGroup; ++h) l_run[h] = NAN;
-    }
-#pragma unroll
-    for (int h = 0; h < kMaxGroup; ++h) {
-      if (h >= G) break;
-      if (v.rec < 0) {
-        const float inv = recip_sum(l_run[h]);
-        const int64_t base = ((int64_t)v.seq * a.num_q_heads + (int64_t)v.g * G + h) * D;
-#pragma unroll
-        for (int jj = 0; jj < DPL; ++jj) store1(a, base + lane + 64 * jj, o[h][jj] * inv);
-      } else {
-        const int64_t rec = (int64_t)v.rec * G + h;
-#pragma unroll
-        for (int jj = 0; jj < DPL; ++jj) a.partial_o[rec * D + lane + 64 * jj] = o[h][jj];
-        if (lane == 0) *reinterpret_cast<float2*>(a.partial_ml + 2 * rec) = make_float2(m_run[h], l_run[h]);
-      }
-    }
-  }
-}
-
-// --------------------------------------------------------------------------
 // Merge: for every (sequence, KV head) cut into pieces, combine the piece
 // records in piece order,
 //   M = max_p m_p,  out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p.
@@ -1179,24 +945,7 @@ hipError_t launch_decode_attention(const DecodeArgs& a, hipStream_t stream) {
 #undef PA_BF16_CASE
 #undef PA_BF16_LAUNCH
   } else {
-#define PA_F32_CASE(BS, DD)                                                                  \
-  if (!launched && a.block_size == BS && a.head_dim == DD) {                                 \
-    hipLaunchKernelGGL((decode_f32_kernel<BS, DD>), grid, dim3(kNW * 64), 0, stream, a);     \
-    launched = true;                                                                         \
-  }
-    PA_F32_CASE(1, 64)
-    PA_F32_CASE(2, 64)
-    PA_F32_CASE(4, 64)
-    PA_F32_CASE(8, 64)
-    PA_F32_CASE(16, 64)
-    PA_F32_CASE(32, 64)
-    PA_F32_CASE(1, 128)
-    PA_F32_CASE(2, 128)
-    PA_F32_CASE(4, 128)
-    PA_F32_CASE(8, 128)
-    PA_F32_CASE(16, 128)
-    PA_F32_CASE(32, 128)
-#undef PA_F32_CASE
+    return launch_decode_attention_f32(a, stream);
   }
   if (!launched) return hipErrorInvalidValue;
   return hipGetLastError();

@@ -58,6 +58,8 @@ struct DecodeArgs {
 // Attention launch (persistent grid of a.num_workgroups; nothing when the
 // plan has no jobs) on `stream`.
 hipError_t launch_decode_attention(const DecodeArgs& a, hipStream_t stream);
+// The same for an fp32 pool (decode_f32_kernels.hip).
+hipError_t launch_decode_attention_f32(const DecodeArgs& a, hipStream_t stream);
 // Merge launch: one workgroup per merge row, then, with a fused append
 // (a.new_k set), one per sequence writing its appended row into the pool;
 // nothing when neither is needed.

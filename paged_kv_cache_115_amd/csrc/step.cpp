@@ -56,7 +56,7 @@ extern "C" pa_status pa_bm_prepare_decode_step(pa_bm* bm, const int64_t* seqs, i
       return fail(PA_ERR_INVALID, "%s: sequence %lld grows to %d tokens, past max_blocks %d of %d slots", who,
                   (long long)seqs[i], lens[i], max_blocks, B);
   pa_decode_plan_info info{};
-  // Below 8 slots per block the bf16 kernel's jobs cover at most 8 * B tiles.
+  // Below 8 slots per block the kernels' jobs cover at most 8 * B tiles.
   const int32_t max_piece_tiles = B < 8 ? 8 * B : 0;
   // With plan reuse (pa_bm_set_plan_reuse), the last step's plan advances to
   // these lengths when it can; otherwise a new one is built (and kept).

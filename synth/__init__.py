@@ -44,6 +44,10 @@ CONFIGS: dict[str, dict] = {
     "c3": dict(seed=3, num_seqs=256, num_q_heads=32, num_kv_heads=8, head_dim=128,
                block_size=16, dtype="bf16",
                lengths=("lognormal", math.log(200.0) - 0.5, 1.0, 1, 4096)),
+    # The batch-256 GQA batch with an fp32 pool (the same lengths as c3).
+    "c3f": dict(seed=3, num_seqs=256, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                block_size=16, dtype="f32",
+                lengths=("lognormal", math.log(200.0) - 0.5, 1.0, 1, 4096)),
     # Long context GQA group 8, batch 16, lengths uniform on [16384, 32768].
     "c4": dict(seed=4, num_seqs=16, num_q_heads=64, num_kv_heads=8, head_dim=128,
                block_size=16, dtype="bf16", lengths=("uniform", 16384, 32768),

@@ -297,6 +297,40 @@ def test_merge_of_many_pieces(pk, dt, d, cap, parts):
     assert_close(got["out"], ref["out"], dt, f"merge {parts} pieces {dt}")
 
 
+def _f32_case(lens, b, hq, hkv, d, seed):
+    """_edge_case with float32 keys, values and queries (standard normal)."""
+    case = _edge_case(lens, b, hq=hq, hkv=hkv, d=d, seed=seed)
+    rng = np.random.default_rng(seed + 1)
+    total = int(np.asarray(lens).sum())
+    case["cfg"]["dtype"] = "f32"
+    case["keys"] = rng.standard_normal((total, hkv, d), dtype=np.float32)
+    case["values"] = rng.standard_normal((total, hkv, d), dtype=np.float32)
+    case["q"] = rng.standard_normal((len(lens), hq, d), dtype=np.float32)
+    return case
+
+
+@pytest.mark.parametrize("b,d,hq,hkv", [(16, 128, 32, 8), (32, 128, 64, 4), (8, 64, 6, 3), (2, 128, 8, 8),
+                                        (4, 64, 20, 2), (1, 128, 16, 4)])
+def test_f32_decode_matches_oracle(pk, b, d, hq, hkv):
+    """The fp32 path (both contractions on fp32 MFMA) against the float64
+    oracle at fp32's tolerance: groups of 1 to 16 query heads per KV head, a
+    KV-head count that leaves wavefronts idle, head_dim 64 and 128, every
+    block size, contexts that are empty, one token, tile and block multiples
+    and one past them, whole and cut into pieces, the append separate and
+    fused."""
+    lens = [0, 1, 7, 8, 9, 15, 16, 17, 31, 32, 33, 63, 64, 65, 0, 255, 256, 257, 1023, 1025]
+    case = _f32_case(lens, b, hq, hkv, d, seed=90 + b)
+    ref = oracle_decode_step(case)
+    for schedule in (DEFAULT, TINY_PIECES, SMALL_PIECES):
+        for fused in (False, True):
+            log(f"f32 B={b} D={d} {hq}/{hkv} schedule={schedule} fused={fused}")
+            got = product_decode_step(pk, case, schedule, fused=fused)
+            for s in np.flatnonzero(np.asarray(lens) == 0):
+                assert np.array_equal(got["out"][s], np.zeros((hq, d), np.float32))
+            stats = assert_close(got["out"], ref["out"], "f32", f"f32 B={b} D={d} {schedule} fused={fused}")
+            log(f"  max|err|={stats['max_abs']:.3g}")
+
+
 @pytest.mark.parametrize("b", [8, 16])
 @pytest.mark.parametrize("kind", ["lpt", "chunks"])
 def test_advanced_plan_matches_oracle(pk, b, kind):
