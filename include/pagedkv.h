@@ -376,11 +376,12 @@ pa_status pa_decode_plan_advance(void* plan, pa_decode_plan_info* info, const in
 
 /* How pa_decode, with these arguments, loads the tiles of its attention
  * launch, for diagnostics and benchmark reports: 0 without new rows; with
- * them (the append fused) 1 = the tile holding a sequence's new token on a
+ * them (the append fused) 4 = every tile by buffer loads at 32-bit offsets
+ * in a 4 GiB window holding the pool and the new rows (block sizes 16 and 32,
+ * when both pools' windows fit: place the step's new rows within 4 GiB of the
+ * pools for it); otherwise 1 = the tile holding a sequence's new token on a
  * path of its own (long contexts), 2 = every tile through per-lane 64-bit
- * addresses, 4 = every tile by buffer loads at 32-bit offsets in a 4 GiB
- * window holding the pool and the new rows (taken over 2 when both pools'
- * windows fit: place the step's new rows within 4 GiB of the pools for it).
+ * addresses.
  * Depends on the plan's tiles per sequence, the query heads per KV head, the
  * block size and the addresses; reads no memory.  -1 (pa_last_error) for bad
  * arguments. */

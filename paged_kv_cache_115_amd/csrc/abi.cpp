@@ -1252,8 +1252,12 @@ int32_t fused_mode(const pa_kv_pool* pool, const void* new_key, const void* new_
   const int32_t hkv = pool->num_kv_heads;
   const int64_t seq_streams = (int64_t)num_seqs * ((hkv + 3) / 4);
   const bool short_seqs = (int64_t)info->num_tiles < kShortSequenceTiles * seq_streams;
-  if (!(short_seqs || group < 4 || pool->block_size < 8)) return 1;
-  if (pool->block_size < 16) return 2;
+  // Mode 4 (window loads) whenever the tiles are whole blocks and both
+  // windows fit: measured at least as fast as 1 and 2 on every workload
+  // (C2, C3, C4, C5, c6).  Otherwise the separate path for long contexts
+  // with 4 or more query heads per KV head, per-lane addresses for the rest.
+  const int32_t fallback = !(short_seqs || group < 4 || pool->block_size < 8) ? 1 : 2;
+  if (pool->block_size < 16) return fallback;
   const uint64_t pool_bytes = (uint64_t)pool->num_blocks * (uint64_t)pool_block_bytes(*pool);
   const uint64_t new_bytes = (uint64_t)num_seqs * hkv * pool->head_dim * 2;
   DecodeArgs scratch{};
@@ -1271,7 +1275,7 @@ int32_t fused_mode(const pa_kv_pool* pool, const void* new_key, const void* new_
   };
   const bool windows = window(pool->k, new_key, &w.k_win, &w.k_win_bytes, &w.k_off, &w.nk_off) &&
                        window(pool->v, new_value, &w.v_win, &w.v_win_bytes, &w.v_off, &w.nv_off);
-  return windows ? 4 : 2;
+  return windows ? 4 : fallback;
 }
 
 pa_status decode_stages(int stages, const char* who, const pa_kv_pool* pool, const void* q, void* out,

@@ -4,9 +4,9 @@ choice reads only sizes and addresses, so fake device addresses do).
 The tile holding a sequence's new token mixes pool rows and the new row
 (mercemay.com "Blocks, tables, and the indirection": the token written this
 step is the one attended last).  pa_decode_fused_loads reports the load path
-pa_decode takes: a path of its own for that tile on long contexts (1),
-per-lane addresses on every tile for short ones (2), or buffer loads in a
-4 GiB window holding a pool and its new rows when both windows fit (4)."""
+pa_decode takes: buffer loads in a 4 GiB window holding a pool and its new
+rows when both windows fit (4); otherwise a path of its own for that tile on
+long contexts (1) or per-lane addresses on every tile (2)."""
 import ctypes
 
 import numpy as np
@@ -46,10 +46,13 @@ def test_fused_loads_choice():
     # one pool out of reach: per-lane addresses
     assert _mode(pool, near_k, base + 8 * GiB, p_short, 32) == 2
     assert _mode(pool, base + 6 * GiB, base + 6 * GiB + new_bytes, p_short, 32) == 2
-    # long contexts with 4 query heads per KV head: the separate path
-    assert _mode(pool, near_k, near_v, p_long, 32) == 1
-    # one query head per KV head: per-lane loads even for long contexts
+    # long contexts: window loads when the windows fit, else, with 4 query
+    # heads per KV head, the separate path
+    assert _mode(pool, near_k, near_v, p_long, 32) == 4
+    assert _mode(pool, near_k, base + 8 * GiB, p_long, 32) == 1
+    # one query head per KV head: per-lane loads for long contexts too
     assert _mode(pool, near_k, near_v, p_long, 8) == 4
+    assert _mode(pool, near_k, base + 8 * GiB, p_long, 8) == 2
     # 8-slot blocks: the window loads read whole 16-row tiles of one block
     pool8, per8 = _pool(base, 10000, 8)
     assert _mode(pool8, base + 2 * per8, base + 2 * per8 + new_bytes, p_short, 32) == 2
