@@ -761,17 +761,21 @@ pa_status schedule_prefix(const int32_t* lens, int32_t num_seqs, int32_t num_kv_
 // two workgroups (each job also costs kSplitJobUs); schedule_lpt splits each
 // pair's jobs to minimise it.
 constexpr double kRateOlder = 0.51, kRateYounger = 0.32, kRateAlone = 0.75, kSplitJobUs = 0.5;
+constexpr double kPerTileOlder = 1.0 / kRateOlder, kPerTileYounger = 1.0 / kRateYounger,
+                 kPerTileAlone = 1.0 / kRateAlone;
 constexpr int kSplitMaxJobs = 8;  // pairs with more jobs keep the greedy split
 
 double pair_end_us(double older_tiles, int older_jobs, double younger_tiles, int younger_jobs) {
-  const double t_older = older_tiles / kRateOlder + kSplitJobUs * older_jobs;
-  const double t_younger = younger_tiles / kRateYounger + kSplitJobUs * younger_jobs;
-  if (t_older <= t_younger) {
-    const double done = kRateYounger * std::max(0.0, t_older - kSplitJobUs * younger_jobs);
-    return t_older + std::max(0.0, younger_tiles - done) / kRateAlone;
-  }
-  const double done = kRateOlder * std::max(0.0, t_younger - kSplitJobUs * older_jobs);
-  return t_younger + std::max(0.0, older_tiles - done) / kRateAlone;
+  const double t_older = older_tiles * kPerTileOlder + kSplitJobUs * older_jobs;
+  const double t_younger = younger_tiles * kPerTileYounger + kSplitJobUs * younger_jobs;
+  // Both cases computed and one selected: the comparison is unpredictable
+  // over the subsets a plan tries, and a branch on it costs more than the
+  // arithmetic.
+  const double younger_done = kRateYounger * std::max(0.0, t_older - kSplitJobUs * younger_jobs);
+  const double older_first = t_older + std::max(0.0, younger_tiles - younger_done) * kPerTileAlone;
+  const double older_done = kRateOlder * std::max(0.0, t_younger - kSplitJobUs * older_jobs);
+  const double younger_first = t_younger + std::max(0.0, older_tiles - older_done) * kPerTileAlone;
+  return t_older <= t_younger ? older_first : younger_first;
 }
 
 pa_status schedule_lpt(const int32_t* lens, int32_t num_seqs, int32_t num_kv_heads, int64_t nwg_req,
@@ -883,10 +887,9 @@ pa_status schedule_lpt(const int32_t* lens, int32_t num_seqs, int32_t num_kv_hea
         for (uint32_t m = 0; m <= full; ++m) {
           const int older_jobs = __builtin_popcount(m);
           const double e = pair_end_us(sum[m], older_jobs, sum[full] - sum[m], np - older_jobs);
-          if (e < best) {
-            best = e;
-            best_mask = m;
-          }
+          const bool better = e < best;
+          best = better ? e : best;
+          best_mask = better ? m : best_mask;
         }
         for (int i = 0; i < np; ++i) placed_wg[pj[i]] = (int32_t)(((best_mask >> i) & 1) ? b : b + bins);
       }

@@ -71,8 +71,10 @@ struct F32Rows {
     return base + slot * ((int64_t)a.num_kv_heads * D);
   }
 
+  // Rows of tile t of the job; t < 0 (a filler past the job's last tile)
+  // reads only the fill rows, which stay in the caches.
   __device__ __forceinline__ void load(int32_t t, F32Tile<D>& T) const {
-    const int32_t tok0 = kTile * (v.t0 + t);
+    const int32_t tok0 = t < 0 ? v.L : kTile * (v.t0 + t);
     const int32_t first = (kTile * v.t0) / B;
     // K: row li.
     {
@@ -177,16 +179,16 @@ __global__ __launch_bounds__(kNW * 64, 2) void decode_f32_kernel(DecodeArgs a) {
 #pragma unroll
     for (int i = 0; i < 4 * (D / 64); ++i) st.o[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     // Two register slots, the loop unrolled over them so that a fresh load
-    // never has to be moved between registers.  Loads past the job's last
-    // tile re-read its last tile.
+    // never has to be moved between registers.  The load past the job's last
+    // tile is a filler that reads the fill rows only.
     F32Tile<D> ta, tb;
     const int32_t cnt = v.cnt;
     rows.load(0, ta);
     for (int32_t t = 0; t < cnt; t += 2) {
-      rows.load(min(t + 1, cnt - 1), tb);
+      rows.load(t + 1 < cnt ? t + 1 : -1, tb);
       compute_f32_tile<D>(a, v, t, li, lq, qf, ta, st);
       if (t + 1 >= cnt) break;
-      rows.load(min(t + 2, cnt - 1), ta);
+      rows.load(t + 2 < cnt ? t + 2 : -1, ta);
       compute_f32_tile<D>(a, v, t + 1, li, lq, qf, tb, st);
     }
     float lt = col_sum(st.l);

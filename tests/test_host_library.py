@@ -515,12 +515,12 @@ def _lpt_model(lens, hkv, nwg, cap):
                 younger = float(sum(jobs[i][2] for k, i in enumerate(pj) if not m >> k & 1))
                 jo = bin(m).count("1")
                 jy = len(pj) - jo
-                t_o = older / 0.51 + 0.5 * jo
-                t_y = younger / 0.32 + 0.5 * jy
+                t_o = older * (1.0 / 0.51) + 0.5 * jo
+                t_y = younger * (1.0 / 0.32) + 0.5 * jy
                 if t_o <= t_y:
-                    e = t_o + max(0.0, younger - 0.32 * max(0.0, t_o - 0.5 * jy)) / 0.75
+                    e = t_o + max(0.0, younger - 0.32 * max(0.0, t_o - 0.5 * jy)) * (1.0 / 0.75)
                 else:
-                    e = t_y + max(0.0, older - 0.51 * max(0.0, t_y - 0.5 * jo)) / 0.75
+                    e = t_y + max(0.0, older - 0.51 * max(0.0, t_y - 0.5 * jo)) * (1.0 / 0.75)
                 if e < best:
                     best, best_m = e, m
             wg_jobs[b] = [i for k, i in enumerate(pj) if best_m >> k & 1]
