@@ -112,6 +112,7 @@ __device__ __forceinline__ void store1(const DecodeArgs& a, int64_t idx, float x
 // Job fields as seen by one wavefront (all wave-uniform).
 struct JobView {
   int32_t seq, g, t0, cnt, L, rec;
+  int32_t L_dev; // the sequence's device length (load_ref requests it with the job's table entries)
   int32_t w;     // wavefront's KV head within the head block
   int32_t grp;   // shared job: its group descriptor
   int32_t part;  // shared job: piece of the shared prefix

@@ -71,6 +71,10 @@ template <int B>
 __device__ __forceinline__ void load_ref(const DecodeArgs& a, const pa_decode_job& jd, int w, int lane, JobRef<B>& J) {
   constexpr int kTilesPerBlock = B >= kTile ? B / kTile : 1;
   view_job(a, jd, w, B, J.v);
+  // The device length, compared with the planned one when the job is
+  // written: requested here, two job boundaries before the job starts, so
+  // writing a finished job waits for no load.
+  J.v.L_dev = as_const(a.lens)[J.v.seq];
   // Lanes past the job's last tile read an in-row entry that is never used.
   const int32_t* trow = a.tables + (int64_t)J.v.seq * a.max_blocks;
   if (B < 8) {
@@ -302,9 +306,7 @@ struct SoftmaxState {
 // sequence is NaN, whether written directly or through the merge of its
 // records.  The comparison sits outside the tile loop's hot path: code in
 // the loop costs registers there.
-__device__ __forceinline__ float sum_or_nan(const DecodeArgs& a, int32_t seq, int32_t len_plan, float l) {
-  return as_const(a.lens)[seq] == len_plan ? l : NAN;
-}
+__device__ __forceinline__ float sum_or_nan(const JobView& v, float l) { return v.L_dev == v.L ? l : NAN; }
 
 // One 16-token tile (tile t of job v): scores, online-softmax update, PV
 // accumulation.
@@ -377,7 +379,7 @@ __device__ __forceinline__ void compute_bf16_tile(const DecodeArgs& a, const Job
 
 // Finished jobs are staged in LDS and written to memory after the
 // wavefront's last job (once the staging area is full, later jobs are
-// written directly).  On gfx9 the
+// written directly, and the last job itself is).  On gfx9 the
 // vector memory counter retires loads and stores in issue order, so a store
 // issued between tile loads makes every later tile wait for the store's
 // acknowledgement; staging keeps the tile stream free of stores.
@@ -385,7 +387,7 @@ __device__ __forceinline__ void compute_bf16_tile(const DecodeArgs& a, const Job
 // Per wavefront: kStageFloats floats of accumulators (an entry holds, for the
 // G live columns, the 32 values of each lane (li, lq): entry float index
 // ((k * 4 + lq) * G + li) * 4 + c for k = 0..7, c = 0..3, i.e. o[4 * (k & 1) + c][k >> 1]),
-// then (m, l) per (entry, column), then (seq, g, record) per entry.
+// then (m, l) per (entry, column), then (seq, g, record, lengths agree) per entry.
 constexpr int kStageMax = 7;                      // entries per wavefront
 constexpr int kStageFloats = kStageMax * 4 * 128; // accumulator floats per wavefront (G = 4 fills 7 entries)
 constexpr int kStageWaveFloats = kStageFloats + kStageMax * 16 * 2 + kStageMax * 4;
@@ -405,14 +407,14 @@ __device__ __forceinline__ void flush_stage(const DecodeArgs& a, Stage& sg, int 
     const int32_t seq = __builtin_amdgcn_readfirstlane(sg.meta[4 * e + 0]);
     const int32_t g = __builtin_amdgcn_readfirstlane(sg.meta[4 * e + 1]);
     const int32_t rec = __builtin_amdgcn_readfirstlane(sg.meta[4 * e + 2]);
-    const int32_t len_plan = __builtin_amdgcn_readfirstlane(sg.meta[4 * e + 3]);
+    const int32_t len_ok = __builtin_amdgcn_readfirstlane(sg.meta[4 * e + 3]);
     if (li >= G || rec < -1) continue;  // -2: a shared job's member without a valid record
     const float* eo = sg.o + e * 128 * G;
     float4 v[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) v[k] = *reinterpret_cast<const float4*>(eo + ((k * 4 + lq) * G + li) * 4);
     const float m = sg.ml[(e * 16 + li) * 2];
-    const float lt = sum_or_nan(a, seq, len_plan, sg.ml[(e * 16 + li) * 2 + 1]);
+    const float lt = len_ok ? sg.ml[(e * 16 + li) * 2 + 1] : NAN;
     if (rec < 0) {
       const float inv = recip_sum(lt);
       const int64_t base = ((int64_t)seq * a.num_q_heads + (int64_t)g * G + li) * D + 32 * lq;
@@ -438,9 +440,12 @@ __device__ __forceinline__ void flush_stage(const DecodeArgs& a, Stage& sg, int 
 
 // End of a job: stage the output (whole sequence) or the piece's record.
 // Lane (li, lq) holds, for head li, accumulator rows 4*lq + r of instance c:
-// dims 32*lq + 8*r + c.  With the stage full, the job is written directly.
+// dims 32*lq + 8*r + c.  With the stage full, or for the wavefront's last job
+// (`direct`: no tile load follows its stores), the job is written directly;
+// staging the last job and writing it from LDS afterwards cost its wavefront
+// about a microsecond at the end of the launch (C3 38.8 -> 38.4 us).
 __device__ __forceinline__ void finish_bf16_job(const DecodeArgs& a, const JobView& v, int li, int lq,
-                                                const SoftmaxState& st, Stage& sg) {
+                                                const SoftmaxState& st, Stage& sg, bool direct) {
   constexpr int D = 128;
   const int G = a.group;
   float lt = col_sum(st.l);
@@ -458,7 +463,7 @@ __device__ __forceinline__ void finish_bf16_job(const DecodeArgs& a, const JobVi
     const int32_t np = m == 0 ? x2[2] : m == 1 ? x2[3] : m == 2 ? x3[0] : x3[1];
     const int64_t rec = (int64_t)rb + (int64_t)v.w * np + v.part;
     const bool valid = rb >= 0 && v.part < np && rec < a.num_records;
-    if (sg.n + members <= sg.cap) {
+    if (!direct && sg.n + members <= sg.cap) {
       const int e = sg.n + m, lg = li % G;
       if (li < v.ncol) {
         float* eo = sg.o + e * 128 * G;
@@ -474,14 +479,14 @@ __device__ __forceinline__ void finish_bf16_job(const DecodeArgs& a, const JobVi
           sg.meta[4 * e + 0] = v.seq;
           sg.meta[4 * e + 1] = v.g;
           sg.meta[4 * e + 2] = valid ? (int32_t)rec : -2;
-          sg.meta[4 * e + 3] = v.L;
+          sg.meta[4 * e + 3] = v.L_dev == v.L;
         }
       }
       sg.n += members;
       return;
     }
     if (li >= v.ncol || !valid) return;
-    lt = sum_or_nan(a, v.seq, v.L, lt);
+    lt = sum_or_nan(v, lt);
     const int64_t rr = rec * G + li % G;
     float* po = a.partial_o + rr * D + 32 * lq;
 #pragma unroll
@@ -493,9 +498,9 @@ __device__ __forceinline__ void finish_bf16_job(const DecodeArgs& a, const JobVi
     return;
   }
   if (v.rec == -2) return;
-  if (sg.n == sg.cap) {
+  if (direct || sg.n == sg.cap) {
     if (li >= G) return;
-    lt = sum_or_nan(a, v.seq, v.L, lt);
+    lt = sum_or_nan(v, lt);
     if (v.rec < 0) {
       const float inv = recip_sum(lt);
       const int64_t base = ((int64_t)v.seq * a.num_q_heads + (int64_t)v.g * G + li) * D + 32 * lq;
@@ -532,7 +537,7 @@ __device__ __forceinline__ void finish_bf16_job(const DecodeArgs& a, const JobVi
     sg.meta[4 * e + 0] = v.seq;
     sg.meta[4 * e + 1] = v.g;
     sg.meta[4 * e + 2] = v.rec;
-    sg.meta[4 * e + 3] = v.L;
+    sg.meta[4 * e + 3] = v.L_dev == v.L;
   }
   sg.n = e + 1;
 }
@@ -679,7 +684,7 @@ __global__ __launch_bounds__(kNW * 64, kWavesPerSimd) void decode_bf16_kernel(De
     compute_bf16_tile(a, cur.v, qc, x - x0, li, lq, ks, vs, kt, st);
     ++x;
     if (x - x0 < cur.v.cnt) return true;
-    finish_bf16_job(a, cur.v, li, lq, st, sg);
+    finish_bf16_job(a, cur.v, li, lq, st, sg, !hn);
     if (!hn) return false;
     x0 += cur.v.cnt;
     cur = nxt;
