@@ -162,9 +162,9 @@ pa_status pa_swap_blocks(const pa_kv_pool* device_pool, const pa_kv_pool* host_p
  * piece of consecutive tiles of one (sequence, block of four KV heads)
  * stream, and each persistent workgroup runs a list of jobs.  The host plan
  * (pa_decode_plan, which knows the lengths) builds two schedules and keeps
- * the one whose busiest workgroup costs less: equal-work chunks of the
+ * the one whose busiest compute unit costs less: equal-work chunks of the
  * streams laid end to end, cut at tile boundaries (PA_SCHEDULE_CHUNKS), or
- * pieces of at most a workgroup's share placed largest first on the least
+ * pieces of at most two workgroups' shares placed largest first on the least
  * loaded compute unit, i.e. pair of workgroups {b, b + nwg/2}, each
  * workgroup then running its pieces smallest first (PA_SCHEDULE_LPT).  The
  * four waves of a workgroup take the four KV heads
@@ -302,12 +302,16 @@ pa_status pa_decode_plan(const int32_t* context_lens, int32_t num_seqs, int32_t 
  *   4 per stream start), at tile boundaries: a tile goes to the workgroup
  *   whose share holds its midpoint.  A stream's records are per stream.
  * PA_SCHEDULE_LPT: each sequence is cut into near-equal pieces of at most
- *   max_piece_tiles tiles (0: the average tiles per workgroup, clamped to
- *   [4, 64]); one job per (piece, head block); jobs, largest first, go to the
- *   least-loaded compute unit (pair of workgroups), and each workgroup runs
- *   its jobs smallest first.  Fewer jobs, coarser balance.
- * Automatic choice: the schedule whose busiest workgroup costs less, with a
- * job charged as 56 tokens (calibrated on MI355X), the chunks on a tie. */
+ *   max_piece_tiles tiles (0: twice the average tiles per workgroup,
+ *   clamped to [4, 64]); one job per (piece, head block); jobs, largest
+ *   first, go to the least-loaded compute unit (pair of workgroups b and
+ *   b + num_workgroups/2), each pair's jobs are split between its two
+ *   workgroups by a model of their uneven shares of the compute unit, and
+ *   each workgroup runs its jobs smallest first.  Fewer jobs, coarser balance.
+ * Automatic choice: the schedule whose busiest compute unit (the two
+ * workgroups of a pair together; the busiest workgroup for an odd grid)
+ * costs less, with a job charged as 56 tokens (calibrated on MI355X), the
+ * chunks on a tie. */
 pa_status pa_decode_plan_schedule(const int32_t* context_lens, int32_t num_seqs, int32_t num_kv_heads,
                                   int32_t num_workgroups, int32_t max_piece_tiles, int32_t schedule, void* plan,
                                   size_t capacity, pa_decode_plan_info* info);

@@ -736,8 +736,8 @@ pa_status schedule_prefix(const int32_t* lens, int32_t num_seqs, int32_t num_kv_
 }
 
 // Largest pieces first: each sequence's tiles are cut into near-equal pieces
-// of at most `cap` tiles (cap = 0: the average tiles per workgroup, clamped to
-// [4, 64]); one job per (piece, head block).  Fewer, larger jobs than the
+// of at most `cap` tiles (cap = 0: twice the average tiles per workgroup,
+// clamped to [4, 64]); one job per (piece, head block).  Fewer, larger jobs than the
 // chunks when most sequences fit in one workgroup's share.  Records are per
 // sequence: KV head g, piece p at base + g * parts + p.
 //
@@ -783,7 +783,10 @@ pa_status schedule_lpt(const int32_t* lens, int32_t num_seqs, int32_t num_kv_hea
   const int64_t head_blocks = (num_kv_heads + 3) / 4;
   int64_t total = 0;
   for (int32_t s = 0; s < num_seqs; ++s) total += ((int64_t)lens[s] + 15) / 16 * head_blocks;
-  const int64_t cap = cap_req > 0 ? cap_req : std::min<int64_t>(64, std::max<int64_t>(4, (total + nwg_req - 1) / nwg_req));
+  // Default piece: twice the average tiles per workgroup.  The pair split
+  // balances a compute unit's two workgroups, so pieces coarser than one
+  // workgroup's share still balance, with fewer jobs and merge records.
+  const int64_t cap = cap_req > 0 ? cap_req : std::min<int64_t>(64, std::max<int64_t>(4, (2 * total + nwg_req - 1) / nwg_req));
   std::vector<pa_decode_job> jobs;
   {
     int64_t n = 0;
@@ -914,13 +917,22 @@ pa_status schedule_lpt(const int32_t* lens, int32_t num_seqs, int32_t num_kv_hea
   return PA_OK;
 }
 
-// Largest workgroup cost: tokens of its tiles plus kJobCharge per job.
+// Largest compute-unit cost: tokens of its tiles plus kJobCharge per job,
+// summed over the workgroup pair {b, b + nwg/2} that shares a compute unit
+// (an odd grid: the largest workgroup cost).  A pair is the unit because the
+// two workgroups' shares of the compute unit are uneven (pair_end_us): an
+// uneven split within a pair costs little.
 int64_t schedule_cost(const Schedule& sc, const int32_t* lens) {
   std::vector<int64_t> cost(sc.nwg, 0);
   for (const Piece& pc : sc.pieces)
     cost[pc.wg] += kJobCharge + rows_between(lens[pc.job.seq], pc.job.tile_begin, pc.job.tile_begin + pc.job.tile_count);
   int64_t m = 0;
-  for (int64_t c : cost) m = std::max(m, c);
+  if (sc.nwg % 2 == 0) {
+    const int64_t half = sc.nwg / 2;
+    for (int64_t b = 0; b < half; ++b) m = std::max(m, cost[b] + cost[b + half]);
+  } else {
+    for (int64_t c : cost) m = std::max(m, c);
+  }
   return m;
 }
 
@@ -1084,8 +1096,8 @@ extern "C" pa_status pa_decode_plan_schedule(const int32_t* context_lens, int32_
   if (total_tiles > (int64_t)INT32_MAX / 64) return fail(PA_ERR_INVALID, "pa_decode_plan: plan too large");
 
   // Automatic choice: both schedules are built and the one whose busiest
-  // workgroup costs less (tokens plus a charge per job) is kept, the chunks
-  // on a tie.
+  // compute unit costs less (tokens plus a charge per job) is kept, the
+  // chunks on a tie.
   Schedule chunks, lpt;
   pagedkv::ChunkWalk walk;
   if (schedule != PA_SCHEDULE_LPT)

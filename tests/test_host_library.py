@@ -453,8 +453,8 @@ def _plan_model(lens, hkv, nwg, cap):
 
 def _lpt_model(lens, hkv, nwg, cap):
     """Independent statement of the largest-pieces-first schedule: every
-    sequence cut into near-equal pieces of at most cap tiles (cap 0: the
-    average tiles per workgroup clamped to [4, 64]), one job per (piece, head
+    sequence cut into near-equal pieces of at most cap tiles (cap 0: twice
+    the average tiles per workgroup, clamped to [4, 64]), one job per (piece, head
     block); jobs by size, largest first (ties in generation order), each to
     the least-loaded pair of workgroups {b, b + nwg/2} for an even grid, or
     the least-loaded workgroup for an odd one (ties: the one that reached that
@@ -466,7 +466,7 @@ def _lpt_model(lens, hkv, nwg, cap):
     lens = [int(x) for x in lens]
     hb = -(-hkv // 4)
     total = sum(-(-L // 16) * hb for L in lens)
-    cap = cap or min(64, max(4, -(-total // nwg)))
+    cap = cap or min(64, max(4, -(-2 * total // nwg)))
     jobs, merges, records = [], [], 0
     for s, L in enumerate(lens):
         tiles = -(-L // 16)
@@ -570,7 +570,7 @@ def test_decode_plan_small_example_lpt():
     over 6 workgroups, cap 34: 600 tokens (38 tiles) -> pieces 19 + 19,
     1000 tokens (63 tiles) -> 32 + 31, times two head blocks; the 5-token
     sequence is one tile per head block."""
-    plan = pk.decode_plan([0, 5, 600, 1000], 8, num_workgroups=6, schedule=pk.SCHEDULE_LPT)
+    plan = pk.decode_plan([0, 5, 600, 1000], 8, num_workgroups=6, max_piece_tiles=34, schedule=pk.SCHEDULE_LPT)
     assert plan.schedule == pk.SCHEDULE_LPT
     assert (plan.num_workgroups, plan.num_jobs, plan.num_merges, plan.num_records) == (6, 10, 24, 32)
     jobs = sorted(map(tuple, plan.jobs()[:, :7].tolist()))
@@ -591,7 +591,12 @@ def test_decode_plan_small_example_lpt():
     merges = [tuple(m) for m in plan.merges().tolist()]
     assert merges == ([(0, g, 0, -1) for g in range(8)] + [(2, g, 2, 2 * g) for g in range(8)] +
                       [(3, g, 2, 16 + 2 * g) for g in range(8)])
-    assert lists_equal_model(plan, [0, 5, 600, 1000], 8, 6, 0, _lpt_model)
+    assert lists_equal_model(plan, [0, 5, 600, 1000], 8, 6, 34, _lpt_model)
+    # The default piece is twice the 34-tile average, clamped to 64: the
+    # 38- and 63-tile sequences stay whole.
+    whole = pk.decode_plan([0, 5, 600, 1000], 8, num_workgroups=6, schedule=pk.SCHEDULE_LPT)
+    assert (whole.num_jobs, whole.num_records) == (6, 0)
+    assert lists_equal_model(whole, [0, 5, 600, 1000], 8, 6, 0, _lpt_model)
     auto = pk.decode_plan([0, 5, 600, 1000], 8, num_workgroups=6)
     assert auto.schedule in (pk.SCHEDULE_CHUNKS, pk.SCHEDULE_LPT)
     with pytest.raises(pk.PaError):
