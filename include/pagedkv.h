@@ -217,7 +217,7 @@ typedef struct pa_decode_plan_info {
                              query heads per KV head) */
   int32_t num_seqs;       /* sequences the plan was made for: pa_decode refuses another num_seqs */
   int32_t max_context_len; /* longest context planned: pa_decode refuses tables too short for it */
-  int32_t reserved;
+  int32_t wide_jobs;      /* jobs with PA_JOB_WIDE (pa_decode_plan_prefix; 0 otherwise) */
   uint64_t lens_digest;   /* digest of the planned context lengths (pa_decode_plan_check_lens) */
   int32_t max_job_tiles;  /* tiles of the longest job (block sizes below 8 allow at most 8 * B) */
   int32_t reserved2;
@@ -228,6 +228,21 @@ typedef struct pa_decode_plan_info {
  * member (whose table is read), record_base indexes the pa_decode_group,
  * part is the piece of the shared prefix. */
 #define PA_JOB_SHARED (1 << 16)
+
+/* With PA_JOB_SHARED: the job reads the shared prefix for a set of up to four
+ * prefix groups of one key group, on one KV head (the low 16 bits of
+ * head_block are the KV head g, not a head block).  The workgroup's four
+ * wavefronts read the job's tiles four at a time, one tile each, exchange
+ * them through LDS, and wavefront w scores all four against group w of the
+ * set: every prefix tile of the head is read once for the whole set.
+ * record_base indexes the descriptor of the set's first group for head
+ * block g / 4; group k of the set has descriptor record_base + k *
+ * ceil(num_kv_heads / 4).  num_parts packs the set's shape: bits 0-7 the
+ * groups in the set, 8-15 the members of each group but the last, 16-23 the
+ * members of the last.  part is the piece of the shared prefix, the same for
+ * every member of the set (S06 "What's next": one read of a prefix however
+ * many requests share it). */
+#define PA_JOB_WIDE (1 << 17)
 
 /* One prefix group for one head block: up to four sequences whose first
  * blocks are the same physical blocks.  Member i's record for KV head

@@ -13,12 +13,12 @@ import os
 
 import numpy as np
 
-from ._lib import (LIB_PATH, PA_BF16, PA_DECODE_FIRST_BLOCKS, PA_DECODE_SHARED_KV, PA_F32, PA_JOB_SHARED, PA_SWAP_ENGINE_MEMCPY,
+from ._lib import (LIB_PATH, PA_BF16, PA_DECODE_FIRST_BLOCKS, PA_DECODE_SHARED_KV, PA_F32, PA_JOB_SHARED, PA_JOB_WIDE, PA_SWAP_ENGINE_MEMCPY,
                    PA_SWAP_ENGINE_KERNEL, PA_SWAP_IN, PA_SWAP_OUT, PaDecodePlanInfo, PaError, PaKvPool, lib)
 
 __all__ = [
     "set_debug", "validate_slots", "validate_copy_pairs", "validate_decode",
-    "LIB_PATH", "PA_F32", "PA_BF16", "PA_DECODE_SHARED_KV", "PA_DECODE_FIRST_BLOCKS", "PA_JOB_SHARED", "PaError", "BlockManager", "KvPool",
+    "LIB_PATH", "PA_F32", "PA_BF16", "PA_DECODE_SHARED_KV", "PA_DECODE_FIRST_BLOCKS", "PA_JOB_SHARED", "PA_JOB_WIDE", "PaError", "BlockManager", "KvPool",
     "reshape_and_cache", "copy_blocks", "decode_plan", "decode_workspace_bytes",
     "decode", "decode_noalloc", "DecodePlan", "default_workgroups", "HostKvPool", "swap_blocks", "PA_SWAP_OUT", "PA_SWAP_IN",
     "PA_SWAP_ENGINE_KERNEL", "PA_SWAP_ENGINE_MEMCPY",

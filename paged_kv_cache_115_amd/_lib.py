@@ -15,6 +15,7 @@ PA_BF16 = 1
 PA_DECODE_SHARED_KV = 1
 PA_DECODE_FIRST_BLOCKS = 2
 PA_JOB_SHARED = 1 << 16
+PA_JOB_WIDE = 1 << 17
 PA_SWAP_OUT = 0
 PA_SWAP_IN = 1
 PA_SWAP_ENGINE_KERNEL = 0
@@ -42,7 +43,7 @@ class PaDecodePlanInfo(ctypes.Structure):
                 ("flags", ctypes.c_int32), ("schedule", ctypes.c_int32), ("num_groups", ctypes.c_int32),
                 ("groups_at", ctypes.c_int32), ("group_size", ctypes.c_int32), ("first_at", ctypes.c_int32),
                 ("first_block_size", ctypes.c_int32), ("num_tiles", ctypes.c_int32),
-                ("num_seqs", ctypes.c_int32), ("max_context_len", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("num_seqs", ctypes.c_int32), ("max_context_len", ctypes.c_int32), ("wide_jobs", ctypes.c_int32),
                 ("lens_digest", ctypes.c_uint64), ("max_job_tiles", ctypes.c_int32), ("reserved2", ctypes.c_int32)]
 
 

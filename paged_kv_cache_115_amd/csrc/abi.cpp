@@ -481,12 +481,20 @@ pa_status finish_chunks(const int32_t* lens, int32_t num_seqs, int32_t num_kv_he
 // b mod kDies, and the dies do not share their L2 caches (MI355X: 8 XCDs of
 // 32 compute units, 4 MB of L2 each).
 constexpr int64_t kDies = 8;
+// Groups per set (one per wavefront of a workgroup; see schedule_prefix).
+constexpr int32_t kSetGroups = 4;
 // Cost, in tokens, of a 16-token tile of a prefix that several planned
 // groups share and that is placed as below: after the first reader on a die
 // the tile comes from that die's L2, not from HBM (measured on MI355X: about
 // 1.0 us per tile and wavefront against 1.3 us for a tile from HBM; 12
-// balanced the c6-shaped batch best among 4, 8, 12 and 16).
+// balanced best among 4, 8, 12 and 16 on 256 requests over four 2,000-token
+// prompts, G = 4).
 constexpr int64_t kWideTileCost = 12;
+// The same for a set's tile of one KV head (PA_JOB_WIDE), which its four
+// wavefronts score against four groups after one read: 8 balanced the same
+// batch best among 3, 5, 7, 8, 9, 10 and 12 (attention launch 67.5 us at 8,
+// 75.8 us at 12).
+constexpr int64_t kSetTileCost = 8;
 
 // Placement of the shared streams of wide prefixes (a key group cut into
 // several planned groups, each reading the same prefix blocks) so that the
@@ -503,14 +511,13 @@ constexpr int64_t kWideTileCost = 12;
 // shared piece before their other jobs, the second half after them:
 // workgroups b and b + nwg/2 share a compute unit, which then streams from
 // HBM with one while it reads from L2 with the other.  Adds each workgroup's
-// cost to `base`.
+// cost to `base`, `unit` per tile.
 void place_wide(const std::vector<Stream>& streams, const std::vector<int32_t>& wide,
-                const std::vector<int32_t>& set_of, int64_t nwg, int64_t cap, Schedule& out,
+                const std::vector<int32_t>& set_of, int64_t nwg, int64_t cap, int64_t unit, Schedule& out,
                 std::vector<int32_t>& first, std::vector<int32_t>& count, std::vector<int64_t>& base) {
   const int64_t per_die = nwg / kDies;
   int64_t total = 0;
   for (int32_t i : wide) total += streams[i].t_end - streams[i].t_begin;
-  const int64_t unit = kWideTileCost;
   std::vector<std::vector<Piece>> own(streams.size());
   // Tiles [t0, t1) of a stream on slot c (of n) of a die.
   auto put = [&](int64_t die, int32_t si, int32_t t0, int32_t t1, int64_t c, int64_t n) {
@@ -582,7 +589,7 @@ void place_wide(const std::vector<Stream>& streams, const std::vector<int32_t>& 
 // schedule.
 pa_status schedule_prefix(const int32_t* lens, int32_t num_seqs, int32_t num_kv_heads, int32_t group_cap,
                           const int32_t* prefix_group, const int32_t* prefix_tokens, int64_t nwg_req, int64_t cap,
-                          Schedule& out) {
+                          bool use_sets, Schedule& out) {
   const int32_t head_blocks = (num_kv_heads + 3) / 4;
   // Groups: members in sequence order, cut into groups of at most group_cap.
   std::vector<int32_t> by_key;
@@ -615,13 +622,59 @@ pa_status schedule_prefix(const int32_t* lens, int32_t num_seqs, int32_t num_kv_
   std::vector<int32_t> group_of(num_seqs, -1);
   for (size_t gi = 0; gi < groups.size(); ++gi)
     for (int32_t m : groups[gi]) group_of[m] = (int32_t)gi;
+  const bool die_aware = nwg_req % kDies == 0 && nwg_req >= 8 * kDies;
+  // Wide key groups (cut into several planned groups) are read in sets: up to
+  // kSetGroups consecutive groups of one key group with the same shared tiles.  A
+  // set's shared tiles are read once per KV head by one workgroup, whose
+  // wavefront w scores group w of the set (PA_JOB_WIDE); a wavefront holding
+  // one group of at most 16 query columns keeps its registers as for any job.
+  std::vector<int32_t> set_first, set_n, set_of_group(groups.size(), -1);
+  if (die_aware && use_sets) {
+    for (size_t gi = 0; gi < groups.size();) {
+      const int32_t key = prefix_group[groups[gi][0]];
+      size_t gj = gi;
+      while (gj < groups.size() && prefix_group[groups[gj][0]] == key) ++gj;
+      if (gj - gi >= 2) {
+        for (size_t k = gi; k < gj;) {
+          size_t e = k + 1;
+          while (e < gj && e - k < (size_t)kSetGroups && shared_tiles[e] == shared_tiles[k]) ++e;
+          for (size_t x = k; x < e; ++x) set_of_group[x] = (int32_t)set_first.size();
+          set_first.push_back((int32_t)k);
+          set_n.push_back((int32_t)(e - k));
+          k = e;
+        }
+      }
+      gi = gj;
+    }
+  }
   // Streams: shared items first in the list, then every sequence's own item.
   std::vector<Stream> streams;
+  std::vector<int32_t> shared_of(groups.size() * head_blocks, -1), head_of;
   int32_t item = 0;
-  for (size_t gi = 0; gi < groups.size(); ++gi, ++item) {
+  for (size_t gi = 0; gi < groups.size(); ++gi) {
     const int32_t lead = groups[gi][0];
-    for (int32_t hb = 0; hb < head_blocks; ++hb)
-      streams.push_back(Stream{lead, hb, 0, shared_tiles[gi], lens[lead], (int32_t)(gi * head_blocks + hb), item});
+    const int32_t si = set_of_group[gi];
+    if (si < 0) {
+      for (int32_t hb = 0; hb < head_blocks; ++hb) {
+        shared_of[gi * head_blocks + hb] = (int32_t)streams.size();
+        head_of.push_back(-1);
+        streams.push_back(Stream{lead, hb, 0, shared_tiles[gi], lens[lead], (int32_t)(gi * head_blocks + hb), item});
+      }
+      ++item;
+      continue;
+    }
+    const int32_t f = set_first[si];
+    if ((int32_t)gi == f) {
+      for (int32_t hb = 0; hb < head_blocks; ++hb)
+        for (int32_t g = 4 * hb; g < std::min<int32_t>(num_kv_heads, 4 * hb + 4); ++g) {
+          if (g == 4 * hb) shared_of[gi * head_blocks + hb] = (int32_t)streams.size();
+          head_of.push_back(g);
+          streams.push_back(Stream{lead, hb, 0, shared_tiles[gi], lens[lead], (int32_t)(gi * head_blocks + hb), item});
+        }
+      ++item;
+    } else {
+      for (int32_t hb = 0; hb < head_blocks; ++hb) shared_of[gi * head_blocks + hb] = shared_of[f * head_blocks + hb];
+    }
   }
   std::vector<int32_t> own_stream(num_seqs, -1);
   for (int32_t s = 0; s < num_seqs; ++s, ++item) {
@@ -630,21 +683,22 @@ pa_status schedule_prefix(const int32_t* lens, int32_t num_seqs, int32_t num_kv_
     own_stream[s] = (int32_t)streams.size();
     for (int32_t hb = 0; hb < head_blocks; ++hb) streams.push_back(Stream{s, hb, t0, (lens[s] + 15) / 16, lens[s], -1, item});
   }
+  head_of.resize(streams.size(), -1);  // own streams: no KV head of their own
   std::vector<int32_t> first, count, order;
   // Shared streams of wide prefixes (several planned groups of one key group)
   // get a placement of their own when the grid covers every die evenly.
   std::vector<int32_t> wide, rest, set_of(streams.size(), -1);
-  if (nwg_req % kDies == 0 && nwg_req >= 8 * kDies) {
+  if (die_aware) {
     // Groups of one key group are consecutive; a set is one (key group, head
     // block) of a key group planned as several groups.
     int32_t run = -1;
     for (size_t gi = 0; gi < groups.size(); ++gi) {
       const int32_t key = prefix_group[groups[gi][0]];
       if (gi == 0 || prefix_group[groups[gi - 1][0]] != key) ++run;
-      const bool w = (gi > 0 && prefix_group[groups[gi - 1][0]] == key) ||
-                     (gi + 1 < groups.size() && prefix_group[groups[gi + 1][0]] == key);
-      if (!w) continue;
-      for (int32_t hb = 0; hb < head_blocks; ++hb) set_of[gi * head_blocks + hb] = run * head_blocks + hb;
+      if (set_of_group[gi] < 0 || set_first[set_of_group[gi]] != (int32_t)gi) continue;
+      for (size_t i = 0; i < streams.size(); ++i)
+        if (streams[i].group >= 0 && streams[i].group / head_blocks == (int32_t)gi)
+          set_of[i] = run * head_blocks + streams[i].hb;
     }
     // By set, then group.
     std::vector<int32_t> ws;
@@ -658,7 +712,8 @@ pa_status schedule_prefix(const int32_t* lens, int32_t num_seqs, int32_t num_kv_
     first.assign(streams.size(), 0);
     count.assign(streams.size(), 0);
     std::vector<int64_t> base(nwg_req, 0);
-    place_wide(streams, wide, set_of, nwg_req, cap, out, first, count, base);
+    place_wide(streams, wide, set_of, nwg_req, cap, set_first.empty() ? kWideTileCost : kSetTileCost, out, first,
+               count, base);
     std::vector<Stream> rs;
     rs.reserve(rest.size());
     for (int32_t i : rest) rs.push_back(streams[i]);
@@ -670,6 +725,13 @@ pa_status schedule_prefix(const int32_t* lens, int32_t num_seqs, int32_t num_kv_
     }
     for (int32_t k : ro) order.push_back(rest[k]);
   }
+  // A member's records are laid out per head block (KV head 4*hb + w, piece
+  // p at record_base + w * parts + p), so the head streams of a set within a
+  // head block must be cut into equally many pieces.  The die placement cuts
+  // them alike unless a die holds more streams than workgroups; the caller
+  // then plans without sets.
+  for (size_t i = 0; i < streams.size(); ++i)
+    if (head_of[i] >= 0 && count[i] != count[shared_of[(size_t)streams[i].group]]) return PA_REPLAN;
   // Records, in layout order of the own streams: a grouped member always has
   // records (its shared pieces and its own); others only when cut.
   std::vector<int32_t> rb((size_t)num_seqs * head_blocks, -1), parts((size_t)num_seqs * head_blocks, 0);
@@ -678,7 +740,7 @@ pa_status schedule_prefix(const int32_t* lens, int32_t num_seqs, int32_t num_kv_
     if (st.group >= 0) continue;
     const int32_t s = st.seq, hb = st.hb;
     const int32_t gi = group_of[s];
-    const int32_t ks = gi >= 0 ? count[gi * head_blocks + hb] : 0;  // shared streams come first in the list
+    const int32_t ks = gi >= 0 ? count[shared_of[gi * head_blocks + hb]] : 0;
     const int32_t np = ks + count[i];
     if (np <= 1) continue;
     const int64_t heads = std::min<int64_t>(4, num_kv_heads - 4 * hb);
@@ -707,7 +769,24 @@ pa_status schedule_prefix(const int32_t* lens, int32_t num_seqs, int32_t num_kv_
       }
       const int32_t di = (int32_t)out.groups.size();
       out.groups.push_back(d);
-      const int32_t i = (int32_t)(gi * head_blocks + hb);
+      const int32_t si = set_of_group[gi];
+      if (si >= 0) {
+        if (set_first[si] != (int32_t)gi) continue;
+        const int32_t n = set_n[si];
+        const int32_t enc = n | ((int32_t)groups[gi].size() << 8) | ((int32_t)groups[gi + n - 1].size() << 16);
+        for (size_t i = 0; i < streams.size(); ++i) {
+          if (head_of[i] < 0 || streams[i].group != (int32_t)(gi * head_blocks + hb)) continue;
+          for (int32_t p = 0; p < count[i]; ++p) {
+            pa_decode_job& j = out.pieces[first[i] + p].job;
+            j.head_block = head_of[i] | PA_JOB_SHARED | PA_JOB_WIDE;
+            j.part = p;
+            j.num_parts = enc;
+            j.record_base = di;
+          }
+        }
+        continue;
+      }
+      const int32_t i = shared_of[gi * head_blocks + hb];
       for (int32_t p = 0; p < count[i]; ++p) {
         pa_decode_job& j = out.pieces[first[i] + p].job;
         j.head_block = hb | PA_JOB_SHARED;
@@ -988,6 +1067,8 @@ pa_status emit_plan(const Schedule& sc, int32_t schedule_id, int32_t num_kv_head
     in.max_job_tiles = std::max(in.max_job_tiles, pc.job.tile_count);
   }
   in.num_tiles = (int32_t)tiles;
+  in.wide_jobs = 0;
+  for (const Piece& pc : jobs) in.wide_jobs += (pc.job.head_block & PA_JOB_WIDE) != 0;
   in.num_seqs = num_seqs;
   in.max_context_len = 0;
   for (int32_t i = 0; i < num_seqs; ++i) in.max_context_len = std::max(in.max_context_len, lens[i]);
@@ -1054,11 +1135,16 @@ extern "C" pa_status pa_decode_plan_prefix(const int32_t* context_lens, int32_t 
   if (total_tiles > (int64_t)INT32_MAX / 64) return fail(PA_ERR_INVALID, "pa_decode_plan_prefix: plan too large");
   const int32_t group = num_q_heads / num_kv_heads;
   const int32_t group_cap = std::min(4, std::max(1, 16 / group));
+  const int64_t cap = max_piece_tiles > 0 ? max_piece_tiles : 64;
   pagedkv::Schedule sc;
-  if (pa_status st = pagedkv::schedule_prefix(context_lens, num_seqs, num_kv_heads, group_cap, prefix_group,
-                                              prefix_tokens, num_workgroups, max_piece_tiles > 0 ? max_piece_tiles : 64,
-                                              sc))
-    return st;
+  pa_status ps = pagedkv::schedule_prefix(context_lens, num_seqs, num_kv_heads, group_cap, prefix_group, prefix_tokens,
+                                          num_workgroups, cap, true, sc);
+  if (ps == PA_REPLAN) {  // the sets could not be cut alike: every group reads on its own
+    sc = pagedkv::Schedule{};
+    ps = pagedkv::schedule_prefix(context_lens, num_seqs, num_kv_heads, group_cap, prefix_group, prefix_tokens,
+                                  num_workgroups, cap, false, sc);
+  }
+  if (ps != PA_OK) return ps;
   const pa_status st =
       pagedkv::emit_plan(sc, PA_SCHEDULE_CHUNKS, num_kv_heads, context_lens, num_seqs, plan, capacity, info);
   // Loads keep blocks in the caches only when some block is read by more
@@ -1347,7 +1433,8 @@ pa_status decode_stages(int stages, const char* who, const pa_kv_pool* pool, con
       (int64_t)info->jobs_per_workgroup * info->num_workgroups < (int64_t)info->num_jobs ||
       (int64_t)info->merges_at < 32 * (int64_t)info->jobs_per_workgroup * info->num_workgroups ||
       (int64_t)info->bytes < (int64_t)info->merges_at + 16 * (int64_t)info->num_merges ||
-      info->num_groups < 0 ||
+      info->num_groups < 0 || info->wide_jobs < 0 || info->wide_jobs > info->num_jobs ||
+      (info->wide_jobs > 0 && info->num_groups == 0) ||
       (info->num_groups > 0 && (info->groups_at % 64 != 0 ||
                                 (int64_t)info->groups_at < (int64_t)info->merges_at + 16 * (int64_t)info->num_merges ||
                                 (int64_t)info->bytes < (int64_t)info->groups_at + 64 * (int64_t)info->num_groups)))
@@ -1385,6 +1472,7 @@ pa_status decode_stages(int stages, const char* who, const pa_kv_pool* pool, con
                        ? reinterpret_cast<const int32_t*>(pb + info->first_at)
                        : nullptr;
   a.num_groups = info->num_groups;
+  a.wide_jobs = info->wide_jobs;
   char* ws = static_cast<char*>(workspace);
   a.partial_ml = info->num_records > 0 ? reinterpret_cast<float*>(ws + lay.ml) : nullptr;
   a.partial_o = info->num_records > 0 ? reinterpret_cast<float*>(ws + lay.o) : nullptr;

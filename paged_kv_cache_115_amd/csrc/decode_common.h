@@ -117,23 +117,36 @@ struct JobView {
   int32_t grp;   // shared job: its group descriptor
   int32_t part;  // shared job: piece of the shared prefix
   int32_t ncol;  // query columns computed: G, or members x G for a shared job
+  int32_t T;     // tiles of the job (cnt counts positions: T for a job, ceil(T / 4) for a wide one)
   bool idle;     // the wavefront's KV head is past the last one: read nothing, write nothing
+                 // (in a wide job: the wavefront has no group of the set; it still loads its tiles)
   bool shared;   // the job reads a prefix shared by the members of a group
+  bool wide;     // PA_JOB_WIDE: the workgroup's wavefronts share one KV head and exchange tiles
 };
 
 // The fields of job record jd for wavefront w (the context length comes
 // with the record).  Any record (an empty slot included) gives in-range
 // addresses; a wavefront whose KV head is past the last one is idle.
+// Kernels built without kWide never receive wide jobs (the launch picks the
+// kWide kernel for plans that hold them).
+template <bool kWide = false>
 __device__ __forceinline__ void view_job(const DecodeArgs& a, const pa_decode_job& jd, int w, int B, JobView& v) {
   v.shared = (jd.head_block & PA_JOB_SHARED) != 0;
-  const int32_t g = (jd.head_block & 0xffff) * kNW + w;
-  v.w = w;
-  v.idle = g < 0 || g >= a.num_kv_heads || (v.shared && a.num_groups <= 0);
-  v.grp = v.shared ? min(max(jd.record_base, 0), max(a.num_groups - 1, 0)) : 0;
+  v.wide = kWide && v.shared && (jd.head_block & PA_JOB_WIDE) != 0;
+  const int32_t g = v.wide ? (jd.head_block & 0xffff) : (jd.head_block & 0xffff) * kNW + w;
+  // A wide job's set: jd.num_parts packs (groups, members per group, members of the last group).
+  const int32_t ngr = jd.num_parts & 0xff;
+  const int32_t members =
+      v.wide ? (w < ngr - 1 ? (jd.num_parts >> 8) & 0xff : (jd.num_parts >> 16) & 0xff) : jd.num_parts;
+  v.w = v.wide ? (g & 3) : w;
+  v.idle = g < 0 || g >= a.num_kv_heads || (v.shared && a.num_groups <= 0) || (v.wide && w >= ngr);
+  const int32_t grp = jd.record_base + (v.wide ? w * ((a.num_kv_heads + 3) / 4) : 0);
+  v.grp = v.shared ? min(max(grp, 0), max(a.num_groups - 1, 0)) : 0;
   v.part = max(jd.part, 0);
-  v.ncol = v.shared ? min(max(jd.num_parts, 1), 4) * a.group : a.group;
+  v.ncol = v.shared ? min(max(members, 1), 4) * a.group : a.group;
   v.g = min(max(g, 0), a.num_kv_heads - 1);
-  v.cnt = min(max(jd.tile_count, 0), kMaxTiles);
+  v.T = min(max(jd.tile_count, 0), kMaxTiles);
+  v.cnt = v.wide ? (v.T + 3) / 4 : v.T;
   v.seq = min(max(jd.seq, 0), a.num_seqs - 1);
   v.t0 = max(jd.tile_begin, 0);
   v.L = min(max(jd.context_len, 0), a.max_blocks * B);

@@ -67,10 +67,10 @@ struct JobRef {
 
 // The context length, the table entries and (load_q) the query of one job
 // depend only on its record, so they are fetched together.
-template <int B>
+template <int B, bool kWide>
 __device__ __forceinline__ void load_ref(const DecodeArgs& a, const pa_decode_job& jd, int w, int lane, JobRef<B>& J) {
   constexpr int kTilesPerBlock = B >= kTile ? B / kTile : 1;
-  view_job(a, jd, w, B, J.v);
+  view_job<kWide>(a, jd, w, B, J.v);
   // The device length, compared with the planned one when the job is
   // written: requested here, two job boundaries before the job starts, so
   // writing a finished job waits for no load.
@@ -308,24 +308,12 @@ struct SoftmaxState {
 // the loop costs registers there.
 __device__ __forceinline__ float sum_or_nan(const JobView& v, float l) { return v.L_dev == v.L ? l : NAN; }
 
-// One 16-token tile (tile t of job v): scores, online-softmax update, PV
-// accumulation.
-__device__ __forceinline__ void compute_bf16_tile(const DecodeArgs& a, const JobView& v, const bf16x8_t (&qf)[4],
-                                                  int32_t t, int li, int lq, uint4 (&kf)[4], uint4 (&vf)[4],
-                                                  lds_char* kt, SoftmaxState& st) {
-  const int32_t tok0 = kTile * (v.t0 + t);
-  if (tok0 >= v.L) return;  // beyond the context (only if the plan and lengths disagree)
-  // K row li into lane li, in place (the slot's registers): through the
-  // wavefront's LDS area, rows padded to kKtRow bytes so that the 16 rows one
-  // read pass touches fall in distinct banks.  LDS operations of a wavefront
-  // complete in order, so the reads see the writes, and the next tile's
-  // writes follow these reads.
-#pragma unroll
-  for (int r = 0; r < 4; ++r)
-    *reinterpret_cast<lds_u32x4*>(kt + (4 * lq + r) * kKtRow + 16 * li) = __builtin_bit_cast(u32x4_t, kf[r]);
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks)
-    kf[ks] = __builtin_bit_cast(uint4, *reinterpret_cast<const lds_u32x4*>(kt + li * kKtRow + 16 * (4 * ks + lq)));
+// Scores, online-softmax update and PV accumulation of the 16-token tile
+// whose first token is tok0: kf holds the K operand (K row li in lane li,
+// after the transposition), vf the V rows as loaded.
+__device__ __forceinline__ void tile_math(const DecodeArgs& a, const JobView& v, const bf16x8_t (&qf)[4],
+                                          int32_t tok0, int li, int lq, const uint4 (&kf)[4], uint4 (&vf)[4],
+                                          SoftmaxState& st) {
   const bool tail = tok0 + kTile > v.L;
   if (tail) {
     // Slots past the end hold arbitrary bits; V must be exactly zero there
@@ -377,6 +365,87 @@ __device__ __forceinline__ void compute_bf16_tile(const DecodeArgs& a, const Job
   }
 }
 
+// One 16-token tile (tile t of job v): scores, online-softmax update, PV
+// accumulation.
+__device__ __forceinline__ void compute_bf16_tile(const DecodeArgs& a, const JobView& v, const bf16x8_t (&qf)[4],
+                                                  int32_t t, int li, int lq, uint4 (&kf)[4], uint4 (&vf)[4],
+                                                  lds_char* kt, SoftmaxState& st) {
+  const int32_t tok0 = kTile * (v.t0 + t);
+  if (tok0 >= v.L) return;  // beyond the context (only if the plan and lengths disagree)
+  // K row li into lane li, in place (the slot's registers): through the
+  // wavefront's LDS area, rows padded to kKtRow bytes so that the 16 rows one
+  // read pass touches fall in distinct banks.  LDS operations of a wavefront
+  // complete in order, so the reads see the writes, and the next tile's
+  // writes follow these reads.
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    *reinterpret_cast<lds_u32x4*>(kt + (4 * lq + r) * kKtRow + 16 * li) = __builtin_bit_cast(u32x4_t, kf[r]);
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+    kf[ks] = __builtin_bit_cast(uint4, *reinterpret_cast<const lds_u32x4*>(kt + li * kKtRow + 16 * (4 * ks + lq)));
+  tile_math(a, v, qf, tok0, li, lq, kf, vf, st);
+}
+
+// LDS stores of this wavefront complete, then the workgroup meets.  No wait
+// for vector memory: the tile loads in flight stay in flight.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// The kernel for plans with wide jobs computes every position here.  A
+// plain position is one tile, as in compute_bf16_tile.  A wide job's
+// position covers tiles 4p .. 4p + 3 of the job, of which wavefront w loaded
+// tile 4p + w (of the set's KV head, whole rows as for any tile).  Each
+// wavefront stores its tile in LDS (K rows in its transposition area, V rows
+// in its V area); after a barrier every wavefront scores all four tiles,
+// read back in the operand layouts, against its own group of the set.  A
+// second barrier keeps the next position's stores behind every wavefront's
+// reads.  All four wavefronts take both barriers at every position of every
+// wide job (they walk the same job list), idle ones included: those load
+// and store their tiles and skip the scoring.  One loop serves both kinds of
+// position (with two code paths the registers spill).
+__device__ __forceinline__ void compute_position(const DecodeArgs& a, const JobView& v, const bf16x8_t (&qf)[4],
+                                                 int32_t p, int w, int li, int lq, const uint4 (&kf)[4],
+                                                 uint4 (&vf)[4], lds_char* kt_all, lds_char* vt_all,
+                                                 SoftmaxState& st) {
+  const bool wide = v.wide;
+  lds_char* ktw = kt_all + w * (kTile * kKtRow);
+  lds_char* vtw = vt_all + w * (kTile * kHeadDim * 2);
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    *reinterpret_cast<lds_u32x4*>(ktw + (4 * lq + r) * kKtRow + 16 * li) = __builtin_bit_cast(u32x4_t, kf[r]);
+  if (wide) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      *reinterpret_cast<lds_u32x4*>(vtw + (4 * lq + r) * (kHeadDim * 2) + 16 * li) =
+          __builtin_bit_cast(u32x4_t, vf[r]);
+    lds_barrier();
+  }
+  const int n = wide ? kNW : 1;
+#pragma unroll 1
+  for (int i = 0; i < n; ++i) {
+    const int j = wide ? i : w;  // whose LDS area holds the tile
+    const int32_t tile = wide ? 4 * p + i : p;
+    const int32_t tok0 = kTile * (v.t0 + tile);
+    // Past the context only if the plan and lengths disagree.
+    if ((!wide || (!v.idle && tile < v.T)) && tok0 < v.L) {
+      const lds_char* ktj = kt_all + j * (kTile * kKtRow);
+      const lds_char* vtj = vt_all + j * (kTile * kHeadDim * 2);
+      uint4 kk[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        kk[ks] =
+            __builtin_bit_cast(uint4, *reinterpret_cast<const lds_u32x4*>(ktj + li * kKtRow + 16 * (4 * ks + lq)));
+      if (wide) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          vf[r] = __builtin_bit_cast(
+              uint4, *reinterpret_cast<const lds_u32x4*>(vtj + (4 * lq + r) * (kHeadDim * 2) + 16 * li));
+      }
+      tile_math(a, v, qf, tok0, li, lq, kk, vf, st);
+    }
+  }
+  if (wide) lds_barrier();
+}
+
 // Finished jobs are staged in LDS and written to memory after the
 // wavefront's last job (once the staging area is full, later jobs are
 // written directly, and the last job itself is).  On gfx9 the
@@ -390,7 +459,11 @@ __device__ __forceinline__ void compute_bf16_tile(const DecodeArgs& a, const Job
 // then (m, l) per (entry, column), then (seq, g, record, lengths agree) per entry.
 constexpr int kStageMax = 7;                      // entries per wavefront
 constexpr int kStageFloats = kStageMax * 4 * 128; // accumulator floats per wavefront (G = 4 fills 7 entries)
-constexpr int kStageWaveFloats = kStageFloats + kStageMax * 16 * 2 + kStageMax * 4;
+// The kernel for plans with wide jobs also holds the V areas of a position
+// (4 x 4 KB) and stages 5 entries, so that two workgroups still fit a
+// compute unit's 160 KB of LDS.
+constexpr int kStageMaxWide = 5;
+constexpr int stage_wave_floats(int n) { return n * 4 * 128 + n * 16 * 2 + n * 4; }
 
 struct Stage {
   float* o;      // accumulator entries
@@ -542,7 +615,7 @@ __device__ __forceinline__ void finish_bf16_job(const DecodeArgs& a, const JobVi
   sg.n = e + 1;
 }
 
-template <int B, bool kStream, int kFused>
+template <int B, bool kStream, int kFused, bool kWide>
 __global__ __launch_bounds__(kNW * 64, kWavesPerSimd) void decode_bf16_kernel(DecodeArgs a) {
   static_assert(B == 1 || B == 2 || B == 4 || B == 8 || B == 16 || B == 32, "block size");
   static_assert(kFused != 4 || B >= 16, "window loads read whole tiles of one block");
@@ -550,15 +623,19 @@ __global__ __launch_bounds__(kNW * 64, kWavesPerSimd) void decode_bf16_kernel(De
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: keeps job fields in SGPRs
   const int li = lane & 15;  // MFMA row / column within a 16-lane group
   const int lq = lane >> 4;  // which 16-lane group
-  __shared__ float stage_lds[kNW * kStageWaveFloats];
+  constexpr int kSM = kWide ? kStageMaxWide : kStageMax;
+  constexpr int kSWF = stage_wave_floats(kSM);
+  __shared__ float stage_lds[kNW * kSWF];
   __shared__ __attribute__((aligned(16))) char kt_lds[kNW * kTile * kKtRow];
+  // V areas of a wide job's position (one byte when the kernel has no wide jobs).
+  __shared__ __attribute__((aligned(16))) char vt_lds[kWide ? kNW * kTile * kHeadDim * 2 : 1];
   lds_char* kt = (lds_char*)(kt_lds + w * kTile * kKtRow);
   Stage sg;
-  sg.o = stage_lds + w * kStageWaveFloats;
-  sg.ml = sg.o + kStageFloats;
-  sg.meta = reinterpret_cast<int32_t*>(sg.ml + kStageMax * 16 * 2);
+  sg.o = stage_lds + w * kSWF;
+  sg.ml = sg.o + kSM * 4 * 128;
+  sg.meta = reinterpret_cast<int32_t*>(sg.ml + kSM * 16 * 2);
   sg.n = 0;
-  sg.cap = min(kStageMax, kStageFloats / (128 * a.group));
+  sg.cap = min(kSM, kSM * 4 * 128 / (128 * a.group));
   // The workgroup's jobs are the slots k = 0, 1, ... of its column of the
   // job table (entry k * num_workgroups + blockIdx.x); an empty slot
   // (tile_count 0) ends the column.
@@ -612,8 +689,8 @@ __global__ __launch_bounds__(kNW * 64, kWavesPerSimd) void decode_bf16_kernel(De
   // current job's last tile without fetching anything), so the waits the
   // compiler inserts count exactly the loads in flight.
   JobRef<B> cur, nxt, nx2;
-  load_ref<B>(a, r0, w, lane, cur);
-  view_job(a, r1, w, B, nxt.v);
+  load_ref<B, kWide>(a, r0, w, lane, cur);
+  view_job<kWide>(a, r1, w, B, nxt.v);
   nxt.tb0 = nxt.tb1 = 0;
   // The third job's table entries and the second job's query, and with the
   // plan's first-tile entries the second job's table entries too, are
@@ -621,7 +698,7 @@ __global__ __launch_bounds__(kNW * 64, kWavesPerSimd) void decode_bf16_kernel(De
   // counter retires loads in issue order, so the first tile's wait would
   // otherwise also wait for them.  The first two positions never reach the
   // third job, and with first-tile entries they read no table.
-  view_job(a, r2, w, B, nx2.v);
+  view_job<kWide>(a, r2, w, B, nx2.v);
   nx2.tb0 = nx2.tb1 = 0;
   bf16x8_t qc[4], qn[4];
   load_q(a, cur.v, li, lq, qc);
@@ -644,7 +721,10 @@ __global__ __launch_bounds__(kNW * 64, kWavesPerSimd) void decode_bf16_kernel(De
     const bool in_c = r < cur.v.cnt;
     const bool in_n = !in_c && hn && rn < nxt.v.cnt;
     const bool in_n2 = !in_c && !in_n && hn && hn2 && rn2 < nx2.v.cnt;
-    const int32_t t = in_c ? r : in_n ? rn : in_n2 ? rn2 : cur.v.cnt - 1;
+    const int32_t tp = in_c ? r : in_n ? rn : in_n2 ? rn2 : cur.v.cnt - 1;
+    // A wide job's position covers four tiles; this wavefront loads tile 4 * tp + w.
+    const bool wide = kWide && (in_n ? nxt.v.wide : in_n2 ? nx2.v.wide : cur.v.wide);
+    const int32_t t = wide ? 4 * tp + w : tp;
     const int32_t g = in_n ? nxt.v.g : in_n2 ? nx2.v.g : cur.v.g;
     const int32_t t0 = in_n ? nxt.v.t0 : in_n2 ? nx2.v.t0 : cur.v.t0;
     int32_t e0, e1;
@@ -664,7 +744,10 @@ __global__ __launch_bounds__(kNW * 64, kWavesPerSimd) void decode_bf16_kernel(De
     }
     const int32_t L = in_n ? nxt.v.L : in_n2 ? nx2.v.L : cur.v.L;
     const bool idle = in_n ? nxt.v.idle : in_n2 ? nx2.v.idle : cur.v.idle;
-    const bool live = (in_c || in_n || in_n2) && !idle;
+    // Wide jobs: every wavefront loads its tile (the others score it), and
+    // the tiles of the last position past the job read nothing.
+    const int32_t T = in_n ? nxt.v.T : in_n2 ? nx2.v.T : cur.v.T;
+    const bool live = (in_c || in_n || in_n2) && (wide ? t < T : !idle);
     const int32_t rows = live ? L - kTile * (t0 + t) : 0;
     // Row of this step's appended token in the tile, when the append is fused
     // into this launch and the tile holds it.
@@ -681,7 +764,10 @@ __global__ __launch_bounds__(kNW * 64, kWavesPerSimd) void decode_bf16_kernel(De
   // into slot (kp, vp); false when the stream is done.
   auto step = [&](uint4 (&ks)[4], uint4 (&vs)[4], uint4 (&kp)[4], uint4 (&vp)[4]) {
     issue(x + kDepth, kp, vp);
-    compute_bf16_tile(a, cur.v, qc, x - x0, li, lq, ks, vs, kt, st);
+    if (kWide)
+      compute_position(a, cur.v, qc, x - x0, w, li, lq, ks, vs, (lds_char*)kt_lds, (lds_char*)vt_lds, st);
+    else
+      compute_bf16_tile(a, cur.v, qc, x - x0, li, lq, ks, vs, kt, st);
     ++x;
     if (x - x0 < cur.v.cnt) return true;
     finish_bf16_job(a, cur.v, li, lq, st, sg, !hn);
@@ -714,7 +800,7 @@ __global__ __launch_bounds__(kNW * 64, kWavesPerSimd) void decode_bf16_kernel(De
     // record after it is requested.  Past the column (or at an empty slot)
     // the fields are in-range copies that are never used.
     hn2 = hn && s3 < jend && r3.tile_count > 0;
-    load_ref<B>(a, r3, w, lane, nx2);
+    load_ref<B, kWide>(a, r3, w, lane, nx2);
     ++s3;
     // The query of the next job first: a shared job reads its group
     // descriptor with a scalar load, and the wait for it would otherwise also
@@ -724,16 +810,19 @@ __global__ __launch_bounds__(kNW * 64, kWavesPerSimd) void decode_bf16_kernel(De
     st.reset();
     return true;
   };
-  if (B >= 8 && a.first_blocks != nullptr) {
+  // The first-tile entries name tiles 0 and 1 of a job; a wide job's first
+  // positions need tiles w and 4 + w, so the kernel for wide plans reads the
+  // table entries.
+  if (B >= 8 && !kWide && a.first_blocks != nullptr) {
 #pragma unroll
     for (int u = 0; u < kDepth; ++u) issue_at(u, kf[u], vf[u], true, f0, f1);
-    load_ref<B>(a, r1, w, lane, nxt);
+    load_ref<B, kWide>(a, r1, w, lane, nxt);
   } else {
-    load_ref<B>(a, r1, w, lane, nxt);
+    load_ref<B, kWide>(a, r1, w, lane, nxt);
 #pragma unroll
     for (int u = 0; u < kDepth; ++u) issue(u, kf[u], vf[u]);
   }
-  load_ref<B>(a, r2, w, lane, nx2);
+  load_ref<B, kWide>(a, r2, w, lane, nx2);
   load_q(a, nxt.v, li, lq, qn);
   // The slot ring, unrolled so that every slot index is a constant and the
   // slots stay in registers.
@@ -938,21 +1027,27 @@ hipError_t launch_decode_attention(const DecodeArgs& a, hipStream_t stream) {
   const dim3 grid((unsigned)a.num_workgroups);
   bool launched = false;
   if (a.bf16) {
-#define PA_BF16_LAUNCH(BS, STREAM)                                                                      \
+#define PA_BF16_LAUNCH(BS, STREAM, WIDE)                                                                \
   if (a.new_k == nullptr)                                                                               \
-    hipLaunchKernelGGL((decode_bf16_kernel<BS, STREAM, 0>), grid, dim3(kNW * 64), 0, stream, a);        \
+    hipLaunchKernelGGL((decode_bf16_kernel<BS, STREAM, 0, WIDE>), grid, dim3(kNW * 64), 0, stream, a);  \
   else if (a.fused_loads == 2)                                                                          \
-    hipLaunchKernelGGL((decode_bf16_kernel<BS, STREAM, 2>), grid, dim3(kNW * 64), 0, stream, a);        \
+    hipLaunchKernelGGL((decode_bf16_kernel<BS, STREAM, 2, WIDE>), grid, dim3(kNW * 64), 0, stream, a);  \
   else if (a.fused_loads == 4 && BS >= 16)                                                              \
-    hipLaunchKernelGGL((decode_bf16_kernel<(BS >= 16 ? BS : 16), STREAM, 4>), grid, dim3(kNW * 64), 0, stream, a); \
+    hipLaunchKernelGGL((decode_bf16_kernel<(BS >= 16 ? BS : 16), STREAM, 4, WIDE>), grid, dim3(kNW * 64), 0, \
+                       stream, a);                                                                      \
   else                                                                                                  \
-    hipLaunchKernelGGL((decode_bf16_kernel<BS, STREAM, 1>), grid, dim3(kNW * 64), 0, stream, a);
+    hipLaunchKernelGGL((decode_bf16_kernel<BS, STREAM, 1, WIDE>), grid, dim3(kNW * 64), 0, stream, a);
+  // Plans with wide jobs (which read prefixes shared by several groups, so
+  // their blocks are read more than once) take the kernel that reads them,
+  // with caching loads.
 #define PA_BF16_CASE(BS)                                                                                \
   case BS:                                                                                              \
-    if (a.shared_kv) {                                                                                  \
-      PA_BF16_LAUNCH(BS, false)                                                                         \
+    if (a.wide_jobs > 0) {                                                                              \
+      PA_BF16_LAUNCH(BS, false, true)                                                                   \
+    } else if (a.shared_kv) {                                                                           \
+      PA_BF16_LAUNCH(BS, false, false)                                                                  \
     } else {                                                                                            \
-      PA_BF16_LAUNCH(BS, true)                                                                          \
+      PA_BF16_LAUNCH(BS, true, false)                                                                   \
     }                                                                                                   \
     launched = true;                                                                                    \
     break;
@@ -986,7 +1081,7 @@ hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t stream) {
 }
 
 hipError_t decode_resident_workgroups_per_cu(int* n) {
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, decode_bf16_kernel<16, true, 0>, kNW * 64, 0);
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, decode_bf16_kernel<16, true, 0, false>, kNW * 64, 0);
 }
 
 }  // namespace pagedkv

@@ -41,6 +41,7 @@ struct DecodeArgs {
   int32_t num_merges;
   int32_t num_records;
   int32_t num_groups;
+  int32_t wide_jobs;             // jobs with PA_JOB_WIDE: the launch picks the kernel that reads them
   int32_t bf16;                  // pool dtype: 1 bfloat16, 0 float32
   int32_t shared_kv;             // 1: sequences share blocks (keep K/V cached), 0: stream K/V
   int32_t out_bf16;              // 1: write bfloat16, 0: float32

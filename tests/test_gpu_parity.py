@@ -457,16 +457,21 @@ def test_wide_prefix_cascade_matches_oracle(pk, b, schedule):
     """Prompts sampled 14 times: each prefix is shared by four groups (three of
     four samples and one of two), which the plan places on one die of the grid
     when the grid is a multiple of 8 of at least 64 workgroups (512, 64, 72),
-    and by the chunk schedule otherwise (7).  Same outputs as the oracle
-    within tolerance and as the per-sequence plan within the
-    accumulation-order difference."""
+    reading each prefix once per KV head for the set of four groups (wide
+    jobs: the workgroup's wavefronts exchange tiles through LDS), and by the
+    chunk schedule otherwise (7).  Same outputs as the oracle within
+    tolerance and as the per-sequence plan within the accumulation-order
+    difference."""
     log(f"cascade c5w B={b} schedule={schedule}")
     case = synth.prefix_case("c5w", b)
     got = product_prefix(pk, case, schedule, cascade=True)
     assert got["plan"].num_groups > 0 and got["plan"].info.flags == pk.PA_DECODE_SHARED_KV
+    if schedule == (512, 0):
+        assert got["plan"].info.wide_jobs > 0
     ref = oracle_prefix(case)
     stats = assert_close(got["out"], ref["out"], "bf16", f"cascade c5w/B{b}/{schedule}")
-    log(f"  max|err|={stats['max_abs']:.3g} mean|err|={stats['mean_abs']:.3g} groups={got['plan'].num_groups}")
+    log(f"  max|err|={stats['max_abs']:.3g} mean|err|={stats['mean_abs']:.3g} groups={got['plan'].num_groups} "
+        f"wide jobs={got['plan'].info.wide_jobs}")
     plain = product_prefix(pk, case, schedule)
     assert np.abs(got["out"] - plain["out"]).max() < 2e-3
 
@@ -483,11 +488,14 @@ def test_cascade_decode_with_first_tile_entries(pk, b):
     assert np.array_equal(bits(to_host(out)), bits(got["out"]))
 
 
-def test_cascade_decode_with_fused_append(pk):
+@pytest.mark.parametrize("name,schedule", [("c5s", SMALL_PIECES), ("c5w", (512, 0))])
+def test_cascade_decode_with_fused_append(pk, name, schedule):
     """The append fused into a shared-prefix decode: the appended tokens sit in
-    each sample's own tiles; pools byte-identical to the separate write."""
-    case = synth.prefix_case("c5s", 16)
-    got = product_prefix(pk, case, SMALL_PIECES)
+    each sample's own tiles; pools byte-identical to the separate write.  c5w
+    on the full grid reads its prefixes with wide jobs."""
+    log(f"cascade {name} fused append, schedule={schedule}")
+    case = synth.prefix_case(name, 16)
+    got = product_prefix(pk, case, schedule)
     bm, pool, lens = got["bm"], got["pool"], got["lens"]
     nseq = len(lens)
     # one more token per sample: block manager slots, then fused vs separate
@@ -501,10 +509,11 @@ def test_cascade_decode_with_fused_append(pk):
     k_sep, v_sep = pool.k.clone(), pool.v.clone()
     sep = pk.KvPool(k_sep, v_sep)
     pk.reshape_and_cache(sep, to_dev(nk), to_dev(nv), to_dev(np.asarray(slots, np.int64)))
-    out_sep, _ = cascade_decode(pk, sep, to_dev(case["q"]), tables, lens2, case["scale"], bm, np.arange(nseq),
-                                SMALL_PIECES)
+    out_sep, plan = cascade_decode(pk, sep, to_dev(case["q"]), tables, lens2, case["scale"], bm, np.arange(nseq),
+                                   schedule)
+    assert name != "c5w" or plan.info.wide_jobs > 0
     out_fused, _ = cascade_decode(pk, pool, to_dev(case["q"]), tables, lens2, case["scale"], bm, np.arange(nseq),
-                                  SMALL_PIECES, new_key=to_dev(nk), new_value=to_dev(nv))
+                                  schedule, new_key=to_dev(nk), new_value=to_dev(nv))
     torch.cuda.synchronize()
     assert np.array_equal(bits(to_host(pool.k)), bits(to_host(k_sep)))
     assert np.array_equal(bits(to_host(pool.v)), bits(to_host(v_sep)))

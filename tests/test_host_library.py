@@ -891,7 +891,11 @@ def test_prefix_plan_cache_policy():
 
 
 def _check_prefix_plan(plan, lens, hkv, hq, group, tokens):
-    """Structural invariants of a shared-prefix plan."""
+    """Structural invariants of a shared-prefix plan, per (sequence, KV head,
+    tile): every tile of every sequence read by exactly one job, shared
+    pieces numbered before each member's own pieces, records disjoint.  A
+    wide job (PA_JOB_WIDE) reads one KV head for a set of up to four groups
+    whose descriptors lie ceil(hkv / 4) apart."""
     G = hq // hkv
     cap = min(4, max(1, 16 // G))
     hb_n = -(-hkv // 4)
@@ -900,31 +904,50 @@ def _check_prefix_plan(plan, lens, hkv, hq, group, tokens):
     groups = plan.groups()
     covered = {}
     own = {}
+    wide_jobs = 0
+
+    def cover(s, g, t0, cnt, what):
+        for t in range(t0, t0 + cnt):
+            assert (s, g, t) not in covered
+            covered[(s, g, t)] = what
+
     for seq, t0, cnt, hbf, part, nparts, rb, L in jobs:
         shared = bool(hbf & pk.PA_JOB_SHARED)
-        hb = hbf & 0xFFFF
         assert L == lens[seq] and 1 <= cnt <= 64
-        if shared:
+        if shared and hbf & pk.PA_JOB_WIDE:
+            wide_jobs += 1
+            g = hbf & 0xFFFF
+            ngr, full, last = nparts & 0xFF, (nparts >> 8) & 0xFF, (nparts >> 16) & 0xFF
+            assert 1 <= ngr <= 4 and 0 <= g < hkv
+            for k in range(ngr):
+                d = groups[rb + k * hb_n]
+                n = int(d[0])
+                assert n == (full if k < ngr - 1 else last) and 2 <= n <= cap and d[1] == g // 4
+                assert k > 0 or d[2] == seq
+                for m in range(n):
+                    cover(int(d[2 + m]), g, t0, cnt, ("shared", part))
+        elif shared:
+            hb = hbf & 0xFFFF
             d = groups[rb]
             n = int(d[0])
             assert 2 <= n <= cap and d[1] == hb and d[2] == seq and nparts == n
             for m in range(n):
-                s = int(d[2 + m])
-                for t in range(t0, t0 + cnt):
-                    assert (s, hb, t) not in covered
-                    covered[(s, hb, t)] = ("shared", part)
+                for g in range(4 * hb, min(hkv, 4 * hb + 4)):
+                    cover(int(d[2 + m]), g, t0, cnt, ("shared", part))
         else:
-            for t in range(t0, t0 + cnt):
-                assert (seq, hb, t) not in covered
-                covered[(seq, hb, t)] = ("own", part)
+            hb = hbf & 0xFFFF
+            for g in range(4 * hb, min(hkv, 4 * hb + 4)):
+                cover(seq, g, t0, cnt, ("own", part))
             own.setdefault((seq, hb), []).append((part, nparts, rb))
+    assert plan.info.wide_jobs == wide_jobs
     for s, L in enumerate(lens):
-        for hb in range(hb_n):
+        for g in range(hkv):
             for t in range(-(-int(L) // 16)):
-                assert (s, hb, t) in covered
-    # num_tiles counts the tiles read: a shared tile once for its whole group
+                assert (s, g, t) in covered
+    # num_tiles counts the tiles read: a shared tile once for its whole group (or set)
     assert plan.info.num_tiles == sum(j[2] for j in jobs)
-    # every group's members: shared tiles below T, same T for all, records consistent
+    # every group's members: shared pieces 0 .. k - 1 on every KV head of the
+    # head block, own pieces k .. parts - 1, records consistent and disjoint
     used = set()
     for d in groups:
         n, hb = int(d[0]), int(d[1])
@@ -932,9 +955,13 @@ def _check_prefix_plan(plan, lens, hkv, hq, group, tokens):
             s, rb, np_ = int(d[2 + m]), int(d[6 + m]), int(d[10 + m])
             parts = sorted(own[(s, hb)])
             assert all(p[1] == np_ and p[2] == rb for p in parts)
-            shared_parts = {v[1] for k, v in covered.items() if k[0] == s and k[1] == hb and v[0] == "shared"}
-            assert sorted(shared_parts) == list(range(len(shared_parts)))
-            assert [p[0] for p in parts] == list(range(len(shared_parts), np_))
+            ks = None
+            for g in range(4 * hb, min(hkv, 4 * hb + 4)):
+                shared_parts = sorted({v[1] for k, v in covered.items() if k[0] == s and k[1] == g and v[0] == "shared"})
+                assert shared_parts == list(range(len(shared_parts)))
+                assert ks is None or ks == len(shared_parts)
+                ks = len(shared_parts)
+            assert [p[0] for p in parts] == list(range(ks, np_))
             for w in range(min(4, hkv - 4 * hb)):
                 for p in range(np_):
                     r = rb + w * np_ + p
@@ -993,6 +1020,28 @@ def test_wide_prefix_plan_invariants(nwg):
         plan = pk.decode_plan_prefix(lens, hkv, hq, group, tokens, num_workgroups=nwg)
         assert plan.num_groups > 0 and plan.info.flags == pk.PA_DECODE_SHARED_KV
         _check_prefix_plan(plan, lens, hkv, hq, group, tokens)
+        # The full grid reads each prefix in sets of groups, per KV head; a
+        # grid that is not a multiple of the 8 dies never does.
+        if nwg == 512:
+            assert plan.info.wide_jobs > 0
+        if nwg == 7:
+            assert plan.info.wide_jobs == 0
+
+
+def test_wide_sets_fall_back_when_cuts_differ():
+    """A die holding more of a key group's head streams than workgroups cuts
+    them unevenly; the four KV heads of a set's head block would then hold
+    different numbers of shared pieces, which the per-head-block record
+    layout cannot express, so the plan reads every group on its own."""
+    rng = np.random.default_rng(5)
+    bm, seqs = _forked_batch(16, 12, 20, 600, rng.integers(1, 200, 240))
+    tables, lens = bm.export(seqs, 128)
+    group, tokens = bm.prefix_groups(seqs)
+    sets = pk.decode_plan_prefix(lens, 8, 32, group, tokens, num_workgroups=64)
+    alone = pk.decode_plan_prefix(lens, 4, 16, group, tokens, num_workgroups=64)
+    assert sets.info.wide_jobs > 0 and alone.info.wide_jobs == 0
+    _check_prefix_plan(sets, lens, 8, 32, group, tokens)
+    _check_prefix_plan(alone, lens, 4, 16, group, tokens)
 
 
 def _placement(plan):
