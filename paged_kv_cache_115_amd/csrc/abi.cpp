@@ -832,7 +832,8 @@ pa_status schedule_prefix(const int32_t* lens, int32_t num_seqs, int32_t num_kv_
 // The two workgroups of a compute unit do not share it equally.  Workgroup b
 // is dispatched just before b + nwg / 2, on the same compute unit, and its
 // wavefronts win the issue arbitration of the SIMDs the two share.  Measured
-// on MI355X at C3 with per-wavefront timestamps: while both run, the older
+// on MI355X (batch 256, 8 KV heads, lognormal lengths around 200 tokens)
+// with per-wavefront timestamps: while both run, the older
 // workgroup streams about 0.51 tiles/us and the younger 0.32; a workgroup
 // left alone streams 0.75.  Split evenly by tiles, the older finished about
 // 8 us first and the compute unit spent its last quarter at one workgroup.
@@ -947,8 +948,8 @@ pa_status schedule_lpt(const int32_t* lens, int32_t num_seqs, int32_t num_kv_hea
     if (paired) {
       // Each pair's jobs are split between its two workgroups by the
       // modelled end time (pair_end_us), over every subset of the pair's jobs
-      // (subset sums built incrementally).  Measured at C3: attention launch
-      // 39.65 -> 39.1 us.
+      // (subset sums built incrementally).  Measured on the batch of 256
+      // (8 KV heads): attention launch 39.65 -> 39.1 us.
       std::vector<int32_t> first((size_t)bins + 1, 0), list(jobs.size());
       for (size_t j = 0; j < jobs.size(); ++j) first[placed_wg[j] % bins + 1] += 1;
       for (int64_t b = 0; b < bins; ++b) first[b + 1] += first[b];
@@ -980,8 +981,8 @@ pa_status schedule_lpt(const int32_t* lens, int32_t num_seqs, int32_t num_kv_hea
   // Each workgroup runs its jobs smallest first (ties in generation order):
   // job boundaries then fall in the start-up, where every tile waits in the
   // memory queue anyway, and the workgroup ends on its longest, unbroken
-  // stream.  Measured at C3: 39.8 against 40.1 us in generation order and
-  // 40.4 us largest first.
+  // stream.  Measured on the batch of 256 (8 KV heads): 39.8 against 40.1
+  // us in generation order and 40.4 us largest first.
   out.pieces.clear();
   out.pieces.reserve(jobs.size());
   {
@@ -1345,7 +1346,7 @@ namespace pagedkv {
 // addresses win and each pool and its new rows lie within one 4 GiB window
 // (4), every tile is read by buffer loads at 32-bit lane offsets in that
 // window: the streaming cache policy is kept, with less lane arithmetic than
-// 64-bit addresses (C3 39.65 against 39.85 us).
+// 64-bit addresses (batch of 256, 8 KV heads: 39.65 against 39.85 us).
 int32_t fused_mode(const pa_kv_pool* pool, const void* new_key, const void* new_value, int32_t num_seqs,
                    int32_t group, const pa_decode_plan_info* info, DecodeArgs* a) {
   if (new_key == nullptr) return 0;
@@ -1354,8 +1355,9 @@ int32_t fused_mode(const pa_kv_pool* pool, const void* new_key, const void* new_
   const int64_t seq_streams = (int64_t)num_seqs * ((hkv + 3) / 4);
   const bool short_seqs = (int64_t)info->num_tiles < kShortSequenceTiles * seq_streams;
   // Mode 4 (window loads) whenever the tiles are whole blocks and both
-  // windows fit: measured at least as fast as 1 and 2 on every workload
-  // (C2, C3, C4, C5, c6).  Otherwise the separate path for long contexts
+  // windows fit: measured at least as fast as 1 and 2 on every batch shape
+  // tried (MHA batch 64; GQA batch 256; long contexts, batch 16; forked
+  // prefixes; shared system prompts).  Otherwise the separate path for long contexts
   // with 4 or more query heads per KV head, per-lane addresses for the rest.
   const int32_t fallback = !(short_seqs || group < 4 || pool->block_size < 8) ? 1 : 2;
   if (pool->block_size < 16) return fallback;
